@@ -1,0 +1,252 @@
+#!/usr/bin/env python
+"""Benchmark of the MLA forward on one MI355X.
+
+One step = one DeepSeek-V3-shaped prefill (B=1, S=4096, bf16, interleaved
+RoPE) followed by one absorbed decode step (B=64 sequences, latent cache
+capacity 8193, lengths uniform in [1024, 8192], bf16).  Inputs are seeded
+synthetic tensors already resident in HBM when timing starts.
+
+Printed: one JSON line.  `value` is the prefill throughput in algorithmic
+TFLOP/s (2 B S sum(params) + 2 B H S(S+1)/2 (d_n + d_r + d_v); the masked
+upper triangle is not counted).  The decode result (latent-cache GB/s of the
+attention kernel, algorithmic bytes = sum_b (L_b + 1) (r_kv + d_r) 2) sits in
+"decode".  Kernel times come from HIP events the library records at its
+stage boundaries on the launch stream.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_BF16_TFLOPS = 2516.6   # dense MFMA bf16 peak
+MI355X_HBM_GBS = 8000.0       # HBM3E peak
+METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
+
+
+def prefill_flops(c, B, S):
+    D, H = c["hidden_size"], c["num_attention_heads"]
+    rq, rkv = c["q_lora_rank"], c["kv_lora_rank"]
+    dn, dr, dv = c["qk_nope_head_dim"], c["qk_rope_head_dim"], c["v_head_dim"]
+    params = (rq * D + H * dn * rq + H * dr * rq + rkv * D + dr * D + H * dn * rkv
+              + H * dv * rkv + D * H * dv)
+    proj = 2.0 * B * S * params
+    attn = 2.0 * B * H * (S * (S + 1) / 2.0) * (dn + dr + dv)
+    return proj, attn, {
+        "down_proj": 2.0 * B * S * (rq + rkv + dr) * D,
+        "q_up_proj": 2.0 * B * S * H * (dn + dr) * rq,
+        "kv_up_proj": 2.0 * B * S * H * (dn + dv) * rkv,
+        "attention": attn,
+        "out_proj": 2.0 * B * S * D * H * dv,
+    }
+
+
+def decode_bytes(c, lens):
+    w = c["kv_lora_rank"] + c["qk_rope_head_dim"]
+    return float(sum(int(L) + 1 for L in lens) * w * 2)
+
+
+def decode_flops(c, lens):
+    H, r, dr = c["num_attention_heads"], c["kv_lora_rank"], c["qk_rope_head_dim"]
+    return float(sum(int(L) + 1 for L in lens) * H * (2 * (r + dr) + 2 * r))
+
+
+def cpu_baseline(c_pre, x, w, c_dec, xd, wd, lens, cache, seconds_hint=True):
+    """The float64 oracle, untuned, on bounded samples of the same workloads."""
+    import numpy as np
+
+    import oracle as orc
+    from tests.helpers import oracle_cfg
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    s_sample = 1024
+    t0 = time.perf_counter()
+    orc.mla_prefill(oracle_cfg(c_pre), w, x[:, :s_sample])
+    t_pre = time.perf_counter() - t0
+    proj, attn, _ = prefill_flops(c_pre, 1, s_sample)
+    n_seq = 8
+    t0 = time.perf_counter()
+    orc.mla_decode_absorbed(oracle_cfg(c_dec), wd, xd[:n_seq], cache[:n_seq], lens[:n_seq])
+    t_dec = time.perf_counter() - t0
+    return {
+        "value": (proj + attn) / t_pre / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"prefill of the first {s_sample} tokens of the S=4096 input "
+                  f"({(proj + attn) / 1e9:.1f} GFLOP, {t_pre:.2f} s, float64 NumPy)",
+        "decode": {
+            "value": decode_bytes(c_dec, lens[:n_seq]) / t_dec / 1e9,
+            "unit": "GB/s",
+            "sample": f"absorbed decode of {n_seq} of the 64 sequences ({t_dec:.2f} s)",
+        },
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replicas", type=int, default=3,
+                    help="decode cache replicas rotated per step (defeats the 256 MB MALL)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import head_latent_attention_08_amd as m
+    import synth_inputs as si
+    from tests.gpu_util import mla_cfg, to_dev, weights_to_dev
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    torch.cuda.set_device(0)
+    c_pre = si.CONFIGS["v3_prefill"]
+    c_dec = si.CONFIGS["v3_decode"]
+    log("bench: generating V3 prefill inputs (seed 3000)")
+    x, w = si.make_inputs(c_pre)
+    cfg_pre = mla_cfg(c_pre)
+    xd_pre = to_dev(x, "bf16")
+    wd_pre = weights_to_dev(w, "bf16")
+    B, S = x.shape[0], x.shape[1]
+    y_pre = torch.empty((B, S, c_pre["hidden_size"]), dtype=torch.bfloat16, device="cuda")
+    lat_pre = torch.empty((B, S, 576), dtype=torch.bfloat16, device="cuda")
+    ws_pre = torch.empty(m.mla_prefill_workspace_size(cfg_pre, B, S), dtype=torch.uint8,
+                         device="cuda")
+
+    log("bench: generating V3 decode inputs (seed 4000)")
+    xdec, wdec, lens, cache = si.make_decode_inputs(c_dec)
+    cfg_dec = mla_cfg(c_dec)
+    caches = [to_dev(cache, "bf16")]
+    for _ in range(args.replicas - 1):
+        caches.append(caches[0].clone())
+    lens_d = torch.from_numpy(lens).cuda()
+    xdec_d = to_dev(xdec, "bf16")
+    wdec_d = weights_to_dev(wdec, "bf16")
+    Bd = xdec.shape[0]
+    y_dec = torch.empty((Bd, c_dec["hidden_size"]), dtype=torch.bfloat16, device="cuda")
+    ws_dec = torch.empty(m.mla_decode_workspace_size(cfg_dec, Bd, caches[0].shape[1]),
+                         dtype=torch.uint8, device="cuda")
+
+    n_pe = len(m.PREFILL_STAGES) + 1
+    n_de = len(m.DECODE_STAGES) + 1
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record()  # creates the underlying hipEvent_t
+        return evs
+
+    def step(i, pe=None, de=None):
+        m.mla_set_stage_events([e.cuda_event for e in pe] if pe else None)
+        m.mla_prefill_forward(cfg_pre, wd_pre, xd_pre, y=y_pre, latent_out=lat_pre,
+                              workspace=ws_pre)
+        m.mla_set_stage_events([e.cuda_event for e in de] if de else None)
+        m.mla_decode_absorbed(cfg_dec, wdec_d, xdec_d, caches[i % len(caches)], lens_d,
+                              y=y_dec, workspace=ws_dec)
+        m.mla_set_stage_events(None)
+
+    log(f"bench: warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pev = [new_events(n_pe) for _ in range(args.steps)]
+    dev_ = [new_events(n_de) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, pev[i], dev_[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+
+    def stage_ms(evs, names):
+        per = {n: [] for n in names}
+        whole = []
+        for e in evs:
+            for k, n in enumerate(names):
+                per[n].append(e[k].elapsed_time(e[k + 1]))
+            whole.append(e[0].elapsed_time(e[-1]))
+        return {n: float(np.mean(v)) for n, v in per.items()}, float(np.mean(whole)), \
+            float(np.min(whole))
+
+    pst, pre_ms, pre_min = stage_ms(pev, m.PREFILL_STAGES)
+    dst, dec_ms, dec_min = stage_ms(dev_, m.DECODE_STAGES)
+    proj, attn, per_flops = prefill_flops(c_pre, B, S)
+    pre_tflops = (proj + attn) / (pre_ms * 1e-3) / 1e12
+    kv_bytes = decode_bytes(c_dec, lens)
+    att_ms = dst["latent_attention"]
+    att_merge_ms = dst["latent_attention"] + dst["split_merge"]
+    dec_gbs = kv_bytes / (att_ms * 1e-3) / 1e9
+
+    stage_tf = {k: per_flops[k] / (pst[k] * 1e-3) / 1e12 for k in per_flops}
+    dom = max(per_flops, key=lambda k: pst[k])
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": stage_tf[dom],
+                "peak": MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": stage_tf[dom] / MI355X_BF16_TFLOPS, "traffic": None,
+                "flops_per_launch": per_flops[dom], "ms_per_launch": pst[dom]}
+    decode_roofline = {"bound": "hbm", "kernel": "latent_attention", "achieved": dec_gbs,
+                       "peak": MI355X_HBM_GBS, "unit": "GB/s", "frac": dec_gbs / MI355X_HBM_GBS,
+                       "traffic": None, "bytes_per_launch": kv_bytes, "ms_per_launch": att_ms}
+
+    out = {
+        "metric": METRIC,
+        "value": pre_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations and cache, N(0,0.006^2) weights)",
+        "config": {"workload": "v3_prefill_b1_s4096 + v3_decode_b64_cap8193",
+                   "prefill": {"batch": B, "seq_len": S, "rope": "interleaved",
+                               "gflop": (proj + attn) / 1e9},
+                   "decode": {"batch": Bd, "cache_capacity": int(caches[0].shape[1]),
+                              "lens": "U{1024..8192} seed 4001",
+                              "latent_bytes": kv_bytes, "replicas": len(caches)}},
+        "prefill": {"ms": pre_ms, "ms_min": pre_min, "tflops": pre_tflops,
+                    "frac_of_bf16_peak": pre_tflops / MI355X_BF16_TFLOPS,
+                    "stage_ms": pst, "stage_tflops": stage_tf},
+        "decode": {"value": dec_gbs, "unit": "GB/s", "attention_ms": att_ms,
+                   "attention_plus_merge_ms": att_merge_ms,
+                   "attention_plus_merge_gbs": kv_bytes / (att_merge_ms * 1e-3) / 1e9,
+                   "attention_tflops": decode_flops(c_dec, lens) / (att_ms * 1e-3) / 1e12,
+                   "step_ms": dec_ms, "step_ms_min": dec_min, "stage_ms": dst},
+        "roofline": roofline,
+        "decode_roofline": decode_roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the float64 oracle on bounded samples")
+        out["cpu_baseline"] = cpu_baseline(c_pre, x, w, c_dec, xdec, wdec, lens, cache)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,28 @@
+"""MI355X-native DeepSeek-V3 Multi-head Latent Attention forward.
+
+The compute lives in libmla.so (hand-written gfx950 HIP kernels behind the C
+ABI in include/mla.h); this package is its ctypes binding.
+"""
+
+from .mla import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_F32,
+    ROPE_HALF_SPLIT,
+    ROPE_INTERLEAVED,
+    MlaConfig,
+    MlaError,
+    RopeParams,
+    load_library,
+    mla_decode_absorbed,
+    mla_decode_layout_of,
+    mla_decode_workspace_size,
+    mla_prefill_forward,
+    mla_prefill_layout_of,
+    mla_prefill_workspace_size,
+    mla_rope_apply,
+    mla_set_stage_events,
+    PREFILL_STAGES,
+    DECODE_STAGES,
+    mla_softmax_scale,
+    mla_version,
+)

@@ -1,0 +1,151 @@
+// Bandwidth-bound helpers of the MLA forward: RMSNorm of c_q, RoPE in both
+// conventions, latent-row copies and the decode cache append.
+
+#include "common.h"
+#include "internal.h"
+
+namespace mla {
+namespace {
+
+// RMSNorm: one wave per row, fp32 sum of squares, x * rsqrt(mean + eps) * g.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(T *x, int64_t rows, int64_t ld, int n,
+                                                      const T *g, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  T *xr = x + row * ld;
+  float ss = 0.f;
+  for (int c = lane; c < n; c += 64) {
+    float v = to_f32(xr[c]);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)n + eps);
+  for (int c = lane; c < n; c += 64) xr[c] = from_f32<T>(to_f32(xr[c]) * inv * to_f32(g[c]));
+}
+
+// RoPE.  A workgroup takes `tpb` consecutive tokens: it first forms
+// cos/sin of every (token, pair) in float64 (the angle pos * inv_freq is
+// reduced in double precision, so large positions keep full accuracy), then
+// rotates all heads of those tokens.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(T *x, int64_t n_tok, int64_t S, int64_t sb,
+                                                   int64_t ss, int n_heads, int64_t sh,
+                                                   const int32_t *positions, RopeTab tab,
+                                                   int tpb) {
+  __shared__ float cs[256], sn[256];
+  const int P = tab.pairs;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  for (int i = threadIdx.x; i < tpb * P; i += blockDim.x) {
+    const int64_t t = t0 + i / P;
+    if (t < n_tok) {
+      const int pr = i % P;
+      const double pos = positions ? (double)positions[t] : (double)(t % S);
+      double s, c;
+      sincos(pos * tab.inv_freq[pr], &s, &c);
+      cs[i] = (float)c * tab.amp;
+      sn[i] = (float)s * tab.amp;
+    }
+  }
+  __syncthreads();
+  const int per_tok = n_heads * P;
+  for (int i = threadIdx.x; i < tpb * per_tok; i += blockDim.x) {
+    const int tl = i / per_tok;
+    const int64_t t = t0 + tl;
+    if (t >= n_tok) break;
+    const int rem = i - tl * per_tok;
+    const int h = rem / P, pr = rem - h * P;
+    T *base = x + (t / S) * sb + (t % S) * ss + (int64_t)h * sh;
+    const int i0 = tab.convention == 0 ? pr : 2 * pr;
+    const int i1 = tab.convention == 0 ? pr + P : 2 * pr + 1;
+    const float a = to_f32(base[i0]), b = to_f32(base[i1]);
+    const float c = cs[tl * P + pr], s = sn[tl * P + pr];
+    base[i0] = from_f32<T>(a * c - b * s);
+    base[i1] = from_f32<T>(b * c + a * s);
+  }
+}
+
+template <typename T>
+__global__ void copy_rows_kernel(T *dst, int64_t ldd, const T *src, int64_t lds, int64_t rows,
+                                 int width) {
+  const int64_t total = rows * width;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / width;
+    const int c = (int)(i - r * width);
+    dst[r * ldd + c] = src[r * lds + c];
+  }
+}
+
+template <typename T>
+__global__ void cache_append_kernel(T *cache, int64_t cap, const int32_t *lens, const T *src,
+                                    int64_t lds, int width) {
+  const int b = blockIdx.x;
+  const int32_t L = lens[b];
+  if (L < 0 || (int64_t)L >= cap) return;
+  T *dst = cache + ((int64_t)b * cap + L) * width;
+  for (int c = threadIdx.x; c < width; c += blockDim.x) dst[c] = src[(int64_t)b * lds + c];
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(int dtype, void *x, int64_t rows, int64_t ld, int n, const void *g,
+                          float eps, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + 3) / 4));
+  if (dtype == BF16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16>, grid, dim3(256), 0, st, (bf16 *)x, rows, ld, n,
+                       (const bf16 *)g, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, st, (float *)x, rows, ld, n,
+                       (const float *)g, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb, int64_t ss,
+                       int n_heads, int64_t sh, const int32_t *positions, const RopeTab &tab,
+                       hipStream_t st) {
+  if (n_tok <= 0) return hipSuccess;
+  int per_tok = n_heads * tab.pairs;
+  int tpb = per_tok >= 256 ? 1 : 256 / per_tok;
+  if (tpb * tab.pairs > 256) tpb = 256 / tab.pairs;
+  if (tpb < 1) tpb = 1;
+  dim3 grid((unsigned)((n_tok + tpb - 1) / tpb));
+  if (dtype == BF16)
+    hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(256), 0, st, (bf16 *)x, n_tok, S, sb, ss,
+                       n_heads, sh, positions, tab, tpb);
+  else
+    hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, st, (float *)x, n_tok, S, sb, ss,
+                       n_heads, sh, positions, tab, tpb);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src, int64_t lds,
+                            int64_t rows, int width, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  int64_t total = rows * width;
+  unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+  if (dtype == BF16)
+    hipLaunchKernelGGL(copy_rows_kernel<bf16>, dim3(blocks), dim3(256), 0, st, (bf16 *)dst, ldd,
+                       (const bf16 *)src, lds, rows, width);
+  else
+    hipLaunchKernelGGL(copy_rows_kernel<float>, dim3(blocks), dim3(256), 0, st, (float *)dst,
+                       ldd, (const float *)src, lds, rows, width);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_append(int dtype, void *cache, int64_t cap, const int32_t *lens,
+                               const void *src, int64_t lds, int64_t batch, int width,
+                               hipStream_t st) {
+  if (batch <= 0) return hipSuccess;
+  if (dtype == BF16)
+    hipLaunchKernelGGL(cache_append_kernel<bf16>, dim3((unsigned)batch), dim3(256), 0, st,
+                       (bf16 *)cache, cap, lens, (const bf16 *)src, lds, width);
+  else
+    hipLaunchKernelGGL(cache_append_kernel<float>, dim3((unsigned)batch), dim3(256), 0, st,
+                       (float *)cache, cap, lens, (const float *)src, lds, width);
+  return hipGetLastError();
+}
+
+}  // namespace mla

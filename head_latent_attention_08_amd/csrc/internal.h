@@ -1,0 +1,111 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum DType { F32 = 0, BF16 = 1 };
+
+inline size_t dtype_size(int dt) { return dt == BF16 ? 2 : 4; }
+
+// One contiguous range of output columns [n_begin, next n_begin) of a GEMM:
+// where its B rows come from and where its results go.  Output column n of
+// the range maps to head h = (n - n_begin) / dh and channel d = (n - n_begin)
+// % dh, and output row m to (b, s) = (m / S, m % S); the element lands at
+//   C + ((b * H + h) * S + s) * ld + off + d.
+// With H = 1 and dh >= width this is a plain row-major store with row pitch ld.
+struct GemmSeg {
+  const void *B;
+  int64_t ldb;
+  int n_begin;
+  void *C;
+  int dh;
+  int64_t ld;
+  int off;
+};
+
+struct GemmDesc {
+  int dtype = BF16;
+  int M = 0, N = 0, K = 0;
+  int batch = 1;
+  const void *A = nullptr;
+  int64_t lda = 0, strideA = 0;  // elements
+  int64_t strideB = 0, strideC = 0;
+  bool b_kn = false;  // B stored [K][N] (N contiguous) instead of [N][K]
+  int S = 1, H = 1;
+  int nseg = 1;
+  GemmSeg seg[3];
+};
+
+hipError_t launch_gemm(const GemmDesc &d, hipStream_t st);
+
+// In-place RMSNorm of n columns of `rows` rows with pitch ld: x * (mean(x^2)
+// + eps)^-1/2 * g, fp32 reduction.
+hipError_t launch_rmsnorm(int dtype, void *x, int64_t rows, int64_t ld, int n,
+                          const void *g, float eps, hipStream_t st);
+
+// RoPE frequencies, resolved on the host in float64.
+struct RopeTab {
+  double inv_freq[64];
+  float amp;        // multiplies cos and sin (YaRN mscale ratio)
+  int pairs;        // rope_dim / 2
+  int convention;   // 0 half-split, 1 interleaved
+};
+
+// In-place RoPE: element (t, h, i) at x + (t / S) * sb + (t % S) * ss + h * sh + i,
+// position positions[t] (device) or t % S when positions is NULL.
+hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb,
+                       int64_t ss, int n_heads, int64_t sh,
+                       const int32_t *positions, const RopeTab &tab,
+                       hipStream_t st);
+
+// Copy `width` contiguous elements per row: dst row t at dst + t * ldd from
+// src + t * lds (prefill latent output).
+hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src,
+                            int64_t lds, int64_t rows, int width,
+                            hipStream_t st);
+
+// Decode: write row t of src (width elements) into cache[b, lens[b]] when
+// 0 <= lens[b] < cap.
+hipError_t launch_cache_append(int dtype, void *cache, int64_t cap,
+                               const int32_t *lens, const void *src,
+                               int64_t lds, int64_t batch, int width,
+                               hipStream_t st);
+
+struct PrefillAttnArgs {
+  const void *q;      // [B, H, S, dn + dr]
+  const void *k_nope; // [B, H, S, dn]
+  const void *k_pe;   // rows of pitch ld_kpe, token t = b * S + s
+  int64_t ld_kpe;
+  const void *v;      // [B, H, S, dv]
+  void *o;            // [B * S, H * dv]
+  int B, S, H;
+  float scale;
+};
+
+hipError_t launch_prefill_attention(int dtype, int dn, int dr, int dv,
+                                    const PrefillAttnArgs &a, hipStream_t st);
+
+struct DecodeAttnArgs {
+  const void *q_lat;  // [B, H, r + dr]  absorbed query ‖ post-RoPE q_pe
+  const void *cache;  // [B, cap, r + dr]
+  const int32_t *lens;
+  void *o_lat;        // [B, H, r]
+  float *part_o;      // [(n_blocks + B), H, r]
+  float *part_ml;     // [(n_blocks + B), H, 2]
+  int64_t cap;
+  int B, H;
+  int n_blocks;
+  float scale;
+};
+
+hipError_t launch_decode_attention(int dtype, int r, int dr,
+                                   const DecodeAttnArgs &a, hipStream_t st);
+hipError_t launch_decode_merge(int dtype, int r, const DecodeAttnArgs &a,
+                               hipStream_t st);
+
+int decode_blocks();
+
+}  // namespace mla

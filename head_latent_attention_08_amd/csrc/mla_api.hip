@@ -1,0 +1,662 @@
+// C ABI of the MLA forward: argument checks, workspace carving, launch
+// sequences for prefill and absorbed decode, and the standalone RoPE.
+//
+// The prefill follows MultiHeadLatentAttention.forward of "The Evolving
+// Transformer -- DeepSeek V2 & V3" (section 01) step by step:
+//   1. down projections  [c_q ‖ c_kv ‖ k_pe] = x [w_down_q; w_down_kv; w_kr]^T
+//   2. RMSNorm of c_q      3. RoPE of k_pe (shared key)
+//   4. q up-projection into head-major q = [q_nope ‖ q_pe], then RoPE of q_pe
+//   5. kv up-projection into head-major k_nope and v
+//   6. causal attention  7. output projection y = o wo^T
+// The decode step replaces 5-6 by the absorbed form over the latent cache.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/mla.h"
+#include "internal.h"
+
+using namespace mla;
+
+namespace {
+
+thread_local std::string g_err;
+thread_local void *const *g_events = nullptr;
+thread_local int g_n_events = 0;
+
+mla_status fail(mla_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+mla_status fail(mla_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+mla_status hip_fail(hipError_t e, const char *where) {
+  return fail(MLA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define MLA_HIP(call, where)                         \
+  do {                                               \
+    hipError_t e_ = (call);                          \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+// Record stage event k on the stream when the caller asked for stage timing.
+hipError_t mark(int k, hipStream_t st) {
+  if (g_events && k < g_n_events && g_events[k])
+    return hipEventRecord((hipEvent_t)g_events[k], st);
+  return hipSuccess;
+}
+
+#define MLA_MARK(k) MLA_HIP(mark((k), st), "stage event")
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+mla_status check_rope(const mla_rope_params *rp, int rope_dim) {
+  if (!rp) return fail(MLA_ERR_INVALID_ARGUMENT, "rope params are NULL");
+  if (rp->convention != MLA_ROPE_HALF_SPLIT && rp->convention != MLA_ROPE_INTERLEAVED)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "rope convention %d is neither 0 nor 1",
+                rp->convention);
+  if (!(rp->theta > 1.0f) || !std::isfinite(rp->theta))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "rope theta must be finite and > 1");
+  if (!(rp->factor >= 1.0f) || !std::isfinite(rp->factor))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "rope factor must be finite and >= 1");
+  if (rp->factor > 1.0f) {
+    if (rp->original_max_position < 1)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "YaRN needs original_max_position >= 1");
+    if (!(rp->beta_fast > 0) || !(rp->beta_slow > 0))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "YaRN betas must be > 0");
+  }
+  if (rope_dim < 2 || rope_dim > 128 || (rope_dim & 1))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "rope_dim %d must be even and in [2, 128]", rope_dim);
+  return MLA_OK;
+}
+
+double yarn_mscale(double s, double m) { return s <= 1.0 ? 1.0 : 0.1 * m * std::log(s) + 1.0; }
+
+// Frequencies of pair i: theta^(-2i/d).  With YaRN (factor > 1) the pairs
+// between the correction indices of beta_fast and beta_slow blend linearly
+// (in pair index) from the original frequency to frequency / factor; pairs
+// past the slow bound are fully divided.  The cos/sin amplitude is
+// mscale(factor, mscale) / mscale(factor, mscale_all_dim).
+RopeTab make_rope_tab(const mla_rope_params &rp, int rope_dim) {
+  RopeTab t;
+  std::memset(&t, 0, sizeof t);
+  const int P = rope_dim / 2;
+  t.pairs = P;
+  t.convention = rp.convention;
+  const double theta = rp.theta;
+  for (int i = 0; i < P; ++i) t.inv_freq[i] = std::pow(theta, -2.0 * i / rope_dim);
+  t.amp = 1.0f;
+  if (rp.factor > 1.0f) {
+    const double f = rp.factor;
+    auto corr = [&](double rot) {
+      return rope_dim * std::log(rp.original_max_position / (rot * 2.0 * M_PI)) /
+             (2.0 * std::log(theta));
+    };
+    double lo = std::floor(corr(rp.beta_fast));
+    double hi = std::ceil(corr(rp.beta_slow));
+    if (lo < 0) lo = 0;
+    if (hi > rope_dim - 1) hi = rope_dim - 1;
+    if (hi == lo) hi += 0.001;
+    for (int i = 0; i < P; ++i) {
+      double ramp = (i - lo) / (hi - lo);
+      ramp = ramp < 0 ? 0 : (ramp > 1 ? 1 : ramp);
+      t.inv_freq[i] = t.inv_freq[i] * (1.0 - ramp) + t.inv_freq[i] / f * ramp;
+    }
+    t.amp = (float)(yarn_mscale(f, rp.mscale) / yarn_mscale(f, rp.mscale_all_dim));
+  }
+  return t;
+}
+
+float resolve_scale(const mla_config &c) {
+  if (c.softmax_scale > 0) return c.softmax_scale;
+  double s = 1.0 / std::sqrt((double)(c.qk_nope_head_dim + c.qk_rope_head_dim));
+  if (c.rope.factor > 1.0f) {
+    double m = yarn_mscale(c.rope.factor, c.rope.mscale_all_dim);
+    s *= m * m;
+  }
+  return (float)s;
+}
+
+bool prefill_instance(const mla_config &c) {
+  const int dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim;
+  return (dn == 16 && dr == 8 && dv == 16) || (dn == 64 && dr == 32 && dv == 64) ||
+         (dn == 128 && dr == 64 && dv == 128);
+}
+
+bool decode_instance(const mla_config &c) {
+  const int r = c.kv_lora_rank, dr = c.qk_rope_head_dim;
+  return (r == 16 && dr == 8) || (r == 128 && dr == 32) || (r == 512 && dr == 64);
+}
+
+mla_status check_config(const mla_config *c) {
+  if (!c) return fail(MLA_ERR_INVALID_ARGUMENT, "config is NULL");
+  const struct {
+    const char *name;
+    int v;
+  } dims[] = {{"hidden_size", c->hidden_size},           {"num_heads", c->num_heads},
+              {"q_lora_rank", c->q_lora_rank},           {"kv_lora_rank", c->kv_lora_rank},
+              {"qk_nope_head_dim", c->qk_nope_head_dim}, {"qk_rope_head_dim", c->qk_rope_head_dim},
+              {"v_head_dim", c->v_head_dim}};
+  for (auto &d : dims) {
+    if (d.v < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "%s = %d must be >= 1", d.name, d.v);
+    if (d.name != std::string("num_heads") && d.v % 8)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "%s = %d must be a multiple of 8", d.name, d.v);
+  }
+  if (c->num_heads > 65535) return fail(MLA_ERR_INVALID_ARGUMENT, "num_heads too large");
+  if (c->dtype != MLA_DTYPE_F32 && c->dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "dtype %d is neither 0 (fp32) nor 1 (bf16)", c->dtype);
+  if (!(c->rms_norm_eps >= 0.0f) || !std::isfinite(c->rms_norm_eps))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "rms_norm_eps must be finite and >= 0");
+  if (!std::isfinite(c->softmax_scale))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  return check_rope(&c->rope, c->qk_rope_head_dim);
+}
+
+mla_status check_weights(const mla_weights *w) {
+  if (!w) return fail(MLA_ERR_INVALID_ARGUMENT, "weights are NULL");
+  const struct {
+    const char *name;
+    const void *p;
+  } ws[] = {{"w_down_q", w->w_down_q},   {"q_norm", w->q_norm}, {"w_up_q", w->w_up_q},
+            {"w_qr", w->w_qr},           {"w_down_kv", w->w_down_kv}, {"w_kr", w->w_kr},
+            {"w_up_k", w->w_up_k},       {"w_up_v", w->w_up_v}, {"wo", w->wo}};
+  for (auto &x : ws) {
+    if (!x.p) return fail(MLA_ERR_INVALID_ARGUMENT, "weight %s is NULL", x.name);
+    if (!aligned16(x.p))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "weight %s is not 16-byte aligned", x.name);
+  }
+  return MLA_OK;
+}
+
+struct PrefillPlan {
+  int64_t ld_down;
+  size_t off_down, off_q, off_kn, off_v, off_o, total;
+};
+
+PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S) {
+  const size_t es = dtype_size(c.dtype);
+  const int64_t M = B * S, H = c.num_heads;
+  PrefillPlan p;
+  p.ld_down = (int64_t)round_up(c.q_lora_rank + c.kv_lora_rank + c.qk_rope_head_dim, 8);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  p.off_down = take((size_t)M * p.ld_down * es);
+  p.off_q = take((size_t)M * H * (c.qk_nope_head_dim + c.qk_rope_head_dim) * es);
+  p.off_kn = take((size_t)M * H * c.qk_nope_head_dim * es);
+  p.off_v = take((size_t)M * H * c.v_head_dim * es);
+  p.off_o = take((size_t)M * H * c.v_head_dim * es);
+  p.total = off;
+  return p;
+}
+
+struct DecodePlan {
+  int64_t ld_down;
+  int n_blocks;
+  size_t off_down, off_qn, off_qlat, off_po, off_pml, off_olat, off_o, total;
+};
+
+DecodePlan plan_decode(const mla_config &c, int64_t B) {
+  const size_t es = dtype_size(c.dtype);
+  const int64_t H = c.num_heads, r = c.kv_lora_rank, dr = c.qk_rope_head_dim;
+  DecodePlan p;
+  p.ld_down = (int64_t)round_up(c.q_lora_rank + r + dr, 8);
+  p.n_blocks = decode_blocks();
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  p.off_down = take((size_t)B * p.ld_down * es);
+  p.off_qn = take((size_t)B * H * c.qk_nope_head_dim * es);
+  p.off_qlat = take((size_t)B * H * (r + dr) * es);
+  p.off_po = take((size_t)(p.n_blocks + B) * H * r * sizeof(float));
+  p.off_pml = take((size_t)(p.n_blocks + B) * H * 2 * sizeof(float));
+  p.off_olat = take((size_t)B * H * r * es);
+  p.off_o = take((size_t)B * H * c.v_head_dim * es);
+  p.total = off;
+  return p;
+}
+
+mla_status check_prefill_sizes(const mla_config *cfg, int64_t B, int64_t S) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (B < 1 || S < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch and seq must be >= 1");
+  if (B > 65535 || S > (1 << 24) || B * S > (1LL << 30))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch %lld x seq %lld is too large", (long long)B,
+                (long long)S);
+  if (!prefill_instance(*cfg))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "head dims (nope %d, rope %d, v %d) are not instantiated; supported: "
+                "(16,8,16), (64,32,64), (128,64,128)",
+                cfg->qk_nope_head_dim, cfg->qk_rope_head_dim, cfg->v_head_dim);
+  return MLA_OK;
+}
+
+mla_status check_decode_sizes(const mla_config *cfg, int64_t B, int64_t cap) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (B < 1 || B > 4096) return fail(MLA_ERR_INVALID_ARGUMENT, "batch must be in [1, 4096]");
+  if (cap < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "cache_capacity must be >= 1");
+  if (B * cap > (1LL << 30))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch x cache_capacity is too large");
+  if (!decode_instance(*cfg))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "(kv_lora_rank %d, rope %d) is not instantiated; supported: (16,8), (128,32), "
+                "(512,64)",
+                cfg->kv_lora_rank, cfg->qk_rope_head_dim);
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_last_error(void) { return g_err.c_str(); }
+
+mla_status mla_set_stage_events(void *const *events, int32_t n_events) {
+  if (n_events < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_events must be >= 0");
+  g_events = (n_events > 0) ? events : nullptr;
+  g_n_events = g_events ? n_events : 0;
+  return MLA_OK;
+}
+
+const char *mla_version(void) { return "mla-mi355x 0.1.0 (gfx950)"; }
+
+float mla_softmax_scale(const mla_config *cfg) {
+  if (!cfg) return 0.f;
+  return resolve_scale(*cfg);
+}
+
+mla_status mla_prefill_workspace_size(const mla_config *cfg, int64_t batch, int64_t seq,
+                                      size_t *bytes) {
+  mla_status s = check_prefill_sizes(cfg, batch, seq);
+  if (s != MLA_OK) return s;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = plan_prefill(*cfg, batch, seq).total;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_layout_of(const mla_config *cfg, int64_t batch, int64_t seq,
+                                 mla_prefill_layout *layout) {
+  mla_status s = check_prefill_sizes(cfg, batch, seq);
+  if (s != MLA_OK) return s;
+  if (!layout) return fail(MLA_ERR_INVALID_ARGUMENT, "layout is NULL");
+  const PrefillPlan p = plan_prefill(*cfg, batch, seq);
+  const size_t es = dtype_size(cfg->dtype);
+  layout->c_q = p.off_down;
+  layout->c_kv = p.off_down + (size_t)cfg->q_lora_rank * es;
+  layout->k_pe = p.off_down + (size_t)(cfg->q_lora_rank + cfg->kv_lora_rank) * es;
+  layout->q = p.off_q;
+  layout->k_nope = p.off_kn;
+  layout->v = p.off_v;
+  layout->o = p.off_o;
+  layout->ld_down = p.ld_down;
+  layout->total = p.total;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, const void *x,
+                               int64_t batch, int64_t seq, void *y, void *latent_out,
+                               void *workspace, size_t workspace_bytes, void *hip_stream) {
+  mla_status s = check_prefill_sizes(cfg, batch, seq);
+  if (s != MLA_OK) return s;
+  if ((s = check_weights(w)) != MLA_OK) return s;
+  if (!x || !y || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "x, y and workspace must not be NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) ||
+      (latent_out && !aligned16(latent_out)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "x, y, latent_out and workspace must be 16-byte aligned");
+  const mla_config &c = *cfg;
+  const PrefillPlan p = plan_prefill(c, batch, seq);
+  if (workspace_bytes < p.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
+                workspace_bytes, p.total);
+
+  hipStream_t st = (hipStream_t)hip_stream;
+  const size_t es = dtype_size(c.dtype);
+  char *ws = (char *)workspace;
+  char *down = ws + p.off_down;
+  char *q = ws + p.off_q;
+  char *kn = ws + p.off_kn;
+  char *v = ws + p.off_v;
+  char *o = ws + p.off_o;
+  const int B = (int)batch, S = (int)seq, M = B * S, H = c.num_heads;
+  const int D = c.hidden_size, rq = c.q_lora_rank, rkv = c.kv_lora_rank;
+  const int dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim;
+  const int dqk = dn + dr;
+  const RopeTab tab = make_rope_tab(c.rope, dr);
+
+  // 1. [c_q ‖ c_kv ‖ k_pe] = x [w_down_q; w_down_kv; w_kr]^T
+  MLA_MARK(0);
+  {
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = M;
+    g.N = rq + rkv + dr;
+    g.K = D;
+    g.A = x;
+    g.lda = D;
+    g.S = M;
+    g.H = 1;
+    g.nseg = 3;
+    g.seg[0] = GemmSeg{w->w_down_q, D, 0, down, rq, p.ld_down, 0};
+    g.seg[1] = GemmSeg{w->w_down_kv, D, rq, down, rkv, p.ld_down, rq};
+    g.seg[2] = GemmSeg{w->w_kr, D, rq + rkv, down, dr, p.ld_down, rq + rkv};
+    MLA_HIP(launch_gemm(g, st), "down projection");
+  }
+  // 2. RMSNorm(c_q)
+  MLA_MARK(1);
+  MLA_HIP(launch_rmsnorm(c.dtype, down, M, p.ld_down, rq, w->q_norm, c.rms_norm_eps, st),
+          "rmsnorm");
+  // 3. RoPE of the shared key at positions 0..S-1
+  MLA_MARK(2);
+  MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, M, S, (int64_t)S * p.ld_down,
+                      p.ld_down, 1, 0, nullptr, tab, st),
+          "rope k_pe");
+  if (latent_out)
+    MLA_HIP(launch_copy_rows(c.dtype, latent_out, rkv + dr, down + (size_t)rq * es, p.ld_down, M,
+                             rkv + dr, st),
+            "latent copy");
+  // 4. q = [q_nope ‖ q_pe] per head, then RoPE of q_pe
+  MLA_MARK(3);
+  {
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = M;
+    g.N = H * dqk;
+    g.K = rq;
+    g.A = down;
+    g.lda = p.ld_down;
+    g.S = S;
+    g.H = H;
+    g.nseg = 2;
+    g.seg[0] = GemmSeg{w->w_up_q, rq, 0, q, dn, dqk, 0};
+    g.seg[1] = GemmSeg{w->w_qr, rq, H * dn, q, dr, dqk, dn};
+    MLA_HIP(launch_gemm(g, st), "q up-projection");
+  }
+  MLA_MARK(4);
+  MLA_HIP(launch_rope(c.dtype, q + (size_t)dn * es, M, S, (int64_t)H * S * dqk, dqk, H,
+                      (int64_t)S * dqk, nullptr, tab, st),
+          "rope q_pe");
+  // 5. k_nope and v per head
+  MLA_MARK(5);
+  {
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = M;
+    g.N = H * (dn + dv);
+    g.K = rkv;
+    g.A = down + (size_t)rq * es;
+    g.lda = p.ld_down;
+    g.S = S;
+    g.H = H;
+    g.nseg = 2;
+    g.seg[0] = GemmSeg{w->w_up_k, rkv, 0, kn, dn, dn, 0};
+    g.seg[1] = GemmSeg{w->w_up_v, rkv, H * dn, v, dv, dv, 0};
+    MLA_HIP(launch_gemm(g, st), "kv up-projection");
+  }
+  // 6. causal attention
+  MLA_MARK(6);
+  {
+    PrefillAttnArgs a;
+    a.q = q;
+    a.k_nope = kn;
+    a.k_pe = down + (size_t)(rq + rkv) * es;
+    a.ld_kpe = p.ld_down;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.S = S;
+    a.H = H;
+    a.scale = resolve_scale(c);
+    MLA_HIP(launch_prefill_attention(c.dtype, dn, dr, dv, a, st), "attention");
+  }
+  // 7. y = o wo^T
+  MLA_MARK(7);
+  {
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = M;
+    g.N = D;
+    g.K = H * dv;
+    g.A = o;
+    g.lda = (int64_t)H * dv;
+    g.S = M;
+    g.H = 1;
+    g.nseg = 1;
+    g.seg[0] = GemmSeg{w->wo, (int64_t)H * dv, 0, y, D, D, 0};
+    MLA_HIP(launch_gemm(g, st), "output projection");
+  }
+  MLA_MARK(8);
+  return MLA_OK;
+}
+
+mla_status mla_decode_workspace_size(const mla_config *cfg, int64_t batch, int64_t cache_capacity,
+                                     size_t *bytes) {
+  mla_status s = check_decode_sizes(cfg, batch, cache_capacity);
+  if (s != MLA_OK) return s;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = plan_decode(*cfg, batch).total;
+  return MLA_OK;
+}
+
+mla_status mla_decode_layout_of(const mla_config *cfg, int64_t batch, int64_t cache_capacity,
+                                mla_decode_layout *layout) {
+  mla_status s = check_decode_sizes(cfg, batch, cache_capacity);
+  if (s != MLA_OK) return s;
+  if (!layout) return fail(MLA_ERR_INVALID_ARGUMENT, "layout is NULL");
+  const DecodePlan p = plan_decode(*cfg, batch);
+  layout->c_q = p.off_down;
+  layout->c_kv = p.off_down + (size_t)cfg->q_lora_rank * dtype_size(cfg->dtype);
+  layout->q = p.off_qn;
+  layout->q_lat = p.off_qlat;
+  layout->o_lat = p.off_olat;
+  layout->o = p.off_o;
+  layout->ld_down = p.ld_down;
+  layout->n_splits = p.n_blocks;
+  layout->split_len = 0;
+  layout->total = p.total;
+  return MLA_OK;
+}
+
+mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, const void *x,
+                               int64_t batch, void *latent_cache, int64_t cache_capacity,
+                               const int32_t *cache_lens, void *y, void *workspace,
+                               size_t workspace_bytes, void *hip_stream) {
+  mla_status s = check_decode_sizes(cfg, batch, cache_capacity);
+  if (s != MLA_OK) return s;
+  if ((s = check_weights(w)) != MLA_OK) return s;
+  if (!x || !y || !workspace || !latent_cache || !cache_lens)
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "x, latent_cache, cache_lens, y and workspace must not be NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || !aligned16(latent_cache))
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "x, y, latent_cache and workspace must be 16-byte aligned");
+  const mla_config &c = *cfg;
+  const DecodePlan p = plan_decode(c, batch);
+  if (workspace_bytes < p.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
+                workspace_bytes, p.total);
+
+  hipStream_t st = (hipStream_t)hip_stream;
+  const size_t es = dtype_size(c.dtype);
+  char *ws = (char *)workspace;
+  char *down = ws + p.off_down;
+  char *qn = ws + p.off_qn;
+  char *qlat = ws + p.off_qlat;
+  char *olat = ws + p.off_olat;
+  char *o = ws + p.off_o;
+  const int B = (int)batch, H = c.num_heads;
+  const int D = c.hidden_size, rq = c.q_lora_rank, rkv = c.kv_lora_rank;
+  const int dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim;
+  const int wl = rkv + dr;  // latent row width
+  const RopeTab tab = make_rope_tab(c.rope, dr);
+
+  // 1. down projections of the new tokens
+  MLA_MARK(0);
+  {
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = B;
+    g.N = rq + rkv + dr;
+    g.K = D;
+    g.A = x;
+    g.lda = D;
+    g.S = B;
+    g.H = 1;
+    g.nseg = 3;
+    g.seg[0] = GemmSeg{w->w_down_q, D, 0, down, rq, p.ld_down, 0};
+    g.seg[1] = GemmSeg{w->w_down_kv, D, rq, down, rkv, p.ld_down, rq};
+    g.seg[2] = GemmSeg{w->w_kr, D, rq + rkv, down, dr, p.ld_down, rq + rkv};
+    MLA_HIP(launch_gemm(g, st), "decode down projection");
+  }
+  MLA_MARK(1);
+  MLA_HIP(launch_rmsnorm(c.dtype, down, B, p.ld_down, rq, w->q_norm, c.rms_norm_eps, st),
+          "decode rmsnorm");
+  // 2. RoPE of the new key at position lens[b], then append [c_kv ‖ k_pe] at row lens[b]
+  MLA_MARK(2);
+  MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, B, B, 0, p.ld_down, 1, 0,
+                      cache_lens, tab, st),
+          "decode rope k_pe");
+  MLA_HIP(launch_cache_append(c.dtype, latent_cache, cache_capacity, cache_lens,
+                              down + (size_t)rq * es, p.ld_down, B, wl, st),
+          "cache append");
+  // 3. q_nope per head, q_pe straight into the absorbed query rows, RoPE of q_pe
+  MLA_MARK(3);
+  {
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = B;
+    g.N = H * (dn + dr);
+    g.K = rq;
+    g.A = down;
+    g.lda = p.ld_down;
+    g.S = 1;
+    g.H = H;
+    g.nseg = 2;
+    g.seg[0] = GemmSeg{w->w_up_q, rq, 0, qn, dn, dn, 0};
+    g.seg[1] = GemmSeg{w->w_qr, rq, H * dn, qlat, dr, wl, rkv};
+    MLA_HIP(launch_gemm(g, st), "decode q up-projection");
+  }
+  MLA_MARK(4);
+  MLA_HIP(launch_rope(c.dtype, qlat + (size_t)rkv * es, B, B, 0, (int64_t)H * wl, H, wl,
+                      cache_lens, tab, st),
+          "decode rope q_pe");
+  // 4. absorb: q_lat[b, h] = w_up_k_h^T q_nope[b, h]   (batched over heads)
+  MLA_MARK(5);
+  {
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = B;
+    g.N = rkv;
+    g.K = dn;
+    g.batch = H;
+    g.A = qn;
+    g.lda = (int64_t)H * dn;
+    g.strideA = dn;
+    g.b_kn = true;
+    g.strideB = (int64_t)dn * rkv;
+    g.strideC = wl;
+    g.S = B;
+    g.H = 1;
+    g.nseg = 1;
+    g.seg[0] = GemmSeg{w->w_up_k, rkv, 0, qlat, rkv, (int64_t)H * wl, 0};
+    MLA_HIP(launch_gemm(g, st), "absorb");
+  }
+  // 5. latent attention over rows 0..lens[b], split evenly over workgroups, merged
+  MLA_MARK(6);
+  {
+    DecodeAttnArgs a;
+    a.q_lat = qlat;
+    a.cache = latent_cache;
+    a.lens = cache_lens;
+    a.o_lat = olat;
+    a.part_o = (float *)(ws + p.off_po);
+    a.part_ml = (float *)(ws + p.off_pml);
+    a.cap = cache_capacity;
+    a.B = B;
+    a.H = H;
+    a.n_blocks = p.n_blocks;
+    a.scale = resolve_scale(c);
+    MLA_HIP(launch_decode_attention(c.dtype, rkv, dr, a, st), "decode attention");
+    MLA_MARK(7);
+    MLA_HIP(launch_decode_merge(c.dtype, rkv, a, st), "decode merge");
+  }
+  // 6. un-absorb: o[b, h] = w_up_v_h o_lat[b, h]   (batched over heads)
+  MLA_MARK(8);
+  {
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = B;
+    g.N = dv;
+    g.K = rkv;
+    g.batch = H;
+    g.A = olat;
+    g.lda = (int64_t)H * rkv;
+    g.strideA = rkv;
+    g.strideB = (int64_t)dv * rkv;
+    g.strideC = dv;
+    g.S = B;
+    g.H = 1;
+    g.nseg = 1;
+    g.seg[0] = GemmSeg{w->w_up_v, rkv, 0, o, dv, (int64_t)H * dv, 0};
+    MLA_HIP(launch_gemm(g, st), "un-absorb");
+  }
+  // 7. y = o wo^T
+  MLA_MARK(9);
+  {
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = B;
+    g.N = D;
+    g.K = H * dv;
+    g.A = o;
+    g.lda = (int64_t)H * dv;
+    g.S = B;
+    g.H = 1;
+    g.nseg = 1;
+    g.seg[0] = GemmSeg{w->wo, (int64_t)H * dv, 0, y, D, D, 0};
+    MLA_HIP(launch_gemm(g, st), "decode output projection");
+  }
+  MLA_MARK(10);
+  return MLA_OK;
+}
+
+mla_status mla_rope_apply(void *x, int32_t dtype, int64_t n_tokens, int32_t n_heads,
+                          int32_t rope_dim, int64_t token_stride, int64_t head_stride,
+                          const int32_t *positions, const mla_rope_params *params,
+                          void *hip_stream) {
+  if (!x) return fail(MLA_ERR_INVALID_ARGUMENT, "x is NULL");
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "dtype %d is neither 0 (fp32) nor 1 (bf16)", dtype);
+  if (n_tokens < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "n_tokens must be >= 0");
+  if (n_heads < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "n_heads must be >= 1");
+  mla_status s = check_rope(params, rope_dim);
+  if (s != MLA_OK) return s;
+  if (!positions && n_tokens > 0) return fail(MLA_ERR_INVALID_ARGUMENT, "positions is NULL");
+  if (((uintptr_t)x) % dtype_size(dtype))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "x is not aligned to its element size");
+  const RopeTab tab = make_rope_tab(*params, rope_dim);
+  MLA_HIP(launch_rope(dtype, x, n_tokens, n_tokens > 0 ? n_tokens : 1, 0, token_stride, n_heads,
+                      head_stride, positions, tab, (hipStream_t)hip_stream),
+          "rope");
+  return MLA_OK;
+}
+
+}  // extern "C"

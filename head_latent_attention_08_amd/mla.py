@@ -1,0 +1,302 @@
+"""ctypes binding of libmla.so: argument marshalling only.
+
+Every step of the forward runs in the library's HIP kernels; PyTorch only
+provides device memory and the current stream.  There is no fallback: if the
+library is not built, or no GPU is present, the calls raise.
+
+Names match the C ABI in include/mla.h.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch  # noqa: F401  (loads the HIP runtime the library links against)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE_TOO_SMALL = 3
+MLA_ERR_HIP = 4
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+ROPE_HALF_SPLIT = 0
+ROPE_INTERLEAVED = 1
+
+_TORCH_DTYPE = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"mla status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class RopeParams(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_float), ("convention", ctypes.c_int32),
+                ("factor", ctypes.c_float), ("original_max_position", ctypes.c_int32),
+                ("beta_fast", ctypes.c_float), ("beta_slow", ctypes.c_float),
+                ("mscale", ctypes.c_float), ("mscale_all_dim", ctypes.c_float)]
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("hidden_size", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("q_lora_rank", ctypes.c_int32), ("kv_lora_rank", ctypes.c_int32),
+                ("qk_nope_head_dim", ctypes.c_int32), ("qk_rope_head_dim", ctypes.c_int32),
+                ("v_head_dim", ctypes.c_int32), ("rms_norm_eps", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float), ("rope", RopeParams),
+                ("dtype", ctypes.c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_down_q", "q_norm", "w_up_q", "w_qr", "w_down_kv", "w_kr", "w_up_k", "w_up_v", "wo")]
+
+
+class PrefillLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("c_q", "c_kv", "k_pe", "q", "k_nope", "v", "o")] + [
+        ("ld_down", ctypes.c_int64), ("total", ctypes.c_size_t)]
+
+
+class DecodeLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("c_q", "c_kv", "q", "q_lat", "o_lat", "o")] + [
+        ("ld_down", ctypes.c_int64), ("n_splits", ctypes.c_int64), ("split_len", ctypes.c_int64),
+        ("total", ctypes.c_size_t)]
+
+
+WEIGHT_NAMES = [f[0] for f in Weights._fields_]
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m head_latent_attention_08_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    st = ctypes.c_int
+    lib.mla_prefill_workspace_size.argtypes = [ctypes.POINTER(Config), i64, i64,
+                                               ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_prefill_layout_of.argtypes = [ctypes.POINTER(Config), i64, i64,
+                                          ctypes.POINTER(PrefillLayout)]
+    lib.mla_prefill_forward.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P, i64,
+                                        i64, P, P, P, ctypes.c_size_t, P]
+    lib.mla_decode_workspace_size.argtypes = [ctypes.POINTER(Config), i64, i64,
+                                              ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_decode_layout_of.argtypes = [ctypes.POINTER(Config), i64, i64,
+                                         ctypes.POINTER(DecodeLayout)]
+    lib.mla_decode_absorbed.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P, i64,
+                                        P, i64, P, P, P, ctypes.c_size_t, P]
+    lib.mla_rope_apply.argtypes = [P, ctypes.c_int32, i64, ctypes.c_int32, ctypes.c_int32, i64,
+                                   i64, P, ctypes.POINTER(RopeParams), P]
+    for fn in ("mla_prefill_workspace_size", "mla_prefill_layout_of", "mla_prefill_forward",
+               "mla_decode_workspace_size", "mla_decode_layout_of", "mla_decode_absorbed",
+               "mla_rope_apply"):
+        getattr(lib, fn).restype = st
+    lib.mla_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+    lib.mla_set_stage_events.restype = st
+    lib.mla_softmax_scale.argtypes = [ctypes.POINTER(Config)]
+    lib.mla_softmax_scale.restype = ctypes.c_float
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        raise MlaError(status, load_library().mla_last_error().decode())
+
+
+@dataclass
+class MlaConfig:
+    """Python mirror of mla_config (DeepSeek-V3 field names)."""
+
+    hidden_size: int
+    num_heads: int
+    q_lora_rank: int
+    kv_lora_rank: int
+    qk_nope_head_dim: int
+    qk_rope_head_dim: int
+    v_head_dim: int
+    rms_norm_eps: float = 1e-6
+    softmax_scale: float = 0.0
+    rope_theta: float = 10000.0
+    rope_convention: int = ROPE_HALF_SPLIT
+    rope_factor: float = 1.0
+    original_max_position: int = 4096
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+    mscale: float = 1.0
+    mscale_all_dim: float = 1.0
+    dtype: int = DTYPE_BF16
+
+    def rope_params(self) -> RopeParams:
+        return RopeParams(self.rope_theta, self.rope_convention, self.rope_factor,
+                          self.original_max_position, self.beta_fast, self.beta_slow,
+                          self.mscale, self.mscale_all_dim)
+
+    def c(self) -> Config:
+        return Config(self.hidden_size, self.num_heads, self.q_lora_rank, self.kv_lora_rank,
+                      self.qk_nope_head_dim, self.qk_rope_head_dim, self.v_head_dim,
+                      self.rms_norm_eps, self.softmax_scale, self.rope_params(), self.dtype)
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPE[self.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_weights(w: dict) -> Weights:
+    for n in WEIGHT_NAMES:
+        t = w[n]
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"weight {n} must be a contiguous device tensor")
+    return Weights(*[w[n].data_ptr() for n in WEIGHT_NAMES])
+
+
+def mla_softmax_scale(cfg: MlaConfig) -> float:
+    c = cfg.c()
+    return float(load_library().mla_softmax_scale(ctypes.byref(c)))
+
+
+def mla_version() -> str:
+    return load_library().mla_version().decode()
+
+
+PREFILL_STAGES = ("down_proj", "rmsnorm", "rope_k", "q_up_proj", "rope_q", "kv_up_proj",
+                  "attention", "out_proj")
+DECODE_STAGES = ("down_proj", "rmsnorm", "rope_k_append", "q_up_proj", "rope_q", "absorb",
+                 "latent_attention", "split_merge", "unabsorb", "out_proj")
+
+
+def mla_set_stage_events(events) -> None:
+    """Record the given hipEvent_t handles (ints) at stage boundaries of the
+    next prefill/decode calls on this thread; None switches it off."""
+    lib = load_library()
+    if not events:
+        _check(lib.mla_set_stage_events(None, 0))
+        mla_set_stage_events._keep = None
+        return
+    arr = (ctypes.c_void_p * len(events))(*events)
+    mla_set_stage_events._keep = arr  # the library keeps the pointer
+    _check(lib.mla_set_stage_events(arr, len(events)))
+
+
+def mla_prefill_workspace_size(cfg: MlaConfig, batch: int, seq: int) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().mla_prefill_workspace_size(ctypes.byref(c), batch, seq, ctypes.byref(n)))
+    return n.value
+
+
+def mla_prefill_layout_of(cfg: MlaConfig, batch: int, seq: int) -> PrefillLayout:
+    lay = PrefillLayout()
+    c = cfg.c()
+    _check(load_library().mla_prefill_layout_of(ctypes.byref(c), batch, seq, ctypes.byref(lay)))
+    return lay
+
+
+def mla_decode_workspace_size(cfg: MlaConfig, batch: int, capacity: int) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().mla_decode_workspace_size(ctypes.byref(c), batch, capacity,
+                                                    ctypes.byref(n)))
+    return n.value
+
+
+def mla_decode_layout_of(cfg: MlaConfig, batch: int, capacity: int) -> DecodeLayout:
+    lay = DecodeLayout()
+    c = cfg.c()
+    _check(load_library().mla_decode_layout_of(ctypes.byref(c), batch, capacity,
+                                               ctypes.byref(lay)))
+    return lay
+
+
+def _device_check(*ts):
+    for t in ts:
+        if t is not None and not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def mla_prefill_forward(cfg: MlaConfig, weights: dict, x: torch.Tensor, y=None, latent_out=None,
+                        workspace=None, stream=None, want_latent: bool = False):
+    """y = MLA prefill of x [B, S, D].  Returns (y, latent_out, workspace)."""
+    B, S, D = x.shape
+    dev = x.device
+    if y is None:
+        y = torch.empty((B, S, D), dtype=cfg.torch_dtype, device=dev)
+    if latent_out is None and want_latent:
+        latent_out = torch.empty((B, S, cfg.kv_lora_rank + cfg.qk_rope_head_dim),
+                                 dtype=cfg.torch_dtype, device=dev)
+    need = mla_prefill_workspace_size(cfg, B, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _device_check(x, y, latent_out, workspace)
+    w = make_weights(weights)
+    c = cfg.c()
+    _check(load_library().mla_prefill_forward(
+        ctypes.byref(c), ctypes.byref(w), _ptr(x), B, S, _ptr(y), _ptr(latent_out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y, latent_out, workspace
+
+
+def mla_decode_absorbed(cfg: MlaConfig, weights: dict, x: torch.Tensor, latent_cache: torch.Tensor,
+                        cache_lens: torch.Tensor, y=None, workspace=None, stream=None):
+    """One absorbed decode step for x [B, D]; writes row lens[b] of the cache.
+    Returns (y, workspace)."""
+    B, D = x.shape
+    cap = latent_cache.shape[1]
+    dev = x.device
+    if y is None:
+        y = torch.empty((B, D), dtype=cfg.torch_dtype, device=dev)
+    need = mla_decode_workspace_size(cfg, B, cap)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if cache_lens.dtype != torch.int32:
+        raise ValueError("cache_lens must be int32")
+    _device_check(x, y, latent_cache, cache_lens, workspace)
+    w = make_weights(weights)
+    c = cfg.c()
+    _check(load_library().mla_decode_absorbed(
+        ctypes.byref(c), ctypes.byref(w), _ptr(x), B, _ptr(latent_cache), cap, _ptr(cache_lens),
+        _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y, workspace
+
+
+def mla_rope_apply(x: torch.Tensor, positions: torch.Tensor, params: RopeParams, stream=None):
+    """In-place RoPE of x [n_tokens, n_heads, rope_dim] (any strides, unit
+    stride on the last axis) at positions [n_tokens] int32."""
+    if x.dim() != 3 or x.stride(-1) != 1:
+        raise ValueError("x must be [n_tokens, n_heads, rope_dim] with unit last stride")
+    if positions.dtype != torch.int32 or not positions.is_cuda:
+        raise ValueError("positions must be a device int32 tensor")
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[x.dtype]
+    n, h, d = x.shape
+    _check(load_library().mla_rope_apply(
+        _ptr(x), dt, n, h, d, x.stride(0), x.stride(1), _ptr(positions), ctypes.byref(params),
+        _stream(stream)))
+    return x

@@ -1,0 +1,219 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) Multi-head Latent Attention forward.
+ *
+ * The operation is the DeepSeek-V3 MLA forward as the pages state it:
+ *   "The Evolving Transformer -- DeepSeek V2 & V3", section 01 "Multi-head
+ *   Latent Attention (MLA)": module MultiHeadLatentAttention (projections
+ *   w_down_kv, w_up_k, w_up_v, w_kr, w_down_q, w_up_q, w_qr, wo; K = cat(K_nope,
+ *   K_rope), Q = cat(Q_nope, Q_rope), V from the nope width; causal softmax
+ *   attention scaled by 1/sqrt(dk); heads concatenated head-major; then wo) and
+ *   the cache formula below it (c_kv is what gets cached).
+ *   "DeepSeek-V3 Decoupled Implementation" README, "Architecture" list and
+ *   "Key Dimensions (671B variant)" table: field names and V3 sizes, 512-dim
+ *   latent, decoupled 64-dim RoPE stream, YaRN factor 40.
+ *   "[DeepSeek-V3] Different rotary embedding implementation between
+ *   DeepSeek-AI and Transformers": the two RoPE conventions.
+ *
+ * Where the pages are silent this library reads them as follows:
+ *   - RMSNorm(c_q) = c_q * (mean(c_q^2) + eps)^-1/2 * q_norm, before both
+ *     w_up_q and w_qr; there is no norm on c_kv.
+ *   - k_pe = w_kr x is ONE shared rope_dim vector per token (w_kr is
+ *     [rope_dim, hidden]), broadcast to every head.
+ *   - softmax scale = (nope + rope)^-1/2, times mscale(factor,
+ *     mscale_all_dim)^2 under YaRN; the same scale in decode.
+ *   - RoPE pair i turns by +pos * inv_freq_i, inv_freq_i = theta^(-2i/d),
+ *     positions start at 0, angles are reduced in float64.
+ *   - decode: the new token's position is cache_lens[b]; it attends to cache
+ *     rows 0..cache_lens[b], itself included.
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller allocates and owns every buffer.  The library never
+ *     allocates device memory, never frees, and keeps no pointer past the call.
+ *     Scratch comes from the caller's workspace, sized by *_workspace_size.
+ *   - Asynchrony: work is enqueued on `hip_stream` (a hipStream_t; NULL = the
+ *     null stream) and the call returns after the launches, with no host
+ *     synchronisation.  Buffers must stay alive until the stream reaches the
+ *     work.  Calls that run concurrently must not share a workspace.
+ *   - Layout: row-major, C order.  Weights are nn.Linear matrices [out][in]
+ *     (y = x W^T, no bias).  Every float tensor of one call has the dtype of
+ *     cfg->dtype (fp32 or bf16); accumulation is always fp32.
+ *   - Errors: arguments are validated before anything is launched; a failing
+ *     call returns a status != MLA_OK, launches nothing, and leaves a message
+ *     for mla_last_error().  The library never aborts the process.
+ */
+#ifndef MLA_MI355X_H
+#define MLA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define MLA_API __attribute__((visibility("default")))
+#else
+#define MLA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, bad size, bad enum value   */
+  MLA_ERR_UNSUPPORTED = 2,        /* head-dim combination not instantiated    */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,/* workspace_bytes below *_workspace_size   */
+  MLA_ERR_HIP = 4                 /* a HIP launch failed (message has details)*/
+} mla_status;
+
+typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
+
+typedef enum {
+  /* pairs (i, i + d/2): the rotate-half ("Eleuther") formulation */
+  MLA_ROPE_HALF_SPLIT = 0,
+  /* pairs (2i, 2i + 1): the complex formulation of the DeepSeek-AI code;
+   * the output keeps the interleaved layout */
+  MLA_ROPE_INTERLEAVED = 1
+} mla_rope_convention;
+
+typedef struct {
+  float theta;                    /* base, e.g. 10000                          */
+  int32_t convention;             /* mla_rope_convention                       */
+  float factor;                   /* YaRN scaling factor; 1 = plain RoPE       */
+  int32_t original_max_position;  /* YaRN original context (4096 for V3)       */
+  float beta_fast, beta_slow;     /* YaRN correction bounds (32, 1)            */
+  float mscale, mscale_all_dim;   /* YaRN attention temperature terms (1, 1)   */
+} mla_rope_params;
+
+typedef struct {                  /* DeepSeek-V3 config field names            */
+  int32_t hidden_size;            /* D   (7168 for V3)                         */
+  int32_t num_heads;              /* H   (128)                                 */
+  int32_t q_lora_rank;            /* r_q (1536)                                */
+  int32_t kv_lora_rank;           /* r_kv (512)                                */
+  int32_t qk_nope_head_dim;       /* d_n (128)                                 */
+  int32_t qk_rope_head_dim;       /* d_r (64)                                  */
+  int32_t v_head_dim;             /* d_v (128)                                 */
+  float rms_norm_eps;             /* 1e-6                                      */
+  float softmax_scale;            /* <= 0: default (see above)                 */
+  mla_rope_params rope;
+  int32_t dtype;                  /* mla_dtype of every float tensor           */
+} mla_config;
+
+typedef struct {                  /* device pointers, nn.Linear [out][in]      */
+  const void *w_down_q;           /* [r_q, D]                                  */
+  const void *q_norm;             /* [r_q]   RMSNorm gain                      */
+  const void *w_up_q;             /* [H*d_n, r_q]                              */
+  const void *w_qr;               /* [H*d_r, r_q]                              */
+  const void *w_down_kv;          /* [r_kv, D]                                 */
+  const void *w_kr;               /* [d_r, D]   shared RoPE key              */
+  const void *w_up_k;             /* [H*d_n, r_kv]                             */
+  const void *w_up_v;             /* [H*d_v, r_kv]                             */
+  const void *wo;                 /* [D, H*d_v]                                */
+} mla_weights;
+
+/* Byte offsets, inside the workspace, of the intermediates a prefill leaves
+ * there (all in cfg->dtype, valid once the stream has run the call):
+ *   c_q   [B*S, r_q]           c_q = x w_down_q^T, then RMS-normalised in place
+ *   c_kv  [B*S, r_kv]          latent;  k_pe [B*S, d_r] post-RoPE
+ *   q     [B, H, S, d_n+d_r]   q_nope ‖ post-RoPE q_pe per head
+ *   k_nope[B, H, S, d_n]       v [B, H, S, d_v]
+ *   o     [B*S, H*d_v]         attention output, head-major columns
+ * Row strides: c_q, c_kv and k_pe share one row of ld_down elements
+ * (c_q at column 0, c_kv at r_q, k_pe at r_q + r_kv). */
+typedef struct {
+  size_t c_q, c_kv, k_pe, q, k_nope, v, o;
+  int64_t ld_down;
+  size_t total;
+} mla_prefill_layout;
+
+/* ------------------------------------------------------------------ prefill
+ * y = MLA(x) for x [B, S, D] at positions 0..S-1 with the causal mask.
+ *   x          [B, S, D]             device, read
+ *   y          [B, S, D]             device, written
+ *   latent_out [B, S, r_kv + d_r]    device, written if not NULL: per token
+ *              c_kv then the post-RoPE k_pe (the latent-cache row format)
+ * Status: INVALID_ARGUMENT for NULL x/y/weights/workspace, B or S < 1, a
+ * dimension < 1 or not a multiple of 8 (d_r: of 2, <= 128); UNSUPPORTED for a
+ * (d_n, d_r, d_v) other than (16,8,16), (64,32,64), (128,64,128);
+ * WORKSPACE_TOO_SMALL; HIP. */
+MLA_API mla_status mla_prefill_workspace_size(const mla_config *cfg, int64_t batch,
+                                      int64_t seq, size_t *bytes);
+MLA_API mla_status mla_prefill_layout_of(const mla_config *cfg, int64_t batch,
+                                 int64_t seq, mla_prefill_layout *layout);
+MLA_API mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w,
+                               const void *x, int64_t batch, int64_t seq,
+                               void *y, void *latent_out, void *workspace,
+                               size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------------- decode
+ * One absorbed decode step (the cache formula of the MLA section, with
+ * w_up_k folded into the query side and w_up_v into the output side, per
+ * head, at run time):
+ *   q_lat_h = w_up_k_h^T q_nope_h ; s_t = scale (q_lat_h . c_kv_t + q_pe_h . k_pe_t)
+ *   o_lat_h = sum_t softmax(s)_t c_kv_t ; o_h = w_up_v_h o_lat_h ; y = wo o
+ *   x            [B, D]                    device, one new token per sequence
+ *   latent_cache [B, capacity, r_kv + d_r] device; rows [0, lens[b]) are read,
+ *                row lens[b] is written with the new token's c_kv ‖ k_pe
+ *   cache_lens   [B] int32                 device, read only (the caller
+ *                advances it); 0 <= lens[b] < capacity is a device-side
+ *                precondition: a sequence that violates it gets a NaN y row
+ *                and no cache write.
+ *   y            [B, D]                    device, written
+ * Status: as prefill; also INVALID_ARGUMENT for capacity < 1. */
+typedef struct {
+  size_t c_q, c_kv, q, q_lat, o_lat, o;   /* see mla_decode_layout_of */
+  int64_t ld_down, n_splits, split_len;
+  size_t total;
+} mla_decode_layout;
+
+MLA_API mla_status mla_decode_workspace_size(const mla_config *cfg, int64_t batch,
+                                     int64_t cache_capacity, size_t *bytes);
+MLA_API mla_status mla_decode_layout_of(const mla_config *cfg, int64_t batch,
+                                int64_t cache_capacity,
+                                mla_decode_layout *layout);
+MLA_API mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w,
+                               const void *x, int64_t batch,
+                               void *latent_cache, int64_t cache_capacity,
+                               const int32_t *cache_lens, void *y,
+                               void *workspace, size_t workspace_bytes,
+                               void *hip_stream);
+
+/* --------------------------------------------------------------------- RoPE
+ * In-place RoPE of x[t, h, 0..rope_dim) at positions[t] (device int32 [n_tokens]),
+ * element (t, h, i) at x + t*token_stride + h*head_stride + i (strides in
+ * elements).  Convention, theta and YaRN from *params (host struct).
+ * Status: INVALID_ARGUMENT for NULL x/positions/params, n_tokens < 0,
+ * n_heads < 1, rope_dim odd, < 2 or > 128, bad dtype or convention. */
+MLA_API mla_status mla_rope_apply(void *x, int32_t dtype, int64_t n_tokens,
+                          int32_t n_heads, int32_t rope_dim,
+                          int64_t token_stride, int64_t head_stride,
+                          const int32_t *positions,
+                          const mla_rope_params *params, void *hip_stream);
+
+/* ---------------------------------------------------------- measurement
+ * While set, every mla_prefill_forward / mla_decode_absorbed call made on
+ * this thread records events[k] (hipEvent_t handles the caller created) on
+ * the call's stream just before it launches stage k, and events[n_stages]
+ * after its last launch, for every index < n_events.  Stage order:
+ *   prefill: 0 down projections, 1 RMSNorm, 2 k_pe RoPE (+ latent copy),
+ *            3 q up-projection, 4 q_pe RoPE, 5 kv up-projection,
+ *            6 attention, 7 output projection            (9 events)
+ *   decode:  0 down projections, 1 RMSNorm, 2 k_pe RoPE + cache append,
+ *            3 q up-projection, 4 q_pe RoPE, 5 absorption, 6 latent
+ *            attention, 7 split merge, 8 un-absorption, 9 output projection
+ *                                                         (11 events)
+ * events = NULL (or n_events = 0) switches it off.  The library keeps the
+ * pointer array until then; the caller keeps it alive.  A failing
+ * hipEventRecord makes the call return MLA_ERR_HIP. */
+MLA_API mla_status mla_set_stage_events(void *const *events, int32_t n_events);
+
+/* Softmax scale the library uses for *cfg (resolves softmax_scale <= 0). */
+MLA_API float mla_softmax_scale(const mla_config *cfg);
+
+/* Message of the last failing call on this thread ("" if none). */
+MLA_API const char *mla_last_error(void);
+MLA_API const char *mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_MI355X_H */

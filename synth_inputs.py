@@ -56,11 +56,16 @@ CONFIGS = {
 
 def round_bf16(a) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); the result is
-    float32 holding bf16-representable values."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    float32 holding bf16-representable values.  Finite inputs only (the
+    uint32 sum cannot overflow below the NaN bit patterns)."""
+    a = np.array(a, dtype=np.float32, copy=True, order="C")
+    u = a.view(np.uint32)
+    lsb = u >> 16
+    lsb &= 1
+    lsb += 0x7FFF
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return a
 
 
 def bf16_bits(a) -> np.ndarray:

@@ -1,0 +1,156 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point include/mla.h declares, sizes workspaces, and rejects bad arguments
+with a status and a message before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_latent_attention_08_amd as m
+from head_latent_attention_08_amd import mla as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+V3 = dict(hidden_size=7168, num_heads=128, q_lora_rank=1536, kv_lora_rank=512,
+          qk_nope_head_dim=128, qk_rope_head_dim=64, v_head_dim=128)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MLA_API\s+[\w\s\*]*?\b(mla_\w+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for n in ("mla_prefill_forward", "mla_decode_absorbed", "mla_rope_apply",
+              "mla_prefill_workspace_size", "mla_decode_workspace_size", "mla_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m.load_library()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    # and the exported dynamic symbols are exactly those
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = sorted(set(re.findall(r"\bT (mla_\w+)", out)))
+    assert exported == _declared()
+
+
+def test_version_and_scale():
+    assert "gfx950" in m.mla_version()
+    assert m.mla_softmax_scale(m.MlaConfig(**V3)) == pytest.approx(192 ** -0.5, rel=1e-7)
+    yarn = m.MlaConfig(**V3, rope_factor=40.0)
+    assert m.mla_softmax_scale(yarn) == pytest.approx(0.135234, abs=1e-6)
+    assert m.mla_softmax_scale(m.MlaConfig(**V3, softmax_scale=0.5)) == 0.5
+
+
+def test_workspace_sizes():
+    cfg = m.MlaConfig(**V3)
+    n = m.mla_prefill_workspace_size(cfg, 1, 4096)
+    lay = m.mla_prefill_layout_of(cfg, 1, 4096)
+    assert lay.total == n
+    # q, k_nope, v and o dominate: 4096 tokens x 128 heads x (192+128+128+128) x 2 B
+    assert n >= 4096 * 128 * 576 * 2
+    offs = [lay.c_q, lay.q, lay.k_nope, lay.v, lay.o]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.c_kv == lay.c_q + 1536 * 2 and lay.k_pe == lay.c_kv + 512 * 2
+    d = m.mla_decode_workspace_size(cfg, 64, 8193)
+    dl = m.mla_decode_layout_of(cfg, 64, 8193)
+    assert dl.total == d and dl.n_splits >= 1
+    assert m.mla_prefill_workspace_size(m.MlaConfig(**V3, dtype=m.DTYPE_F32), 1, 4096) > n
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hidden_size", 0, b.MLA_ERR_INVALID_ARGUMENT),
+    ("hidden_size", 7170, b.MLA_ERR_INVALID_ARGUMENT),
+    ("num_heads", -1, b.MLA_ERR_INVALID_ARGUMENT),
+    ("qk_nope_head_dim", 96, b.MLA_ERR_UNSUPPORTED),
+    ("v_head_dim", 64, b.MLA_ERR_UNSUPPORTED),
+    ("qk_rope_head_dim", 60, b.MLA_ERR_INVALID_ARGUMENT),
+    ("dtype", 7, b.MLA_ERR_INVALID_ARGUMENT),
+    ("rope_convention", 2, b.MLA_ERR_INVALID_ARGUMENT),
+    ("rope_factor", 0.5, b.MLA_ERR_INVALID_ARGUMENT),
+    ("rope_theta", -3.0, b.MLA_ERR_INVALID_ARGUMENT),
+    ("rms_norm_eps", -1.0, b.MLA_ERR_INVALID_ARGUMENT),
+])
+def test_bad_config_rejected(field, value, status):
+    kw = dict(V3)
+    kw[field] = value
+    with pytest.raises(m.MlaError) as e:
+        m.mla_prefill_workspace_size(m.MlaConfig(**kw), 1, 16)
+    assert e.value.status == status
+    assert e.value.message
+
+
+def test_bad_sizes_rejected():
+    cfg = m.MlaConfig(**V3)
+    for B, S in [(0, 16), (1, 0), (-1, 4)]:
+        with pytest.raises(m.MlaError) as e:
+            m.mla_prefill_workspace_size(cfg, B, S)
+        assert e.value.status == b.MLA_ERR_INVALID_ARGUMENT
+    with pytest.raises(m.MlaError) as e:
+        m.mla_decode_workspace_size(cfg, 64, 0)
+    assert e.value.status == b.MLA_ERR_INVALID_ARGUMENT
+    with pytest.raises(m.MlaError) as e:
+        m.mla_decode_workspace_size(m.MlaConfig(**dict(V3, kv_lora_rank=256)), 4, 16)
+    assert e.value.status == b.MLA_ERR_UNSUPPORTED
+
+
+def _raw_prefill(lib, cfg, w, x, y, ws, nbytes):
+    c = cfg.c()
+    return lib.mla_prefill_forward(ctypes.byref(c), ctypes.byref(w) if w is not None else None,
+                                   x, 1, 16, y, None, ws, nbytes, None)
+
+
+def test_null_and_misaligned_pointers_rejected_without_launch():
+    # validation runs before any HIP call, so this works without a GPU
+    lib = m.load_library()
+    cfg = m.MlaConfig(**V3)
+    need = m.mla_prefill_workspace_size(cfg, 1, 16)
+    good = ctypes.c_void_p(0x10000)
+    w = b.Weights(*([0x10000] * 9))
+    assert _raw_prefill(lib, cfg, None, good, good, good, need) == b.MLA_ERR_INVALID_ARGUMENT
+    assert b"weights" in lib.mla_last_error()
+    wnull = b.Weights(*([0x10000] * 8 + [0]))
+    assert _raw_prefill(lib, cfg, wnull, good, good, good, need) == b.MLA_ERR_INVALID_ARGUMENT
+    assert b"wo" in lib.mla_last_error()
+    assert _raw_prefill(lib, cfg, w, None, good, good, need) == b.MLA_ERR_INVALID_ARGUMENT
+    assert _raw_prefill(lib, cfg, w, ctypes.c_void_p(0x10002), good, good,
+                        need) == b.MLA_ERR_INVALID_ARGUMENT
+    assert b"aligned" in lib.mla_last_error()
+    assert _raw_prefill(lib, cfg, w, good, good, good, need - 1) == b.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert b"needs" in lib.mla_last_error()
+    c = cfg.c()
+    st = lib.mla_decode_absorbed(ctypes.byref(c), ctypes.byref(w), good, 4, good, 16, None, good,
+                                 good, 1 << 30, None)
+    assert st == b.MLA_ERR_INVALID_ARGUMENT and b"cache_lens" in lib.mla_last_error()
+    rp = cfg.rope_params()
+    assert lib.mla_rope_apply(None, 1, 4, 1, 64, 64, 64, good, ctypes.byref(rp),
+                              None) == b.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_rope_apply(good, 1, 4, 1, 63, 64, 64, good, ctypes.byref(rp),
+                              None) == b.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_rope_apply(good, 1, 4, 1, 64, 64, 64, None, ctypes.byref(rp),
+                              None) == b.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_error_message_is_per_thread():
+    import threading
+    lib = m.load_library()
+    with pytest.raises(m.MlaError):
+        m.mla_prefill_workspace_size(m.MlaConfig(**dict(V3, hidden_size=0)), 1, 1)
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(lib.mla_last_error()))
+    t.start()
+    t.join()
+    assert seen == [b""]
+    assert b"hidden_size" in lib.mla_last_error()
