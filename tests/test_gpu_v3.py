@@ -81,12 +81,19 @@ def test_p5_shape_conventions():
     w2["w_qr"] = w["w_qr"].reshape(128, 64, -1)[:, P].reshape(128 * 64, -1)
     w2["w_kr"] = w["w_kr"][P]
     y_hs_perm, _ = _prefill(c, "half_split", x, w2)
+    refs = {}
     for conv, y in (("interleaved", y_il), ("half_split", y_hs)):
-        ref, _ = orc.mla_prefill_rows(oracle_cfg(c, rope=conv), w, x, rows)
-        assert_close_rows(to_np(y[0, rows]), ref, "bf16", conv)
+        refs[conv], _ = orc.mla_prefill_rows(oracle_cfg(c, rope=conv), w, x, rows)
+        assert_close_rows(to_np(y[0, rows]), refs[conv], "bf16", conv)
     yi, yh, yp = to_np(y_il[0]), to_np(y_hs[0]), to_np(y_hs_perm[0])
     assert_close_rows(yp, yi, "bf16", "permuted half-split vs interleaved")
-    assert np.abs(yh[1:] - yi[1:]).max() > 0.2 * np.abs(yi[1:]).max()
+    # with V3-scale weights the logits are nearly uniform, so the two
+    # conventions differ only slightly; the GPU must reproduce the oracle's
+    # difference itself, well above its own rounding
+    d_ref = refs["half_split"][1:] - refs["interleaved"][1:]
+    d_gpu = yh[rows[1:]] - yi[rows[1:]]
+    assert np.corrcoef(d_ref.ravel(), d_gpu.ravel())[0, 1] > 0.95
+    assert np.abs(d_ref).max() > 10 * np.abs(yp[rows[1:]] - yi[rows[1:]]).mean()
 
 
 def test_causality_bitwise():
