@@ -172,6 +172,204 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile bf16 kernel for the prefill projections (M in the thousands).
+//
+// 256x256 output tile per 256-thread workgroup: four waves in a 2x2 grid of
+// 128x128 wave tiles (4x4 MFMA 32x32 tiles, 256 fp32 accumulators per lane,
+// held in the accumulation registers), one wave per SIMD.  K advances in
+// 64-wide slabs through two LDS stages; the slab after next is fetched into
+// registers while the current one is multiplied, so one barrier per slab
+// suffices.  LDS rows are 64 elements (8 chunks of 16 bytes) with chunk j of
+// row r stored at j ^ (r & 7): the 16-byte writes of a row and the MFMA
+// fragment reads of eight consecutive rows hit distinct bank groups without
+// padding.
+//
+// Tiles are numbered so that each of the eight XCDs (which take workgroup ids
+// round-robin) works on a contiguous run of tiles, walked in groups of
+// GROUP_M tile rows, so concurrently running tiles share A and B slabs in that
+// XCD's L2.
+//
+// The accumulators leave through LDS: the tile is written there as bf16, then
+// every thread stores 16-byte runs of 8 consecutive columns, which fall in one
+// head of the destination (all column ranges and head widths are multiples of
+// 8), so the head-scatter store stays vectorised.
+constexpr int GB_M = 256, GB_N = 256, GB_K = 64, GB_THREADS = 256, GROUP_M = 4;
+constexpr int GB_CPITCH = GB_N + 8;               // epilogue LDS pitch (elements)
+constexpr int GB_STAGE = (GB_M + GB_N) * GB_K;    // elements per operand stage
+constexpr int GB_LDS = GB_M * GB_CPITCH > 2 * GB_STAGE ? GB_M * GB_CPITCH : 2 * GB_STAGE;
+
+__device__ inline int swz(int r, int k) { return r * GB_K + ((((k >> 3) ^ r) & 7) << 3) + (k & 7); }
+
+__device__ inline int seg_of(const GemmParams &p, int n) {
+  return (p.nseg > 1 && n >= p.seg[1].n_begin) ? ((p.nseg > 2 && n >= p.seg[2].n_begin) ? 2 : 1) : 0;
+}
+
+// Fields of column range s, read with constant indices only (a dynamic index
+// into the kernel-argument struct would copy it to scratch memory).
+#define SEG_FIELD(p, s, f) ((s) == 0 ? (p).seg[0].f : ((s) == 1 ? (p).seg[1].f : (p).seg[2].f))
+
+__global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int tiles_m,
+                                                              int tiles_n, int remap) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[GB_LDS];
+  bf16 *As0 = lds, *Bs0 = lds + GB_M * GB_K;
+
+  // tile index: contiguous run per XCD, then grouped row-major order
+  const int T = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if (remap) t = (t & 7) * (T >> 3) + (t >> 3);
+  const int per_group = GROUP_M * tiles_n;
+  const int grp = t / per_group;
+  const int first_m = grp * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (t % per_group) % gm;
+  const int tn = (t % per_group) / gm;
+  const int m0 = tm * GB_M, n0 = tn * GB_N;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 5, l32 = lane & 31;
+  const bf16 *A = reinterpret_cast<const bf16 *>(p.A);
+
+  // this thread's chunks: rows r0 + 32 i (i < 8) of the A and B slabs, chunk ch
+  const int r0 = tid >> 3, ch = tid & 7;
+  // Tile bases are uniform; each thread keeps 32-bit element offsets of its
+  // rows (clamped into the matrix: rows past M or N only feed outputs that
+  // are never stored).  Column ranges start at multiples of 256 (checked on
+  // the host), so one tile reads B from a single range.
+  const int st = seg_of(p, n0);
+  const int64_t t_ldb = SEG_FIELD(p, st, ldb);
+  const int t_nb = SEG_FIELD(p, st, n_begin);
+  const bf16 *Ab = A + (int64_t)m0 * p.lda + ch * 8;
+  const bf16 *Bb = reinterpret_cast<const bf16 *>(SEG_FIELD(p, st, B)) + (int64_t)(n0 - t_nb) * t_ldb + ch * 8;
+  const int lda = (int)p.lda, ldb = (int)t_ldb;
+#define GB_OFF(i)                                                            \
+  const int oa##i = (min(m0 + r0 + 32 * i, p.M - 1) - m0) * lda;            \
+  const int ob##i = (min(n0 + r0 + 32 * i, p.N - 1) - n0) * ldb;
+  GB_OFF(0) GB_OFF(1) GB_OFF(2) GB_OFF(3) GB_OFF(4) GB_OFF(5) GB_OFF(6) GB_OFF(7)
+#undef GB_OFF
+  uint4 ra0, ra1, ra2, ra3, ra4, ra5, ra6, ra7, rb0, rb1, rb2, rb3, rb4, rb5, rb6, rb7;
+#define GB_FETCH(k0)                                                         \
+  do {                                                                       \
+    const bf16 *a_ = Ab + (k0), *b_ = Bb + (k0);                             \
+    ra0 = *reinterpret_cast<const uint4 *>(a_ + oa0);                        \
+    ra1 = *reinterpret_cast<const uint4 *>(a_ + oa1);                        \
+    ra2 = *reinterpret_cast<const uint4 *>(a_ + oa2);                        \
+    ra3 = *reinterpret_cast<const uint4 *>(a_ + oa3);                        \
+    ra4 = *reinterpret_cast<const uint4 *>(a_ + oa4);                        \
+    ra5 = *reinterpret_cast<const uint4 *>(a_ + oa5);                        \
+    ra6 = *reinterpret_cast<const uint4 *>(a_ + oa6);                        \
+    ra7 = *reinterpret_cast<const uint4 *>(a_ + oa7);                        \
+    rb0 = *reinterpret_cast<const uint4 *>(b_ + ob0);                        \
+    rb1 = *reinterpret_cast<const uint4 *>(b_ + ob1);                        \
+    rb2 = *reinterpret_cast<const uint4 *>(b_ + ob2);                        \
+    rb3 = *reinterpret_cast<const uint4 *>(b_ + ob3);                        \
+    rb4 = *reinterpret_cast<const uint4 *>(b_ + ob4);                        \
+    rb5 = *reinterpret_cast<const uint4 *>(b_ + ob5);                        \
+    rb6 = *reinterpret_cast<const uint4 *>(b_ + ob6);                        \
+    rb7 = *reinterpret_cast<const uint4 *>(b_ + ob7);                        \
+  } while (0)
+#define GB_STASH1(As, Bs, i, ra, rb)                                         \
+  *reinterpret_cast<uint4 *>(&(As)[swz(r0 + 32 * (i), ch * 8)]) = ra;        \
+  *reinterpret_cast<uint4 *>(&(Bs)[swz(r0 + 32 * (i), ch * 8)]) = rb;
+#define GB_STASH(As, Bs)                                                     \
+  do {                                                                       \
+    GB_STASH1(As, Bs, 0, ra0, rb0) GB_STASH1(As, Bs, 1, ra1, rb1)            \
+    GB_STASH1(As, Bs, 2, ra2, rb2) GB_STASH1(As, Bs, 3, ra3, rb3)            \
+    GB_STASH1(As, Bs, 4, ra4, rb4) GB_STASH1(As, Bs, 5, ra5, rb5)            \
+    GB_STASH1(As, Bs, 6, ra6, rb6) GB_STASH1(As, Bs, 7, ra7, rb7)            \
+  } while (0)
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // one slab: the fragments of k-step s+1 are read from LDS while the 16
+  // MFMAs of k-step s run; sched_barrier keeps the compiler from hoisting all
+  // reads of the slab (which would need 128 more registers)
+  auto load_frags = [&](const bf16 *As, const bf16 *Bs, int kk, bf16x8 *a, bf16x8 *b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(wm * 128 + i * 32 + l32, kk + g * 8)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(wn * 128 + j * 32 + l32, kk + g * 8)]);
+  };
+  auto mma16 = [&](const bf16x8 *a, const bf16x8 *b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  auto compute = [&](const bf16 *As, const bf16 *Bs) {
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    load_frags(As, Bs, 0, a0, b0);
+    load_frags(As, Bs, 16, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(As, Bs, 32, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(As, Bs, 48, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(a1, b1);
+  };
+
+  const int nk = p.K / GB_K;
+  GB_FETCH(0);
+  GB_STASH(As0, Bs0);
+  if (nk > 1) GB_FETCH(GB_K);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = (kt & 1) * GB_STAGE, nxt = GB_STAGE - cur;
+    compute(lds + cur, lds + cur + GB_M * GB_K);
+    if (kt + 1 < nk) {
+      bf16 *An = lds + nxt, *Bn = lds + nxt + GB_M * GB_K;
+      GB_STASH(An, Bn);
+      if (kt + 2 < nk) GB_FETCH((kt + 2) * GB_K);
+    }
+    __syncthreads();
+  }
+#undef GB_FETCH
+#undef GB_STASH
+#undef GB_STASH1
+
+  // epilogue through LDS (the operand stages are free after the last barrier)
+  bf16 *Cs = lds;
+  bf16 *t_C = reinterpret_cast<bf16 *>(SEG_FIELD(p, st, C));
+  const int t_dh = SEG_FIELD(p, st, dh), t_off = SEG_FIELD(p, st, off);
+  const int64_t t_ld = SEG_FIELD(p, st, ld);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        Cs[(wm * 128 + i * 32 + acc_row(r, lane)) * GB_CPITCH + wn * 128 + j * 32 + l32] =
+            (bf16)acc[i][j][r];
+  __syncthreads();
+  for (int it = 0; it < (GB_M * GB_N / 8) / GB_THREADS; ++it) {
+    const int c = tid + GB_THREADS * it;
+    const int row = c >> 5, cc = c & 31;
+    const int m = m0 + row, n = n0 + cc * 8;
+    if (m >= p.M || n >= p.N) continue;
+    const int nn = n - t_nb;
+    const int h = nn / t_dh, d = nn - h * t_dh;
+    const int b = m / p.S, sq = m - b * p.S;
+    bf16 *dst = t_C + ((int64_t)(b * p.H + h) * p.S + sq) * t_ld + t_off + d;
+    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * GB_CPITCH + cc * 8]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
@@ -189,6 +387,17 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   p.H = d.H;
   p.nseg = d.nseg;
   for (int i = 0; i < 3; ++i) p.seg[i] = d.seg[i];
+  bool big = d.dtype == BF16 && !d.b_kn && d.batch == 1 && d.K % GB_K == 0 && d.M >= 512 &&
+             d.N % 8 == 0 && (int64_t)d.M * d.lda < (1LL << 31);
+  for (int i = 0; i < d.nseg && big; ++i)
+    big = d.seg[i].n_begin % GB_N == 0 && (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
+  if (big) {
+    const int tm = (d.M + GB_M - 1) / GB_M, tn = (d.N + GB_N - 1) / GB_N;
+    const int T = tm * tn;
+    hipLaunchKernelGGL(gemm_big_kernel, dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn,
+                       (T % 8 == 0) ? 1 : 0);
+    return hipGetLastError();
+  }
   dim3 grid((d.N + BN - 1) / BN, (d.M + BM - 1) / BM, d.batch);
   dim3 block(256);
   if (d.dtype == BF16) {
