@@ -13,9 +13,19 @@
 // of a single query: the row max needs one cross-lane swap (lane l and l^32)
 // and the rescale of the output accumulator is a per-lane multiply.  The
 // probabilities stay in registers and feed O^T += V^T P^T directly as the B
-// operand; V is stored transposed in LDS so the matching A operand is two
-// 8-byte LDS reads.  Query tiles are issued longest-first (causal work grows
-// with the query index).
+// operand; V arrives channel-major ([d][key], written that way by the kv
+// up-projection), so the matching A operand is two 8-byte LDS reads.
+//
+// Keys stream in tiles of 32 through two LDS stages: the tile after next is
+// fetched into registers while the current one is multiplied, one barrier
+// per tile.  The softmax keeps a stale running max until a new score exceeds
+// it by more than 2^8 (exp2 domain): the probabilities then stay below 256,
+// exact in fp32, and the output accumulator is rescaled only on those tiles.
+// The score scale folds into the exponent's FMA.
+//
+// Order: all query tiles of a (b, h) run on one XCD (workgroup ids go to the
+// eight XCDs round-robin), longest tiles first, so the K/V of a head are
+// fetched from HBM about once and then served from that XCD's L2.
 
 #include "common.h"
 #include "internal.h"
@@ -23,8 +33,9 @@
 namespace mla {
 namespace {
 
-constexpr int BQ = 128, BKV = 64;
+constexpr int BQ = 128, BKV = 32;
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RESCALE_LOG2 = 8.0f;
 
 template <typename T, int DN, int DR, int DV>
 struct AttnCfg {
@@ -35,28 +46,45 @@ struct AttnCfg {
   static constexpr int DVP = (DV + 31) / 32 * 32;
   static constexpr int KPITCH = DQKP + VEC;
   static constexpr int VPITCH = BKV + VEC;
+  static constexpr int KSTAGE = BKV * KPITCH;
+  static constexpr int VSTAGE = DVP * VPITCH;
   static constexpr int NQF = DQKP / MF::KSTEP;
   static constexpr int NDT = DVP / 32;
+  static constexpr int CPRK = DQKP / VEC;        // 16-byte chunks per K row
+  static constexpr int CPRV = BKV / VEC;         // 16-byte chunks per V^T row
+  static constexpr int KCH = (BKV * CPRK + 255) / 256;
+  static constexpr int VCH = (DV * CPRV + 255) / 256;
 };
 
 template <typename T>
 __device__ inline uint4 ld16(const T *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 template <typename T, int DN, int DR, int DV>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(PrefillAttnArgs a) {
   using C = AttnCfg<T, DN, DR, DV>;
   using MF = typename C::MF;
-  constexpr int VEC = C::VEC, DQK = C::DQK, DQKP = C::DQKP, KPITCH = C::KPITCH,
-                VPITCH = C::VPITCH, NQF = C::NQF, NDT = C::NDT, DVP = C::DVP;
-  __shared__ __attribute__((aligned(16))) T Ks[BKV * KPITCH];
-  __shared__ __attribute__((aligned(16))) T Vt[DVP * VPITCH];
+  constexpr int VEC = C::VEC, DQK = C::DQK, KPITCH = C::KPITCH, VPITCH = C::VPITCH,
+                NQF = C::NQF, NDT = C::NDT, DVP = C::DVP, CPRK = C::CPRK, CPRV = C::CPRV,
+                KCH = C::KCH, VCH = C::VCH, KSTAGE = C::KSTAGE, VSTAGE = C::VSTAGE;
+  __shared__ __attribute__((aligned(16))) T Ks[2 * KSTAGE];
+  __shared__ __attribute__((aligned(16))) T Vt[2 * VSTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int S = a.S, H = a.H;
   const int nq = (S + BQ - 1) / BQ;
-  const int qt = nq - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int P = a.B * H;
+  const int w = blockIdx.x;
+  int pair, qt;
+  if ((P & 7) == 0) {
+    const int local = w >> 3;
+    pair = (w & 7) * (P >> 3) + local / nq;
+    qt = nq - 1 - local % nq;
+  } else {
+    pair = w / nq;
+    qt = nq - 1 - w % nq;
+  }
+  const int b = pair / H, h = pair - b * H;
   const int q0 = qt * BQ;
   const int qw0 = q0 + wave * 32;
   const int iq = qw0 + l32;  // this lane's query
@@ -65,11 +93,13 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
   const T *qp = reinterpret_cast<const T *>(a.q) + bh * S * DQK;
   const T *kn = reinterpret_cast<const T *>(a.k_nope) + bh * S * DN;
   const T *kpe = reinterpret_cast<const T *>(a.k_pe) + (int64_t)b * S * a.ld_kpe;
-  const T *vp = reinterpret_cast<const T *>(a.v) + bh * S * DV;
+  const T *vt = reinterpret_cast<const T *>(a.vt) + bh * DV * S;
 
-  // zero the padding rows of V^T once (d >= DV never gets written)
   if constexpr (DVP > DV) {
-    for (int i = tid; i < (DVP - DV) * VPITCH; i += 256) Vt[DV * VPITCH + i] = from_f32<T>(0.f);
+    for (int i = tid; i < (DVP - DV) * VPITCH; i += 256) {
+      Vt[DV * VPITCH + i] = from_f32<T>(0.f);
+      Vt[VSTAGE + DV * VPITCH + i] = from_f32<T>(0.f);
+    }
   }
 
   // this lane's query fragments, kept in registers for the whole key loop
@@ -84,10 +114,67 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
         uint4 v = ld16(qp + (int64_t)iq * DQK + c);
         qf[f] = *reinterpret_cast<typename MF::frag *>(&v);
       } else {
+#pragma unroll
         for (int e = 0; e < MF::KPL; ++e) qf[f][e] = from_f32<T>(0.f);
       }
     }
   }
+
+  // register staging of one K / V^T tile (plain code, not lambdas: the
+  // staging registers must not end up in scratch memory)
+  uint4 rk[KCH], rv[VCH];
+#define ATT_FETCH(J0)                                                               \
+  do {                                                                              \
+    const int j0_ = (J0);                                                           \
+    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                               \
+      const int c = tid + 256 * i;                                                  \
+      const int jr = c / CPRK, cc = (c - jr * CPRK) * VEC;                          \
+      const int j = j0_ + jr;                                                       \
+      uint4 v = make_uint4(0, 0, 0, 0);                                             \
+      if (c < BKV * CPRK && j < S) {                                                \
+        if (cc < DN) v = ld16(kn + (int64_t)j * DN + cc);                           \
+        else if (cc < DQK) v = ld16(kpe + (int64_t)j * a.ld_kpe + (cc - DN));       \
+      }                                                                             \
+      rk[i] = v;                                                                    \
+    }                                                                               \
+    _Pragma("unroll") for (int i = 0; i < VCH; ++i) {                               \
+      const int c = tid + 256 * i;                                                  \
+      const int d = c / CPRV, jc = (c - d * CPRV) * VEC;                            \
+      const int j = j0_ + jc;                                                       \
+      uint4 v = make_uint4(0, 0, 0, 0);                                             \
+      if (c < DV * CPRV) {                                                          \
+        const T *src = vt + (int64_t)d * S + j;                                     \
+        if (j + VEC <= S) {                                                         \
+          v = ld16(src);                                                            \
+        } else {                                                                    \
+          T e[VEC];                                                                 \
+          _Pragma("unroll") for (int k = 0; k < VEC; ++k)                           \
+              e[k] = (j + k < S) ? src[k] : from_f32<T>(0.f);                       \
+          v = *reinterpret_cast<const uint4 *>(e);                                  \
+        }                                                                           \
+      }                                                                             \
+      rv[i] = v;                                                                    \
+    }                                                                               \
+  } while (0)
+#define ATT_STASH(STAGE)                                                            \
+  do {                                                                              \
+    T *ks_ = Ks + (STAGE) * KSTAGE;                                                 \
+    T *vs_ = Vt + (STAGE) * VSTAGE;                                                 \
+    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                               \
+      const int c = tid + 256 * i;                                                  \
+      if (c < BKV * CPRK) {                                                         \
+        const int jr = c / CPRK, cc = (c - jr * CPRK) * VEC;                        \
+        *reinterpret_cast<uint4 *>(&ks_[jr * KPITCH + cc]) = rk[i];                 \
+      }                                                                             \
+    }                                                                               \
+    _Pragma("unroll") for (int i = 0; i < VCH; ++i) {                               \
+      const int c = tid + 256 * i;                                                  \
+      if (c < DV * CPRV) {                                                          \
+        const int d = c / CPRV, jc = (c - d * CPRV) * VEC;                          \
+        *reinterpret_cast<uint4 *>(&vs_[d * VPITCH + jc]) = rv[i];                  \
+      }                                                                             \
+    }                                                                               \
+  } while (0)
 
   f32x16 o[NDT];
 #pragma unroll
@@ -98,97 +185,66 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
   const float sl2 = a.scale * LOG2E;
 
   const int kv_end = min(S, q0 + BQ);
-  for (int j0 = 0; j0 < kv_end; j0 += BKV) {
-    __syncthreads();  // previous tile fully consumed
-    // stage K = [k_nope ‖ k_pe] rows j0..j0+63 (zero outside) into LDS
-    constexpr int CPR = DQKP / VEC;
-    for (int c = tid; c < BKV * CPR; c += 256) {
-      const int jr = c / CPR, cc = (c - jr * CPR) * VEC;
-      const int j = j0 + jr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < S) {
-        if (cc < DN) v = ld16(kn + (int64_t)j * DN + cc);
-        else if (cc < DQK) v = ld16(kpe + (int64_t)j * a.ld_kpe + (cc - DN));
-      }
-      *reinterpret_cast<uint4 *>(&Ks[jr * KPITCH + cc]) = v;
-    }
-    // stage V^T: lane-consecutive keys so the 2-byte LDS writes do not collide
-    constexpr int VCH = DV / VEC;
-    for (int c = tid; c < BKV * VCH; c += 256) {
-      const int jr = c & (BKV - 1), dc = c / BKV;
-      const int j = j0 + jr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < S) v = ld16(vp + (int64_t)j * DV + dc * VEC);
-      const T *e = reinterpret_cast<const T *>(&v);
+  const int ntiles = (kv_end + BKV - 1) / BKV;
+  ATT_FETCH(0);
+  ATT_STASH(0);
+  if (ntiles > 1) ATT_FETCH(BKV);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * BKV;
+    const T *ks = Ks + (t & 1) * KSTAGE;
+    const T *vs = Vt + (t & 1) * VSTAGE;
+    if (j0 <= qw0 + 31) {
+      f32x16 st;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) Vt[(dc * VEC + i) * VPITCH + jr] = e[i];
-    }
-    __syncthreads();
-
-    if (j0 > qw0 + 31) continue;  // every key of the tile is after this wave's queries
-
-    f32x16 st[BKV / 32];
-#pragma unroll
-    for (int jt = 0; jt < BKV / 32; ++jt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[jt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) st[r] = 0.f;
 #pragma unroll
       for (int f = 0; f < NQF; ++f) {
         const typename MF::frag kf = *reinterpret_cast<const typename MF::frag *>(
-            &Ks[(jt * 32 + l32) * KPITCH + f * MF::KSTEP + g * MF::KPL]);
-        st[jt] = MF::mma(kf, qf[f], st[jt]);
+            &ks[l32 * KPITCH + f * MF::KSTEP + g * MF::KPL]);
+        st = MF::mma(kf, qf[f], st);
       }
-    }
-    // scale, causal mask, tile max of this lane's query
-    const bool diag = j0 + BKV - 1 > qw0;
-    float mx = -INFINITY;
+      // causal mask on the diagonal tiles, then the tile max of this query
+      if (j0 + BKV - 1 > qw0) {
 #pragma unroll
-    for (int jt = 0; jt < BKV / 32; ++jt)
+        for (int r = 0; r < 16; ++r)
+          if (j0 + acc_row(r, lane) > iq) st[r] = -INFINITY;
+      }
+      float mx = st[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // rescale only when the max grew past the allowance (or on first use)
+      const bool need = mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
+      if (__any(need)) {
+        const float alpha = need ? exp2f((m_run - mx) * sl2) : 1.0f;
+        if (need) m_run = mx;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDT; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      }
+      const float neg = m_run == -INFINITY ? 0.f : -m_run * sl2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float s = st[jt][r] * sl2;
-        if (diag) {
-          const int j = j0 + jt * 32 + acc_row(r, lane);
-          if (j > iq) s = -INFINITY;
-        }
-        st[jt][r] = s;
-        mx = fmaxf(mx, s);
+        const float pr = exp2f(fmaf(st[r], sl2, neg));
+        st[r] = pr;
+        l_run += pr;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < BKV / 32; ++jt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = exp2f(st[jt][r] - m_use);
-        st[jt][r] = pr;
-        psum += pr;
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int d = 0; d < NDT; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-
-    // O^T += V^T P^T, P^T taken from the score accumulators in place
-#pragma unroll
-    for (int jt = 0; jt < BKV / 32; ++jt) {
+      // O^T += V^T P^T with P^T taken from the score accumulators in place
 #pragma unroll
       for (int u = 0; u < 16 / MF::KPL; ++u) {
         typename MF::frag pf;
         if constexpr (MF::KPL == 1) {
-          pf = st[jt][u];
+          pf = st[u];
         } else {
 #pragma unroll
-          for (int e = 0; e < MF::KPL; ++e) pf[e] = from_f32<T>(st[jt][u * MF::KPL + e]);
+          for (int e = 0; e < MF::KPL; ++e) pf[e] = from_f32<T>(st[u * MF::KPL + e]);
         }
 #pragma unroll
         for (int d = 0; d < NDT; ++d) {
-          const T *row = &Vt[(d * 32 + l32) * VPITCH + jt * 32];
+          const T *row = &vs[(d * 32 + l32) * VPITCH];
           typename MF::frag vf;
           if constexpr (MF::KPL == 1) {
             vf = to_f32(row[acc_row(u, lane)]);
@@ -202,7 +258,14 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
         }
       }
     }
+    if (t + 1 < ntiles) {
+      ATT_STASH((t + 1) & 1);
+      if (t + 2 < ntiles) ATT_FETCH((t + 2) * BKV);
+    }
+    __syncthreads();
   }
+#undef ATT_FETCH
+#undef ATT_STASH
 
   // normalise and store o[b, i, h, d]
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -221,7 +284,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
 
 template <typename T, int DN, int DR, int DV>
 hipError_t launch_t(const PrefillAttnArgs &a, hipStream_t st) {
-  dim3 grid((a.S + BQ - 1) / BQ, a.H, a.B);
+  const int nq = (a.S + BQ - 1) / BQ;
+  dim3 grid(nq * a.H * a.B);
   hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

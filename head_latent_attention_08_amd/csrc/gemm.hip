@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     const GemmSeg &sg = p.seg[s];
     const int nn = n - sg.n_begin;
     const int h = nn / sg.dh, d = nn - h * sg.dh;
-    T *Cb = reinterpret_cast<T *>(sg.C) + (int64_t)z * p.strideC + sg.off + d;
+    T *Cb = reinterpret_cast<T *>(sg.C) + (int64_t)z * p.strideC;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -165,7 +165,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         const int m = m0 + wm * 64 + i * 32 + acc_row(r, lane);
         if (m < p.M) {
           const int b = m / p.S, sq = m - b * p.S;
-          Cb[((int64_t)(b * p.H + h) * p.S + sq) * sg.ld] = from_f32<T>(acc[i][j][r]);
+          const int64_t at = sg.tr ? ((int64_t)(b * p.H + h) * sg.dh + d) * p.S + sq
+                                   : ((int64_t)(b * p.H + h) * p.S + sq) * sg.ld + sg.off + d;
+          Cb[at] = from_f32<T>(acc[i][j][r]);
         }
       }
     }
@@ -357,16 +359,41 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
         Cs[(wm * 128 + i * 32 + acc_row(r, lane)) * GB_CPITCH + wn * 128 + j * 32 + l32] =
             (bf16)acc[i][j][r];
   __syncthreads();
-  for (int it = 0; it < (GB_M * GB_N / 8) / GB_THREADS; ++it) {
-    const int c = tid + GB_THREADS * it;
-    const int row = c >> 5, cc = c & 31;
-    const int m = m0 + row, n = n0 + cc * 8;
-    if (m >= p.M || n >= p.N) continue;
-    const int nn = n - t_nb;
-    const int h = nn / t_dh, d = nn - h * t_dh;
-    const int b = m / p.S, sq = m - b * p.S;
-    bf16 *dst = t_C + ((int64_t)(b * p.H + h) * p.S + sq) * t_ld + t_off + d;
-    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * GB_CPITCH + cc * 8]);
+  if (!SEG_FIELD(p, st, tr)) {
+    for (int it = 0; it < (GB_M * GB_N / 8) / GB_THREADS; ++it) {
+      const int c = tid + GB_THREADS * it;
+      const int row = c >> 5, cc = c & 31;
+      const int m = m0 + row, n = n0 + cc * 8;
+      if (m >= p.M || n >= p.N) continue;
+      const int nn = n - t_nb;
+      const int h = nn / t_dh, d = nn - h * t_dh;
+      const int b = m / p.S, sq = m - b * p.S;
+      bf16 *dst = t_C + ((int64_t)(b * p.H + h) * p.S + sq) * t_ld + t_off + d;
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * GB_CPITCH + cc * 8]);
+    }
+  } else {
+    // channel-major destination: runs of 8 consecutive rows (tokens) of one
+    // column; lane-consecutive columns keep the 2-byte LDS reads conflict-free
+    for (int it = 0; it < (GB_M * GB_N / 8) / GB_THREADS; ++it) {
+      const int c = tid + GB_THREADS * it;
+      const int col = c & (GB_N - 1), rg = c / GB_N;
+      const int m = m0 + rg * 8, n = n0 + col;
+      if (m >= p.M || n >= p.N) continue;
+      const int nn = n - t_nb;
+      const int h = nn / t_dh, d = nn - h * t_dh;
+      const int b = m / p.S, sq = m - b * p.S;
+      if (sq + 8 <= p.S && m + 8 <= p.M) {
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = Cs[(rg * 8 + e) * GB_CPITCH + col];
+        *reinterpret_cast<bf16x8 *>(t_C + ((int64_t)(b * p.H + h) * t_dh + d) * p.S + sq) = v;
+      } else {
+        for (int e = 0; e < 8 && m + e < p.M; ++e) {
+          const int me = m + e, be = me / p.S, se = me - be * p.S;
+          t_C[((int64_t)(be * p.H + h) * t_dh + d) * p.S + se] = Cs[(rg * 8 + e) * GB_CPITCH + col];
+        }
+      }
+    }
   }
 }
 

@@ -14,8 +14,10 @@ inline size_t dtype_size(int dt) { return dt == BF16 ? 2 : 4; }
 // where its B rows come from and where its results go.  Output column n of
 // the range maps to head h = (n - n_begin) / dh and channel d = (n - n_begin)
 // % dh, and output row m to (b, s) = (m / S, m % S); the element lands at
-//   C + ((b * H + h) * S + s) * ld + off + d.
-// With H = 1 and dh >= width this is a plain row-major store with row pitch ld.
+//   C + ((b * H + h) * S + s) * ld + off + d              (tr == 0)
+//   C + ((b * H + h) * dh + d) * S + s                    (tr == 1, channel-major)
+// With H = 1 and dh >= width the first is a plain row-major store with row
+// pitch ld.
 struct GemmSeg {
   const void *B;
   int64_t ldb;
@@ -24,6 +26,7 @@ struct GemmSeg {
   int dh;
   int64_t ld;
   int off;
+  int tr = 0;
 };
 
 struct GemmDesc {
@@ -79,7 +82,7 @@ struct PrefillAttnArgs {
   const void *k_nope; // [B, H, S, dn]
   const void *k_pe;   // rows of pitch ld_kpe, token t = b * S + s
   int64_t ld_kpe;
-  const void *v;      // [B, H, S, dv]
+  const void *vt;     // [B, H, dv, S]  (channel-major, keys contiguous)
   void *o;            // [B * S, H * dv]
   int B, S, H;
   float scale;

@@ -394,7 +394,7 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
   MLA_HIP(launch_rope(c.dtype, q + (size_t)dn * es, M, S, (int64_t)H * S * dqk, dqk, H,
                       (int64_t)S * dqk, nullptr, tab, st),
           "rope q_pe");
-  // 5. k_nope and v per head
+  // 5. k_nope [B, H, S, d_n] and v channel-major [B, H, d_v, S] per head
   MLA_MARK(5);
   {
     GemmDesc g;
@@ -408,7 +408,7 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
     g.H = H;
     g.nseg = 2;
     g.seg[0] = GemmSeg{w->w_up_k, rkv, 0, kn, dn, dn, 0};
-    g.seg[1] = GemmSeg{w->w_up_v, rkv, H * dn, v, dv, dv, 0};
+    g.seg[1] = GemmSeg{w->w_up_v, rkv, H * dn, v, dv, dv, 0, 1};  // v channel-major
     MLA_HIP(launch_gemm(g, st), "kv up-projection");
   }
   // 6. causal attention
@@ -419,7 +419,7 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
     a.k_nope = kn;
     a.k_pe = down + (size_t)(rq + rkv) * es;
     a.ld_kpe = p.ld_down;
-    a.v = v;
+    a.vt = v;
     a.o = o;
     a.B = B;
     a.S = S;

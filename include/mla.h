@@ -115,7 +115,7 @@ typedef struct {                  /* device pointers, nn.Linear [out][in]      *
  *   c_q   [B*S, r_q]           c_q = x w_down_q^T, then RMS-normalised in place
  *   c_kv  [B*S, r_kv]          latent;  k_pe [B*S, d_r] post-RoPE
  *   q     [B, H, S, d_n+d_r]   q_nope ‖ post-RoPE q_pe per head
- *   k_nope[B, H, S, d_n]       v [B, H, S, d_v]
+ *   k_nope[B, H, S, d_n]       v [B, H, d_v, S] (channel-major: keys contiguous)
  *   o     [B*S, H*d_v]         attention output, head-major columns
  * Row strides: c_q, c_kv and k_pe share one row of ld_down elements
  * (c_q at column 0, c_kv at r_q, k_pe at r_q + r_kv). */

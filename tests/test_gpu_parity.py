@@ -114,7 +114,7 @@ def _check_intermediates(m, cfg, c, x, ws, inter, dtype):
         "k_pe": ws_view(ws, lay.k_pe, (M, dr), td, ld),
         "q": ws_view(ws, lay.q, (B, H, S, dn + dr), td),
         "k_nope": ws_view(ws, lay.k_nope, (B, H, S, dn), td),
-        "v": ws_view(ws, lay.v, (B, H, S, dv), td),
+        "v": ws_view(ws, lay.v, (B, H, dv, S), td).transpose(2, 3),
         "o": ws_view(ws, lay.o, (M, H * dv), td),
     }
     q_ref = np.concatenate([inter["q_nope"], inter["q_pe"]], -1).transpose(0, 2, 1, 3)
