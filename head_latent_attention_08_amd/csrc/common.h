@@ -40,6 +40,29 @@ template <> struct Mfma32<float> {
   }
 };
 
+// 16x16 MFMA tile traits (same conventions): A lane l holds row l%16 and
+// KPL k values from (l/16)*KPL; B lane l holds column l%16 and the same k
+// values; accumulator element r of lane l is row (l/16)*4 + r, column l%16.
+template <typename T> struct Mfma16;
+
+template <> struct Mfma16<bf16> {
+  static constexpr int KPL = 8;
+  static constexpr int KSTEP = 32;
+  using frag = bf16x8;
+  __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma16<float> {
+  static constexpr int KPL = 1;
+  static constexpr int KSTEP = 4;
+  using frag = float;
+  __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
 __device__ inline int acc_row(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }

@@ -9,19 +9,32 @@
 // streams each row from HBM once for all heads of a head group.
 //
 // Work split: the rows of all sequences (lens[b] + 1 each, the new token
-// included) are laid end to end and cut into n_blocks equal ranges, one per
-// workgroup, so long and short sequences load the GPU evenly.  A range that
-// spans sequence boundaries yields one partial (unnormalised o_lat, running
-// max, running sum) per sequence piece, in slot (block + b) -- unique because
-// block and sequence indices both rise along the flattened rows.  A merge
-// kernel combines the pieces of each sequence with log-sum-exp weights.
+// included) are laid end to end and cut into n_blocks equal ranges, so long
+// and short sequences load the GPU evenly.  Each range is processed by one
+// workgroup per group of 64 heads; the workgroups of a range are numbered so
+// they land on the same XCD at the same time (workgroup ids go to the eight
+// XCDs round-robin) and the second read of every cache tile hits that XCD's
+// L2.  A range that spans sequence boundaries yields one partial
+// (unnormalised o_lat, running max, running sum) per sequence piece, in slot
+// (range + b) -- unique because range and sequence indices both rise along
+// the flattened rows.  A merge kernel combines the pieces of each sequence
+// with log-sum-exp weights.
 //
-// Inside a workgroup: four waves, 32 heads each.  A wave computes S^T = C Q^T
-// on 32x32 MFMA tiles (32 cache rows x 32 heads, K = 576), keeps the softmax
-// online per head (each lane holds one head), and accumulates O^T += C^T P^T
-// with P^T taken from the score accumulators in place.  Cache tiles are staged
-// in LDS twice: row-major for the score product and transposed (latent part
-// only) for the value product.
+// Inside a workgroup: four waves, 16 heads each, on 16x16x32 MFMAs.  A wave
+// computes S^T = C Q^T (16 cache rows x 16 heads per tile, K = 576), keeps the
+// softmax online per head, and accumulates O^T += C^T P^T with P^T taken from
+// the score accumulators in place.  The C^T operand comes straight from the
+// row-major cache tile through the 16-bit transposing LDS read: within each
+// 16-lane group, lane i receives element i % 4 of the 8-byte chunks
+// addressed by lanes 4e + i / 4 (e = 0..3), so pointing lane s at row
+// j0 + s / 4, column c0 + 4 (s % 4) hands every lane keys j0..j0+3 of its own
+// column c0 + i.  Cache tiles of 32 rows stream through two LDS stages with
+// register prefetch of the tile after next; the running max is kept stale
+// until a score exceeds it by 2^8, so the accumulators are rarely rescaled.
+// Sixteen heads per wave keep the per-lane state (128 accumulators, 72
+// registers of queries) well inside the register file; LDS read bandwidth
+// (about 215 B/clk per CU measured for 16-byte reads) covers the four waves
+// reading every tile.
 
 #include "common.h"
 #include "internal.h"
@@ -29,20 +42,25 @@
 namespace mla {
 namespace {
 
-constexpr int TK = 32;  // cache rows per tile
+constexpr int TK = 32;   // cache rows per tile
+constexpr int HPW = 16;  // heads per wave
+constexpr int HPB = 64;  // heads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RESCALE_LOG2 = 8.0f;
 
 template <typename T, int R, int DR>
 struct DecCfg {
-  using MF = Mfma32<T>;
+  using MF = Mfma16<T>;
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int W = R + DR;
   static constexpr int WP = (W + MF::KSTEP - 1) / MF::KSTEP * MF::KSTEP;
-  static constexpr int RP = (R + 31) / 32 * 32;
-  static constexpr int CPITCH = WP + VEC;
-  static constexpr int TPITCH = TK + VEC;
+  static constexpr int RP = (R + 15) / 16 * 16;
+  static constexpr int CPITCH = (WP > RP ? WP : RP) + VEC;  // 1168 B at V3 sizes
+  static constexpr int STAGE = TK * CPITCH;
   static constexpr int NQF = WP / MF::KSTEP;
-  static constexpr int NCT = RP / 32;
+  static constexpr int NCT = RP / 16;
+  static constexpr int CPR = W / VEC;                 // 16-byte chunks per cache row
+  static constexpr int NCH = (TK * CPR + 255) / 256;  // staging chunks per thread
 };
 
 // Rows of sequence b in the flattened order: lens[b] + 1 for a valid length.
@@ -51,22 +69,33 @@ __device__ inline int seq_rows(const int32_t *lens, int b, int64_t cap) {
   return (L >= 0 && (int64_t)L < cap) ? L + 1 : 0;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 template <typename T, int R, int DR>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
   using C = DecCfg<T, R, DR>;
   using MF = typename C::MF;
-  constexpr int VEC = C::VEC, W = C::W, WP = C::WP, RP = C::RP, CPITCH = C::CPITCH,
-                TPITCH = C::TPITCH, NQF = C::NQF, NCT = C::NCT;
-  __shared__ __attribute__((aligned(16))) T Cs[TK * CPITCH];
-  __shared__ __attribute__((aligned(16))) T Ct[RP * TPITCH];
+  constexpr int VEC = C::VEC, W = C::W, CPITCH = C::CPITCH, STAGE = C::STAGE, NQF = C::NQF,
+                NCT = C::NCT, CPR = C::CPR, NCH = C::NCH;
+  __shared__ __attribute__((aligned(16))) T Cs[2 * STAGE];
   extern __shared__ int starts[];  // [B + 1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
+  const int q = lane >> 4, l16 = lane & 15;
   const int B = a.B, H = a.H;
-  const int blk = blockIdx.x;
-  const int h = blockIdx.y * 128 + wave * 32 + l32;
-  const bool wave_live = blockIdx.y * 128 + wave * 32 < H;
+  const int n_hg = (H + HPB - 1) / HPB;
+  // workgroup -> (range, head group); head groups of one range share an XCD
+  int blk, hg;
+  if ((a.n_blocks & 7) == 0) {
+    const int local = blockIdx.x >> 3;
+    hg = local % n_hg;
+    blk = (local / n_hg) * 8 + (blockIdx.x & 7);
+  } else {
+    hg = blockIdx.x % n_hg;
+    blk = blockIdx.x / n_hg;
+  }
+  const int h = hg * HPB + wave * HPW + l16;
+  const bool wave_live = hg * HPB + wave * HPW < H;
 
   // prefix sums of per-sequence row counts
   for (int b = tid; b < B; b += 256) starts[b + 1] = seq_rows(a.lens, b, a.cap);
@@ -95,22 +124,51 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
   int b = 0;
   while (starts[b + 1] <= r0) ++b;  // first sequence holding row r0
 
-  if constexpr (RP > R) {
-    for (int i = tid; i < (RP - R) * TPITCH; i += 256) Ct[R * TPITCH + i] = from_f32<T>(0.f);
+  if constexpr (CPITCH - VEC > W) {
+    // columns past the row width feed only products with zero queries or
+    // output channels >= R; keep them finite
+    for (int i = tid; i < 2 * TK; i += 256)
+      for (int c = W; c < CPITCH; ++c) Cs[(i / TK) * STAGE + (i % TK) * CPITCH + c] = from_f32<T>(0.f);
   }
   const float sl2 = a.scale * LOG2E;
   const T *cache = reinterpret_cast<const T *>(a.cache);
+
+  uint4 rc[NCH];
+#define DEC_FETCH(T0)                                                                \
+  do {                                                                               \
+    const int t0_ = (T0);                                                            \
+    _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                \
+      const int c = tid + 256 * i;                                                   \
+      const int jr = c / CPR, cc = (c - jr * CPR) * VEC;                             \
+      uint4 v = make_uint4(0, 0, 0, 0);                                              \
+      if (c < TK * CPR && t0_ + jr < t_end)                                          \
+        v = *reinterpret_cast<const uint4 *>(cb + (int64_t)(t0_ + jr) * W + cc);     \
+      rc[i] = v;                                                                     \
+    }                                                                                \
+  } while (0)
+#define DEC_STASH(STG)                                                               \
+  do {                                                                               \
+    T *cs_ = Cs + (STG) * STAGE;                                                     \
+    _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                \
+      const int c = tid + 256 * i;                                                   \
+      if (c < TK * CPR) {                                                            \
+        const int jr = c / CPR, cc = (c - jr * CPR) * VEC;                           \
+        *reinterpret_cast<uint4 *>(&cs_[jr * CPITCH + cc]) = rc[i];                  \
+      }                                                                              \
+    }                                                                                \
+  } while (0)
 
   while (r0 < r1) {
     const int seg_end = min(r1, starts[b + 1]);
     const int t_begin = r0 - starts[b], t_end = seg_end - starts[b];
     const T *cb = cache + (int64_t)b * a.cap * W;
 
+    // B operand of S^T = C Q^T: lane holds head l16, k values q*KPL.. of each step
     typename MF::frag qf[NQF];
     const T *qp = reinterpret_cast<const T *>(a.q_lat) + ((int64_t)b * H + h) * W;
 #pragma unroll
     for (int f = 0; f < NQF; ++f) {
-      const int c = f * MF::KSTEP + g * MF::KPL;
+      const int c = f * MF::KSTEP + q * MF::KPL;
       if constexpr (MF::KPL == 1) {
         qf[f] = (h < H && c < W) ? to_f32(qp[c]) : 0.f;
       } else {
@@ -118,172 +176,200 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
           uint4 v = *reinterpret_cast<const uint4 *>(qp + c);
           qf[f] = *reinterpret_cast<typename MF::frag *>(&v);
         } else {
+#pragma unroll
           for (int e = 0; e < MF::KPL; ++e) qf[f][e] = from_f32<T>(0.f);
         }
       }
     }
-    f32x16 o[NCT];
+    f32x4 o[NCT];
 #pragma unroll
     for (int d = 0; d < NCT; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+      for (int r = 0; r < 4; ++r) o[d][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int t0 = t_begin; t0 < t_end; t0 += TK) {
-      __syncthreads();
-      constexpr int CPR = WP / VEC;
-      for (int c = tid; c < TK * CPR; c += 256) {
-        const int jr = c / CPR, cc = (c - jr * CPR) * VEC;
-        const int t = t0 + jr;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < t_end && cc < W) v = *reinterpret_cast<const uint4 *>(cb + (int64_t)t * W + cc);
-        *reinterpret_cast<uint4 *>(&Cs[jr * CPITCH + cc]) = v;
-        if (cc < R) {
-          const T *e = reinterpret_cast<const T *>(&v);
+    const int ntiles = (t_end - t_begin + TK - 1) / TK;
+    __syncthreads();  // the previous segment's last tile is fully consumed
+    DEC_FETCH(t_begin);
+    DEC_STASH(0);
+    if (ntiles > 1) DEC_FETCH(t_begin + TK);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int t0 = t_begin + it * TK;
+      const T *cs = Cs + (it & 1) * STAGE;
+      if (wave_live) {
+        // S^T for keys 0..15 (s0) and 16..31 (s1) of the tile: lane holds keys
+        // q*4 + r (+16), head l16
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) Ct[(cc + i) * TPITCH + jr] = e[i];
-        }
-      }
-      __syncthreads();
-      if (!wave_live) continue;
-
-      f32x16 st;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = 0.f;
-#pragma unroll
-      for (int f = 0; f < NQF; ++f) {
-        const typename MF::frag kf = *reinterpret_cast<const typename MF::frag *>(
-            &Cs[l32 * CPITCH + f * MF::KSTEP + g * MF::KPL]);
-        st = MF::mma(kf, qf[f], st);
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = st[r] * sl2;
-        if (t0 + acc_row(r, lane) >= t_end) s = -INFINITY;
-        st[r] = s;
-        mx = fmaxf(mx, s);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = exp2f(st[r] - m_use);
-        st[r] = pr;
-        psum += pr;
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int d = 0; d < NCT; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-#pragma unroll
-      for (int u = 0; u < 16 / MF::KPL; ++u) {
-        typename MF::frag pf;
-        if constexpr (MF::KPL == 1) {
-          pf = st[u];
-        } else {
-#pragma unroll
-          for (int e = 0; e < MF::KPL; ++e) pf[e] = from_f32<T>(st[u * MF::KPL + e]);
-        }
-#pragma unroll
-        for (int d = 0; d < NCT; ++d) {
-          const T *row = &Ct[(d * 32 + l32) * TPITCH];
-          typename MF::frag vf;
+        for (int f = 0; f < NQF; ++f) {
+          const int c = f * MF::KSTEP + q * MF::KPL;
+          typename MF::frag k0, k1;
           if constexpr (MF::KPL == 1) {
-            vf = to_f32(row[acc_row(u, lane)]);
+            k0 = to_f32(cs[l16 * CPITCH + c]);
+            k1 = to_f32(cs[(16 + l16) * CPITCH + c]);
           } else {
-            const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + u * 16 + g * 4);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + u * 16 + 8 + g * 4);
-            vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            k0 = *reinterpret_cast<const typename MF::frag *>(&cs[l16 * CPITCH + c]);
+            k1 = *reinterpret_cast<const typename MF::frag *>(&cs[(16 + l16) * CPITCH + c]);
           }
-          o[d] = MF::mma(vf, pf, o[d]);
+          s0 = MF::mma(k0, qf[f], s0);
+          s1 = MF::mma(k1, qf[f], s1);
+        }
+        if (t0 + TK > t_end) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (t0 + q * 4 + r >= t_end) s0[r] = -INFINITY;
+            if (t0 + 16 + q * 4 + r >= t_end) s1[r] = -INFINITY;
+          }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool need =
+            mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
+        if (__any(need)) {
+          const float alpha = need ? exp2f((m_run - mx) * sl2) : 1.0f;
+          if (need) m_run = mx;
+          l_run *= alpha;
+#pragma unroll
+          for (int d = 0; d < NCT; ++d) o[d] *= alpha;
+        }
+        const float neg = m_run == -INFINITY ? 0.f : -m_run * sl2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s0[r] = exp2f(fmaf(s0[r], sl2, neg));
+          s1[r] = exp2f(fmaf(s1[r], sl2, neg));
+          l_run += s0[r] + s1[r];
+        }
+        // O^T += C^T P^T: for bf16 one MFMA per 16 latent channels covers all
+        // 32 keys; k slots 0..3 are keys q*4 + e, slots 4..7 keys 16 + q*4 + e
+        if constexpr (MF::KPL == 1) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float pf = t < 4 ? s0[t] : s1[t - 4];
+            const int key = (t < 4 ? 0 : 16) + q * 4 + (t & 3);
+#pragma unroll
+            for (int d = 0; d < NCT; ++d)
+              o[d] = MF::mma(to_f32(cs[key * CPITCH + d * 16 + l16]), pf, o[d]);
+          }
+        } else {
+          typename MF::frag pf;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pf[e] = from_f32<T>(s0[e]);
+            pf[4 + e] = from_f32<T>(s1[e]);
+          }
+          const T *pbase = &cs[(q * 4 + (l16 >> 2)) * CPITCH + 4 * (l16 & 3)];
+#pragma unroll
+          for (int d = 0; d < NCT; ++d) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(pbase + d * 16));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(pbase + 16 * CPITCH + d * 16));
+            const typename MF::frag vf = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[d] = MF::mma(vf, pf, o[d]);
+          }
         }
       }
+      if (it + 1 < ntiles) {
+        DEC_STASH((it + 1) & 1);
+        if (it + 2 < ntiles) DEC_FETCH(t0 + 2 * TK);
+      }
+      __syncthreads();
     }
 
-    // partial of this sequence piece: unnormalised o_lat, max (log2 domain), sum
-    if (wave_live && h < H) {
-      const int slot = blk + b;
-      float *po = a.part_o + ((int64_t)slot * H + h) * R;
+    // partial of this sequence piece: unnormalised o_lat (log2-domain max, sum)
+    if (wave_live) {
+      float l_tot = l_run + __shfl_xor(l_run, 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      if (h < H) {
+        const int slot = blk + b;
+        float *po = a.part_o + ((int64_t)slot * H + h) * R;
 #pragma unroll
-      for (int d = 0; d < NCT; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = d * 32 + acc_row(r, lane);
-          if (c < R) po[c] = o[d][r];
+        for (int d = 0; d < NCT; ++d) {
+          const int c = d * 16 + q * 4;
+          if (c + 4 <= R) *reinterpret_cast<f32x4 *>(po + c) = o[d];
         }
-      const float l_tot = l_run + __shfl_xor(l_run, 32);
-      if (g == 0) {
-        a.part_ml[((int64_t)slot * H + h) * 2 + 0] = m_run;
-        a.part_ml[((int64_t)slot * H + h) * 2 + 1] = l_tot;
+        if (q == 0) {
+          a.part_ml[((int64_t)slot * H + h) * 2 + 0] = m_run * sl2;
+          a.part_ml[((int64_t)slot * H + h) * 2 + 1] = l_tot;
+        }
       }
     }
     r0 = seg_end;
     ++b;
   }
+#undef DEC_FETCH
+#undef DEC_STASH
 }
 
 // Combine the pieces of sequence b: o_lat = sum_i w_i O_i / sum_i w_i l_i,
 // w_i = exp2(m_i - max_i m_i).  A sequence with no valid rows gets NaN.
+// One workgroup per (sequence, group of 8 heads).
+constexpr int MERGE_HEADS = 8;
+
 template <typename T, int R>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
-  __shared__ int red[256];
-  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  int before = 0, all = 0;
-  for (int i = tid; i < a.B; i += 256) {
-    const int n = seq_rows(a.lens, i, a.cap);
-    all += n;
-    if (i < b) before += n;
+  __shared__ int sh[2];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (tid < 64) {
+    int before = 0, all = 0;
+    for (int i = tid; i < a.B; i += 64) {
+      const int n = seq_rows(a.lens, i, a.cap);
+      all += n;
+      if (i < b) before += n;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      before += __shfl_xor(before, o);
+      all += __shfl_xor(all, o);
+    }
+    if (tid == 0) {
+      sh[0] = before;
+      sh[1] = all;
+    }
   }
-  red[tid] = before;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const int start = red[0];
-  __syncthreads();
-  red[tid] = all;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const int total = red[0];
+  const int start = sh[0], total = sh[1];
   const int n_b = seq_rows(a.lens, b, a.cap);
-  T *out = reinterpret_cast<T *>(a.o_lat) + ((int64_t)b * a.H + h) * R;
+  const int h0 = blockIdx.y * MERGE_HEADS;
   if (n_b == 0) {
-    for (int c = tid; c < R; c += 256) out[c] = from_f32<T>(NAN);
+    for (int i = tid; i < MERGE_HEADS * R; i += 256) {
+      const int h = h0 + i / R;
+      if (h < a.H) reinterpret_cast<T *>(a.o_lat)[((int64_t)b * a.H + h) * R + i % R] = from_f32<T>(NAN);
+    }
     return;
   }
   const int per = (total + a.n_blocks - 1) / a.n_blocks;
   const int i0 = start / per, i1 = (start + n_b - 1) / per;
-  float M = -INFINITY;
-  for (int i = i0; i <= i1; ++i) M = fmaxf(M, a.part_ml[((int64_t)(i + b) * a.H + h) * 2]);
-  float L = 0.f;
-  for (int i = i0; i <= i1; ++i) {
-    const float *ml = a.part_ml + ((int64_t)(i + b) * a.H + h) * 2;
-    L += exp2f(ml[0] - M) * ml[1];
-  }
-  const float invL = 1.0f / L;
-  for (int c = tid; c < R; c += 256) {
-    float acc = 0.f;
+  for (int hh = 0; hh < MERGE_HEADS; ++hh) {
+    const int h = h0 + hh;
+    if (h >= a.H) break;
+    float M = -INFINITY;
+    for (int i = i0; i <= i1; ++i) M = fmaxf(M, a.part_ml[((int64_t)(i + b) * a.H + h) * 2]);
+    float L = 0.f;
     for (int i = i0; i <= i1; ++i) {
-      const float w = exp2f(a.part_ml[((int64_t)(i + b) * a.H + h) * 2] - M);
-      acc += w * a.part_o[((int64_t)(i + b) * a.H + h) * R + c];
+      const float *ml = a.part_ml + ((int64_t)(i + b) * a.H + h) * 2;
+      L += exp2f(ml[0] - M) * ml[1];
     }
-    out[c] = from_f32<T>(acc * invL);
+    const float invL = 1.0f / L;
+    T *out = reinterpret_cast<T *>(a.o_lat) + ((int64_t)b * a.H + h) * R;
+    for (int c = tid; c < R; c += 256) {
+      float acc = 0.f;
+      for (int i = i0; i <= i1; ++i) {
+        const float w = exp2f(a.part_ml[((int64_t)(i + b) * a.H + h) * 2] - M);
+        acc += w * a.part_o[((int64_t)(i + b) * a.H + h) * R + c];
+      }
+      out[c] = from_f32<T>(acc * invL);
+    }
   }
 }
 
 template <typename T, int R, int DR>
 hipError_t launch_t(const DecodeAttnArgs &a, hipStream_t st) {
-  dim3 grid(a.n_blocks, (a.H + 127) / 128);
+  dim3 grid(a.n_blocks * ((a.H + HPB - 1) / HPB));
   size_t shm = (size_t)(a.B + 1) * sizeof(int);
   hipLaunchKernelGGL((decode_attn_kernel<T, R, DR>), grid, dim3(256), shm, st, a);
   return hipGetLastError();
@@ -291,13 +377,14 @@ hipError_t launch_t(const DecodeAttnArgs &a, hipStream_t st) {
 
 template <typename T, int R>
 hipError_t launch_merge_t(const DecodeAttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_merge_kernel<T, R>), dim3(a.B, a.H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, R>), dim3(a.B, (a.H + MERGE_HEADS - 1) / MERGE_HEADS),
+                     dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int decode_blocks() { return 256; }
+int decode_blocks() { return 128; }
 
 hipError_t launch_decode_attention(int dtype, int r, int dr, const DecodeAttnArgs &a,
                                    hipStream_t st) {
