@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one of the two workloads only (profiling aid; no JSON line)")
     ap.add_argument("--replicas", type=int, default=3,
                     help="decode cache replicas rotated per step (defeats the 256 MB MALL)")
     args = ap.parse_args()
@@ -122,16 +124,17 @@ def main():
     torch.cuda.set_device(0)
     c_pre = si.CONFIGS["v3_prefill"]
     c_dec = si.CONFIGS["v3_decode"]
-    log("bench: generating V3 prefill inputs (seed 3000)")
-    x, w = si.make_inputs(c_pre)
     cfg_pre = mla_cfg(c_pre)
-    xd_pre = to_dev(x, "bf16")
-    wd_pre = weights_to_dev(w, "bf16")
-    B, S = x.shape[0], x.shape[1]
-    y_pre = torch.empty((B, S, c_pre["hidden_size"]), dtype=torch.bfloat16, device="cuda")
-    lat_pre = torch.empty((B, S, 576), dtype=torch.bfloat16, device="cuda")
-    ws_pre = torch.empty(m.mla_prefill_workspace_size(cfg_pre, B, S), dtype=torch.uint8,
-                         device="cuda")
+    B, S = c_pre["batch"], c_pre["seq"]
+    if args.only != "decode":
+        log("bench: generating V3 prefill inputs (seed 3000)")
+        x, w = si.make_inputs(c_pre)
+        xd_pre = to_dev(x, "bf16")
+        wd_pre = weights_to_dev(w, "bf16")
+        y_pre = torch.empty((B, S, c_pre["hidden_size"]), dtype=torch.bfloat16, device="cuda")
+        lat_pre = torch.empty((B, S, 576), dtype=torch.bfloat16, device="cuda")
+        ws_pre = torch.empty(m.mla_prefill_workspace_size(cfg_pre, B, S), dtype=torch.uint8,
+                             device="cuda")
 
     log("bench: generating V3 decode inputs (seed 4000)")
     xdec, wdec, lens, cache = si.make_decode_inputs(c_dec)
@@ -157,12 +160,14 @@ def main():
         return evs
 
     def step(i, pe=None, de=None):
-        m.mla_set_stage_events([e.cuda_event for e in pe] if pe else None)
-        m.mla_prefill_forward(cfg_pre, wd_pre, xd_pre, y=y_pre, latent_out=lat_pre,
-                              workspace=ws_pre)
-        m.mla_set_stage_events([e.cuda_event for e in de] if de else None)
-        m.mla_decode_absorbed(cfg_dec, wdec_d, xdec_d, caches[i % len(caches)], lens_d,
-                              y=y_dec, workspace=ws_dec)
+        if args.only != "decode":
+            m.mla_set_stage_events([e.cuda_event for e in pe] if pe else None)
+            m.mla_prefill_forward(cfg_pre, wd_pre, xd_pre, y=y_pre, latent_out=lat_pre,
+                                  workspace=ws_pre)
+        if args.only != "prefill":
+            m.mla_set_stage_events([e.cuda_event for e in de] if de else None)
+            m.mla_decode_absorbed(cfg_dec, wdec_d, xdec_d, caches[i % len(caches)], lens_d,
+                                  y=y_dec, workspace=ws_dec)
         m.mla_set_stage_events(None)
 
     log(f"bench: warmup {args.warmup} steps")
@@ -182,6 +187,13 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+    if args.only:
+        log(f"bench: {args.only} only, {total_ms / args.steps:.3f} ms per step")
+        evs, names = (pev, m.PREFILL_STAGES) if args.only == "prefill" else (dev_, m.DECODE_STAGES)
+        for k, n in enumerate(names):
+            t = sum(e[k].elapsed_time(e[k + 1]) for e in evs) / len(evs)
+            log(f"bench:   {n:18s} {t * 1e3:9.1f} us")
+        return
 
     def stage_ms(evs, names):
         per = {n: [] for n in names}

@@ -20,21 +20,23 @@
 // the flattened rows.  A merge kernel combines the pieces of each sequence
 // with log-sum-exp weights.
 //
-// Inside a workgroup: four waves, 16 heads each, on 16x16x32 MFMAs.  A wave
-// computes S^T = C Q^T (16 cache rows x 16 heads per tile, K = 576), keeps the
-// softmax online per head, and accumulates O^T += C^T P^T with P^T taken from
-// the score accumulators in place.  The C^T operand comes straight from the
-// row-major cache tile through the 16-bit transposing LDS read: within each
-// 16-lane group, lane i receives element i % 4 of the 8-byte chunks
-// addressed by lanes 4e + i / 4 (e = 0..3), so pointing lane s at row
-// j0 + s / 4, column c0 + 4 (s % 4) hands every lane keys j0..j0+3 of its own
-// column c0 + i.  Cache tiles of 32 rows stream through two LDS stages with
-// register prefetch of the tile after next; the running max is kept stale
-// until a score exceeds it by 2^8, so the accumulators are rarely rescaled.
-// Sixteen heads per wave keep the per-lane state (128 accumulators, 72
-// registers of queries) well inside the register file; LDS read bandwidth
-// (about 215 B/clk per CU measured for 16-byte reads) covers the four waves
-// reading every tile.
+// Inside a workgroup: four waves, 32 heads each (one head per lane pair), on
+// 32x32x16 MFMAs.  A wave computes S^T = C Q^T (32 cache rows x 32 heads per
+// tile, K = 576), keeps the softmax online per head, and accumulates
+// O^T += C^T P^T with P^T taken from the score accumulators in place.  The
+// C^T operand comes straight from the row-major cache tile through the 16-bit
+// transposing LDS read: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte chunks addressed by lanes 4e + i / 4 (e = 0..3), so
+// pointing lane s at row j0 + s / 4, column c0 + 4 (s % 4) hands every lane
+// keys j0..j0+3 of its own column c0 + i.  Cache tiles of 32 rows stream
+// through two LDS stages with register prefetch of the tile after next.  The
+// softmax reference max of a sequence piece is the max of its first tile and
+// is never moved, so the 256 accumulators per lane are never rescaled (a
+// rescale would pull them through the vector registers); a score more than
+// 2^64 above the reference makes the piece run again with its true max.  Thirty-two heads per wave keep
+// LDS reads at four per tile per workgroup; to leave room for the 256
+// accumulators, half of the query channels are read from LDS each tile
+// instead of being held in registers.
 
 #include "common.h"
 #include "internal.h"
@@ -42,25 +44,33 @@
 namespace mla {
 namespace {
 
-constexpr int TK = 32;   // cache rows per tile
-constexpr int HPW = 16;  // heads per wave
-constexpr int HPB = 64;  // heads per workgroup
+constexpr int TK = 32;    // cache rows per tile
+constexpr int HPW = 32;   // heads per wave
+constexpr int HPB = 128;  // heads per workgroup
+constexpr int DTHREADS = 256;
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float RESCALE_LOG2 = 8.0f;
+// a segment's reference max is its first tile's max; scores may exceed it
+// by up to 2^64 (exp2 domain) before fp32 sums could overflow
+constexpr float HEADROOM_LOG2 = 64.0f;
 
 template <typename T, int R, int DR>
 struct DecCfg {
-  using MF = Mfma16<T>;
+  using MF = Mfma32<T>;
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int W = R + DR;
   static constexpr int WP = (W + MF::KSTEP - 1) / MF::KSTEP * MF::KSTEP;
-  static constexpr int RP = (R + 15) / 16 * 16;
+  static constexpr int RP = (R + 31) / 32 * 32;
   static constexpr int CPITCH = (WP > RP ? WP : RP) + VEC;  // 1168 B at V3 sizes
   static constexpr int STAGE = TK * CPITCH;
   static constexpr int NQF = WP / MF::KSTEP;
-  static constexpr int NCT = RP / 16;
-  static constexpr int CPR = W / VEC;                 // 16-byte chunks per cache row
-  static constexpr int NCH = (TK * CPR + 255) / 256;  // staging chunks per thread
+  // the first NQR query fragments live in registers, the rest in LDS
+  static constexpr int NQR = NQF > 16 ? 16 : NQF;
+  static constexpr int NQL = NQF - NQR;
+  static constexpr int QPITCH = NQL * MF::KSTEP + VEC;
+  static constexpr int NCT = RP / 32;
+  static constexpr int CPR = W / VEC;            // 16-byte chunks per cache row
+  // staging: thread t owns row t / 8 of the tile and chunks t % 8 + 8 i
+  static constexpr int NCH = (CPR + 7) / 8;
 };
 
 // Rows of sequence b in the flattened order: lens[b] + 1 for a valid length.
@@ -72,16 +82,18 @@ __device__ inline int seq_rows(const int32_t *lens, int b, int64_t cap) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T, int R, int DR>
-__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
+__global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a) {
   using C = DecCfg<T, R, DR>;
   using MF = typename C::MF;
   constexpr int VEC = C::VEC, W = C::W, CPITCH = C::CPITCH, STAGE = C::STAGE, NQF = C::NQF,
-                NCT = C::NCT, CPR = C::CPR, NCH = C::NCH;
+                NQR = C::NQR, NQL = C::NQL, QPITCH = C::QPITCH, NCT = C::NCT, CPR = C::CPR,
+                NCH = C::NCH;
   __shared__ __attribute__((aligned(16))) T Cs[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) T Qs[NQL > 0 ? HPB * QPITCH : VEC];
   extern __shared__ int starts[];  // [B + 1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = lane >> 4, l16 = lane & 15;
+  const int g = lane >> 5, l32 = lane & 31;
   const int B = a.B, H = a.H;
   const int n_hg = (H + HPB - 1) / HPB;
   // workgroup -> (range, head group); head groups of one range share an XCD
@@ -94,11 +106,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
     hg = blockIdx.x % n_hg;
     blk = blockIdx.x / n_hg;
   }
-  const int h = hg * HPB + wave * HPW + l16;
+  const int h = hg * HPB + wave * HPW + l32;
   const bool wave_live = hg * HPB + wave * HPW < H;
 
   // prefix sums of per-sequence row counts
-  for (int b = tid; b < B; b += 256) starts[b + 1] = seq_rows(a.lens, b, a.cap);
+  for (int b = tid; b < B; b += DTHREADS) starts[b + 1] = seq_rows(a.lens, b, a.cap);
   __syncthreads();
   if (wave == 0) {
     int carry = 0;
@@ -125,37 +137,34 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
   while (starts[b + 1] <= r0) ++b;  // first sequence holding row r0
 
   if constexpr (CPITCH - VEC > W) {
-    // columns past the row width feed only products with zero queries or
-    // output channels >= R; keep them finite
-    for (int i = tid; i < 2 * TK; i += 256)
+    // columns past the row width meet zero queries or feed output channels
+    // >= R (never stored); keep them finite
+    for (int i = tid; i < 2 * TK; i += DTHREADS)
       for (int c = W; c < CPITCH; ++c) Cs[(i / TK) * STAGE + (i % TK) * CPITCH + c] = from_f32<T>(0.f);
   }
   const float sl2 = a.scale * LOG2E;
   const T *cache = reinterpret_cast<const T *>(a.cache);
 
+  // staging: one row slice per thread, so every chunk address is a common
+  // base plus an immediate offset
+  static_assert(TK * 8 == DTHREADS, "staging map needs 8 threads per tile row");
+  const int srow = tid >> 3, sc8 = tid & 7;
   uint4 rc[NCH];
 #define DEC_FETCH(T0)                                                                \
   do {                                                                               \
-    const int t0_ = (T0);                                                            \
+    const bool ok_ = (T0) + srow < t_end;                                            \
+    const T *src_ = cb + (int64_t)((T0) + srow) * W + sc8 * VEC;                     \
     _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                \
-      const int c = tid + 256 * i;                                                   \
-      const int jr = c / CPR, cc = (c - jr * CPR) * VEC;                             \
       uint4 v = make_uint4(0, 0, 0, 0);                                              \
-      if (c < TK * CPR && t0_ + jr < t_end)                                          \
-        v = *reinterpret_cast<const uint4 *>(cb + (int64_t)(t0_ + jr) * W + cc);     \
+      if (ok_ && sc8 + 8 * i < CPR) v = *reinterpret_cast<const uint4 *>(src_ + 8 * i * VEC); \
       rc[i] = v;                                                                     \
     }                                                                                \
   } while (0)
 #define DEC_STASH(STG)                                                               \
   do {                                                                               \
-    T *cs_ = Cs + (STG) * STAGE;                                                     \
-    _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                \
-      const int c = tid + 256 * i;                                                   \
-      if (c < TK * CPR) {                                                            \
-        const int jr = c / CPR, cc = (c - jr * CPR) * VEC;                           \
-        *reinterpret_cast<uint4 *>(&cs_[jr * CPITCH + cc]) = rc[i];                  \
-      }                                                                              \
-    }                                                                                \
+    T *dst_ = Cs + (STG) * STAGE + srow * CPITCH + sc8 * VEC;                        \
+    _Pragma("unroll") for (int i = 0; i < NCH; ++i)                                  \
+      if (sc8 + 8 * i < CPR) *reinterpret_cast<uint4 *>(dst_ + 8 * i * VEC) = rc[i];  \
   } while (0)
 
   while (r0 < r1) {
@@ -163,12 +172,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
     const int t_begin = r0 - starts[b], t_end = seg_end - starts[b];
     const T *cb = cache + (int64_t)b * a.cap * W;
 
-    // B operand of S^T = C Q^T: lane holds head l16, k values q*KPL.. of each step
-    typename MF::frag qf[NQF];
+    // B operand of S^T = C Q^T: lane holds head l32, k values g*KPL.. of a step
+    typename MF::frag qf[NQR];
     const T *qp = reinterpret_cast<const T *>(a.q_lat) + ((int64_t)b * H + h) * W;
 #pragma unroll
-    for (int f = 0; f < NQF; ++f) {
-      const int c = f * MF::KSTEP + q * MF::KPL;
+    for (int f = 0; f < NQR; ++f) {
+      const int c = f * MF::KSTEP + g * MF::KPL;
       if constexpr (MF::KPL == 1) {
         qf[f] = (h < H && c < W) ? to_f32(qp[c]) : 0.f;
       } else {
@@ -181,15 +190,39 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
         }
       }
     }
-    f32x4 o[NCT];
+    f32x16 o[NCT];
+    float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
+    bool ovf = false;
+    const int ntiles = (t_end - t_begin + TK - 1) / TK;
+    // The softmax reference max is fixed at the first tile, so the
+    // accumulators are never rescaled inside the loop (they stay in the MFMA
+    // accumulation registers).  A score more than 2^64 above it sets ovf and
+    // the segment is run a second time with the true max, known by then.
+    for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+      if (!__syncthreads_or(ovf)) break;
+      m_ref = m_true;
+      ovf = false;
+    }
 #pragma unroll
     for (int d = 0; d < NCT; ++d)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[d][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-
-    const int ntiles = (t_end - t_begin + TK - 1) / TK;
-    __syncthreads();  // the previous segment's last tile is fully consumed
+      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    l_run = 0.f;
+    __syncthreads();  // the previous segment's tiles and queries are consumed
+    if constexpr (NQL > 0) {
+      // query channels NQR*KSTEP.. of this workgroup's heads
+      constexpr int QCH = NQL * MF::KSTEP / VEC;
+      for (int i = tid; i < HPB * QCH; i += DTHREADS) {
+        const int hh = i / QCH, cc = (i - hh * QCH) * VEC;
+        const int hq = hg * HPB + hh;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (hq < H && NQR * MF::KSTEP + cc < W)
+          v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(a.q_lat) +
+                                               ((int64_t)b * H + hq) * W + NQR * MF::KSTEP + cc);
+        *reinterpret_cast<uint4 *>(&Qs[hh * QPITCH + cc]) = v;
+      }
+    }
     DEC_FETCH(t_begin);
     DEC_STASH(0);
     if (ntiles > 1) DEC_FETCH(t_begin + TK);
@@ -198,78 +231,103 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
       const int t0 = t_begin + it * TK;
       const T *cs = Cs + (it & 1) * STAGE;
       if (wave_live) {
-        // S^T for keys 0..15 (s0) and 16..31 (s1) of the tile: lane holds keys
-        // q*4 + r (+16), head l16
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        // S^T = C Q^T; fragment reads run two MFMAs ahead (the fences keep
+        // the compiler from hoisting all of them)
+        f32x16 st;
 #pragma unroll
-        for (int f = 0; f < NQF; ++f) {
-          const int c = f * MF::KSTEP + q * MF::KPL;
-          typename MF::frag k0, k1;
-          if constexpr (MF::KPL == 1) {
-            k0 = to_f32(cs[l16 * CPITCH + c]);
-            k1 = to_f32(cs[(16 + l16) * CPITCH + c]);
-          } else {
-            k0 = *reinterpret_cast<const typename MF::frag *>(&cs[l16 * CPITCH + c]);
-            k1 = *reinterpret_cast<const typename MF::frag *>(&cs[(16 + l16) * CPITCH + c]);
-          }
-          s0 = MF::mma(k0, qf[f], s0);
-          s1 = MF::mma(k1, qf[f], s1);
+        for (int r = 0; r < 16; ++r) st[r] = 0.f;
+        typename MF::frag ka[2], qa[2], kb[2], qb[2];
+#define DEC_KLOAD(KA, QA, F0)                                                         \
+  _Pragma("unroll") for (int e = 0; e < 2; ++e) {                                     \
+    const int f_ = (F0) + e;                                                          \
+    if (f_ < NQF) {                                                                   \
+      const int c_ = f_ * MF::KSTEP + g * MF::KPL;                                    \
+      if constexpr (MF::KPL == 1) {                                                   \
+        KA[e] = to_f32(cs[l32 * CPITCH + c_]);                                        \
+        if (f_ >= NQR) QA[e] = to_f32(Qs[(wave * HPW + l32) * QPITCH + c_ - NQR * MF::KSTEP]); \
+      } else {                                                                        \
+        KA[e] = *reinterpret_cast<const typename MF::frag *>(&cs[l32 * CPITCH + c_]); \
+        if (f_ >= NQR)                                                                \
+          QA[e] = *reinterpret_cast<const typename MF::frag *>(                       \
+              &Qs[(wave * HPW + l32) * QPITCH + c_ - NQR * MF::KSTEP]);               \
+      }                                                                               \
+    }                                                                                 \
+  }
+#define DEC_KMMA(KA, QA, F0)                                                          \
+  _Pragma("unroll") for (int e = 0; e < 2; ++e) {                                     \
+    const int f_ = (F0) + e;                                                          \
+    if (f_ < NQF) st = MF::mma(KA[e], f_ < NQR ? qf[f_ < NQR ? f_ : 0] : QA[e], st);  \
+  }
+        DEC_KLOAD(ka, qa, 0)
+#pragma unroll
+        for (int f0 = 0; f0 < NQF; f0 += 4) {
+          DEC_KLOAD(kb, qb, f0 + 2)
+          __builtin_amdgcn_sched_barrier(0);
+          DEC_KMMA(ka, qa, f0)
+          __builtin_amdgcn_sched_barrier(0);
+          DEC_KLOAD(ka, qa, f0 + 4)
+          __builtin_amdgcn_sched_barrier(0);
+          DEC_KMMA(kb, qb, f0 + 2)
+          __builtin_amdgcn_sched_barrier(0);
         }
+#undef DEC_KLOAD
+#undef DEC_KMMA
         if (t0 + TK > t_end) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (t0 + q * 4 + r >= t_end) s0[r] = -INFINITY;
-            if (t0 + 16 + q * 4 + r >= t_end) s1[r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (t0 + acc_row(r, lane) >= t_end) st[r] = -INFINITY;
         }
-        float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        float mx = st[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool need =
-            mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
-        if (__any(need)) {
-          const float alpha = need ? exp2f((m_run - mx) * sl2) : 1.0f;
-          if (need) m_run = mx;
-          l_run *= alpha;
+        m_true = fmaxf(m_true, mx);
+        if (m_ref == -INFINITY) m_ref = mx;  // first tile of the segment
+        if ((mx - m_ref) * sl2 > HEADROOM_LOG2) ovf = true;
+        const float neg = -m_ref * sl2;
 #pragma unroll
-          for (int d = 0; d < NCT; ++d) o[d] *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, neg));
+          l_run += st[r];
         }
-        const float neg = m_run == -INFINITY ? 0.f : -m_run * sl2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s0[r] = exp2f(fmaf(s0[r], sl2, neg));
-          s1[r] = exp2f(fmaf(s1[r], sl2, neg));
-          l_run += s0[r] + s1[r];
-        }
-        // O^T += C^T P^T: for bf16 one MFMA per 16 latent channels covers all
-        // 32 keys; k slots 0..3 are keys q*4 + e, slots 4..7 keys 16 + q*4 + e
+        // O^T += C^T P^T
         if constexpr (MF::KPL == 1) {
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float pf = t < 4 ? s0[t] : s1[t - 4];
-            const int key = (t < 4 ? 0 : 16) + q * 4 + (t & 3);
+          for (int t = 0; t < 16; ++t)
 #pragma unroll
             for (int d = 0; d < NCT; ++d)
-              o[d] = MF::mma(to_f32(cs[key * CPITCH + d * 16 + l16]), pf, o[d]);
-          }
+              o[d] = MF::mma(to_f32(cs[acc_row(t, lane) * CPITCH + d * 32 + l32]), st[t], o[d]);
         } else {
-          typename MF::frag pf;
+          // k slots e of MFMA u: keys 16u + (e/4)*8 + 4g + e%4, matching the
+          // score accumulator layout
+          const int s16 = lane & 15;
+          const T *pb0 = &cs[(4 * g + (s16 >> 2)) * CPITCH + (lane & 16) + 4 * (s16 & 3)];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pf[e] = from_f32<T>(s0[e]);
-            pf[4 + e] = from_f32<T>(s1[e]);
-          }
-          const T *pbase = &cs[(q * 4 + (l16 >> 2)) * CPITCH + 4 * (l16 & 3)];
+          for (int u = 0; u < 2; ++u) {
+            typename MF::frag pf;
 #pragma unroll
-          for (int d = 0; d < NCT; ++d) {
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(pbase + d * 16));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(pbase + 16 * CPITCH + d * 16));
-            const typename MF::frag vf = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[d] = MF::mma(vf, pf, o[d]);
+            for (int e = 0; e < 8; ++e) pf[e] = from_f32<T>(st[u * 8 + e]);
+            typename MF::frag vf[NCT];
+#define DEC_VLOAD(D)                                                                    \
+  if ((D) < NCT) {                                                                      \
+    const T *p_ = pb0 + u * 16 * CPITCH + (D) * 32;                                     \
+    const s16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                          \
+        (__attribute__((address_space(3))) s16x4 *)(p_));                               \
+    const s16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                          \
+        (__attribute__((address_space(3))) s16x4 *)(p_ + 8 * CPITCH));                  \
+    vf[(D) < NCT ? (D) : 0] =                                                           \
+        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7)); \
+  }
+            DEC_VLOAD(0)
+            DEC_VLOAD(1)
+#pragma unroll
+            for (int d = 0; d < NCT; ++d) {
+              DEC_VLOAD(d + 2)
+              __builtin_amdgcn_sched_barrier(0);
+              o[d] = MF::mma(vf[d], pf, o[d]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+#undef DEC_VLOAD
           }
         }
       }
@@ -279,21 +337,26 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
       }
       __syncthreads();
     }
+    }  // pass
 
     // partial of this sequence piece: unnormalised o_lat (log2-domain max, sum)
     if (wave_live) {
-      float l_tot = l_run + __shfl_xor(l_run, 16);
-      l_tot += __shfl_xor(l_tot, 32);
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
       if (h < H) {
         const int slot = blk + b;
         float *po = a.part_o + ((int64_t)slot * H + h) * R;
 #pragma unroll
-        for (int d = 0; d < NCT; ++d) {
-          const int c = d * 16 + q * 4;
-          if (c + 4 <= R) *reinterpret_cast<f32x4 *>(po + c) = o[d];
-        }
-        if (q == 0) {
-          a.part_ml[((int64_t)slot * H + h) * 2 + 0] = m_run * sl2;
+        for (int d = 0; d < NCT; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; r += 4) {
+            const int c = d * 32 + acc_row(r, lane);
+            if (c + 4 <= R) {
+              f32x4 v = {o[d][r], o[d][r + 1], o[d][r + 2], o[d][r + 3]};
+              *reinterpret_cast<f32x4 *>(po + c) = v;
+            }
+          }
+        if (g == 0) {
+          a.part_ml[((int64_t)slot * H + h) * 2 + 0] = m_ref * sl2;
           a.part_ml[((int64_t)slot * H + h) * 2 + 1] = l_tot;
         }
       }
@@ -371,7 +434,7 @@ template <typename T, int R, int DR>
 hipError_t launch_t(const DecodeAttnArgs &a, hipStream_t st) {
   dim3 grid(a.n_blocks * ((a.H + HPB - 1) / HPB));
   size_t shm = (size_t)(a.B + 1) * sizeof(int);
-  hipLaunchKernelGGL((decode_attn_kernel<T, R, DR>), grid, dim3(256), shm, st, a);
+  hipLaunchKernelGGL((decode_attn_kernel<T, R, DR>), grid, dim3(DTHREADS), shm, st, a);
   return hipGetLastError();
 }
 
@@ -384,7 +447,7 @@ hipError_t launch_merge_t(const DecodeAttnArgs &a, hipStream_t st) {
 
 }  // namespace
 
-int decode_blocks() { return 128; }
+int decode_blocks() { return 256; }
 
 hipError_t launch_decode_attention(int dtype, int r, int dr, const DecodeAttnArgs &a,
                                    hipStream_t st) {
@@ -394,7 +457,9 @@ hipError_t launch_decode_attention(int dtype, int r, int dr, const DecodeAttnArg
     return dtype == BF16 ? launch_t<bf16, R_, DR_>(a, st) : launch_t<float, R_, DR_>(a, st);
   MLA_DEC_CASE(16, 8)
   MLA_DEC_CASE(128, 32)
-  MLA_DEC_CASE(512, 64)
+  // fp32 at the V3 latent width would need more LDS than a CU has; the host
+  // rejects it before launching
+  if (r == 512 && dr == 64 && dtype == BF16) return launch_t<bf16, 512, 64>(a, st);
 #undef MLA_DEC_CASE
   return hipErrorInvalidValue;
 }
@@ -405,7 +470,7 @@ hipError_t launch_decode_merge(int dtype, int r, const DecodeAttnArgs &a, hipStr
   if (r == R_) return dtype == BF16 ? launch_merge_t<bf16, R_>(a, st) : launch_merge_t<float, R_>(a, st);
   MLA_MERGE_CASE(16)
   MLA_MERGE_CASE(128)
-  MLA_MERGE_CASE(512)
+  if (r == 512 && dtype == BF16) return launch_merge_t<bf16, 512>(a, st);
 #undef MLA_MERGE_CASE
   return hipErrorInvalidValue;
 }

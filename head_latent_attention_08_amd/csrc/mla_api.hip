@@ -136,7 +136,8 @@ bool prefill_instance(const mla_config &c) {
 
 bool decode_instance(const mla_config &c) {
   const int r = c.kv_lora_rank, dr = c.qk_rope_head_dim;
-  return (r == 16 && dr == 8) || (r == 128 && dr == 32) || (r == 512 && dr == 64);
+  return (r == 16 && dr == 8) || (r == 128 && dr == 32) ||
+         (r == 512 && dr == 64 && c.dtype == MLA_DTYPE_BF16);
 }
 
 mla_status check_config(const mla_config *c) {
@@ -257,8 +258,8 @@ mla_status check_decode_sizes(const mla_config *cfg, int64_t B, int64_t cap) {
     return fail(MLA_ERR_INVALID_ARGUMENT, "batch x cache_capacity is too large");
   if (!decode_instance(*cfg))
     return fail(MLA_ERR_UNSUPPORTED,
-                "(kv_lora_rank %d, rope %d) is not instantiated; supported: (16,8), (128,32), "
-                "(512,64)",
+                "(kv_lora_rank %d, rope %d) is not instantiated for this dtype; supported: "
+                "(16,8), (128,32), and (512,64) in bf16",
                 cfg->kv_lora_rank, cfg->qk_rope_head_dim);
   return MLA_OK;
 }

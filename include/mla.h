@@ -158,7 +158,9 @@ MLA_API mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights 
  *                precondition: a sequence that violates it gets a NaN y row
  *                and no cache write.
  *   y            [B, D]                    device, written
- * Status: as prefill; also INVALID_ARGUMENT for capacity < 1. */
+ * Status: as prefill, except that the instantiated (kv_lora_rank, d_r) pairs
+ * are (16,8), (128,32) and, in bf16 only, (512,64); also INVALID_ARGUMENT for
+ * capacity < 1 or batch > 4096. */
 typedef struct {
   size_t c_q, c_kv, q, q_lat, o_lat, o;   /* see mla_decode_layout_of */
   int64_t ld_down, n_splits, split_len;

@@ -248,3 +248,38 @@ def test_decode_edge_lengths():
     assert_close_rows(yn[ok], ref, "bf16", "y")
     assert np.all(np.isnan(yn[3]))
     np.testing.assert_array_equal(to_np(cache_d)[3], cache[3].astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_score_range_beyond_first_tile(dtype):
+    # cache rows after the first tile are scaled up so their scores exceed
+    # the first tile's max by far more than fp32 exp headroom: the decode
+    # kernel must notice and redo the piece with the true max
+    m = _m()
+    c = shrink(si.CONFIGS["small"], dtype=dtype)
+    B, cap = 3, 400
+    x, w, lens, cache = si.make_decode_inputs(c, batch=B, capacity=cap, len_lo=200, len_hi=390,
+                                              gains="random", seed=6100)
+    w["w_up_k"] = si._store(w["w_up_k"] * 40.0, dtype)
+    cache = cache.copy()
+    cache[:, 100:] = si._store(cache[:, 100:] * 8.0, dtype)
+    cfg = mla_cfg(c)
+    ocfg = oracle_cfg(c)
+    cache_d = to_dev(cache, dtype)
+    y, _ = m.mla_decode_absorbed(cfg, weights_to_dev(w, dtype), to_dev(x, dtype), cache_d,
+                                 torch.from_numpy(lens).cuda(),
+                                 workspace=_poisoned(m.mla_decode_workspace_size(cfg, B, cap)))
+    torch.cuda.synchronize()
+    ref, _ = orc.mla_decode_absorbed(ocfg, w, x, cache, lens)
+    # the logit range really spans more than the kernel's headroom
+    q_lat = orc.mla_decode_absorbed(ocfg, w, x, cache, lens, want_intermediates=True)[2]["q_lat"]
+    s0 = np.einsum("hr,tr->ht", q_lat[0], cache[0, :32, :128].astype(np.float64))
+    s1 = np.einsum("hr,tr->ht", q_lat[0], cache[0, 100:lens[0], :128].astype(np.float64))
+    scale = orc.softmax_scale(ocfg)
+    assert (s1.max() - s0.max()) * scale / np.log(2) > 64
+    if dtype == "fp32":
+        assert_close_rows(to_np(y), ref, "fp32", "y")
+    else:
+        rel, ab = row_errors(to_np(y), ref)
+        # sharp softmax: bf16 logit rounding moves probabilities (relative bound only)
+        assert np.isfinite(to_np(y)).all() and rel.max() <= 5e-2, rel.max()
