@@ -407,26 +407,28 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
   }
   const int per = (total + a.n_blocks - 1) / a.n_blocks;
   const int i0 = start / per, i1 = (start + n_b - 1) / per;
-  for (int hh = 0; hh < MERGE_HEADS; ++hh) {
-    const int h = h0 + hh;
-    if (h >= a.H) break;
-    float M = -INFINITY;
-    for (int i = i0; i <= i1; ++i) M = fmaxf(M, a.part_ml[((int64_t)(i + b) * a.H + h) * 2]);
-    float L = 0.f;
+  // 32 threads per head; each thread owns channels 4 t + 128 j
+  const int hh = tid >> 5, ln = tid & 31;
+  const int h = h0 + hh;
+  if (h >= a.H) return;
+  float M = -INFINITY;
+  for (int i = i0; i <= i1; ++i) M = fmaxf(M, a.part_ml[((int64_t)(i + b) * a.H + h) * 2]);
+  float L = 0.f;
+  for (int i = i0; i <= i1; ++i) {
+    const float *ml = a.part_ml + ((int64_t)(i + b) * a.H + h) * 2;
+    L += exp2f(ml[0] - M) * ml[1];
+  }
+  const float invL = 1.0f / L;
+  T *out = reinterpret_cast<T *>(a.o_lat) + ((int64_t)b * a.H + h) * R;
+  for (int c = ln * 4; c < R; c += 128) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int i = i0; i <= i1; ++i) {
-      const float *ml = a.part_ml + ((int64_t)(i + b) * a.H + h) * 2;
-      L += exp2f(ml[0] - M) * ml[1];
+      const float w = exp2f(a.part_ml[((int64_t)(i + b) * a.H + h) * 2] - M) * invL;
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(a.part_o + ((int64_t)(i + b) * a.H + h) * R + c);
+      acc += w * v;
     }
-    const float invL = 1.0f / L;
-    T *out = reinterpret_cast<T *>(a.o_lat) + ((int64_t)b * a.H + h) * R;
-    for (int c = tid; c < R; c += 256) {
-      float acc = 0.f;
-      for (int i = i0; i <= i1; ++i) {
-        const float w = exp2f(a.part_ml[((int64_t)(i + b) * a.H + h) * 2] - M);
-        acc += w * a.part_o[((int64_t)(i + b) * a.H + h) * R + c];
-      }
-      out[c] = from_f32<T>(acc * invL);
-    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[c + e] = from_f32<T>(acc[e]);
   }
 }
 

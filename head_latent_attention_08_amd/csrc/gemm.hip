@@ -397,7 +397,146 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny bf16 kernel for decode (M <= 64 rows, weights streamed once).
+//
+// With one token per sequence the projections are weight-bandwidth bound:
+// every weight element is used by at most 64 rows.  A 256-thread workgroup
+// owns a 64x128 output tile and one K slice; the grid covers the N tiles times
+// a split of K chosen on the host so about two workgroups per CU stream
+// weights at once.  Slices write fp32 partial tiles; a second kernel adds the
+// slices in a fixed order (deterministic) and applies the column-range store
+// mapping.  Operand chunks of 64 k values go through two LDS stages with
+// register prefetch of the next chunk.
+constexpr int SK_M = 64, SK_N = 128, SK_K = 64, SK_PITCH = SK_K + 8;
+
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, float *part, int kslice) {
+  __shared__ __attribute__((aligned(16))) bf16 As[2][SK_M * SK_PITCH];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][SK_N * SK_PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int n0 = blockIdx.x * SK_N, ks = blockIdx.y, z = blockIdx.z;
+  const int k_begin = ks * kslice;
+  const int nk = kslice / SK_K;
+  const bf16 *A = reinterpret_cast<const bf16 *>(p.A) + (int64_t)z * p.strideA;
+  // B rows: column ranges start at multiples of 128 (checked on the host)
+  const int st = seg_of(p, n0);
+  const int t_nb = SEG_FIELD(p, st, n_begin);
+  const int64_t t_ldb = SEG_FIELD(p, st, ldb);
+  const bf16 *Bb = reinterpret_cast<const bf16 *>(SEG_FIELD(p, st, B)) + (int64_t)z * p.strideB;
+
+  // staging: A rows tid/8 (+32), B rows tid/8 (+32, +64, +96); chunk tid%8
+  const int sr = tid >> 3, sc = (tid & 7) * 8;
+  const bf16 *pa0 = A + (int64_t)min(sr, p.M - 1) * p.lda + k_begin + sc;
+  const bf16 *pa1 = A + (int64_t)min(sr + 32, p.M - 1) * p.lda + k_begin + sc;
+  const bf16 *pb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    pb[i] = Bb + (int64_t)(min(n0 + sr + 32 * i, p.N - 1) - t_nb) * t_ldb + k_begin + sc;
+  uint4 ra0, ra1, rb0, rb1, rb2, rb3;
+#define SK_FETCH(KK)                                                                  \
+  do {                                                                                \
+    const int k_ = (KK);                                                              \
+    ra0 = *reinterpret_cast<const uint4 *>(pa0 + k_);                                 \
+    ra1 = *reinterpret_cast<const uint4 *>(pa1 + k_);                                 \
+    rb0 = *reinterpret_cast<const uint4 *>(pb[0] + k_);                               \
+    rb1 = *reinterpret_cast<const uint4 *>(pb[1] + k_);                               \
+    rb2 = *reinterpret_cast<const uint4 *>(pb[2] + k_);                               \
+    rb3 = *reinterpret_cast<const uint4 *>(pb[3] + k_);                               \
+  } while (0)
+#define SK_STASH(BUF)                                                                 \
+  do {                                                                                \
+    *reinterpret_cast<uint4 *>(&As[BUF][sr * SK_PITCH + sc]) = ra0;                   \
+    *reinterpret_cast<uint4 *>(&As[BUF][(sr + 32) * SK_PITCH + sc]) = ra1;            \
+    *reinterpret_cast<uint4 *>(&Bs[BUF][sr * SK_PITCH + sc]) = rb0;                   \
+    *reinterpret_cast<uint4 *>(&Bs[BUF][(sr + 32) * SK_PITCH + sc]) = rb1;            \
+    *reinterpret_cast<uint4 *>(&Bs[BUF][(sr + 64) * SK_PITCH + sc]) = rb2;            \
+    *reinterpret_cast<uint4 *>(&Bs[BUF][(sr + 96) * SK_PITCH + sc]) = rb3;            \
+  } while (0)
+
+  // wave tile: rows (wave / 2) * 32, columns (wave % 2) * 64 (two 32x32 tiles)
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+
+  SK_FETCH(0);
+  SK_STASH(0);
+  if (nk > 1) SK_FETCH(SK_K);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+#pragma unroll
+    for (int kk = 0; kk < SK_K; kk += 16) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[buf][(wm * 32 + l32) * SK_PITCH + kk + g * 8]);
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&Bs[buf][(wn * 64 + l32) * SK_PITCH + kk + g * 8]);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(&Bs[buf][(wn * 64 + 32 + l32) * SK_PITCH + kk + g * 8]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      SK_STASH(buf ^ 1);
+      if (kt + 2 < nk) SK_FETCH((kt + 2) * SK_K);
+    }
+    __syncthreads();
+  }
+#undef SK_FETCH
+#undef SK_STASH
+  // fp32 partial tile [z][ks][M][N]
+  float *pt = part + (((int64_t)z * gridDim.y + ks) * p.M) * p.N;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = wm * 32 + acc_row(r, lane);
+    const int n = n0 + wn * 64 + l32;
+    if (m < p.M) {
+      if (n < p.N) pt[(int64_t)m * p.N + n] = acc0[r];
+      if (n + 32 < p.N) pt[(int64_t)m * p.N + n + 32] = acc1[r];
+    }
+  }
+}
+
+// Sum the K slices in order and store through the column-range mapping.
+__global__ __launch_bounds__(256) void gemm_skinny_reduce(GemmParams p, const float *part,
+                                                          int nsplit) {
+  const int z = blockIdx.y;
+  const int64_t total = (int64_t)p.M * p.N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int m = (int)(i / p.N), n = (int)(i - (int64_t)m * p.N);
+    const float *src = part + (int64_t)z * nsplit * total + i;
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) acc += src[(int64_t)s * total];
+    const int st = seg_of(p, n);
+    const int nn = n - SEG_FIELD(p, st, n_begin);
+    const int dh = SEG_FIELD(p, st, dh);
+    const int h = nn / dh, d = nn - h * dh;
+    const int b = m / p.S, sq = m - b * p.S;
+    bf16 *C = reinterpret_cast<bf16 *>(SEG_FIELD(p, st, C)) + (int64_t)z * p.strideC;
+    const int64_t at = SEG_FIELD(p, st, tr)
+                           ? ((int64_t)(b * p.H + h) * dh + d) * p.S + sq
+                           : ((int64_t)(b * p.H + h) * p.S + sq) * SEG_FIELD(p, st, ld) +
+                                 SEG_FIELD(p, st, off) + d;
+    C[at] = (bf16)acc;
+  }
+}
+
 }  // namespace
+
+// Split of K the skinny kernel uses for an M <= 64 product: the largest
+// divisor of K/64 that keeps the grid near 512 workgroups.
+static int skinny_split(int N, int K, int batch) {
+  const int ntile = (N + SK_N - 1) / SK_N;
+  const int kchunks = K / SK_K;
+  const int want = (512 + ntile * batch - 1) / (ntile * batch);
+  int nsplit = 1;
+  for (int c = 1; c <= kchunks; ++c)
+    if (kchunks % c == 0 && c <= want) nsplit = c;
+  return nsplit;
+}
+
+size_t gemm_scratch_bytes(int dtype, int M, int N, int K, int batch) {
+  if (dtype != BF16 || M > SK_M || K % SK_K != 0) return 0;
+  return (size_t)skinny_split(N, K, batch) * batch * M * N * sizeof(float);
+}
 
 hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   if (d.M <= 0 || d.N <= 0 || d.K <= 0 || d.batch <= 0) return hipSuccess;
@@ -424,6 +563,25 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
     hipLaunchKernelGGL(gemm_big_kernel, dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn,
                        (T % 8 == 0) ? 1 : 0);
     return hipGetLastError();
+  }
+  bool skinny = d.dtype == BF16 && !d.b_kn && d.M <= SK_M && d.K % SK_K == 0 && d.N % 8 == 0 &&
+                d.workspace != nullptr;
+  for (int i = 0; i < d.nseg && skinny; ++i) skinny = d.seg[i].n_begin % SK_N == 0;
+  if (skinny) {
+    const int ntile = (d.N + SK_N - 1) / SK_N;
+    int nsplit = skinny_split(d.N, d.K, d.batch);
+    if ((size_t)nsplit * d.batch * d.M * d.N * sizeof(float) > d.workspace_bytes) nsplit = 1;
+    if ((size_t)nsplit * d.batch * d.M * d.N * sizeof(float) <= d.workspace_bytes) {
+      float *part = reinterpret_cast<float *>(d.workspace);
+      hipLaunchKernelGGL(gemm_skinny_kernel, dim3(ntile, nsplit, d.batch), dim3(256), 0, st, p,
+                         part, d.K / nsplit);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t total = (int64_t)d.M * d.N;
+      const unsigned rb = (unsigned)std::min<int64_t>((total + 255) / 256, 2048);
+      hipLaunchKernelGGL(gemm_skinny_reduce, dim3(rb, d.batch), dim3(256), 0, st, p, part, nsplit);
+      return hipGetLastError();
+    }
   }
   dim3 grid((d.N + BN - 1) / BN, (d.M + BM - 1) / BM, d.batch);
   dim3 block(256);

@@ -40,9 +40,17 @@ struct GemmDesc {
   int S = 1, H = 1;
   int nseg = 1;
   GemmSeg seg[3];
+  // optional fp32 scratch for split-K partial tiles (decode-sized M); when
+  // NULL or too small the kernels run without splitting K
+  void *workspace = nullptr;
+  size_t workspace_bytes = 0;
 };
 
 hipError_t launch_gemm(const GemmDesc &d, hipStream_t st);
+
+// Scratch bytes launch_gemm can use for split-K partials of an M x N x K
+// product (0 when it never splits).
+size_t gemm_scratch_bytes(int dtype, int M, int N, int K, int batch);
 
 // In-place RMSNorm of n columns of `rows` rows with pitch ld: x * (mean(x^2)
 // + eps)^-1/2 * g, fp32 reduction.

@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <string>
 
 #include "../../include/mla.h"
@@ -208,7 +209,7 @@ PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S) {
 struct DecodePlan {
   int64_t ld_down;
   int n_blocks;
-  size_t off_down, off_qn, off_qlat, off_po, off_pml, off_olat, off_o, total;
+  size_t off_down, off_qn, off_qlat, off_po, off_pml, off_olat, off_o, off_gemm, gemm_bytes, total;
 };
 
 DecodePlan plan_decode(const mla_config &c, int64_t B) {
@@ -230,6 +231,14 @@ DecodePlan plan_decode(const mla_config &c, int64_t B) {
   p.off_pml = take((size_t)(p.n_blocks + B) * H * 2 * sizeof(float));
   p.off_olat = take((size_t)B * H * r * es);
   p.off_o = take((size_t)B * H * c.v_head_dim * es);
+  // split-K partials of the weight-streaming projections (largest of the four)
+  const int D = c.hidden_size, rq = c.q_lora_rank, dn = c.qk_nope_head_dim, dv = c.v_head_dim;
+  size_t gb = gemm_scratch_bytes(c.dtype, (int)B, rq + (int)r + (int)dr, D, 1);
+  gb = std::max(gb, gemm_scratch_bytes(c.dtype, (int)B, (int)H * (dn + (int)dr), rq, 1));
+  gb = std::max(gb, gemm_scratch_bytes(c.dtype, (int)B, dv, (int)r, (int)H));
+  gb = std::max(gb, gemm_scratch_bytes(c.dtype, (int)B, D, (int)H * dv, 1));
+  p.gemm_bytes = gb;
+  p.off_gemm = take(gb);
   p.total = off;
   return p;
 }
@@ -525,6 +534,8 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
     g.seg[0] = GemmSeg{w->w_down_q, D, 0, down, rq, p.ld_down, 0};
     g.seg[1] = GemmSeg{w->w_down_kv, D, rq, down, rkv, p.ld_down, rq};
     g.seg[2] = GemmSeg{w->w_kr, D, rq + rkv, down, dr, p.ld_down, rq + rkv};
+    g.workspace = ws + p.off_gemm;
+    g.workspace_bytes = p.gemm_bytes;
     MLA_HIP(launch_gemm(g, st), "decode down projection");
   }
   MLA_MARK(1);
@@ -553,6 +564,8 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
     g.nseg = 2;
     g.seg[0] = GemmSeg{w->w_up_q, rq, 0, qn, dn, dn, 0};
     g.seg[1] = GemmSeg{w->w_qr, rq, H * dn, qlat, dr, wl, rkv};
+    g.workspace = ws + p.off_gemm;
+    g.workspace_bytes = p.gemm_bytes;
     MLA_HIP(launch_gemm(g, st), "decode q up-projection");
   }
   MLA_MARK(4);
@@ -617,6 +630,8 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
     g.H = 1;
     g.nseg = 1;
     g.seg[0] = GemmSeg{w->w_up_v, rkv, 0, o, dv, (int64_t)H * dv, 0};
+    g.workspace = ws + p.off_gemm;
+    g.workspace_bytes = p.gemm_bytes;
     MLA_HIP(launch_gemm(g, st), "un-absorb");
   }
   // 7. y = o wo^T
@@ -633,6 +648,8 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
     g.H = 1;
     g.nseg = 1;
     g.seg[0] = GemmSeg{w->wo, (int64_t)H * dv, 0, y, D, D, 0};
+    g.workspace = ws + p.off_gemm;
+    g.workspace_bytes = p.gemm_bytes;
     MLA_HIP(launch_gemm(g, st), "decode output projection");
   }
   MLA_MARK(10);
