@@ -11,10 +11,10 @@
 // Work split: the rows of all sequences (lens[b] + 1 each, the new token
 // included) are laid end to end and cut into n_blocks equal ranges, so long
 // and short sequences load the GPU evenly.  Each range is processed by one
-// workgroup per group of 64 heads; the workgroups of a range are numbered so
-// they land on the same XCD at the same time (workgroup ids go to the eight
-// XCDs round-robin) and the second read of every cache tile hits that XCD's
-// L2.  A range that spans sequence boundaries yields one partial
+// workgroup per group of 128 heads (a single one at 128 heads, so every cache
+// row leaves HBM once); with more head groups the workgroups of a range are
+// numbered so they land on the same XCD (workgroup ids go to the eight XCDs
+// round-robin) and the repeated reads of a cache tile hit that XCD's L2.  A range that spans sequence boundaries yields one partial
 // (unnormalised o_lat, running max, running sum) per sequence piece, in slot
 // (range + b) -- unique because range and sequence indices both rise along
 // the flattened rows.  A merge kernel combines the pieces of each sequence
@@ -29,14 +29,15 @@
 // i % 4 of the 8-byte chunks addressed by lanes 4e + i / 4 (e = 0..3), so
 // pointing lane s at row j0 + s / 4, column c0 + 4 (s % 4) hands every lane
 // keys j0..j0+3 of its own column c0 + i.  Cache tiles of 32 rows stream
-// through two LDS stages with register prefetch of the tile after next.  The
+// from HBM straight into three LDS stages (global_load_lds, 16 bytes a lane,
+// issued two tiles ahead), so no staging registers are needed.  The
 // softmax reference max of a sequence piece is the max of its first tile and
 // is never moved, so the 256 accumulators per lane are never rescaled (a
 // rescale would pull them through the vector registers); a score more than
-// 2^64 above the reference makes the piece run again with its true max.  Thirty-two heads per wave keep
-// LDS reads at four per tile per workgroup; to leave room for the 256
-// accumulators, half of the query channels are read from LDS each tile
-// instead of being held in registers.
+// 2^64 above the reference makes the piece run again with its true max.
+// Thirty-two heads per wave keep LDS reads at four per tile per workgroup;
+// to leave room for the 256 accumulators, the last query channels are read
+// from LDS each tile instead of being held in registers.
 
 #include "common.h"
 #include "internal.h"
@@ -61,17 +62,23 @@ struct DecCfg {
   static constexpr int WP = (W + MF::KSTEP - 1) / MF::KSTEP * MF::KSTEP;
   static constexpr int RP = (R + 31) / 32 * 32;
   static constexpr int CPITCH = (WP > RP ? WP : RP) + VEC;  // 1168 B at V3 sizes
-  static constexpr int STAGE = TK * CPITCH;
+  static constexpr int ROWB = CPITCH * (int)sizeof(T);       // row pitch in bytes
+  // a stage is whole 1 KB blocks: one DMA instruction fills 64 lanes x 16 B
+  static constexpr int NINS = (TK * ROWB + 1023) / 1024;
+  static constexpr int STAGEB = NINS * 1024;
   static constexpr int NQF = WP / MF::KSTEP;
   // the first NQR query fragments live in registers, the rest in LDS
-  static constexpr int NQR = NQF > 16 ? 16 : NQF;
+  static constexpr int NQR = NQF > 26 ? 26 : NQF;
   static constexpr int NQL = NQF - NQR;
   static constexpr int QPITCH = NQL * MF::KSTEP + VEC;
   static constexpr int NCT = RP / 32;
-  static constexpr int CPR = W / VEC;            // 16-byte chunks per cache row
-  // staging: thread t owns row t / 8 of the tile and chunks t % 8 + 8 i
-  static constexpr int NCH = (CPR + 7) / 8;
 };
+
+constexpr int NSTAGE = 3;  // cache tiles in flight: current, next, and the one after
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (gfx9 encoding; expcnt and lgkmcnt left open).
+#define DEC_VMCNT(n) ((((n) & 15)) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
 // Rows of sequence b in the flattened order: lens[b] + 1 for a valid length.
 __device__ inline int seq_rows(const int32_t *lens, int b, int64_t cap) {
@@ -85,14 +92,15 @@ template <typename T, int R, int DR>
 __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a) {
   using C = DecCfg<T, R, DR>;
   using MF = typename C::MF;
-  constexpr int VEC = C::VEC, W = C::W, CPITCH = C::CPITCH, STAGE = C::STAGE, NQF = C::NQF,
-                NQR = C::NQR, NQL = C::NQL, QPITCH = C::QPITCH, NCT = C::NCT, CPR = C::CPR,
-                NCH = C::NCH;
-  __shared__ __attribute__((aligned(16))) T Cs[2 * STAGE];
+  constexpr int VEC = C::VEC, W = C::W, CPITCH = C::CPITCH, ROWB = C::ROWB, NINS = C::NINS,
+                STAGEB = C::STAGEB, NQF = C::NQF, NQR = C::NQR, NQL = C::NQL, QPITCH = C::QPITCH,
+                NCT = C::NCT;
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGEB];
   __shared__ __attribute__((aligned(16))) T Qs[NQL > 0 ? HPB * QPITCH : VEC];
   extern __shared__ int starts[];  // [B + 1]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int B = a.B, H = a.H;
   const int n_hg = (H + HPB - 1) / HPB;
@@ -136,41 +144,49 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
   int b = 0;
   while (starts[b + 1] <= r0) ++b;  // first sequence holding row r0
 
-  if constexpr (CPITCH - VEC > W) {
-    // columns past the row width meet zero queries or feed output channels
-    // >= R (never stored); keep them finite
-    for (int i = tid; i < 2 * TK; i += DTHREADS)
-      for (int c = W; c < CPITCH; ++c) Cs[(i / TK) * STAGE + (i % TK) * CPITCH + c] = from_f32<T>(0.f);
-  }
   const float sl2 = a.scale * LOG2E;
-  const T *cache = reinterpret_cast<const T *>(a.cache);
-
-  // staging: one row slice per thread, so every chunk address is a common
-  // base plus an immediate offset
-  static_assert(TK * 8 == DTHREADS, "staging map needs 8 threads per tile row");
-  const int srow = tid >> 3, sc8 = tid & 7;
-  uint4 rc[NCH];
-#define DEC_FETCH(T0)                                                                \
-  do {                                                                               \
-    const bool ok_ = (T0) + srow < t_end;                                            \
-    const T *src_ = cb + (int64_t)((T0) + srow) * W + sc8 * VEC;                     \
-    _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                \
-      uint4 v = make_uint4(0, 0, 0, 0);                                              \
-      if (ok_ && sc8 + 8 * i < CPR) v = *reinterpret_cast<const uint4 *>(src_ + 8 * i * VEC); \
-      rc[i] = v;                                                                     \
-    }                                                                                \
-  } while (0)
-#define DEC_STASH(STG)                                                               \
-  do {                                                                               \
-    T *dst_ = Cs + (STG) * STAGE + srow * CPITCH + sc8 * VEC;                        \
-    _Pragma("unroll") for (int i = 0; i < NCH; ++i)                                  \
-      if (sc8 + 8 * i < CPR) *reinterpret_cast<uint4 *>(dst_ + 8 * i * VEC) = rc[i];  \
-  } while (0)
+  const char *cache = reinterpret_cast<const char *>(a.cache);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
+  // DMA instructions per tile issued by this wave (instructions wave, wave+4, ..)
+  const int n_dma = (NINS - wave + 3) / 4;
 
   while (r0 < r1) {
     const int seg_end = min(r1, starts[b + 1]);
     const int t_begin = r0 - starts[b], t_end = seg_end - starts[b];
-    const T *cb = cache + (int64_t)b * a.cap * W;
+    const char *cb = cache + (int64_t)b * a.cap * W * (int64_t)sizeof(T);
+
+    // Cache tile t0 -> stage: instruction i of the stage fills bytes
+    // [1024 i, 1024 i + 1024) of the stage, lane l the 16 bytes at 16 l.  A
+    // lane whose bytes fall on the row padding, past the tile or past the
+    // segment copies the tile's first chunk instead (finite data that is
+    // never read as a valid row: those rows are masked, the padding columns
+    // meet zero queries or output channels >= R).
+    // Written as inline asm with explicit vmcnt waits: the compiler builtin for
+    // this load makes every later LDS read wait for all outstanding copies,
+    // which would serialise the two-tiles-ahead pipeline.
+#define DEC_DMA(STG, T0)                                                                 \
+  do {                                                                                   \
+    const int t0_ = (T0);                                                                \
+    const char *row0_ = cb + (int64_t)t0_ * W * (int64_t)sizeof(T);                      \
+    /* opaque lane offset: the per-lane addresses are recomputed here rather */          \
+    /* than hoisted out of the tile loop and kept live (or spilled)         */          \
+    int lo_ = lane * 16;                                                                 \
+    asm volatile("" : "+v"(lo_));                                                        \
+    _Pragma("unroll") for (int k = 0; k < (NINS + 3) / 4; ++k) {                         \
+      const int ins = wave + 4 * k;                                                      \
+      if (ins < NINS) {                                                                  \
+        const int o = ins * 1024 + lo_;                                                  \
+        const int row = o / ROWB, cbyte = o - row * ROWB;                                \
+        const bool ok = row < TK && cbyte < W * (int)sizeof(T) && t0_ + row < t_end;     \
+        const char *src = ok ? row0_ + (int64_t)row * W * (int64_t)sizeof(T) + cbyte : row0_; \
+        const uint32_t m0 = lds_base + (STG) * STAGEB + ins * 1024;                     \
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"               \
+                     :                                                                   \
+                     : "v"(src), "s"(m0)                                                 \
+                     : "memory", "m0");                                                  \
+      }                                                                                  \
+    }                                                                                    \
+  } while (0)
 
     // B operand of S^T = C Q^T: lane holds head l32, k values g*KPL.. of a step
     typename MF::frag qf[NQR];
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
     l_run = 0.f;
-    __syncthreads();  // the previous segment's tiles and queries are consumed
+    __syncthreads();  // every stage of the previous piece has been consumed
     if constexpr (NQL > 0) {
       // query channels NQR*KSTEP.. of this workgroup's heads
       constexpr int QCH = NQL * MF::KSTEP / VEC;
@@ -223,13 +239,25 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
         *reinterpret_cast<uint4 *>(&Qs[hh * QPITCH + cc]) = v;
       }
     }
-    DEC_FETCH(t_begin);
-    DEC_STASH(0);
-    if (ntiles > 1) DEC_FETCH(t_begin + TK);
-    __syncthreads();
+    DEC_DMA(0, t_begin);
+    if (ntiles > 1) DEC_DMA(1, t_begin + TK);
+    int rd = 0;
     for (int it = 0; it < ntiles; ++it) {
       const int t0 = t_begin + it * TK;
-      const T *cs = Cs + (it & 1) * STAGE;
+      // this wave's copies of tile it are in LDS once at most the next tile's
+      // instructions are outstanding; the barrier publishes every wave's copy
+      // and frees the stage read in the previous iteration
+      if (it + 1 < ntiles) {
+        if (n_dma == NINS / 4) __builtin_amdgcn_s_waitcnt(DEC_VMCNT(NINS / 4));
+        else __builtin_amdgcn_s_waitcnt(DEC_VMCNT((NINS + 3) / 4));
+      } else {
+        __builtin_amdgcn_s_waitcnt(DEC_VMCNT(0));
+      }
+      __syncthreads();
+      // stage rd holds tile it; tile it + 2 goes to the stage read last time
+      if (it + 2 < ntiles) DEC_DMA(rd == 0 ? NSTAGE - 1 : rd - 1, t0 + 2 * TK);
+      const T *cs = reinterpret_cast<const T *>(lds + __builtin_amdgcn_readfirstlane(rd * STAGEB));
+      rd = rd == NSTAGE - 1 ? 0 : rd + 1;
       if (wave_live) {
         // S^T = C Q^T; fragment reads run two MFMAs ahead (the fences keep
         // the compiler from hoisting all of them)
@@ -331,11 +359,6 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
           }
         }
       }
-      if (it + 1 < ntiles) {
-        DEC_STASH((it + 1) & 1);
-        if (it + 2 < ntiles) DEC_FETCH(t0 + 2 * TK);
-      }
-      __syncthreads();
     }
     }  // pass
 
@@ -364,8 +387,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
     r0 = seg_end;
     ++b;
   }
-#undef DEC_FETCH
-#undef DEC_STASH
+#undef DEC_DMA
 }
 
 // Combine the pieces of sequence b: o_lat = sum_i w_i O_i / sum_i w_i l_i,
