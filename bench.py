@@ -69,12 +69,12 @@ def cpu_baseline(c_pre, x, w, c_dec, xd, wd, lens, cache, seconds_hint=True):
         threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    s_sample = 1024
+    s_sample = x.shape[1]  # the whole S=4096 prefill: about 10 s of float64 work
     t0 = time.perf_counter()
     orc.mla_prefill(oracle_cfg(c_pre), w, x[:, :s_sample])
     t_pre = time.perf_counter() - t0
     proj, attn, _ = prefill_flops(c_pre, 1, s_sample)
-    n_seq = 8
+    n_seq = len(lens)  # all 64 sequences
     t0 = time.perf_counter()
     orc.mla_decode_absorbed(oracle_cfg(c_dec), wd, xd[:n_seq], cache[:n_seq], lens[:n_seq])
     t_dec = time.perf_counter() - t0
@@ -83,12 +83,12 @@ def cpu_baseline(c_pre, x, w, c_dec, xd, wd, lens, cache, seconds_hint=True):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"prefill of the first {s_sample} tokens of the S=4096 input "
-                  f"({(proj + attn) / 1e9:.1f} GFLOP, {t_pre:.2f} s, float64 NumPy)",
+        "sample": f"the full prefill workload (B=1, S={s_sample}; {(proj + attn) / 1e9:.1f} GFLOP "
+                  f"in {t_pre:.2f} s, float64 NumPy)",
         "decode": {
             "value": decode_bytes(c_dec, lens[:n_seq]) / t_dec / 1e9,
             "unit": "GB/s",
-            "sample": f"absorbed decode of {n_seq} of the 64 sequences ({t_dec:.2f} s)",
+            "sample": f"absorbed decode of all {n_seq} sequences ({t_dec:.2f} s)",
         },
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
@@ -105,6 +105,9 @@ def main():
                     help="time one of the two workloads only (profiling aid; no JSON line)")
     ap.add_argument("--replicas", type=int, default=3,
                     help="decode cache replicas rotated per step (defeats the 256 MB MALL)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times: the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -113,6 +116,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"read_bytes": n, "write_bytes": n, "launches": 3}}),
+              flush=True)
+        return
 
     import head_latent_attention_08_amd as m
     import synth_inputs as si
