@@ -204,11 +204,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             &ks[l32 * KPITCH + f * MF::KSTEP + g * MF::KPL]);
         st = MF::mma(kf, qf[f], st);
       }
-      // causal mask on the diagonal tiles, then the tile max of this query
-      if (j0 + BKV - 1 > qw0) {
+      // causal mask on the diagonal tiles only (a wave-uniform branch), then
+      // the tile max of this query; key j0 + acc_row(r) is masked when
+      // acc_row(r) exceeds iq - j0
+      if (__builtin_amdgcn_readfirstlane(j0 + BKV - 1 > qw0)) {
+        const int lim = iq - j0 - g * 4;  // acc_row(r) = (r/4)*8 + g*4 + r%4
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (j0 + acc_row(r, lane) > iq) st[r] = -INFINITY;
+          if ((r >> 2) * 8 + (r & 3) > lim) st[r] = -INFINITY;
       }
       float mx = st[0];
 #pragma unroll
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // rescale only when the max grew past the allowance (or on first use)
       const bool need = mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
       if (__any(need)) {
-        const float alpha = need ? exp2f((m_run - mx) * sl2) : 1.0f;
+        const float alpha = need ? __builtin_amdgcn_exp2f((m_run - mx) * sl2) : 1.0f;
         if (need) m_run = mx;
         l_run *= alpha;
 #pragma unroll
@@ -228,7 +231,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float neg = m_run == -INFINITY ? 0.f : -m_run * sl2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = exp2f(fmaf(st[r], sl2, neg));
+        // hardware exp2: arguments are <= 2^8 above zero, and large negative
+        // ones (masked keys) may flush to 0
+        const float pr = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, neg));
         st[r] = pr;
         l_run += pr;
       }
