@@ -65,6 +65,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   using MF = typename C::MF;
   constexpr int VEC = C::VEC, DQK = C::DQK, KPITCH = C::KPITCH, VPITCH = C::VPITCH,
                 NQF = C::NQF, NDT = C::NDT, DVP = C::DVP, CPRK = C::CPRK, CPRV = C::CPRV,
+                DQKP = C::DQKP,
                 KCH = C::KCH, VCH = C::VCH, KSTAGE = C::KSTAGE, VSTAGE = C::VSTAGE;
   __shared__ __attribute__((aligned(16))) T Ks[2 * KSTAGE];
   __shared__ __attribute__((aligned(16))) T Vt[2 * VSTAGE];
@@ -123,35 +124,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // register staging of one K / V^T tile (plain code, not lambdas: the
   // staging registers must not end up in scratch memory)
   uint4 rk[KCH], rv[VCH];
+  const bool v_whole = __builtin_amdgcn_readfirstlane(S % VEC == 0 && S >= VEC);
 #define ATT_FETCH(J0)                                                               \
   do {                                                                              \
     const int j0_ = (J0);                                                           \
     _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                               \
-      const int c = tid + 256 * i;                                                  \
+      const int c = min(tid + 256 * i, BKV * CPRK - 1);                             \
       const int jr = c / CPRK, cc = (c - jr * CPRK) * VEC;                          \
-      const int j = j0_ + jr;                                                       \
-      uint4 v = make_uint4(0, 0, 0, 0);                                             \
-      if (c < BKV * CPRK && j < S) {                                                \
-        if (cc < DN) v = ld16(kn + (int64_t)j * DN + cc);                           \
-        else if (cc < DQK) v = ld16(kpe + (int64_t)j * a.ld_kpe + (cc - DN));       \
-      }                                                                             \
+      /* keys past the end repeat the last key: finite, and masked */               \
+      const int j = min(j0_ + jr, S - 1);                                           \
+      const T *src = cc < DN ? kn + (int64_t)j * DN + cc                            \
+                             : kpe + (int64_t)j * a.ld_kpe + (cc < DQK ? cc - DN : 0); \
+      uint4 v = ld16(src);                                                          \
+      if (DQKP > DQK && cc >= DQK) v = make_uint4(0, 0, 0, 0);                      \
       rk[i] = v;                                                                    \
     }                                                                               \
     _Pragma("unroll") for (int i = 0; i < VCH; ++i) {                               \
-      const int c = tid + 256 * i;                                                  \
+      const int c = min(tid + 256 * i, DV * CPRV - 1);                              \
       const int d = c / CPRV, jc = (c - d * CPRV) * VEC;                            \
       const int j = j0_ + jc;                                                       \
-      uint4 v = make_uint4(0, 0, 0, 0);                                             \
-      if (c < DV * CPRV) {                                                          \
+      uint4 v;                                                                      \
+      if (v_whole) {                                                                \
+        /* S is a multiple of VEC: a chunk is wholly inside or wholly past */       \
+        /* the end; past-the-end chunks repeat the last one (masked keys) */        \
+        v = ld16(vt + (int64_t)d * S + min(j, S - VEC));                            \
+      } else {                                                                      \
         const T *src = vt + (int64_t)d * S + j;                                     \
-        if (j + VEC <= S) {                                                         \
-          v = ld16(src);                                                            \
-        } else {                                                                    \
-          T e[VEC];                                                                 \
-          _Pragma("unroll") for (int k = 0; k < VEC; ++k)                           \
-              e[k] = (j + k < S) ? src[k] : from_f32<T>(0.f);                       \
-          v = *reinterpret_cast<const uint4 *>(e);                                  \
-        }                                                                           \
+        T e[VEC];                                                                   \
+        _Pragma("unroll") for (int k = 0; k < VEC; ++k)                             \
+            e[k] = (j + k < S) ? src[k] : from_f32<T>(0.f);                         \
+        v = *reinterpret_cast<const uint4 *>(e);                                    \
       }                                                                             \
       rv[i] = v;                                                                    \
     }                                                                               \
