@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // ones (masked keys) may flush to 0
         const float pr = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, neg));
         st[r] = pr;
-        l_run += pr;
+        if constexpr (MF::KPL == 1) l_run += pr;
       }
       // O^T += V^T P^T with P^T taken from the score accumulators in place
 #pragma unroll
@@ -248,6 +248,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         } else {
 #pragma unroll
           for (int e = 0; e < MF::KPL; ++e) pf[e] = from_f32<T>(st[u * MF::KPL + e]);
+          const bf16x2 one2 = {from_f32<T>(1.f), from_f32<T>(1.f)};
+#pragma unroll
+          for (int e = 0; e < MF::KPL; e += 2) {
+            const bf16x2 p2 = {pf[e], pf[e + 1]};
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, one2, l_run, false);
+          }
         }
 #pragma unroll
         for (int d = 0; d < NDT; ++d) {
@@ -282,9 +288,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int d = 0; d < NDT; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; r += 4) {
         const int dd = d * 32 + acc_row(r, lane);
-        if (dd < DV) op[dd] = from_f32<T>(o[d][r] * inv);
+        if (dd + 4 <= DV) {
+          T v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = from_f32<T>(o[d][r + e] * inv);
+          if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<uint2 *>(op + dd) = *reinterpret_cast<const uint2 *>(v4);
+          } else {
+            *reinterpret_cast<uint4 *>(op + dd) = *reinterpret_cast<const uint4 *>(v4);
+          }
+        }
       }
   }
 }
