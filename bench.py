@@ -27,6 +27,31 @@ sys.path.insert(0, ROOT)
 
 MI355X_BF16_TFLOPS = 2516.6   # dense MFMA bf16 peak
 MI355X_HBM_GBS = 8000.0       # HBM3E peak
+
+# HBM traffic per launch of the kernels a roofline line can name, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per
+# dispatch, mean over the dispatches of that kernel), each scaled by what the
+# same counter reads for a plain 1 GiB device copy (--copy-calibration):
+# FETCH_SIZE reports half of the bytes the copy reads, WRITE_SIZE all it
+# writes.  An entry holds only for the kernel sources it was measured on
+# (SHA-256 over the listed files); otherwise the traffic is null.
+COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+KERNEL_SOURCES = {
+    "attention": ["attn_prefill.hip", "common.h", "internal.h"],
+    "out_proj": ["gemm.hip", "common.h", "internal.h"],
+    "latent_attention": ["decode.hip", "common.h", "internal.h"],
+}
+TRAFFIC = {
+    "attention": {
+        "sha256": "e1115fff438d25f61ed62872c46a2c2811f2db73c20c39b9681d3f5efde3599e",
+        "FETCH_SIZE_KiB": 243650.8, "WRITE_SIZE_KiB": 131074.2},
+    "out_proj": {
+        "sha256": "69db5267c2f3a0182e6e70cebfea67ab8982e6ccd06ea36934f0ea3fb53371f3",
+        "FETCH_SIZE_KiB": 1163740.4, "WRITE_SIZE_KiB": 59136.0},
+    "latent_attention": {
+        "sha256": "0b05271a3b51811b342bc126be1298c4416eb3e510bf561efc649d3dd01568f4",
+        "FETCH_SIZE_KiB": 182809.7, "WRITE_SIZE_KiB": 81983.0},
+}
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
 
@@ -45,6 +70,24 @@ def prefill_flops(c, B, S):
         "attention": attn,
         "out_proj": 2.0 * B * S * D * H * dv,
     }
+
+
+def kernel_sha(stage):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, "head_latent_attention_08_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(stage):
+    """Measured HBM bytes per launch of a stage's kernel, or None."""
+    t = TRAFFIC.get(stage)
+    if not t or t["sha256"] != kernel_sha(stage):
+        return None
+    return (t["FETCH_SIZE_KiB"] * COUNTER_SCALE["FETCH_SIZE"]
+            + t["WRITE_SIZE_KiB"] * COUNTER_SCALE["WRITE_SIZE"]) * 1024.0
 
 
 def decode_bytes(c, lens):
@@ -105,6 +148,8 @@ def main():
                     help="time one of the two workloads only (profiling aid; no JSON line)")
     ap.add_argument("--replicas", type=int, default=3,
                     help="decode cache replicas rotated per step (defeats the 256 MB MALL)")
+    ap.add_argument("--kernel-sha", action="store_true",
+                    help="print the source hashes the traffic table is keyed on and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times: the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -113,6 +158,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note, not built)", file=sys.stderr)
         sys.exit(2)
+
+    if args.kernel_sha:
+        print(json.dumps({k: kernel_sha(k) for k in KERNEL_SOURCES}))
+        return
 
     import numpy as np
     import torch
@@ -232,11 +281,12 @@ def main():
     dom = max(per_flops, key=lambda k: pst[k])
     roofline = {"bound": "mfma", "kernel": dom, "achieved": stage_tf[dom],
                 "peak": MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": stage_tf[dom] / MI355X_BF16_TFLOPS, "traffic": None,
+                "frac": stage_tf[dom] / MI355X_BF16_TFLOPS, "traffic": traffic_bytes(dom),
                 "flops_per_launch": per_flops[dom], "ms_per_launch": pst[dom]}
     decode_roofline = {"bound": "hbm", "kernel": "latent_attention", "achieved": dec_gbs,
                        "peak": MI355X_HBM_GBS, "unit": "GB/s", "frac": dec_gbs / MI355X_HBM_GBS,
-                       "traffic": None, "bytes_per_launch": kv_bytes, "ms_per_launch": att_ms}
+                       "traffic": traffic_bytes("latent_attention"),
+                       "bytes_per_launch": kv_bytes, "ms_per_launch": att_ms}
 
     out = {
         "metric": METRIC,
