@@ -67,8 +67,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 NQF = C::NQF, NDT = C::NDT, DVP = C::DVP, CPRK = C::CPRK, CPRV = C::CPRV,
                 DQKP = C::DQKP,
                 KCH = C::KCH, VCH = C::VCH, KSTAGE = C::KSTAGE, VSTAGE = C::VSTAGE;
-  __shared__ __attribute__((aligned(16))) T Ks[2 * KSTAGE];
-  __shared__ __attribute__((aligned(16))) T Vt[2 * VSTAGE];
+  __shared__ __attribute__((aligned(16))) T Ks[3 * KSTAGE];
+  __shared__ __attribute__((aligned(16))) T Vt[3 * VSTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = tid; i < (DVP - DV) * VPITCH; i += 256) {
       Vt[DV * VPITCH + i] = from_f32<T>(0.f);
       Vt[VSTAGE + DV * VPITCH + i] = from_f32<T>(0.f);
+      Vt[2 * VSTAGE + DV * VPITCH + i] = from_f32<T>(0.f);
     }
   }
 
@@ -188,36 +189,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int kv_end = min(S, q0 + BQ);
   const int ntiles = (kv_end + BKV - 1) / BKV;
+  const int tw = qw0 / BKV;  // this wave's diagonal tile, the last one it needs
+
+  // S^T of key tile KS (stage pointer) for this wave's queries
+#define ATT_QK(ST, KS)                                                                \
+  do {                                                                                \
+    _Pragma("unroll") for (int r = 0; r < 16; ++r) ST[r] = 0.f;                       \
+    _Pragma("unroll") for (int f = 0; f < NQF; ++f) {                                 \
+      const typename MF::frag kf_ = *reinterpret_cast<const typename MF::frag *>(     \
+          &(KS)[l32 * KPITCH + f * MF::KSTEP + g * MF::KPL]);                         \
+      ST = MF::mma(kf_, qf[f], ST);                                                   \
+    }                                                                                 \
+  } while (0)
+  // Pipeline over key tiles: tile t sits in LDS stage t % 3.  Iteration t
+  // finishes tile t (softmax, O^T += V^T P^T) while the MFMAs of tile t+1's
+  // scores run underneath the exponentials, then stores tile t+2 (fetched
+  // into registers one iteration earlier) into the stage tile t-1 used.
   ATT_FETCH(0);
   ATT_STASH(0);
-  if (ntiles > 1) ATT_FETCH(BKV);
+  if (ntiles > 1) {
+    ATT_FETCH(BKV);
+    ATT_STASH(1);
+  }
+  if (ntiles > 2) ATT_FETCH(2 * BKV);
   __syncthreads();
+  f32x16 s_cur;
+  ATT_QK(s_cur, Ks);
+  int rd = 0;  // stage of tile t
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BKV;
-    const T *ks = Ks + (t & 1) * KSTAGE;
-    const T *vs = Vt + (t & 1) * VSTAGE;
-    if (j0 <= qw0 + 31) {
-      f32x16 st;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = 0.f;
-#pragma unroll
-      for (int f = 0; f < NQF; ++f) {
-        const typename MF::frag kf = *reinterpret_cast<const typename MF::frag *>(
-            &ks[l32 * KPITCH + f * MF::KSTEP + g * MF::KPL]);
-        st = MF::mma(kf, qf[f], st);
-      }
-      // causal mask on the diagonal tiles only (a wave-uniform branch), then
-      // the tile max of this query; key j0 + acc_row(r) is masked when
-      // acc_row(r) exceeds iq - j0
-      if (__builtin_amdgcn_readfirstlane(j0 + BKV - 1 > qw0)) {
+    const int rn = rd == 2 ? 0 : rd + 1;   // stage of tile t + 1
+    const int rw = rd == 0 ? 2 : rd - 1;   // stage of tile t + 2 (held tile t - 1)
+    if (t <= tw) {
+      // causal mask on the diagonal tile only; key j0 + acc_row(r) is masked
+      // when acc_row(r) exceeds iq - j0
+      if (t == tw) {
         const int lim = iq - j0 - g * 4;  // acc_row(r) = (r/4)*8 + g*4 + r%4
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if ((r >> 2) * 8 + (r & 3) > lim) st[r] = -INFINITY;
+          if ((r >> 2) * 8 + (r & 3) > lim) s_cur[r] = -INFINITY;
       }
-      float mx = st[0];
+      float mx = s_cur[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // rescale only when the max grew past the allowance (or on first use)
       const bool need = mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
@@ -230,24 +244,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
       }
+      // hardware exp2: arguments are <= 2^8 above zero, and large negative
+      // ones (masked keys) may flush to 0
       const float neg = m_run == -INFINITY ? 0.f : -m_run * sl2;
+      // Tile t+1's score MFMAs, each followed by a share of tile t's
+      // exponentials: independent work the wave issues while the MFMA runs.
+      // They run even when the wave needs no tile t+1 (its diagonal tile or
+      // the last tile): the stage then holds stale but in-bounds data and
+      // the result is dropped; a branch here would let the compiler hoist
+      // the exponentials out of the interleaving.
+      f32x16 s_nxt;
+      {
+        const T *ksn = Ks + rn * KSTAGE + l32 * KPITCH + g * MF::KPL;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // hardware exp2: arguments are <= 2^8 above zero, and large negative
-        // ones (masked keys) may flush to 0
-        const float pr = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, neg));
-        st[r] = pr;
-        if constexpr (MF::KPL == 1) l_run += pr;
+        for (int r = 0; r < 16; ++r) s_nxt[r] = 0.f;
+        // the fences keep the issue order as written: read fragment f+1,
+        // MFMA f, then VALU work that does not depend on it
+        typename MF::frag kf = *reinterpret_cast<const typename MF::frag *>(ksn);
+#pragma unroll
+        for (int f = 0; f < NQF; ++f) {
+          typename MF::frag kn_ = kf;
+          if (f + 1 < NQF)
+            kn_ = *reinterpret_cast<const typename MF::frag *>(ksn + (f + 1) * MF::KSTEP);
+          __builtin_amdgcn_sched_barrier(0);
+          s_nxt = MF::mma(kf, qf[f], s_nxt);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = f * 16 / NQF; r < (f + 1) * 16 / NQF; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s_cur[r], sl2, neg));
+            s_cur[r] = pr;
+            if constexpr (MF::KPL == 1) l_run += pr;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          kf = kn_;
+        }
       }
       // O^T += V^T P^T with P^T taken from the score accumulators in place
+      const T *vs = Vt + rd * VSTAGE;
 #pragma unroll
       for (int u = 0; u < 16 / MF::KPL; ++u) {
         typename MF::frag pf;
         if constexpr (MF::KPL == 1) {
-          pf = st[u];
+          pf = s_cur[u];
         } else {
 #pragma unroll
-          for (int e = 0; e < MF::KPL; ++e) pf[e] = from_f32<T>(st[u * MF::KPL + e]);
+          for (int e = 0; e < MF::KPL; ++e) pf[e] = from_f32<T>(s_cur[u * MF::KPL + e]);
+          // the row sum takes the bf16 probabilities the PV product uses, two
+          // at a time (dot with (1, 1))
           const bf16x2 one2 = {from_f32<T>(1.f), from_f32<T>(1.f)};
 #pragma unroll
           for (int e = 0; e < MF::KPL; e += 2) {
@@ -270,13 +313,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           o[d] = MF::mma(vf, pf, o[d]);
         }
       }
+      s_cur = s_nxt;
     }
-    if (t + 1 < ntiles) {
-      ATT_STASH((t + 1) & 1);
-      if (t + 2 < ntiles) ATT_FETCH((t + 2) * BKV);
+    if (t + 2 < ntiles) {
+      ATT_STASH(rw);
+      if (t + 3 < ntiles) ATT_FETCH((t + 3) * BKV);
     }
     __syncthreads();
+    rd = rn;
   }
+#undef ATT_QK
 #undef ATT_FETCH
 #undef ATT_STASH
 
