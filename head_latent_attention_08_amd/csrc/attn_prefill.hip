@@ -14,7 +14,9 @@
 // and the rescale of the output accumulator is a per-lane multiply.  The
 // probabilities stay in registers and feed O^T += V^T P^T directly as the B
 // operand; V arrives channel-major ([d][key], written that way by the kv
-// up-projection), so the matching A operand is two 8-byte LDS reads.
+// up-projection) and is stored to LDS with the middle two 4-key quads of
+// every 16-key group swapped, so the eight keys a lane's A operand needs
+// (4g..4g+3 and 8+4g..8+4g+3) are one 16-byte read.
 //
 // Keys stream in tiles of 32 through two LDS stages: the tile after next is
 // fetched into registers while the current one is multiplied, one barrier
@@ -174,7 +176,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int c = tid + 256 * i;                                                  \
       if (c < DV * CPRV) {                                                          \
         const int d = c / CPRV, jc = (c - d * CPRV) * VEC;                          \
-        *reinterpret_cast<uint4 *>(&vs_[d * VPITCH + jc]) = rv[i];                  \
+        if constexpr (MF::KPL > 1) {                                                \
+          /* keys 8h..8h+7 of a 16-key group: quads to positions 4h and 4h+8 */    \
+          T *dst_ = &vs_[d * VPITCH + (jc & ~15) + ((jc >> 1) & 4)];                \
+          *reinterpret_cast<uint2 *>(dst_) = make_uint2(rv[i].x, rv[i].y);          \
+          *reinterpret_cast<uint2 *>(dst_ + 8) = make_uint2(rv[i].z, rv[i].w);      \
+        } else {                                                                    \
+          *reinterpret_cast<uint4 *>(&vs_[d * VPITCH + jc]) = rv[i];                \
+        }                                                                           \
       }                                                                             \
     }                                                                               \
   } while (0)
@@ -221,6 +230,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int rn = rd == 2 ? 0 : rd + 1;   // stage of tile t + 1
     const int rw = rd == 0 ? 2 : rd - 1;   // stage of tile t + 2 (held tile t - 1)
     if (t <= tw) {
+      // V^T fragments of tile t, read now so that they have landed by the
+      // time the PV MFMAs issue (bf16; the fp32 path reads them in place)
+      const T *vs = Vt + rd * VSTAGE;
+      typename MF::frag vpre[MF::KPL > 1 ? 2 : 1][NDT];
+      if constexpr (MF::KPL > 1) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int d = 0; d < NDT; ++d) {
+            // k slots e = 0..7 hold keys (e/4)*8 + g*4 + e%4 of 16-key slice u,
+            // which the stash laid out contiguously at u*16 + g*8
+            const T *row = &vs[(d * 32 + l32) * VPITCH];
+            vpre[u][d] = *reinterpret_cast<const typename MF::frag *>(row + u * 16 + g * 8);
+          }
+      }
       // causal mask on the diagonal tile only; key j0 + acc_row(r) is masked
       // when acc_row(r) exceeds iq - j0
       if (t == tw) {
@@ -232,7 +256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       float mx = s_cur[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = half_swap_max(mx);
       // rescale only when the max grew past the allowance (or on first use)
       const bool need = mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
       if (__any(need)) {
@@ -280,7 +304,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
       // O^T += V^T P^T with P^T taken from the score accumulators in place
-      const T *vs = Vt + rd * VSTAGE;
 #pragma unroll
       for (int u = 0; u < 16 / MF::KPL; ++u) {
         typename MF::frag pf;
@@ -302,14 +325,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int d = 0; d < NDT; ++d) {
           const T *row = &vs[(d * 32 + l32) * VPITCH];
           typename MF::frag vf;
-          if constexpr (MF::KPL == 1) {
-            vf = to_f32(row[acc_row(u, lane)]);
-          } else {
-            // k slots e = 0..7 hold keys (e/4)*8 + g*4 + e%4 of this 16-key slice
-            const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + u * 16 + g * 4);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + u * 16 + 8 + g * 4);
-            vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
+          if constexpr (MF::KPL == 1) vf = to_f32(row[acc_row(u, lane)]);
+          else vf = vpre[u][d];
           o[d] = MF::mma(vf, pf, o[d]);
         }
       }
@@ -327,7 +344,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #undef ATT_STASH
 
   // normalise and store o[b, i, h, d]
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_swap_sum(l_run);
   const float inv = 1.0f / l_tot;
   if (iq < S) {
     T *op = reinterpret_cast<T *>(a.o) + ((int64_t)b * S + iq) * (int64_t)H * DV + (int64_t)h * DV;

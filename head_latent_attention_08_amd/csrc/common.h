@@ -76,6 +76,17 @@ template <typename T> struct Vec16 {
   static constexpr int N = 16 / sizeof(T);
 };
 
+// max / sum of v over lanes l and l ^ 32, in every lane: one VALU lane swap
+// between the wave's halves (v_permlane32_swap) instead of an LDS permute.
+__device__ inline float half_swap_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_swap_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
