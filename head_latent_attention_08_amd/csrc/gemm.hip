@@ -182,10 +182,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 // held in the accumulation registers), one wave per SIMD.  K advances in
 // 64-wide slabs through two LDS stages; the slab after next is fetched into
 // registers while the current one is multiplied, so one barrier per slab
-// suffices.  LDS rows are 64 elements (8 chunks of 16 bytes) with chunk j of
-// row r stored at j ^ (r & 7): the 16-byte writes of a row and the MFMA
-// fragment reads of eight consecutive rows hit distinct bank groups without
-// padding.
+// suffices.  LDS rows are 64 elements (8 chunks of 16 bytes, half of the 64
+// banks) with chunk j of row r stored at j ^ ((r >> 1) & 7): the fragment
+// reads of sixteen consecutive rows (one 16-lane LDS cycle) and the 16-byte
+// writes of a row hit distinct bank groups without padding.
 //
 // Tiles are numbered so that each of the eight XCDs (which take workgroup ids
 // round-robin) works on a contiguous run of tiles, walked in groups of
@@ -201,7 +201,10 @@ constexpr int GB_CPITCH = GB_N + 8;               // epilogue LDS pitch (element
 constexpr int GB_STAGE = (GB_M + GB_N) * GB_K;    // elements per operand stage
 constexpr int GB_LDS = GB_M * GB_CPITCH > 2 * GB_STAGE ? GB_M * GB_CPITCH : 2 * GB_STAGE;
 
-__device__ inline int swz(int r, int k) { return r * GB_K + ((((k >> 3) ^ r) & 7) << 3) + (k & 7); }
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left open (gfx9 encoding)
+constexpr int GB_VMCNT0 = (7 << 4) | (15 << 8);
+
+__device__ inline int swz(int r, int k) { return r * GB_K + ((((k >> 3) ^ (r >> 1)) & 7) << 3) + (k & 7); }
 
 __device__ inline int seg_of(const GemmParams &p, int n) {
   return (p.nseg > 1 && n >= p.seg[1].n_begin) ? ((p.nseg > 2 && n >= p.seg[2].n_begin) ? 2 : 1) : 0;
@@ -214,7 +217,6 @@ __device__ inline int seg_of(const GemmParams &p, int n) {
 __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int tiles_m,
                                                               int tiles_n, int remap) {
   __shared__ __attribute__((aligned(16))) bf16 lds[GB_LDS];
-  bf16 *As0 = lds, *Bs0 = lds + GB_M * GB_K;
 
   // tile index: contiguous run per XCD, then grouped row-major order
   const int T = tiles_m * tiles_n;
@@ -228,58 +230,54 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   const int tn = (t % per_group) / gm;
   const int m0 = tm * GB_M, n0 = tn * GB_N;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
   const int wm = wave >> 1, wn = wave & 1;
   const int g = lane >> 5, l32 = lane & 31;
   const bf16 *A = reinterpret_cast<const bf16 *>(p.A);
 
-  // this thread's chunks: rows r0 + 32 i (i < 8) of the A and B slabs, chunk ch
-  const int r0 = tid >> 3, ch = tid & 7;
-  // Tile bases are uniform; each thread keeps 32-bit element offsets of its
-  // rows (clamped into the matrix: rows past M or N only feed outputs that
-  // are never stored).  Column ranges start at multiples of 256 (checked on
-  // the host), so one tile reads B from a single range.
+  // Slabs are copied from global memory straight into LDS
+  // (global_load_lds_dwordx4: lane l of a copy writes the 16 bytes at LDS
+  // offset 16 l of a 1 KB block, i.e. eight 128-byte slab rows), so no
+  // staging registers and no LDS store instructions are involved.  A slab
+  // is 32 blocks; block b of A (or B) holds rows 8b..8b+7, and lane l fills
+  // row 8b + l/8 at position l%8, where the swizzle keeps logical chunk
+  // (l%8) ^ (row/2 % 8).  Wave w issues blocks w, w+4, ... of A then of B;
+  // each lane's source offset of each of its 16 blocks is fixed for the
+  // whole K loop (rows clamped into the matrix: rows past M or N only feed
+  // outputs that are never stored), and the slab's k offset moves the
+  // scalar base.  Column ranges start at multiples of 256 (checked on the
+  // host), so one tile reads B from a single range.
   const int st = seg_of(p, n0);
   const int64_t t_ldb = SEG_FIELD(p, st, ldb);
   const int t_nb = SEG_FIELD(p, st, n_begin);
-  const bf16 *Ab = A + (int64_t)m0 * p.lda + ch * 8;
-  const bf16 *Bb = reinterpret_cast<const bf16 *>(SEG_FIELD(p, st, B)) + (int64_t)(n0 - t_nb) * t_ldb + ch * 8;
-  const int lda = (int)p.lda, ldb = (int)t_ldb;
-#define GB_OFF(i)                                                            \
-  const int oa##i = (min(m0 + r0 + 32 * i, p.M - 1) - m0) * lda;            \
-  const int ob##i = (min(n0 + r0 + 32 * i, p.N - 1) - n0) * ldb;
-  GB_OFF(0) GB_OFF(1) GB_OFF(2) GB_OFF(3) GB_OFF(4) GB_OFF(5) GB_OFF(6) GB_OFF(7)
-#undef GB_OFF
-  uint4 ra0, ra1, ra2, ra3, ra4, ra5, ra6, ra7, rb0, rb1, rb2, rb3, rb4, rb5, rb6, rb7;
-#define GB_FETCH(k0)                                                         \
-  do {                                                                       \
-    const bf16 *a_ = Ab + (k0), *b_ = Bb + (k0);                             \
-    ra0 = *reinterpret_cast<const uint4 *>(a_ + oa0);                        \
-    ra1 = *reinterpret_cast<const uint4 *>(a_ + oa1);                        \
-    ra2 = *reinterpret_cast<const uint4 *>(a_ + oa2);                        \
-    ra3 = *reinterpret_cast<const uint4 *>(a_ + oa3);                        \
-    ra4 = *reinterpret_cast<const uint4 *>(a_ + oa4);                        \
-    ra5 = *reinterpret_cast<const uint4 *>(a_ + oa5);                        \
-    ra6 = *reinterpret_cast<const uint4 *>(a_ + oa6);                        \
-    ra7 = *reinterpret_cast<const uint4 *>(a_ + oa7);                        \
-    rb0 = *reinterpret_cast<const uint4 *>(b_ + ob0);                        \
-    rb1 = *reinterpret_cast<const uint4 *>(b_ + ob1);                        \
-    rb2 = *reinterpret_cast<const uint4 *>(b_ + ob2);                        \
-    rb3 = *reinterpret_cast<const uint4 *>(b_ + ob3);                        \
-    rb4 = *reinterpret_cast<const uint4 *>(b_ + ob4);                        \
-    rb5 = *reinterpret_cast<const uint4 *>(b_ + ob5);                        \
-    rb6 = *reinterpret_cast<const uint4 *>(b_ + ob6);                        \
-    rb7 = *reinterpret_cast<const uint4 *>(b_ + ob7);                        \
-  } while (0)
-#define GB_STASH1(As, Bs, i, ra, rb)                                         \
-  *reinterpret_cast<uint4 *>(&(As)[swz(r0 + 32 * (i), ch * 8)]) = ra;        \
-  *reinterpret_cast<uint4 *>(&(Bs)[swz(r0 + 32 * (i), ch * 8)]) = rb;
-#define GB_STASH(As, Bs)                                                     \
-  do {                                                                       \
-    GB_STASH1(As, Bs, 0, ra0, rb0) GB_STASH1(As, Bs, 1, ra1, rb1)            \
-    GB_STASH1(As, Bs, 2, ra2, rb2) GB_STASH1(As, Bs, 3, ra3, rb3)            \
-    GB_STASH1(As, Bs, 4, ra4, rb4) GB_STASH1(As, Bs, 5, ra5, rb5)            \
-    GB_STASH1(As, Bs, 6, ra6, rb6) GB_STASH1(As, Bs, 7, ra7, rb7)            \
+  const bf16 *Ab = A + (int64_t)m0 * p.lda;
+  const bf16 *Bb = reinterpret_cast<const bf16 *>(SEG_FIELD(p, st, B)) + (int64_t)(n0 - t_nb) * t_ldb;
+  uint32_t doff[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int blk = wave + 4 * (q & 7);
+    const int row = 8 * blk + (lane >> 3);
+    const int j = (lane & 7) ^ ((row >> 1) & 7);
+    const int rc = q < 8 ? min(row, p.M - 1 - m0) : min(row, p.N - 1 - n0);
+    const int64_t ld = q < 8 ? p.lda : t_ldb;
+    doff[q] = (uint32_t)((rc * ld + j * 8) * (int64_t)sizeof(bf16));
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16 *)lds;
+#define GB_DMA(K0, STG)                                                           \
+  do {                                                                            \
+    const bf16 *a_ = Ab + (K0), *b_ = Bb + (K0);                                  \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                              \
+      const int blk = wave + 4 * (q & 7);                                         \
+      const uint32_t m0_ = lds_base + (STG) * (GB_STAGE * 2) +                    \
+                           (q < 8 ? 0 : GB_M * GB_K * 2) + blk * 1024;            \
+      if (q < 8)                                                                  \
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"         \
+                     :: "v"(doff[q]), "s"(a_), "s"(m0_) : "memory", "m0");        \
+      else                                                                        \
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"         \
+                     :: "v"(doff[q]), "s"(b_), "s"(m0_) : "memory", "m0");        \
+    }                                                                             \
   } while (0)
 
   f32x16 acc[4][4];
@@ -290,9 +288,9 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // one slab: the fragments of k-step s+1 are read from LDS while the 16
-  // MFMAs of k-step s run; sched_barrier keeps the compiler from hoisting all
-  // reads of the slab (which would need 128 more registers)
+  // fragments of k-step s+1 are read from LDS while the 16 MFMAs of k-step
+  // s run; sched_barrier keeps the compiler from hoisting all reads of the
+  // slab (which would need 128 more registers)
   auto load_frags = [&](const bf16 *As, const bf16 *Bs, int kk, bf16x8 *a, bf16x8 *b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -308,7 +306,17 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
-  auto compute = [&](const bf16 *As, const bf16 *Bs) {
+
+  const int nk = p.K / GB_K;
+  GB_DMA(0, 0);
+  __builtin_amdgcn_s_waitcnt(GB_VMCNT0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bf16 *As = lds + cur * GB_STAGE, *Bs = As + GB_M * GB_K;
+    // the next slab goes to the stage every wave finished reading before
+    // the last barrier, and has this iteration's MFMAs to arrive
+    if (kt + 1 < nk) GB_DMA((kt + 1) * GB_K, cur ^ 1);
     bf16x8 a0[4], b0[4], a1[4], b1[4];
     load_frags(As, Bs, 0, a0, b0);
     load_frags(As, Bs, 16, a1, b1);
@@ -324,26 +332,11 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
     mma16(a0, b0);
     __builtin_amdgcn_sched_barrier(0);
     mma16(a1, b1);
-  };
-
-  const int nk = p.K / GB_K;
-  GB_FETCH(0);
-  GB_STASH(As0, Bs0);
-  if (nk > 1) GB_FETCH(GB_K);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = (kt & 1) * GB_STAGE, nxt = GB_STAGE - cur;
-    compute(lds + cur, lds + cur + GB_M * GB_K);
-    if (kt + 1 < nk) {
-      bf16 *An = lds + nxt, *Bn = lds + nxt + GB_M * GB_K;
-      GB_STASH(An, Bn);
-      if (kt + 2 < nk) GB_FETCH((kt + 2) * GB_K);
-    }
+    // this wave's copies have landed; the barrier publishes every wave's
+    __builtin_amdgcn_s_waitcnt(GB_VMCNT0);
     __syncthreads();
   }
-#undef GB_FETCH
-#undef GB_STASH
-#undef GB_STASH1
+#undef GB_DMA
 
   // epilogue through LDS (the operand stages are free after the last barrier)
   bf16 *Cs = lds;
