@@ -189,14 +189,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 //
 // Tiles are numbered so that each of the eight XCDs (which take workgroup ids
 // round-robin) works on a contiguous run of tiles, walked in groups of
-// GROUP_M tile rows, so concurrently running tiles share A and B slabs in that
-// XCD's L2.
+// group_m tile rows, so concurrently running tiles share A and B slabs in that
+// XCD's L2 (taller groups pay off for long K, flat ones for short K, where
+// the output stores dominate).
 //
 // The accumulators leave through LDS: the tile is written there as bf16, then
 // every thread stores 16-byte runs of 8 consecutive columns, which fall in one
 // head of the destination (all column ranges and head widths are multiples of
 // 8), so the head-scatter store stays vectorised.
-constexpr int GB_M = 256, GB_N = 256, GB_K = 64, GB_THREADS = 256, GROUP_M = 4;
+constexpr int GB_M = 256, GB_N = 256, GB_K = 64, GB_THREADS = 256;
 constexpr int GB_CPITCH = GB_N + 8;               // epilogue LDS pitch (elements)
 constexpr int GB_STAGE = (GB_M + GB_N) * GB_K;    // elements per operand stage
 constexpr int GB_LDS = GB_M * GB_CPITCH > 2 * GB_STAGE ? GB_M * GB_CPITCH : 2 * GB_STAGE;
@@ -215,17 +216,17 @@ __device__ inline int seg_of(const GemmParams &p, int n) {
 #define SEG_FIELD(p, s, f) ((s) == 0 ? (p).seg[0].f : ((s) == 1 ? (p).seg[1].f : (p).seg[2].f))
 
 __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int tiles_m,
-                                                              int tiles_n, int remap) {
+                                                              int tiles_n, int remap, int group_m) {
   __shared__ __attribute__((aligned(16))) bf16 lds[GB_LDS];
 
   // tile index: contiguous run per XCD, then grouped row-major order
   const int T = tiles_m * tiles_n;
   int t = blockIdx.x;
   if (remap) t = (t & 7) * (T >> 3) + (t >> 3);
-  const int per_group = GROUP_M * tiles_n;
+  const int per_group = group_m * tiles_n;
   const int grp = t / per_group;
-  const int first_m = grp * GROUP_M;
-  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int first_m = grp * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
   const int tm = first_m + (t % per_group) % gm;
   const int tn = (t % per_group) / gm;
   const int m0 = tm * GB_M, n0 = tn * GB_N;
@@ -553,8 +554,9 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   if (big) {
     const int tm = (d.M + GB_M - 1) / GB_M, tn = (d.N + GB_N - 1) / GB_N;
     const int T = tm * tn;
+    const int group_m = d.K >= 4096 ? 8 : (d.K <= 1024 ? 2 : 4);
     hipLaunchKernelGGL(gemm_big_kernel, dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn,
-                       (T % 8 == 0) ? 1 : 0);
+                       (T % 8 == 0) ? 1 : 0, group_m);
     return hipGetLastError();
   }
   bool skinny = d.dtype == BF16 && !d.b_kn && d.M <= SK_M && d.K % SK_K == 0 && d.N % 8 == 0 &&
