@@ -149,6 +149,19 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
   // DMA instructions per tile issued by this wave (instructions wave, wave+4, ..)
   const int n_dma = (NINS - wave + 3) / 4;
+  // this lane's byte offset from a tile's first row and its row, per copy
+  // instruction (padding and out-of-tile lanes: offset 0, row 0)
+  constexpr int NPW = (NINS + 3) / 4;
+  uint32_t dof[NPW];
+  int drow[NPW];
+#pragma unroll
+  for (int k = 0; k < NPW; ++k) {
+    const int o = (wave + 4 * k) * 1024 + lane * 16;
+    const int row = o / ROWB, cbyte = o - row * ROWB;
+    const bool ok = wave + 4 * k < NINS && row < TK && cbyte < W * (int)sizeof(T);
+    dof[k] = ok ? (uint32_t)(row * W * (int)sizeof(T) + cbyte) : 0u;
+    drow[k] = ok ? row : 0;
+  }
 
   while (r0 < r1) {
     const int seg_end = min(r1, starts[b + 1]);
@@ -157,32 +170,30 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
 
     // Cache tile t0 -> stage: instruction i of the stage fills bytes
     // [1024 i, 1024 i + 1024) of the stage, lane l the 16 bytes at 16 l.  A
-    // lane whose bytes fall on the row padding, past the tile or past the
-    // segment copies the tile's first chunk instead (finite data that is
-    // never read as a valid row: those rows are masked, the padding columns
-    // meet zero queries or output channels >= R).
+    // lane whose bytes fall on the row padding or past the segment copies
+    // the tile's first chunk instead (finite data that is never read as a
+    // valid row: those rows are masked, the padding columns meet zero
+    // queries or output channels >= R).  The lane's offset from the tile's
+    // first row is fixed (dof, drow); the tile base is a scalar.
     // Written as inline asm with explicit vmcnt waits: the compiler builtin for
     // this load makes every later LDS read wait for all outstanding copies,
     // which would serialise the two-tiles-ahead pipeline.
 #define DEC_DMA(STG, T0)                                                                 \
   do {                                                                                   \
     const int t0_ = (T0);                                                                \
-    const char *row0_ = cb + (int64_t)t0_ * W * (int64_t)sizeof(T);                      \
-    /* opaque lane offset: the per-lane addresses are recomputed here rather */          \
-    /* than hoisted out of the tile loop and kept live (or spilled)         */          \
-    int lo_ = lane * 16;                                                                 \
-    asm volatile("" : "+v"(lo_));                                                        \
-    _Pragma("unroll") for (int k = 0; k < (NINS + 3) / 4; ++k) {                         \
+    const uint64_t r0a_ = (uint64_t)(cb + (int64_t)t0_ * W * (int64_t)sizeof(T));        \
+    const char *row0_ = reinterpret_cast<const char *>(                                  \
+        ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(r0a_ >> 32)) << 32) |       \
+        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r0a_));             \
+    const int lim_ = t_end - t0_;                                                        \
+    _Pragma("unroll") for (int k = 0; k < NPW; ++k) {                                    \
       const int ins = wave + 4 * k;                                                      \
       if (ins < NINS) {                                                                  \
-        const int o = ins * 1024 + lo_;                                                  \
-        const int row = o / ROWB, cbyte = o - row * ROWB;                                \
-        const bool ok = row < TK && cbyte < W * (int)sizeof(T) && t0_ + row < t_end;     \
-        const char *src = ok ? row0_ + (int64_t)row * W * (int64_t)sizeof(T) + cbyte : row0_; \
+        const uint32_t off_ = drow[k] < lim_ ? dof[k] : 0u;                              \
         const uint32_t m0 = lds_base + (STG) * STAGEB + ins * 1024;                     \
-        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"               \
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"                \
                      :                                                                   \
-                     : "v"(src), "s"(m0)                                                 \
+                     : "v"(off_), "s"(row0_), "s"(m0)                                    \
                      : "memory", "m0");                                                  \
       }                                                                                  \
     }                                                                                    \
