@@ -43,14 +43,14 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "e1115fff438d25f61ed62872c46a2c2811f2db73c20c39b9681d3f5efde3599e",
-        "FETCH_SIZE_KiB": 243650.8, "WRITE_SIZE_KiB": 131074.2},
+        "sha256": "9768966f720e744bedf420d578b0e612fa1f23046ee37351a88bea66ff537a9c",
+        "FETCH_SIZE_KiB": 243048.2, "WRITE_SIZE_KiB": 131084.3},
     "out_proj": {
-        "sha256": "69db5267c2f3a0182e6e70cebfea67ab8982e6ccd06ea36934f0ea3fb53371f3",
-        "FETCH_SIZE_KiB": 1163740.4, "WRITE_SIZE_KiB": 59136.0},
+        "sha256": "fd2194f454effcd107fb258477b9aa39dc208c01b7b149fbf54dbcd75f332b45",
+        "FETCH_SIZE_KiB": 822087.6, "WRITE_SIZE_KiB": 57344.0},
     "latent_attention": {
-        "sha256": "0b05271a3b51811b342bc126be1298c4416eb3e510bf561efc649d3dd01568f4",
-        "FETCH_SIZE_KiB": 182809.7, "WRITE_SIZE_KiB": 81983.0},
+        "sha256": "3e4039c58861ae64ebc4ad0bb54e81ec938cca53072446bb19bf42fc456b2972",
+        "FETCH_SIZE_KiB": 182787.8, "WRITE_SIZE_KiB": 81983.1},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
