@@ -8,21 +8,61 @@ namespace mla {
 namespace {
 
 // RMSNorm: one wave per row, fp32 sum of squares, x * rsqrt(mean + eps) * g.
+// Rows are read in 16-byte chunks (n and the row stride are multiples of 8
+// elements and rows 16-byte aligned, checked on the host); the chunks a lane
+// owns are loaded together so their latencies overlap.
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(T *x, int64_t rows, int64_t ld, int n,
                                                       const T *g, float eps) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int UNR = 4;  // chunks in flight per lane
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   T *xr = x + row * ld;
+  const int nch = n / VEC;
   float ss = 0.f;
-  for (int c = lane; c < n; c += 64) {
-    float v = to_f32(xr[c]);
-    ss += v * v;
+  for (int c0 = 0; c0 < nch; c0 += 64 * UNR) {
+    uint4 v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int c = c0 + u * 64 + lane;
+      v[u] = c < nch ? *reinterpret_cast<const uint4 *>(xr + c * VEC) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const T *e = reinterpret_cast<const T *>(&v[u]);
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        const float f = to_f32(e[k]);
+        ss += f * f;
+      }
+    }
   }
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)n + eps);
-  for (int c = lane; c < n; c += 64) xr[c] = from_f32<T>(to_f32(xr[c]) * inv * to_f32(g[c]));
+  for (int c0 = 0; c0 < nch; c0 += 64 * UNR) {
+    uint4 v[UNR], w[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < nch) {
+        v[u] = *reinterpret_cast<const uint4 *>(xr + c * VEC);
+        w[u] = *reinterpret_cast<const uint4 *>(g + c * VEC);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < nch) {
+        T o[VEC];
+        const T *e = reinterpret_cast<const T *>(&v[u]), *ge = reinterpret_cast<const T *>(&w[u]);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) o[k] = from_f32<T>(to_f32(e[k]) * inv * to_f32(ge[k]));
+        *reinterpret_cast<uint4 *>(xr + c * VEC) = *reinterpret_cast<const uint4 *>(o);
+      }
+    }
+  }
 }
 
 // RoPE.  A workgroup takes `tpb` consecutive tokens: it first forms
@@ -63,6 +103,81 @@ __global__ __launch_bounds__(256) void rope_kernel(T *x, int64_t n_tok, int64_t 
     const float c = cs[tl * P + pr], s = sn[tl * P + pr];
     base[i0] = from_f32<T>(a * c - b * s);
     base[i1] = from_f32<T>(b * c + a * s);
+  }
+}
+
+// RoPE with 16-byte accesses: a thread rotates 8 pairs of one (token, head),
+// held in two 16-byte chunks -- elements 16c..16c+15 (interleaved pairs) or
+// 8c..8c+7 with their partners 8c+P..8c+P+7 (half-split).  Needs rope_dim a
+// multiple of 16 and 16-byte aligned rows (checked on the host).  Blocks take
+// tpb tokens (all heads) or, for many heads, one token and a range of heads
+// (grid y); the cos/sin of the block's tokens are formed in float64 first.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_vec_kernel(T *x, int64_t n_tok, int64_t S, int64_t sb,
+                                                       int64_t ss, int n_heads, int64_t sh,
+                                                       const int32_t *positions, RopeTab tab,
+                                                       int tpb) {
+  static_assert(sizeof(T) == 2 || sizeof(T) == 4, "16-byte chunks of bf16 or fp32");
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float cs[256], sn[256];
+  const int P = tab.pairs, CH = P / 8;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  for (int i = threadIdx.x; i < tpb * P; i += blockDim.x) {
+    const int64_t t = t0 + i / P;
+    if (t < n_tok) {
+      const int pr = i % P;
+      const double pos = positions ? (double)positions[t] : (double)(t % S);
+      double s, c;
+      sincos(pos * tab.inv_freq[pr], &s, &c);
+      cs[i] = (float)c * tab.amp;
+      sn[i] = (float)s * tab.amp;
+    }
+  }
+  __syncthreads();
+  const int per_tok = n_heads * CH;
+  const int i = blockIdx.y * blockDim.x + threadIdx.x;
+  const int tl = i / per_tok;
+  const int64_t t = t0 + tl;
+  if (tl >= tpb || t >= n_tok) return;
+  const int rem = i - tl * per_tok;
+  const int h = rem / CH, c = rem - h * CH;
+  T *base = x + (t / S) * sb + (t % S) * ss + (int64_t)h * sh;
+  const float *ct = cs + tl * P, *st = sn + tl * P;
+  if (tab.convention == 0) {
+    // pairs (8c + k, 8c + k + P), k < 8
+    T a[8], b[8];
+#pragma unroll
+    for (int q = 0; q < 8 / VEC; ++q) {
+      *reinterpret_cast<uint4 *>(a + q * VEC) = *reinterpret_cast<const uint4 *>(base + 8 * c + q * VEC);
+      *reinterpret_cast<uint4 *>(b + q * VEC) = *reinterpret_cast<const uint4 *>(base + 8 * c + P + q * VEC);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float fa = to_f32(a[k]), fb = to_f32(b[k]), co = ct[8 * c + k], si = st[8 * c + k];
+      a[k] = from_f32<T>(fa * co - fb * si);
+      b[k] = from_f32<T>(fb * co + fa * si);
+    }
+#pragma unroll
+    for (int q = 0; q < 8 / VEC; ++q) {
+      *reinterpret_cast<uint4 *>(base + 8 * c + q * VEC) = *reinterpret_cast<const uint4 *>(a + q * VEC);
+      *reinterpret_cast<uint4 *>(base + 8 * c + P + q * VEC) = *reinterpret_cast<const uint4 *>(b + q * VEC);
+    }
+  } else {
+    // pairs (16c + 2k, 16c + 2k + 1), k < 8
+    T v[16];
+#pragma unroll
+    for (int q = 0; q < 16 / VEC; ++q)
+      *reinterpret_cast<uint4 *>(v + q * VEC) = *reinterpret_cast<const uint4 *>(base + 16 * c + q * VEC);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float fa = to_f32(v[2 * k]), fb = to_f32(v[2 * k + 1]);
+      const float co = ct[8 * c + k], si = st[8 * c + k];
+      v[2 * k] = from_f32<T>(fa * co - fb * si);
+      v[2 * k + 1] = from_f32<T>(fb * co + fa * si);
+    }
+#pragma unroll
+    for (int q = 0; q < 16 / VEC; ++q)
+      *reinterpret_cast<uint4 *>(base + 16 * c + q * VEC) = *reinterpret_cast<const uint4 *>(v + q * VEC);
   }
 }
 
@@ -107,6 +222,23 @@ hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb,
                        int n_heads, int64_t sh, const int32_t *positions, const RopeTab &tab,
                        hipStream_t st) {
   if (n_tok <= 0) return hipSuccess;
+  const int64_t vec = dtype == BF16 ? 8 : 4;
+  const bool vector = tab.pairs % 8 == 0 && ((uintptr_t)x & 15) == 0 && sb % vec == 0 &&
+                      ss % vec == 0 && sh % vec == 0 && tab.pairs <= 256;
+  if (vector) {
+    const int per_tok = n_heads * (tab.pairs / 8);
+    int tpb = per_tok >= 256 ? 1 : 256 / per_tok;
+    if (tpb * tab.pairs > 256) tpb = 256 / tab.pairs;
+    if (tpb < 1) tpb = 1;
+    dim3 grid((unsigned)((n_tok + tpb - 1) / tpb), (unsigned)((tpb * per_tok + 255) / 256));
+    if (dtype == BF16)
+      hipLaunchKernelGGL(rope_vec_kernel<bf16>, grid, dim3(256), 0, st, (bf16 *)x, n_tok, S, sb,
+                         ss, n_heads, sh, positions, tab, tpb);
+    else
+      hipLaunchKernelGGL(rope_vec_kernel<float>, grid, dim3(256), 0, st, (float *)x, n_tok, S,
+                         sb, ss, n_heads, sh, positions, tab, tpb);
+    return hipGetLastError();
+  }
   int per_tok = n_heads * tab.pairs;
   int tpb = per_tok >= 256 ? 1 : 256 / per_tok;
   if (tpb * tab.pairs > 256) tpb = 256 / tab.pairs;
