@@ -36,6 +36,10 @@ namespace mla {
 namespace {
 
 constexpr int BQ = 128, BKV = 32;
+
+// s_waitcnt immediate: at most n vector-memory operations of this wave
+// outstanding (gfx9 encoding; expcnt and lgkmcnt left open)
+#define ATT_VMCNT(n) ((((n) & 15)) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LOG2 = 8.0f;
 
@@ -56,6 +60,16 @@ struct AttnCfg {
   static constexpr int CPRV = BKV / VEC;         // 16-byte chunks per V^T row
   static constexpr int KCH = (BKV * CPRK + 255) / 256;
   static constexpr int VCH = (DV * CPRV + 255) / 256;
+  // K stage in LDS, filled by 1 KB copy blocks: k_nope rows (pitch KNP), then
+  // k_pe rows (pitch KPP, padded to whole query fragments)
+  static constexpr int ES = sizeof(T);
+  static constexpr int NQN = DN / MF::KSTEP;   // query fragments over k_nope
+  static constexpr int KNP = DN + VEC;
+  static constexpr int KPP = (DQKP - DN) + VEC;
+  static constexpr int NKN = (BKV * KNP * ES + 1023) / 1024;
+  static constexpr int NKP = (BKV * KPP * ES + 1023) / 1024;
+  static constexpr int KSTAGEB = (NKN + NKP) * 1024;
+  static constexpr int NKPW = (NKN + NKP + 3) / 4;  // copy blocks per wave (at most)
 };
 
 template <typename T>
@@ -67,12 +81,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   using MF = typename C::MF;
   constexpr int VEC = C::VEC, DQK = C::DQK, KPITCH = C::KPITCH, VPITCH = C::VPITCH,
                 NQF = C::NQF, NDT = C::NDT, DVP = C::DVP, CPRK = C::CPRK, CPRV = C::CPRV,
-                DQKP = C::DQKP,
+                DQKP = C::DQKP, ES = C::ES, NQN = C::NQN, KNP = C::KNP, KPP = C::KPP,
+                NKN = C::NKN, NKP = C::NKP, KSTAGEB = C::KSTAGEB, NKPW = C::NKPW,
                 KCH = C::KCH, VCH = C::VCH, KSTAGE = C::KSTAGE, VSTAGE = C::VSTAGE;
-  __shared__ __attribute__((aligned(16))) T Ks[3 * KSTAGE];
+  __shared__ __attribute__((aligned(1024))) char Kl[3 * KSTAGEB];
   __shared__ __attribute__((aligned(16))) T Vt[3 * VSTAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
   const int g = lane >> 5, l32 = lane & 31;
   const int S = a.S, H = a.H;
   const int nq = (S + BQ - 1) / BQ;
@@ -124,24 +140,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  // register staging of one K / V^T tile (plain code, not lambdas: the
-  // staging registers must not end up in scratch memory)
-  uint4 rk[KCH], rv[VCH];
+  // K tiles are copied from global memory straight into LDS
+  // (global_load_lds_dwordx4, 16 bytes a lane into consecutive LDS bytes of a
+  // 1 KB block).  This wave copies blocks wave, wave + 4, ..; a lane's row
+  // and byte column in its block are fixed for the whole loop (padding
+  // lanes copy the tile's first chunk: finite values that only meet zero
+  // query columns), the tile base is a scalar, and rows past the end of the
+  // sequence (last tile only, masked keys) repeat the last row.
+  int drow[NKPW], dcb[NKPW];
+#pragma unroll
+  for (int k = 0; k < NKPW; ++k) {
+    const int blk = wave + 4 * k;
+    drow[k] = 0;
+    dcb[k] = 0;
+    if (blk < NKN) {
+      const int o = blk * 1024 + lane * 16, row = o / (KNP * ES), cb = o - row * (KNP * ES);
+      if (row < BKV && cb < DN * ES) { drow[k] = row; dcb[k] = cb; }
+    } else if (blk < NKN + NKP) {
+      const int o = (blk - NKN) * 1024 + lane * 16, row = o / (KPP * ES), cb = o - row * (KPP * ES);
+      if (row < BKV && cb < DR * ES) { drow[k] = row; dcb[k] = cb; }
+    }
+  }
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)Kl;
+#define ATT_KDMA(STG, J0)                                                               \
+  do {                                                                                  \
+    const int j0_ = (J0);                                                               \
+    const int lim_ = S - 1 - j0_;                                                       \
+    const T *bn_ = kn + (int64_t)j0_ * DN;                                              \
+    const T *bp_ = kpe + (int64_t)j0_ * a.ld_kpe;                                       \
+    _Pragma("unroll") for (int k = 0; k < NKPW; ++k) {                                  \
+      const int blk = wave + 4 * k;                                                     \
+      const int r_ = min(drow[k], lim_);                                                \
+      const uint32_t m0_ = lds_k + (STG) * KSTAGEB + blk * 1024;                        \
+      if (blk < NKN) {                                                                  \
+        const uint32_t off_ = (uint32_t)(r_ * DN * ES + dcb[k]);                        \
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"               \
+                     :: "v"(off_), "s"(bn_), "s"(m0_) : "memory", "m0");                \
+      } else if (blk < NKN + NKP) {                                                     \
+        const uint32_t off_ = (uint32_t)(r_ * a.ld_kpe * ES + dcb[k]);                  \
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"               \
+                     :: "v"(off_), "s"(bp_), "s"(m0_) : "memory", "m0");                \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+
+  // register staging of one V^T tile (plain code, not lambdas: the staging
+  // registers must not end up in scratch memory)
+  uint4 rv[VCH];
   const bool v_whole = __builtin_amdgcn_readfirstlane(S % VEC == 0 && S >= VEC);
 #define ATT_FETCH(J0)                                                               \
   do {                                                                              \
     const int j0_ = (J0);                                                           \
-    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                               \
-      const int c = min(tid + 256 * i, BKV * CPRK - 1);                             \
-      const int jr = c / CPRK, cc = (c - jr * CPRK) * VEC;                          \
-      /* keys past the end repeat the last key: finite, and masked */               \
-      const int j = min(j0_ + jr, S - 1);                                           \
-      const T *src = cc < DN ? kn + (int64_t)j * DN + cc                            \
-                             : kpe + (int64_t)j * a.ld_kpe + (cc < DQK ? cc - DN : 0); \
-      uint4 v = ld16(src);                                                          \
-      if (DQKP > DQK && cc >= DQK) v = make_uint4(0, 0, 0, 0);                      \
-      rk[i] = v;                                                                    \
-    }                                                                               \
     _Pragma("unroll") for (int i = 0; i < VCH; ++i) {                               \
       const int c = min(tid + 256 * i, DV * CPRV - 1);                              \
       const int d = c / CPRV, jc = (c - d * CPRV) * VEC;                            \
@@ -163,15 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   } while (0)
 #define ATT_STASH(STAGE)                                                            \
   do {                                                                              \
-    T *ks_ = Ks + (STAGE) * KSTAGE;                                                 \
     T *vs_ = Vt + (STAGE) * VSTAGE;                                                 \
-    _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                               \
-      const int c = tid + 256 * i;                                                  \
-      if (c < BKV * CPRK) {                                                         \
-        const int jr = c / CPRK, cc = (c - jr * CPRK) * VEC;                        \
-        *reinterpret_cast<uint4 *>(&ks_[jr * KPITCH + cc]) = rk[i];                 \
-      }                                                                             \
-    }                                                                               \
     _Pragma("unroll") for (int i = 0; i < VCH; ++i) {                               \
       const int c = tid + 256 * i;                                                  \
       if (c < DV * CPRV) {                                                          \
@@ -200,35 +241,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int ntiles = (kv_end + BKV - 1) / BKV;
   const int tw = qw0 / BKV;  // this wave's diagonal tile, the last one it needs
 
-  // S^T of key tile KS (stage pointer) for this wave's queries
-#define ATT_QK(ST, KS)                                                                \
+  // fragment f of this lane's key row in the K stage starting at byte KB:
+  // k_nope region for f < NQN, k_pe region after it
+#define ATT_KFRAG(KB, f)                                                              \
+  (*reinterpret_cast<const typename MF::frag *>(                                      \
+      (f) < NQN ? reinterpret_cast<const T *>(KB) + l32 * KNP + (f) * MF::KSTEP + g * MF::KPL \
+                : reinterpret_cast<const T *>((KB) + NKN * 1024) + l32 * KPP +        \
+                      ((f) - NQN) * MF::KSTEP + g * MF::KPL))
+  // S^T of key tile at stage byte base KB for this wave's queries
+#define ATT_QK(ST, KB)                                                                \
   do {                                                                                \
     _Pragma("unroll") for (int r = 0; r < 16; ++r) ST[r] = 0.f;                       \
     _Pragma("unroll") for (int f = 0; f < NQF; ++f) {                                 \
-      const typename MF::frag kf_ = *reinterpret_cast<const typename MF::frag *>(     \
-          &(KS)[l32 * KPITCH + f * MF::KSTEP + g * MF::KPL]);                         \
+      const typename MF::frag kf_ = ATT_KFRAG(KB, f);                                 \
       ST = MF::mma(kf_, qf[f], ST);                                                   \
     }                                                                                 \
   } while (0)
   // Pipeline over key tiles: tile t sits in LDS stage t % 3.  Iteration t
+  // starts the copy of tile t+2's keys into the stage tile t-1 used, then
   // finishes tile t (softmax, O^T += V^T P^T) while the MFMAs of tile t+1's
-  // scores run underneath the exponentials, then stores tile t+2 (fetched
-  // into registers one iteration earlier) into the stage tile t-1 used.
+  // scores run underneath the exponentials, and stores tile t+2's V^T
+  // (loaded into registers one iteration earlier).
+  ATT_KDMA(0, 0);
   ATT_FETCH(0);
   ATT_STASH(0);
   if (ntiles > 1) {
+    ATT_KDMA(1, BKV);
     ATT_FETCH(BKV);
     ATT_STASH(1);
   }
   if (ntiles > 2) ATT_FETCH(2 * BKV);
+  __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));
   __syncthreads();
   f32x16 s_cur;
-  ATT_QK(s_cur, Ks);
+  ATT_QK(s_cur, Kl);
   int rd = 0;  // stage of tile t
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BKV;
     const int rn = rd == 2 ? 0 : rd + 1;   // stage of tile t + 1
     const int rw = rd == 0 ? 2 : rd - 1;   // stage of tile t + 2 (held tile t - 1)
+    if (t + 2 < ntiles) ATT_KDMA(rw, (t + 2) * BKV);
     if (t <= tw) {
       // V^T fragments of tile t, read now so that they have landed by the
       // time the PV MFMAs issue (bf16; the fp32 path reads them in place)
@@ -279,17 +331,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // the exponentials out of the interleaving.
       f32x16 s_nxt;
       {
-        const T *ksn = Ks + rn * KSTAGE + l32 * KPITCH + g * MF::KPL;
+        const char *ksn = Kl + __builtin_amdgcn_readfirstlane(rn * KSTAGEB);
 #pragma unroll
         for (int r = 0; r < 16; ++r) s_nxt[r] = 0.f;
         // the fences keep the issue order as written: read fragment f+1,
         // MFMA f, then VALU work that does not depend on it
-        typename MF::frag kf = *reinterpret_cast<const typename MF::frag *>(ksn);
+        typename MF::frag kf = ATT_KFRAG(ksn, 0);
 #pragma unroll
         for (int f = 0; f < NQF; ++f) {
           typename MF::frag kn_ = kf;
-          if (f + 1 < NQF)
-            kn_ = *reinterpret_cast<const typename MF::frag *>(ksn + (f + 1) * MF::KSTEP);
+          if (f + 1 < NQF) kn_ = ATT_KFRAG(ksn, f + 1);
           __builtin_amdgcn_sched_barrier(0);
           s_nxt = MF::mma(kf, qf[f], s_nxt);
           __builtin_amdgcn_sched_barrier(0);
@@ -336,9 +387,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       ATT_STASH(rw);
       if (t + 3 < ntiles) ATT_FETCH((t + 3) * BKV);
     }
+    // this wave's key copies of tile t+2 have landed (only the V^T loads of
+    // tile t+3, issued after them, may still be in flight); the barrier
+    // publishes every wave's copies and stores
+    if (t + 3 < ntiles && v_whole) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(VCH));
+    else __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));
     __syncthreads();
     rd = rn;
   }
+#undef ATT_KFRAG
+#undef ATT_KDMA
 #undef ATT_QK
 #undef ATT_FETCH
 #undef ATT_STASH
