@@ -405,6 +405,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
 // w_i = exp2(m_i - max_i m_i).  A sequence with no valid rows gets NaN.
 // One workgroup per (sequence, group of 8 heads).
 constexpr int MERGE_HEADS = 8;
+constexpr int MERGE_MAXP = 264;  // pieces per sequence: at most n_blocks + 1
 
 template <typename T, int R>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
@@ -440,28 +441,109 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
   }
   const int per = (total + a.n_blocks - 1) / a.n_blocks;
   const int i0 = start / per, i1 = (start + n_b - 1) / per;
-  // 32 threads per head; each thread owns channels 4 t + 128 j
+  // 32 threads per head; each thread owns channels 4 t + 128 j.  The piece
+  // weights w_i / L go to LDS first; then every piece costs each thread NJ
+  // independent 16-byte loads.
+  __shared__ float wsh[MERGE_HEADS][MERGE_MAXP];
   const int hh = tid >> 5, ln = tid & 31;
   const int h = h0 + hh;
-  if (h >= a.H) return;
-  float M = -INFINITY;
-  for (int i = i0; i <= i1; ++i) M = fmaxf(M, a.part_ml[((int64_t)(i + b) * a.H + h) * 2]);
-  float L = 0.f;
-  for (int i = i0; i <= i1; ++i) {
-    const float *ml = a.part_ml + ((int64_t)(i + b) * a.H + h) * 2;
-    L += exp2f(ml[0] - M) * ml[1];
-  }
-  const float invL = 1.0f / L;
-  T *out = reinterpret_cast<T *>(a.o_lat) + ((int64_t)b * a.H + h) * R;
-  for (int c = ln * 4; c < R; c += 128) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int np = i1 - i0 + 1;  // <= n_blocks + 1 <= MERGE_MAXP (checked on the host)
+  if (h < a.H) {
+    float M = -INFINITY;
+    for (int i = i0; i <= i1; ++i) M = fmaxf(M, a.part_ml[((int64_t)(i + b) * a.H + h) * 2]);
+    float L = 0.f;
     for (int i = i0; i <= i1; ++i) {
-      const float w = exp2f(a.part_ml[((int64_t)(i + b) * a.H + h) * 2] - M) * invL;
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(a.part_o + ((int64_t)(i + b) * a.H + h) * R + c);
-      acc += w * v;
+      const float *ml = a.part_ml + ((int64_t)(i + b) * a.H + h) * 2;
+      L += exp2f(ml[0] - M) * ml[1];
     }
+    const float invL = 1.0f / L;
+    for (int i = ln; i < np; i += 32)
+      wsh[hh][i] = exp2f(a.part_ml[((int64_t)(i0 + i + b) * a.H + h) * 2] - M) * invL;
+  }
+  __syncthreads();
+  if (h >= a.H) return;
+  constexpr int NJ = (R + 127) / 128;
+  f32x4 acc[NJ];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[c + e] = from_f32<T>(acc[e]);
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < np; ++i) {
+    const float w = wsh[hh][i];
+    const float *po = a.part_o + ((int64_t)(i0 + i + b) * a.H + h) * R;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = ln * 4 + 128 * j;
+      if (c < R) acc[j] += w * *reinterpret_cast<const f32x4 *>(po + c);
+    }
+  }
+  T *out = reinterpret_cast<T *>(a.o_lat) + ((int64_t)b * a.H + h) * R;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = ln * 4 + 128 * j;
+    if (c < R) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[c + e] = from_f32<T>(acc[j][e]);
+    }
+  }
+}
+
+// Absorption q_lat[b, h, :] = W_uk_h^T q_nope[b, h] (bf16): one workgroup per
+// (head, 128 latent channels, 64 sequences).  The head's W_uk rows (k = nope
+// channel, n = latent channel, n contiguous) are staged in LDS; the MFMA B
+// operand needs 8 consecutive k of one n per lane, read with the 16-bit
+// transposing LDS read (lane s of a 16-lane group addresses row k0 + s/4,
+// columns n0 + 4 (s%4) .. +3; lane i then holds rows k0..k0+3 of column
+// n0 + i).  q_nope rows are the A operand straight from global memory.
+constexpr int AB_N = 128, AB_M = 64;
+
+template <int DN>
+__global__ __launch_bounds__(256) void absorb_kernel(const bf16 *qn, int64_t ldq, const bf16 *wuk,
+                                                     int r, bf16 *qlat, int64_t ldo,
+                                                     int64_t head_stride, int B) {
+  constexpr int WP = AB_N + 8;  // LDS row pitch (elements)
+  __shared__ __attribute__((aligned(16))) bf16 Ws[DN * WP];
+  const int h = blockIdx.x, n0 = blockIdx.y * AB_N, b0 = blockIdx.z * AB_M;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  // stage W_uk_h[:, n0 .. n0 + 127]
+  for (int c = tid; c < DN * (AB_N / 8); c += 256) {
+    const int k = c / (AB_N / 8), cc = (c % (AB_N / 8)) * 8;
+    const int n = n0 + cc;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (n < r) v = *reinterpret_cast<const uint4 *>(wuk + ((int64_t)h * DN + k) * r + n);
+    *reinterpret_cast<uint4 *>(&Ws[k * WP + cc]) = v;
+  }
+  // A fragments: row b = b0 + 32 (wave & 1) + l32, k = 16 f + 8 g .. + 7
+  const int bm = b0 + 32 * (wave & 1) + l32;
+  bf16x8 af[DN / 16];
+#pragma unroll
+  for (int f = 0; f < DN / 16; ++f) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (bm < B) v = *reinterpret_cast<const uint4 *>(qn + (int64_t)bm * ldq + (int64_t)h * DN + 16 * f + 8 * g);
+    af[f] = __builtin_bit_cast(bf16x8, v);
+  }
+  __syncthreads();
+  // this wave: rows 32 (wave & 1) .., columns 64 (wave >> 1) + 32 t, t < 2
+  const int s16 = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int nb = 64 * (wave >> 1) + 32 * t;
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int f = 0; f < DN / 16; ++f) {
+      const bf16 *p = &Ws[(16 * f + 8 * g + (s16 >> 2)) * WP + nb + (lane & 16) + 4 * (s16 & 3)];
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p + 4 * WP));
+      const bf16x8 bfr = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f], bfr, acc, 0, 0, 0);
+    }
+    const int n = n0 + nb + l32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int bb = b0 + 32 * (wave & 1) + acc_row(e, lane);
+      if (bb < B && n < r) qlat[(int64_t)bb * ldo + (int64_t)h * head_stride + n] = (bf16)acc[e];
+    }
   }
 }
 
@@ -499,8 +581,20 @@ hipError_t launch_decode_attention(int dtype, int r, int dr, const DecodeAttnArg
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_absorb(int dtype, int dn, int r, int H, int B, const void *qn, int64_t ldq,
+                         const void *wuk, void *qlat, int64_t ldo, int64_t head_stride,
+                         hipStream_t st) {
+  if (dtype != BF16 || dn != 128 || r % 8 != 0) return hipErrorInvalidValue;
+  if (B <= 0) return hipSuccess;
+  dim3 grid(H, (r + AB_N - 1) / AB_N, (B + AB_M - 1) / AB_M);
+  hipLaunchKernelGGL(absorb_kernel<128>, grid, dim3(256), 0, st, (const bf16 *)qn, ldq,
+                     (const bf16 *)wuk, r, (bf16 *)qlat, ldo, head_stride, B);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_merge(int dtype, int r, const DecodeAttnArgs &a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
+  if (a.n_blocks + 1 > MERGE_MAXP) return hipErrorInvalidValue;  // piece weights must fit LDS
 #define MLA_MERGE_CASE(R_)                                                           \
   if (r == R_) return dtype == BF16 ? launch_merge_t<bf16, R_>(a, st) : launch_merge_t<float, R_>(a, st);
   MLA_MERGE_CASE(16)

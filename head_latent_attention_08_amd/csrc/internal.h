@@ -119,4 +119,12 @@ hipError_t launch_decode_merge(int dtype, int r, const DecodeAttnArgs &a,
 
 int decode_blocks();
 
+// q_lat[b, h, 0:r] = W_uk_h^T q_nope[b, h]: q_nope row b at qn + b*ldq + h*dn,
+// W_uk rows h*dn + k of length r, q_lat row b head h at qlat + b*ldo +
+// h*head_stride.  bf16 with dn = 128 only; anything else returns
+// hipErrorInvalidValue (the caller falls back to the general GEMM).
+hipError_t launch_absorb(int dtype, int dn, int r, int H, int B, const void *qn, int64_t ldq,
+                         const void *wuk, void *qlat, int64_t ldo, int64_t head_stride,
+                         hipStream_t st);
+
 }  // namespace mla

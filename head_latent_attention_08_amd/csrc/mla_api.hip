@@ -574,7 +574,11 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
           "decode rope q_pe");
   // 4. absorb: q_lat[b, h] = w_up_k_h^T q_nope[b, h]   (batched over heads)
   MLA_MARK(5);
-  {
+  if (c.dtype == MLA_DTYPE_BF16 && dn == 128) {
+    MLA_HIP(launch_absorb(c.dtype, dn, rkv, H, B, qn, (int64_t)H * dn, w->w_up_k, qlat,
+                          (int64_t)H * wl, wl, st),
+            "absorb");
+  } else {
     GemmDesc g;
     g.dtype = c.dtype;
     g.M = B;
