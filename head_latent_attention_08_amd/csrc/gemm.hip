@@ -204,6 +204,8 @@ constexpr int GB_LDS = GB_M * GB_CPITCH > 2 * GB_STAGE ? GB_M * GB_CPITCH : 2 * 
 
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left open (gfx9 encoding)
 constexpr int GB_VMCNT0 = (7 << 4) | (15 << 8);
+// at most n vector-memory operations of this wave outstanding
+#define GB_VMCNT(n) ((((n) & 15)) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
 __device__ inline int swz(int r, int k) { return r * GB_K + ((((k >> 3) ^ (r >> 1)) & 7) << 3) + (k & 7); }
 
@@ -397,55 +399,105 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
 // With one token per sequence the projections are weight-bandwidth bound:
 // every weight element is used by at most 64 rows.  A 256-thread workgroup
 // owns a 64x128 output tile and one K slice; the grid covers the N tiles times
-// a split of K chosen on the host so about two workgroups per CU stream
-// weights at once.  Slices write fp32 partial tiles; a second kernel adds the
-// slices in a fixed order (deterministic) and applies the column-range store
-// mapping.  Operand chunks of 64 k values go through two LDS stages with
-// register prefetch of the next chunk.
-constexpr int SK_M = 64, SK_N = 128, SK_K = 64, SK_PITCH = SK_K + 8;
+// a split of K chosen on the host.  Slices write fp32 partial tiles; a second
+// kernel adds the slices in a fixed order (deterministic) and applies the
+// column-range store mapping.  Operand chunks of 128 k values (256 bytes of
+// every row) are copied global -> LDS with global_load_lds through SK_NST
+// stages: one copy instruction moves four whole 256-byte row pieces, so each
+// weight row is fetched in long contiguous runs rather than scattered
+// 128-byte pieces, which keeps HBM pages open across the request.
+#ifndef SK_STAGES
+#define SK_STAGES 3
+#endif
+constexpr int SK_M = 64, SK_N = 128, SK_K = 128, SK_NST = SK_STAGES;
+constexpr int SK_STAGE = (SK_M + SK_N) * SK_K;    // elements per stage
+constexpr int SK_CPW = (SK_M + SK_N) / 4 / 4;      // copy instructions per wave per chunk
+// LDS position of element (r, k) of a stage operand: 128-element rows whose
+// 16-byte pieces are XOR-permuted by the row index, so the 32 consecutive rows
+// one MFMA fragment read touches fall in distinct banks.
+__device__ inline int swz_sk(int r, int k) {
+  return r * SK_K + ((((k >> 3) ^ r) & 15) << 3) + (k & 7);
+}
+
+// A pointer the whole wave holds, moved to scalar registers (inline-asm
+// scalar operands need it there even when the compiler computed it with
+// vector instructions).
+template <typename P> __device__ inline P *uniform_ptr(P *q) {
+  const uint64_t v = (uint64_t)q;
+  return reinterpret_cast<P *>(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                               (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
+}
+
+// Output column n (in column range st) of batch z under the column-range
+// mapping (head-major rows, optionally transposed); element (m, n) goes to
+// C + at(m).
+struct SkinnyCol {
+  bf16 *C;
+  int64_t ld, h, d, dh;
+  bool tr;
+  __device__ SkinnyCol(const GemmParams &p, int z, int st, int n) {
+    const int nn = n - SEG_FIELD(p, st, n_begin);
+    dh = SEG_FIELD(p, st, dh);
+    h = nn / dh;
+    d = nn - h * dh;
+    tr = SEG_FIELD(p, st, tr);
+    ld = SEG_FIELD(p, st, ld);
+    C = reinterpret_cast<bf16 *>(SEG_FIELD(p, st, C)) + (int64_t)z * p.strideC +
+        (tr ? 0 : SEG_FIELD(p, st, off) + d);
+  }
+  __device__ void store(const GemmParams &p, int m, float v) const {
+    const int b = m / p.S, sq = m - b * p.S;
+    const int64_t at = tr ? ((b * p.H + h) * dh + d) * p.S + sq : ((b * p.H + h) * p.S + sq) * ld;
+    C[at] = (bf16)v;
+  }
+};
 
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, float *part, int kslice) {
-  __shared__ __attribute__((aligned(16))) bf16 As[2][SK_M * SK_PITCH];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][SK_N * SK_PITCH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[SK_NST * SK_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
   const int g = lane >> 5, l32 = lane & 31;
   const int n0 = blockIdx.x * SK_N, ks = blockIdx.y, z = blockIdx.z;
   const int k_begin = ks * kslice;
   const int nk = kslice / SK_K;
-  const bf16 *A = reinterpret_cast<const bf16 *>(p.A) + (int64_t)z * p.strideA;
+  const bf16 *A = reinterpret_cast<const bf16 *>(p.A) + (int64_t)z * p.strideA + k_begin;
   // B rows: column ranges start at multiples of 128 (checked on the host)
   const int st = seg_of(p, n0);
   const int t_nb = SEG_FIELD(p, st, n_begin);
   const int64_t t_ldb = SEG_FIELD(p, st, ldb);
-  const bf16 *Bb = reinterpret_cast<const bf16 *>(SEG_FIELD(p, st, B)) + (int64_t)z * p.strideB;
+  const bf16 *Bb = reinterpret_cast<const bf16 *>(SEG_FIELD(p, st, B)) + (int64_t)z * p.strideB +
+                   (int64_t)(n0 - t_nb) * t_ldb + k_begin;
 
-  // staging: A rows tid/8 (+32), B rows tid/8 (+32, +64, +96); chunk tid%8
-  const int sr = tid >> 3, sc = (tid & 7) * 8;
-  const bf16 *pa0 = A + (int64_t)min(sr, p.M - 1) * p.lda + k_begin + sc;
-  const bf16 *pa1 = A + (int64_t)min(sr + 32, p.M - 1) * p.lda + k_begin + sc;
-  const bf16 *pb[4];
+  // Copy blocks of a chunk: 16 of A (rows 4b..4b+3) then 32 of B; wave w
+  // issues blocks w, w+4, ..  Lane l fills row 4b + l/16 at position l%16,
+  // which holds logical 16-byte piece (l%16) ^ (row % 16).  Rows past M or N
+  // are clamped (they only feed outputs that are never stored).
+  uint32_t doff[SK_CPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    pb[i] = Bb + (int64_t)(min(n0 + sr + 32 * i, p.N - 1) - t_nb) * t_ldb + k_begin + sc;
-  uint4 ra0, ra1, rb0, rb1, rb2, rb3;
-#define SK_FETCH(KK)                                                                  \
+  for (int q = 0; q < SK_CPW; ++q) {
+    const int blk = wave + 4 * q;  // 0..47
+    const bool is_a = blk < SK_M / 4;
+    const int row = 4 * (is_a ? blk : blk - SK_M / 4) + (lane >> 4);
+    const int j = (lane & 15) ^ (row & 15);
+    const int rc = is_a ? min(row, p.M - 1) : min(row, p.N - 1 - n0);
+    const int64_t ld = is_a ? p.lda : t_ldb;
+    doff[q] = (uint32_t)((rc * ld + j * 8) * (int64_t)sizeof(bf16));
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16 *)lds;
+#define SK_DMA(KK, STG)                                                               \
   do {                                                                                \
-    const int k_ = (KK);                                                              \
-    ra0 = *reinterpret_cast<const uint4 *>(pa0 + k_);                                 \
-    ra1 = *reinterpret_cast<const uint4 *>(pa1 + k_);                                 \
-    rb0 = *reinterpret_cast<const uint4 *>(pb[0] + k_);                               \
-    rb1 = *reinterpret_cast<const uint4 *>(pb[1] + k_);                               \
-    rb2 = *reinterpret_cast<const uint4 *>(pb[2] + k_);                               \
-    rb3 = *reinterpret_cast<const uint4 *>(pb[3] + k_);                               \
-  } while (0)
-#define SK_STASH(BUF)                                                                 \
-  do {                                                                                \
-    *reinterpret_cast<uint4 *>(&As[BUF][sr * SK_PITCH + sc]) = ra0;                   \
-    *reinterpret_cast<uint4 *>(&As[BUF][(sr + 32) * SK_PITCH + sc]) = ra1;            \
-    *reinterpret_cast<uint4 *>(&Bs[BUF][sr * SK_PITCH + sc]) = rb0;                   \
-    *reinterpret_cast<uint4 *>(&Bs[BUF][(sr + 32) * SK_PITCH + sc]) = rb1;            \
-    *reinterpret_cast<uint4 *>(&Bs[BUF][(sr + 64) * SK_PITCH + sc]) = rb2;            \
-    *reinterpret_cast<uint4 *>(&Bs[BUF][(sr + 96) * SK_PITCH + sc]) = rb3;            \
+    const bf16 *a_ = uniform_ptr(A + (KK)), *b_ = uniform_ptr(Bb + (KK));             \
+    _Pragma("unroll") for (int q = 0; q < SK_CPW; ++q) {                              \
+      const int blk = wave + 4 * q;                                                   \
+      const uint32_t m0_ =                                                            \
+          __builtin_amdgcn_readfirstlane(lds_base + (STG) * (SK_STAGE * 2) + blk * 1024); \
+      if (blk < SK_M / 4)                                                             \
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"             \
+                     :: "v"(doff[q]), "s"(a_), "s"(m0_) : "memory", "m0");            \
+      else                                                                            \
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"             \
+                     :: "v"(doff[q]), "s"(b_), "s"(m0_) : "memory", "m0");            \
+    }                                                                                 \
   } while (0)
 
   // wave tile: rows (wave / 2) * 32, columns (wave % 2) * 64 (two 32x32 tiles)
@@ -454,34 +506,54 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, float *p
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
 
-  SK_FETCH(0);
-  SK_STASH(0);
-  if (nk > 1) SK_FETCH(SK_K);
-  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < SK_NST - 1; ++c)
+    if (c < nk) SK_DMA(c * SK_K, c);
+  int cs = 0;  // stage of chunk kt
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
+    // this wave's copies of chunk kt have landed once at most the later
+    // chunks already issued (up to SK_NST - 2 of them) are outstanding; the
+    // barrier publishes every wave's copies and frees the stage read in the
+    // previous iteration for chunk kt + SK_NST - 1
+    const int later = min(nk - 1 - kt, SK_NST - 2);
+    if (later >= SK_NST - 2) __builtin_amdgcn_s_waitcnt(GB_VMCNT(SK_CPW * (SK_NST - 2)));
+    else if (SK_NST > 3 && later == 2) __builtin_amdgcn_s_waitcnt(GB_VMCNT(2 * SK_CPW));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(GB_VMCNT(SK_CPW));
+    else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
+    __syncthreads();
+    if (kt + SK_NST - 1 < nk) SK_DMA((kt + SK_NST - 1) * SK_K, cs == 0 ? SK_NST - 1 : cs - 1);
+    const bf16 *As = lds + cs * SK_STAGE, *Bs = As + SK_M * SK_K;
+    cs = cs == SK_NST - 1 ? 0 : cs + 1;
 #pragma unroll
     for (int kk = 0; kk < SK_K; kk += 16) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[buf][(wm * 32 + l32) * SK_PITCH + kk + g * 8]);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&Bs[buf][(wn * 64 + l32) * SK_PITCH + kk + g * 8]);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(&Bs[buf][(wn * 64 + 32 + l32) * SK_PITCH + kk + g * 8]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&As[swz_sk(wm * 32 + l32, kk + g * 8)]);
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&Bs[swz_sk(wn * 64 + l32, kk + g * 8)]);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(&Bs[swz_sk(wn * 64 + 32 + l32, kk + g * 8)]);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      SK_STASH(buf ^ 1);
-      if (kt + 2 < nk) SK_FETCH((kt + 2) * SK_K);
-    }
-    __syncthreads();
   }
-#undef SK_FETCH
-#undef SK_STASH
-  // fp32 partial tile [z][ks][M][N]
+#undef SK_DMA
+  // without a split of K the tile is final: store bf16 through the mapping;
+  // otherwise an fp32 partial tile [z][ks][M][N] for the reduce kernel
+  const int n = n0 + wn * 64 + l32;
+  if (gridDim.y == 1) {
+    // the 128 columns of a tile lie in one column range (st)
+    const SkinnyCol c0(p, z, st, min(n, p.N - 1)), c1(p, z, st, min(n + 32, p.N - 1));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = wm * 32 + acc_row(r, lane);
+      if (m < p.M) {
+        if (n < p.N) c0.store(p, m, acc0[r]);
+        if (n + 32 < p.N) c1.store(p, m, acc1[r]);
+      }
+    }
+    return;
+  }
   float *pt = part + (((int64_t)z * gridDim.y + ks) * p.M) * p.N;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = wm * 32 + acc_row(r, lane);
-    const int n = n0 + wn * 64 + l32;
     if (m < p.M) {
       if (n < p.N) pt[(int64_t)m * p.N + n] = acc0[r];
       if (n + 32 < p.N) pt[(int64_t)m * p.N + n + 32] = acc1[r];
@@ -499,28 +571,20 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce(GemmParams p, const fl
     const float *src = part + (int64_t)z * nsplit * total + i;
     float acc = 0.f;
     for (int s = 0; s < nsplit; ++s) acc += src[(int64_t)s * total];
-    const int st = seg_of(p, n);
-    const int nn = n - SEG_FIELD(p, st, n_begin);
-    const int dh = SEG_FIELD(p, st, dh);
-    const int h = nn / dh, d = nn - h * dh;
-    const int b = m / p.S, sq = m - b * p.S;
-    bf16 *C = reinterpret_cast<bf16 *>(SEG_FIELD(p, st, C)) + (int64_t)z * p.strideC;
-    const int64_t at = SEG_FIELD(p, st, tr)
-                           ? ((int64_t)(b * p.H + h) * dh + d) * p.S + sq
-                           : ((int64_t)(b * p.H + h) * p.S + sq) * SEG_FIELD(p, st, ld) +
-                                 SEG_FIELD(p, st, off) + d;
-    C[at] = (bf16)acc;
+    SkinnyCol(p, z, seg_of(p, n), n).store(p, m, acc);
   }
 }
 
 }  // namespace
 
 // Split of K the skinny kernel uses for an M <= 64 product: the largest
-// divisor of K/64 that keeps the grid near 512 workgroups.
+// divisor of K/128 that keeps the grid within one workgroup per CU (a stage
+// set fills most of a CU's LDS, and a second round of workgroups would leave
+// the tail of the launch running on a fraction of the chip).
 static int skinny_split(int N, int K, int batch) {
   const int ntile = (N + SK_N - 1) / SK_N;
   const int kchunks = K / SK_K;
-  const int want = (512 + ntile * batch - 1) / (ntile * batch);
+  const int want = std::max(1, 256 / (ntile * batch));
   int nsplit = 1;
   for (int c = 1; c <= kchunks; ++c)
     if (kchunks % c == 0 && c <= want) nsplit = c;
@@ -571,7 +635,7 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
       hipLaunchKernelGGL(gemm_skinny_kernel, dim3(ntile, nsplit, d.batch), dim3(256), 0, st, p,
                          part, d.K / nsplit);
       hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      if (e != hipSuccess || nsplit == 1) return e;
       const int64_t total = (int64_t)d.M * d.N;
       const unsigned rb = (unsigned)std::min<int64_t>((total + 255) / 256, 2048);
       hipLaunchKernelGGL(gemm_skinny_reduce, dim3(rb, d.batch), dim3(256), 0, st, p, part, nsplit);
