@@ -373,26 +373,25 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
     }
     }  // pass
 
-    // partial of this sequence piece: unnormalised o_lat (log2-domain max, sum)
+    // partial of this sequence piece: unnormalised o_lat (log2-domain max,
+    // sum).  o_lat is stored in the accumulator layout, 32 heads x RP
+    // channels per block: channel tile d, row quad q, lane, 4 floats, so each
+    // store instruction writes 1 KB of consecutive bytes.
     if (wave_live) {
       const float l_tot = l_run + __shfl_xor(l_run, 32);
-      if (h < H) {
-        const int slot = blk + b;
-        float *po = a.part_o + ((int64_t)slot * H + h) * R;
+      const int slot = blk + b;
+      float *po = a.part_o + ((int64_t)slot * ((H + HPW - 1) / HPW) + hg * (HPB / HPW) + wave) *
+                                 (HPW * NCT * 32) + lane * 4;
 #pragma unroll
-        for (int d = 0; d < NCT; ++d)
+      for (int d = 0; d < NCT; ++d)
 #pragma unroll
-          for (int r = 0; r < 16; r += 4) {
-            const int c = d * 32 + acc_row(r, lane);
-            if (c + 4 <= R) {
-              f32x4 v = {o[d][r], o[d][r + 1], o[d][r + 2], o[d][r + 3]};
-              *reinterpret_cast<f32x4 *>(po + c) = v;
-            }
-          }
-        if (g == 0) {
-          a.part_ml[((int64_t)slot * H + h) * 2 + 0] = m_ref * sl2;
-          a.part_ml[((int64_t)slot * H + h) * 2 + 1] = l_tot;
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v = {o[d][4 * q], o[d][4 * q + 1], o[d][4 * q + 2], o[d][4 * q + 3]};
+          *reinterpret_cast<f32x4 *>(po + (d * 4 + q) * 256) = v;
         }
+      if (h < H && g == 0) {
+        a.part_ml[((int64_t)slot * H + h) * 2 + 0] = m_ref * sl2;
+        a.part_ml[((int64_t)slot * H + h) * 2 + 1] = l_tot;
       }
     }
     r0 = seg_end;
@@ -403,14 +402,21 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
 
 // Combine the pieces of sequence b: o_lat = sum_i w_i O_i / sum_i w_i l_i,
 // w_i = exp2(m_i - max_i m_i).  A sequence with no valid rows gets NaN.
-// One workgroup per (sequence, group of 8 heads).
-constexpr int MERGE_HEADS = 8;
+// One workgroup per (sequence, block of 32 heads).  A piece's block is 32
+// heads x RP channels in the attention kernel's accumulator layout (16-byte
+// chunk k holds lane k % 64 of accumulator quad k / 64: head k % 32,
+// channels (k / 256) * 32 + (k / 64 % 4) * 8 + (k % 64 / 32) * 4 + 0..3), so
+// thread t reads chunks t, t + 256, .. -- whole 1 KB runs per wave -- and
+// they all belong to one head.
 constexpr int MERGE_MAXP = 264;  // pieces per sequence: at most n_blocks + 1
 
 template <typename T, int R>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
+  constexpr int RP = (R + 31) / 32 * 32;
+  constexpr int NCH = HPW * RP / 4 / 256;  // chunks per thread (RP / 32)
   __shared__ int sh[2];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ float wsh[HPW][MERGE_MAXP], lsh[HPW][MERGE_MAXP];
+  const int b = blockIdx.x, hb = blockIdx.y, tid = threadIdx.x;
   if (tid < 64) {
     int before = 0, all = 0;
     for (int i = tid; i < a.B; i += 64) {
@@ -431,57 +437,85 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
   __syncthreads();
   const int start = sh[0], total = sh[1];
   const int n_b = seq_rows(a.lens, b, a.cap);
-  const int h0 = blockIdx.y * MERGE_HEADS;
+  const int lane = tid & 63, hl = lane & 31, g = lane >> 5;
+  const int h = hb * HPW + hl;
+  T *out = reinterpret_cast<T *>(a.o_lat) + ((int64_t)b * a.H + h) * R;
   if (n_b == 0) {
-    for (int i = tid; i < MERGE_HEADS * R; i += 256) {
-      const int h = h0 + i / R;
-      if (h < a.H) reinterpret_cast<T *>(a.o_lat)[((int64_t)b * a.H + h) * R + i % R] = from_f32<T>(NAN);
-    }
+    if (h < a.H)
+      for (int k = 0; k < NCH; ++k) {
+        const int c = (k * 4 + (tid >> 6)) * 8 + g * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < R) out[c + e] = from_f32<T>(NAN);
+      }
     return;
   }
   const int per = (total + a.n_blocks - 1) / a.n_blocks;
   const int i0 = start / per, i1 = (start + n_b - 1) / per;
-  // 32 threads per head; each thread owns channels 4 t + 128 j.  The piece
-  // weights w_i / L go to LDS first; then every piece costs each thread NJ
-  // independent 16-byte loads.
-  __shared__ float wsh[MERGE_HEADS][MERGE_MAXP];
-  const int hh = tid >> 5, ln = tid & 31;
-  const int h = h0 + hh;
   const int np = i1 - i0 + 1;  // <= n_blocks + 1 <= MERGE_MAXP (checked on the host)
-  if (h < a.H) {
-    float M = -INFINITY;
-    for (int i = i0; i <= i1; ++i) M = fmaxf(M, a.part_ml[((int64_t)(i + b) * a.H + h) * 2]);
-    float L = 0.f;
-    for (int i = i0; i <= i1; ++i) {
-      const float *ml = a.part_ml + ((int64_t)(i + b) * a.H + h) * 2;
-      L += exp2f(ml[0] - M) * ml[1];
-    }
-    const float invL = 1.0f / L;
-    for (int i = ln; i < np; i += 32)
-      wsh[hh][i] = exp2f(a.part_ml[((int64_t)(i0 + i + b) * a.H + h) * 2] - M) * invL;
+  // piece weights w_i / L of the block's heads: the (max, sum) pairs of all
+  // pieces are loaded in parallel into LDS, then one thread per head reduces
+  for (int idx = tid; idx < HPW * np; idx += 256) {
+    const int hw = idx % HPW, i = idx / HPW;
+    float2 ml = make_float2(-INFINITY, 0.f);
+    if (hb * HPW + hw < a.H)
+      ml = *reinterpret_cast<const float2 *>(a.part_ml + ((int64_t)(i0 + i + b) * a.H + hb * HPW + hw) * 2);
+    wsh[hw][i] = ml.x;
+    lsh[hw][i] = ml.y;
   }
   __syncthreads();
-  if (h >= a.H) return;
-  constexpr int NJ = (R + 127) / 128;
-  f32x4 acc[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < np; ++i) {
-    const float w = wsh[hh][i];
-    const float *po = a.part_o + ((int64_t)(i0 + i + b) * a.H + h) * R;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = ln * 4 + 128 * j;
-      if (c < R) acc[j] += w * *reinterpret_cast<const f32x4 *>(po + c);
-    }
+  if (tid < HPW) {
+    float M = -INFINITY;
+    for (int i = 0; i < np; ++i) M = fmaxf(M, wsh[tid][i]);
+    float L = 0.f;
+    for (int i = 0; i < np; ++i) L += exp2f(wsh[tid][i] - M) * lsh[tid][i];
+    const float invL = 1.0f / L;
+    for (int i = 0; i < np; ++i) wsh[tid][i] = exp2f(wsh[tid][i] - M) * invL;
   }
-  T *out = reinterpret_cast<T *>(a.o_lat) + ((int64_t)b * a.H + h) * R;
+  __syncthreads();
+  const int n_hb = (a.H + HPW - 1) / HPW;
+  f32x4 acc[NCH];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int c = ln * 4 + 128 * j;
-    if (c < R) {
+  for (int k = 0; k < NCH; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (h < a.H) {
+    // two register sets: the loads of piece i + 1 are in flight while piece
+    // i is accumulated (loads past the last piece re-read it and are not
+    // used; unconditional loads keep the wait counts exact)
+    const f32x4 *po = reinterpret_cast<const f32x4 *>(
+        a.part_o + ((int64_t)(i0 + b) * n_hb + hb) * (HPW * RP)) + tid;
+    const int64_t pstride = (int64_t)n_hb * HPW * RP / 4;  // f32x4 per piece
+    f32x4 va[NCH], vb[NCH];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[c + e] = from_f32<T>(acc[j][e]);
+    for (int k = 0; k < NCH; ++k) va[k] = po[k * 256];
+    for (int i = 0; i < np; i += 2) {
+      const f32x4 *pb = po + min(i + 1, np - 1) * pstride;
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) vb[k] = pb[k * 256];
+      const float wa = wsh[hl][i];
+      const float wb = i + 1 < np ? wsh[hl][i + 1] : 0.f;
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) acc[k] += wa * va[k];
+      const f32x4 *pa = po + min(i + 2, np - 1) * pstride;
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) va[k] = pa[k * 256];
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) acc[k] += wb * vb[k];
+    }
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int c = (k * 4 + (tid >> 6)) * 8 + g * 4;
+      if constexpr (sizeof(T) == 2 && R % 4 == 0) {
+        if (c < R) {
+          const bf16x2 lo = {from_f32<T>(acc[k][0]), from_f32<T>(acc[k][1])};
+          const bf16x2 hi = {from_f32<T>(acc[k][2]), from_f32<T>(acc[k][3])};
+          *reinterpret_cast<uint2 *>(out + c) =
+              make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < R) out[c + e] = from_f32<T>(acc[k][e]);
+      }
     }
   }
 }
@@ -557,7 +591,7 @@ hipError_t launch_t(const DecodeAttnArgs &a, hipStream_t st) {
 
 template <typename T, int R>
 hipError_t launch_merge_t(const DecodeAttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_merge_kernel<T, R>), dim3(a.B, (a.H + MERGE_HEADS - 1) / MERGE_HEADS),
+  hipLaunchKernelGGL((decode_merge_kernel<T, R>), dim3(a.B, (a.H + HPW - 1) / HPW),
                      dim3(256), 0, st, a);
   return hipGetLastError();
 }

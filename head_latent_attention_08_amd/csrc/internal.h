@@ -104,7 +104,8 @@ struct DecodeAttnArgs {
   const void *cache;  // [B, cap, r + dr]
   const int32_t *lens;
   void *o_lat;        // [B, H, r]
-  float *part_o;      // [(n_blocks + B), H, r]
+  float *part_o;      // [(n_blocks + B), ceil(H/32)] blocks of 32 heads x r padded to 32
+                      // (MFMA accumulator order)
   float *part_ml;     // [(n_blocks + B), H, 2]
   int64_t cap;
   int B, H;

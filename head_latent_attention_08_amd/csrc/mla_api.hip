@@ -227,7 +227,9 @@ DecodePlan plan_decode(const mla_config &c, int64_t B) {
   p.off_down = take((size_t)B * p.ld_down * es);
   p.off_qn = take((size_t)B * H * c.qk_nope_head_dim * es);
   p.off_qlat = take((size_t)B * H * (r + dr) * es);
-  p.off_po = take((size_t)(p.n_blocks + B) * H * r * sizeof(float));
+  // attention partials: blocks of 32 heads x (r rounded up to 32) channels
+  p.off_po = take((size_t)(p.n_blocks + B) * ((H + 31) / 32) * 32 * ((r + 31) / 32 * 32) *
+                  sizeof(float));
   p.off_pml = take((size_t)(p.n_blocks + B) * H * 2 * sizeof(float));
   p.off_olat = take((size_t)B * H * r * es);
   p.off_o = take((size_t)B * H * c.v_head_dim * es);
