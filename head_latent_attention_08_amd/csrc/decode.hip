@@ -61,7 +61,14 @@ struct DecCfg {
   static constexpr int W = R + DR;
   static constexpr int WP = (W + MF::KSTEP - 1) / MF::KSTEP * MF::KSTEP;
   static constexpr int RP = (R + 31) / 32 * 32;
-  static constexpr int CPITCH = (WP > RP ? WP : RP) + VEC;  // 1168 B at V3 sizes
+  // Rows whose width is a whole number of 128-byte groups (bf16 at V3
+  // sizes: 1152 B) are stored unpadded with their 16-byte chunks permuted
+  // within each group of eight (dec_swz), which keeps both the row-wise
+  // 16-byte reads of the score step and the transposing 8-byte reads of the
+  // output step free of bank conflicts, and makes a stage an exact number of
+  // copy instructions.  Other shapes use a padded pitch.
+  static constexpr bool SWZ = sizeof(T) == 2 && (W * 2) % 128 == 0 && WP == W && RP <= W;
+  static constexpr int CPITCH = SWZ ? W : (WP > RP ? WP : RP) + VEC;
   static constexpr int ROWB = CPITCH * (int)sizeof(T);       // row pitch in bytes
   // a stage is whole 1 KB blocks: one DMA instruction fills 64 lanes x 16 B
   static constexpr int NINS = (TK * ROWB + 1023) / 1024;
@@ -75,6 +82,15 @@ struct DecCfg {
 };
 
 constexpr int NSTAGE = 3;  // cache tiles in flight: current, next, and the one after
+
+// Chunk permutation of the swizzled stage layout: in row r, logical 16-byte
+// chunk c sits at position (c & ~7) | ((c & 7) ^ dec_swz(r)).  Rows 2m and
+// 2m+1 share a value and fall 32 banks apart; the values of the eight pairs
+// in 16 rows are distinct, and rows 4i, 4i+2 differ in bit 2.
+__device__ inline int dec_swz(int row) {
+  const int m = (row >> 1) & 7;
+  return ((m & 1) << 2) | (m >> 1);
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (gfx9 encoding; expcnt and lgkmcnt left open).
@@ -100,7 +116,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
   extern __shared__ int starts[];  // [B + 1]
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
   const int g = lane >> 5, l32 = lane & 31;
   const int B = a.B, H = a.H;
   const int n_hg = (H + HPB - 1) / HPB;
@@ -141,8 +157,15 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
   int r0 = blk * per;
   const int r1 = min(r0 + per, total);
   if (r0 >= r1) return;
+  // first sequence holding row r0: the number of sequences ending at or
+  // before it (row-count prefix sums are non-decreasing), one ballot per 64
   int b = 0;
-  while (starts[b + 1] <= r0) ++b;  // first sequence holding row r0
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int i = c0 + lane;
+    const int n = __popcll(__ballot(i < B && starts[i + 1] <= r0));
+    b += n;
+    if (n < 64) break;
+  }
 
   const float sl2 = a.scale * LOG2E;
   const char *cache = reinterpret_cast<const char *>(a.cache);
@@ -159,9 +182,20 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
     const int o = (wave + 4 * k) * 1024 + lane * 16;
     const int row = o / ROWB, cbyte = o - row * ROWB;
     const bool ok = wave + 4 * k < NINS && row < TK && cbyte < W * (int)sizeof(T);
-    dof[k] = ok ? (uint32_t)(row * W * (int)sizeof(T) + cbyte) : 0u;
+    int src = cbyte;  // byte of the cache row this lane's 16 bytes come from
+    if constexpr (C::SWZ) {
+      const int pch = cbyte >> 4;
+      src = ((pch & ~7) | ((pch & 7) ^ dec_swz(row))) << 4;
+    }
+    dof[k] = ok ? (uint32_t)(row * W * (int)sizeof(T) + src) : 0u;
     drow[k] = ok ? row : 0;
   }
+
+  // swizzled layout: element offset of this lane's score-step chunk
+  // 2 f + g of row l32 is kofs[f % 4] + 64 (f / 4)
+  int kofs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kofs[i] = l32 * CPITCH + (((2 * i + g) ^ dec_swz(l32)) << 3);
 
   while (r0 < r1) {
     const int seg_end = min(r1, starts[b + 1]);
@@ -178,27 +212,40 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
     // Written as inline asm with explicit vmcnt waits: the compiler builtin for
     // this load makes every later LDS read wait for all outstanding copies,
     // which would serialise the two-tiles-ahead pipeline.
-#define DEC_DMA(STG, T0)                                                                 \
-  do {                                                                                   \
-    const int t0_ = (T0);                                                                \
-    const uint64_t r0a_ = (uint64_t)(cb + (int64_t)t0_ * W * (int64_t)sizeof(T));        \
-    const char *row0_ = reinterpret_cast<const char *>(                                  \
+#define DEC_ROW0(T0)                                                                     \
+  [&] {                                                                                  \
+    const uint64_t r0a_ = (uint64_t)(cb + (int64_t)(T0) * W * (int64_t)sizeof(T));       \
+    return reinterpret_cast<const char *>(                                               \
         ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(r0a_ >> 32)) << 32) |       \
         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)r0a_));             \
-    const int lim_ = t_end - t0_;                                                        \
-    _Pragma("unroll") for (int k = 0; k < NPW; ++k) {                                    \
-      const int ins = wave + 4 * k;                                                      \
-      if (ins < NINS) {                                                                  \
-        const uint32_t off_ = drow[k] < lim_ ? dof[k] : 0u;                              \
-        const uint32_t m0 = lds_base + (STG) * STAGEB + ins * 1024;                     \
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"                \
-                     :                                                                   \
-                     : "v"(off_), "s"(row0_), "s"(m0)                                    \
-                     : "memory", "m0");                                                  \
-      }                                                                                  \
+  }()
+    // copy instruction k of this wave for the tile whose first row is ROW0
+    // (LIM rows of it valid) into stage STG
+#define DEC_DMA_INS(STG, ROW0, LIM, K)                                                   \
+  do {                                                                                   \
+    const int ins_ = wave + 4 * (K);                                                     \
+    if ((K) < NPW && ins_ < NINS) {                                                      \
+      const uint32_t off_ = drow[(K) < NPW ? (K) : 0] < (LIM) ? dof[(K) < NPW ? (K) : 0] : 0u; \
+      const uint32_t m0 = lds_base + (STG) * STAGEB + ins_ * 1024;                       \
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"                    \
+                   :                                                                     \
+                   : "v"(off_), "s"(ROW0), "s"(m0)                                       \
+                   : "memory", "m0");                                                    \
     }                                                                                    \
   } while (0)
+#define DEC_DMA(STG, T0)                                                                 \
+  do {                                                                                   \
+    const char *row0_ = DEC_ROW0(T0);                                                    \
+    const int lim_ = t_end - (T0);                                                       \
+    _Pragma("unroll") for (int k = 0; k < NPW; ++k) DEC_DMA_INS(STG, row0_, lim_, k);    \
+  } while (0)
 
+    const int ntiles = (t_end - t_begin + TK - 1) / TK;
+    // Query fragments first (the loads of all workgroups at once are the
+    // start-up burst; copies issued before them would stall the wave at
+    // issue).  Then every wave has left the previous piece's tile loop, so
+    // its stages and query rows are free for the query rows and the first
+    // two tiles.
     // B operand of S^T = C Q^T: lane holds head l32, k values g*KPL.. of a step
     typename MF::frag qf[NQR];
     const T *qp = reinterpret_cast<const T *>(a.q_lat) + ((int64_t)b * H + h) * W;
@@ -217,28 +264,10 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
         }
       }
     }
-    f32x16 o[NCT];
-    float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
-    bool ovf = false;
-    const int ntiles = (t_end - t_begin + TK - 1) / TK;
-    // The softmax reference max is fixed at the first tile, so the
-    // accumulators are never rescaled inside the loop (they stay in the MFMA
-    // accumulation registers).  A score more than 2^64 above it sets ovf and
-    // the segment is run a second time with the true max, known by then.
-    for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 1) {
-      if (!__syncthreads_or(ovf)) break;
-      m_ref = m_true;
-      ovf = false;
-    }
-#pragma unroll
-    for (int d = 0; d < NCT; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
-    l_run = 0.f;
-    __syncthreads();  // every stage of the previous piece has been consumed
+    __syncthreads();
     if constexpr (NQL > 0) {
-      // query channels NQR*KSTEP.. of this workgroup's heads
+      // query channels NQR*KSTEP.. of this workgroup's heads; the first
+      // tile's barrier publishes them
       constexpr int QCH = NQL * MF::KSTEP / VEC;
       for (int i = tid; i < HPB * QCH; i += DTHREADS) {
         const int hh = i / QCH, cc = (i - hh * QCH) * VEC;
@@ -250,8 +279,29 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
         *reinterpret_cast<uint4 *>(&Qs[hh * QPITCH + cc]) = v;
       }
     }
-    DEC_DMA(0, t_begin);
+    if (ntiles > 0) DEC_DMA(0, t_begin);
     if (ntiles > 1) DEC_DMA(1, t_begin + TK);
+    f32x16 o[NCT];
+    float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.f;
+    bool ovf = false;
+    // The softmax reference max is fixed at the first tile, so the
+    // accumulators are never rescaled inside the loop (they stay in the MFMA
+    // accumulation registers).  A score more than 2^64 above it sets ovf and
+    // the segment is run a second time with the true max, known by then.
+    for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+      // every wave is past its tile loop here, so the stages are free
+      if (!__syncthreads_or(ovf)) break;
+      m_ref = m_true;
+      ovf = false;
+      DEC_DMA(0, t_begin);
+      if (ntiles > 1) DEC_DMA(1, t_begin + TK);
+    }
+#pragma unroll
+    for (int d = 0; d < NCT; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    l_run = 0.f;
     int rd = 0;
     for (int it = 0; it < ntiles; ++it) {
       const int t0 = t_begin + it * TK;
@@ -265,8 +315,17 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
         __builtin_amdgcn_s_waitcnt(DEC_VMCNT(0));
       }
       __syncthreads();
-      // stage rd holds tile it; tile it + 2 goes to the stage read last time
-      if (it + 2 < ntiles) DEC_DMA(rd == 0 ? NSTAGE - 1 : rd - 1, t0 + 2 * TK);
+      // stage rd holds tile it; tile it + 2 goes to the stage read last time.
+      // A live wave spreads its copy instructions over the score MFMAs (issued
+      // in a burst, the copies of all four waves queue behind each other).
+      const bool dma_next = it + 2 < ntiles;
+      const int dstg = rd == 0 ? NSTAGE - 1 : rd - 1;
+      const char *drow0 = DEC_ROW0(t0 + 2 * TK);
+      const int dlim = t_end - (t0 + 2 * TK);
+      if (!wave_live && dma_next) {
+#pragma unroll
+        for (int k = 0; k < NPW; ++k) DEC_DMA_INS(dstg, drow0, dlim, k);
+      }
       const T *cs = reinterpret_cast<const T *>(lds + __builtin_amdgcn_readfirstlane(rd * STAGEB));
       rd = rd == NSTAGE - 1 ? 0 : rd + 1;
       if (wave_live) {
@@ -285,7 +344,8 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
         KA[e] = to_f32(cs[l32 * CPITCH + c_]);                                        \
         if (f_ >= NQR) QA[e] = to_f32(Qs[(wave * HPW + l32) * QPITCH + c_ - NQR * MF::KSTEP]); \
       } else {                                                                        \
-        KA[e] = *reinterpret_cast<const typename MF::frag *>(&cs[l32 * CPITCH + c_]); \
+        KA[e] = *reinterpret_cast<const typename MF::frag *>(                          \
+            &cs[C::SWZ ? kofs[f_ & 3] + 64 * (f_ >> 2) : l32 * CPITCH + c_]);           \
         if (f_ >= NQR)                                                                \
           QA[e] = *reinterpret_cast<const typename MF::frag *>(                       \
               &Qs[(wave * HPW + l32) * QPITCH + c_ - NQR * MF::KSTEP]);               \
@@ -298,8 +358,15 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
     if (f_ < NQF) st = MF::mma(KA[e], f_ < NQR ? qf[f_ < NQR ? f_ : 0] : QA[e], st);  \
   }
         DEC_KLOAD(ka, qa, 0)
+        constexpr int NIT = (NQF + 3) / 4;  // score steps of four MFMAs
 #pragma unroll
         for (int f0 = 0; f0 < NQF; f0 += 4) {
+          if (dma_next) {
+            // copy instructions [j NPW / NIT, (j + 1) NPW / NIT) at step j
+#pragma unroll
+            for (int k = f0 / 4 * NPW / NIT; k < (f0 / 4 + 1) * NPW / NIT; ++k)
+              DEC_DMA_INS(dstg, drow0, dlim, k);
+          }
           DEC_KLOAD(kb, qb, f0 + 2)
           __builtin_amdgcn_sched_barrier(0);
           DEC_KMMA(ka, qa, f0)
@@ -341,6 +408,23 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
           // score accumulator layout
           const int s16 = lane & 15;
           const T *pb0 = &cs[(4 * g + (s16 >> 2)) * CPITCH + (lane & 16) + 4 * (s16 & 3)];
+          // swizzled layout: rows 16u + 4g + s16/4 (+ 8 for the upper four
+          // keys), chunk 4D + x, x = (lane & 16)/8 + (s16 & 3)/2; the permuted
+          // position is 4 (D ^ fb) + (x ^ (f & 3)), fb = f / 4, so the offset
+          // is a per-lane base +- 32 fb for even / odd D plus 32 D
+          int vofs[2][2][2];  // [u][upper][D odd]
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {
+              const int rr = 16 * u + 4 * g + (s16 >> 2) + 8 * hi;
+              const int fr = dec_swz(rr);
+              const int x = ((lane & 16) >> 3) + ((s16 & 3) >> 1);
+              const int base = rr * CPITCH + ((x ^ (fr & 3)) << 3) + 4 * (s16 & 1);
+              const int fb = fr >> 2;
+              vofs[u][hi][0] = base + 32 * fb;
+              vofs[u][hi][1] = base - 32 * fb;
+            }
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             typename MF::frag pf;
@@ -349,11 +433,12 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
             typename MF::frag vf[NCT];
 #define DEC_VLOAD(D)                                                                    \
   if ((D) < NCT) {                                                                      \
-    const T *p_ = pb0 + u * 16 * CPITCH + (D) * 32;                                     \
+    const T *p_ = C::SWZ ? cs + vofs[u][0][(D) & 1] + (D) * 32 : pb0 + u * 16 * CPITCH + (D) * 32; \
+    const T *q_ = C::SWZ ? cs + vofs[u][1][(D) & 1] + (D) * 32 : p_ + 8 * CPITCH;      \
     const s16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                          \
         (__attribute__((address_space(3))) s16x4 *)(p_));                               \
     const s16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                          \
-        (__attribute__((address_space(3))) s16x4 *)(p_ + 8 * CPITCH));                  \
+        (__attribute__((address_space(3))) s16x4 *)(q_));                               \
     vf[(D) < NCT ? (D) : 0] =                                                           \
         __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7)); \
   }
@@ -398,6 +483,8 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
     ++b;
   }
 #undef DEC_DMA
+#undef DEC_DMA_INS
+#undef DEC_ROW0
 }
 
 // Combine the pieces of sequence b: o_lat = sum_i w_i O_i / sum_i w_i l_i,
