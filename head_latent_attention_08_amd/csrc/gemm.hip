@@ -197,17 +197,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 // every thread stores 16-byte runs of 8 consecutive columns, which fall in one
 // head of the destination (all column ranges and head widths are multiples of
 // 8), so the head-scatter store stays vectorised.
-constexpr int GB_M = 256, GB_N = 256, GB_K = 64, GB_THREADS = 256;
+constexpr int GB_M = 256, GB_N = 256, GB_K = 32, GB_THREADS = 256, GB_NST = 4;
 constexpr int GB_CPITCH = GB_N + 8;               // epilogue LDS pitch (elements)
 constexpr int GB_STAGE = (GB_M + GB_N) * GB_K;    // elements per operand stage
-constexpr int GB_LDS = GB_M * GB_CPITCH > 2 * GB_STAGE ? GB_M * GB_CPITCH : 2 * GB_STAGE;
+constexpr int GB_LDS = GB_M * GB_CPITCH > GB_NST * GB_STAGE ? GB_M * GB_CPITCH : GB_NST * GB_STAGE;
 
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left open (gfx9 encoding)
 constexpr int GB_VMCNT0 = (7 << 4) | (15 << 8);
 // at most n vector-memory operations of this wave outstanding
 #define GB_VMCNT(n) ((((n) & 15)) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
-__device__ inline int swz(int r, int k) { return r * GB_K + ((((k >> 3) ^ (r >> 1)) & 7) << 3) + (k & 7); }
+// LDS position of element (r, k) of a 32-wide operand slab: 64-byte rows whose
+// four 16-byte chunks are XOR-permuted by (r / 4) % 4, so the 16 consecutive
+// rows one fragment read of a quarter wave touches fall in distinct banks.
+__device__ inline int swz(int r, int k) { return r * GB_K + ((((k >> 3) ^ (r >> 2)) & 3) << 3) + (k & 7); }
 
 __device__ inline int seg_of(const GemmParams &p, int n) {
   return (p.nseg > 1 && n >= p.seg[1].n_begin) ? ((p.nseg > 2 && n >= p.seg[2].n_begin) ? 2 : 1) : 0;
@@ -216,6 +219,15 @@ __device__ inline int seg_of(const GemmParams &p, int n) {
 // Fields of column range s, read with constant indices only (a dynamic index
 // into the kernel-argument struct would copy it to scratch memory).
 #define SEG_FIELD(p, s, f) ((s) == 0 ? (p).seg[0].f : ((s) == 1 ? (p).seg[1].f : (p).seg[2].f))
+
+// A pointer the whole wave holds, moved to scalar registers (inline-asm
+// scalar operands need it there even when the compiler computed it with
+// vector instructions).
+template <typename P> __device__ inline P *uniform_ptr(P *q) {
+  const uint64_t v = (uint64_t)q;
+  return reinterpret_cast<P *>(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                               (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
+}
 
 __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int tiles_m,
                                                               int tiles_n, int remap, int group_m) {
@@ -239,48 +251,48 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   const int g = lane >> 5, l32 = lane & 31;
   const bf16 *A = reinterpret_cast<const bf16 *>(p.A);
 
-  // Slabs are copied from global memory straight into LDS
+  // Slabs of 32 k are copied from global memory straight into LDS
   // (global_load_lds_dwordx4: lane l of a copy writes the 16 bytes at LDS
-  // offset 16 l of a 1 KB block, i.e. eight 128-byte slab rows), so no
+  // offset 16 l of a 1 KB block, i.e. sixteen 64-byte slab rows), so no
   // staging registers and no LDS store instructions are involved.  A slab
-  // is 32 blocks; block b of A (or B) holds rows 8b..8b+7, and lane l fills
-  // row 8b + l/8 at position l%8, where the swizzle keeps logical chunk
-  // (l%8) ^ (row/2 % 8).  Wave w issues blocks w, w+4, ... of A then of B;
-  // each lane's source offset of each of its 16 blocks is fixed for the
-  // whole K loop (rows clamped into the matrix: rows past M or N only feed
-  // outputs that are never stored), and the slab's k offset moves the
-  // scalar base.  Column ranges start at multiples of 256 (checked on the
-  // host), so one tile reads B from a single range.
+  // is 32 blocks; block b of A (or B) holds rows 16b..16b+15, and lane l
+  // fills row 16b + l/4 at position l%4, which holds logical chunk
+  // (l%4) ^ (row/4 % 4).  Wave w issues blocks w, w+4, .. of A then of B;
+  // each lane's source offset of each of its 8 blocks is fixed for the whole
+  // K loop (rows clamped into the matrix: rows past M or N only feed outputs
+  // that are never stored), and the slab's k offset moves the scalar base.
+  // Column ranges start at multiples of 256 (checked on the host), so one
+  // tile reads B from a single range.
   const int st = seg_of(p, n0);
   const int64_t t_ldb = SEG_FIELD(p, st, ldb);
   const int t_nb = SEG_FIELD(p, st, n_begin);
   const bf16 *Ab = A + (int64_t)m0 * p.lda;
   const bf16 *Bb = reinterpret_cast<const bf16 *>(SEG_FIELD(p, st, B)) + (int64_t)(n0 - t_nb) * t_ldb;
-  uint32_t doff[16];
+  uint32_t doff[8];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int blk = wave + 4 * (q & 7);
-    const int row = 8 * blk + (lane >> 3);
-    const int j = (lane & 7) ^ ((row >> 1) & 7);
-    const int rc = q < 8 ? min(row, p.M - 1 - m0) : min(row, p.N - 1 - n0);
-    const int64_t ld = q < 8 ? p.lda : t_ldb;
+  for (int q = 0; q < 8; ++q) {
+    const int blk = wave + 4 * (q & 3);
+    const int row = 16 * blk + (lane >> 2);
+    const int j = (lane & 3) ^ ((row >> 2) & 3);
+    const int rc = q < 4 ? min(row, p.M - 1 - m0) : min(row, p.N - 1 - n0);
+    const int64_t ld = q < 4 ? p.lda : t_ldb;
     doff[q] = (uint32_t)((rc * ld + j * 8) * (int64_t)sizeof(bf16));
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16 *)lds;
-#define GB_DMA(K0, STG)                                                           \
+  // copy q (0..7) of slab KT into stage KT % GB_NST
+#define GB_DMA1(KT, Q)                                                            \
   do {                                                                            \
-    const bf16 *a_ = Ab + (K0), *b_ = Bb + (K0);                                  \
-    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                              \
-      const int blk = wave + 4 * (q & 7);                                         \
-      const uint32_t m0_ = lds_base + (STG) * (GB_STAGE * 2) +                    \
-                           (q < 8 ? 0 : GB_M * GB_K * 2) + blk * 1024;            \
-      if (q < 8)                                                                  \
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"         \
-                     :: "v"(doff[q]), "s"(a_), "s"(m0_) : "memory", "m0");        \
-      else                                                                        \
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"         \
-                     :: "v"(doff[q]), "s"(b_), "s"(m0_) : "memory", "m0");        \
-    }                                                                             \
+    const int kt_ = (KT);                                                         \
+    const bf16 *a_ = uniform_ptr(Ab + kt_ * GB_K), *b_ = uniform_ptr(Bb + kt_ * GB_K); \
+    const int blk = wave + 4 * ((Q) & 3);                                         \
+    const uint32_t m0_ = __builtin_amdgcn_readfirstlane(                          \
+        lds_base + (kt_ % GB_NST) * (GB_STAGE * 2) + ((Q) < 4 ? 0 : GB_M * GB_K * 2) + blk * 1024); \
+    if ((Q) < 4)                                                                  \
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"           \
+                   :: "v"(doff[Q]), "s"(a_), "s"(m0_) : "memory", "m0");          \
+    else                                                                          \
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"           \
+                   :: "v"(doff[Q]), "s"(b_), "s"(m0_) : "memory", "m0");          \
   } while (0)
 
   f32x16 acc[4][4];
@@ -291,10 +303,8 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragments of k-step s+1 are read from LDS while the 16 MFMAs of k-step
-  // s run; sched_barrier keeps the compiler from hoisting all reads of the
-  // slab (which would need 128 more registers)
-  auto load_frags = [&](const bf16 *As, const bf16 *Bs, int kk, bf16x8 *a, bf16x8 *b) {
+  auto load_frags = [&](int kt, int kk, bf16x8 *a, bf16x8 *b) {
+    const bf16 *As = lds + (kt % GB_NST) * GB_STAGE, *Bs = As + GB_M * GB_K;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       a[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(wm * 128 + i * 32 + l32, kk + g * 8)]);
@@ -302,44 +312,73 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
     for (int j = 0; j < 4; ++j)
       b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(wn * 128 + j * 32 + l32, kk + g * 8)]);
   };
-  auto mma16 = [&](const bf16x8 *a, const bf16x8 *b) {
+  // the 16 MFMAs of one k-step; with DMA_KT >= 0, copies Q0..Q0+3 of that
+  // slab go one after every fourth MFMA (a copy instruction stalls its wave
+  // until the address unit takes it; between MFMAs the stall overlaps the
+  // matrix pipe instead of idling it)
+  auto mma16 = [&](const bf16x8 *a, const bf16x8 *b, int dma_kt, int q0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      if (dma_kt >= 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (q0 == 0) GB_DMA1(dma_kt, i);
+        else GB_DMA1(dma_kt, 4 + i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
+  // Pipeline over barrier intervals j: the interval runs k-step 16..31 of
+  // slab j and k-step 0..15 of slab j+1 (whose fragments are read from LDS
+  // while the previous MFMAs run), copies slab j+4 into the stage slab j
+  // used (free once every wave passed barrier j: a wave's LDS reads are
+  // complete at its barrier), then waits for slab j+2.
   const int nk = p.K / GB_K;
-  GB_DMA(0, 0);
-  __builtin_amdgcn_s_waitcnt(GB_VMCNT0);
+#pragma unroll
+  for (int c = 0; c < GB_NST; ++c)
+    if (c < nk) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) GB_DMA1(c, q);
+    }
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  // slab 0 landed: at most slabs 1..3 outstanding
+  if (nk >= 4) __builtin_amdgcn_s_waitcnt(GB_VMCNT(24));
+  else if (nk == 3) __builtin_amdgcn_s_waitcnt(GB_VMCNT(16));
+  else if (nk == 2) __builtin_amdgcn_s_waitcnt(GB_VMCNT(8));
+  else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bf16 *As = lds + cur * GB_STAGE, *Bs = As + GB_M * GB_K;
-    // the next slab goes to the stage every wave finished reading before
-    // the last barrier, and has this iteration's MFMAs to arrive
-    if (kt + 1 < nk) GB_DMA((kt + 1) * GB_K, cur ^ 1);
-    bf16x8 a0[4], b0[4], a1[4], b1[4];
-    load_frags(As, Bs, 0, a0, b0);
-    load_frags(As, Bs, 16, a1, b1);
+  load_frags(0, 0, a0, b0);
+  load_frags(0, 16, a1, b1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma16(a0, b0, -1, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // slab 1 landed
+  if (nk >= 4) __builtin_amdgcn_s_waitcnt(GB_VMCNT(16));
+  else if (nk == 3) __builtin_amdgcn_s_waitcnt(GB_VMCNT(8));
+  else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
+  __syncthreads();
+  for (int j = 0; j + 1 < nk; ++j) {
+    const int dma_kt = j + GB_NST < nk ? j + GB_NST : -1;
+    load_frags(j + 1, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    mma16(a0, b0);
+    mma16(a1, b1, dma_kt, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_frags(As, Bs, 32, a0, b0);
+    load_frags(j + 1, 16, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    mma16(a1, b1);
+    mma16(a0, b0, dma_kt, 4);
     __builtin_amdgcn_sched_barrier(0);
-    load_frags(As, Bs, 48, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(a1, b1);
-    // this wave's copies have landed; the barrier publishes every wave's
-    __builtin_amdgcn_s_waitcnt(GB_VMCNT0);
+    // slab j+2 landed: slabs j+3 .. min(nk-1, j+4) may stay outstanding
+    const int later = min(nk - 1, j + GB_NST) - (j + 2);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(GB_VMCNT(16));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(GB_VMCNT(8));
+    else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
     __syncthreads();
   }
-#undef GB_DMA
+  mma16(a1, b1, -1, 0);  // k-step 16..31 of the last slab
+#undef GB_DMA1
 
   // epilogue through LDS (the operand stages are free after the last barrier)
   bf16 *Cs = lds;
@@ -417,15 +456,6 @@ constexpr int SK_CPW = (SK_M + SK_N) / 4 / 4;      // copy instructions per wave
 // one MFMA fragment read touches fall in distinct banks.
 __device__ inline int swz_sk(int r, int k) {
   return r * SK_K + ((((k >> 3) ^ r) & 15) << 3) + (k & 7);
-}
-
-// A pointer the whole wave holds, moved to scalar registers (inline-asm
-// scalar operands need it there even when the compiler computed it with
-// vector instructions).
-template <typename P> __device__ inline P *uniform_ptr(P *q) {
-  const uint64_t v = (uint64_t)q;
-  return reinterpret_cast<P *>(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
-                               (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
 }
 
 // Output column n (in column range st) of batch z under the column-range
