@@ -70,12 +70,28 @@ struct AttnCfg {
   static constexpr int NKP = (BKV * KPP * ES + 1023) / 1024;
   static constexpr int KSTAGEB = (NKN + NKP) * 1024;
   static constexpr int NKPW = (NKN + NKP + 3) / 4;  // copy blocks per wave (at most)
+  // V^T stage copied straight from global memory (bf16, 32 keys = 64-byte
+  // rows): DVP rows in 1 KB blocks of 16
+  static constexpr int NVB = DVP / 16;
+  static constexpr int NVPW = (NVB + 3) / 4;
 };
+
+// Key order inside each 16-key group of a tile as seen by the score MFMA when
+// V^T is copied verbatim: the lane feeding score row x reads key pk16(x)
+// (bits 2 and 3 of x swapped).  A lane of half g holds score rows
+// 16u + 8a + 4g + c (a < 2, c < 4) of slice u, i.e. keys 16u + 8g + 4a + c:
+// the eight k slots of its probability operand are eight consecutive keys,
+// which the V^T operand reads as one 16-byte chunk of its row.
+__device__ inline int pk16(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 template <typename T>
 __device__ inline uint4 ld16(const T *p) { return *reinterpret_cast<const uint4 *>(p); }
 
-template <typename T, int DN, int DR, int DV>
+// VD: bf16 with S a multiple of 8 -- V^T tiles are copied global -> LDS by
+// the same copy instructions as the keys (no staging registers, no LDS
+// stores), with the score MFMA reading keys in pk16 order.  Otherwise V^T
+// is staged through registers and stored to LDS with two quads swapped.
+template <typename T, int DN, int DR, int DV, bool VD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(PrefillAttnArgs a) {
   using C = AttnCfg<T, DN, DR, DV>;
   using MF = typename C::MF;
@@ -83,9 +99,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 NQF = C::NQF, NDT = C::NDT, DVP = C::DVP, CPRK = C::CPRK, CPRV = C::CPRV,
                 DQKP = C::DQKP, ES = C::ES, NQN = C::NQN, KNP = C::KNP, KPP = C::KPP,
                 NKN = C::NKN, NKP = C::NKP, KSTAGEB = C::KSTAGEB, NKPW = C::NKPW,
-                KCH = C::KCH, VCH = C::VCH, KSTAGE = C::KSTAGE, VSTAGE = C::VSTAGE;
+                KCH = C::KCH, VCH = C::VCH, KSTAGE = C::KSTAGE, VSTAGE = C::VSTAGE,
+                NVB = C::NVB, NVPW = C::NVPW;
+  static_assert(!VD || (sizeof(T) == 2 && BKV == 32), "verbatim V^T copies need bf16 tiles of 32");
   __shared__ __attribute__((aligned(1024))) char Kl[3 * KSTAGEB];
-  __shared__ __attribute__((aligned(16))) T Vt[3 * VSTAGE];
+  __shared__ __attribute__((aligned(1024))) char Vl[VD ? 3 * NVB * 1024 : 16];
+  __shared__ __attribute__((aligned(16))) T Vt[VD ? VEC : 3 * VSTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
@@ -114,7 +133,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const T *kpe = reinterpret_cast<const T *>(a.k_pe) + (int64_t)b * S * a.ld_kpe;
   const T *vt = reinterpret_cast<const T *>(a.vt) + bh * DV * S;
 
-  if constexpr (DVP > DV) {
+  if constexpr (DVP > DV && !VD) {
     for (int i = tid; i < (DVP - DV) * VPITCH; i += 256) {
       Vt[DV * VPITCH + i] = from_f32<T>(0.f);
       Vt[VSTAGE + DV * VPITCH + i] = from_f32<T>(0.f);
@@ -184,6 +203,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }                                                                                   \
   } while (0)
 
+  // VD: V^T tile copies.  Block vb = wave + 4k holds rows 16 vb .. + 15 (64
+  // bytes = 32 keys each); lane l fills row 16 vb + l/4 at position l%4,
+  // which holds logical 16-byte chunk (l%4) ^ (row/4 % 4) (conflict-free
+  // 16-byte reads of 16 consecutive rows).  Rows past DV repeat row 0 (their
+  // output channels are never stored); chunks past the sequence repeat the
+  // last one (masked keys).
+  const T *vt_bh = reinterpret_cast<const T *>(a.vt) + bh * DV * S;
+  int vrow[NVPW], vch[NVPW];
+#pragma unroll
+  for (int k = 0; k < NVPW; ++k) {
+    const int row = 16 * (wave + 4 * k) + (lane >> 2);
+    vrow[k] = row < DV ? row : 0;
+    vch[k] = (lane & 3) ^ ((row >> 2) & 3);
+  }
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)Vl;
+#define ATT_VDMA(STG, J0)                                                               \
+  do {                                                                                  \
+    const int j0_ = (J0);                                                               \
+    _Pragma("unroll") for (int k = 0; k < NVPW; ++k) {                                  \
+      const int vb = wave + 4 * k;                                                      \
+      if (vb < NVB) {                                                                   \
+        const uint32_t off_ = (uint32_t)((vrow[k] * S + min(j0_ + 8 * vch[k], S - 8)) * ES); \
+        const uint32_t m0_ = lds_v + (STG) * (NVB * 1024) + vb * 1024;                  \
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"               \
+                     :: "v"(off_), "s"(vt_bh), "s"(m0_) : "memory", "m0");              \
+      }                                                                                 \
+    }                                                                                   \
+  } while (0)
+  // copies of this wave per tile (keys and V^T), for the wait counts
+  const int ncopy = (NKN + NKP - wave + 3) / 4 + (VD ? (NVB - wave + 3) / 4 : 0);
+
   // register staging of one V^T tile (plain code, not lambdas: the staging
   // registers must not end up in scratch memory)
   uint4 rv[VCH];
@@ -243,10 +293,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // fragment f of this lane's key row in the K stage starting at byte KB:
   // k_nope region for f < NQN, k_pe region after it
+  const int kr = VD ? pk16(l32) : l32;  // key row this lane feeds to the score MFMA
 #define ATT_KFRAG(KB, f)                                                              \
   (*reinterpret_cast<const typename MF::frag *>(                                      \
-      (f) < NQN ? reinterpret_cast<const T *>(KB) + l32 * KNP + (f) * MF::KSTEP + g * MF::KPL \
-                : reinterpret_cast<const T *>((KB) + NKN * 1024) + l32 * KPP +        \
+      (f) < NQN ? reinterpret_cast<const T *>(KB) + kr * KNP + (f) * MF::KSTEP + g * MF::KPL \
+                : reinterpret_cast<const T *>((KB) + NKN * 1024) + kr * KPP +         \
                       ((f) - NQN) * MF::KSTEP + g * MF::KPL))
   // S^T of key tile at stage byte base KB for this wave's queries
 #define ATT_QK(ST, KB)                                                                \
@@ -262,15 +313,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // finishes tile t (softmax, O^T += V^T P^T) while the MFMAs of tile t+1's
   // scores run underneath the exponentials, and stores tile t+2's V^T
   // (loaded into registers one iteration earlier).
-  ATT_KDMA(0, 0);
-  ATT_FETCH(0);
-  ATT_STASH(0);
-  if (ntiles > 1) {
-    ATT_KDMA(1, BKV);
-    ATT_FETCH(BKV);
-    ATT_STASH(1);
+  if constexpr (VD) {
+    ATT_KDMA(0, 0);
+    ATT_VDMA(0, 0);
+    if (ntiles > 1) {
+      ATT_KDMA(1, BKV);
+      ATT_VDMA(1, BKV);
+    }
+  } else {
+    ATT_KDMA(0, 0);
+    ATT_FETCH(0);
+    ATT_STASH(0);
+    if (ntiles > 1) {
+      ATT_KDMA(1, BKV);
+      ATT_FETCH(BKV);
+      ATT_STASH(1);
+    }
+    if (ntiles > 2) ATT_FETCH(2 * BKV);
   }
-  if (ntiles > 2) ATT_FETCH(2 * BKV);
   __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));
   __syncthreads();
   f32x16 s_cur;
@@ -280,13 +340,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int j0 = t * BKV;
     const int rn = rd == 2 ? 0 : rd + 1;   // stage of tile t + 1
     const int rw = rd == 0 ? 2 : rd - 1;   // stage of tile t + 2 (held tile t - 1)
-    if (t + 2 < ntiles) ATT_KDMA(rw, (t + 2) * BKV);
+    if (t + 2 < ntiles) {
+      ATT_KDMA(rw, (t + 2) * BKV);
+      if constexpr (VD) ATT_VDMA(rw, (t + 2) * BKV);
+    }
     if (t <= tw) {
       // V^T fragments of tile t, read now so that they have landed by the
       // time the PV MFMAs issue (bf16; the fp32 path reads them in place)
       const T *vs = Vt + rd * VSTAGE;
       typename MF::frag vpre[MF::KPL > 1 ? 2 : 1][NDT];
-      if constexpr (MF::KPL > 1) {
+      if constexpr (VD) {
+        // rows d*32 + l32 of the verbatim stage; keys 16u + 8g .. +7 are
+        // logical chunk 2u + g
+        const T *vl = reinterpret_cast<const T *>(Vl + __builtin_amdgcn_readfirstlane(rd * NVB * 1024));
+        const int sw = (l32 >> 2) & 3;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int d = 0; d < NDT; ++d)
+            vpre[u][d] = *reinterpret_cast<const typename MF::frag *>(
+                vl + (d * 32 + l32) * BKV + (((2 * u + g) ^ sw) << 3));
+      } else if constexpr (MF::KPL > 1) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -300,10 +374,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // causal mask on the diagonal tile only; key j0 + acc_row(r) is masked
       // when acc_row(r) exceeds iq - j0
       if (t == tw) {
-        const int lim = iq - j0 - g * 4;  // acc_row(r) = (r/4)*8 + g*4 + r%4
+        if constexpr (VD) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if ((r >> 2) * 8 + (r & 3) > lim) s_cur[r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (pk16(acc_row(r, lane)) > iq - j0) s_cur[r] = -INFINITY;
+        } else {
+          const int lim = iq - j0 - g * 4;  // acc_row(r) = (r/4)*8 + g*4 + r%4
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((r >> 2) * 8 + (r & 3) > lim) s_cur[r] = -INFINITY;
+        }
       }
       float mx = s_cur[0];
 #pragma unroll
@@ -383,15 +463,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       s_cur = s_nxt;
     }
-    if (t + 2 < ntiles) {
-      ATT_STASH(rw);
-      if (t + 3 < ntiles) ATT_FETCH((t + 3) * BKV);
+    if constexpr (VD) {
+      // this wave's copies of tile t+1 have landed once at most tile t+2's
+      // are outstanding; the barrier publishes every wave's
+      constexpr int MX = C::NKPW + NVPW;
+      if (t + 2 < ntiles) {
+        if (ncopy == MX) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(MX));
+        else if (ncopy == MX - 1) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(MX - 1));
+        else if (ncopy == MX - 2) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(MX - 2));
+        else __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));
+      } else {
+        __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));
+      }
+    } else {
+      if (t + 2 < ntiles) {
+        ATT_STASH(rw);
+        if (t + 3 < ntiles) ATT_FETCH((t + 3) * BKV);
+      }
+      // this wave's key copies of tile t+2 have landed (only the V^T loads of
+      // tile t+3, issued after them, may still be in flight); the barrier
+      // publishes every wave's copies and stores
+      if (t + 3 < ntiles && v_whole) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(VCH));
+      else __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));
     }
-    // this wave's key copies of tile t+2 have landed (only the V^T loads of
-    // tile t+3, issued after them, may still be in flight); the barrier
-    // publishes every wave's copies and stores
-    if (t + 3 < ntiles && v_whole) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(VCH));
-    else __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));
     __syncthreads();
     rd = rn;
   }
@@ -400,6 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #undef ATT_QK
 #undef ATT_FETCH
 #undef ATT_STASH
+#undef ATT_VDMA
 
   // normalise and store o[b, i, h, d]
   const float l_tot = half_swap_sum(l_run);
@@ -429,7 +524,10 @@ template <typename T, int DN, int DR, int DV>
 hipError_t launch_t(const PrefillAttnArgs &a, hipStream_t st) {
   const int nq = (a.S + BQ - 1) / BQ;
   dim3 grid(nq * a.H * a.B);
-  hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV>), grid, dim3(256), 0, st, a);
+  if (sizeof(T) == 2 && a.S % 8 == 0)
+    hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, sizeof(T) == 2>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
