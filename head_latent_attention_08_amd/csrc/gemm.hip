@@ -197,22 +197,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 // every thread stores 16-byte runs of 8 consecutive columns, which fall in one
 // head of the destination (all column ranges and head widths are multiples of
 // 8), so the head-scatter store stays vectorised.
-constexpr int GB_M = 256, GB_K = 32, GB_THREADS = 256, GB_NST = 4;
-
-// Tile shape of the large-product kernel for an N tile of TN columns (256, or
-// 224 where that packs the tiles into fewer rounds of workgroups).  Four
-// waves: 2x2 of 128x128 at TN = 256, otherwise 4x1 of 64xTN.
-template <int TN> struct GbCfg {
-  static constexpr int WGN = TN == 256 ? 2 : 1, WGM = 4 / WGN;
-  static constexpr int RM = GB_M / WGM, CN = TN / WGN;  // wave tile
-  static constexpr int NI = RM / 32, NJ = CN / 32;      // 32x32 MFMA tiles per wave
-  static constexpr int CPITCH = TN + 8;                 // epilogue LDS pitch (elements)
-  static constexpr int STAGE = (GB_M + TN) * GB_K;      // elements per operand stage
-  static constexpr int LDS = GB_M * CPITCH > GB_NST * STAGE ? GB_M * CPITCH : GB_NST * STAGE;
-  static constexpr int NB = (GB_M + TN) / 16;           // 1 KB copy blocks per slab
-  static constexpr int NPW = (NB + 3) / 4;              // copies per wave per slab (at most)
-  static constexpr int MPH = NI * NJ;                   // MFMAs per k-step of 16
-};
+constexpr int GB_M = 256, GB_N = 256, GB_K = 32, GB_THREADS = 256, GB_NST = 4;
+constexpr int GB_CPITCH = GB_N + 8;               // epilogue LDS pitch (elements)
+constexpr int GB_STAGE = (GB_M + GB_N) * GB_K;    // elements per operand stage
+constexpr int GB_LDS = GB_M * GB_CPITCH > GB_NST * GB_STAGE ? GB_M * GB_CPITCH : GB_NST * GB_STAGE;
 
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left open (gfx9 encoding)
 constexpr int GB_VMCNT0 = (7 << 4) | (15 << 8);
@@ -241,13 +229,9 @@ template <typename P> __device__ inline P *uniform_ptr(P *q) {
                                (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
 }
 
-template <int TN>
 __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int tiles_m,
                                                               int tiles_n, int remap, int group_m) {
-  using C = GbCfg<TN>;
-  constexpr int NI = C::NI, NJ = C::NJ, NB = C::NB, NPW = C::NPW, MPH = C::MPH, CPITCH = C::CPITCH,
-                STAGE = C::STAGE;
-  __shared__ __attribute__((aligned(16))) bf16 lds[C::LDS];
+  __shared__ __attribute__((aligned(16))) bf16 lds[GB_LDS];
 
   // tile index: contiguous run per XCD, then grouped row-major order
   const int T = tiles_m * tiles_n;
@@ -259,11 +243,11 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   const int gm = min(tiles_m - first_m, group_m);
   const int tm = first_m + (t % per_group) % gm;
   const int tn = (t % per_group) / gm;
-  const int m0 = tm * GB_M, n0 = tn * TN;
+  const int m0 = tm * GB_M, n0 = tn * GB_N;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;  // uniform: feeds M0
-  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
+  const int wm = wave >> 1, wn = wave & 1;
   const int g = lane >> 5, l32 = lane & 31;
   const bf16 *A = reinterpret_cast<const bf16 *>(p.A);
 
@@ -273,84 +257,77 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   // staging registers and no LDS store instructions are involved.  A slab
   // is 32 blocks; block b of A (or B) holds rows 16b..16b+15, and lane l
   // fills row 16b + l/4 at position l%4, which holds logical chunk
-  // (l%4) ^ (row/4 % 4).  Wave w issues blocks w, w+4, .. (16 of A, then
-  // TN/16 of B); each lane's source offset of each of its blocks is fixed for the whole
+  // (l%4) ^ (row/4 % 4).  Wave w issues blocks w, w+4, .. of A then of B;
+  // each lane's source offset of each of its 8 blocks is fixed for the whole
   // K loop (rows clamped into the matrix: rows past M or N only feed outputs
   // that are never stored), and the slab's k offset moves the scalar base.
-  // Column ranges start at multiples of TN (checked on the host), so one
+  // Column ranges start at multiples of 256 (checked on the host), so one
   // tile reads B from a single range.
   const int st = seg_of(p, n0);
   const int64_t t_ldb = SEG_FIELD(p, st, ldb);
   const int t_nb = SEG_FIELD(p, st, n_begin);
   const bf16 *Ab = A + (int64_t)m0 * p.lda;
   const bf16 *Bb = reinterpret_cast<const bf16 *>(SEG_FIELD(p, st, B)) + (int64_t)(n0 - t_nb) * t_ldb;
-  // copies of this wave per slab (the last one only for the first NB % 4 waves)
-  const int cw = (NB - wave + 3) / 4;
-  uint32_t doff[NPW];
+  uint32_t doff[8];
 #pragma unroll
-  for (int q = 0; q < NPW; ++q) {
-    const int blk = wave + 4 * q;
-    const bool is_a = blk < 16;
-    const int row = 16 * (is_a ? blk : blk - 16) + (lane >> 2);
+  for (int q = 0; q < 8; ++q) {
+    const int blk = wave + 4 * (q & 3);
+    const int row = 16 * blk + (lane >> 2);
     const int j = (lane & 3) ^ ((row >> 2) & 3);
-    const int rc = is_a ? min(row, p.M - 1 - m0) : min(row, p.N - 1 - n0);
-    const int64_t ld = is_a ? p.lda : t_ldb;
+    const int rc = q < 4 ? min(row, p.M - 1 - m0) : min(row, p.N - 1 - n0);
+    const int64_t ld = q < 4 ? p.lda : t_ldb;
     doff[q] = (uint32_t)((rc * ld + j * 8) * (int64_t)sizeof(bf16));
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16 *)lds;
-  // copy q of this wave for slab KT into stage KT % GB_NST (block
-  // wave + 4q: A rows for blocks < 16, B rows after)
+  // copy q (0..7) of slab KT into stage KT % GB_NST
 #define GB_DMA1(KT, Q)                                                            \
   do {                                                                            \
     const int kt_ = (KT);                                                         \
-    const int blk = wave + 4 * (Q);                                               \
-    if ((Q) < NPW && blk < NB) {                                                  \
-      const bf16 *a_ = uniform_ptr(Ab + kt_ * GB_K), *b_ = uniform_ptr(Bb + kt_ * GB_K); \
-      const uint32_t m0_ = __builtin_amdgcn_readfirstlane(                        \
-          lds_base + (kt_ % GB_NST) * (STAGE * 2) + blk * 1024);                  \
-      if (blk < 16)                                                               \
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"         \
-                     :: "v"(doff[(Q) < NPW ? (Q) : 0]), "s"(a_), "s"(m0_) : "memory", "m0"); \
-      else                                                                        \
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"         \
-                     :: "v"(doff[(Q) < NPW ? (Q) : 0]), "s"(b_), "s"(m0_) : "memory", "m0"); \
-    }                                                                             \
+    const bf16 *a_ = uniform_ptr(Ab + kt_ * GB_K), *b_ = uniform_ptr(Bb + kt_ * GB_K); \
+    const int blk = wave + 4 * ((Q) & 3);                                         \
+    const uint32_t m0_ = __builtin_amdgcn_readfirstlane(                          \
+        lds_base + (kt_ % GB_NST) * (GB_STAGE * 2) + ((Q) < 4 ? 0 : GB_M * GB_K * 2) + blk * 1024); \
+    if ((Q) < 4)                                                                  \
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"           \
+                   :: "v"(doff[Q]), "s"(a_), "s"(m0_) : "memory", "m0");          \
+    else                                                                          \
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"           \
+                   :: "v"(doff[Q]), "s"(b_), "s"(m0_) : "memory", "m0");          \
   } while (0)
 
-  f32x16 acc[NI][NJ];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   auto load_frags = [&](int kt, int kk, bf16x8 *a, bf16x8 *b) {
-    const bf16 *As = lds + (kt % GB_NST) * STAGE, *Bs = As + GB_M * GB_K;
+    const bf16 *As = lds + (kt % GB_NST) * GB_STAGE, *Bs = As + GB_M * GB_K;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      a[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(wm * C::RM + i * 32 + l32, kk + g * 8)]);
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(wm * 128 + i * 32 + l32, kk + g * 8)]);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(wn * C::CN + j * 32 + l32, kk + g * 8)]);
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(wn * 128 + j * 32 + l32, kk + g * 8)]);
   };
-  // the MPH MFMAs of one k-step; with DMA_KT >= 0, this half's copies of
-  // that slab (NPW/2 of them, from Q0) are spread over the MFMAs (a copy
-  // instruction stalls its wave until the address unit takes it; between
-  // MFMAs the stall overlaps the matrix pipe instead of idling it)
-  constexpr int DPH = (NPW + 1) / 2;  // copies per half interval
-  auto mma = [&](const bf16x8 *a, const bf16x8 *b, int dma_kt, int q0) {
+  // the 16 MFMAs of one k-step; with DMA_KT >= 0, copies Q0..Q0+3 of that
+  // slab go one after every fourth MFMA (a copy instruction stalls its wave
+  // until the address unit takes it; between MFMAs the stall overlaps the
+  // matrix pipe instead of idling it)
+  auto mma16 = [&](const bf16x8 *a, const bf16x8 *b, int dma_kt, int q0) {
 #pragma unroll
-    for (int x = 0; x < MPH; ++x) {
-      const int i = x / NJ, j = x % NJ;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int k = 0; k < DPH; ++k)
-        if (x == ((k + 1) * MPH) / DPH - 1 && dma_kt >= 0) {
-          __builtin_amdgcn_sched_barrier(0);
-          GB_DMA1(dma_kt, q0 + k);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      if (dma_kt >= 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (q0 == 0) GB_DMA1(dma_kt, i);
+        else GB_DMA1(dma_kt, 4 + i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -364,52 +341,44 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   for (int c = 0; c < GB_NST; ++c)
     if (c < nk) {
 #pragma unroll
-      for (int q = 0; q < NPW; ++q) GB_DMA1(c, q);
+      for (int q = 0; q < 8; ++q) GB_DMA1(c, q);
     }
-  bf16x8 a0[NI], b0[NJ], a1[NI], b1[NJ];
-  // waits for "slab s landed while up to n later slabs stay in flight": this
-  // wave has cw copies per slab (NPW or NPW - 1)
-#define GB_WAIT_LATER(n)                                                          \
-  do {                                                                            \
-    if (cw == NPW) __builtin_amdgcn_s_waitcnt(GB_VMCNT((n) * NPW));               \
-    else __builtin_amdgcn_s_waitcnt(GB_VMCNT((n) * (NPW - 1)));                   \
-  } while (0)
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
   // slab 0 landed: at most slabs 1..3 outstanding
-  if (nk >= 4) GB_WAIT_LATER(3);
-  else if (nk == 3) GB_WAIT_LATER(2);
-  else if (nk == 2) GB_WAIT_LATER(1);
+  if (nk >= 4) __builtin_amdgcn_s_waitcnt(GB_VMCNT(24));
+  else if (nk == 3) __builtin_amdgcn_s_waitcnt(GB_VMCNT(16));
+  else if (nk == 2) __builtin_amdgcn_s_waitcnt(GB_VMCNT(8));
   else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
   __syncthreads();
   load_frags(0, 0, a0, b0);
   load_frags(0, 16, a1, b1);
   __builtin_amdgcn_sched_barrier(0);
-  mma(a0, b0, -1, 0);
+  mma16(a0, b0, -1, 0);
   __builtin_amdgcn_sched_barrier(0);
   // slab 1 landed
-  if (nk >= 4) GB_WAIT_LATER(2);
-  else if (nk == 3) GB_WAIT_LATER(1);
+  if (nk >= 4) __builtin_amdgcn_s_waitcnt(GB_VMCNT(16));
+  else if (nk == 3) __builtin_amdgcn_s_waitcnt(GB_VMCNT(8));
   else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
   __syncthreads();
   for (int j = 0; j + 1 < nk; ++j) {
     const int dma_kt = j + GB_NST < nk ? j + GB_NST : -1;
     load_frags(j + 1, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1, dma_kt, 0);
+    mma16(a1, b1, dma_kt, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_frags(j + 1, 16, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0, dma_kt, DPH);
+    mma16(a0, b0, dma_kt, 4);
     __builtin_amdgcn_sched_barrier(0);
     // slab j+2 landed: slabs j+3 .. min(nk-1, j+4) may stay outstanding
     const int later = min(nk - 1, j + GB_NST) - (j + 2);
-    if (later >= 2) GB_WAIT_LATER(2);
-    else if (later == 1) GB_WAIT_LATER(1);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(GB_VMCNT(16));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(GB_VMCNT(8));
     else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
     __syncthreads();
   }
-  mma(a1, b1, -1, 0);  // k-step 16..31 of the last slab
+  mma16(a1, b1, -1, 0);  // k-step 16..31 of the last slab
 #undef GB_DMA1
-#undef GB_WAIT_LATER
 
   // epilogue through LDS (the operand stages are free after the last barrier)
   bf16 *Cs = lds;
@@ -417,32 +386,32 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   const int t_dh = SEG_FIELD(p, st, dh), t_off = SEG_FIELD(p, st, off);
   const int64_t t_ld = SEG_FIELD(p, st, ld);
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        Cs[(wm * C::RM + i * 32 + acc_row(r, lane)) * CPITCH + wn * C::CN + j * 32 + l32] =
+        Cs[(wm * 128 + i * 32 + acc_row(r, lane)) * GB_CPITCH + wn * 128 + j * 32 + l32] =
             (bf16)acc[i][j][r];
   __syncthreads();
   if (!SEG_FIELD(p, st, tr)) {
-    for (int it = 0; it < (GB_M * TN / 8) / GB_THREADS; ++it) {
+    for (int it = 0; it < (GB_M * GB_N / 8) / GB_THREADS; ++it) {
       const int c = tid + GB_THREADS * it;
-      const int row = c / (TN / 8), cc = c % (TN / 8);
+      const int row = c >> 5, cc = c & 31;
       const int m = m0 + row, n = n0 + cc * 8;
       if (m >= p.M || n >= p.N) continue;
       const int nn = n - t_nb;
       const int h = nn / t_dh, d = nn - h * t_dh;
       const int b = m / p.S, sq = m - b * p.S;
       bf16 *dst = t_C + ((int64_t)(b * p.H + h) * p.S + sq) * t_ld + t_off + d;
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * CPITCH + cc * 8]);
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * GB_CPITCH + cc * 8]);
     }
   } else {
     // channel-major destination: runs of 8 consecutive rows (tokens) of one
     // column; lane-consecutive columns keep the 2-byte LDS reads conflict-free
-    for (int it = 0; it < (GB_M * TN / 8) / GB_THREADS; ++it) {
+    for (int it = 0; it < (GB_M * GB_N / 8) / GB_THREADS; ++it) {
       const int c = tid + GB_THREADS * it;
-      const int col = c % TN, rg = c / TN;
+      const int col = c & (GB_N - 1), rg = c / GB_N;
       const int m = m0 + rg * 8, n = n0 + col;
       if (m >= p.M || n >= p.N) continue;
       const int nn = n - t_nb;
@@ -451,12 +420,12 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
       if (sq + 8 <= p.S && m + 8 <= p.M) {
         bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = Cs[(rg * 8 + e) * CPITCH + col];
+        for (int e = 0; e < 8; ++e) v[e] = Cs[(rg * 8 + e) * GB_CPITCH + col];
         *reinterpret_cast<bf16x8 *>(t_C + ((int64_t)(b * p.H + h) * t_dh + d) * p.S + sq) = v;
       } else {
         for (int e = 0; e < 8 && m + e < p.M; ++e) {
           const int me = m + e, be = me / p.S, se = me - be * p.S;
-          t_C[((int64_t)(be * p.H + h) * t_dh + d) * p.S + se] = Cs[(rg * 8 + e) * CPITCH + col];
+          t_C[((int64_t)(be * p.H + h) * t_dh + d) * p.S + se] = Cs[(rg * 8 + e) * GB_CPITCH + col];
         }
       }
     }
@@ -674,41 +643,15 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   for (int i = 0; i < 3; ++i) p.seg[i] = d.seg[i];
   bool big = d.dtype == BF16 && !d.b_kn && d.batch == 1 && d.K % GB_K == 0 && d.M >= 512 &&
              d.N % 8 == 0 && (int64_t)d.M * d.lda < (1LL << 31);
-  for (int i = 0; i < d.nseg && big; ++i) big = (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
+  for (int i = 0; i < d.nseg && big; ++i)
+    big = d.seg[i].n_begin % GB_N == 0 && (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
   if (big) {
-    // N tile: 256, or 224 when the column ranges allow it and the tiles then
-    // fill fewer rounds of one workgroup per CU (time ~ rounds x tile width)
-    int cus = 256;
-    {
-      int dev = 0;
-      if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (cus <= 0) cus = 256;
-    }
-    auto fits = [&](int tn_w) {
-      for (int i = 0; i < d.nseg; ++i)
-        if (d.seg[i].n_begin % tn_w != 0) return false;
-      return true;
-    };
-    const int tm = (d.M + GB_M - 1) / GB_M;
-    auto cost = [&](int tn_w) {
-      const int64_t T = (int64_t)tm * ((d.N + tn_w - 1) / tn_w);
-      return ((T + cus - 1) / cus) * tn_w;
-    };
-    const bool use224 = fits(224) && cost(224) < cost(256);
-    if (use224 || fits(256)) {
-      const int tnw = use224 ? 224 : 256;
-      const int tn = (d.N + tnw - 1) / tnw;
-      const int T = tm * tn;
-      const int group_m = d.K >= 4096 ? 8 : (d.K <= 1024 ? 2 : 4);
-      if (use224)
-        hipLaunchKernelGGL(gemm_big_kernel<224>, dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn,
-                           (T % 8 == 0) ? 1 : 0, group_m);
-      else
-        hipLaunchKernelGGL(gemm_big_kernel<256>, dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn,
-                           (T % 8 == 0) ? 1 : 0, group_m);
-      return hipGetLastError();
-    }
+    const int tm = (d.M + GB_M - 1) / GB_M, tn = (d.N + GB_N - 1) / GB_N;
+    const int T = tm * tn;
+    const int group_m = d.K >= 4096 ? 8 : (d.K <= 1024 ? 2 : 4);
+    hipLaunchKernelGGL(gemm_big_kernel, dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn,
+                       (T % 8 == 0) ? 1 : 0, group_m);
+    return hipGetLastError();
   }
   bool skinny = d.dtype == BF16 && !d.b_kn && d.M <= SK_M && d.K % SK_K == 0 && d.N % 8 == 0 &&
                 d.workspace != nullptr;
