@@ -43,14 +43,14 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "9768966f720e744bedf420d578b0e612fa1f23046ee37351a88bea66ff537a9c",
-        "FETCH_SIZE_KiB": 243048.2, "WRITE_SIZE_KiB": 131084.3},
+        "sha256": "c19082f5352e7362fac679aabcd3d000fb38ea1fc7d16ff5e6e0f4e4d823b5b1",
+        "FETCH_SIZE_KiB": 242959.3, "WRITE_SIZE_KiB": 131086.0},
     "out_proj": {
-        "sha256": "fd2194f454effcd107fb258477b9aa39dc208c01b7b149fbf54dbcd75f332b45",
-        "FETCH_SIZE_KiB": 822087.6, "WRITE_SIZE_KiB": 57344.0},
+        "sha256": "0ebe29289c211ea3ebaba456341b84ef59b77f1792a7871843a8852ff073e32d",
+        "FETCH_SIZE_KiB": 1511553.0, "WRITE_SIZE_KiB": 57344.0},
     "latent_attention": {
-        "sha256": "3e4039c58861ae64ebc4ad0bb54e81ec938cca53072446bb19bf42fc456b2972",
-        "FETCH_SIZE_KiB": 182787.8, "WRITE_SIZE_KiB": 81983.1},
+        "sha256": "8dfc4c1e4896683b5d87062cb91e712bf45314747dbd8af069dda25a172ec300",
+        "FETCH_SIZE_KiB": 182835.0, "WRITE_SIZE_KiB": 81983.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
