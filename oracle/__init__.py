@@ -26,4 +26,5 @@ from .mla_oracle import (  # noqa: F401
     mla_prefill_rows,
     mla_decode_expanded,
     mla_decode_absorbed,
+    mla_decode_absorbed_multi,
 )

@@ -395,3 +395,48 @@ def mla_decode_absorbed(cfg: Cfg, w: dict, x, cache, lens,
     if want_intermediates:
         return y, new_rows, dict(q_lat=q_lats, o_lat=o_lats)
     return y, new_rows
+
+
+def mla_decode_absorbed_multi(cfg: Cfg, w: dict, x, cache, lens):
+    """Several new tokens per sequence in one absorbed decode step (the
+    multi-token / speculative-verification use of the cache formula).
+
+    Token t of sequence b sits at position L_b + t; its latent row is written
+    at cache row L_b + t, and it attends to rows 0..L_b + t -- the cached
+    prefix and the new tokens up to itself, which is the causal tril mask of
+    the MLA listing ("The Evolving Transformer -- DeepSeek V2 & V3", section
+    01) applied to the new tokens.  Per token the arithmetic is the absorbed
+    form of :func:`mla_decode_absorbed`.
+
+    x: [B, T, D]; cache: [B, cap, r_kv + d_r] (rows < lens[b] valid).
+    Returns (y [B, T, D], new_rows [B, T, r_kv + d_r])."""
+    x = _f64(x)
+    B, T = x.shape[0], x.shape[1]
+    H = cfg.num_attention_heads
+    dn, dv = cfg.qk_nope_head_dim, cfg.v_head_dim
+    r = cfg.kv_lora_rank
+    wuk = _f64(w["w_up_k"]).reshape(H, dn, r)
+    wuv = _f64(w["w_up_v"]).reshape(H, dv, r)
+    wo = _f64(w["wo"])
+    scale = softmax_scale(cfg)
+    y = np.empty((B, T, cfg.hidden_size))
+    new_rows = np.empty((B, T, cache.shape[-1]))
+    for b in range(B):
+        L = int(lens[b])
+        toks = [_decode_new_token(cfg, w, x[b, t], L + t) for t in range(T)]
+        for t in range(T):
+            new_rows[b, t] = toks[t][2]
+        rows_all = np.concatenate([_f64(cache[b, :L]), new_rows[b]], axis=0)  # [L+T, W]
+        for t in range(T):
+            q_nope, q_pe, _ = toks[t]
+            rows = rows_all[:L + t + 1]
+            c, kp = rows[:, :r], rows[:, r:]
+            q_lat = np.einsum("hd,hdr->hr", q_nope, wuk)
+            s = scale * (q_lat @ c.T + q_pe @ kp.T)  # [H, L+t+1]
+            s = s - s.max(axis=-1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=-1, keepdims=True)
+            o = np.einsum("hvr,hr->hv", wuv, p @ c)
+            y[b, t] = o.reshape(-1) @ wo.T
+    return y, new_rows
+

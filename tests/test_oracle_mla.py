@@ -278,6 +278,40 @@ def test_decode_after_prefill(conv):
                                atol=1e-14)
 
 
+@pytest.mark.parametrize("conv", ["half_split", "interleaved"])
+def test_multi_token_decode_equals_sequential_decodes(conv):
+    # T new tokens in one step equal T single-token decodes, each appending
+    # its row before the next one runs
+    c = shrink(si.CONFIGS["small"], rope=conv)
+    T, B = 3, 3
+    x1, w, lens, cache = si.make_decode_inputs(c, batch=B, capacity=80, len_lo=0, len_hi=70,
+                                               gains="random")
+    xs, _ = si.make_inputs(c, seq=T, batch=B, gains="random")
+    cfg = oracle_cfg(c)
+    y_m, rows_m = orc.mla_decode_absorbed_multi(cfg, w, xs, cache, lens)
+    cache_s = cache.astype(np.float64).copy()
+    for t in range(T):
+        y_t, row_t = orc.mla_decode_absorbed(cfg, w, xs[:, t], cache_s, lens + t)
+        for b in range(B):
+            cache_s[b, lens[b] + t] = row_t[b]
+        np.testing.assert_allclose(y_m[:, t], y_t, rtol=1e-12, atol=1e-15)
+        np.testing.assert_array_equal(rows_m[:, t], row_t)
+
+
+def test_multi_token_decode_equals_prefill_tail():
+    # decoding tokens S..S+T-1 over a prefill's latent rows of tokens 0..S-1
+    # equals rows S..S+T-1 of a prefill of all S+T tokens
+    c = shrink(si.CONFIGS["small"], rope="interleaved")
+    S, T = 30, 4
+    x, w = si.make_inputs(c, seq=S + T, batch=2, gains="random")
+    cfg = oracle_cfg(c)
+    y_full = orc.mla_prefill(cfg, w, x)
+    _, inter = orc.mla_prefill(cfg, w, x[:, :S], want_intermediates=True)
+    cache = np.concatenate([inter["c_kv"], inter["k_pe"]], axis=-1)
+    y_dec, _ = orc.mla_decode_absorbed_multi(cfg, w, x[:, S:], cache, np.array([S, S]))
+    np.testing.assert_allclose(y_dec, y_full[:, S:], rtol=1e-11, atol=1e-14)
+
+
 def test_latent_cache_is_small():
     # per token the cache holds c_kv (512) + k_pe (64) = 576 values, against
     # 2 * 128 heads * 128 = 32768 for per-head K and V at V3 sizes
