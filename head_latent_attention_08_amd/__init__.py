@@ -14,6 +14,8 @@ from .mla import (  # noqa: F401
     RopeParams,
     load_library,
     mla_decode_absorbed,
+    mla_decode_absorbed_multi,
+    mla_decode_multi_workspace_size,
     mla_decode_layout_of,
     mla_decode_workspace_size,
     mla_prefill_forward,

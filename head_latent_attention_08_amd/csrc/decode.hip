@@ -96,10 +96,11 @@ __device__ inline int dec_swz(int row) {
 // this wave are outstanding (gfx9 encoding; expcnt and lgkmcnt left open).
 #define DEC_VMCNT(n) ((((n) & 15)) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
-// Rows of sequence b in the flattened order: lens[b] + 1 for a valid length.
-__device__ inline int seq_rows(const int32_t *lens, int b, int64_t cap) {
+// Rows of sequence b in the flattened order: lens[b] + q_len (the cached
+// prefix and the new tokens) for a valid length, else 0.
+__device__ inline int seq_rows(const int32_t *lens, int b, int64_t cap, int q_len) {
   const int32_t L = lens[b];
-  return (L >= 0 && (int64_t)L < cap) ? L + 1 : 0;
+  return (L >= 0 && (int64_t)L + q_len <= cap) ? L + q_len : 0;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
   const bool wave_live = hg * HPB + wave * HPW < H;
 
   // prefix sums of per-sequence row counts
-  for (int b = tid; b < B; b += DTHREADS) starts[b + 1] = seq_rows(a.lens, b, a.cap);
+  for (int b = tid; b < B; b += DTHREADS) starts[b + 1] = seq_rows(a.lens, b, a.cap, a.q_len);
   __syncthreads();
   if (wave == 0) {
     int carry = 0;
@@ -197,9 +198,19 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
 #pragma unroll
   for (int i = 0; i < 4; ++i) kofs[i] = l32 * CPITCH + (((2 * i + g) ^ dec_swz(l32)) << 3);
 
+  // this lane's new token: query head h is token h / heads_per_tok's head
+  const int hpt = a.heads_per_tok > 0 ? a.heads_per_tok : H;
+  const int tok = min(h, H - 1) / hpt;
+
   while (r0 < r1) {
     const int seg_end = min(r1, starts[b + 1]);
     const int t_begin = r0 - starts[b], t_end = seg_end - starts[b];
+    // token tok sees rows 0 .. lens[b] + tok, i.e. all but the last
+    // q_len - 1 - tok rows of the sequence; t_end_min is the lowest such
+    // limit among the lanes (all of them at q_len = 1)
+    const int rows_b = starts[b + 1] - starts[b];
+    const int t_lim = min(t_end, rows_b - (a.q_len - 1 - tok));
+    const int t_end_min = min(t_end, rows_b - (a.q_len - 1));
     const char *cb = cache + (int64_t)b * a.cap * W * (int64_t)sizeof(T);
 
     // Cache tile t0 -> stage: instruction i of the stage fills bytes
@@ -378,10 +389,10 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
         }
 #undef DEC_KLOAD
 #undef DEC_KMMA
-        if (t0 + TK > t_end) {
+        if (t0 + TK > t_end_min) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (t0 + acc_row(r, lane) >= t_end) st[r] = -INFINITY;
+            if (t0 + acc_row(r, lane) >= t_lim) st[r] = -INFINITY;
         }
         float mx = st[0];
 #pragma unroll
@@ -390,7 +401,9 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
         m_true = fmaxf(m_true, mx);
         if (m_ref == -INFINITY) m_ref = mx;  // first tile of the segment
         if ((mx - m_ref) * sl2 > HEADROOM_LOG2) ovf = true;
-        const float neg = -m_ref * sl2;
+        // a lane whose rows of this piece are all past its token's limit
+        // keeps m_ref = -inf: its probabilities are exp2(-inf) = 0
+        const float neg = m_ref == -INFINITY ? 0.f : -m_ref * sl2;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, neg));
@@ -507,7 +520,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
   if (tid < 64) {
     int before = 0, all = 0;
     for (int i = tid; i < a.B; i += 64) {
-      const int n = seq_rows(a.lens, i, a.cap);
+      const int n = seq_rows(a.lens, i, a.cap, a.q_len);
       all += n;
       if (i < b) before += n;
     }
@@ -523,7 +536,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
   }
   __syncthreads();
   const int start = sh[0], total = sh[1];
-  const int n_b = seq_rows(a.lens, b, a.cap);
+  const int n_b = seq_rows(a.lens, b, a.cap, a.q_len);
   const int lane = tid & 63, hl = lane & 31, g = lane >> 5;
   const int h = hb * HPW + hl;
   T *out = reinterpret_cast<T *>(a.o_lat) + ((int64_t)b * a.H + h) * R;

@@ -194,13 +194,18 @@ __global__ void copy_rows_kernel(T *dst, int64_t ldd, const T *src, int64_t lds,
 }
 
 template <typename T>
-__global__ void cache_append_kernel(T *cache, int64_t cap, const int32_t *lens, const T *src,
-                                    int64_t lds, int width) {
-  const int b = blockIdx.x;
+__global__ void cache_append_kernel(T *cache, int64_t cap, const int32_t *lens, int q_len,
+                                    const T *src, int64_t lds, int width) {
+  const int row = blockIdx.x, b = row / q_len, t = row - b * q_len;
   const int32_t L = lens[b];
-  if (L < 0 || (int64_t)L >= cap) return;
-  T *dst = cache + ((int64_t)b * cap + L) * width;
-  for (int c = threadIdx.x; c < width; c += blockDim.x) dst[c] = src[(int64_t)b * lds + c];
+  if (L < 0 || (int64_t)L + q_len > cap) return;
+  T *dst = cache + ((int64_t)b * cap + L + t) * width;
+  for (int c = threadIdx.x; c < width; c += blockDim.x) dst[c] = src[(int64_t)row * lds + c];
+}
+
+__global__ void decode_positions_kernel(const int32_t *lens, int n, int q_len, int32_t *pos) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) pos[i] = lens[i / q_len] + i % q_len;
 }
 
 }  // namespace
@@ -267,16 +272,26 @@ hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src, 
   return hipGetLastError();
 }
 
-hipError_t launch_cache_append(int dtype, void *cache, int64_t cap, const int32_t *lens,
+hipError_t launch_cache_append(int dtype, void *cache, int64_t cap, const int32_t *lens, int q_len,
                                const void *src, int64_t lds, int64_t batch, int width,
                                hipStream_t st) {
-  if (batch <= 0) return hipSuccess;
+  if (batch <= 0 || q_len <= 0) return hipSuccess;
+  const unsigned rows = (unsigned)(batch * q_len);
   if (dtype == BF16)
-    hipLaunchKernelGGL(cache_append_kernel<bf16>, dim3((unsigned)batch), dim3(256), 0, st,
-                       (bf16 *)cache, cap, lens, (const bf16 *)src, lds, width);
+    hipLaunchKernelGGL(cache_append_kernel<bf16>, dim3(rows), dim3(256), 0, st, (bf16 *)cache, cap,
+                       lens, q_len, (const bf16 *)src, lds, width);
   else
-    hipLaunchKernelGGL(cache_append_kernel<float>, dim3((unsigned)batch), dim3(256), 0, st,
-                       (float *)cache, cap, lens, (const float *)src, lds, width);
+    hipLaunchKernelGGL(cache_append_kernel<float>, dim3(rows), dim3(256), 0, st, (float *)cache,
+                       cap, lens, q_len, (const float *)src, lds, width);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_positions(const int32_t *lens, int batch, int q_len, int32_t *pos,
+                                   hipStream_t st) {
+  const int n = batch * q_len;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_positions_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     lens, n, q_len, pos);
   return hipGetLastError();
 }
 

@@ -80,10 +80,17 @@ hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src,
 
 // Decode: write row t of src (width elements) into cache[b, lens[b]] when
 // 0 <= lens[b] < cap.
+// Write the q_len new latent rows of each sequence: token row b*q_len + t of
+// src (pitch lds) goes to cache row lens[b] + t; a sequence with lens[b] < 0
+// or lens[b] + q_len > cap is left untouched.
 hipError_t launch_cache_append(int dtype, void *cache, int64_t cap,
-                               const int32_t *lens, const void *src,
+                               const int32_t *lens, int q_len, const void *src,
                                int64_t lds, int64_t batch, int width,
                                hipStream_t st);
+
+// pos[b*q_len + t] = lens[b] + t
+hipError_t launch_decode_positions(const int32_t *lens, int batch, int q_len,
+                                   int32_t *pos, hipStream_t st);
 
 struct PrefillAttnArgs {
   const void *q;      // [B, H, S, dn + dr]
@@ -99,6 +106,10 @@ struct PrefillAttnArgs {
 hipError_t launch_prefill_attention(int dtype, int dn, int dr, int dv,
                                     const PrefillAttnArgs &a, hipStream_t st);
 
+// B sequences with q_len new tokens each; H = q_len * heads_per_tok query
+// heads per sequence (token t's head h is query head t*heads_per_tok + h).
+// Sequence b holds lens[b] + q_len cache rows; token t sees rows
+// 0..lens[b] + t.
 struct DecodeAttnArgs {
   const void *q_lat;  // [B, H, r + dr]  absorbed query ‖ post-RoPE q_pe
   const void *cache;  // [B, cap, r + dr]
@@ -109,6 +120,7 @@ struct DecodeAttnArgs {
   float *part_ml;     // [(n_blocks + B), H, 2]
   int64_t cap;
   int B, H;
+  int q_len = 1, heads_per_tok = 0;
   int n_blocks;
   float scale;
 };

@@ -209,10 +209,15 @@ PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S) {
 struct DecodePlan {
   int64_t ld_down;
   int n_blocks;
-  size_t off_down, off_qn, off_qlat, off_po, off_pml, off_olat, off_o, off_gemm, gemm_bytes, total;
+  size_t off_down, off_qn, off_qlat, off_po, off_pml, off_olat, off_o, off_gemm, gemm_bytes,
+      off_pos, total;
 };
 
-DecodePlan plan_decode(const mla_config &c, int64_t B) {
+// Workspace of a decode step of B sequences with T new tokens each: the
+// per-token buffers hold B*T rows; the attention partials cover T*H query
+// heads (token t's head h is query head t*H + h).
+DecodePlan plan_decode(const mla_config &c, int64_t Bseq, int64_t T = 1) {
+  const int64_t B = Bseq * T;  // token rows
   const size_t es = dtype_size(c.dtype);
   const int64_t H = c.num_heads, r = c.kv_lora_rank, dr = c.qk_rope_head_dim;
   DecodePlan p;
@@ -228,9 +233,9 @@ DecodePlan plan_decode(const mla_config &c, int64_t B) {
   p.off_qn = take((size_t)B * H * c.qk_nope_head_dim * es);
   p.off_qlat = take((size_t)B * H * (r + dr) * es);
   // attention partials: blocks of 32 heads x (r rounded up to 32) channels
-  p.off_po = take((size_t)(p.n_blocks + B) * ((H + 31) / 32) * 32 * ((r + 31) / 32 * 32) *
+  p.off_po = take((size_t)(p.n_blocks + Bseq) * ((T * H + 31) / 32) * 32 * ((r + 31) / 32 * 32) *
                   sizeof(float));
-  p.off_pml = take((size_t)(p.n_blocks + B) * H * 2 * sizeof(float));
+  p.off_pml = take((size_t)(p.n_blocks + Bseq) * T * H * 2 * sizeof(float));
   p.off_olat = take((size_t)B * H * r * es);
   p.off_o = take((size_t)B * H * c.v_head_dim * es);
   // split-K partials of the weight-streaming projections (largest of the four)
@@ -241,6 +246,7 @@ DecodePlan plan_decode(const mla_config &c, int64_t B) {
   gb = std::max(gb, gemm_scratch_bytes(c.dtype, (int)B, D, (int)H * dv, 1));
   p.gemm_bytes = gb;
   p.off_gemm = take(gb);
+  p.off_pos = take((size_t)B * sizeof(int32_t));  // positions lens[b] + t (T > 1)
   p.total = off;
   return p;
 }
@@ -260,10 +266,12 @@ mla_status check_prefill_sizes(const mla_config *cfg, int64_t B, int64_t S) {
   return MLA_OK;
 }
 
-mla_status check_decode_sizes(const mla_config *cfg, int64_t B, int64_t cap) {
+mla_status check_decode_sizes(const mla_config *cfg, int64_t B, int64_t cap, int64_t T = 1) {
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if (B < 1 || B > 4096) return fail(MLA_ERR_INVALID_ARGUMENT, "batch must be in [1, 4096]");
+  if (T < 1 || T > 16) return fail(MLA_ERR_INVALID_ARGUMENT, "q_len must be in [1, 16]");
+  if (T > cap) return fail(MLA_ERR_INVALID_ARGUMENT, "q_len exceeds cache_capacity");
   if (cap < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "cache_capacity must be >= 1");
   if (B * cap > (1LL << 30))
     return fail(MLA_ERR_INVALID_ARGUMENT, "batch x cache_capacity is too large");
@@ -468,6 +476,15 @@ mla_status mla_decode_workspace_size(const mla_config *cfg, int64_t batch, int64
   return MLA_OK;
 }
 
+mla_status mla_decode_multi_workspace_size(const mla_config *cfg, int64_t batch, int64_t q_len,
+                                           int64_t cache_capacity, size_t *bytes) {
+  mla_status s = check_decode_sizes(cfg, batch, cache_capacity, q_len);
+  if (s != MLA_OK) return s;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = plan_decode(*cfg, batch, q_len).total;
+  return MLA_OK;
+}
+
 mla_status mla_decode_layout_of(const mla_config *cfg, int64_t batch, int64_t cache_capacity,
                                 mla_decode_layout *layout) {
   mla_status s = check_decode_sizes(cfg, batch, cache_capacity);
@@ -487,11 +504,12 @@ mla_status mla_decode_layout_of(const mla_config *cfg, int64_t batch, int64_t ca
   return MLA_OK;
 }
 
-mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, const void *x,
-                               int64_t batch, void *latent_cache, int64_t cache_capacity,
-                               const int32_t *cache_lens, void *y, void *workspace,
-                               size_t workspace_bytes, void *hip_stream) {
-  mla_status s = check_decode_sizes(cfg, batch, cache_capacity);
+namespace {
+mla_status decode_impl(const mla_config *cfg, const mla_weights *w, const void *x, int64_t batch,
+                       int64_t q_len, void *latent_cache, int64_t cache_capacity,
+                       const int32_t *cache_lens, void *y, void *workspace,
+                       size_t workspace_bytes, void *hip_stream) {
+  mla_status s = check_decode_sizes(cfg, batch, cache_capacity, q_len);
   if (s != MLA_OK) return s;
   if ((s = check_weights(w)) != MLA_OK) return s;
   if (!x || !y || !workspace || !latent_cache || !cache_lens)
@@ -501,12 +519,13 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
     return fail(MLA_ERR_INVALID_ARGUMENT,
                 "x, y, latent_cache and workspace must be 16-byte aligned");
   const mla_config &c = *cfg;
-  const DecodePlan p = plan_decode(c, batch);
+  const DecodePlan p = plan_decode(c, batch, q_len);
   if (workspace_bytes < p.total)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
                 workspace_bytes, p.total);
 
   hipStream_t st = (hipStream_t)hip_stream;
+  const int T = (int)q_len;
   const size_t es = dtype_size(c.dtype);
   char *ws = (char *)workspace;
   char *down = ws + p.off_down;
@@ -514,11 +533,19 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
   char *qlat = ws + p.off_qlat;
   char *olat = ws + p.off_olat;
   char *o = ws + p.off_o;
-  const int B = (int)batch, H = c.num_heads;
+  // B token rows (sequence b's token t is row b*T + t); Bs sequences
+  const int Bs = (int)batch, B = Bs * T, H = c.num_heads;
   const int D = c.hidden_size, rq = c.q_lora_rank, rkv = c.kv_lora_rank;
   const int dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim;
   const int wl = rkv + dr;  // latent row width
   const RopeTab tab = make_rope_tab(c.rope, dr);
+  // position of each token row: lens[b] + t (the lengths themselves at T = 1)
+  const int32_t *pos = cache_lens;
+  if (T > 1) {
+    int32_t *pw = (int32_t *)(ws + p.off_pos);
+    MLA_HIP(launch_decode_positions(cache_lens, Bs, T, pw, st), "decode positions");
+    pos = pw;
+  }
 
   // 1. down projections of the new tokens
   MLA_MARK(0);
@@ -545,11 +572,11 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
           "decode rmsnorm");
   // 2. RoPE of the new key at position lens[b], then append [c_kv ‖ k_pe] at row lens[b]
   MLA_MARK(2);
-  MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, B, B, 0, p.ld_down, 1, 0,
-                      cache_lens, tab, st),
+  MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, B, B, 0, p.ld_down, 1, 0, pos,
+                      tab, st),
           "decode rope k_pe");
-  MLA_HIP(launch_cache_append(c.dtype, latent_cache, cache_capacity, cache_lens,
-                              down + (size_t)rq * es, p.ld_down, B, wl, st),
+  MLA_HIP(launch_cache_append(c.dtype, latent_cache, cache_capacity, cache_lens, T,
+                              down + (size_t)rq * es, p.ld_down, Bs, wl, st),
           "cache append");
   // 3. q_nope per head, q_pe straight into the absorbed query rows, RoPE of q_pe
   MLA_MARK(3);
@@ -571,8 +598,8 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
     MLA_HIP(launch_gemm(g, st), "decode q up-projection");
   }
   MLA_MARK(4);
-  MLA_HIP(launch_rope(c.dtype, qlat + (size_t)rkv * es, B, B, 0, (int64_t)H * wl, H, wl,
-                      cache_lens, tab, st),
+  MLA_HIP(launch_rope(c.dtype, qlat + (size_t)rkv * es, B, B, 0, (int64_t)H * wl, H, wl, pos,
+                      tab, st),
           "decode rope q_pe");
   // 4. absorb: q_lat[b, h] = w_up_k_h^T q_nope[b, h]   (batched over heads)
   MLA_MARK(5);
@@ -610,8 +637,10 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
     a.part_o = (float *)(ws + p.off_po);
     a.part_ml = (float *)(ws + p.off_pml);
     a.cap = cache_capacity;
-    a.B = B;
-    a.H = H;
+    a.B = Bs;
+    a.H = T * H;  // query heads: token t's head h is t*H + h
+    a.q_len = T;
+    a.heads_per_tok = H;
     a.n_blocks = p.n_blocks;
     a.scale = resolve_scale(c);
     MLA_HIP(launch_decode_attention(c.dtype, rkv, dr, a, st), "decode attention");
@@ -660,6 +689,23 @@ mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, cons
   }
   MLA_MARK(10);
   return MLA_OK;
+}
+}  // namespace
+
+mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights *w, const void *x,
+                               int64_t batch, void *latent_cache, int64_t cache_capacity,
+                               const int32_t *cache_lens, void *y, void *workspace,
+                               size_t workspace_bytes, void *hip_stream) {
+  return decode_impl(cfg, w, x, batch, 1, latent_cache, cache_capacity, cache_lens, y, workspace,
+                     workspace_bytes, hip_stream);
+}
+
+mla_status mla_decode_absorbed_multi(const mla_config *cfg, const mla_weights *w, const void *x,
+                                     int64_t batch, int64_t q_len, void *latent_cache,
+                                     int64_t cache_capacity, const int32_t *cache_lens, void *y,
+                                     void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return decode_impl(cfg, w, x, batch, q_len, latent_cache, cache_capacity, cache_lens, y,
+                     workspace, workspace_bytes, hip_stream);
 }
 
 mla_status mla_rope_apply(void *x, int32_t dtype, int64_t n_tokens, int32_t n_heads,

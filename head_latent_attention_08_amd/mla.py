@@ -101,11 +101,15 @@ def load_library(path: str = LIB_PATH):
                                          ctypes.POINTER(DecodeLayout)]
     lib.mla_decode_absorbed.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P, i64,
                                         P, i64, P, P, P, ctypes.c_size_t, P]
+    lib.mla_decode_multi_workspace_size.argtypes = [ctypes.POINTER(Config), i64, i64, i64,
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_decode_absorbed_multi.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P,
+                                              i64, i64, P, i64, P, P, P, ctypes.c_size_t, P]
     lib.mla_rope_apply.argtypes = [P, ctypes.c_int32, i64, ctypes.c_int32, ctypes.c_int32, i64,
                                    i64, P, ctypes.POINTER(RopeParams), P]
     for fn in ("mla_prefill_workspace_size", "mla_prefill_layout_of", "mla_prefill_forward",
                "mla_decode_workspace_size", "mla_decode_layout_of", "mla_decode_absorbed",
-               "mla_rope_apply"):
+               "mla_decode_multi_workspace_size", "mla_decode_absorbed_multi", "mla_rope_apply"):
         getattr(lib, fn).restype = st
     lib.mla_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
     lib.mla_set_stage_events.restype = st
@@ -284,6 +288,39 @@ def mla_decode_absorbed(cfg: MlaConfig, weights: dict, x: torch.Tensor, latent_c
     _check(load_library().mla_decode_absorbed(
         ctypes.byref(c), ctypes.byref(w), _ptr(x), B, _ptr(latent_cache), cap, _ptr(cache_lens),
         _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y, workspace
+
+
+def mla_decode_multi_workspace_size(cfg: MlaConfig, batch: int, q_len: int, capacity: int) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().mla_decode_multi_workspace_size(ctypes.byref(c), batch, q_len, capacity,
+                                                          ctypes.byref(n)))
+    return n.value
+
+
+def mla_decode_absorbed_multi(cfg: MlaConfig, weights: dict, x: torch.Tensor,
+                              latent_cache: torch.Tensor, cache_lens: torch.Tensor, y=None,
+                              workspace=None, stream=None):
+    """Absorbed decode of q_len new tokens per sequence, x [B, q_len, D];
+    writes cache rows lens[b] .. lens[b] + q_len - 1.  Returns (y, workspace)."""
+    B, T, D = x.shape
+    cap = latent_cache.shape[1]
+    dev = x.device
+    if y is None:
+        y = torch.empty((B, T, D), dtype=cfg.torch_dtype, device=dev)
+    need = mla_decode_multi_workspace_size(cfg, B, T, cap)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if cache_lens.dtype != torch.int32:
+        raise ValueError("cache_lens must be int32")
+    _device_check(x, y, latent_cache, cache_lens, workspace)
+    w = make_weights(weights)
+    c = cfg.c()
+    _check(load_library().mla_decode_absorbed_multi(
+        ctypes.byref(c), ctypes.byref(w), _ptr(x), B, T, _ptr(latent_cache), cap,
+        _ptr(cache_lens), _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return y, workspace
 
 

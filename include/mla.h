@@ -179,6 +179,34 @@ MLA_API mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights 
                                void *workspace, size_t workspace_bytes,
                                void *hip_stream);
 
+/* Multi-token absorbed decode: q_len new tokens per sequence in one step
+ * (the verification pass of speculative or multi-token decoding).  Token t
+ * of sequence b sits at position lens[b] + t, its latent row is written at
+ * cache row lens[b] + t, and it attends to rows 0..lens[b] + t: the cached
+ * prefix and the new tokens up to itself (the causal tril mask of the MLA
+ * section applied to the new tokens).  Per token the arithmetic is that of
+ * mla_decode_absorbed, which is this call at q_len = 1.
+ *   x            [B, q_len, D]            device
+ *   latent_cache [B, capacity, r_kv + d_r] device; rows [0, lens[b]) read,
+ *                rows lens[b] .. lens[b] + q_len - 1 written
+ *   cache_lens   [B] int32                 device, read only (the caller
+ *                advances it by q_len); 0 <= lens[b] and lens[b] + q_len <=
+ *                capacity is a device-side precondition: a sequence that
+ *                violates it gets NaN y rows and no cache write.
+ *   y            [B, q_len, D]            device, written
+ * Status: as mla_decode_absorbed; INVALID_ARGUMENT also for q_len outside
+ * [1, 16] or above capacity.  The workspace depends on q_len: size it with
+ * mla_decode_multi_workspace_size. */
+MLA_API mla_status mla_decode_multi_workspace_size(const mla_config *cfg, int64_t batch,
+                                           int64_t q_len, int64_t cache_capacity,
+                                           size_t *bytes);
+MLA_API mla_status mla_decode_absorbed_multi(const mla_config *cfg, const mla_weights *w,
+                                     const void *x, int64_t batch, int64_t q_len,
+                                     void *latent_cache, int64_t cache_capacity,
+                                     const int32_t *cache_lens, void *y,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *hip_stream);
+
 /* --------------------------------------------------------------------- RoPE
  * In-place RoPE of x[t, h, 0..rope_dim) at positions[t] (device int32 [n_tokens]),
  * element (t, h, i) at x + t*token_stride + h*head_stride + i (strides in

@@ -104,6 +104,14 @@ def test_bad_sizes_rejected():
     with pytest.raises(m.MlaError) as e:
         m.mla_decode_workspace_size(m.MlaConfig(**dict(V3, kv_lora_rank=256)), 4, 16)
     assert e.value.status == b.MLA_ERR_UNSUPPORTED
+    for T, cap in [(0, 16), (17, 64), (5, 4)]:
+        with pytest.raises(m.MlaError) as e:
+            m.mla_decode_multi_workspace_size(cfg, 4, T, cap)
+        assert e.value.status == b.MLA_ERR_INVALID_ARGUMENT
+    # q_len = 1 needs what the single-token call needs; more tokens need more
+    one = m.mla_decode_multi_workspace_size(cfg, 64, 1, 8193)
+    assert one == m.mla_decode_workspace_size(cfg, 64, 8193)
+    assert m.mla_decode_multi_workspace_size(cfg, 32, 2, 8193) > m.mla_decode_workspace_size(cfg, 32, 8193)
 
 
 def _raw_prefill(lib, cfg, w, x, y, ws, nbytes):

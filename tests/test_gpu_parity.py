@@ -250,6 +250,82 @@ def test_decode_edge_lengths():
     np.testing.assert_array_equal(to_np(cache_d)[3], cache[3].astype(np.float64))
 
 
+def _run_decode_multi(c, conv, B, T, cap, lens, seed=None):
+    m = _m()
+    _, w, _, cache = si.make_decode_inputs(c, batch=B, capacity=cap, len_lo=0, len_hi=1,
+                                           gains="random", seed=seed)
+    xs, _ = si.make_inputs(c, seq=T, batch=B, gains="random", seed=seed)
+    lens = np.asarray(lens, dtype=np.int32)
+    cfg = mla_cfg(c, rope=conv)
+    dt = c["dtype"]
+    cache_d = to_dev(cache, dt)
+    ws = _poisoned(m.mla_decode_multi_workspace_size(cfg, B, T, cap))
+    y, ws = m.mla_decode_absorbed_multi(cfg, weights_to_dev(w, dt), to_dev(xs, dt), cache_d,
+                                        torch.from_numpy(lens).cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    return xs, w, lens, cache, y, cache_d
+
+
+@pytest.mark.parametrize("name,conv,T", [("tiny", "half_split", 2), ("small", "interleaved", 2),
+                                         ("small", "half_split", 3), ("small", "interleaved", 4)])
+def test_multi_token_decode_matches_oracle(name, conv, T):
+    # q_len new tokens per sequence: token t attends to rows 0..lens[b] + t;
+    # lengths include an empty history, tile edges and a sequence that ends
+    # exactly at capacity
+    c = si.CONFIGS[name]
+    B, cap = 6, 200
+    lens = [0, 31, 32 - T, 97, cap - T, 150]
+    xs, w, lens, cache, y, cache_d = _run_decode_multi(c, conv, B, T, cap, lens, seed=7100 + T)
+    ref, new_rows = orc.mla_decode_absorbed_multi(oracle_cfg(c, rope=conv), w, xs, cache, lens)
+    yn = to_np(y)
+    for t in range(T):
+        assert_close_rows(yn[:, t], ref[:, t], c["dtype"], f"y token {t}")
+    got = to_np(cache_d)
+    for t in range(T):
+        rows = np.stack([got[b, lens[b] + t] for b in range(B)])
+        assert_close_rows(rows, new_rows[:, t], c["dtype"], f"new cache row {t}")
+    mask = np.ones(cache.shape[:2], dtype=bool)
+    for b in range(B):
+        mask[b, lens[b]:lens[b] + T] = False
+    np.testing.assert_array_equal(got[mask], cache.astype(np.float64)[mask])
+
+
+def test_multi_token_decode_invalid_length():
+    # lens[b] + q_len > capacity: NaN rows for that sequence, no cache write,
+    # the others unaffected
+    c = si.CONFIGS["small"]
+    B, T, cap = 3, 3, 120
+    lens = [10, cap - 2, 50]
+    xs, w, lens, cache, y, cache_d = _run_decode_multi(c, "interleaved", B, T, cap, lens,
+                                                       seed=7200)
+    ok = [0, 2]
+    ref, _ = orc.mla_decode_absorbed_multi(oracle_cfg(c, rope="interleaved"), w, xs[ok],
+                                           cache[ok], lens[ok])
+    yn = to_np(y)
+    for t in range(T):
+        assert_close_rows(yn[ok, t], ref[:, t], "bf16", f"y token {t}")
+    assert np.all(np.isnan(yn[1]))
+    np.testing.assert_array_equal(to_np(cache_d)[1], cache[1].astype(np.float64))
+
+
+def test_multi_token_decode_q_len_one_is_single_decode():
+    # q_len = 1 through the multi-token entry point equals mla_decode_absorbed
+    m = _m()
+    c = si.CONFIGS["small"]
+    B, cap = 4, 150
+    x, w, lens, cache = si.make_decode_inputs(c, batch=B, capacity=cap, len_lo=0, len_hi=cap - 1,
+                                              gains="random", seed=7300)
+    cfg = mla_cfg(c, rope="interleaved")
+    wd = weights_to_dev(w, "bf16")
+    lens_d = torch.from_numpy(lens).cuda()
+    c1, c2 = to_dev(cache, "bf16"), to_dev(cache, "bf16")
+    y1, _ = m.mla_decode_absorbed(cfg, wd, to_dev(x, "bf16"), c1, lens_d)
+    y2, _ = m.mla_decode_absorbed_multi(cfg, wd, to_dev(x[:, None], "bf16"), c2, lens_d)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(y2)[:, 0], to_np(y1))
+    np.testing.assert_array_equal(to_np(c2), to_np(c1))
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_decode_score_range_beyond_first_tile(dtype):
     # cache rows after the first tile are scaled up so their scores exceed

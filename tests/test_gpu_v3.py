@@ -180,3 +180,28 @@ def test_v3_decode_expanded_spot_check():
     torch.cuda.synchronize()
     ref, _ = orc.mla_decode_expanded(oracle_cfg(c), w, x, cache, lens)
     assert_close_rows(to_np(y), ref, "bf16", "y")
+
+
+def test_v3_multi_token_decode():
+    # two new tokens per sequence at V3 shapes (the verification pass of
+    # speculative decoding): 16 sequences, lengths U{1024..4096}
+    m = _m()
+    c = si.CONFIGS["v3_decode"]
+    B, T, cap = 16, 2, 4100
+    print("v3 multi-token decode: B=16 T=2 cap=4100, seed 4200", flush=True)
+    _, w, lens, cache = si.make_decode_inputs(c, batch=B, capacity=cap, len_lo=1024, len_hi=4096,
+                                              seed=4200)
+    xs, _ = si.make_inputs(c, seq=T, batch=B, seed=4200)
+    cfg = mla_cfg(c)
+    cache_d = to_dev(cache, "bf16")
+    y, _ = m.mla_decode_absorbed_multi(cfg, weights_to_dev(w, "bf16"), to_dev(xs, "bf16"),
+                                       cache_d, torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    ref, new_rows = orc.mla_decode_absorbed_multi(oracle_cfg(c), w, xs, cache, lens)
+    yn = to_np(y)
+    for t in range(T):
+        assert_close_rows(yn[:, t], ref[:, t], "bf16", f"y token {t}")
+    got = to_np(cache_d)
+    for t in range(T):
+        rows = np.stack([got[b, lens[b] + t] for b in range(B)])
+        assert_close_rows(rows, new_rows[:, t], "bf16", f"new cache row {t}")
