@@ -100,6 +100,15 @@ def decode_flops(c, lens):
     return float(sum(int(L) + 1 for L in lens) * H * (2 * (r + dr) + 2 * r))
 
 
+def multi_token_bytes_flops(c, lens, T):
+    """Cache bytes (each row of a sequence read once for all its new tokens)
+    and FLOPs of a multi-token decode step with T new tokens per sequence."""
+    H, r, dr = c["num_attention_heads"], c["kv_lora_rank"], c["qk_rope_head_dim"]
+    rows = sum(int(L) + T for L in lens)
+    seen = sum(int(L) + t + 1 for L in lens for t in range(T))
+    return float(rows * (r + dr) * 2), float(seen * H * (2 * (r + dr) + 2 * r))
+
+
 def cpu_baseline(c_pre, x, w, c_dec, xd, wd, lens, cache, seconds_hint=True):
     """The float64 oracle, untuned, on bounded samples of the same workloads."""
     import numpy as np
@@ -144,6 +153,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-multi-token", action="store_true",
+                    help="skip the multi-token decode lines (q_len 2 and 4)")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="time one of the two workloads only (profiling aid; no JSON line)")
     ap.add_argument("--replicas", type=int, default=3,
@@ -318,6 +329,37 @@ def main():
         "roofline": roofline,
         "decode_roofline": decode_roofline,
     }
+    if not args.no_multi_token:
+        # Multi-token absorbed decode (q_len new tokens per sequence) on the
+        # first sequences of the same cache, 64 token rows per step; not part
+        # of the headline value
+        lines = []
+        for Bm, T in ((32, 2), (16, 4)):
+            lm = np.minimum(lens[:Bm], caches[0].shape[1] - T).astype(np.int32)
+            xm = torch.randn((Bm, T, c_dec["hidden_size"]), dtype=torch.float32,
+                             generator=torch.Generator().manual_seed(4300 + T)).to(
+                                 "cuda", torch.bfloat16)
+            ym = torch.empty_like(xm)
+            wsm = torch.empty(m.mla_decode_multi_workspace_size(cfg_dec, Bm, T, caches[0].shape[1]),
+                              dtype=torch.uint8, device="cuda")
+            lmd = torch.from_numpy(lm).cuda()
+            evm = [new_events(n_de) for _ in range(8)]
+            for i in range(8):
+                m.mla_set_stage_events([e.cuda_event for e in evm[i]])
+                m.mla_decode_absorbed_multi(cfg_dec, wdec_d, xm, caches[i % len(caches)][:Bm], lmd,
+                                            y=ym, workspace=wsm)
+                m.mla_set_stage_events(None)
+            torch.cuda.synchronize()
+            mst, m_ms, _ = stage_ms(evm[3:], m.DECODE_STAGES)
+            mb, mf = multi_token_bytes_flops(c_dec, lm, T)
+            a_ms = mst["latent_attention"]
+            lines.append({"q_len": T, "batch": Bm, "attention_ms": a_ms,
+                          "cache_gbs": mb / (a_ms * 1e-3) / 1e9,
+                          "attention_tflops": mf / (a_ms * 1e-3) / 1e12,
+                          "step_ms": m_ms, "cache_bytes": mb})
+            log(f"bench: multi-token decode q_len={T} B={Bm}: attention {a_ms * 1e3:.1f} us, "
+                f"{mb / (a_ms * 1e-3) / 1e9:.0f} GB/s, step {m_ms * 1e3:.1f} us")
+        out["decode_multi_token"] = lines
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on bounded samples")
         out["cpu_baseline"] = cpu_baseline(c_pre, x, w, c_dec, xdec, wdec, lens, cache)

@@ -698,7 +698,10 @@ hipError_t launch_merge_t(const DecodeAttnArgs &a, hipStream_t st) {
 
 }  // namespace
 
-int decode_blocks() { return 256; }
+// Row ranges of a decode step: one workgroup per (range, group of 128 query
+// heads) fills the 256 CUs once, so with q_len tokens (q_len head groups at
+// 128 heads) the rows are cut into 256 / q_len ranges.
+int decode_blocks(int q_len) { return q_len > 1 ? std::max(1, 256 / q_len) : 256; }
 
 hipError_t launch_decode_attention(int dtype, int r, int dr, const DecodeAttnArgs &a,
                                    hipStream_t st) {

@@ -130,7 +130,7 @@ hipError_t launch_decode_attention(int dtype, int r, int dr,
 hipError_t launch_decode_merge(int dtype, int r, const DecodeAttnArgs &a,
                                hipStream_t st);
 
-int decode_blocks();
+int decode_blocks(int q_len);
 
 // q_lat[b, h, 0:r] = W_uk_h^T q_nope[b, h]: q_nope row b at qn + b*ldq + h*dn,
 // W_uk rows h*dn + k of length r, q_lat row b head h at qlat + b*ldo +

@@ -222,7 +222,7 @@ DecodePlan plan_decode(const mla_config &c, int64_t Bseq, int64_t T = 1) {
   const int64_t H = c.num_heads, r = c.kv_lora_rank, dr = c.qk_rope_head_dim;
   DecodePlan p;
   p.ld_down = (int64_t)round_up(c.q_lora_rank + r + dr, 8);
-  p.n_blocks = decode_blocks();
+  p.n_blocks = decode_blocks((int)T);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
