@@ -270,7 +270,7 @@ mla_status check_decode_sizes(const mla_config *cfg, int64_t B, int64_t cap, int
   mla_status s = check_config(cfg);
   if (s != MLA_OK) return s;
   if (B < 1 || B > 4096) return fail(MLA_ERR_INVALID_ARGUMENT, "batch must be in [1, 4096]");
-  if (T < 1 || T > 16) return fail(MLA_ERR_INVALID_ARGUMENT, "q_len must be in [1, 16]");
+  if (T < 1 || T > 256) return fail(MLA_ERR_INVALID_ARGUMENT, "q_len must be in [1, 256]");
   if (T > cap) return fail(MLA_ERR_INVALID_ARGUMENT, "q_len exceeds cache_capacity");
   if (cap < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "cache_capacity must be >= 1");
   if (B * cap > (1LL << 30))

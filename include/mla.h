@@ -194,8 +194,13 @@ MLA_API mla_status mla_decode_absorbed(const mla_config *cfg, const mla_weights 
  *                capacity is a device-side precondition: a sequence that
  *                violates it gets NaN y rows and no cache write.
  *   y            [B, q_len, D]            device, written
+ * With lens[b] = 0 and q_len = S this is the causal prefill of S tokens in
+ * absorbed form, and in general a prefill chunk of q_len tokens against a
+ * latent cache of lens[b] rows (the absorbed form costs 2(r_kv + d_r) + 2 r_kv
+ * flops per query-row pair, against 2(d_n + d_r) + 2 d_v expanded, so it
+ * suits short chunks).
  * Status: as mla_decode_absorbed; INVALID_ARGUMENT also for q_len outside
- * [1, 16] or above capacity.  The workspace depends on q_len: size it with
+ * [1, 256] or above capacity.  The workspace depends on q_len: size it with
  * mla_decode_multi_workspace_size. */
 MLA_API mla_status mla_decode_multi_workspace_size(const mla_config *cfg, int64_t batch,
                                            int64_t q_len, int64_t cache_capacity,

@@ -104,7 +104,7 @@ def test_bad_sizes_rejected():
     with pytest.raises(m.MlaError) as e:
         m.mla_decode_workspace_size(m.MlaConfig(**dict(V3, kv_lora_rank=256)), 4, 16)
     assert e.value.status == b.MLA_ERR_UNSUPPORTED
-    for T, cap in [(0, 16), (17, 64), (5, 4)]:
+    for T, cap in [(0, 16), (257, 400), (5, 4)]:
         with pytest.raises(m.MlaError) as e:
             m.mla_decode_multi_workspace_size(cfg, 4, T, cap)
         assert e.value.status == b.MLA_ERR_INVALID_ARGUMENT

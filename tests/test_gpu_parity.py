@@ -359,3 +359,24 @@ def test_decode_score_range_beyond_first_tile(dtype):
         rel, ab = row_errors(to_np(y), ref)
         # sharp softmax: bf16 logit rounding moves probabilities (relative bound only)
         assert np.isfinite(to_np(y)).all() and rel.max() <= 5e-2, rel.max()
+
+
+@pytest.mark.parametrize("prefix", [0, 100])
+def test_multi_token_decode_as_chunked_prefill(prefix):
+    # a 64-token chunk against a latent cache of `prefix` rows (prefix 0: the
+    # causal prefill of 64 tokens in absorbed form)
+    c = si.CONFIGS["small"]
+    B, T, cap = 2, 64, 200
+    xs, w, lens, cache, y, cache_d = _run_decode_multi(c, "interleaved", B, T, cap,
+                                                       [prefix, prefix + 7], seed=7400 + prefix)
+    ref, new_rows = orc.mla_decode_absorbed_multi(oracle_cfg(c, rope="interleaved"), w, xs, cache,
+                                                  lens)
+    yn = to_np(y)
+    assert_close_rows(yn.reshape(B * T, -1), ref.reshape(B * T, -1), "bf16", "y")
+    if prefix == 0:
+        # equal to the expanded prefill of the same 64 tokens (b = 0)
+        yp = orc.mla_prefill(oracle_cfg(c, rope="interleaved"), w, xs[:1])
+        assert_close_rows(yn[0], yp[0], "bf16", "y vs prefill")
+    got = to_np(cache_d)
+    for b in range(B):
+        assert_close_rows(got[b, lens[b]:lens[b] + T], new_rows[b], "bf16", "new rows")
