@@ -8,17 +8,19 @@
 // so every head reads the same 576-wide cache rows [c_kv ‖ k_pe].  This kernel
 // streams each row from HBM once for all heads of a head group.
 //
-// Work split: the rows of all sequences (lens[b] + 1 each, the new token
-// included) are laid end to end and cut into n_blocks equal ranges, so long
-// and short sequences load the GPU evenly.  Each range is processed by one
-// workgroup per group of 128 heads (a single one at 128 heads, so every cache
-// row leaves HBM once); with more head groups the workgroups of a range are
+// Work split: the rows of all sequences (lens[b] + q_len each, the new
+// tokens included) are laid end to end, each non-empty sequence preceded by
+// PIECE_COST_ROWS virtual rows standing for the cost of starting a piece,
+// and cut into n_blocks equal ranges, so long and short sequences load the
+// GPU evenly.  Each range is processed by one workgroup per group of 128
+// query heads (a single one at 128 heads and one token, so every cache row
+// leaves HBM once); with more head groups the workgroups of a range are
 // numbered so they land on the same XCD (workgroup ids go to the eight XCDs
-// round-robin) and the repeated reads of a cache tile hit that XCD's L2.  A range that spans sequence boundaries yields one partial
-// (unnormalised o_lat, running max, running sum) per sequence piece, in slot
-// (range + b) -- unique because range and sequence indices both rise along
-// the flattened rows.  A merge kernel combines the pieces of each sequence
-// with log-sum-exp weights.
+// round-robin) and the repeated reads of a cache tile hit that XCD's L2.  A
+// range that spans sequence boundaries yields one partial (unnormalised
+// o_lat, running max, running sum) per sequence piece, in slot (range + b)
+// -- unique because range and sequence indices both rise along the rows.  A
+// merge kernel combines the pieces of each sequence with log-sum-exp weights.
 //
 // Inside a workgroup: four waves, 32 heads each (one head per lane pair), on
 // 32x32x16 MFMAs.  A wave computes S^T = C Q^T (32 cache rows x 32 heads per
@@ -96,11 +98,22 @@ __device__ inline int dec_swz(int row) {
 // this wave are outstanding (gfx9 encoding; expcnt and lgkmcnt left open).
 #define DEC_VMCNT(n) ((((n) & 15)) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
-// Rows of sequence b in the flattened order: lens[b] + q_len (the cached
-// prefix and the new tokens) for a valid length, else 0.
+// Rows of sequence b: lens[b] + q_len (the cached prefix and the new
+// tokens) for a valid length, else 0.
 __device__ inline int seq_rows(const int32_t *lens, int b, int64_t cap, int q_len) {
   const int32_t L = lens[b];
   return (L >= 0 && (int64_t)L + q_len <= cap) ? L + q_len : 0;
+}
+
+// Starting a sequence piece (query loads, first tiles in flight, partial
+// stores) costs a workgroup about as much as this many rows of the tile
+// loop.  The rows are laid end to end with this many virtual rows in front
+// of every non-empty sequence before the total is cut into equal ranges, so
+// a range that starts a second sequence gets that many fewer real rows.
+constexpr int PIECE_COST_ROWS = 384;
+__device__ inline int seq_vrows(const int32_t *lens, int b, int64_t cap, int q_len) {
+  const int n = seq_rows(lens, b, cap, q_len);
+  return n > 0 ? n + PIECE_COST_ROWS : 0;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
   const bool wave_live = hg * HPB + wave * HPW < H;
 
   // prefix sums of per-sequence row counts
-  for (int b = tid; b < B; b += DTHREADS) starts[b + 1] = seq_rows(a.lens, b, a.cap, a.q_len);
+  for (int b = tid; b < B; b += DTHREADS) starts[b + 1] = seq_vrows(a.lens, b, a.cap, a.q_len);
   __syncthreads();
   if (wave == 0) {
     int carry = 0;
@@ -202,13 +215,21 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
   const int hpt = a.heads_per_tok > 0 ? a.heads_per_tok : H;
   const int tok = min(h, H - 1) / hpt;
 
-  while (r0 < r1) {
-    const int seg_end = min(r1, starts[b + 1]);
-    const int t_begin = r0 - starts[b], t_end = seg_end - starts[b];
+  while (r0 < r1 && b < B) {
+    // sequence b's real rows sit at [rs, re) of the virtual row axis
+    const int re = starts[b + 1];
+    const int rs = re > starts[b] ? starts[b] + PIECE_COST_ROWS : re;
+    const int pb = max(r0, rs), pe = min(r1, re);
+    if (pb >= pe) {  // only virtual rows of b in this range (uniform)
+      r0 = re;
+      ++b;
+      continue;
+    }
+    const int t_begin = pb - rs, t_end = pe - rs;
     // token tok sees rows 0 .. lens[b] + tok, i.e. all but the last
     // q_len - 1 - tok rows of the sequence; t_end_min is the lowest such
     // limit among the lanes (all of them at q_len = 1)
-    const int rows_b = starts[b + 1] - starts[b];
+    const int rows_b = re - rs;
     const int t_lim = min(t_end, rows_b - (a.q_len - 1 - tok));
     const int t_end_min = min(t_end, rows_b - (a.q_len - 1));
     const char *cb = cache + (int64_t)b * a.cap * W * (int64_t)sizeof(T);
@@ -492,7 +513,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
         a.part_ml[((int64_t)slot * H + h) * 2 + 1] = l_tot;
       }
     }
-    r0 = seg_end;
+    r0 = re;
     ++b;
   }
 #undef DEC_DMA
@@ -520,7 +541,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
   if (tid < 64) {
     int before = 0, all = 0;
     for (int i = tid; i < a.B; i += 64) {
-      const int n = seq_rows(a.lens, i, a.cap, a.q_len);
+      const int n = seq_vrows(a.lens, i, a.cap, a.q_len);
       all += n;
       if (i < b) before += n;
     }
@@ -550,8 +571,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
       }
     return;
   }
+  // pieces: the ranges that hold the real rows [start + PIECE_COST_ROWS, + n_b)
+  // of the virtual row axis
   const int per = (total + a.n_blocks - 1) / a.n_blocks;
-  const int i0 = start / per, i1 = (start + n_b - 1) / per;
+  const int i0 = (start + PIECE_COST_ROWS) / per, i1 = (start + PIECE_COST_ROWS + n_b - 1) / per;
   const int np = i1 - i0 + 1;  // <= n_blocks + 1 <= MERGE_MAXP (checked on the host)
   // piece weights w_i / L of the block's heads: the (max, sum) pairs of all
   // pieces are loaded in parallel into LDS, then one thread per head reduces
