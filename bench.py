@@ -43,14 +43,14 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "c19082f5352e7362fac679aabcd3d000fb38ea1fc7d16ff5e6e0f4e4d823b5b1",
-        "FETCH_SIZE_KiB": 242959.3, "WRITE_SIZE_KiB": 131086.0},
+        "sha256": "da180ac97fcc9c8cfe3521c81033873e5640aa6a602a973325527fe40eef9c42",
+        "FETCH_SIZE_KiB": 243028.1, "WRITE_SIZE_KiB": 131085.5},
     "out_proj": {
-        "sha256": "0ebe29289c211ea3ebaba456341b84ef59b77f1792a7871843a8852ff073e32d",
-        "FETCH_SIZE_KiB": 1511553.0, "WRITE_SIZE_KiB": 57344.0},
+        "sha256": "d9837b641516f022229959c57588eae8c1ad9173a279e9778961aacebe2e8918",
+        "FETCH_SIZE_KiB": 1509229.5, "WRITE_SIZE_KiB": 57344.0},
     "latent_attention": {
-        "sha256": "8dfc4c1e4896683b5d87062cb91e712bf45314747dbd8af069dda25a172ec300",
-        "FETCH_SIZE_KiB": 182835.0, "WRITE_SIZE_KiB": 81983.0},
+        "sha256": "028af137d69e026b2a01b548c26796f76083073cf5bd131b255170a64222b415",
+        "FETCH_SIZE_KiB": 181376.0, "WRITE_SIZE_KiB": 76843.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
