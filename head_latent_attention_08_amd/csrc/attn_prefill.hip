@@ -18,9 +18,12 @@
 // every 16-key group swapped, so the eight keys a lane's A operand needs
 // (4g..4g+3 and 8+4g..8+4g+3) are one 16-byte read.
 //
-// Keys stream in tiles of 32 through two LDS stages: the tile after next is
-// fetched into registers while the current one is multiplied, one barrier
-// per tile.  The softmax keeps a stale running max until a new score exceeds
+// Keys (and, for bf16, V^T) stream in tiles of 32 through three LDS stages,
+// copied global -> LDS two tiles ahead, one barrier per tile.  Iteration t
+// finishes tile t and computes tile t+1's scores; before its barrier a wave
+// waits for every copy the next iteration reads (tile t+2's keys included,
+// which it issued itself), leaving only its V^T copies of tile t+2 in
+// flight.  The softmax keeps a stale running max until a new score exceeds
 // it by more than 2^8 (exp2 domain): the probabilities then stay below 256,
 // exact in fp32, and the output accumulator is rescaled only on those tiles.
 // The score scale folds into the exponent's FMA.
@@ -231,8 +234,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }                                                                                 \
     }                                                                                   \
   } while (0)
-  // copies of this wave per tile (keys and V^T), for the wait counts
-  const int ncopy = (NKN + NKP - wave + 3) / 4 + (VD ? (NVB - wave + 3) / 4 : 0);
+  // V^T copies of this wave per tile (0 .. NVPW), for the wait counts
+  const int nvcopy = (NVB - wave + 3) / 4;
 
   // register staging of one V^T tile (plain code, not lambdas: the staging
   // registers must not end up in scratch memory)
@@ -464,13 +467,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       s_cur = s_nxt;
     }
     if constexpr (VD) {
-      // this wave's copies of tile t+1 have landed once at most tile t+2's
-      // are outstanding; the barrier publishes every wave's
-      constexpr int MX = C::NKPW + NVPW;
+      // The next iteration reads tile t+1's V^T and tile t+2's keys (its
+      // next-tile scores).  This iteration issued tile t+2's key copies
+      // before its V^T copies, so once at most this wave's V^T copies of
+      // tile t+2 are outstanding, everything the next iteration reads from
+      // this wave has landed; the barrier publishes every wave's.
       if (t + 2 < ntiles) {
-        if (ncopy == MX) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(MX));
-        else if (ncopy == MX - 1) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(MX - 1));
-        else if (ncopy == MX - 2) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(MX - 2));
+        if (nvcopy == NVPW) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(NVPW));
+        else if (nvcopy == NVPW - 1) __builtin_amdgcn_s_waitcnt(ATT_VMCNT(NVPW - 1));
         else __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));
       } else {
         __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));

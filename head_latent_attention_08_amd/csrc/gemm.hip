@@ -177,15 +177,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // Large-tile bf16 kernel for the prefill projections (M in the thousands).
 //
-// 256x256 output tile per 256-thread workgroup: four waves in a 2x2 grid of
-// 128x128 wave tiles (4x4 MFMA 32x32 tiles, 256 fp32 accumulators per lane,
-// held in the accumulation registers), one wave per SIMD.  K advances in
-// 64-wide slabs through two LDS stages; the slab after next is fetched into
-// registers while the current one is multiplied, so one barrier per slab
-// suffices.  LDS rows are 64 elements (8 chunks of 16 bytes, half of the 64
-// banks) with chunk j of row r stored at j ^ ((r >> 1) & 7): the fragment
-// reads of sixteen consecutive rows (one 16-lane LDS cycle) and the 16-byte
-// writes of a row hit distinct bank groups without padding.
+// A (64*TM) x (64*TN) output tile per 256-thread workgroup: four waves in a
+// 2x2 grid of (32*TM) x (32*TN) wave tiles (TM x TN MFMA 32x32 tiles, up to
+// 256 fp32 accumulators per lane held in the accumulation registers), one
+// wave per SIMD; the projections use the square 256x256 tile (TM = TN = 4).
+// A copy block of B rows takes its column range's weight matrix, so range
+// starts only need to be multiples of 16 (channel-major ranges, whose stores
+// differ, start on tile boundaries).
+//
+// K advances in 32-wide slabs through four LDS stages.  LDS rows are 32
+// elements (four 16-byte chunks) with chunk j of row r stored at position
+// j ^ ((r / 4) % 4), so the sixteen consecutive rows one quarter wave reads
+// for a fragment fall in distinct banks.
 //
 // Tiles are numbered so that each of the eight XCDs (which take workgroup ids
 // round-robin) works on a contiguous run of tiles, walked in groups of
@@ -195,12 +198,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 //
 // The accumulators leave through LDS: the tile is written there as bf16, then
 // every thread stores 16-byte runs of 8 consecutive columns, which fall in one
-// head of the destination (all column ranges and head widths are multiples of
-// 8), so the head-scatter store stays vectorised.
-constexpr int GB_M = 256, GB_N = 256, GB_K = 32, GB_THREADS = 256, GB_NST = 4;
-constexpr int GB_CPITCH = GB_N + 8;               // epilogue LDS pitch (elements)
-constexpr int GB_STAGE = (GB_M + GB_N) * GB_K;    // elements per operand stage
-constexpr int GB_LDS = GB_M * GB_CPITCH > GB_NST * GB_STAGE ? GB_M * GB_CPITCH : GB_NST * GB_STAGE;
+// head of one column range of the destination (all column ranges and head
+// widths are multiples of 8), so the head-scatter store stays vectorised.
+constexpr int GB_K = 32, GB_THREADS = 256;
+constexpr int GB_STAGES = 4;
+
+template <int TM, int TN, int NST> struct BigTile {
+  static constexpr int M = 64 * TM, N = 64 * TN;            // output tile
+  static constexpr int CPITCH = N + 8;                      // epilogue LDS pitch (elements)
+  static constexpr int STAGE = (M + N) * GB_K;              // elements per operand stage
+  static constexpr int LDS = M * CPITCH > NST * STAGE ? M * CPITCH : NST * STAGE;
+  static constexpr int ABLK = M / 16, NQ = (M + N) / 64;    // A copy blocks; copies per wave per slab
+  static constexpr int QH = (NQ + 1) / 2;                   // copies spread over the first k-step
+  static_assert(ABLK % 4 == 0 && (M + N) % 64 == 0, "copy blocks must split evenly over four waves");
+};
 
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left open (gfx9 encoding)
 constexpr int GB_VMCNT0 = (7 << 4) | (15 << 8);
@@ -229,9 +240,22 @@ template <typename P> __device__ inline P *uniform_ptr(P *q) {
                                (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
 }
 
-__global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int tiles_m,
-                                                              int tiles_n, int remap, int group_m) {
-  __shared__ __attribute__((aligned(16))) bf16 lds[GB_LDS];
+// vmcnt immediates of the K loop, per wave: q copies per slab
+template <int Q> __device__ inline void wait_slabs_outstanding(int slabs) {
+  if (slabs >= 4) __builtin_amdgcn_s_waitcnt(GB_VMCNT(4 * Q));
+  else if (slabs == 3) __builtin_amdgcn_s_waitcnt(GB_VMCNT(3 * Q));
+  else if (slabs == 2) __builtin_amdgcn_s_waitcnt(GB_VMCNT(2 * Q));
+  else if (slabs == 1) __builtin_amdgcn_s_waitcnt(GB_VMCNT(Q));
+  else __builtin_amdgcn_s_waitcnt(GB_VMCNT0);
+}
+
+// Launch window: output columns [n_base, n_base + tiles_n * tile N) of every row.
+template <int TM, int TN, int GB_NST>
+__global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int tiles_m, int tiles_n,
+                                                              int n_base, int remap, int group_m) {
+  using BT = BigTile<TM, TN, GB_NST>;
+  constexpr int NQ = BT::NQ, QH = BT::QH, ABLK = BT::ABLK;
+  __shared__ __attribute__((aligned(16))) bf16 lds[BT::LDS];
 
   // tile index: contiguous run per XCD, then grouped row-major order
   const int T = tiles_m * tiles_n;
@@ -243,7 +267,8 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   const int gm = min(tiles_m - first_m, group_m);
   const int tm = first_m + (t % per_group) % gm;
   const int tn = (t % per_group) / gm;
-  const int m0 = tm * GB_M, n0 = tn * GB_N;
+  const int m0 = tm * BT::M, n0 = n_base + tn * BT::N;
+  const int nk = p.K / GB_K;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
@@ -254,78 +279,91 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   // Slabs of 32 k are copied from global memory straight into LDS
   // (global_load_lds_dwordx4: lane l of a copy writes the 16 bytes at LDS
   // offset 16 l of a 1 KB block, i.e. sixteen 64-byte slab rows), so no
-  // staging registers and no LDS store instructions are involved.  A slab
-  // is 32 blocks; block b of A (or B) holds rows 16b..16b+15, and lane l
-  // fills row 16b + l/4 at position l%4, which holds logical chunk
-  // (l%4) ^ (row/4 % 4).  Wave w issues blocks w, w+4, .. of A then of B;
-  // each lane's source offset of each of its 8 blocks is fixed for the whole
-  // K loop (rows clamped into the matrix: rows past M or N only feed outputs
-  // that are never stored), and the slab's k offset moves the scalar base.
-  // Column ranges start at multiples of 256 (checked on the host), so one
-  // tile reads B from a single range.
-  const int st = seg_of(p, n0);
-  const int64_t t_ldb = SEG_FIELD(p, st, ldb);
-  const int t_nb = SEG_FIELD(p, st, n_begin);
-  const bf16 *Ab = A + (int64_t)m0 * p.lda;
-  const bf16 *Bb = reinterpret_cast<const bf16 *>(SEG_FIELD(p, st, B)) + (int64_t)(n0 - t_nb) * t_ldb;
-  uint32_t doff[8];
+  // staging registers and no LDS store instructions are involved.  A stage
+  // holds M/16 blocks of A rows then N/16 blocks of B rows; block b holds
+  // rows 16b..16b+15, and lane l fills row 16b + l/4 at position l%4, which
+  // holds logical chunk (l%4) ^ (row/4 % 4).  Wave w issues blocks w, w+4,
+  // w+8, ..; each copy's scalar base (its column range's weight matrix: a
+  // block never straddles two ranges, whose starts are multiples of 16) and
+  // each lane's offset are fixed for the whole K loop (rows clamped into the
+  // matrix: rows past M or N only feed outputs that are never stored), and
+  // the slab's k offset moves the scalar base.
+  const bf16 *qbase[NQ];
+  uint32_t doff[NQ];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int blk = wave + 4 * (q & 3);
-    const int row = 16 * blk + (lane >> 2);
-    const int j = (lane & 3) ^ ((row >> 2) & 3);
-    const int rc = q < 4 ? min(row, p.M - 1 - m0) : min(row, p.N - 1 - n0);
-    const int64_t ld = q < 4 ? p.lda : t_ldb;
-    doff[q] = (uint32_t)((rc * ld + j * 8) * (int64_t)sizeof(bf16));
+  for (int q = 0; q < NQ; ++q) {
+    const int blk = wave + 4 * q;
+    if (q < ABLK / 4) {
+      const int row = 16 * blk + (lane >> 2);
+      const int j = (lane & 3) ^ ((row >> 2) & 3);
+      qbase[q] = A + (int64_t)m0 * p.lda;
+      doff[q] = (uint32_t)(((int64_t)min(row, p.M - 1 - m0) * p.lda + j * 8) * (int64_t)sizeof(bf16));
+    } else {
+      const int rt = 16 * (blk - ABLK);                     // block's first row within the tile
+      const int row = rt + (lane >> 2);
+      const int j = (lane & 3) ^ ((row >> 2) & 3);
+      const int s = seg_of(p, min(n0 + rt, p.N - 1));       // uniform: one range per block
+      const int nb = SEG_FIELD(p, s, n_begin);
+      const int64_t ldb = SEG_FIELD(p, s, ldb);
+      qbase[q] = reinterpret_cast<const bf16 *>(SEG_FIELD(p, s, B));
+      doff[q] = (uint32_t)(((int64_t)(min(n0 + row, p.N - 1) - nb) * ldb + j * 8) * (int64_t)sizeof(bf16));
+    }
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16 *)lds;
-  // copy q (0..7) of slab KT into stage KT % GB_NST
-#define GB_DMA1(KT, Q)                                                            \
-  do {                                                                            \
-    const int kt_ = (KT);                                                         \
-    const bf16 *a_ = uniform_ptr(Ab + kt_ * GB_K), *b_ = uniform_ptr(Bb + kt_ * GB_K); \
-    const int blk = wave + 4 * ((Q) & 3);                                         \
-    const uint32_t m0_ = __builtin_amdgcn_readfirstlane(                          \
-        lds_base + (kt_ % GB_NST) * (GB_STAGE * 2) + ((Q) < 4 ? 0 : GB_M * GB_K * 2) + blk * 1024); \
-    if ((Q) < 4)                                                                  \
-      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"           \
-                   :: "v"(doff[Q]), "s"(a_), "s"(m0_) : "memory", "m0");          \
-    else                                                                          \
-      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"           \
-                   :: "v"(doff[Q]), "s"(b_), "s"(m0_) : "memory", "m0");          \
-  } while (0)
+  // Scalar operands of the copies of one slab (global base per copy, LDS
+  // block address for M0), formed before the MFMAs they are spread over, so
+  // that a copy between two MFMAs is just an M0 write and the copy itself.
+  struct SlabOps {
+    const bf16 *src[NQ];
+    uint32_t dst[NQ];
+  };
+  auto slab_ops = [&](int kt, SlabOps &o) {
+    const uint32_t stage = lds_base + (kt % GB_NST) * (BT::STAGE * 2);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      o.src[q] = uniform_ptr(qbase[q] + kt * GB_K);
+      o.dst[q] = __builtin_amdgcn_readfirstlane(stage + (wave + 4 * q) * 1024);
+    }
+  };
+#define GB_COPY(O, Q)                                                           \
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"            \
+               :: "v"(doff[Q]), "s"((O).src[Q]), "s"((O).dst[Q]) : "memory", "m0")
 
-  f32x16 acc[4][4];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   auto load_frags = [&](int kt, int kk, bf16x8 *a, bf16x8 *b) {
-    const bf16 *As = lds + (kt % GB_NST) * GB_STAGE, *Bs = As + GB_M * GB_K;
+    const bf16 *As = lds + (kt % GB_NST) * BT::STAGE, *Bs = As + BT::M * GB_K;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(wm * 128 + i * 32 + l32, kk + g * 8)]);
+    for (int i = 0; i < TM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8 *>(&As[swz(wm * 32 * TM + i * 32 + l32, kk + g * 8)]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(wn * 128 + j * 32 + l32, kk + g * 8)]);
+    for (int j = 0; j < TN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[swz(wn * 32 * TN + j * 32 + l32, kk + g * 8)]);
   };
-  // the 16 MFMAs of one k-step; with DMA_KT >= 0, copies Q0..Q0+3 of that
-  // slab go one after every fourth MFMA (a copy instruction stalls its wave
+  // the TM x TN MFMAs of one k-step; with DMA_KT >= 0, copies of that slab go
+  // between rows of MFMAs: the first k-step of an interval (H = 0) issues
+  // copies 0..QH-1, the second QH..NQ-1 (a copy instruction stalls its wave
   // until the address unit takes it; between MFMAs the stall overlaps the
   // matrix pipe instead of idling it)
-  auto mma16 = [&](const bf16x8 *a, const bf16x8 *b, int dma_kt, int q0) {
+  auto mma = [&](const bf16x8 *a, const bf16x8 *b, const SlabOps *ops, int h) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      if (dma_kt >= 0) {
+      if (ops) {
         __builtin_amdgcn_sched_barrier(0);
-        if (q0 == 0) GB_DMA1(dma_kt, i);
-        else GB_DMA1(dma_kt, 4 + i);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int lo = h * QH + (i * QH) / TM, hi = h * QH + ((i + 1) * QH) / TM;
+          if (q >= lo && q < hi && q < (h + 1) * QH) GB_COPY(*ops, q);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -333,85 +371,97 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
 
   // Pipeline over barrier intervals j: the interval runs k-step 16..31 of
   // slab j and k-step 0..15 of slab j+1 (whose fragments are read from LDS
-  // while the previous MFMAs run), copies slab j+4 into the stage slab j
+  // while the previous MFMAs run), copies slab j+NST into the stage slab j
   // used (free once every wave passed barrier j: a wave's LDS reads are
-  // complete at its barrier), then waits for slab j+2.
-  const int nk = p.K / GB_K;
+  // complete at its barrier), then waits for slab j+2.  The main loop always
+  // copies (constant wait, no branches); the last intervals only drain.
+  SlabOps ops;
 #pragma unroll
   for (int c = 0; c < GB_NST; ++c)
     if (c < nk) {
+      slab_ops(c, ops);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) GB_DMA1(c, q);
+      for (int q = 0; q < NQ; ++q) GB_COPY(ops, q);
     }
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
-  // slab 0 landed: at most slabs 1..3 outstanding
-  if (nk >= 4) __builtin_amdgcn_s_waitcnt(GB_VMCNT(24));
-  else if (nk == 3) __builtin_amdgcn_s_waitcnt(GB_VMCNT(16));
-  else if (nk == 2) __builtin_amdgcn_s_waitcnt(GB_VMCNT(8));
-  else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
+  bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+  // slab 0 landed: at most slabs 1..NST-1 outstanding
+  wait_slabs_outstanding<NQ>(min(nk, GB_NST) - 1);
   __syncthreads();
   load_frags(0, 0, a0, b0);
   load_frags(0, 16, a1, b1);
   __builtin_amdgcn_sched_barrier(0);
-  mma16(a0, b0, -1, 0);
+  mma(a0, b0, nullptr, 0);
   __builtin_amdgcn_sched_barrier(0);
   // slab 1 landed
-  if (nk >= 4) __builtin_amdgcn_s_waitcnt(GB_VMCNT(16));
-  else if (nk == 3) __builtin_amdgcn_s_waitcnt(GB_VMCNT(8));
-  else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
+  wait_slabs_outstanding<NQ>(min(nk, GB_NST) - 2);
   __syncthreads();
-  for (int j = 0; j + 1 < nk; ++j) {
-    const int dma_kt = j + GB_NST < nk ? j + GB_NST : -1;
+  int j = 0;
+  for (; j + GB_NST < nk; ++j) {
+    slab_ops(j + GB_NST, ops);
     load_frags(j + 1, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    mma16(a1, b1, dma_kt, 0);
+    mma(a1, b1, &ops, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_frags(j + 1, 16, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    mma16(a0, b0, dma_kt, 4);
+    mma(a0, b0, &ops, 1);
     __builtin_amdgcn_sched_barrier(0);
-    // slab j+2 landed: slabs j+3 .. min(nk-1, j+4) may stay outstanding
-    const int later = min(nk - 1, j + GB_NST) - (j + 2);
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(GB_VMCNT(16));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(GB_VMCNT(8));
-    else __builtin_amdgcn_s_waitcnt(GB_VMCNT(0));
+    // slab j+2 landed: slabs j+3 .. j+NST may stay outstanding
+    __builtin_amdgcn_s_waitcnt(GB_VMCNT((GB_NST - 2) * NQ));
     __syncthreads();
   }
-  mma16(a1, b1, -1, 0);  // k-step 16..31 of the last slab
-#undef GB_DMA1
+  for (; j + 1 < nk; ++j) {
+    load_frags(j + 1, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1, nullptr, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(j + 1, 16, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0, nullptr, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_slabs_outstanding<NQ>(nk - 1 - (j + 2));
+    __syncthreads();
+  }
+  mma(a1, b1, nullptr, 0);  // k-step 16..31 of the last slab
+#undef GB_COPY
 
   // epilogue through LDS (the operand stages are free after the last barrier)
   bf16 *Cs = lds;
-  bf16 *t_C = reinterpret_cast<bf16 *>(SEG_FIELD(p, st, C));
-  const int t_dh = SEG_FIELD(p, st, dh), t_off = SEG_FIELD(p, st, off);
-  const int64_t t_ld = SEG_FIELD(p, st, ld);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        Cs[(wm * 128 + i * 32 + acc_row(r, lane)) * GB_CPITCH + wn * 128 + j * 32 + l32] =
+        Cs[(wm * 32 * TM + i * 32 + acc_row(r, lane)) * BT::CPITCH + wn * 32 * TN + j * 32 + l32] =
             (bf16)acc[i][j][r];
   __syncthreads();
-  if (!SEG_FIELD(p, st, tr)) {
-    for (int it = 0; it < (GB_M * GB_N / 8) / GB_THREADS; ++it) {
+  // Channel-major ranges are aligned to the tile on the host, so a tile is
+  // either all row-major or all channel-major.
+  const int st0 = seg_of(p, min(n0, p.N - 1));
+  if (!SEG_FIELD(p, st0, tr)) {
+    constexpr int RUNS = BT::N / 8;
+    for (int it = 0; it < (BT::M * RUNS) / GB_THREADS; ++it) {
       const int c = tid + GB_THREADS * it;
-      const int row = c >> 5, cc = c & 31;
+      const int row = c / RUNS, cc = c - row * RUNS;
       const int m = m0 + row, n = n0 + cc * 8;
       if (m >= p.M || n >= p.N) continue;
-      const int nn = n - t_nb;
-      const int h = nn / t_dh, d = nn - h * t_dh;
+      const int s = seg_of(p, n);
+      const int nn = n - SEG_FIELD(p, s, n_begin), dh = SEG_FIELD(p, s, dh);
+      const int h = nn / dh, d = nn - h * dh;
       const int b = m / p.S, sq = m - b * p.S;
-      bf16 *dst = t_C + ((int64_t)(b * p.H + h) * p.S + sq) * t_ld + t_off + d;
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * GB_CPITCH + cc * 8]);
+      bf16 *dst = reinterpret_cast<bf16 *>(SEG_FIELD(p, s, C)) +
+                  ((int64_t)(b * p.H + h) * p.S + sq) * SEG_FIELD(p, s, ld) + SEG_FIELD(p, s, off) + d;
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * BT::CPITCH + cc * 8]);
     }
   } else {
     // channel-major destination: runs of 8 consecutive rows (tokens) of one
     // column; lane-consecutive columns keep the 2-byte LDS reads conflict-free
-    for (int it = 0; it < (GB_M * GB_N / 8) / GB_THREADS; ++it) {
+    bf16 *t_C = reinterpret_cast<bf16 *>(SEG_FIELD(p, st0, C));
+    const int t_dh = SEG_FIELD(p, st0, dh), t_nb = SEG_FIELD(p, st0, n_begin);
+    for (int it = 0; it < (BT::M * BT::N / 8) / GB_THREADS; ++it) {
       const int c = tid + GB_THREADS * it;
-      const int col = c & (GB_N - 1), rg = c / GB_N;
+      const int rg = c / BT::N, col = c - rg * BT::N;
       const int m = m0 + rg * 8, n = n0 + col;
       if (m >= p.M || n >= p.N) continue;
       const int nn = n - t_nb;
@@ -420,12 +470,12 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
       if (sq + 8 <= p.S && m + 8 <= p.M) {
         bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = Cs[(rg * 8 + e) * GB_CPITCH + col];
+        for (int e = 0; e < 8; ++e) v[e] = Cs[(rg * 8 + e) * BT::CPITCH + col];
         *reinterpret_cast<bf16x8 *>(t_C + ((int64_t)(b * p.H + h) * t_dh + d) * p.S + sq) = v;
       } else {
         for (int e = 0; e < 8 && m + e < p.M; ++e) {
           const int me = m + e, be = me / p.S, se = me - be * p.S;
-          t_C[((int64_t)(be * p.H + h) * t_dh + d) * p.S + se] = Cs[(rg * 8 + e) * GB_CPITCH + col];
+          t_C[((int64_t)(be * p.H + h) * t_dh + d) * p.S + se] = Cs[(rg * 8 + e) * BT::CPITCH + col];
         }
       }
     }
@@ -626,6 +676,24 @@ size_t gemm_scratch_bytes(int dtype, int M, int N, int K, int batch) {
   return (size_t)skinny_split(N, K, batch) * batch * M * N * sizeof(float);
 }
 
+// A big-kernel tile must not mix row-major and channel-major column ranges.
+static bool tr_aligned(const GemmDesc &d, int bn) {
+  for (int i = 1; i < d.nseg; ++i)
+    if (d.seg[i].tr != d.seg[i - 1].tr && d.seg[i].n_begin % bn != 0) return false;
+  return true;
+}
+
+template <int TM, int TN>
+static hipError_t launch_big(const GemmParams &p, const GemmDesc &d, int n_lo, int n_hi, hipStream_t st) {
+  constexpr int BM = 64 * TM, BN = 64 * TN;
+  const int tm = (d.M + BM - 1) / BM, tn = (n_hi - n_lo + BN - 1) / BN;
+  const int T = tm * tn;
+  const int group_m = d.K >= 4096 ? 8 : (d.K <= 1024 ? 2 : 4);
+  hipLaunchKernelGGL((gemm_big_kernel<TM, TN, GB_STAGES>), dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn, n_lo,
+                     (T % 8 == 0) ? 1 : 0, group_m);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   if (d.M <= 0 || d.N <= 0 || d.K <= 0 || d.batch <= 0) return hipSuccess;
   GemmParams p;
@@ -644,15 +712,8 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   bool big = d.dtype == BF16 && !d.b_kn && d.batch == 1 && d.K % GB_K == 0 && d.M >= 512 &&
              d.N % 8 == 0 && (int64_t)d.M * d.lda < (1LL << 31);
   for (int i = 0; i < d.nseg && big; ++i)
-    big = d.seg[i].n_begin % GB_N == 0 && (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
-  if (big) {
-    const int tm = (d.M + GB_M - 1) / GB_M, tn = (d.N + GB_N - 1) / GB_N;
-    const int T = tm * tn;
-    const int group_m = d.K >= 4096 ? 8 : (d.K <= 1024 ? 2 : 4);
-    hipLaunchKernelGGL(gemm_big_kernel, dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn,
-                       (T % 8 == 0) ? 1 : 0, group_m);
-    return hipGetLastError();
-  }
+    big = d.seg[i].n_begin % 16 == 0 && (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
+  if (big && tr_aligned(d, BigTile<4, 4, GB_STAGES>::N)) return launch_big<4, 4>(p, d, 0, d.N, st);
   bool skinny = d.dtype == BF16 && !d.b_kn && d.M <= SK_M && d.K % SK_K == 0 && d.N % 8 == 0 &&
                 d.workspace != nullptr;
   for (int i = 0; i < d.nseg && skinny; ++i) skinny = d.seg[i].n_begin % SK_N == 0;

@@ -127,6 +127,43 @@ def test_determinism_bitwise():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.timeout(300)
+def test_v3_determinism_bitwise():
+    # At full size (many key tiles per query block, big-tile projections,
+    # decode rows cut into ranges) every run gives bit-identical results,
+    # whatever the workspace held before: no copy is read before it lands.
+    m = _m()
+    c = si.CONFIGS["v3_prefill"]
+    x, w = si.make_inputs(c)
+    print("v3 determinism: prefill B=1 S=4096 x3, seed 3000", flush=True)
+    cfg = mla_cfg(c)
+    wd, xd = weights_to_dev(w, "bf16"), to_dev(x, "bf16")
+    ws = torch.empty(m.mla_prefill_workspace_size(cfg, 1, x.shape[1]), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for fill in (0, 255, 0):
+        ws.fill_(fill)
+        y, lat, _ = m.mla_prefill_forward(cfg, wd, xd, workspace=ws, want_latent=True)
+        torch.cuda.synchronize()
+        outs.append((y, lat))
+    for y, lat in outs[1:]:
+        assert torch.equal(lat, outs[0][1])
+        assert torch.equal(y, outs[0][0]), f"{(y != outs[0][0]).sum().item()} elements differ"
+    del outs, ws, wd, xd
+    c = si.CONFIGS["v3_decode"]
+    print("v3 determinism: decode B=64 cap=8193 x2, seed 4000", flush=True)
+    x, w, lens, cache = si.make_decode_inputs(c)
+    cfg = mla_cfg(c)
+    wd, xd, lens_d = weights_to_dev(w, "bf16"), to_dev(x, "bf16"), torch.from_numpy(lens).cuda()
+    res = []
+    for _ in range(2):
+        cache_d = to_dev(cache, "bf16")
+        y, _ = m.mla_decode_absorbed(cfg, wd, xd, cache_d, lens_d)
+        torch.cuda.synchronize()
+        res.append((y, cache_d))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
 @pytest.mark.parametrize("name", ["small", "v3_prefill"])
 def test_decode_after_prefill(name):
     # decoding token S over the latent rows a GPU prefill of tokens 0..S-1
