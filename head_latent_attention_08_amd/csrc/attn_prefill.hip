@@ -38,7 +38,7 @@
 namespace mla {
 namespace {
 
-constexpr int BQ = 128, BKV = 32;
+constexpr int BKV = 32;
 
 // s_waitcnt immediate: at most n vector-memory operations of this wave
 // outstanding (gfx9 encoding; expcnt and lgkmcnt left open)
@@ -46,7 +46,7 @@ constexpr int BQ = 128, BKV = 32;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LOG2 = 8.0f;
 
-template <typename T, int DN, int DR, int DV>
+template <typename T, int DN, int DR, int DV, int NW>
 struct AttnCfg {
   using MF = Mfma32<T>;
   static constexpr int VEC = 16 / sizeof(T);
@@ -72,11 +72,11 @@ struct AttnCfg {
   static constexpr int NKN = (BKV * KNP * ES + 1023) / 1024;
   static constexpr int NKP = (BKV * KPP * ES + 1023) / 1024;
   static constexpr int KSTAGEB = (NKN + NKP) * 1024;
-  static constexpr int NKPW = (NKN + NKP + 3) / 4;  // copy blocks per wave (at most)
+  static constexpr int NKPW = (NKN + NKP + NW - 1) / NW;  // copy blocks per wave (at most)
   // V^T stage copied straight from global memory (bf16, 32 keys = 64-byte
   // rows): DVP rows in 1 KB blocks of 16
   static constexpr int NVB = DVP / 16;
-  static constexpr int NVPW = (NVB + 3) / 4;
+  static constexpr int NVPW = (NVB + NW - 1) / NW;
 };
 
 // Key order inside each 16-key group of a tile as seen by the score MFMA when
@@ -94,9 +94,10 @@ __device__ inline uint4 ld16(const T *p) { return *reinterpret_cast<const uint4 
 // the same copy instructions as the keys (no staging registers, no LDS
 // stores), with the score MFMA reading keys in pk16 order.  Otherwise V^T
 // is staged through registers and stored to LDS with two quads swapped.
-template <typename T, int DN, int DR, int DV, bool VD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(PrefillAttnArgs a) {
-  using C = AttnCfg<T, DN, DR, DV>;
+template <typename T, int DN, int DR, int DV, bool VD, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(PrefillAttnArgs a) {
+  using C = AttnCfg<T, DN, DR, DV, NW>;
+  constexpr int BQ = 32 * NW;  // queries per workgroup: 32 per wave
   using MF = typename C::MF;
   constexpr int VEC = C::VEC, DQK = C::DQK, KPITCH = C::KPITCH, VPITCH = C::VPITCH,
                 NQF = C::NQF, NDT = C::NDT, DVP = C::DVP, CPRK = C::CPRK, CPRV = C::CPRV,
@@ -105,6 +106,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 KCH = C::KCH, VCH = C::VCH, KSTAGE = C::KSTAGE, VSTAGE = C::VSTAGE,
                 NVB = C::NVB, NVPW = C::NVPW;
   static_assert(!VD || (sizeof(T) == 2 && BKV == 32), "verbatim V^T copies need bf16 tiles of 32");
+  static_assert(VD || NW == 4, "the register-staged V^T path assumes 256 threads");
   __shared__ __attribute__((aligned(1024))) char Kl[3 * KSTAGEB];
   __shared__ __attribute__((aligned(1024))) char Vl[VD ? 3 * NVB * 1024 : 16];
   __shared__ __attribute__((aligned(16))) T Vt[VD ? VEC : 3 * VSTAGE];
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // K tiles are copied from global memory straight into LDS
   // (global_load_lds_dwordx4, 16 bytes a lane into consecutive LDS bytes of a
-  // 1 KB block).  This wave copies blocks wave, wave + 4, ..; a lane's row
+  // 1 KB block).  This wave copies blocks wave, wave + NW, ..; a lane's row
   // and byte column in its block are fixed for the whole loop (padding
   // lanes copy the tile's first chunk: finite values that only meet zero
   // query columns), the tile base is a scalar, and rows past the end of the
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int drow[NKPW], dcb[NKPW];
 #pragma unroll
   for (int k = 0; k < NKPW; ++k) {
-    const int blk = wave + 4 * k;
+    const int blk = wave + NW * k;
     drow[k] = 0;
     dcb[k] = 0;
     if (blk < NKN) {
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const T *bn_ = kn + (int64_t)j0_ * DN;                                              \
     const T *bp_ = kpe + (int64_t)j0_ * a.ld_kpe;                                       \
     _Pragma("unroll") for (int k = 0; k < NKPW; ++k) {                                  \
-      const int blk = wave + 4 * k;                                                     \
+      const int blk = wave + NW * k;                                                    \
       const int r_ = min(drow[k], lim_);                                                \
       const uint32_t m0_ = lds_k + (STG) * KSTAGEB + blk * 1024;                        \
       if (blk < NKN) {                                                                  \
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }                                                                                   \
   } while (0)
 
-  // VD: V^T tile copies.  Block vb = wave + 4k holds rows 16 vb .. + 15 (64
+  // VD: V^T tile copies.  Block vb = wave + NW k holds rows 16 vb .. + 15 (64
   // bytes = 32 keys each); lane l fills row 16 vb + l/4 at position l%4,
   // which holds logical 16-byte chunk (l%4) ^ (row/4 % 4) (conflict-free
   // 16-byte reads of 16 consecutive rows).  Rows past DV repeat row 0 (their
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int vrow[NVPW], vch[NVPW];
 #pragma unroll
   for (int k = 0; k < NVPW; ++k) {
-    const int row = 16 * (wave + 4 * k) + (lane >> 2);
+    const int row = 16 * (wave + NW * k) + (lane >> 2);
     vrow[k] = row < DV ? row : 0;
     vch[k] = (lane & 3) ^ ((row >> 2) & 3);
   }
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   do {                                                                                  \
     const int j0_ = (J0);                                                               \
     _Pragma("unroll") for (int k = 0; k < NVPW; ++k) {                                  \
-      const int vb = wave + 4 * k;                                                      \
+      const int vb = wave + NW * k;                                                     \
       if (vb < NVB) {                                                                   \
         const uint32_t off_ = (uint32_t)((vrow[k] * S + min(j0_ + 8 * vch[k], S - 8)) * ES); \
         const uint32_t m0_ = lds_v + (STG) * (NVB * 1024) + vb * 1024;                  \
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }                                                                                   \
   } while (0)
   // V^T copies of this wave per tile (0 .. NVPW), for the wait counts
-  const int nvcopy = (NVB - wave + 3) / 4;
+  const int nvcopy = (NVB - wave + NW - 1) / NW;
 
   // register staging of one V^T tile (plain code, not lambdas: the staging
   // registers must not end up in scratch memory)
@@ -524,14 +526,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// Waves per workgroup on the bf16 copy path.  Eight waves over 256 queries
+// halve the copies per key tile but run 9% slower than two independent
+// 4-wave workgroups per CU, whose phases drift apart so that one's softmax
+// overlaps the other's MFMAs.
+constexpr int ATT_VD_WAVES = 4;
+
 template <typename T, int DN, int DR, int DV>
 hipError_t launch_t(const PrefillAttnArgs &a, hipStream_t st) {
-  const int nq = (a.S + BQ - 1) / BQ;
-  dim3 grid(nq * a.H * a.B);
-  if (sizeof(T) == 2 && a.S % 8 == 0)
-    hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, sizeof(T) == 2>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, false>), grid, dim3(256), 0, st, a);
+  if constexpr (sizeof(T) == 2) {
+    if (a.S % 8 == 0) {
+      constexpr int NW = ATT_VD_WAVES;
+      dim3 grid((a.S + 32 * NW - 1) / (32 * NW) * a.H * a.B);
+      hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, true, NW>), grid, dim3(64 * NW), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  dim3 grid((a.S + 127) / 128 * a.H * a.B);
+  hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, false, 4>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
