@@ -427,19 +427,19 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
 
   // epilogue through LDS (the operand stages are free after the last barrier)
   bf16 *Cs = lds;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        Cs[(wm * 32 * TM + i * 32 + acc_row(r, lane)) * BT::CPITCH + wn * 32 * TN + j * 32 + l32] =
-            (bf16)acc[i][j][r];
-  __syncthreads();
   // Channel-major ranges are aligned to the tile on the host, so a tile is
   // either all row-major or all channel-major.
   const int st0 = seg_of(p, min(n0, p.N - 1));
   if (!SEG_FIELD(p, st0, tr)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          Cs[(wm * 32 * TM + i * 32 + acc_row(r, lane)) * BT::CPITCH + wn * 32 * TN + j * 32 + l32] =
+              (bf16)acc[i][j][r];
+    __syncthreads();
     constexpr int RUNS = BT::N / 8;
     for (int it = 0; it < (BT::M * RUNS) / GB_THREADS; ++it) {
       const int c = tid + GB_THREADS * it;
@@ -455,27 +455,46 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
       *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * BT::CPITCH + cc * 8]);
     }
   } else {
-    // channel-major destination: runs of 8 consecutive rows (tokens) of one
-    // column; lane-consecutive columns keep the 2-byte LDS reads conflict-free
+    // Channel-major destination: the tile goes to LDS transposed (column n
+    // holds the tile's rows, i.e. tokens, contiguously).  A lane's
+    // accumulators hold four consecutive rows of one column, written as one
+    // 8-byte store; then lanes take consecutive 8-token runs of one column,
+    // so a half wave writes 512 consecutive bytes of the output.
+    constexpr int TP = BT::M + 8;  // transposed pitch (elements)
+    static_assert(BT::N * TP <= BT::LDS, "transposed tile must fit the LDS area");
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // acc rows 8q + 4g .. +3 (acc_row of r = 4q .. 4q+3) of column l32
+          bf16 v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)acc[i][j][4 * q + e];
+          *reinterpret_cast<uint2 *>(&Cs[(wn * 32 * TN + j * 32 + l32) * TP + wm * 32 * TM + i * 32 +
+                                         acc_row(4 * q, lane)]) = *reinterpret_cast<const uint2 *>(v4);
+        }
+    __syncthreads();
     bf16 *t_C = reinterpret_cast<bf16 *>(SEG_FIELD(p, st0, C));
     const int t_dh = SEG_FIELD(p, st0, dh), t_nb = SEG_FIELD(p, st0, n_begin);
+    constexpr int RG = BT::M / 8;  // 8-token runs per column
     for (int it = 0; it < (BT::M * BT::N / 8) / GB_THREADS; ++it) {
       const int c = tid + GB_THREADS * it;
-      const int rg = c / BT::N, col = c - rg * BT::N;
+      const int col = c / RG, rg = c - col * RG;
       const int m = m0 + rg * 8, n = n0 + col;
       if (m >= p.M || n >= p.N) continue;
       const int nn = n - t_nb;
       const int h = nn / t_dh, d = nn - h * t_dh;
       const int b = m / p.S, sq = m - b * p.S;
+      const bf16 *src = &Cs[col * TP + rg * 8];
       if (sq + 8 <= p.S && m + 8 <= p.M) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = Cs[(rg * 8 + e) * BT::CPITCH + col];
-        *reinterpret_cast<bf16x8 *>(t_C + ((int64_t)(b * p.H + h) * t_dh + d) * p.S + sq) = v;
+        *reinterpret_cast<uint4 *>(t_C + ((int64_t)(b * p.H + h) * t_dh + d) * p.S + sq) =
+            *reinterpret_cast<const uint4 *>(src);
       } else {
         for (int e = 0; e < 8 && m + e < p.M; ++e) {
           const int me = m + e, be = me / p.S, se = me - be * p.S;
-          t_C[((int64_t)(be * p.H + h) * t_dh + d) * p.S + se] = Cs[(rg * 8 + e) * BT::CPITCH + col];
+          t_C[((int64_t)(be * p.H + h) * t_dh + d) * p.S + se] = src[e];
         }
       }
     }

@@ -152,9 +152,12 @@ def test_prefill_small_bf16(conv):
                       "latent")
 
 
-@pytest.mark.parametrize("S,B", [(1, 1), (7, 2), (100, 1), (129, 3), (300, 1)])
+@pytest.mark.parametrize("S,B", [(1, 1), (7, 2), (100, 1), (129, 3), (300, 1), (300, 2), (515, 1)])
 def test_prefill_ragged_lengths(S, B):
-    # sequence lengths that leave partial query/key tiles, and a single token
+    # sequence lengths that leave partial query/key tiles, and a single token;
+    # with B*S >= 512 the projections run on the large-tile kernel, whose
+    # channel-major stores then meet 8-token runs that cross a sequence end
+    # (S = 300, B = 2) and a ragged last row tile (S = 515)
     c = si.CONFIGS["small"]
     m, cfg, x, w, y, lat, ws = _run_prefill(c, "interleaved", S=S, B=B)
     ref = orc.mla_prefill(oracle_cfg(c, rope="interleaved"), w, x)
