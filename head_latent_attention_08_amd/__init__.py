@@ -20,6 +20,8 @@ from .mla import (  # noqa: F401
     mla_decode_workspace_size,
     mla_prefill_forward,
     mla_prefill_layout_of,
+    mla_prefill_varlen_forward,
+    mla_prefill_varlen_workspace_size,
     mla_prefill_workspace_size,
     mla_rope_apply,
     mla_set_stage_events,

@@ -94,7 +94,7 @@ __device__ inline uint4 ld16(const T *p) { return *reinterpret_cast<const uint4 
 // the same copy instructions as the keys (no staging registers, no LDS
 // stores), with the score MFMA reading keys in pk16 order.  Otherwise V^T
 // is staged through registers and stored to LDS with two quads swapped.
-template <typename T, int DN, int DR, int DV, bool VD, int NW>
+template <typename T, int DN, int DR, int DV, bool VD, int NW, bool VARLEN>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(PrefillAttnArgs a) {
   using C = AttnCfg<T, DN, DR, DV, NW>;
   constexpr int BQ = 32 * NW;  // queries per workgroup: 32 per wave
@@ -293,8 +293,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const float sl2 = a.scale * LOG2E;
 
   const int kv_end = min(S, q0 + BQ);
-  const int ntiles = (kv_end + BKV - 1) / BKV;
-  const int tw = qw0 / BKV;  // this wave's diagonal tile, the last one it needs
+  // Key tiles t = 0.. start at key jb: 0, or for packed variable-length
+  // sequences the tile of the first query's sequence start (starts never
+  // decrease along the token stream, so no query of the block needs keys
+  // before it); a lane masks the keys before its own sequence's start.
+  const int key_lo = VARLEN ? a.kv_start[min(iq, S - 1)] : 0;
+  const int jb = VARLEN ? a.kv_start[q0] / BKV * BKV : 0;
+  const int ntiles = (kv_end + BKV - 1) / BKV - jb / BKV;
+  const int tw = qw0 / BKV - jb / BKV;  // this wave's diagonal tile, the last one it needs
 
   // fragment f of this lane's key row in the K stage starting at byte KB:
   // k_nope region for f < NQN, k_pe region after it
@@ -319,22 +325,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // scores run underneath the exponentials, and stores tile t+2's V^T
   // (loaded into registers one iteration earlier).
   if constexpr (VD) {
-    ATT_KDMA(0, 0);
-    ATT_VDMA(0, 0);
+    ATT_KDMA(0, jb);
+    ATT_VDMA(0, jb);
     if (ntiles > 1) {
-      ATT_KDMA(1, BKV);
-      ATT_VDMA(1, BKV);
+      ATT_KDMA(1, jb + BKV);
+      ATT_VDMA(1, jb + BKV);
     }
   } else {
-    ATT_KDMA(0, 0);
-    ATT_FETCH(0);
+    ATT_KDMA(0, jb);
+    ATT_FETCH(jb);
     ATT_STASH(0);
     if (ntiles > 1) {
-      ATT_KDMA(1, BKV);
-      ATT_FETCH(BKV);
+      ATT_KDMA(1, jb + BKV);
+      ATT_FETCH(jb + BKV);
       ATT_STASH(1);
     }
-    if (ntiles > 2) ATT_FETCH(2 * BKV);
+    if (ntiles > 2) ATT_FETCH(jb + 2 * BKV);
   }
   __builtin_amdgcn_s_waitcnt(ATT_VMCNT(0));
   __syncthreads();
@@ -342,12 +348,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   ATT_QK(s_cur, Kl);
   int rd = 0;  // stage of tile t
   for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * BKV;
+    const int j0 = jb + t * BKV;
     const int rn = rd == 2 ? 0 : rd + 1;   // stage of tile t + 1
     const int rw = rd == 0 ? 2 : rd - 1;   // stage of tile t + 2 (held tile t - 1)
     if (t + 2 < ntiles) {
-      ATT_KDMA(rw, (t + 2) * BKV);
-      if constexpr (VD) ATT_VDMA(rw, (t + 2) * BKV);
+      ATT_KDMA(rw, jb + (t + 2) * BKV);
+      if constexpr (VD) ATT_VDMA(rw, jb + (t + 2) * BKV);
     }
     if (t <= tw) {
       // V^T fragments of tile t, read now so that they have landed by the
@@ -375,6 +381,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             const T *row = &vs[(d * 32 + l32) * VPITCH];
             vpre[u][d] = *reinterpret_cast<const typename MF::frag *>(row + u * 16 + g * 8);
           }
+      }
+      // keys before this query's sequence start (packed variable-length
+      // sequences only)
+      if constexpr (VARLEN) {
+        if (j0 < key_lo) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (j0 + (VD ? pk16(acc_row(r, lane)) : acc_row(r, lane)) < key_lo) s_cur[r] = -INFINITY;
+        }
       }
       // causal mask on the diagonal tile only; key j0 + acc_row(r) is masked
       // when acc_row(r) exceeds iq - j0
@@ -484,7 +499,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     } else {
       if (t + 2 < ntiles) {
         ATT_STASH(rw);
-        if (t + 3 < ntiles) ATT_FETCH((t + 3) * BKV);
+        if (t + 3 < ntiles) ATT_FETCH(jb + (t + 3) * BKV);
       }
       // this wave's key copies of tile t+2 have landed (only the V^T loads of
       // tile t+3, issued after them, may still be in flight); the barrier
@@ -504,7 +519,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // normalise and store o[b, i, h, d]
   const float l_tot = half_swap_sum(l_run);
-  const float inv = 1.0f / l_tot;
+  // invalid sequence offsets: every output is NaN
+  const float inv = (VARLEN && a.valid && *a.valid == 0) ? __builtin_nanf("") : 1.0f / l_tot;
   if (iq < S) {
     T *op = reinterpret_cast<T *>(a.o) + ((int64_t)b * S + iq) * (int64_t)H * DV + (int64_t)h * DV;
 #pragma unroll
@@ -534,16 +550,25 @@ constexpr int ATT_VD_WAVES = 4;
 
 template <typename T, int DN, int DR, int DV>
 hipError_t launch_t(const PrefillAttnArgs &a, hipStream_t st) {
+  const bool varlen = a.kv_start != nullptr;
   if constexpr (sizeof(T) == 2) {
     if (a.S % 8 == 0) {
       constexpr int NW = ATT_VD_WAVES;
       dim3 grid((a.S + 32 * NW - 1) / (32 * NW) * a.H * a.B);
-      hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, true, NW>), grid, dim3(64 * NW), 0, st, a);
+      if (varlen)
+        hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, true, NW, true>), grid, dim3(64 * NW), 0,
+                           st, a);
+      else
+        hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, true, NW, false>), grid, dim3(64 * NW), 0,
+                           st, a);
       return hipGetLastError();
     }
   }
   dim3 grid((a.S + 127) / 128 * a.H * a.B);
-  hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, false, 4>), grid, dim3(256), 0, st, a);
+  if (varlen)
+    hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, false, 4, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_attn_kernel<T, DN, DR, DV, false, 4, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -258,6 +258,51 @@ hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb,
   return hipGetLastError();
 }
 
+namespace {
+// Token t of a packed stream: the first token of its sequence (the largest b
+// with cu[b] <= t; cu is non-decreasing when valid) and its position in it.
+// The start is clamped into [0, t] so that every later access stays in range
+// even for invalid offsets.
+__global__ __launch_bounds__(256) void varlen_index_kernel(const int32_t *cu, int n_seq, int64_t T,
+                                                           int32_t *start, int32_t *pos) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int lo = 0, hi = n_seq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  int64_t s0 = cu[lo];
+  s0 = s0 < 0 ? 0 : (s0 > t ? t : s0);
+  start[t] = (int32_t)s0;
+  pos[t] = (int32_t)(t - s0);
+}
+
+// valid[0] = 1 when cu[0] = 0, cu is non-decreasing and cu[n_seq] = T, else 0
+// (one workgroup).
+__global__ __launch_bounds__(256) void varlen_check_kernel(const int32_t *cu, int n_seq, int64_t T,
+                                                           int32_t *valid) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = (cu[0] != 0 || (int64_t)cu[n_seq] != T) ? 1 : 0;
+  __syncthreads();
+  int mine = 0;
+  for (int b = threadIdx.x; b < n_seq; b += 256) mine |= cu[b] > cu[b + 1] ? 1 : 0;
+  if (mine) atomicOr(&bad, 1);
+  __syncthreads();
+  if (threadIdx.x == 0) valid[0] = bad ? 0 : 1;
+}
+}  // namespace
+
+hipError_t launch_varlen_index(const int32_t *cu_seqlens, int n_seq, int64_t total, int32_t *start,
+                               int32_t *pos, int32_t *valid, hipStream_t st) {
+  if (n_seq <= 0 || total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(varlen_check_kernel, dim3(1), dim3(256), 0, st, cu_seqlens, n_seq, total, valid);
+  hipLaunchKernelGGL(varlen_index_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     cu_seqlens, n_seq, total, start, pos);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src, int64_t lds,
                             int64_t rows, int width, hipStream_t st) {
   if (rows <= 0) return hipSuccess;

@@ -184,9 +184,10 @@ mla_status check_weights(const mla_weights *w) {
 struct PrefillPlan {
   int64_t ld_down;
   size_t off_down, off_q, off_kn, off_v, off_o, total;
+  size_t off_start, off_pos, off_valid;  // packed variable-length sequences only
 };
 
-PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S) {
+PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S, bool varlen = false) {
   const size_t es = dtype_size(c.dtype);
   const int64_t M = B * S, H = c.num_heads;
   PrefillPlan p;
@@ -202,6 +203,12 @@ PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S) {
   p.off_kn = take((size_t)M * H * c.qk_nope_head_dim * es);
   p.off_v = take((size_t)M * H * c.v_head_dim * es);
   p.off_o = take((size_t)M * H * c.v_head_dim * es);
+  p.off_start = p.off_pos = p.off_valid = 0;
+  if (varlen) {
+    p.off_start = take((size_t)M * sizeof(int32_t));
+    p.off_pos = take((size_t)M * sizeof(int32_t));
+    p.off_valid = take(sizeof(int32_t));
+  }
   p.total = off;
   return p;
 }
@@ -331,9 +338,12 @@ mla_status mla_prefill_layout_of(const mla_config *cfg, int64_t batch, int64_t s
   return MLA_OK;
 }
 
-mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, const void *x,
-                               int64_t batch, int64_t seq, void *y, void *latent_out,
-                               void *workspace, size_t workspace_bytes, void *hip_stream) {
+// The prefill of B equal-length sequences, or (cu_seqlens set) of n_seq
+// packed sequences of different lengths run as one stream of seq tokens.
+static mla_status prefill_common(const mla_config *cfg, const mla_weights *w, const void *x,
+                                 int64_t batch, int64_t seq, void *y, void *latent_out,
+                                 void *workspace, size_t workspace_bytes, void *hip_stream,
+                                 const int32_t *cu_seqlens, int64_t n_seq) {
   mla_status s = check_prefill_sizes(cfg, batch, seq);
   if (s != MLA_OK) return s;
   if ((s = check_weights(w)) != MLA_OK) return s;
@@ -343,7 +353,8 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
       (latent_out && !aligned16(latent_out)))
     return fail(MLA_ERR_INVALID_ARGUMENT, "x, y, latent_out and workspace must be 16-byte aligned");
   const mla_config &c = *cfg;
-  const PrefillPlan p = plan_prefill(c, batch, seq);
+  const bool varlen = cu_seqlens != nullptr;
+  const PrefillPlan p = plan_prefill(c, batch, seq, varlen);
   if (workspace_bytes < p.total)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
                 workspace_bytes, p.total);
@@ -361,9 +372,16 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
   const int dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim;
   const int dqk = dn + dr;
   const RopeTab tab = make_rope_tab(c.rope, dr);
+  // packed sequences: per token its sequence start and position
+  int32_t *vl_start = varlen ? reinterpret_cast<int32_t *>(ws + p.off_start) : nullptr;
+  int32_t *vl_pos = varlen ? reinterpret_cast<int32_t *>(ws + p.off_pos) : nullptr;
+  int32_t *vl_valid = varlen ? reinterpret_cast<int32_t *>(ws + p.off_valid) : nullptr;
 
   // 1. [c_q ‖ c_kv ‖ k_pe] = x [w_down_q; w_down_kv; w_kr]^T
   MLA_MARK(0);
+  if (varlen)
+    MLA_HIP(launch_varlen_index(cu_seqlens, (int)n_seq, M, vl_start, vl_pos, vl_valid, st),
+            "sequence offsets");
   {
     GemmDesc g;
     g.dtype = c.dtype;
@@ -387,7 +405,7 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
   // 3. RoPE of the shared key at positions 0..S-1
   MLA_MARK(2);
   MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, M, S, (int64_t)S * p.ld_down,
-                      p.ld_down, 1, 0, nullptr, tab, st),
+                      p.ld_down, 1, 0, vl_pos, tab, st),
           "rope k_pe");
   if (latent_out)
     MLA_HIP(launch_copy_rows(c.dtype, latent_out, rkv + dr, down + (size_t)rq * es, p.ld_down, M,
@@ -412,7 +430,7 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
   }
   MLA_MARK(4);
   MLA_HIP(launch_rope(c.dtype, q + (size_t)dn * es, M, S, (int64_t)H * S * dqk, dqk, H,
-                      (int64_t)S * dqk, nullptr, tab, st),
+                      (int64_t)S * dqk, vl_pos, tab, st),
           "rope q_pe");
   // 5. k_nope [B, H, S, d_n] and v channel-major [B, H, d_v, S] per head
   MLA_MARK(5);
@@ -445,6 +463,8 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
     a.S = S;
     a.H = H;
     a.scale = resolve_scale(c);
+    a.kv_start = vl_start;
+    a.valid = vl_valid;
     MLA_HIP(launch_prefill_attention(c.dtype, dn, dr, dv, a, st), "attention");
   }
   // 7. y = o wo^T
@@ -465,6 +485,42 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
   }
   MLA_MARK(8);
   return MLA_OK;
+}
+
+mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, const void *x,
+                               int64_t batch, int64_t seq, void *y, void *latent_out,
+                               void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return prefill_common(cfg, w, x, batch, seq, y, latent_out, workspace, workspace_bytes,
+                        hip_stream, nullptr, 0);
+}
+
+static mla_status check_varlen(const mla_config *cfg, int64_t n_seq, int64_t total) {
+  if (n_seq < 1 || n_seq > (1 << 24))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "n_seq must be in [1, 2^24]");
+  return check_prefill_sizes(cfg, 1, total);
+}
+
+mla_status mla_prefill_varlen_workspace_size(const mla_config *cfg, int64_t n_seq,
+                                             int64_t total_tokens, size_t *bytes) {
+  mla_status s = check_varlen(cfg, n_seq, total_tokens);
+  if (s != MLA_OK) return s;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = plan_prefill(*cfg, 1, total_tokens, true).total;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_varlen_forward(const mla_config *cfg, const mla_weights *w, const void *x,
+                                      const int32_t *cu_seqlens, int64_t n_seq,
+                                      int64_t total_tokens, void *y, void *latent_out,
+                                      void *workspace, size_t workspace_bytes,
+                                      void *hip_stream) {
+  mla_status s = check_varlen(cfg, n_seq, total_tokens);
+  if (s != MLA_OK) return s;
+  if (!cu_seqlens) return fail(MLA_ERR_INVALID_ARGUMENT, "cu_seqlens must not be NULL");
+  if (((uintptr_t)cu_seqlens & 3) != 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  return prefill_common(cfg, w, x, 1, total_tokens, y, latent_out, workspace, workspace_bytes,
+                        hip_stream, cu_seqlens, n_seq);
 }
 
 mla_status mla_decode_workspace_size(const mla_config *cfg, int64_t batch, int64_t cache_capacity,

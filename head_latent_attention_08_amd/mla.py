@@ -95,6 +95,10 @@ def load_library(path: str = LIB_PATH):
                                           ctypes.POINTER(PrefillLayout)]
     lib.mla_prefill_forward.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P, i64,
                                         i64, P, P, P, ctypes.c_size_t, P]
+    lib.mla_prefill_varlen_workspace_size.argtypes = [ctypes.POINTER(Config), i64, i64,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_prefill_varlen_forward.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P,
+                                               P, i64, i64, P, P, P, ctypes.c_size_t, P]
     lib.mla_decode_workspace_size.argtypes = [ctypes.POINTER(Config), i64, i64,
                                               ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_decode_layout_of.argtypes = [ctypes.POINTER(Config), i64, i64,
@@ -108,6 +112,7 @@ def load_library(path: str = LIB_PATH):
     lib.mla_rope_apply.argtypes = [P, ctypes.c_int32, i64, ctypes.c_int32, ctypes.c_int32, i64,
                                    i64, P, ctypes.POINTER(RopeParams), P]
     for fn in ("mla_prefill_workspace_size", "mla_prefill_layout_of", "mla_prefill_forward",
+               "mla_prefill_varlen_workspace_size", "mla_prefill_varlen_forward",
                "mla_decode_workspace_size", "mla_decode_layout_of", "mla_decode_absorbed",
                "mla_decode_multi_workspace_size", "mla_decode_absorbed_multi", "mla_rope_apply"):
         getattr(lib, fn).restype = st
@@ -265,6 +270,42 @@ def mla_prefill_forward(cfg: MlaConfig, weights: dict, x: torch.Tensor, y=None, 
     _check(load_library().mla_prefill_forward(
         ctypes.byref(c), ctypes.byref(w), _ptr(x), B, S, _ptr(y), _ptr(latent_out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y, latent_out, workspace
+
+
+def mla_prefill_varlen_workspace_size(cfg: MlaConfig, n_seq: int, total_tokens: int) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().mla_prefill_varlen_workspace_size(ctypes.byref(c), n_seq, total_tokens,
+                                                            ctypes.byref(n)))
+    return n.value
+
+
+def mla_prefill_varlen_forward(cfg: MlaConfig, weights: dict, x: torch.Tensor,
+                               cu_seqlens: torch.Tensor, y=None, latent_out=None, workspace=None,
+                               stream=None, want_latent: bool = False):
+    """Prefill of packed sequences: x [T, D], cu_seqlens int32 [n_seq + 1] on
+    the device.  Returns (y [T, D], latent_out [T, r_kv + d_r], workspace)."""
+    T, D = x.shape
+    n_seq = cu_seqlens.numel() - 1
+    dev = x.device
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if y is None:
+        y = torch.empty((T, D), dtype=cfg.torch_dtype, device=dev)
+    if latent_out is None and want_latent:
+        latent_out = torch.empty((T, cfg.kv_lora_rank + cfg.qk_rope_head_dim),
+                                 dtype=cfg.torch_dtype, device=dev)
+    need = mla_prefill_varlen_workspace_size(cfg, n_seq, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _device_check(x, cu_seqlens, y, latent_out, workspace)
+    w = make_weights(weights)
+    c = cfg.c()
+    _check(load_library().mla_prefill_varlen_forward(
+        ctypes.byref(c), ctypes.byref(w), _ptr(x), _ptr(cu_seqlens), n_seq, T, _ptr(y),
+        _ptr(latent_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return y, latent_out, workspace
 
 

@@ -144,6 +144,32 @@ MLA_API mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights 
                                void *y, void *latent_out, void *workspace,
                                size_t workspace_bytes, void *hip_stream);
 
+/* --------------------------------------------------- variable-length prefill
+ * A batch of n_seq sequences of different lengths packed end to end: the
+ * forward of each sequence on its own (the MLA section's causal mask within
+ * the sequence, RoPE positions 0..len_b-1), run as one stream of
+ * T = total_tokens rows so the projections see every token at once.
+ *   cu_seqlens [n_seq + 1]         int32, device, read: sequence b is rows
+ *              cu_seqlens[b] .. cu_seqlens[b+1]-1; a valid array starts at 0,
+ *              never decreases (empty sequences are allowed) and ends at T
+ *   x          [T, D]              device, read
+ *   y          [T, D]              device, written
+ *   latent_out [T, r_kv + d_r]     device, written if not NULL (as for
+ *              mla_prefill_forward)
+ * The offsets live in device memory, so the library checks them on the
+ * device: for an invalid array every row of y is NaN (latent_out is still
+ * written; rows use the clamped offsets).  The workspace holds the
+ * intermediates of a B = 1, S = T prefill plus two int32 per token.
+ * Status: as mla_prefill_forward, with T >= 1, 1 <= n_seq <= 2^24 and
+ * cu_seqlens not NULL and 4-byte aligned. */
+MLA_API mla_status mla_prefill_varlen_workspace_size(const mla_config *cfg, int64_t n_seq,
+                                             int64_t total_tokens, size_t *bytes);
+MLA_API mla_status mla_prefill_varlen_forward(const mla_config *cfg, const mla_weights *w,
+                                      const void *x, const int32_t *cu_seqlens,
+                                      int64_t n_seq, int64_t total_tokens, void *y,
+                                      void *latent_out, void *workspace,
+                                      size_t workspace_bytes, void *hip_stream);
+
 /* ------------------------------------------------------------------- decode
  * One absorbed decode step (the cache formula of the MLA section, with
  * w_up_k folded into the query side and w_up_v into the output side, per

@@ -23,6 +23,7 @@ from .mla_oracle import (  # noqa: F401
     softmax_scale,
     causal_attention,
     mla_prefill,
+    mla_prefill_varlen,
     mla_prefill_rows,
     mla_decode_expanded,
     mla_decode_absorbed,

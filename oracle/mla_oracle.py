@@ -275,6 +275,30 @@ def mla_prefill(cfg: Cfg, w: dict, x, want_intermediates: bool = False):
                    k_pe=k_pe, k_nope=k_nope, v=v, o=o)
 
 
+def mla_prefill_varlen(cfg: Cfg, w: dict, x, cu_seqlens):
+    """Prefill of sequences of different lengths packed end to end: x [T, D],
+    sequence b at rows cu_seqlens[b] .. cu_seqlens[b+1]-1.  Each sequence is a
+    prefill of its own (positions from 0, causal mask within the sequence:
+    the MLA section's forward applied per sequence).
+
+    Returns y [T, D] and the latent rows [T, r_kv + d_r] (c_kv, then the
+    post-RoPE k_pe)."""
+    x = _f64(x)
+    cu = [int(v) for v in cu_seqlens]
+    T, D = x.shape
+    width = cfg.kv_lora_rank + cfg.qk_rope_head_dim
+    y = np.empty((T, D))
+    lat = np.empty((T, width))
+    for b in range(len(cu) - 1):
+        a, e = cu[b], cu[b + 1]
+        if e == a:
+            continue
+        yb, inter = mla_prefill(cfg, w, x[None, a:e], want_intermediates=True)
+        y[a:e] = yb[0]
+        lat[a:e] = np.concatenate([inter["c_kv"][0], inter["k_pe"][0]], axis=-1)
+    return y, lat
+
+
 def mla_prefill_rows(cfg: Cfg, w: dict, x, rows, batch: int = 0):
     """y[batch, r] for the query rows ``rows`` of a prefill of x [B, S, D].
 

@@ -114,6 +114,32 @@ def test_bad_sizes_rejected():
     assert m.mla_decode_multi_workspace_size(cfg, 32, 2, 8193) > m.mla_decode_workspace_size(cfg, 32, 8193)
 
 
+def test_varlen_sizes_and_arguments_rejected_without_launch():
+    cfg = m.MlaConfig(**V3)
+    # the packed prefill needs the B = 1, S = T intermediates plus two int32 per token
+    n = m.mla_prefill_varlen_workspace_size(cfg, 3, 4096)
+    assert n >= m.mla_prefill_workspace_size(cfg, 1, 4096) + 2 * 4096 * 4
+    for n_seq, T in [(0, 16), (-1, 16), (2, 0), (1 << 25, 16)]:
+        with pytest.raises(m.MlaError) as e:
+            m.mla_prefill_varlen_workspace_size(cfg, n_seq, T)
+        assert e.value.status == b.MLA_ERR_INVALID_ARGUMENT
+    lib = m.load_library()
+    c = cfg.c()
+    good = ctypes.c_void_p(0x10000)
+    w = b.Weights(*([0x10000] * 9))
+    need = m.mla_prefill_varlen_workspace_size(cfg, 2, 16)
+    st = lib.mla_prefill_varlen_forward(ctypes.byref(c), ctypes.byref(w), good, None, 2, 16, good,
+                                        None, good, need, None)
+    assert st == b.MLA_ERR_INVALID_ARGUMENT and b"cu_seqlens" in lib.mla_last_error()
+    st = lib.mla_prefill_varlen_forward(ctypes.byref(c), ctypes.byref(w), good,
+                                        ctypes.c_void_p(0x10002), 2, 16, good, None, good, need,
+                                        None)
+    assert st == b.MLA_ERR_INVALID_ARGUMENT and b"aligned" in lib.mla_last_error()
+    st = lib.mla_prefill_varlen_forward(ctypes.byref(c), ctypes.byref(w), good, good, 2, 16, good,
+                                        None, good, need - 1, None)
+    assert st == b.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
 def _raw_prefill(lib, cfg, w, x, y, ws, nbytes):
     c = cfg.c()
     return lib.mla_prefill_forward(ctypes.byref(c), ctypes.byref(w) if w is not None else None,

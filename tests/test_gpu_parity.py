@@ -152,6 +152,66 @@ def test_prefill_small_bf16(conv):
                       "latent")
 
 
+# ------------------------------------------------------- packed sequences ---
+
+def _run_varlen(c, conv, lens=None, cu=None, T=None):
+    m = _m()
+    cu_h = (np.concatenate([[0], np.cumsum(lens)]) if cu is None else np.asarray(cu)).astype(np.int32)
+    T = int(cu_h[-1]) if T is None else T
+    x, w = si.make_inputs(c, seq=T, batch=1, gains="random")
+    cfg = mla_cfg(c, rope=conv)
+    n_seq = len(cu_h) - 1
+    print(f"varlen {c['dtype']} T={T} cu={cu_h.tolist()[:8]}", flush=True)
+    ws = _poisoned(m.mla_prefill_varlen_workspace_size(cfg, n_seq, T))
+    y, lat, ws = m.mla_prefill_varlen_forward(cfg, weights_to_dev(w, c["dtype"]),
+                                              to_dev(x[0], c["dtype"]),
+                                              torch.from_numpy(cu_h).cuda(), workspace=ws,
+                                              want_latent=True)
+    torch.cuda.synchronize()
+    return m, cfg, x[0], w, cu_h, y, lat
+
+
+@pytest.mark.parametrize("name,conv,lens", [
+    # T = 531: large-tile projections, query tiles spanning sequence ends
+    ("small", "interleaved", [1, 37, 300, 64, 129]),
+    # T = 512: the bf16 copy path of the attention, an empty sequence
+    ("small", "half_split", [100, 0, 156, 256]),
+    # fp32, generic projections
+    ("tiny", "half_split", [5, 3, 8]),
+])
+def test_prefill_varlen_matches_oracle(name, conv, lens):
+    c = si.CONFIGS[name]
+    m, cfg, x, w, cu, y, lat = _run_varlen(c, conv, lens)
+    ref, ref_lat = orc.mla_prefill_varlen(oracle_cfg(c, rope=conv), w, x, cu)
+    assert_close_rows(to_np(y), ref, c["dtype"], "y")
+    assert_close_rows(to_np(lat), ref_lat, c["dtype"], "latent")
+
+
+def test_prefill_varlen_equal_lengths_match_batched():
+    # two packed sequences of 256 tokens against the batched prefill of the
+    # same tokens: the latent rows (same projection rows and RoPE positions)
+    # are bit-identical, the outputs agree to rounding
+    c = si.CONFIGS["small"]
+    m = _m()
+    x, w = si.make_inputs(c, seq=256, batch=2, gains="random")
+    cfg = mla_cfg(c, rope="interleaved")
+    wd = weights_to_dev(w, "bf16")
+    yb, lb, _ = m.mla_prefill_forward(cfg, wd, to_dev(x, "bf16"), want_latent=True)
+    cu = torch.tensor([0, 256, 512], dtype=torch.int32, device="cuda")
+    yv, lv, _ = m.mla_prefill_varlen_forward(cfg, wd, to_dev(x.reshape(512, -1), "bf16"), cu,
+                                             want_latent=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lv, lb.reshape(512, -1))
+    assert_close_rows(to_np(yv), to_np(yb.reshape(512, -1)), "bf16", "y")
+
+
+@pytest.mark.parametrize("cu", [[0, 10, 5, 20], [0, 10, 18], [1, 10, 20]])
+def test_prefill_varlen_invalid_offsets_give_nan(cu):
+    # decreasing, not ending at T, not starting at 0: every output row is NaN
+    m, cfg, x, w, cu_h, y, lat = _run_varlen(si.CONFIGS["small"], "interleaved", cu=cu, T=20)
+    assert torch.isnan(y.float()).all()
+
+
 @pytest.mark.parametrize("S,B", [(1, 1), (7, 2), (100, 1), (129, 3), (300, 1), (300, 2), (515, 1)])
 def test_prefill_ragged_lengths(S, B):
     # sequence lengths that leave partial query/key tiles, and a single token;

@@ -42,6 +42,27 @@ def test_v3_prefill_sampled_rows():
     assert_close_rows(to_np(lat[0]), ref_lat, "bf16", "latent rows")
 
 
+def test_v3_prefill_varlen_sampled_rows():
+    # three V3 sequences packed into 4096 tokens; sampled rows of each against
+    # the oracle's prefill of that sequence alone
+    m = _m()
+    c = si.CONFIGS["v3_prefill"]
+    x, w = si.make_inputs(c)
+    lens = [1000, 2500, 596]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    print(f"v3 varlen: lens {lens}, seed 3000", flush=True)
+    cfg = mla_cfg(c, rope="interleaved")
+    y, lat, _ = m.mla_prefill_varlen_forward(cfg, weights_to_dev(w, "bf16"), to_dev(x[0], "bf16"),
+                                             torch.from_numpy(cu).cuda(), want_latent=True)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        a = int(cu[b])
+        rows = np.unique(np.array([0, 1, 31, 32, L // 2, L - 1]))
+        ref, ref_lat = orc.mla_prefill_rows(oracle_cfg(c), w, x[:, a:a + L], rows)
+        assert_close_rows(to_np(y[a + rows]), ref, "bf16", f"seq {b} y rows")
+        assert_close_rows(to_np(lat[a:a + L]), ref_lat, "bf16", f"seq {b} latent")
+
+
 def test_v3_prefill_half_split_spot_check():
     c = si.CONFIGS["v3_prefill"]
     x, w = si.make_inputs(c, seq=1024)

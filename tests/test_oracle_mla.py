@@ -90,6 +90,41 @@ def test_prefill_matches_brute_force(conv):
                                rtol=1e-10, atol=1e-13)
 
 
+@pytest.mark.parametrize("conv", ["half_split", "interleaved"])
+def test_varlen_prefill_is_per_sequence_brute_force(conv):
+    # packed sequences of lengths 3, 0, 5, 1: each block of rows is the
+    # brute-force forward of that sequence alone (positions from 0)
+    cfg, x, w = _tiny_inputs(conv, S=9, B=1)
+    lens = [3, 0, 5, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    y, lat = orc.mla_prefill_varlen(cfg, w, x[0], cu)
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        a = cu[b]
+        ref = _brute_force_prefill(cfg, w, x[:, a:a + L])[0]
+        np.testing.assert_allclose(y[a:a + L], ref, rtol=1e-10, atol=1e-13)
+    # latent rows: c_kv then the post-RoPE k_pe of each token at its own position
+    _, inter = orc.mla_prefill(cfg, w, x[:, 3:8], want_intermediates=True)
+    np.testing.assert_allclose(lat[3:8], np.concatenate([inter["c_kv"][0], inter["k_pe"][0]], -1),
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_varlen_prefill_order_and_independence():
+    # reordering the sequences reorders the output blocks; changing one
+    # sequence's tokens leaves every other sequence's rows unchanged
+    cfg, x, w = _tiny_inputs("interleaved", S=12, B=1)
+    x = x[0]
+    y, _ = orc.mla_prefill_varlen(cfg, w, x, [0, 5, 12])
+    y_sw, _ = orc.mla_prefill_varlen(cfg, w, np.concatenate([x[5:], x[:5]]), [0, 7, 12])
+    np.testing.assert_allclose(y_sw[:7], y[5:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(y_sw[7:], y[:5], rtol=1e-12, atol=1e-14)
+    x2 = x.copy()
+    x2[6] += 1.0
+    y2, _ = orc.mla_prefill_varlen(cfg, w, x2, [0, 5, 12])
+    assert np.array_equal(y2[:5], y[:5]) and not np.allclose(y2[5:], y[5:])
+
+
 def _torch_library_prefill(cfg, w, x):
     """The same forward built from PyTorch float64 library routines: linear,
     rms_norm, complex multiplication for RoPE, causal SDPA."""
