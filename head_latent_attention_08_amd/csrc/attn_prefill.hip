@@ -115,6 +115,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
   const int g = lane >> 5, l32 = lane & 31;
   const int S = a.S, H = a.H;
+  // keys: the queries' own tokens, or (key ranges) a key stream of its own
+  const int SK = VARLEN ? a.Sk : S;
   const int nq = (S + BQ - 1) / BQ;
   const int P = a.B * H;
   const int w = blockIdx.x;
@@ -134,9 +136,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int64_t bh = (int64_t)b * H + h;
   const T *qp = reinterpret_cast<const T *>(a.q) + bh * S * DQK;
-  const T *kn = reinterpret_cast<const T *>(a.k_nope) + bh * S * DN;
-  const T *kpe = reinterpret_cast<const T *>(a.k_pe) + (int64_t)b * S * a.ld_kpe;
-  const T *vt = reinterpret_cast<const T *>(a.vt) + bh * DV * S;
+  const T *kn = reinterpret_cast<const T *>(a.k_nope) + bh * SK * DN;
+  const T *kpe = reinterpret_cast<const T *>(a.k_pe) + (int64_t)b * SK * a.ld_kpe;
+  const T *vt = reinterpret_cast<const T *>(a.vt) + bh * DV * SK;
 
   if constexpr (DVP > DV && !VD) {
     for (int i = tid; i < (DVP - DV) * VPITCH; i += 256) {
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #define ATT_KDMA(STG, J0)                                                               \
   do {                                                                                  \
     const int j0_ = (J0);                                                               \
-    const int lim_ = S - 1 - j0_;                                                       \
+    const int lim_ = SK - 1 - j0_;                                                      \
     const T *bn_ = kn + (int64_t)j0_ * DN;                                              \
     const T *bp_ = kpe + (int64_t)j0_ * a.ld_kpe;                                       \
     _Pragma("unroll") for (int k = 0; k < NKPW; ++k) {                                  \
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // 16-byte reads of 16 consecutive rows).  Rows past DV repeat row 0 (their
   // output channels are never stored); chunks past the sequence repeat the
   // last one (masked keys).
-  const T *vt_bh = reinterpret_cast<const T *>(a.vt) + bh * DV * S;
+  const T *vt_bh = reinterpret_cast<const T *>(a.vt) + bh * DV * SK;
   int vrow[NVPW], vch[NVPW];
 #pragma unroll
   for (int k = 0; k < NVPW; ++k) {
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     _Pragma("unroll") for (int k = 0; k < NVPW; ++k) {                                  \
       const int vb = wave + NW * k;                                                     \
       if (vb < NVB) {                                                                   \
-        const uint32_t off_ = (uint32_t)((vrow[k] * S + min(j0_ + 8 * vch[k], S - 8)) * ES); \
+        const uint32_t off_ = (uint32_t)((vrow[k] * SK + min(j0_ + 8 * vch[k], SK - 8)) * ES); \
         const uint32_t m0_ = lds_v + (STG) * (NVB * 1024) + vb * 1024;                  \
         asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"               \
                      :: "v"(off_), "s"(vt_bh), "s"(m0_) : "memory", "m0");              \
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // register staging of one V^T tile (plain code, not lambdas: the staging
   // registers must not end up in scratch memory)
   uint4 rv[VCH];
-  const bool v_whole = __builtin_amdgcn_readfirstlane(S % VEC == 0 && S >= VEC);
+  const bool v_whole = __builtin_amdgcn_readfirstlane(SK % VEC == 0 && SK >= VEC);
 #define ATT_FETCH(J0)                                                               \
   do {                                                                              \
     const int j0_ = (J0);                                                           \
@@ -254,12 +256,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (v_whole) {                                                                \
         /* S is a multiple of VEC: a chunk is wholly inside or wholly past */       \
         /* the end; past-the-end chunks repeat the last one (masked keys) */        \
-        v = ld16(vt + (int64_t)d * S + min(j, S - VEC));                            \
+        v = ld16(vt + (int64_t)d * SK + min(j, SK - VEC));                          \
       } else {                                                                      \
-        const T *src = vt + (int64_t)d * S + j;                                     \
+        const T *src = vt + (int64_t)d * SK + j;                                    \
         T e[VEC];                                                                   \
         _Pragma("unroll") for (int k = 0; k < VEC; ++k)                             \
-            e[k] = (j + k < S) ? src[k] : from_f32<T>(0.f);                         \
+            e[k] = (j + k < SK) ? src[k] : from_f32<T>(0.f);                        \
         v = *reinterpret_cast<const uint4 *>(e);                                    \
       }                                                                             \
       rv[i] = v;                                                                    \
@@ -292,15 +294,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * LOG2E;
 
-  const int kv_end = min(S, q0 + BQ);
-  // Key tiles t = 0.. start at key jb: 0, or for packed variable-length
-  // sequences the tile of the first query's sequence start (starts never
-  // decrease along the token stream, so no query of the block needs keys
-  // before it); a lane masks the keys before its own sequence's start.
-  const int key_lo = VARLEN ? a.kv_start[min(iq, S - 1)] : 0;
-  const int jb = VARLEN ? a.kv_start[q0] / BKV * BKV : 0;
+  // Key tiles t = 0.. start at key jb.  Causal: keys 0..iq, jb = 0.  Key
+  // ranges: query iq takes keys kv_lo[iq] .. kv_hi[iq], both non-decreasing
+  // along the queries, so the block needs the tiles from its first query's
+  // kv_lo to its last query's kv_hi; a lane masks the keys outside its own
+  // range.
+  const int iqc = min(iq, S - 1);
+  const int key_lo = VARLEN ? a.kv_lo[iqc] : 0;
+  const int key_hi = VARLEN ? a.kv_hi[iqc] : iq;
+  const int jb = VARLEN ? a.kv_lo[q0] / BKV * BKV : 0;
+  const int kv_end = VARLEN ? a.kv_hi[min(S, q0 + BQ) - 1] + 1 : min(S, q0 + BQ);
   const int ntiles = (kv_end + BKV - 1) / BKV - jb / BKV;
-  const int tw = qw0 / BKV - jb / BKV;  // this wave's diagonal tile, the last one it needs
+  // this wave's last tile (a wave with no query left needs none)
+  const int tw = VARLEN ? (qw0 < S ? a.kv_hi[min(qw0 + 31, S - 1)] / BKV - jb / BKV : -1)
+                        : qw0 / BKV - jb / BKV;
 
   // fragment f of this lane's key row in the K stage starting at byte KB:
   // k_nope region for f < NQN, k_pe region after it
@@ -382,18 +389,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             vpre[u][d] = *reinterpret_cast<const typename MF::frag *>(row + u * 16 + g * 8);
           }
       }
-      // keys before this query's sequence start (packed variable-length
-      // sequences only)
       if constexpr (VARLEN) {
-        if (j0 < key_lo) {
+        // keys outside this query's range
+        if (j0 < key_lo || j0 + BKV - 1 > key_hi) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (j0 + (VD ? pk16(acc_row(r, lane)) : acc_row(r, lane)) < key_lo) s_cur[r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int kj = j0 + (VD ? pk16(acc_row(r, lane)) : acc_row(r, lane));
+            if (kj < key_lo || kj > key_hi) s_cur[r] = -INFINITY;
+          }
         }
-      }
-      // causal mask on the diagonal tile only; key j0 + acc_row(r) is masked
-      // when acc_row(r) exceeds iq - j0
-      if (t == tw) {
+      } else if (t == tw) {
+        // causal mask on the diagonal tile only; key j0 + acc_row(r) is
+        // masked when acc_row(r) exceeds iq - j0
         if constexpr (VD) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
@@ -520,7 +527,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // normalise and store o[b, i, h, d]
   const float l_tot = half_swap_sum(l_run);
   // invalid sequence offsets: every output is NaN
-  const float inv = (VARLEN && a.valid && *a.valid == 0) ? __builtin_nanf("") : 1.0f / l_tot;
+  const float inv = (VARLEN && a.valid && a.valid[iqc] == 0) ? __builtin_nanf("") : 1.0f / l_tot;
   if (iq < S) {
     T *op = reinterpret_cast<T *>(a.o) + ((int64_t)b * S + iq) * (int64_t)H * DV + (int64_t)h * DV;
 #pragma unroll
@@ -550,9 +557,10 @@ constexpr int ATT_VD_WAVES = 4;
 
 template <typename T, int DN, int DR, int DV>
 hipError_t launch_t(const PrefillAttnArgs &a, hipStream_t st) {
-  const bool varlen = a.kv_start != nullptr;
+  const bool varlen = a.kv_lo != nullptr;
+  const int sk = varlen ? a.Sk : a.S;
   if constexpr (sizeof(T) == 2) {
-    if (a.S % 8 == 0) {
+    if (sk % 8 == 0) {
       constexpr int NW = ATT_VD_WAVES;
       dim3 grid((a.S + 32 * NW - 1) / (32 * NW) * a.H * a.B);
       if (varlen)

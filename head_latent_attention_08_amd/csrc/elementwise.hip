@@ -260,11 +260,14 @@ hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb,
 
 namespace {
 // Token t of a packed stream: the first token of its sequence (the largest b
-// with cu[b] <= t; cu is non-decreasing when valid) and its position in it.
-// The start is clamped into [0, t] so that every later access stays in range
-// even for invalid offsets.
+// with cu[b] <= t; cu is non-decreasing when valid), which is the first key
+// t attends (the last is t itself), and its position in the sequence.  The
+// start is clamped into [0, t] so that every later access stays in range
+// even for invalid offsets; valid[t] copies the check's verdict.
 __global__ __launch_bounds__(256) void varlen_index_kernel(const int32_t *cu, int n_seq, int64_t T,
-                                                           int32_t *start, int32_t *pos) {
+                                                           int32_t *start, int32_t *last,
+                                                           int32_t *pos, int32_t *valid,
+                                                           const int32_t *ok) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
   int lo = 0, hi = n_seq - 1;
@@ -276,7 +279,9 @@ __global__ __launch_bounds__(256) void varlen_index_kernel(const int32_t *cu, in
   int64_t s0 = cu[lo];
   s0 = s0 < 0 ? 0 : (s0 > t ? t : s0);
   start[t] = (int32_t)s0;
+  last[t] = (int32_t)t;
   pos[t] = (int32_t)(t - s0);
+  valid[t] = ok[0];
 }
 
 // valid[0] = 1 when cu[0] = 0, cu is non-decreasing and cu[n_seq] = T, else 0
@@ -295,11 +300,12 @@ __global__ __launch_bounds__(256) void varlen_check_kernel(const int32_t *cu, in
 }  // namespace
 
 hipError_t launch_varlen_index(const int32_t *cu_seqlens, int n_seq, int64_t total, int32_t *start,
-                               int32_t *pos, int32_t *valid, hipStream_t st) {
+                               int32_t *last, int32_t *pos, int32_t *valid, int32_t *ok,
+                               hipStream_t st) {
   if (n_seq <= 0 || total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(varlen_check_kernel, dim3(1), dim3(256), 0, st, cu_seqlens, n_seq, total, valid);
+  hipLaunchKernelGGL(varlen_check_kernel, dim3(1), dim3(256), 0, st, cu_seqlens, n_seq, total, ok);
   hipLaunchKernelGGL(varlen_index_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     cu_seqlens, n_seq, total, start, pos);
+                     cu_seqlens, n_seq, total, start, last, pos, valid, ok);
   return hipGetLastError();
 }
 

@@ -75,10 +75,12 @@ hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb,
 // Copy `width` contiguous elements per row: dst row t at dst + t * ldd from
 // src + t * lds (prefill latent output).
 // Packed variable-length sequences (cu_seqlens [n_seq + 1], device): per
-// token its sequence's first token (start) and its position; valid[0] = 1
-// for well-formed offsets (cu[0] = 0, non-decreasing, cu[n_seq] = total).
+// token t its key range start[t] .. last[t] = t (its sequence's first token
+// to itself), its position, and valid[t] = ok[0] = 1 for well-formed offsets
+// (cu[0] = 0, non-decreasing, cu[n_seq] = total), else 0.
 hipError_t launch_varlen_index(const int32_t *cu_seqlens, int n_seq, int64_t total, int32_t *start,
-                               int32_t *pos, int32_t *valid, hipStream_t st);
+                               int32_t *last, int32_t *pos, int32_t *valid, int32_t *ok,
+                               hipStream_t st);
 
 hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src,
                             int64_t lds, int64_t rows, int width,
@@ -107,11 +109,14 @@ struct PrefillAttnArgs {
   void *o;            // [B * S, H * dv]
   int B, S, H;
   float scale;
-  // Variable-length batches (B = 1, S = all tokens of the packed sequences):
-  // kv_start[t] is the first token of t's sequence, which t's keys start at
-  // (non-decreasing in t); valid, when set and 0, makes every output NaN.
-  const int32_t *kv_start = nullptr;
+  // Key ranges (B = 1; packed sequences, chunks against a cache): query t
+  // takes keys kv_lo[t] .. kv_hi[t] (inclusive, both non-decreasing in t) of
+  // a key stream of Sk tokens (k_nope, k_pe and vt hold Sk keys instead of S);
+  // valid[t] == 0 makes query t's output NaN.  kv_lo NULL: causal over S.
+  const int32_t *kv_lo = nullptr;
+  const int32_t *kv_hi = nullptr;
   const int32_t *valid = nullptr;
+  int Sk = 0;
 };
 
 hipError_t launch_prefill_attention(int dtype, int dn, int dr, int dv,

@@ -184,7 +184,7 @@ mla_status check_weights(const mla_weights *w) {
 struct PrefillPlan {
   int64_t ld_down;
   size_t off_down, off_q, off_kn, off_v, off_o, total;
-  size_t off_start, off_pos, off_valid;  // packed variable-length sequences only
+  size_t off_start, off_last, off_pos, off_valid, off_ok;  // key-range prefills only
 };
 
 PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S, bool varlen = false) {
@@ -203,11 +203,13 @@ PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S, bool varlen 
   p.off_kn = take((size_t)M * H * c.qk_nope_head_dim * es);
   p.off_v = take((size_t)M * H * c.v_head_dim * es);
   p.off_o = take((size_t)M * H * c.v_head_dim * es);
-  p.off_start = p.off_pos = p.off_valid = 0;
+  p.off_start = p.off_last = p.off_pos = p.off_valid = p.off_ok = 0;
   if (varlen) {
     p.off_start = take((size_t)M * sizeof(int32_t));
+    p.off_last = take((size_t)M * sizeof(int32_t));
     p.off_pos = take((size_t)M * sizeof(int32_t));
-    p.off_valid = take(sizeof(int32_t));
+    p.off_valid = take((size_t)M * sizeof(int32_t));
+    p.off_ok = take(sizeof(int32_t));
   }
   p.total = off;
   return p;
@@ -374,13 +376,16 @@ static mla_status prefill_common(const mla_config *cfg, const mla_weights *w, co
   const RopeTab tab = make_rope_tab(c.rope, dr);
   // packed sequences: per token its sequence start and position
   int32_t *vl_start = varlen ? reinterpret_cast<int32_t *>(ws + p.off_start) : nullptr;
+  int32_t *vl_last = varlen ? reinterpret_cast<int32_t *>(ws + p.off_last) : nullptr;
   int32_t *vl_pos = varlen ? reinterpret_cast<int32_t *>(ws + p.off_pos) : nullptr;
   int32_t *vl_valid = varlen ? reinterpret_cast<int32_t *>(ws + p.off_valid) : nullptr;
+  int32_t *vl_ok = varlen ? reinterpret_cast<int32_t *>(ws + p.off_ok) : nullptr;
 
   // 1. [c_q ‖ c_kv ‖ k_pe] = x [w_down_q; w_down_kv; w_kr]^T
   MLA_MARK(0);
   if (varlen)
-    MLA_HIP(launch_varlen_index(cu_seqlens, (int)n_seq, M, vl_start, vl_pos, vl_valid, st),
+    MLA_HIP(launch_varlen_index(cu_seqlens, (int)n_seq, M, vl_start, vl_last, vl_pos, vl_valid,
+                                vl_ok, st),
             "sequence offsets");
   {
     GemmDesc g;
@@ -463,8 +468,10 @@ static mla_status prefill_common(const mla_config *cfg, const mla_weights *w, co
     a.S = S;
     a.H = H;
     a.scale = resolve_scale(c);
-    a.kv_start = vl_start;
+    a.kv_lo = vl_start;
+    a.kv_hi = vl_last;
     a.valid = vl_valid;
+    a.Sk = S;
     MLA_HIP(launch_prefill_attention(c.dtype, dn, dr, dv, a, st), "attention");
   }
   // 7. y = o wo^T
