@@ -18,6 +18,8 @@ from .mla import (  # noqa: F401
     mla_decode_multi_workspace_size,
     mla_decode_layout_of,
     mla_decode_workspace_size,
+    mla_prefill_chunk,
+    mla_prefill_chunk_workspace_size,
     mla_prefill_forward,
     mla_prefill_layout_of,
     mla_prefill_varlen_forward,

@@ -309,6 +309,105 @@ hipError_t launch_varlen_index(const int32_t *cu_seqlens, int n_seq, int64_t tot
   return hipGetLastError();
 }
 
+namespace {
+// Chunk of q_len tokens per sequence against a latent cache, key stream side
+// (one workgroup): sequence b is usable when 0 <= L_b and L_b + q_len <= cap;
+// its keys are its L_b + q_len cache rows, packed at kofs[b] (kofs[B] = all
+// keys).  When the keys do not fit max_keys no sequence is usable.
+// lens_eff[b] = L_b for a usable sequence, else -1 (no keys, no cache write).
+__global__ __launch_bounds__(256) void chunk_scan_kernel(const int32_t *lens, int B, int q_len,
+                                                         int64_t cap, int64_t max_keys,
+                                                         int32_t *lens_eff, int32_t *kofs) {
+  __shared__ int64_t part[256];
+  const int per = (B + 255) / 256, b0 = threadIdx.x * per;
+  int64_t sum = 0;
+  for (int b = b0; b < min(B, b0 + per); ++b) {
+    const int64_t L = lens[b];
+    if (L >= 0 && L + q_len <= cap) sum += L + q_len;
+  }
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  // inclusive scan of the 256 partial sums (Hillis-Steele)
+  for (int d = 1; d < 256; d *= 2) {
+    const int64_t v = threadIdx.x >= d ? part[threadIdx.x - d] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  const bool fits = part[255] <= max_keys;
+  int64_t run = threadIdx.x > 0 ? part[threadIdx.x - 1] : 0;
+  for (int b = b0; b < min(B, b0 + per); ++b) {
+    const int64_t L = lens[b];
+    const bool ok = fits && L >= 0 && L + q_len <= cap;
+    kofs[b] = (int32_t)(fits ? run : 0);
+    lens_eff[b] = ok ? (int32_t)L : -1;
+    if (ok) run += L + q_len;
+  }
+  if (threadIdx.x == 255) kofs[B] = (int32_t)(fits ? part[255] : 0);
+}
+
+// Query b * q_len + t: keys kofs[b] .. kofs[b] + L_b + t of the stream (an
+// empty range for an unusable sequence), position L_b + t, validity.
+__global__ __launch_bounds__(256) void chunk_ranges_kernel(const int32_t *lens_eff, const int32_t *kofs,
+                                                           int n, int q_len, int32_t *lo, int32_t *hi,
+                                                           int32_t *pos, int32_t *valid) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int b = i / q_len, t = i - b * q_len;
+  const int L = lens_eff[b];
+  lo[i] = kofs[b];
+  hi[i] = L >= 0 ? kofs[b] + L + t : kofs[b] - 1;
+  pos[i] = L >= 0 ? L + t : t;
+  valid[i] = L >= 0 ? 1 : 0;
+}
+
+// Key stream row k: row k - kofs[b] of sequence b's cache (the sequence
+// whose packed range holds k), or zeros past the last key.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_keys_kernel(T *dst, int64_t n_rows, const T *cache,
+                                                          int64_t cap, int width, const int32_t *kofs,
+                                                          int B) {
+  const int64_t k = blockIdx.x;
+  if (k >= n_rows) return;
+  T *out = dst + k * width;
+  if (k >= kofs[B]) {
+    for (int c = threadIdx.x; c < width; c += blockDim.x) out[c] = from_f32<T>(0.f);
+    return;
+  }
+  int lo = 0, hi = B - 1;  // the last b with kofs[b] <= k
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (kofs[mid] <= k) lo = mid;
+    else hi = mid - 1;
+  }
+  const T *src = cache + ((int64_t)lo * cap + (k - kofs[lo])) * width;
+  for (int c = threadIdx.x; c < width; c += blockDim.x) out[c] = src[c];
+}
+}  // namespace
+
+hipError_t launch_chunk_index(const int32_t *lens, int B, int q_len, int64_t cap, int64_t max_keys,
+                              int32_t *lens_eff, int32_t *kofs, int32_t *lo, int32_t *hi, int32_t *pos,
+                              int32_t *valid, hipStream_t st) {
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(256), 0, st, lens, B, q_len, cap, max_keys, lens_eff,
+                     kofs);
+  const int n = B * q_len;
+  hipLaunchKernelGGL(chunk_ranges_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, lens_eff, kofs,
+                     n, q_len, lo, hi, pos, valid);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_keys(int dtype, void *dst, int64_t n_rows, const void *cache, int64_t cap,
+                              int width, const int32_t *kofs, int B, hipStream_t st) {
+  if (n_rows <= 0) return hipSuccess;
+  if (dtype == BF16)
+    hipLaunchKernelGGL(gather_keys_kernel<bf16>, dim3((unsigned)n_rows), dim3(256), 0, st, (bf16 *)dst, n_rows,
+                       (const bf16 *)cache, cap, width, kofs, B);
+  else
+    hipLaunchKernelGGL(gather_keys_kernel<float>, dim3((unsigned)n_rows), dim3(256), 0, st, (float *)dst,
+                       n_rows, (const float *)cache, cap, width, kofs, B);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src, int64_t lds,
                             int64_t rows, int width, hipStream_t st) {
   if (rows <= 0) return hipSuccess;

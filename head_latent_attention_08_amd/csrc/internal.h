@@ -82,6 +82,19 @@ hipError_t launch_varlen_index(const int32_t *cu_seqlens, int n_seq, int64_t tot
                                int32_t *last, int32_t *pos, int32_t *valid, int32_t *ok,
                                hipStream_t st);
 
+// A chunk of q_len tokens per sequence against a latent cache (lens [B],
+// device): lens_eff[b] = L_b when 0 <= L_b, L_b + q_len <= cap and all keys
+// fit max_keys, else -1; kofs [B + 1] packed key offsets (sequence b's
+// L_b + q_len keys start at kofs[b]); per query b * q_len + t its key range
+// lo .. hi, position L_b + t and validity.
+hipError_t launch_chunk_index(const int32_t *lens, int B, int q_len, int64_t cap, int64_t max_keys,
+                              int32_t *lens_eff, int32_t *kofs, int32_t *lo, int32_t *hi, int32_t *pos,
+                              int32_t *valid, hipStream_t st);
+// Packed key stream of n_rows rows of width elements: row k is cache row
+// k - kofs[b] of the sequence b that holds k, zeros from kofs[B] on.
+hipError_t launch_gather_keys(int dtype, void *dst, int64_t n_rows, const void *cache, int64_t cap,
+                              int width, const int32_t *kofs, int B, hipStream_t st);
+
 hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src,
                             int64_t lds, int64_t rows, int width,
                             hipStream_t st);

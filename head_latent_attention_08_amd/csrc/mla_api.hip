@@ -539,6 +539,210 @@ mla_status mla_decode_workspace_size(const mla_config *cfg, int64_t batch, int64
   return MLA_OK;
 }
 
+// ------------------------------------------------------------ chunked prefill
+// q_len new tokens per sequence against a latent cache, expanded form: the
+// cached rows (prefix and the new rows) of every usable sequence are packed
+// into one key stream, up-projected to per-head keys and values, and the
+// prefill attention runs each query over its own sequence's keys.
+struct ChunkPlan {
+  int64_t ld_down, kmax;
+  size_t off_down, off_q, off_o, off_kstream, off_kn, off_v, off_lens, off_kofs, off_lo, off_hi,
+      off_pos, off_valid, total;
+};
+
+static ChunkPlan plan_chunk(const mla_config &c, int64_t B, int64_t T, int64_t max_keys) {
+  const size_t es = dtype_size(c.dtype);
+  const int64_t M = B * T, H = c.num_heads, W = c.kv_lora_rank + c.qk_rope_head_dim;
+  ChunkPlan p;
+  p.ld_down = (int64_t)round_up(c.q_lora_rank + W, 8);
+  p.kmax = (int64_t)round_up((size_t)max_keys, 8);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  p.off_down = take((size_t)M * p.ld_down * es);
+  p.off_q = take((size_t)M * H * (c.qk_nope_head_dim + c.qk_rope_head_dim) * es);
+  p.off_o = take((size_t)M * H * c.v_head_dim * es);
+  p.off_kstream = take((size_t)p.kmax * W * es);
+  p.off_kn = take((size_t)p.kmax * H * c.qk_nope_head_dim * es);
+  p.off_v = take((size_t)p.kmax * H * c.v_head_dim * es);
+  p.off_lens = take((size_t)B * sizeof(int32_t));
+  p.off_kofs = take((size_t)(B + 1) * sizeof(int32_t));
+  p.off_lo = take((size_t)M * sizeof(int32_t));
+  p.off_hi = take((size_t)M * sizeof(int32_t));
+  p.off_pos = take((size_t)M * sizeof(int32_t));
+  p.off_valid = take((size_t)M * sizeof(int32_t));
+  p.total = off;
+  return p;
+}
+
+static mla_status check_chunk(const mla_config *cfg, int64_t B, int64_t T, int64_t cap,
+                              int64_t max_keys) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (B < 1 || B > 4096) return fail(MLA_ERR_INVALID_ARGUMENT, "batch must be in [1, 4096]");
+  if (T < 1 || T > cap) return fail(MLA_ERR_INVALID_ARGUMENT, "q_len must be in [1, cache_capacity]");
+  if (B * cap > (1LL << 30) || B * T > (1LL << 24))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch x cache_capacity or batch x q_len is too large");
+  if (max_keys < T || max_keys > (1LL << 24))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "max_keys must be in [q_len, 2^24]");
+  if (!prefill_instance(*cfg))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "head dims (nope %d, rope %d, v %d) are not instantiated; supported: "
+                "(16,8,16), (64,32,64), (128,64,128)",
+                cfg->qk_nope_head_dim, cfg->qk_rope_head_dim, cfg->v_head_dim);
+  return MLA_OK;
+}
+
+mla_status mla_prefill_chunk_workspace_size(const mla_config *cfg, int64_t batch, int64_t q_len,
+                                            int64_t cache_capacity, int64_t max_keys,
+                                            size_t *bytes) {
+  mla_status s = check_chunk(cfg, batch, q_len, cache_capacity, max_keys);
+  if (s != MLA_OK) return s;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = plan_chunk(*cfg, batch, q_len, max_keys).total;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_chunk(const mla_config *cfg, const mla_weights *w, const void *x,
+                             int64_t batch, int64_t q_len, void *latent_cache,
+                             int64_t cache_capacity, const int32_t *cache_lens, int64_t max_keys,
+                             void *y, void *workspace, size_t workspace_bytes, void *hip_stream) {
+  mla_status s = check_chunk(cfg, batch, q_len, cache_capacity, max_keys);
+  if (s != MLA_OK) return s;
+  if ((s = check_weights(w)) != MLA_OK) return s;
+  if (!x || !y || !workspace || !latent_cache || !cache_lens)
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "x, y, latent_cache, cache_lens and workspace must not be NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || !aligned16(latent_cache) ||
+      ((uintptr_t)cache_lens & 3) != 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "x, y, latent_cache and workspace must be 16-byte "
+                                          "aligned, cache_lens 4-byte aligned");
+  const mla_config &c = *cfg;
+  const ChunkPlan p = plan_chunk(c, batch, q_len, max_keys);
+  if (workspace_bytes < p.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
+                workspace_bytes, p.total);
+
+  hipStream_t st = (hipStream_t)hip_stream;
+  const size_t es = dtype_size(c.dtype);
+  char *ws = (char *)workspace;
+  char *down = ws + p.off_down, *q = ws + p.off_q, *o = ws + p.off_o;
+  char *kst = ws + p.off_kstream, *kn = ws + p.off_kn, *v = ws + p.off_v;
+  int32_t *lens_eff = reinterpret_cast<int32_t *>(ws + p.off_lens);
+  int32_t *kofs = reinterpret_cast<int32_t *>(ws + p.off_kofs);
+  int32_t *lo = reinterpret_cast<int32_t *>(ws + p.off_lo);
+  int32_t *hi = reinterpret_cast<int32_t *>(ws + p.off_hi);
+  int32_t *pos = reinterpret_cast<int32_t *>(ws + p.off_pos);
+  int32_t *valid = reinterpret_cast<int32_t *>(ws + p.off_valid);
+  const int B = (int)batch, T = (int)q_len, M = B * T, H = c.num_heads;
+  const int D = c.hidden_size, rq = c.q_lora_rank, rkv = c.kv_lora_rank;
+  const int dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim;
+  const int dqk = dn + dr, W = rkv + dr;
+  const int K = (int)p.kmax;
+  const RopeTab tab = make_rope_tab(c.rope, dr);
+
+  // usable sequences, packed key offsets, per-query key ranges and positions
+  MLA_HIP(launch_chunk_index(cache_lens, B, T, cache_capacity, max_keys, lens_eff, kofs, lo, hi, pos,
+                             valid, st),
+          "chunk index");
+  {  // [c_q ‖ c_kv ‖ k_pe] = x [w_down_q; w_down_kv; w_kr]^T
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = M;
+    g.N = rq + W;
+    g.K = D;
+    g.A = x;
+    g.lda = D;
+    g.S = M;
+    g.H = 1;
+    g.nseg = 3;
+    g.seg[0] = GemmSeg{w->w_down_q, D, 0, down, rq, p.ld_down, 0};
+    g.seg[1] = GemmSeg{w->w_down_kv, D, rq, down, rkv, p.ld_down, rq};
+    g.seg[2] = GemmSeg{w->w_kr, D, rq + rkv, down, dr, p.ld_down, rq + rkv};
+    MLA_HIP(launch_gemm(g, st), "down projection");
+  }
+  MLA_HIP(launch_rmsnorm(c.dtype, down, M, p.ld_down, rq, w->q_norm, c.rms_norm_eps, st), "rmsnorm");
+  MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, M, M, (int64_t)M * p.ld_down,
+                      p.ld_down, 1, 0, pos, tab, st),
+          "rope k_pe");
+  // the new latent rows go to cache rows L_b .. L_b + T - 1 (usable sequences)
+  MLA_HIP(launch_cache_append(c.dtype, latent_cache, cache_capacity, lens_eff, T,
+                              down + (size_t)rq * es, p.ld_down, B, W, st),
+          "cache append");
+  {  // q = [q_nope ‖ q_pe] per head over all M queries
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = M;
+    g.N = H * dqk;
+    g.K = rq;
+    g.A = down;
+    g.lda = p.ld_down;
+    g.S = M;
+    g.H = H;
+    g.nseg = 2;
+    g.seg[0] = GemmSeg{w->w_up_q, rq, 0, q, dn, dqk, 0};
+    g.seg[1] = GemmSeg{w->w_qr, rq, H * dn, q, dr, dqk, dn};
+    MLA_HIP(launch_gemm(g, st), "q up-projection");
+  }
+  MLA_HIP(launch_rope(c.dtype, q + (size_t)dn * es, M, M, (int64_t)H * M * dqk, dqk, H,
+                      (int64_t)M * dqk, pos, tab, st),
+          "rope q_pe");
+  // key stream: every usable sequence's cache rows 0 .. L_b + T - 1, packed
+  MLA_HIP(launch_gather_keys(c.dtype, kst, K, latent_cache, cache_capacity, W, kofs, B, st),
+          "key gather");
+  {  // k_nope [1, H, K, d_n] and v channel-major [1, H, d_v, K]
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = K;
+    g.N = H * (dn + dv);
+    g.K = rkv;
+    g.A = kst;
+    g.lda = W;
+    g.S = K;
+    g.H = H;
+    g.nseg = 2;
+    g.seg[0] = GemmSeg{w->w_up_k, rkv, 0, kn, dn, dn, 0};
+    g.seg[1] = GemmSeg{w->w_up_v, rkv, H * dn, v, dv, dv, 0, 1};
+    MLA_HIP(launch_gemm(g, st), "kv up-projection");
+  }
+  {
+    PrefillAttnArgs a;
+    a.q = q;
+    a.k_nope = kn;
+    a.k_pe = kst + (size_t)rkv * es;
+    a.ld_kpe = W;
+    a.vt = v;
+    a.o = o;
+    a.B = 1;
+    a.S = M;
+    a.H = H;
+    a.scale = resolve_scale(c);
+    a.kv_lo = lo;
+    a.kv_hi = hi;
+    a.valid = valid;
+    a.Sk = K;
+    MLA_HIP(launch_prefill_attention(c.dtype, dn, dr, dv, a, st), "attention");
+  }
+  {  // y = o wo^T
+    GemmDesc g;
+    g.dtype = c.dtype;
+    g.M = M;
+    g.N = D;
+    g.K = H * dv;
+    g.A = o;
+    g.lda = (int64_t)H * dv;
+    g.S = M;
+    g.H = 1;
+    g.nseg = 1;
+    g.seg[0] = GemmSeg{w->wo, (int64_t)H * dv, 0, y, D, D, 0};
+    MLA_HIP(launch_gemm(g, st), "output projection");
+  }
+  return MLA_OK;
+}
+
 mla_status mla_decode_multi_workspace_size(const mla_config *cfg, int64_t batch, int64_t q_len,
                                            int64_t cache_capacity, size_t *bytes) {
   mla_status s = check_decode_sizes(cfg, batch, cache_capacity, q_len);

@@ -99,6 +99,10 @@ def load_library(path: str = LIB_PATH):
                                                       ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_prefill_varlen_forward.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P,
                                                P, i64, i64, P, P, P, ctypes.c_size_t, P]
+    lib.mla_prefill_chunk_workspace_size.argtypes = [ctypes.POINTER(Config), i64, i64, i64, i64,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_prefill_chunk.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P, i64, i64,
+                                      P, i64, P, i64, P, P, ctypes.c_size_t, P]
     lib.mla_decode_workspace_size.argtypes = [ctypes.POINTER(Config), i64, i64,
                                               ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_decode_layout_of.argtypes = [ctypes.POINTER(Config), i64, i64,
@@ -113,6 +117,7 @@ def load_library(path: str = LIB_PATH):
                                    i64, P, ctypes.POINTER(RopeParams), P]
     for fn in ("mla_prefill_workspace_size", "mla_prefill_layout_of", "mla_prefill_forward",
                "mla_prefill_varlen_workspace_size", "mla_prefill_varlen_forward",
+               "mla_prefill_chunk_workspace_size", "mla_prefill_chunk",
                "mla_decode_workspace_size", "mla_decode_layout_of", "mla_decode_absorbed",
                "mla_decode_multi_workspace_size", "mla_decode_absorbed_multi", "mla_rope_apply"):
         getattr(lib, fn).restype = st
@@ -361,6 +366,39 @@ def mla_decode_absorbed_multi(cfg: MlaConfig, weights: dict, x: torch.Tensor,
     _check(load_library().mla_decode_absorbed_multi(
         ctypes.byref(c), ctypes.byref(w), _ptr(x), B, T, _ptr(latent_cache), cap,
         _ptr(cache_lens), _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return y, workspace
+
+
+def mla_prefill_chunk_workspace_size(cfg: MlaConfig, batch: int, q_len: int, capacity: int,
+                                     max_keys: int) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().mla_prefill_chunk_workspace_size(ctypes.byref(c), batch, q_len, capacity,
+                                                           max_keys, ctypes.byref(n)))
+    return n.value
+
+
+def mla_prefill_chunk(cfg: MlaConfig, weights: dict, x: torch.Tensor, latent_cache: torch.Tensor,
+                      cache_lens: torch.Tensor, max_keys: int, y=None, workspace=None, stream=None):
+    """Expanded-form prefill chunk, x [B, q_len, D] against the latent cache;
+    writes cache rows lens[b] .. lens[b] + q_len - 1.  Returns (y, workspace)."""
+    B, T, D = x.shape
+    cap = latent_cache.shape[1]
+    dev = x.device
+    if y is None:
+        y = torch.empty((B, T, D), dtype=cfg.torch_dtype, device=dev)
+    need = mla_prefill_chunk_workspace_size(cfg, B, T, cap, max_keys)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if cache_lens.dtype != torch.int32:
+        raise ValueError("cache_lens must be int32")
+    _device_check(x, y, latent_cache, cache_lens, workspace)
+    w = make_weights(weights)
+    c = cfg.c()
+    _check(load_library().mla_prefill_chunk(
+        ctypes.byref(c), ctypes.byref(w), _ptr(x), B, T, _ptr(latent_cache), cap, _ptr(cache_lens),
+        max_keys, _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return y, workspace
 

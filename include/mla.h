@@ -238,6 +238,41 @@ MLA_API mla_status mla_decode_absorbed_multi(const mla_config *cfg, const mla_we
                                      void *workspace, size_t workspace_bytes,
                                      void *hip_stream);
 
+/* Chunked prefill against a latent cache, expanded form: the same operation
+ * as mla_decode_absorbed_multi (token t of sequence b at position
+ * lens[b] + t, its latent row written at cache row lens[b] + t, attending
+ * rows 0..lens[b] + t), computed the prefill way: the cache rows 0 ..
+ * lens[b] + q_len - 1 of every sequence (the prefix and the new rows) are
+ * packed into one key stream, up-projected with w_up_k / w_up_v to per-head
+ * keys and values (the MLA section's K_i and V_i from c_kv, k_pe shared), and
+ * each query runs the causal softmax over its own sequence's keys.  This
+ * costs 2(d_n + d_r) + 2 d_v flops per query-key pair plus the up-projection
+ * of every key row, so it suits long chunks.
+ *   x            [B, q_len, D]            device
+ *   latent_cache [B, capacity, r_kv + d_r] device; rows [0, lens[b]) read,
+ *                rows lens[b] .. lens[b] + q_len - 1 written, then read
+ *   cache_lens   [B] int32                 device, read only; a sequence with
+ *                lens[b] < 0 or lens[b] + q_len > capacity gets NaN y rows
+ *                and no cache write
+ *   max_keys     host bound on the packed keys, sum over usable sequences of
+ *                lens[b] + q_len: it sizes the workspace (per key: the latent
+ *                row plus H (d_n + d_v) expanded elements, 64 KB at V3 sizes
+ *                in bf16); when the keys exceed it every y row is NaN and no
+ *                cache row is written
+ *   y            [B, q_len, D]            device, written
+ * Status: INVALID_ARGUMENT for NULL or misaligned pointers, B outside
+ * [1, 4096], q_len outside [1, capacity], max_keys outside [q_len, 2^24],
+ * B * q_len > 2^24, or a bad config; UNSUPPORTED, WORKSPACE_TOO_SMALL and HIP
+ * as for mla_prefill_forward. */
+MLA_API mla_status mla_prefill_chunk_workspace_size(const mla_config *cfg, int64_t batch,
+                                            int64_t q_len, int64_t cache_capacity,
+                                            int64_t max_keys, size_t *bytes);
+MLA_API mla_status mla_prefill_chunk(const mla_config *cfg, const mla_weights *w, const void *x,
+                             int64_t batch, int64_t q_len, void *latent_cache,
+                             int64_t cache_capacity, const int32_t *cache_lens,
+                             int64_t max_keys, void *y, void *workspace,
+                             size_t workspace_bytes, void *hip_stream);
+
 /* --------------------------------------------------------------------- RoPE
  * In-place RoPE of x[t, h, 0..rope_dim) at positions[t] (device int32 [n_tokens]),
  * element (t, h, i) at x + t*token_stride + h*head_stride + i (strides in

@@ -140,6 +140,32 @@ def test_varlen_sizes_and_arguments_rejected_without_launch():
     assert st == b.MLA_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_chunk_sizes_and_arguments_rejected_without_launch():
+    cfg = m.MlaConfig(**V3)
+    n = m.mla_prefill_chunk_workspace_size(cfg, 1, 1024, 8192, 4096)
+    # per key the latent row and the expanded keys and values: 128 x (128 + 128) x 2 B
+    assert n >= 4096 * (576 + 128 * 256) * 2
+    for B, T, cap, mk in [(0, 4, 16, 16), (4097, 4, 16, 16), (1, 0, 16, 16), (1, 17, 16, 32),
+                          (1, 8, 16, 7), (1, 8, 16, (1 << 24) + 1)]:
+        with pytest.raises(m.MlaError) as e:
+            m.mla_prefill_chunk_workspace_size(cfg, B, T, cap, mk)
+        assert e.value.status == b.MLA_ERR_INVALID_ARGUMENT
+    lib = m.load_library()
+    c = cfg.c()
+    good = ctypes.c_void_p(0x10000)
+    w = b.Weights(*([0x10000] * 9))
+    need = m.mla_prefill_chunk_workspace_size(cfg, 2, 8, 64, 64)
+    st = lib.mla_prefill_chunk(ctypes.byref(c), ctypes.byref(w), good, 2, 8, good, 64, None, 64,
+                               good, good, need, None)
+    assert st == b.MLA_ERR_INVALID_ARGUMENT and b"cache_lens" in lib.mla_last_error()
+    st = lib.mla_prefill_chunk(ctypes.byref(c), ctypes.byref(w), good, 2, 8, ctypes.c_void_p(0x10008),
+                               64, good, 64, good, good, need, None)
+    assert st == b.MLA_ERR_INVALID_ARGUMENT and b"aligned" in lib.mla_last_error()
+    st = lib.mla_prefill_chunk(ctypes.byref(c), ctypes.byref(w), good, 2, 8, good, 64, good, 64,
+                               good, good, need - 1, None)
+    assert st == b.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
 def _raw_prefill(lib, cfg, w, x, y, ws, nbytes):
     c = cfg.c()
     return lib.mla_prefill_forward(ctypes.byref(c), ctypes.byref(w) if w is not None else None,

@@ -389,6 +389,95 @@ def test_multi_token_decode_q_len_one_is_single_decode():
     np.testing.assert_array_equal(to_np(c2), to_np(c1))
 
 
+# ----------------------------------------------- prefill chunks, expanded ---
+
+def _run_chunk(c, conv, T, cap, lens, max_keys=None, seed=None):
+    m = _m()
+    B = len(lens)
+    _, w, _, cache = si.make_decode_inputs(c, batch=B, capacity=cap, len_lo=0, len_hi=1,
+                                           gains="random", seed=seed)
+    xs, _ = si.make_inputs(c, seq=T, batch=B, gains="random", seed=seed)
+    lens = np.asarray(lens, dtype=np.int32)
+    cfg = mla_cfg(c, rope=conv)
+    dt = c["dtype"]
+    if max_keys is None:
+        max_keys = max(T, sum(int(L) + T for L in lens if 0 <= L and L + T <= cap))
+    print(f"chunk {dt} T={T} cap={cap} lens={lens.tolist()} max_keys={max_keys}", flush=True)
+    cache_d = to_dev(cache, dt)
+    ws = _poisoned(m.mla_prefill_chunk_workspace_size(cfg, B, T, cap, max_keys))
+    y, ws = m.mla_prefill_chunk(cfg, weights_to_dev(w, dt), to_dev(xs, dt), cache_d,
+                                torch.from_numpy(lens).cuda(), max_keys, workspace=ws)
+    torch.cuda.synchronize()
+    return xs, w, lens, cache, y, cache_d
+
+
+@pytest.mark.parametrize("name,conv,T,cap,lens", [
+    # tile edges, an empty prefix and a chunk ending exactly at capacity
+    ("small", "interleaved", 64, 300, [0, 37, 96, 236]),
+    # longer than the absorbed multi-token path takes
+    ("small", "half_split", 300, 512, [0, 150]),
+    ("tiny", "half_split", 5, 20, [0, 3, 15]),
+])
+def test_prefill_chunk_matches_oracle(name, conv, T, cap, lens):
+    # the expanded form computes what the multi-token decode computes: token t
+    # at position lens[b] + t attends rows 0..lens[b] + t, its row appended
+    c = si.CONFIGS[name]
+    xs, w, lens, cache, y, cache_d = _run_chunk(c, conv, T, cap, lens, seed=7500 + T)
+    ref, new_rows = orc.mla_decode_absorbed_multi(oracle_cfg(c, rope=conv), w, xs, cache, lens)
+    yn, got = to_np(y), to_np(cache_d)
+    B = len(lens)
+    for b in range(B):
+        assert_close_rows(yn[b], ref[b], c["dtype"], f"y seq {b}")
+        assert_close_rows(got[b, lens[b]:lens[b] + T], new_rows[b], c["dtype"], f"rows seq {b}")
+    mask = np.ones(cache.shape[:2], dtype=bool)
+    for b in range(B):
+        mask[b, lens[b]:lens[b] + T] = False
+    np.testing.assert_array_equal(got[mask], cache.astype(np.float64)[mask])
+
+
+def test_prefill_chunk_invalid_lengths_and_key_bound():
+    # lens[b] + q_len > capacity: NaN rows and no write for that sequence only;
+    # keys beyond max_keys: every row NaN and no write at all
+    c = si.CONFIGS["small"]
+    T, cap = 40, 120
+    xs, w, lens, cache, y, cache_d = _run_chunk(c, "interleaved", T, cap, [10, cap - 2, 50],
+                                                seed=7600)
+    ok = [0, 2]
+    ref, _ = orc.mla_decode_absorbed_multi(oracle_cfg(c, rope="interleaved"), w, xs[ok],
+                                           cache[ok], lens[ok])
+    yn = to_np(y)
+    for i, b in enumerate(ok):
+        assert_close_rows(yn[b], ref[i], "bf16", f"y seq {b}")
+    assert np.all(np.isnan(yn[1]))
+    np.testing.assert_array_equal(to_np(cache_d)[1], cache[1].astype(np.float64))
+    xs, w, lens, cache, y, cache_d = _run_chunk(c, "interleaved", T, cap, [10, 50],
+                                                max_keys=100, seed=7601)
+    assert np.all(np.isnan(to_np(y)))
+    np.testing.assert_array_equal(to_np(cache_d), cache.astype(np.float64))
+
+
+def test_prefill_chunk_after_prefill_is_the_full_prefill_tail():
+    # prefill the first 200 tokens (their latent rows fill the cache), then the
+    # next 120 as a chunk: the chunk's outputs are rows 200..319 of the prefill
+    # of all 320 tokens
+    m = _m()
+    c = si.CONFIGS["small"]
+    L, T, cap = 200, 120, 400
+    x, w = si.make_inputs(c, seq=L + T, batch=1, gains="random")
+    cfg = mla_cfg(c, rope="half_split")
+    wd = weights_to_dev(w, "bf16")
+    _, lat, _ = m.mla_prefill_forward(cfg, wd, to_dev(x[:, :L], "bf16"), want_latent=True)
+    cache = torch.zeros((1, cap, lat.shape[-1]), dtype=torch.bfloat16, device="cuda")
+    cache[0, :L] = lat[0]
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    y, _ = m.mla_prefill_chunk(cfg, wd, to_dev(x[:, L:], "bf16"), cache, lens, L + T)
+    torch.cuda.synchronize()
+    ref, ref_lat = orc.mla_prefill_rows(oracle_cfg(c, rope="half_split"), w, x,
+                                        np.arange(L, L + T))
+    assert_close_rows(to_np(y[0]), ref, "bf16", "chunk rows")
+    assert_close_rows(to_np(cache[0, :L + T]), ref_lat, "bf16", "cache rows")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_decode_score_range_beyond_first_tile(dtype):
     # cache rows after the first tile are scaled up so their scores exceed

@@ -63,6 +63,28 @@ def test_v3_prefill_varlen_sampled_rows():
         assert_close_rows(to_np(lat[a:a + L]), ref_lat, "bf16", f"seq {b} latent")
 
 
+def test_v3_prefill_chunk_after_prefill_sampled_rows():
+    # V3: prefill 3000 tokens into the latent cache, then the remaining 1096
+    # as one expanded chunk; sampled chunk rows against the oracle's prefill
+    # of all 4096 tokens
+    m = _m()
+    c = si.CONFIGS["v3_prefill"]
+    x, w = si.make_inputs(c)
+    L, T = 3000, 1096
+    print(f"v3 chunk: prefix {L}, chunk {T}, seed 3000", flush=True)
+    cfg = mla_cfg(c, rope="interleaved")
+    wd = weights_to_dev(w, "bf16")
+    _, lat, _ = m.mla_prefill_forward(cfg, wd, to_dev(x[:, :L], "bf16"), want_latent=True)
+    cache = torch.zeros((1, L + T, lat.shape[-1]), dtype=torch.bfloat16, device="cuda")
+    cache[0, :L] = lat[0]
+    y, _ = m.mla_prefill_chunk(cfg, wd, to_dev(x[:, L:], "bf16"), cache,
+                               torch.tensor([L], dtype=torch.int32, device="cuda"), L + T)
+    torch.cuda.synchronize()
+    rows = np.array([L, L + 1, L + 31, L + 32, L + 547, L + T - 1])
+    ref, _ = orc.mla_prefill_rows(oracle_cfg(c), w, x, rows)
+    assert_close_rows(to_np(y[0, rows - L]), ref, "bf16", "chunk rows")
+
+
 def test_v3_prefill_half_split_spot_check():
     c = si.CONFIGS["v3_prefill"]
     x, w = si.make_inputs(c, seq=1024)
