@@ -109,6 +109,19 @@ def multi_token_bytes_flops(c, lens, T):
     return float(rows * (r + dr) * 2), float(seen * H * (2 * (r + dr) + 2 * r))
 
 
+def chunk_flops(c, L, T):
+    """Algorithmic FLOPs of an expanded-form chunk of T tokens after L cached
+    rows (one sequence): projections of the new tokens, the up-projection of
+    all L + T key rows, the causal attention and the output projection."""
+    D, H = c["hidden_size"], c["num_attention_heads"]
+    rq, rkv = c["q_lora_rank"], c["kv_lora_rank"]
+    dn, dr, dv = c["qk_nope_head_dim"], c["qk_rope_head_dim"], c["v_head_dim"]
+    proj = 2 * T * (D * (rq + rkv + dr) + rq * H * (dn + dr) + H * dv * D)
+    kv = 2 * (L + T) * rkv * H * (dn + dv)
+    pairs = sum(L + t + 1 for t in range(T))
+    return float(proj + kv + pairs * H * 2 * (dn + dr + dv))
+
+
 def cpu_baseline(c_pre, x, w, c_dec, xd, wd, lens, cache, seconds_hint=True):
     """The float64 oracle, untuned, on bounded samples of the same workloads."""
     import numpy as np
@@ -362,6 +375,32 @@ def main():
             log(f"bench: multi-token decode q_len={T} B={Bm}: attention {a_ms * 1e3:.1f} us, "
                 f"{mb / (a_ms * 1e-3) / 1e9:.0f} GB/s, step {m_ms * 1e3:.1f} us")
         out["decode_multi_token"] = lines
+        # Chunked prefill against a latent cache, expanded form: one sequence,
+        # 3072 cached rows (a copy of a decode sequence's cache), 1024 new
+        # tokens; context only
+        Lc, Tc = 3072, 1024
+        cache_c = caches[0][:1].clone()
+        lens_c = torch.tensor([Lc], dtype=torch.int32, device="cuda")
+        xc = torch.randn((1, Tc, c_dec["hidden_size"]), dtype=torch.float32,
+                         generator=torch.Generator().manual_seed(4400)).to("cuda", torch.bfloat16)
+        yc = torch.empty_like(xc)
+        wsc = torch.empty(m.mla_prefill_chunk_workspace_size(cfg_dec, 1, Tc, cache_c.shape[1], Lc + Tc),
+                          dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            m.mla_prefill_chunk(cfg_dec, wdec_d, xc, cache_c, lens_c, Lc + Tc, y=yc, workspace=wsc)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            m.mla_prefill_chunk(cfg_dec, wdec_d, xc, cache_c, lens_c, Lc + Tc, y=yc, workspace=wsc)
+        e1.record()
+        torch.cuda.synchronize()
+        c_ms = e0.elapsed_time(e1) / 5
+        c_fl = chunk_flops(c_dec, Lc, Tc)
+        out["prefill_chunk"] = {"cached_rows": Lc, "q_len": Tc, "ms": c_ms,
+                                "tflops": c_fl / (c_ms * 1e-3) / 1e12, "gflop": c_fl / 1e9}
+        log(f"bench: prefill chunk {Tc} tokens after {Lc} cached rows: {c_ms:.3f} ms, "
+            f"{c_fl / (c_ms * 1e-3) / 1e12:.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on bounded samples")
         out["cpu_baseline"] = cpu_baseline(c_pre, x, w, c_dec, xdec, wdec, lens, cache)
