@@ -518,6 +518,7 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
 #define SK_STAGES 3
 #endif
 constexpr int SK_M = 64, SK_N = 128, SK_K = 128, SK_NST = SK_STAGES;
+constexpr int SK_MMAX = 512;  // larger M goes to the large-tile kernel
 constexpr int SK_STAGE = (SK_M + SK_N) * SK_K;    // elements per stage
 constexpr int SK_CPW = (SK_M + SK_N) / 4 / 4;      // copy instructions per wave per chunk
 // LDS position of element (r, k) of a stage operand: 128-element rows whose
@@ -556,10 +557,14 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, float *p
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: feeds M0
   const int g = lane >> 5, l32 = lane & 31;
-  const int n0 = blockIdx.x * SK_N, ks = blockIdx.y, z = blockIdx.z;
+  // grid z: batch index times the 64-row blocks of M
+  const int mblocks = (p.M + SK_M - 1) / SK_M;
+  const int z = blockIdx.z / mblocks, m0 = (blockIdx.z - z * mblocks) * SK_M;
+  const int n0 = blockIdx.x * SK_N, ks = blockIdx.y;
   const int k_begin = ks * kslice;
   const int nk = kslice / SK_K;
-  const bf16 *A = reinterpret_cast<const bf16 *>(p.A) + (int64_t)z * p.strideA + k_begin;
+  const bf16 *A = reinterpret_cast<const bf16 *>(p.A) + (int64_t)z * p.strideA + (int64_t)m0 * p.lda +
+                  k_begin;
   // B rows: column ranges start at multiples of 128 (checked on the host)
   const int st = seg_of(p, n0);
   const int t_nb = SEG_FIELD(p, st, n_begin);
@@ -578,7 +583,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, float *p
     const bool is_a = blk < SK_M / 4;
     const int row = 4 * (is_a ? blk : blk - SK_M / 4) + (lane >> 4);
     const int j = (lane & 15) ^ (row & 15);
-    const int rc = is_a ? min(row, p.M - 1) : min(row, p.N - 1 - n0);
+    const int rc = is_a ? min(row, p.M - 1 - m0) : min(row, p.N - 1 - n0);
     const int64_t ld = is_a ? p.lda : t_ldb;
     doff[q] = (uint32_t)((rc * ld + j * 8) * (int64_t)sizeof(bf16));
   }
@@ -641,7 +646,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, float *p
     const SkinnyCol c0(p, z, st, min(n, p.N - 1)), c1(p, z, st, min(n + 32, p.N - 1));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = wm * 32 + acc_row(r, lane);
+      const int m = m0 + wm * 32 + acc_row(r, lane);
       if (m < p.M) {
         if (n < p.N) c0.store(p, m, acc0[r]);
         if (n + 32 < p.N) c1.store(p, m, acc1[r]);
@@ -652,7 +657,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p, float *p
   float *pt = part + (((int64_t)z * gridDim.y + ks) * p.M) * p.N;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int m = wm * 32 + acc_row(r, lane);
+    const int m = m0 + wm * 32 + acc_row(r, lane);
     if (m < p.M) {
       if (n < p.N) pt[(int64_t)m * p.N + n] = acc0[r];
       if (n + 32 < p.N) pt[(int64_t)m * p.N + n + 32] = acc1[r];
@@ -680,10 +685,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce(GemmParams p, const fl
 // divisor of K/128 that keeps the grid within one workgroup per CU (a stage
 // set fills most of a CU's LDS, and a second round of workgroups would leave
 // the tail of the launch running on a fraction of the chip).
-static int skinny_split(int N, int K, int batch) {
-  const int ntile = (N + SK_N - 1) / SK_N;
+static int skinny_split(int M, int N, int K, int batch) {
+  const int ntile = (N + SK_N - 1) / SK_N, mblocks = (M + SK_M - 1) / SK_M;
   const int kchunks = K / SK_K;
-  const int want = std::max(1, 256 / (ntile * batch));
+  const int want = std::max(1, 256 / (ntile * batch * mblocks));
   int nsplit = 1;
   for (int c = 1; c <= kchunks; ++c)
     if (kchunks % c == 0 && c <= want) nsplit = c;
@@ -691,8 +696,9 @@ static int skinny_split(int N, int K, int batch) {
 }
 
 size_t gemm_scratch_bytes(int dtype, int M, int N, int K, int batch) {
-  if (dtype != BF16 || M > SK_M || K % SK_K != 0) return 0;
-  return (size_t)skinny_split(N, K, batch) * batch * M * N * sizeof(float);
+  if (dtype != BF16 || M > SK_MMAX || K % SK_K != 0) return 0;
+  const int nsplit = skinny_split(M, N, K, batch);
+  return nsplit > 1 ? (size_t)nsplit * batch * M * N * sizeof(float) : 0;
 }
 
 // A big-kernel tile must not mix row-major and channel-major column ranges.
@@ -733,17 +739,20 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   for (int i = 0; i < d.nseg && big; ++i)
     big = d.seg[i].n_begin % 16 == 0 && (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
   if (big && tr_aligned(d, BigTile<4, 4, GB_STAGES>::N)) return launch_big<4, 4>(p, d, 0, d.N, st);
-  bool skinny = d.dtype == BF16 && !d.b_kn && d.M <= SK_M && d.K % SK_K == 0 && d.N % 8 == 0 &&
-                d.workspace != nullptr;
+  bool skinny = d.dtype == BF16 && !d.b_kn && d.M <= SK_MMAX && d.K % SK_K == 0 && d.N % 8 == 0 &&
+                d.batch * ((d.M + SK_M - 1) / SK_M) <= 65535;
   for (int i = 0; i < d.nseg && skinny; ++i) skinny = d.seg[i].n_begin % SK_N == 0;
   if (skinny) {
-    const int ntile = (d.N + SK_N - 1) / SK_N;
-    int nsplit = skinny_split(d.N, d.K, d.batch);
-    if ((size_t)nsplit * d.batch * d.M * d.N * sizeof(float) > d.workspace_bytes) nsplit = 1;
-    if ((size_t)nsplit * d.batch * d.M * d.N * sizeof(float) <= d.workspace_bytes) {
+    // K is split only into a workspace big enough for the fp32 partials
+    const int ntile = (d.N + SK_N - 1) / SK_N, mblocks = (d.M + SK_M - 1) / SK_M;
+    int nsplit = skinny_split(d.M, d.N, d.K, d.batch);
+    if (nsplit > 1 && (d.workspace == nullptr ||
+                       (size_t)nsplit * d.batch * d.M * d.N * sizeof(float) > d.workspace_bytes))
+      nsplit = 1;
+    {
       float *part = reinterpret_cast<float *>(d.workspace);
-      hipLaunchKernelGGL(gemm_skinny_kernel, dim3(ntile, nsplit, d.batch), dim3(256), 0, st, p,
-                         part, d.K / nsplit);
+      hipLaunchKernelGGL(gemm_skinny_kernel, dim3(ntile, nsplit, d.batch * mblocks), dim3(256), 0, st,
+                         p, part, d.K / nsplit);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || nsplit == 1) return e;
       const int64_t total = (int64_t)d.M * d.N;

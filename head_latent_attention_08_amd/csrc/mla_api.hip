@@ -547,7 +547,7 @@ mla_status mla_decode_workspace_size(const mla_config *cfg, int64_t batch, int64
 struct ChunkPlan {
   int64_t ld_down, kmax;
   size_t off_down, off_q, off_o, off_kstream, off_kn, off_v, off_lens, off_kofs, off_lo, off_hi,
-      off_pos, off_valid, total;
+      off_pos, off_valid, off_gemm, gemm_bytes, total;
 };
 
 static ChunkPlan plan_chunk(const mla_config &c, int64_t B, int64_t T, int64_t max_keys) {
@@ -574,6 +574,16 @@ static ChunkPlan plan_chunk(const mla_config &c, int64_t B, int64_t T, int64_t m
   p.off_hi = take((size_t)M * sizeof(int32_t));
   p.off_pos = take((size_t)M * sizeof(int32_t));
   p.off_valid = take((size_t)M * sizeof(int32_t));
+  // fp32 split-K partials of the projections with few rows
+  const int dt = c.dtype, D = c.hidden_size, rq = c.q_lora_rank, rkv = c.kv_lora_rank;
+  const int dqk = c.qk_nope_head_dim + c.qk_rope_head_dim;
+  p.gemm_bytes = std::max(std::max(gemm_scratch_bytes(dt, (int)M, rq + (int)W, D, 1),
+                                   gemm_scratch_bytes(dt, (int)M, (int)H * dqk, rq, 1)),
+                          std::max(gemm_scratch_bytes(dt, (int)M, D, (int)H * c.v_head_dim, 1),
+                                   gemm_scratch_bytes(dt, (int)p.kmax,
+                                                      (int)H * (c.qk_nope_head_dim + c.v_head_dim),
+                                                      rkv, 1)));
+  p.off_gemm = take(p.gemm_bytes);
   p.total = off;
   return p;
 }
@@ -662,6 +672,8 @@ mla_status mla_prefill_chunk(const mla_config *cfg, const mla_weights *w, const 
     g.seg[0] = GemmSeg{w->w_down_q, D, 0, down, rq, p.ld_down, 0};
     g.seg[1] = GemmSeg{w->w_down_kv, D, rq, down, rkv, p.ld_down, rq};
     g.seg[2] = GemmSeg{w->w_kr, D, rq + rkv, down, dr, p.ld_down, rq + rkv};
+    g.workspace = ws + p.off_gemm;
+    g.workspace_bytes = p.gemm_bytes;
     MLA_HIP(launch_gemm(g, st), "down projection");
   }
   MLA_HIP(launch_rmsnorm(c.dtype, down, M, p.ld_down, rq, w->q_norm, c.rms_norm_eps, st), "rmsnorm");
@@ -685,6 +697,8 @@ mla_status mla_prefill_chunk(const mla_config *cfg, const mla_weights *w, const 
     g.nseg = 2;
     g.seg[0] = GemmSeg{w->w_up_q, rq, 0, q, dn, dqk, 0};
     g.seg[1] = GemmSeg{w->w_qr, rq, H * dn, q, dr, dqk, dn};
+    g.workspace = ws + p.off_gemm;
+    g.workspace_bytes = p.gemm_bytes;
     MLA_HIP(launch_gemm(g, st), "q up-projection");
   }
   MLA_HIP(launch_rope(c.dtype, q + (size_t)dn * es, M, M, (int64_t)H * M * dqk, dqk, H,
@@ -706,6 +720,8 @@ mla_status mla_prefill_chunk(const mla_config *cfg, const mla_weights *w, const 
     g.nseg = 2;
     g.seg[0] = GemmSeg{w->w_up_k, rkv, 0, kn, dn, dn, 0};
     g.seg[1] = GemmSeg{w->w_up_v, rkv, H * dn, v, dv, dv, 0, 1};
+    g.workspace = ws + p.off_gemm;
+    g.workspace_bytes = p.gemm_bytes;
     MLA_HIP(launch_gemm(g, st), "kv up-projection");
   }
   {
@@ -738,6 +754,8 @@ mla_status mla_prefill_chunk(const mla_config *cfg, const mla_weights *w, const 
     g.H = 1;
     g.nseg = 1;
     g.seg[0] = GemmSeg{w->wo, (int64_t)H * dv, 0, y, D, D, 0};
+    g.workspace = ws + p.off_gemm;
+    g.workspace_bytes = p.gemm_bytes;
     MLA_HIP(launch_gemm(g, st), "output projection");
   }
   return MLA_OK;
