@@ -701,6 +701,20 @@ size_t gemm_scratch_bytes(int dtype, int M, int N, int K, int batch) {
   return nsplit > 1 ? (size_t)nsplit * batch * M * N * sizeof(float) : 0;
 }
 
+// Compute units of the current device (one resident large-tile workgroup each).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // A big-kernel tile must not mix row-major and channel-major column ranges.
 static bool tr_aligned(const GemmDesc &d, int bn) {
   for (int i = 1; i < d.nseg; ++i)
@@ -738,7 +752,16 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
              d.N % 8 == 0 && (int64_t)d.M * d.lda < (1LL << 31);
   for (int i = 0; i < d.nseg && big; ++i)
     big = d.seg[i].n_begin % 16 == 0 && (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
-  if (big && tr_aligned(d, BigTile<4, 4, GB_STAGES>::N)) return launch_big<4, 4>(p, d, 0, d.N, st);
+  if (big && tr_aligned(d, BigTile<4, 4, GB_STAGES>::N)) {
+    // A product whose 256x256 tiles would leave most CUs idle in its only
+    // round (the down projection: 144 tiles) runs as 192x192 tiles, which
+    // fill one round (242 tiles) at a somewhat lower efficiency per tile.
+    const int cus = device_cus();
+    const int64_t t256 = (int64_t)((d.M + 255) / 256) * ((d.N + 255) / 256);
+    const int64_t t192 = (int64_t)((d.M + 191) / 192) * ((d.N + 191) / 192);
+    if (10 * t256 <= 6 * cus && t192 <= cus && tr_aligned(d, 192)) return launch_big<3, 3>(p, d, 0, d.N, st);
+    return launch_big<4, 4>(p, d, 0, d.N, st);
+  }
   bool skinny = d.dtype == BF16 && !d.b_kn && d.M <= SK_MMAX && d.K % SK_K == 0 && d.N % 8 == 0 &&
                 d.batch * ((d.M + SK_M - 1) / SK_M) <= 65535;
   for (int i = 0; i < d.nseg && skinny; ++i) skinny = d.seg[i].n_begin % SK_N == 0;
