@@ -1,0 +1,138 @@
+"""Plain float64 oracle of block-scaled FP8 (E4M3) projection products.
+
+TEST INFRASTRUCTURE ONLY -- never on the product path.  Slow and obvious on
+purpose: the format is decoded from its bit fields, the encoder rounds by the
+definition, and the product is one float64 matrix multiply of the decoded,
+scaled operands.
+
+Source: the "Deep Seek V3" notes (knlb.dev), section "infrastructure", the
+FP8 bullets: quantisation is fine grained (tile-wise for activations,
+block-wise for weights), the scales come online from the maxima of each tile
+or block, every tensor uses E4M3, the products accumulate at a precision above
+FP8, and attention, normalisation, embedding and output head stay in higher
+precision.
+
+Readings where the notes are silent (each is listed in the design notes):
+
+* E4M3 is the OCP 8-bit E4M3 format: sign, 4 exponent bits with bias 7, 3
+  mantissa bits, subnormals at exponent field 0, no infinities, NaN only for
+  the all-ones exponent and mantissa, largest finite value 448.
+* Encoding rounds to the nearest representable value, ties to the even
+  mantissa.  The scaled inputs never exceed 448, so no saturation rule is
+  needed (the encoder rejects larger magnitudes).
+* Activation tiles are 1 x 128 along the reduction axis (one scale per row per
+  128 columns); weight blocks are 128 x 128 (one scale per 128 output rows per
+  128 reduction columns; a partial last row block keeps its own scale).
+* A scale is a power of two 2^e: the smallest one with amax <= 448 * 2^e,
+  e = 0 for an all-zero tile, e clamped to [-127, 127].  Dividing by it is
+  exact, and it is what the matrix cores apply as a block exponent.
+* The product is C[m, n] = sum_k dec(qa[m, k]) 2^ea[m, k // 128]
+  * dec(qb[n, k]) 2^eb[n // 128, k // 128], the reduction length a multiple
+  of 128.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+TILE = 128
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 byte from its fields (float64; NaN for 0x7F/0xFF)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.ldexp(1.0, e - 7)
+    sub = (m / 8.0) * np.ldexp(1.0, -6)
+    v = np.where(e == 0, sub, normal)
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return sign * v
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 byte of each value (ties to even mantissa); |x| <= 448."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)) or np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("e4m3_encode takes finite values of magnitude <= 448")
+    a = np.abs(x)
+    # spacing of the grid around a: 2^(E-3) in the binade [2^E, 2^(E+1)),
+    # 2^-9 below the smallest normal 2^-6
+    _, ex = np.frexp(a)                      # a = f 2^ex, f in [0.5, 1)
+    E = np.maximum(ex - 1, -6)
+    q = np.ldexp(1.0, E - 3)
+    n = np.rint(a / q)                       # round half to even on the grid
+    v = n * q                                # rounded magnitude (exact)
+    # fields of the rounded magnitude (a carry into the next binade is
+    # handled by re-reading its exponent)
+    _, ev = np.frexp(v)
+    Ev = ev - 1
+    is_sub = (v < 2.0 ** -6)
+    mant_sub = np.rint(v / 2.0 ** -9)
+    mant_norm = np.rint(v / np.ldexp(1.0, Ev) * 8.0) - 8.0
+    efield = np.where(is_sub, 0, Ev + 7)
+    mfield = np.where(is_sub, mant_sub, mant_norm)
+    code = (efield.astype(np.int64) << 3) | mfield.astype(np.int64)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def block_exponent(amax) -> np.ndarray:
+    """Smallest e with amax <= 448 * 2^e (e = 0 where amax == 0), in [-127, 127]."""
+    a = np.asarray(amax, dtype=np.float64)
+    f, ex = np.frexp(a)                      # a = f 2^ex; 448 = 0.875 * 2^9
+    e = ex - 9 + (f > 0.875)
+    e = np.where(a == 0, 0, e)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def quantize_act_tiles(x):
+    """1 x 128 tiles along the last axis of x [M, K] -> (codes [M, K] uint8,
+    exponents [M, K/128] int64)."""
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
+    if K % TILE:
+        raise ValueError("the reduction length must be a multiple of 128")
+    t = x.reshape(M, K // TILE, TILE)
+    e = block_exponent(np.abs(t).max(axis=2))
+    codes = e4m3_encode(t * np.ldexp(1.0, -e)[:, :, None])
+    return codes.reshape(M, K), e
+
+
+def quantize_weight_blocks(w):
+    """128 x 128 blocks of w [N, K] -> (codes [N, K] uint8,
+    exponents [ceil(N/128), K/128] int64)."""
+    w = np.asarray(w, dtype=np.float64)
+    N, K = w.shape
+    if K % TILE:
+        raise ValueError("the reduction length must be a multiple of 128")
+    nb = (N + TILE - 1) // TILE
+    e = np.zeros((nb, K // TILE), dtype=np.int64)
+    codes = np.zeros((N, K), dtype=np.uint8)
+    for i in range(nb):
+        rows = w[i * TILE:(i + 1) * TILE]
+        blk = rows.reshape(rows.shape[0], K // TILE, TILE)
+        e[i] = block_exponent(np.abs(blk).max(axis=(0, 2)))
+        codes[i * TILE:(i + 1) * TILE] = e4m3_encode(
+            blk * np.ldexp(1.0, -e[i])[None, :, None]).reshape(rows.shape[0], K)
+    return codes, e
+
+
+def dequant_act(codes, e):
+    """Float64 values of 1 x 128 tiles: dec(code) * 2^e of the tile."""
+    v = e4m3_decode(codes)
+    return v * np.repeat(np.ldexp(1.0, e), TILE, axis=1)
+
+
+def dequant_weight(codes, e):
+    """Float64 values of 128 x 128 blocks: dec(code) * 2^e of the block."""
+    v = e4m3_decode(codes)
+    s = np.repeat(np.repeat(np.ldexp(1.0, e), TILE, axis=0), TILE, axis=1)
+    return v * s[:v.shape[0]]
+
+
+def fp8_gemm(qa, ea, qb, eb):
+    """C [M, N] = dequant_act(qa, ea) @ dequant_weight(qb, eb)^T in float64."""
+    return dequant_act(qa, ea) @ dequant_weight(qb, eb).T
