@@ -43,14 +43,14 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "e6f7c0c3c3a254ee5dc9798fa33e0c4b5fe779b8a2adddd13e8cf20aff1c436f",
-        "FETCH_SIZE_KiB": 242944.8, "WRITE_SIZE_KiB": 131082.4},
+        "sha256": "0e9438f1315ae3e8eb9c0023bb8457e1e1b6950a71cc0b4130dc0ad4b7fc53d3",
+        "FETCH_SIZE_KiB": 243055.7, "WRITE_SIZE_KiB": 131081.3},
     "out_proj": {
-        "sha256": "d537eff19631999026f4b08112d91190435570d189ecb2c29b0c543e125a7c7a",
-        "FETCH_SIZE_KiB": 1515856.5, "WRITE_SIZE_KiB": 57792.0},
+        "sha256": "a8fac6ab25a9c62a92e8d69d03f2877ccf9f303fbadbecc023cf1d3d8e2687f8",
+        "FETCH_SIZE_KiB": 1518804.9, "WRITE_SIZE_KiB": 57792.0},
     "latent_attention": {
-        "sha256": "028af137d69e026b2a01b548c26796f76083073cf5bd131b255170a64222b415",
-        "FETCH_SIZE_KiB": 181370.4, "WRITE_SIZE_KiB": 76843.0},
+        "sha256": "6633b345c200ec6e88bcbed0abddfcc2568c1c47c2c189a1d5ad0e0f44568c8d",
+        "FETCH_SIZE_KiB": 181371.0, "WRITE_SIZE_KiB": 76843.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
