@@ -18,6 +18,10 @@ from .mla import (  # noqa: F401
     mla_decode_multi_workspace_size,
     mla_decode_layout_of,
     mla_decode_workspace_size,
+    mla_fp8_gemm,
+    mla_fp8_quantize_blocks,
+    mla_fp8_quantize_rows,
+    mla_fp8_scale_pitch,
     mla_prefill_chunk,
     mla_prefill_chunk_workspace_size,
     mla_prefill_forward,

@@ -95,6 +95,19 @@ hipError_t launch_chunk_index(const int32_t *lens, int B, int q_len, int64_t cap
 hipError_t launch_gather_keys(int dtype, void *dst, int64_t n_rows, const void *cache, int64_t cap,
                               int width, const int32_t *kofs, int B, hipStream_t st);
 
+// Block-scaled FP8 (E4M3 codes, E8M0 scale bytes stored [cols/128][ld_s], one
+// per row): 1 x 128 activation tiles, 128 x 128 weight blocks (the block's
+// byte repeated on each of its rows), and C = (A 2^sa)(B 2^sb)^T with A
+// [M, K], B [N, K] bytes, scales padded to fp8_scale_pitch rows.
+hipError_t launch_fp8_quant_rows(int dtype, const void *x, int64_t rows, int64_t cols, int64_t ldx, uint8_t *q,
+                                 int64_t ldq, uint8_t *sexp, int64_t ld_s, hipStream_t st);
+hipError_t launch_fp8_quant_blocks(int dtype, const void *w, int64_t rows, int64_t cols, int64_t ldw, uint8_t *q,
+                                   int64_t ldq, uint8_t *sexp, int64_t ld_s, hipStream_t st);
+hipError_t launch_fp8_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int64_t ld_sa, const uint8_t *b,
+                           int64_t ldb, const uint8_t *sb, int64_t ld_sb, void *c, int c_dtype, int64_t ldc, int M,
+                           int N, int K, hipStream_t st);
+int64_t fp8_scale_pitch(int64_t rows);
+
 hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src,
                             int64_t lds, int64_t rows, int width,
                             hipStream_t st);

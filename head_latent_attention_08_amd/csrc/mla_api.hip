@@ -993,6 +993,74 @@ mla_status mla_decode_absorbed_multi(const mla_config *cfg, const mla_weights *w
                      workspace, workspace_bytes, hip_stream);
 }
 
+int64_t mla_fp8_scale_pitch(int64_t rows) { return rows < 0 ? -1 : fp8_scale_pitch(rows); }
+
+static mla_status check_fp8_quant(const void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                  const uint8_t *q, int64_t ldq, const uint8_t *sexp, int64_t ld_sexp,
+                                  int64_t q_align) {
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "dtype %d is neither 0 (fp32) nor 1 (bf16)", dtype);
+  if (rows < 0 || rows > (1 << 24)) return fail(MLA_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^24]");
+  if (cols < 128 || cols % 128 || cols > (1 << 24))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 128 (at most 2^24)");
+  if (ldx < cols || ldq < cols) return fail(MLA_ERR_INVALID_ARGUMENT, "ldx and ldq must be >= cols");
+  if (ld_sexp < rows) return fail(MLA_ERR_INVALID_ARGUMENT, "ld_sexp must be >= rows");
+  if (ldq % q_align) return fail(MLA_ERR_INVALID_ARGUMENT, "ldq must be a multiple of %lld", (long long)q_align);
+  if (rows == 0) return MLA_OK;
+  if (!x || !q || !sexp) return fail(MLA_ERR_INVALID_ARGUMENT, "x, q and sexp must not be NULL");
+  if ((uintptr_t)x % dtype_size(dtype)) return fail(MLA_ERR_INVALID_ARGUMENT, "x is not aligned to its element size");
+  if ((uintptr_t)q % q_align) return fail(MLA_ERR_INVALID_ARGUMENT, "q must be %lld-byte aligned", (long long)q_align);
+  return MLA_OK;
+}
+
+mla_status mla_fp8_quantize_rows(const void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ldx, uint8_t *q,
+                                 int64_t ldq, uint8_t *sexp, int64_t ld_sexp, void *hip_stream) {
+  mla_status s = check_fp8_quant(x, dtype, rows, cols, ldx, q, ldq, sexp, ld_sexp, 2);
+  if (s != MLA_OK || rows == 0) return s;
+  MLA_HIP(launch_fp8_quant_rows(dtype, x, rows, cols, ldx, q, ldq, sexp, ld_sexp, (hipStream_t)hip_stream),
+          "fp8 quantize rows");
+  return MLA_OK;
+}
+
+mla_status mla_fp8_quantize_blocks(const void *w, int32_t dtype, int64_t rows, int64_t cols, int64_t ldw,
+                                   uint8_t *q, int64_t ldq, uint8_t *sexp, int64_t ld_sexp, void *hip_stream) {
+  mla_status s = check_fp8_quant(w, dtype, rows, cols, ldw, q, ldq, sexp, ld_sexp, 16);
+  if (s != MLA_OK || rows == 0) return s;
+  MLA_HIP(launch_fp8_quant_blocks(dtype, w, rows, cols, ldw, q, ldq, sexp, ld_sexp, (hipStream_t)hip_stream),
+          "fp8 quantize blocks");
+  return MLA_OK;
+}
+
+mla_status mla_fp8_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int64_t ld_sa, const uint8_t *b,
+                        int64_t ldb, const uint8_t *sb, int64_t ld_sb, void *c, int32_t c_dtype, int64_t ldc,
+                        int64_t M, int64_t N, int64_t K, void *hip_stream) {
+  if (c_dtype != MLA_DTYPE_F32 && c_dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "c_dtype %d is neither 0 (fp32) nor 1 (bf16)", c_dtype);
+  if (M < 0 || M > (1 << 24) || N < 1 || N > (1 << 24))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "M must be in [0, 2^24] and N in [1, 2^24]");
+  if (K < 128 || K % 128 || K > (1 << 24))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "K must be a positive multiple of 128 (at most 2^24)");
+  if (lda < K || ldb < K || lda % 16 || ldb % 16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "lda and ldb must be >= K and multiples of 16");
+  if (ld_sa < fp8_scale_pitch(M) || ld_sb < fp8_scale_pitch(N) || ld_sa % 4 || ld_sb % 4)
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "ld_sa / ld_sb must be multiples of 4 and at least mla_fp8_scale_pitch(M) / (N)");
+  if (ldc < N) return fail(MLA_ERR_INVALID_ARGUMENT, "ldc must be >= N");
+  if (c_dtype == MLA_DTYPE_BF16 && (N % 8 || ldc % 8))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "bf16 C needs N and ldc multiples of 8");
+  if (M == 0) return MLA_OK;
+  if (!a || !b || !sa || !sb || !c) return fail(MLA_ERR_INVALID_ARGUMENT, "a, sa, b, sb and c must not be NULL");
+  if ((uintptr_t)a % 16 || (uintptr_t)b % 16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a and b must be 16-byte aligned");
+  if ((uintptr_t)sa % 4 || (uintptr_t)sb % 4) return fail(MLA_ERR_INVALID_ARGUMENT, "sa and sb must be 4-byte aligned");
+  if ((uintptr_t)c % (c_dtype == MLA_DTYPE_BF16 ? 16 : 4))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "c is not aligned (16 bytes for bf16, 4 for fp32)");
+  MLA_HIP(launch_fp8_gemm(a, lda, sa, ld_sa, b, ldb, sb, ld_sb, c, c_dtype == MLA_DTYPE_F32 ? F32 : BF16, ldc,
+                          (int)M, (int)N, (int)K, (hipStream_t)hip_stream),
+          "fp8 gemm");
+  return MLA_OK;
+}
+
 mla_status mla_rope_apply(void *x, int32_t dtype, int64_t n_tokens, int32_t n_heads,
                           int32_t rope_dim, int64_t token_stride, int64_t head_stride,
                           const int32_t *positions, const mla_rope_params *params,

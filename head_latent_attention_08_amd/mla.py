@@ -115,6 +115,13 @@ def load_library(path: str = LIB_PATH):
                                               i64, i64, P, i64, P, P, P, ctypes.c_size_t, P]
     lib.mla_rope_apply.argtypes = [P, ctypes.c_int32, i64, ctypes.c_int32, ctypes.c_int32, i64,
                                    i64, P, ctypes.POINTER(RopeParams), P]
+    lib.mla_fp8_scale_pitch.argtypes = [i64]
+    lib.mla_fp8_scale_pitch.restype = i64
+    lib.mla_fp8_quantize_rows.argtypes = [P, ctypes.c_int32, i64, i64, i64, P, i64, P, i64, P]
+    lib.mla_fp8_quantize_blocks.argtypes = [P, ctypes.c_int32, i64, i64, i64, P, i64, P, i64, P]
+    lib.mla_fp8_gemm.argtypes = [P, i64, P, i64, P, i64, P, i64, P, ctypes.c_int32, i64, i64, i64, i64, P]
+    for fn in ("mla_fp8_quantize_rows", "mla_fp8_quantize_blocks", "mla_fp8_gemm"):
+        getattr(lib, fn).restype = st
     for fn in ("mla_prefill_workspace_size", "mla_prefill_layout_of", "mla_prefill_forward",
                "mla_prefill_varlen_workspace_size", "mla_prefill_varlen_forward",
                "mla_prefill_chunk_workspace_size", "mla_prefill_chunk",
@@ -401,6 +408,54 @@ def mla_prefill_chunk(cfg: MlaConfig, weights: dict, x: torch.Tensor, latent_cac
         max_keys, _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return y, workspace
+
+
+def mla_fp8_scale_pitch(rows: int) -> int:
+    """Row pitch of the scale bytes that mla_fp8_gemm takes for `rows` rows."""
+    return int(load_library().mla_fp8_scale_pitch(rows))
+
+
+def _fp8_quantize(fn, x: torch.Tensor, q_align: int, stream):
+    if x.dim() != 2 or x.stride(-1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a device [rows, cols] tensor with unit last stride")
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[x.dtype]
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    pitch = mla_fp8_scale_pitch(rows)
+    sexp = torch.empty((max(cols // 128, 1), pitch), dtype=torch.uint8, device=x.device)
+    _check(fn(_ptr(x), dt, rows, cols, x.stride(0), _ptr(q), q.stride(0), _ptr(sexp), pitch, _stream(stream)))
+    return q, sexp
+
+
+def mla_fp8_quantize_rows(x: torch.Tensor, stream=None):
+    """1 x 128 activation tiles of x [rows, cols] (fp32/bf16) -> (codes uint8
+    [rows, cols], scale bytes uint8 [cols / 128, mla_fp8_scale_pitch(rows)])."""
+    return _fp8_quantize(load_library().mla_fp8_quantize_rows, x, 2, stream)
+
+
+def mla_fp8_quantize_blocks(w: torch.Tensor, stream=None):
+    """128 x 128 weight blocks of w [rows, cols] -> (codes, scale bytes), the
+    block's byte repeated on each of its rows."""
+    return _fp8_quantize(load_library().mla_fp8_quantize_blocks, w, 16, stream)
+
+
+def mla_fp8_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+                 out_dtype=torch.bfloat16, c: Optional[torch.Tensor] = None, stream=None):
+    """C [M, N] = block-scaled a [M, K] times block-scaled b [N, K] transposed."""
+    for t in (a, sa, b, sb):
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.stride(-1) != 1 or not t.is_cuda:
+            raise ValueError("a, sa, b and sb must be device uint8 matrices with unit last stride")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or sa.shape[0] * 128 < K or sb.shape[0] * 128 < K:
+        raise ValueError("inner dimensions do not match")
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[c.dtype]
+    _check(load_library().mla_fp8_gemm(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(b), b.stride(0),
+                                       _ptr(sb), sb.stride(0), _ptr(c), dt, c.stride(0), M, N, K,
+                                       _stream(stream)))
+    return c
 
 
 def mla_rope_apply(x: torch.Tensor, positions: torch.Tensor, params: RopeParams, stream=None):

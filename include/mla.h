@@ -285,6 +285,65 @@ MLA_API mla_status mla_rope_apply(void *x, int32_t dtype, int64_t n_tokens,
                           const int32_t *positions,
                           const mla_rope_params *params, void *hip_stream);
 
+/* ------------------------------------------------------------------- FP8
+ * Block-scaled FP8 projection products, after the FP8 scheme of the "Deep
+ * Seek V3" notes (section "infrastructure", the FP8 bullets): fine-grained
+ * quantisation, tile-wise for activations and block-wise for weights, scales
+ * from the maxima of each tile, E4M3 for every tensor, accumulation above FP8
+ * precision.
+ *
+ * Codes are OCP E4M3 bytes (bias 7, largest finite 448).  A tile's scale is
+ * the power of two 2^e, e the smallest with amax <= 448 * 2^e (e = 0 for an
+ * all-zero tile, clamped to [-127, 127]); its codes are x / 2^e rounded to
+ * nearest, ties to even.  Scales are stored as E8M0 bytes (value
+ * 2^(byte - 127)) in k-block-major order: the byte of row r for columns
+ * [128 kb, 128 kb + 128) sits at sexp[kb * ld_sexp + r], one byte per row
+ * (a weight block's byte is repeated on each of its rows).  Non-finite
+ * inputs give unspecified codes.  All pointers are device pointers; the
+ * caller owns every buffer; the calls are asynchronous on hip_stream. */
+
+/* Rows rounded up to a multiple of 256: the smallest ld_sa / ld_sb that
+ * mla_fp8_gemm accepts for that many rows (returns -1 for rows < 0). */
+MLA_API int64_t mla_fp8_scale_pitch(int64_t rows);
+
+/* Activation tiles: 1 x 128 tiles of x [rows, cols] (dtype fp32 or bf16,
+ * row pitch ldx elements) -> codes q [rows, cols] (row pitch ldq bytes) and
+ * scale bytes sexp [cols / 128][ld_sexp].
+ * Status: INVALID_ARGUMENT for NULL pointers (rows > 0), rows < 0, cols not
+ * a positive multiple of 128, ldx < cols, ldq < cols, ldq odd, q not 2-byte
+ * aligned, ld_sexp < rows, rows > 2^24, x not aligned to its element size or
+ * a bad dtype. */
+MLA_API mla_status mla_fp8_quantize_rows(const void *x, int32_t dtype, int64_t rows, int64_t cols,
+                                 int64_t ldx, uint8_t *q, int64_t ldq, uint8_t *sexp,
+                                 int64_t ld_sexp, void *hip_stream);
+
+/* Weight blocks: 128 x 128 blocks of w [rows, cols] (rows = output
+ * channels, cols = reduction; a partial last row block has its own scale)
+ * -> codes q [rows, cols] and sexp [cols / 128][ld_sexp] (the block's byte on
+ * each of its rows).
+ * Status: INVALID_ARGUMENT as for mla_fp8_quantize_rows, except that ldq
+ * must be a multiple of 16 and q 16-byte aligned. */
+MLA_API mla_status mla_fp8_quantize_blocks(const void *w, int32_t dtype, int64_t rows, int64_t cols,
+                                   int64_t ldw, uint8_t *q, int64_t ldq, uint8_t *sexp,
+                                   int64_t ld_sexp, void *hip_stream);
+
+/* C [M, N] = sum_k A[m, k] 2^(sa(m, k/128) - 127) B[n, k] 2^(sb(n, k/128) - 127),
+ * fp32 accumulation, C written as c_dtype (fp32 or bf16) with row pitch ldc
+ * elements.  a [M, K] and b [N, K] are E4M3 codes with row pitches lda and
+ * ldb bytes (nn.Linear order: y = x W^T); sa [K / 128][ld_sa] and
+ * sb [K / 128][ld_sb] are scale bytes as written by the quantisers.  Scale
+ * rows past M (N) up to the pitch are read but never affect C.
+ * Status: INVALID_ARGUMENT for NULL pointers (M > 0), M < 0, N < 1, M or N
+ * above 2^24, K not a positive multiple of 128, lda or ldb below K or not a
+ * multiple of 16, a or b not 16-byte aligned, ld_sa < mla_fp8_scale_pitch(M),
+ * ld_sb < mla_fp8_scale_pitch(N), ld_sa / ld_sb not a multiple of 4, sa / sb
+ * not 4-byte aligned, ldc < N, a bad c_dtype; for bf16 C also N or ldc not a
+ * multiple of 8 or c not 16-byte aligned; for fp32 C, c not 4-byte aligned. */
+MLA_API mla_status mla_fp8_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int64_t ld_sa,
+                        const uint8_t *b, int64_t ldb, const uint8_t *sb, int64_t ld_sb,
+                        void *c, int32_t c_dtype, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                        void *hip_stream);
+
 /* ---------------------------------------------------------- measurement
  * While set, every mla_prefill_forward / mla_decode_absorbed call made on
  * this thread records events[k] (hipEvent_t handles the caller created) on

@@ -147,3 +147,25 @@ def sample_rows(c: dict, seq: int):
     rows = set(rng.choice(seq, size=n, replace=False).tolist())
     rows |= {r for r in (0, 4095, 4096, seq - 1) if r < seq}
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def make_fp8_operands(M: int, N: int, K: int, seed: int, *, spread: bool = True,
+                      w_std: float = 0.006):
+    """Operands of one block-scaled FP8 projection product, as bf16 values.
+
+    x [M, K] ~ N(0, 1) (an activation such as the attention output feeding the
+    output projection) and w [N, K] ~ N(0, w_std^2) (nn.Linear weight).  With
+    spread, every 1 x 128 tile of x is multiplied by 2^u, u ~ U{-6..6}, and
+    every 128 x 128 block of w by 2^v, v ~ U{-4..4}, so that tiles and blocks
+    carry different scales.  Drawn in the order x, w, tile exponents, block
+    exponents; rounded once to bf16 (returned as float32)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    w = (rng.standard_normal((N, K), dtype=np.float32) * np.float32(w_std))
+    if spread:
+        u = rng.integers(-6, 7, (M, K // 128))
+        v = rng.integers(-4, 5, ((N + 127) // 128, K // 128))
+        x = x * np.repeat(np.ldexp(np.float32(1), u), 128, axis=1).astype(np.float32)
+        wv = np.repeat(np.repeat(np.ldexp(np.float32(1), v), 128, axis=0), 128, axis=1)[:N]
+        w = w * wv.astype(np.float32)
+    return round_bf16(x), round_bf16(w)

@@ -214,3 +214,39 @@ def test_error_message_is_per_thread():
     t.join()
     assert seen == [b""]
     assert b"hidden_size" in lib.mla_last_error()
+
+
+def test_fp8_arguments_rejected_without_launch():
+    lib = m.load_library()
+    P = ctypes.c_void_p
+    fake = P(1 << 40)          # never dereferenced: every case fails validation first
+    assert lib.mla_fp8_scale_pitch(1) == 256 and lib.mla_fp8_scale_pitch(256) == 256
+    assert lib.mla_fp8_scale_pitch(257) == 512 and lib.mla_fp8_scale_pitch(-1) == -1
+    INV = 1
+    q = lib.mla_fp8_quantize_rows
+    assert q(fake, 1, 4, 100, 128, fake, 128, fake, 256, None) == INV        # cols % 128
+    assert q(fake, 2, 4, 128, 128, fake, 128, fake, 256, None) == INV        # dtype
+    assert q(fake, 1, 4, 128, 100, fake, 128, fake, 256, None) == INV        # ldx < cols
+    assert q(fake, 1, 4, 128, 128, fake, 129, fake, 256, None) == INV        # odd ldq
+    assert q(fake, 1, 300, 128, 128, fake, 128, fake, 256, None) == INV      # ld_sexp < rows
+    assert q(None, 1, 4, 128, 128, fake, 128, fake, 256, None) == INV        # NULL x
+    assert q(P(3), 1, 4, 128, 128, fake, 128, fake, 256, None) == INV        # misaligned x
+    assert q(fake, 1, -1, 128, 128, fake, 128, fake, 256, None) == INV
+    assert q(None, 1, 0, 128, 128, None, 128, None, 256, None) == 0          # empty: no launch
+    assert lib.mla_fp8_quantize_blocks(fake, 1, 4, 128, 128, fake, 136, fake, 256, None) == INV  # ldq % 16
+    assert lib.mla_fp8_quantize_blocks(fake, 1, 4, 128, 128, P((1 << 40) + 8), 128, fake, 256, None) == INV
+    g = lib.mla_fp8_gemm
+    ok = dict(a=fake, lda=512, sa=fake, ld_sa=256, b=fake, ldb=512, sb=fake, ld_sb=256, c=fake,
+              c_dtype=1, ldc=256, M=100, N=256, K=512)
+    def call(**over):
+        d = dict(ok, **over)
+        return g(d["a"], d["lda"], d["sa"], d["ld_sa"], d["b"], d["ldb"], d["sb"], d["ld_sb"],
+                 d["c"], d["c_dtype"], d["ldc"], d["M"], d["N"], d["K"], None)
+    for over in (dict(K=320), dict(K=0), dict(lda=500), dict(ldb=520), dict(lda=256),
+                 dict(ld_sa=128), dict(ld_sb=252), dict(ld_sa=258), dict(M=-1), dict(N=0),
+                 dict(N=252, ldc=256), dict(ldc=250), dict(c_dtype=3), dict(a=None), dict(sb=None),
+                 dict(a=P((1 << 40) + 8)), dict(sa=P((1 << 40) + 2)), dict(c=P((1 << 40) + 4)),
+                 dict(M=(1 << 24) + 1), dict(N=300, ld_sb=512, ldc=300)):
+        assert call(**over) == INV, over
+        assert lib.mla_last_error()
+    assert call(M=0, a=None, sa=None, b=None, sb=None, c=None) == 0
