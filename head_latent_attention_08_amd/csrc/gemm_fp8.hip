@@ -293,25 +293,60 @@ __device__ inline int f8_tile_exponent(float amax) {
 
 template <typename T> __device__ inline float f8_ld(const T *p) { return (float)*p; }
 
-// 1 x 128 activation tiles: one wave per (row, tile), two values per lane.
+// 1 x 128 activation tiles: a wave takes four consecutive tiles of a row,
+// 16 lanes per tile and 8 consecutive values per lane (16-byte loads and
+// 8-byte code stores when `vec`; element accesses otherwise).
 template <typename T>
 __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const T *x, int64_t rows, int64_t ldx, int tiles,
                                                              uint8_t *q, int64_t ldq, uint8_t *sexp,
-                                                             int64_t lds_) {
+                                                             int64_t lds_, int vec) {
+  const int groups = (tiles + 3) / 4;
   const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (w >= rows * tiles) return;
-  const int64_t row = w / tiles;
-  const int kb = (int)(w - row * tiles);
-  const T *src = x + row * ldx + kb * F8_TILE + 2 * lane;
-  const float v0 = f8_ld(src), v1 = f8_ld(src + 1);
-  float amax = fmaxf(fabsf(v0), fabsf(v1));
+  if (w >= rows * groups) return;
+  const int64_t row = w / groups;
+  const int kb = (int)(w - row * groups) * 4 + (lane >> 4);
+  const bool live = kb < tiles;
+  const int64_t col = (int64_t)kb * F8_TILE + 8 * (lane & 15);
+  float v[8];
+  if (live && vec) {
+    if constexpr (sizeof(T) == 2) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(x + row * ldx + col);
+      const bf16 *h = reinterpret_cast<const bf16 *>(&u);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+      for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+    } else {
+      const float4 u0 = *reinterpret_cast<const float4 *>(x + row * ldx + col);
+      const float4 u1 = *reinterpret_cast<const float4 *>(x + row * ldx + col + 4);
+      v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+      v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = live ? f8_ld(x + row * ldx + col + i) : 0.f;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));   // within the 16-lane tile
   const int e = f8_tile_exponent(amax);
-  const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v0, -e), ldexpf(v1, -e), 0, false);
-  *reinterpret_cast<uint16_t *>(q + row * ldq + kb * F8_TILE + 2 * lane) = (uint16_t)(packed & 0xffff);
-  if (lane == 0) sexp[(int64_t)kb * lds_ + row] = (uint8_t)(e + 127);
+  uint32_t pk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * i], -e), ldexpf(v[4 * i + 1], -e), 0, false);
+    pk[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * i + 2], -e), ldexpf(v[4 * i + 3], -e), lo, true);
+  }
+  if (!live) return;
+  uint8_t *dst = q + row * ldq + col;
+  if (vec) {
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(pk[0], pk[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      reinterpret_cast<uint16_t *>(dst)[i] = (uint16_t)(pk[i >> 1] >> (16 * (i & 1)));
+  }
+  if ((lane & 15) == 0) sexp[(int64_t)kb * lds_ + row] = (uint8_t)(e + 127);
 }
 
 // 128 x 128 weight blocks: one workgroup per block, thread t takes row t / 2
@@ -357,15 +392,17 @@ __global__ __launch_bounds__(256) void fp8_quant_blocks_kernel(const T *w, int64
 hipError_t launch_fp8_quant_rows(int dtype, const void *x, int64_t rows, int64_t cols, int64_t ldx, uint8_t *q,
                                  int64_t ldq, uint8_t *sexp, int64_t ld_s, hipStream_t st) {
   const int tiles = (int)(cols / F8_TILE);
-  const int64_t waves = rows * tiles;
+  const int64_t waves = rows * ((tiles + 3) / 4);
   if (waves == 0) return hipSuccess;
   const dim3 grid((unsigned)((waves + 3) / 4));
+  const size_t es = dtype == BF16 ? 2 : 4;
+  const int vec = ((uintptr_t)x % 16 == 0 && (ldx * es) % 16 == 0 && (uintptr_t)q % 8 == 0 && ldq % 8 == 0) ? 1 : 0;
   if (dtype == BF16)
     hipLaunchKernelGGL(fp8_quant_rows_kernel<bf16>, grid, dim3(256), 0, st, reinterpret_cast<const bf16 *>(x), rows,
-                       ldx, tiles, q, ldq, sexp, ld_s);
+                       ldx, tiles, q, ldq, sexp, ld_s, vec);
   else
     hipLaunchKernelGGL(fp8_quant_rows_kernel<float>, grid, dim3(256), 0, st, reinterpret_cast<const float *>(x),
-                       rows, ldx, tiles, q, ldq, sexp, ld_s);
+                       rows, ldx, tiles, q, ldq, sexp, ld_s, vec);
   return hipGetLastError();
 }
 

@@ -169,3 +169,17 @@ def test_gemm_is_deterministic():
     c2 = m.mla_fp8_gemm(qa, sa, qb, sb)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_rows_unaligned_view(dtype):
+    # a column window starting two elements in: element-wise loads and stores
+    m = _m()
+    rows, cols = 70, 640
+    x, _ = si.make_fp8_operands(rows, 8, cols + 128, seed=21)
+    xd = _dev(x, dtype)[:, 2:2 + cols]
+    q, s = m.mla_fp8_quantize_rows(xd)
+    torch.cuda.synchronize()
+    qo, eo = f8.quantize_act_tiles(x[:, 2:2 + cols].astype(np.float64))
+    np.testing.assert_array_equal(q.cpu().numpy(), qo)
+    np.testing.assert_array_equal(s.cpu().numpy()[:, :rows], (eo.T + 127).astype(np.uint8))
