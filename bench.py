@@ -40,17 +40,21 @@ KERNEL_SOURCES = {
     "attention": ["attn_prefill.hip", "common.h", "internal.h"],
     "out_proj": ["gemm.hip", "common.h", "internal.h"],
     "latent_attention": ["decode.hip", "common.h", "internal.h"],
+    "fp8_out_proj": ["gemm_fp8.hip", "common.h", "internal.h"],
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "0e9438f1315ae3e8eb9c0023bb8457e1e1b6950a71cc0b4130dc0ad4b7fc53d3",
-        "FETCH_SIZE_KiB": 243055.7, "WRITE_SIZE_KiB": 131081.3},
+        "sha256": "c1bd530c5f0b3d1d94f73cca343d3a97bb064a8292df1f946034872d12b57fa2",
+        "FETCH_SIZE_KiB": 242916.8, "WRITE_SIZE_KiB": 131082.4},
     "out_proj": {
-        "sha256": "a8fac6ab25a9c62a92e8d69d03f2877ccf9f303fbadbecc023cf1d3d8e2687f8",
-        "FETCH_SIZE_KiB": 1518804.9, "WRITE_SIZE_KiB": 57792.0},
+        "sha256": "8e13d80de7dfc8ece20b886d8ffc7603e09761089b3d30e634658613b7f7a0d4",
+        "FETCH_SIZE_KiB": 1528292.3, "WRITE_SIZE_KiB": 57792.0},
     "latent_attention": {
-        "sha256": "6633b345c200ec6e88bcbed0abddfcc2568c1c47c2c189a1d5ad0e0f44568c8d",
-        "FETCH_SIZE_KiB": 181371.0, "WRITE_SIZE_KiB": 76843.0},
+        "sha256": "1fd44c5350c01dac2d84027f4f481983719fe59c01dc4d7a0abc49db62f270ba",
+        "FETCH_SIZE_KiB": 181375.1, "WRITE_SIZE_KiB": 76843.0},
+    "fp8_out_proj": {
+        "sha256": "a767d8bbf35566a2dd1616b28a1cd5ad0b0e8555d78dd88607f8a44a1ce2452e",
+        "FETCH_SIZE_KiB": 380141.5, "WRITE_SIZE_KiB": 57344.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
@@ -160,6 +164,70 @@ def cpu_baseline(c_pre, x, w, c_dec, xd, wd, lens, cache, seconds_hint=True):
     }
 
 
+MI355X_FP8_TFLOPS = 2 * MI355X_BF16_TFLOPS  # dense E4M3 matrix-core peak
+
+
+def fp8_projections(m, S, log, reps=20):
+    """Block-scaled FP8 products at the prefill projection shapes (S tokens):
+    activation quantisation (1 x 128 tiles) plus the product, per projection,
+    timed with HIP events on the stream both run on.  Operands are seeded
+    device draws (activations N(0, 1), weights N(0, 0.006^2)); the weights
+    are quantised once, outside the timed region (they are static).  A
+    context line: the headline value stays the bf16 path."""
+    import torch
+    D, rq, rkv, dr, H, dn, dv = 7168, 1536, 512, 64, 128, 128, 128
+    shapes = {"down_proj": (S, rq + rkv + dr, D), "q_up_proj": (S, H * (dn + dr), rq),
+              "kv_up_proj": (S, H * (dn + dv), rkv), "out_proj": (S, D, H * dv)}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9000)
+    res, ops = {}, {}
+    for name, (M, N, K) in shapes.items():
+        x = torch.randn(M, K, device="cuda", dtype=torch.float32, generator=gen).to(torch.bfloat16)
+        w = (torch.randn(N, K, device="cuda", dtype=torch.float32, generator=gen) * 0.006).to(torch.bfloat16)
+        qb, sb = m.mla_fp8_quantize_blocks(w)
+        del w
+        qa, sa = m.mla_fp8_quantize_rows(x)
+        ops[name] = (x, qa, sa, qb, sb, torch.empty(M, N, device="cuda", dtype=torch.bfloat16))
+    st = torch.cuda.current_stream()
+    for _ in range(3):
+        for name in shapes:
+            x, qa, sa, qb, sb, c = ops[name]
+            m.mla_fp8_gemm(qa, sa, qb, sb, c=c)
+    torch.cuda.synchronize()
+    tot_q = tot_g = 0.0
+    for name, (M, N, K) in shapes.items():
+        x, qa, sa, qb, sb, c = ops[name]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(st)
+        for _ in range(reps):
+            m.mla_fp8_quantize_rows(x)
+        ev[1].record(st)
+        for _ in range(reps):
+            m.mla_fp8_gemm(qa, sa, qb, sb, c=c)
+        ev[2].record(st)
+        torch.cuda.synchronize()
+        q_ms, g_ms = ev[0].elapsed_time(ev[1]) / reps, ev[1].elapsed_time(ev[2]) / reps
+        fl = 2.0 * M * N * K
+        res[name] = {"M": M, "N": N, "K": K, "quant_ms": q_ms, "gemm_ms": g_ms,
+                     "gemm_tflops": fl / (g_ms * 1e-3) / 1e12,
+                     "frac_of_fp8_peak": fl / (g_ms * 1e-3) / 1e12 / MI355X_FP8_TFLOPS}
+        tot_q += q_ms
+        tot_g += g_ms
+        log(f"bench: fp8 {name} {M}x{N}x{K}: quant {q_ms * 1e3:.1f} us, product {g_ms * 1e3:.1f} us, "
+            f"{res[name]['gemm_tflops']:.0f} TFLOP/s")
+    o = ops["out_proj"]
+    M, N, K = shapes["out_proj"]
+    res["roofline"] = {"bound": "mfma", "kernel": "fp8_gemm_kernel (out_proj)",
+                       "achieved": res["out_proj"]["gemm_tflops"], "peak": MI355X_FP8_TFLOPS,
+                       "unit": "TFLOP/s", "frac": res["out_proj"]["frac_of_fp8_peak"],
+                       "traffic": traffic_bytes("fp8_out_proj"),
+                       "flops_per_launch": 2.0 * M * N * K, "ms_per_launch": res["out_proj"]["gemm_ms"]}
+    res["total_ms"] = {"quant": tot_q, "gemm": tot_g}
+    del ops, o
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +236,8 @@ def main():
     # default warm-up runs ~1.5 s of the same full steps
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the block-scaled FP8 projection products (context line)")
     ap.add_argument("--no-multi-token", action="store_true",
                     help="skip the multi-token decode lines (q_len 2 and 4)")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
@@ -401,6 +471,8 @@ def main():
                                 "tflops": c_fl / (c_ms * 1e-3) / 1e12, "gflop": c_fl / 1e9}
         log(f"bench: prefill chunk {Tc} tokens after {Lc} cached rows: {c_ms:.3f} ms, "
             f"{c_fl / (c_ms * 1e-3) / 1e12:.0f} TFLOP/s")
+    if not args.no_fp8:
+        out["fp8_projections"] = fp8_projections(m, S, log)
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on bounded samples")
         out["cpu_baseline"] = cpu_baseline(c_pre, x, w, c_dec, xdec, wdec, lens, cache)

@@ -183,3 +183,28 @@ def test_quantize_rows_unaligned_view(dtype):
     qo, eo = f8.quantize_act_tiles(x[:, 2:2 + cols].astype(np.float64))
     np.testing.assert_array_equal(q.cpu().numpy(), qo)
     np.testing.assert_array_equal(s.cpu().numpy()[:, :rows], (eo.T + 127).astype(np.uint8))
+
+
+def test_v3_out_projection_shape_sampled_rows():
+    # the product at the output projection's full size (4096 tokens,
+    # 7168 x 16384 weight), launched as the bench launches it (bf16 C): every
+    # weight code and scale byte against the oracle, activation codes and
+    # products on sampled rows
+    m = _m()
+    M, N, K = 4096, 7168, 16384
+    x, w = si.make_fp8_operands(M, N, K, seed=13)
+    qa, sa = m.mla_fp8_quantize_rows(_dev(x, "bf16"))
+    qb, sb = m.mla_fp8_quantize_blocks(_dev(w, "bf16"))
+    c = m.mla_fp8_gemm(qa, sa, qb, sb)
+    torch.cuda.synchronize()
+    qbo, ebo = f8.quantize_weight_blocks(w.astype(np.float64))
+    del w
+    np.testing.assert_array_equal(qb.cpu().numpy(), qbo)
+    np.testing.assert_array_equal(sb.cpu().numpy()[:, :N],
+                                  _weight_bytes(ebo, N, m.mla_fp8_scale_pitch(N))[:, :N])
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 2047, 4095],
+                                     np.random.default_rng(14).integers(0, M, 6)]))
+    qao, eao = f8.quantize_act_tiles(x[rows].astype(np.float64))
+    np.testing.assert_array_equal(qa.cpu().numpy()[rows], qao)
+    np.testing.assert_array_equal(sa.cpu().numpy()[:, rows], (eao.T + 127).astype(np.uint8))
+    _check_product(c.float().cpu().numpy()[rows].astype(np.float64), qao, eao, qbo, ebo, True)
