@@ -124,7 +124,7 @@ __global__ __launch_bounds__(F8_THREADS) void fp8_gemm_kernel(Fp8GemmParams p, i
     const uint8_t *src[F8_OPS];
     uint32_t dst[F8_OPS];
   };
-  auto slab_ops = [&](int kt, SlabOps &o) {
+  auto slab_ops = [&](int kt, SlabOps &o) __attribute__((always_inline)) {
     const uint32_t stage = lds_base + (kt % F8_NST) * F8_STAGE;
 #pragma unroll
     for (int q = 0; q < F8_NQ; ++q) {
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(F8_THREADS) void fp8_gemm_kernel(Fp8GemmParams p, i
     i32x8 a[4], b[4];
     int sa[4], sb[4];
   };
-  auto load_frags = [&](int kt, Frags &f) {
+  auto load_frags = [&](int kt, Frags &f) __attribute__((always_inline)) {
     const uint8_t *st = lds + (kt % F8_NST) * F8_STAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(F8_THREADS) void fp8_gemm_kernel(Fp8GemmParams p, i
   };
   // the 16 MFMAs of one slab; with ops, the slab's copies go between rows of
   // MFMAs (3, 2, 2, 2 per row)
-  auto mma = [&](const Frags &f, const SlabOps *ops) {
+  auto mma = [&](const Frags &f, const SlabOps *ops) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -218,27 +218,45 @@ __global__ __launch_bounds__(F8_THREADS) void fp8_gemm_kernel(Fp8GemmParams p, i
   load_frags(0, f0);
   f8_wait_slabs<F8_OPS>(min(nk, F8_NST) - 2);  // slab 1 landed (and slab 0 read by all)
   __syncthreads();
+  // one interval: MFMAs on cur while nxt receives slab jj+1; with copy, slab
+  // jj+NST goes out (constant wait), else the pipeline drains
+  auto interval = [&](int jj, Frags &cur, Frags &nxt, bool copy) __attribute__((always_inline)) {
+    if (copy) slab_ops(jj + F8_NST, ops);
+    load_frags(jj + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(cur, copy ? &ops : nullptr);
+    __builtin_amdgcn_sched_barrier(0);
+    if (copy) __builtin_amdgcn_s_waitcnt(F8_VMCNT((F8_NST - 2) * F8_OPS));
+    else f8_wait_slabs<F8_OPS>(nk - 1 - (jj + 2));
+    __syncthreads();
+  };
+  // the main loop runs intervals in pairs so the two fragment sets swap roles
+  // without register copies
   int j = 0;
-  for (; j + F8_NST < nk; ++j) {
-    slab_ops(j + F8_NST, ops);
-    load_frags(j + 1, f1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f0, &ops);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(F8_VMCNT((F8_NST - 2) * F8_OPS));
-    __syncthreads();
-    f0 = f1;
+  for (; j + 1 + F8_NST < nk; j += 2) {
+    interval(j, f0, f1, true);
+    interval(j + 1, f1, f0, true);
   }
-  for (; j + 1 < nk; ++j) {
-    load_frags(j + 1, f1);
-    __builtin_amdgcn_sched_barrier(0);
+  // Interval j always works on f0 for even j and f1 for odd j.  After the
+  // pairs, at most one interval still copies (j + NST == nk - 1); at most
+  // NST - 1 intervals are left in all, drained as one pair and one single;
+  // the last slab's MFMAs close.
+  if (j + F8_NST < nk) {
+    interval(j, f0, f1, true);
+    interval(j + 1, f1, f0, false);
+    j += 2;
+  }
+  if (j + 2 < nk) {  // at most once: at most NST - 1 = 3 intervals are left here
+    interval(j, f0, f1, false);
+    interval(j + 1, f1, f0, false);
+    j += 2;
+  }
+  if (j + 1 < nk) {
+    interval(j, f0, f1, false);
+    mma(f1, nullptr);
+  } else {
     mma(f0, nullptr);
-    __builtin_amdgcn_sched_barrier(0);
-    f8_wait_slabs<F8_OPS>(nk - 1 - (j + 2));
-    __syncthreads();
-    f0 = f1;
   }
-  mma(f0, nullptr);
 #undef F8_COPY
 
   if (p.c_f32) {
