@@ -45,16 +45,16 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     "attention": {
         "sha256": "c1bd530c5f0b3d1d94f73cca343d3a97bb064a8292df1f946034872d12b57fa2",
-        "FETCH_SIZE_KiB": 242916.8, "WRITE_SIZE_KiB": 131082.4},
+        "FETCH_SIZE_KiB": 242941.8, "WRITE_SIZE_KiB": 131083.4},
     "out_proj": {
         "sha256": "8e13d80de7dfc8ece20b886d8ffc7603e09761089b3d30e634658613b7f7a0d4",
-        "FETCH_SIZE_KiB": 1528292.3, "WRITE_SIZE_KiB": 57792.0},
+        "FETCH_SIZE_KiB": 1505949.8, "WRITE_SIZE_KiB": 57792.0},
     "latent_attention": {
         "sha256": "1fd44c5350c01dac2d84027f4f481983719fe59c01dc4d7a0abc49db62f270ba",
-        "FETCH_SIZE_KiB": 181375.1, "WRITE_SIZE_KiB": 76843.0},
+        "FETCH_SIZE_KiB": 181370.3, "WRITE_SIZE_KiB": 76843.0},
     "fp8_out_proj": {
-        "sha256": "a767d8bbf35566a2dd1616b28a1cd5ad0b0e8555d78dd88607f8a44a1ce2452e",
-        "FETCH_SIZE_KiB": 380141.5, "WRITE_SIZE_KiB": 57344.0},
+        "sha256": "2b09c1cd419b849a6ecb104b3b1b21654870fa9353478a11786fa801d6602405",
+        "FETCH_SIZE_KiB": 380647.1, "WRITE_SIZE_KiB": 57792.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
