@@ -39,11 +39,14 @@ def causal_attention_probs(q, k, scale):
     return p / np.sum(p, axis=-1, keepdims=True)
 
 
-def causal_attention_backward(q, k, v, dout, scale):
-    """(dq, dk, dv) of one head for the upstream gradient dout [Sq, dv]."""
+def causal_attention_backward(q, k, v, dout, scale, o=None):
+    """(dq, dk, dv) of one head for the upstream gradient dout [Sq, dv].
+
+    o is the forward output the backward is handed (the stored O, which
+    enters through rowsum(dO * O)); by default the exact P V."""
     q, k, v, dout = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout))
     p = causal_attention_probs(q, k, scale)
-    o = p @ v
+    o = p @ v if o is None else np.asarray(o, dtype=np.float64)
     dv = p.T @ dout
     dp = dout @ v.T
     delta = np.sum(dout * o, axis=-1, keepdims=True)
@@ -53,13 +56,15 @@ def causal_attention_backward(q, k, v, dout, scale):
     return dq, dk, dv
 
 
-def attention_backward_heads(q, k, v, dout, scale):
-    """Batched over leading axes: q, k [..., S, dqk], v, dout [..., S, dv]."""
+def attention_backward_heads(q, k, v, dout, scale, o=None):
+    """Batched over leading axes: q, k [..., S, dqk], v, dout [..., S, dv];
+    o (optional) the stored forward output [..., S, dv]."""
     q, k, v, dout = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout))
     lead = q.shape[:-2]
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for idx in np.ndindex(*lead):
-        dq[idx], dk[idx], dv[idx] = causal_attention_backward(q[idx], k[idx], v[idx], dout[idx], scale)
+        dq[idx], dk[idx], dv[idx] = causal_attention_backward(q[idx], k[idx], v[idx], dout[idx], scale,
+                                                              None if o is None else o[idx])
     return dq, dk, dv
 
 

@@ -64,3 +64,20 @@ def test_first_query_sees_only_itself():
     # the last key is seen only by the last query
     p_last = ab.causal_attention_probs(q, k, 0.9)[-1, -1]
     np.testing.assert_allclose(dv[-1], p_last * do[-1], rtol=1e-12)
+
+
+def test_given_output_enters_through_delta_only():
+    # handing the exact forward output changes nothing; a perturbed one moves
+    # dS by -P * rowsum(dout * perturbation), so dV is unaffected
+    q, k, v, do = _case(S=9)
+    ref = ab.causal_attention_backward(q, k, v, do, 0.6)
+    o = ab.attention_forward_heads(q[None], k[None], v[None], 0.6)[0]
+    same = ab.causal_attention_backward(q, k, v, do, 0.6, o=o)
+    for a, b in zip(ref, same):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    eps = 1e-3 * RNG.standard_normal(o.shape)
+    pert = ab.causal_attention_backward(q, k, v, do, 0.6, o=o + eps)
+    np.testing.assert_allclose(pert[2], ref[2], rtol=1e-12, atol=1e-14)
+    p = ab.causal_attention_probs(q, k, 0.6)
+    shift = np.sum(do * eps, axis=-1, keepdims=True)
+    np.testing.assert_allclose(pert[0], ref[0] - 0.6 * (p * shift) @ k, rtol=1e-9, atol=1e-12)
