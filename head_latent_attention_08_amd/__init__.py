@@ -18,6 +18,7 @@ from .mla import (  # noqa: F401
     mla_decode_multi_workspace_size,
     mla_decode_layout_of,
     mla_decode_workspace_size,
+    mla_attention_backward,
     mla_fp8_gemm,
     mla_fp8_quantize_blocks,
     mla_fp8_quantize_rows,

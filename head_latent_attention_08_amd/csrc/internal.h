@@ -108,6 +108,18 @@ hipError_t launch_fp8_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int
                            int N, int K, hipStream_t st);
 int64_t fp8_scale_pitch(int64_t rows);
 
+// Causal attention backward over BH heads of S rows: q, k [BH, S, dqk], v,
+// o, dout [BH, S, dv] in, dq, dk [BH, S, dqk] and dvo [BH, S, dv] out (all of
+// one dtype), lse and delta fp32 [BH * S] scratch.
+struct AttnBwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  void *dq, *dk, *dvo;
+  float *lse, *delta;
+  int BH, S, dqk, dv;
+  float scale;
+};
+hipError_t launch_attention_backward(int dtype, const AttnBwdArgs &a, hipStream_t st);
+
 hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src,
                             int64_t lds, int64_t rows, int width,
                             hipStream_t st);

@@ -993,6 +993,45 @@ mla_status mla_decode_absorbed_multi(const mla_config *cfg, const mla_weights *w
                      workspace, workspace_bytes, hip_stream);
 }
 
+mla_status mla_attention_backward_workspace_size(int64_t batch_heads, int64_t seq, size_t *bytes) {
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (batch_heads < 0 || seq < 0 || batch_heads * seq > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch_heads and seq must be >= 0 with a product below 2^31");
+  *bytes = (size_t)batch_heads * seq * 2 * sizeof(float);
+  return MLA_OK;
+}
+
+mla_status mla_attention_backward(int32_t dtype, int64_t batch_heads, int64_t seq, int32_t d_qk, int32_t d_v,
+                                  float scale, const void *q, const void *k, const void *v, const void *o,
+                                  const void *dout, void *dq, void *dk, void *dv, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream) {
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "dtype %d is neither 0 (fp32) nor 1 (bf16)", dtype);
+  size_t need = 0;
+  mla_status s = mla_attention_backward_workspace_size(batch_heads, seq, &need);
+  if (s != MLA_OK) return s;
+  if (d_qk < 8 || d_qk > 256 || d_qk % 8 || d_v < 8 || d_v > 256 || d_v % 8)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "d_qk and d_v must be multiples of 8 in [8, 256]");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  if (batch_heads * seq == 0) return MLA_OK;
+  const void *ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+  for (const void *p : ptrs) {
+    if (!p) return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor or the workspace is NULL");
+    if ((uintptr_t)p % 16) return fail(MLA_ERR_INVALID_ARGUMENT, "tensors and workspace must be 16-byte aligned");
+  }
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  AttnBwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dvo = dv;
+  a.lse = reinterpret_cast<float *>(workspace);
+  a.delta = a.lse + batch_heads * seq;
+  a.BH = (int)batch_heads; a.S = (int)seq; a.dqk = d_qk; a.dv = d_v; a.scale = scale;
+  MLA_HIP(launch_attention_backward(dtype == MLA_DTYPE_BF16 ? BF16 : F32, a, (hipStream_t)hip_stream),
+          "attention backward");
+  return MLA_OK;
+}
+
 int64_t mla_fp8_scale_pitch(int64_t rows) { return rows < 0 ? -1 : fp8_scale_pitch(rows); }
 
 static mla_status check_fp8_quant(const void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ldx,

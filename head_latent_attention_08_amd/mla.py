@@ -115,6 +115,11 @@ def load_library(path: str = LIB_PATH):
                                               i64, i64, P, i64, P, P, P, ctypes.c_size_t, P]
     lib.mla_rope_apply.argtypes = [P, ctypes.c_int32, i64, ctypes.c_int32, ctypes.c_int32, i64,
                                    i64, P, ctypes.POINTER(RopeParams), P]
+    lib.mla_attention_backward_workspace_size.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_attention_backward.argtypes = [ctypes.c_int32, i64, i64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_float, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    for fn in ("mla_attention_backward_workspace_size", "mla_attention_backward"):
+        getattr(lib, fn).restype = st
     lib.mla_fp8_scale_pitch.argtypes = [i64]
     lib.mla_fp8_scale_pitch.restype = i64
     lib.mla_fp8_quantize_rows.argtypes = [P, ctypes.c_int32, i64, i64, i64, P, i64, P, i64, P]
@@ -408,6 +413,26 @@ def mla_prefill_chunk(cfg: MlaConfig, weights: dict, x: torch.Tensor, latent_cac
         max_keys, _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return y, workspace
+
+
+def mla_attention_backward(q, k, v, o, dout, scale: float, workspace=None, stream=None):
+    """(dq, dk, dv) of causal attention; q, k [..., S, d_qk], v, o, dout
+    [..., S, d_v], contiguous, one dtype (fp32 or bf16)."""
+    ts = (q, k, v, o, dout)
+    if any(not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype for t in ts):
+        raise ValueError("q, k, v, o and dout must be contiguous device tensors of one dtype")
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[q.dtype]
+    S, dqk, dv_ = q.shape[-2], q.shape[-1], v.shape[-1]
+    bh = q.numel() // max(S * dqk, 1)
+    n = ctypes.c_size_t()
+    _check(load_library().mla_attention_backward_workspace_size(bh, S, ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dvt = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(load_library().mla_attention_backward(
+        dt, bh, S, dqk, dv_, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(dq), _ptr(dk),
+        _ptr(dvt), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dvt
 
 
 def mla_fp8_scale_pitch(rows: int) -> int:

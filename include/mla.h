@@ -344,6 +344,29 @@ MLA_API mla_status mla_fp8_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa
                         void *c, int32_t c_dtype, int64_t ldc, int64_t M, int64_t N, int64_t K,
                         void *hip_stream);
 
+/* ------------------------------------------------------ attention backward
+ * Gradients of the causal attention of "The Evolving Transformer -- DeepSeek
+ * V2 & V3", section 01 (per head P = softmax(scale Q K^T, tril mask),
+ * O = P V) for an upstream gradient dO:
+ *   dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)), dQ = scale dS K,
+ *   dK = scale dS^T Q.
+ * Rows are head-major and contiguous: q, k, dq, dk [batch_heads, seq, d_qk];
+ * v, o, dout, dv [batch_heads, seq, d_v]; o is the forward output.  All
+ * tensors have dtype (fp32 or bf16; arithmetic in fp32).  Device pointers,
+ * 16-byte aligned, owned by the caller; the workspace holds 8 bytes per row
+ * (the rows' log-sum-exp and rowsum(dO * O)).  Asynchronous on hip_stream.
+ * Status: INVALID_ARGUMENT for NULL or misaligned pointers (rows > 0),
+ * batch_heads or seq < 0, batch_heads * seq > 2^31 - 1, d_qk or d_v not a
+ * multiple of 8 in [8, 256], a non-finite or non-positive scale or a bad
+ * dtype; WORKSPACE_TOO_SMALL below the size; HIP for a failed launch. */
+MLA_API mla_status mla_attention_backward_workspace_size(int64_t batch_heads, int64_t seq,
+                                                 size_t *bytes);
+MLA_API mla_status mla_attention_backward(int32_t dtype, int64_t batch_heads, int64_t seq,
+                                  int32_t d_qk, int32_t d_v, float scale, const void *q,
+                                  const void *k, const void *v, const void *o,
+                                  const void *dout, void *dq, void *dk, void *dv,
+                                  void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* ---------------------------------------------------------- measurement
  * While set, every mla_prefill_forward / mla_decode_absorbed call made on
  * this thread records events[k] (hipEvent_t handles the caller created) on

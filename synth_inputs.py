@@ -169,3 +169,16 @@ def make_fp8_operands(M: int, N: int, K: int, seed: int, *, spread: bool = True,
         wv = np.repeat(np.repeat(np.ldexp(np.float32(1), v), 128, axis=0), 128, axis=1)[:N]
         w = w * wv.astype(np.float32)
     return round_bf16(x), round_bf16(w)
+
+
+def make_attention_backward_inputs(BH: int, S: int, dqk: int, dv: int, seed: int, bf16: bool = False):
+    """q, k [BH, S, dqk], v [BH, S, dv] and the upstream gradient dout
+    [BH, S, dv], all N(0, 1), drawn in that order (float32; rounded once to
+    bf16 when asked)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((BH, S, dqk), dtype=np.float32)
+    k = rng.standard_normal((BH, S, dqk), dtype=np.float32)
+    v = rng.standard_normal((BH, S, dv), dtype=np.float32)
+    do = rng.standard_normal((BH, S, dv), dtype=np.float32)
+    out = (q, k, v, do)
+    return tuple(round_bf16(a) for a in out) if bf16 else out

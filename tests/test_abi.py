@@ -250,3 +250,21 @@ def test_fp8_arguments_rejected_without_launch():
         assert call(**over) == INV, over
         assert lib.mla_last_error()
     assert call(M=0, a=None, sa=None, b=None, sb=None, c=None) == 0
+
+
+def test_attention_backward_arguments_rejected_without_launch():
+    lib = m.load_library()
+    P = ctypes.c_void_p
+    fake = P(1 << 40)
+    n = ctypes.c_size_t()
+    assert lib.mla_attention_backward_workspace_size(4, 100, ctypes.byref(n)) == 0 and n.value == 3200
+    assert lib.mla_attention_backward_workspace_size(-1, 100, ctypes.byref(n)) == 1
+    def call(dtype=0, bh=2, S=64, dqk=64, dv=64, scale=0.1, ptr=fake, ws=fake, wsb=1024):
+        return lib.mla_attention_backward(dtype, bh, S, dqk, dv, ctypes.c_float(scale), ptr, ptr, ptr, ptr, ptr,
+                                          ptr, ptr, ptr, ws, wsb, None)
+    for kw in (dict(dtype=5), dict(dqk=12), dict(dv=264), dict(dqk=0), dict(scale=0.0),
+               dict(scale=float("inf")), dict(ptr=None), dict(ptr=P((1 << 40) + 4)), dict(ws=None),
+               dict(S=-1)):
+        assert call(**kw) == 1, kw
+    assert call(wsb=100) == 3                      # workspace too small
+    assert call(bh=0, ptr=None, ws=None) == 0      # nothing to do, nothing launched
