@@ -228,6 +228,39 @@ def fp8_projections(m, S, log, reps=20):
     return res
 
 
+def attention_backward_line(m, S, log, reps=2):
+    """Causal attention backward (dQ, dK, dV) at the V3 prefill attention
+    shape: 128 heads, S tokens, d_qk 192, d_v 128, bf16, seeded device draws
+    (N(0, 1) q, k, v, dout; o a stand-in of the same shape: it only enters
+    through rowsum(dout * o)).  Algorithmic work: the five causal products
+    (Q K^T, dO V^T, P^T dO, dS K, dS^T Q) over the S(S+1)/2 visible pairs."""
+    import torch
+    H, dqk, dv = 128, 192, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9500)
+    mk = lambda d: torch.randn((H, S, d), device="cuda", generator=gen).to(torch.bfloat16)
+    q, k, v, o, do = mk(dqk), mk(dqk), mk(dv), mk(dv), mk(dv)
+    scale = dqk ** -0.5
+    m.mla_attention_backward(q, k, v, o, do, scale)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        m.mla_attention_backward(q, k, v, o, do, scale)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    fl = 2.0 * H * (S * (S + 1) / 2.0) * (3 * dqk + 2 * dv)
+    tf = fl / (ms * 1e-3) / 1e12
+    log(f"bench: attention backward H={H} S={S}: {ms:.2f} ms, {tf:.1f} TFLOP/s")
+    del q, k, v, o, do
+    torch.cuda.empty_cache()
+    return {"heads": H, "seq_len": S, "d_qk": dqk, "d_v": dv, "dtype": "bf16", "ms": ms,
+            "gflop": fl / 1e9, "tflops": tf, "frac_of_bf16_peak": tf / MI355X_BF16_TFLOPS,
+            "note": "vector-ALU kernels (no MFMA yet)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +269,8 @@ def main():
     # default warm-up runs ~1.5 s of the same full steps
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the causal attention backward (context line)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the block-scaled FP8 projection products (context line)")
     ap.add_argument("--no-multi-token", action="store_true",
@@ -473,6 +508,8 @@ def main():
             f"{c_fl / (c_ms * 1e-3) / 1e12:.0f} TFLOP/s")
     if not args.no_fp8:
         out["fp8_projections"] = fp8_projections(m, S, log)
+    if not args.no_backward:
+        out["attention_backward"] = attention_backward_line(m, S, log)
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on bounded samples")
         out["cpu_baseline"] = cpu_baseline(c_pre, x, w, c_dec, xdec, wdec, lens, cache)
