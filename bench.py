@@ -44,17 +44,17 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "c1bd530c5f0b3d1d94f73cca343d3a97bb064a8292df1f946034872d12b57fa2",
-        "FETCH_SIZE_KiB": 242941.8, "WRITE_SIZE_KiB": 131083.4},
+        "sha256": "1a3d437ba863dcf428fa406e9ffce47827b53d72f5382ed9d3b04e39b335124b",
+        "FETCH_SIZE_KiB": 242950.8, "WRITE_SIZE_KiB": 131081.2},
     "out_proj": {
-        "sha256": "8e13d80de7dfc8ece20b886d8ffc7603e09761089b3d30e634658613b7f7a0d4",
-        "FETCH_SIZE_KiB": 1505949.8, "WRITE_SIZE_KiB": 57792.0},
+        "sha256": "271d66d0b1d94d15fa8482fca4bce65e280ab064bb80b4cda277d769fa320c0b",
+        "FETCH_SIZE_KiB": 1515516.0, "WRITE_SIZE_KiB": 57792.0},
     "latent_attention": {
-        "sha256": "1fd44c5350c01dac2d84027f4f481983719fe59c01dc4d7a0abc49db62f270ba",
-        "FETCH_SIZE_KiB": 181370.3, "WRITE_SIZE_KiB": 76843.0},
+        "sha256": "11a1c2ef811f88f020b9959285eac89e154fb3b4b7e269dd5095ff8e9b5c8684",
+        "FETCH_SIZE_KiB": 181371.6, "WRITE_SIZE_KiB": 76843.0},
     "fp8_out_proj": {
-        "sha256": "2b09c1cd419b849a6ecb104b3b1b21654870fa9353478a11786fa801d6602405",
-        "FETCH_SIZE_KiB": 380647.1, "WRITE_SIZE_KiB": 57792.0},
+        "sha256": "e9d138f0b318379ea0c39c55ac233d5204ae42f839f53f4d02f38b641cebf2ab",
+        "FETCH_SIZE_KiB": 380591.4, "WRITE_SIZE_KiB": 57792.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
