@@ -8,11 +8,12 @@
 // Three passes, each a wave per row, vector-ALU arithmetic in fp32:
 //  1. per query row i: lse_i = log sum_j<=i exp(s_ij) and delta_i =
 //     rowsum(dO_i * O_i), into a workspace of 8 bytes per row;
-//  2. per key row j: over the queries i >= j, 64 at a time (a lane per
-//     query: s_ij, p_ij = exp(s_ij - lse_i), dp_ij, ds_ij), then the wave
-//     turns to channels (a lane per channel) and accumulates
-//     dV_j += p_ij dO_i and dK_j += ds_ij Q_i, reading the 64 rows coalesced;
-//  3. per query row i: the same over keys j <= i for dQ_i += ds_ij K_j.
+//  2. per 4 key rows j: over the queries i >= j, 64 at a time (a lane per
+//     query: s_ij, p_ij = exp(s_ij - lse_i), dp_ij, ds_ij for the 4 keys),
+//     then the wave turns to channels (a lane per channel) and accumulates
+//     dV_j += p_ij dO_i and dK_j += ds_ij Q_i, reading the 64 rows coalesced
+//     once for the 4 keys;
+//  3. per 4 query rows i: the same over keys j <= i for dQ_i += ds_ij K_j.
 // P is recomputed from lse, never stored.  Rows are [BH, S, d] contiguous,
 // d a multiple of 8 and at most 256, pointers 16-byte aligned.
 
@@ -96,110 +97,186 @@ __global__ __launch_bounds__(256) void attn_bwd_rowstats_kernel(AttnBwdArgs a) {
   }
 }
 
-// pass 2: dK and dV of key row (bh, j)
+// R rows of a head per wave in passes 2 and 3: each streamed row is read
+// once for all R of them (loads shared across R dot products and R sets of
+// accumulators).
+constexpr int AB_R = 4;
+
+// dot of one global row with R LDS vectors
+template <typename T>
+__device__ inline void ab_dot_r(const T *row, const float (*v)[AB_DMAX], int n, float *out) {
+#pragma unroll
+  for (int r = 0; r < AB_R; ++r) out[r] = 0.f;
+  for (int c = 0; c < n; c += 8) {
+    float f[8];
+    ab_load8(row + c, f);
+#pragma unroll
+    for (int r = 0; r < AB_R; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[r] = fmaf(f[e], v[r][c + e], out[r]);
+  }
+}
+
+// pass 2: dK and dV of key rows j0 .. j0 + R - 1 of head bh
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
-  __shared__ float ks[4][AB_DMAX], vs[4][AB_DMAX], ps[4][64], dss[4][64];
+  __shared__ float ks[4][AB_R][AB_DMAX], vs[4][AB_R][AB_DMAX], ps[4][AB_R][64], dss[4][AB_R][64];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
-  if (row >= (int64_t)a.BH * a.S) return;
-  const int j = (int)(row % a.S);
-  const int64_t bh = row / a.S;
+  const int nb = (a.S + AB_R - 1) / AB_R;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wv;
+  if (w >= (int64_t)a.BH * nb) return;
+  const int64_t bh = w / nb;
+  const int j0 = (int)(w - bh * nb) * AB_R;
   const T *qb = reinterpret_cast<const T *>(a.q) + bh * a.S * a.dqk;
   const T *db = reinterpret_cast<const T *>(a.dout) + bh * a.S * a.dv;
   const float *lse = a.lse + bh * a.S, *delta = a.delta + bh * a.S;
-  for (int c = lane; c < a.dqk; c += 64) ks[wv][c] = ab_ld(reinterpret_cast<const T *>(a.k) + row * a.dqk + c);
-  for (int c = lane; c < a.dv; c += 64) vs[wv][c] = ab_ld(reinterpret_cast<const T *>(a.v) + row * a.dv + c);
+#pragma unroll
+  for (int r = 0; r < AB_R; ++r) {
+    const bool ok = j0 + r < a.S;
+    const int64_t row = bh * a.S + j0 + r;
+    for (int c = lane; c < a.dqk; c += 64)
+      ks[wv][r][c] = ok ? ab_ld(reinterpret_cast<const T *>(a.k) + row * a.dqk + c) : 0.f;
+    for (int c = lane; c < a.dv; c += 64)
+      vs[wv][r][c] = ok ? ab_ld(reinterpret_cast<const T *>(a.v) + row * a.dv + c) : 0.f;
+  }
   __builtin_amdgcn_wave_barrier();
-  float dk[AB_DMAX / 64] = {0.f, 0.f, 0.f, 0.f}, dv[AB_DMAX / 64] = {0.f, 0.f, 0.f, 0.f};
-  for (int i0 = j; i0 < a.S; i0 += 64) {
+  float dk[AB_R][AB_DMAX / 64], dv[AB_R][AB_DMAX / 64];
+#pragma unroll
+  for (int r = 0; r < AB_R; ++r)
+#pragma unroll
+    for (int u = 0; u < AB_DMAX / 64; ++u) dk[r][u] = dv[r][u] = 0.f;
+  for (int i0 = j0; i0 < a.S; i0 += 64) {
     const int i = i0 + lane;
-    float p = 0.f, ds = 0.f;
+    float s[AB_R], dp[AB_R];
     if (i < a.S) {
-      const float s = a.scale * ab_dot(qb + (int64_t)i * a.dqk, ks[wv], a.dqk);
-      p = expf(s - lse[i]);
-      const float dp = ab_dot(db + (int64_t)i * a.dv, vs[wv], a.dv);
-      ds = p * (dp - delta[i]);
+      ab_dot_r(qb + (int64_t)i * a.dqk, ks[wv], a.dqk, s);
+      ab_dot_r(db + (int64_t)i * a.dv, vs[wv], a.dv, dp);
     }
-    ps[wv][lane] = p;
-    dss[wv][lane] = ds;
+#pragma unroll
+    for (int r = 0; r < AB_R; ++r) {
+      float p = 0.f, ds = 0.f;
+      if (i < a.S && j0 + r <= i) {   // key j0 + r is visible to query i (and inside the sequence)
+        p = expf(a.scale * s[r] - lse[i]);
+        ds = p * (dp[r] - delta[i]);
+      }
+      ps[wv][r][lane] = p;
+      dss[wv][r][lane] = ds;
+    }
     __builtin_amdgcn_wave_barrier();
     const int n = min(64, a.S - i0);
     for (int t = 0; t < n; ++t) {
-      const float pt = ps[wv][t], dt = dss[wv][t];
       const T *qr = qb + (int64_t)(i0 + t) * a.dqk, *dr = db + (int64_t)(i0 + t) * a.dv;
 #pragma unroll
       for (int u = 0; u < AB_DMAX / 64; ++u) {
         const int c = lane + 64 * u;
-        if (c < a.dqk) dk[u] = fmaf(dt, ab_ld(qr + c), dk[u]);
-        if (c < a.dv) dv[u] = fmaf(pt, ab_ld(dr + c), dv[u]);
+        const float qv = c < a.dqk ? ab_ld(qr + c) : 0.f;
+        const float gv = c < a.dv ? ab_ld(dr + c) : 0.f;
+#pragma unroll
+        for (int r = 0; r < AB_R; ++r) {
+          dk[r][u] = fmaf(dss[wv][r][t], qv, dk[r][u]);
+          dv[r][u] = fmaf(ps[wv][r][t], gv, dv[r][u]);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
   }
-  T *dkr = reinterpret_cast<T *>(a.dk) + row * a.dqk;
-  T *dvr = reinterpret_cast<T *>(a.dvo) + row * a.dv;
 #pragma unroll
-  for (int u = 0; u < AB_DMAX / 64; ++u) {
-    const int c = lane + 64 * u;
-    if (c < a.dqk) dkr[c] = (T)(a.scale * dk[u]);
-    if (c < a.dv) dvr[c] = (T)dv[u];
+  for (int r = 0; r < AB_R; ++r) {
+    if (j0 + r >= a.S) break;
+    const int64_t row = bh * a.S + j0 + r;
+    T *dkr = reinterpret_cast<T *>(a.dk) + row * a.dqk;
+    T *dvr = reinterpret_cast<T *>(a.dvo) + row * a.dv;
+#pragma unroll
+    for (int u = 0; u < AB_DMAX / 64; ++u) {
+      const int c = lane + 64 * u;
+      if (c < a.dqk) dkr[c] = (T)(a.scale * dk[r][u]);
+      if (c < a.dv) dvr[c] = (T)dv[r][u];
+    }
   }
 }
 
-// pass 3: dQ of query row (bh, i)
+// pass 3: dQ of query rows i0 .. i0 + R - 1 of head bh
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
-  __shared__ float qs[4][AB_DMAX], dos[4][AB_DMAX], dss[4][64];
+  __shared__ float qs[4][AB_R][AB_DMAX], dos[4][AB_R][AB_DMAX], dss[4][AB_R][64];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
-  if (row >= (int64_t)a.BH * a.S) return;
-  const int i = (int)(row % a.S);
-  const int64_t bh = row / a.S;
+  const int nb = (a.S + AB_R - 1) / AB_R;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wv;
+  if (w >= (int64_t)a.BH * nb) return;
+  const int64_t bh = w / nb;
+  const int i0 = (int)(w - bh * nb) * AB_R;
+  const int nq = min(AB_R, a.S - i0);
   const T *kb = reinterpret_cast<const T *>(a.k) + bh * a.S * a.dqk;
   const T *vb = reinterpret_cast<const T *>(a.v) + bh * a.S * a.dv;
-  for (int c = lane; c < a.dqk; c += 64) qs[wv][c] = ab_ld(reinterpret_cast<const T *>(a.q) + row * a.dqk + c);
-  for (int c = lane; c < a.dv; c += 64) dos[wv][c] = ab_ld(reinterpret_cast<const T *>(a.dout) + row * a.dv + c);
-  const float lse = a.lse[row], delta = a.delta[row];
+  float lse[AB_R], delta[AB_R];
+#pragma unroll
+  for (int r = 0; r < AB_R; ++r) {
+    const bool ok = r < nq;
+    const int64_t row = bh * a.S + i0 + r;
+    for (int c = lane; c < a.dqk; c += 64)
+      qs[wv][r][c] = ok ? ab_ld(reinterpret_cast<const T *>(a.q) + row * a.dqk + c) : 0.f;
+    for (int c = lane; c < a.dv; c += 64)
+      dos[wv][r][c] = ok ? ab_ld(reinterpret_cast<const T *>(a.dout) + row * a.dv + c) : 0.f;
+    lse[r] = ok ? a.lse[row] : 0.f;
+    delta[r] = ok ? a.delta[row] : 0.f;
+  }
   __builtin_amdgcn_wave_barrier();
-  float dq[AB_DMAX / 64] = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 <= i; j0 += 64) {
+  float dq[AB_R][AB_DMAX / 64];
+#pragma unroll
+  for (int r = 0; r < AB_R; ++r)
+#pragma unroll
+    for (int u = 0; u < AB_DMAX / 64; ++u) dq[r][u] = 0.f;
+  const int last = i0 + nq - 1;  // the last query row of the wave
+  for (int j0 = 0; j0 <= last; j0 += 64) {
     const int j = j0 + lane;
-    float ds = 0.f;
-    if (j <= i) {
-      const float s = a.scale * ab_dot(kb + (int64_t)j * a.dqk, qs[wv], a.dqk);
-      const float p = expf(s - lse);
-      const float dp = ab_dot(vb + (int64_t)j * a.dv, dos[wv], a.dv);
-      ds = p * (dp - delta);
+    float s[AB_R], dp[AB_R];
+    if (j <= last) {
+      ab_dot_r(kb + (int64_t)j * a.dqk, qs[wv], a.dqk, s);
+      ab_dot_r(vb + (int64_t)j * a.dv, dos[wv], a.dv, dp);
     }
-    dss[wv][lane] = ds;
+#pragma unroll
+    for (int r = 0; r < AB_R; ++r) {
+      float ds = 0.f;
+      if (r < nq && j <= i0 + r) {
+        const float p = expf(a.scale * s[r] - lse[r]);
+        ds = p * (dp[r] - delta[r]);
+      }
+      dss[wv][r][lane] = ds;
+    }
     __builtin_amdgcn_wave_barrier();
-    const int n = min(64, i + 1 - j0);
+    const int n = min(64, last + 1 - j0);
     for (int t = 0; t < n; ++t) {
-      const float dt = dss[wv][t];
       const T *kr = kb + (int64_t)(j0 + t) * a.dqk;
 #pragma unroll
       for (int u = 0; u < AB_DMAX / 64; ++u) {
         const int c = lane + 64 * u;
-        if (c < a.dqk) dq[u] = fmaf(dt, ab_ld(kr + c), dq[u]);
+        const float kv = c < a.dqk ? ab_ld(kr + c) : 0.f;
+#pragma unroll
+        for (int r = 0; r < AB_R; ++r) dq[r][u] = fmaf(dss[wv][r][t], kv, dq[r][u]);
       }
     }
     __builtin_amdgcn_wave_barrier();
   }
-  T *dqr = reinterpret_cast<T *>(a.dq) + row * a.dqk;
 #pragma unroll
-  for (int u = 0; u < AB_DMAX / 64; ++u) {
-    const int c = lane + 64 * u;
-    if (c < a.dqk) dqr[c] = (T)(a.scale * dq[u]);
+  for (int r = 0; r < AB_R; ++r) {
+    if (r >= nq) break;
+    T *dqr = reinterpret_cast<T *>(a.dq) + (bh * a.S + i0 + r) * a.dqk;
+#pragma unroll
+    for (int u = 0; u < AB_DMAX / 64; ++u) {
+      const int c = lane + 64 * u;
+      if (c < a.dqk) dqr[c] = (T)(a.scale * dq[r][u]);
+    }
   }
 }
 
 template <typename T> hipError_t launch_t(const AttnBwdArgs &a, hipStream_t st) {
   const int64_t rows = (int64_t)a.BH * a.S;
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const int64_t blocks = (int64_t)a.BH * ((a.S + AB_R - 1) / AB_R);
+  const dim3 rgrid((unsigned)((blocks + 3) / 4));
   hipLaunchKernelGGL(attn_bwd_rowstats_kernel<T>, grid, block, 0, st, a);
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<T>, grid, block, 0, st, a);
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<T>, grid, block, 0, st, a);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<T>, rgrid, block, 0, st, a);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<T>, rgrid, block, 0, st, a);
   return hipGetLastError();
 }
 
