@@ -5,8 +5,8 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three passes, each a wave per row, vector-ALU arithmetic in fp32:
-//  1. per query row i: lse_i = log sum_j<=i exp(s_ij) and delta_i =
+// Three passes, each a wave per 4 rows of a head, vector-ALU arithmetic in fp32:
+//  1. per 4 query rows i: lse_i = log sum_j<=i exp(s_ij) and delta_i =
 //     rowsum(dO_i * O_i), into a workspace of 8 bytes per row;
 //  2. per 4 key rows j: over the queries i >= j, 64 at a time (a lane per
 //     query: s_ij, p_ij = exp(s_ij - lse_i), dp_ij, ds_ij for the 4 keys),
@@ -59,44 +59,6 @@ __device__ inline float ab_wave_sum(float v) {
 
 template <typename T> __device__ inline float ab_ld(const T *p) { return (float)*p; }
 
-// pass 1: lse and delta of query row (bh, i)
-template <typename T>
-__global__ __launch_bounds__(256) void attn_bwd_rowstats_kernel(AttnBwdArgs a) {
-  __shared__ float qs[4][AB_DMAX];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
-  if (row >= (int64_t)a.BH * a.S) return;
-  const int i = (int)(row % a.S);
-  const int64_t bh = row / a.S;
-  const T *q = reinterpret_cast<const T *>(a.q) + row * a.dqk;
-  const T *kb = reinterpret_cast<const T *>(a.k) + bh * a.S * a.dqk;
-  for (int c = lane; c < a.dqk; c += 64) qs[wv][c] = ab_ld(q + c);
-  const T *o = reinterpret_cast<const T *>(a.o) + row * a.dv;
-  const T *dO = reinterpret_cast<const T *>(a.dout) + row * a.dv;
-  float d = 0.f;
-  for (int c = lane; c < a.dv; c += 64) d = fmaf(ab_ld(o + c), ab_ld(dO + c), d);
-  d = ab_wave_sum(d);
-  __builtin_amdgcn_wave_barrier();
-  float m = -INFINITY, l = 0.f;
-  for (int j0 = 0; j0 <= i; j0 += 64) {
-    const int j = j0 + lane;
-    if (j <= i) {
-      const float s = a.scale * ab_dot(kb + (int64_t)j * a.dqk, qs[wv], a.dqk);
-      const float mn = fmaxf(m, s);
-      l = l * expf(m - mn) + expf(s - mn);
-      m = mn;
-    }
-  }
-  float M = m;
-#pragma unroll
-  for (int o2 = 32; o2 > 0; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2));
-  const float L = ab_wave_sum(m == -INFINITY ? 0.f : l * expf(m - M));
-  if (lane == 0) {
-    a.lse[row] = M + logf(L);
-    a.delta[row] = d;
-  }
-}
-
 // R rows of a head per wave in passes 2 and 3: each streamed row is read
 // once for all R of them (loads shared across R dot products and R sets of
 // accumulators).
@@ -114,6 +76,69 @@ __device__ inline void ab_dot_r(const T *row, const float (*v)[AB_DMAX], int n, 
     for (int r = 0; r < AB_R; ++r)
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[r] = fmaf(f[e], v[r][c + e], out[r]);
+  }
+}
+
+// pass 1: lse and delta of query rows i0 .. i0 + R - 1 of head bh
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_rowstats_kernel(AttnBwdArgs a) {
+  __shared__ float qs[4][AB_R][AB_DMAX];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nb = (a.S + AB_R - 1) / AB_R;
+  const int64_t w = (int64_t)blockIdx.x * 4 + wv;
+  if (w >= (int64_t)a.BH * nb) return;
+  const int64_t bh = w / nb;
+  const int i0 = (int)(w - bh * nb) * AB_R;
+  const int nq = min(AB_R, a.S - i0);
+  const T *kb = reinterpret_cast<const T *>(a.k) + bh * a.S * a.dqk;
+  float d[AB_R];
+#pragma unroll
+  for (int r = 0; r < AB_R; ++r) {
+    const bool ok = r < nq;
+    const int64_t row = bh * a.S + i0 + r;
+    for (int c = lane; c < a.dqk; c += 64)
+      qs[wv][r][c] = ok ? ab_ld(reinterpret_cast<const T *>(a.q) + row * a.dqk + c) : 0.f;
+    float x = 0.f;
+    if (ok)
+      for (int c = lane; c < a.dv; c += 64)
+        x = fmaf(ab_ld(reinterpret_cast<const T *>(a.o) + row * a.dv + c),
+                 ab_ld(reinterpret_cast<const T *>(a.dout) + row * a.dv + c), x);
+    d[r] = ab_wave_sum(x);
+  }
+  __builtin_amdgcn_wave_barrier();
+  float m[AB_R], l[AB_R];
+#pragma unroll
+  for (int r = 0; r < AB_R; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+  }
+  const int last = i0 + nq - 1;
+  for (int j0 = 0; j0 <= last; j0 += 64) {
+    const int j = j0 + lane;
+    if (j <= last) {
+      float s[AB_R];
+      ab_dot_r(kb + (int64_t)j * a.dqk, qs[wv], a.dqk, s);
+#pragma unroll
+      for (int r = 0; r < AB_R; ++r) {
+        if (r < nq && j <= i0 + r) {
+          const float x = a.scale * s[r];
+          const float mn = fmaxf(m[r], x);
+          l[r] = l[r] * expf(m[r] - mn) + expf(x - mn);
+          m[r] = mn;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < AB_R; ++r) {
+    float M = m[r];
+#pragma unroll
+    for (int o2 = 32; o2 > 0; o2 >>= 1) M = fmaxf(M, __shfl_xor(M, o2));
+    const float L = ab_wave_sum(m[r] == -INFINITY ? 0.f : l[r] * expf(m[r] - M));
+    if (lane == 0 && r < nq) {
+      a.lse[bh * a.S + i0 + r] = M + logf(L);
+      a.delta[bh * a.S + i0 + r] = d[r];
+    }
   }
 }
 
@@ -270,11 +295,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 }
 
 template <typename T> hipError_t launch_t(const AttnBwdArgs &a, hipStream_t st) {
-  const int64_t rows = (int64_t)a.BH * a.S;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const dim3 block(256);
   const int64_t blocks = (int64_t)a.BH * ((a.S + AB_R - 1) / AB_R);
   const dim3 rgrid((unsigned)((blocks + 3) / 4));
-  hipLaunchKernelGGL(attn_bwd_rowstats_kernel<T>, grid, block, 0, st, a);
+  hipLaunchKernelGGL(attn_bwd_rowstats_kernel<T>, rgrid, block, 0, st, a);
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel<T>, rgrid, block, 0, st, a);
   hipLaunchKernelGGL(attn_bwd_dq_kernel<T>, rgrid, block, 0, st, a);
   return hipGetLastError();
