@@ -45,16 +45,16 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     "attention": {
         "sha256": "1a3d437ba863dcf428fa406e9ffce47827b53d72f5382ed9d3b04e39b335124b",
-        "FETCH_SIZE_KiB": 242950.8, "WRITE_SIZE_KiB": 131081.2},
+        "FETCH_SIZE_KiB": 242949.3, "WRITE_SIZE_KiB": 131080.5},
     "out_proj": {
         "sha256": "271d66d0b1d94d15fa8482fca4bce65e280ab064bb80b4cda277d769fa320c0b",
-        "FETCH_SIZE_KiB": 1515516.0, "WRITE_SIZE_KiB": 57792.0},
+        "FETCH_SIZE_KiB": 1513323.5, "WRITE_SIZE_KiB": 57792.0},
     "latent_attention": {
         "sha256": "11a1c2ef811f88f020b9959285eac89e154fb3b4b7e269dd5095ff8e9b5c8684",
-        "FETCH_SIZE_KiB": 181371.6, "WRITE_SIZE_KiB": 76843.0},
+        "FETCH_SIZE_KiB": 181372.8, "WRITE_SIZE_KiB": 76843.0},
     "fp8_out_proj": {
         "sha256": "e9d138f0b318379ea0c39c55ac233d5204ae42f839f53f4d02f38b641cebf2ab",
-        "FETCH_SIZE_KiB": 380591.4, "WRITE_SIZE_KiB": 57792.0},
+        "FETCH_SIZE_KiB": 380538.4, "WRITE_SIZE_KiB": 57792.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
