@@ -75,3 +75,15 @@ def attention_forward_heads(q, k, v, scale):
     for idx in np.ndindex(*q.shape[:-2]):
         o[idx] = causal_attention(q[idx], k[idx], v[idx], scale)
     return o
+
+
+def rmsnorm_backward(x, g, dy, eps):
+    """(dx, dg) of y = x * (mean(x^2) + eps)^-1/2 * g over the last axis (the
+    RMSNorm on c_q of the MLA module), float64:
+    dx = r (g dy) - x r^3 mean(x g dy), dg = sum over rows of dy x r."""
+    x, g, dy = (np.asarray(a, dtype=np.float64) for a in (x, g, dy))
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    gdy = g * dy
+    dx = r * gdy - x * r ** 3 * np.mean(x * gdy, axis=-1, keepdims=True)
+    dg = np.sum((dy * x * r).reshape(-1, x.shape[-1]), axis=0)
+    return dx, dg

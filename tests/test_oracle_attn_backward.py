@@ -81,3 +81,33 @@ def test_given_output_enters_through_delta_only():
     p = ab.causal_attention_probs(q, k, 0.6)
     shift = np.sum(do * eps, axis=-1, keepdims=True)
     np.testing.assert_allclose(pert[0], ref[0] - 0.6 * (p * shift) @ k, rtol=1e-9, atol=1e-12)
+
+
+def test_rmsnorm_backward_finite_differences_and_autograd():
+    from oracle.mla_oracle import rmsnorm
+    x = RNG.standard_normal((4, 12))
+    g = 1 + 0.1 * RNG.standard_normal(12)
+    dy = RNG.standard_normal((4, 12))
+    eps = 1e-6
+    dx, dg = ab.rmsnorm_backward(x, g, dy, eps)
+    loss = lambda x_, g_: float(np.sum(dy * rmsnorm(x_, g_, eps)))
+    h = 1e-6
+    for idx in np.ndindex(*x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd = (loss(xp, g) - loss(xm, g)) / (2 * h)
+        assert abs(fd - dx[idx]) <= 1e-6 * (1 + abs(fd))
+    for c in range(12):
+        gp, gm = g.copy(), g.copy()
+        gp[c] += h
+        gm[c] -= h
+        fd = (loss(x, gp) - loss(x, gm)) / (2 * h)
+        assert abs(fd - dg[c]) <= 1e-6 * (1 + abs(fd))
+    tx, tg = torch.tensor(x, requires_grad=True), torch.tensor(g, requires_grad=True)
+    torch.nn.functional.rms_norm(tx, (12,), tg, eps).backward(torch.tensor(dy))
+    np.testing.assert_allclose(dx, tx.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dg, tg.grad.numpy(), rtol=1e-10, atol=1e-12)
+    # scale invariance of the normalisation: x is orthogonal to dx when eps = 0
+    dx0, _ = ab.rmsnorm_backward(x, g, dy, 0.0)
+    np.testing.assert_allclose(np.sum(dx0 * x, axis=-1), 0.0, atol=1e-10)
