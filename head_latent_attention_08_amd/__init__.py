@@ -20,6 +20,7 @@ from .mla import (  # noqa: F401
     mla_decode_workspace_size,
     mla_attention_backward,
     mla_fp8_gemm,
+    mla_rmsnorm_backward,
     mla_fp8_quantize_blocks,
     mla_fp8_quantize_rows,
     mla_fp8_scale_pitch,

@@ -294,6 +294,59 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   }
 }
 
+// RMSNorm backward of y = x r g, r = (mean(x^2) + eps)^-1/2 per row:
+// dx = r (g dy) - x r^3 mean(x g dy), one workgroup per row (rinv kept per
+// row); dg[c] = sum over rows of dy x r, one thread per column over all rows
+// in order (deterministic).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_rows_kernel(const T *x, const T *dy, const T *g, int n,
+                                                               float eps, T *dx, float *rinv) {
+  __shared__ float red[2][4];
+  const int64_t row = blockIdx.x;
+  const T *xr = x + row * n, *dr = dy + row * n;
+  float ss = 0.f, xg = 0.f;
+  for (int c = threadIdx.x; c < n; c += 256) {
+    const float xv = (float)xr[c];
+    ss = fmaf(xv, xv, ss);
+    xg = fmaf(xv, (float)g[c] * (float)dr[c], xg);
+  }
+  ss = ab_wave_sum(ss);
+  xg = ab_wave_sum(xg);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = ss;
+    red[1][threadIdx.x >> 6] = xg;
+  }
+  __syncthreads();
+  ss = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  xg = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const float r = 1.f / sqrtf(ss / n + eps);
+  const float k = r * r * r * xg / n;
+  for (int c = threadIdx.x; c < n; c += 256)
+    dx[row * n + c] = (T)(r * (float)g[c] * (float)dr[c] - (float)xr[c] * k);
+  if (threadIdx.x == 0) rinv[row] = r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_dg_kernel(const T *x, const T *dy, int64_t rows, int n,
+                                                             const float *rinv, float *dg) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= n) return;
+  float acc = 0.f;
+  for (int64_t r = 0; r < rows; ++r) acc = fmaf((float)dy[r * n + c] * (float)x[r * n + c], rinv[r], acc);
+  dg[c] = acc;
+}
+
+template <typename T>
+hipError_t launch_rms_t(const void *x, const void *dy, const void *g, int64_t rows, int n, float eps, void *dx,
+                        float *dg, float *rinv, hipStream_t st) {
+  hipLaunchKernelGGL(rmsnorm_bwd_rows_kernel<T>, dim3((unsigned)rows), dim3(256), 0, st,
+                     reinterpret_cast<const T *>(x), reinterpret_cast<const T *>(dy),
+                     reinterpret_cast<const T *>(g), n, eps, reinterpret_cast<T *>(dx), rinv);
+  hipLaunchKernelGGL(rmsnorm_bwd_dg_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const T *>(x), reinterpret_cast<const T *>(dy), rows, n, rinv, dg);
+  return hipGetLastError();
+}
+
 template <typename T> hipError_t launch_t(const AttnBwdArgs &a, hipStream_t st) {
   const dim3 block(256);
   const int64_t blocks = (int64_t)a.BH * ((a.S + AB_R - 1) / AB_R);
@@ -305,6 +358,13 @@ template <typename T> hipError_t launch_t(const AttnBwdArgs &a, hipStream_t st) 
 }
 
 }  // namespace
+
+hipError_t launch_rmsnorm_backward(int dtype, const void *x, const void *dy, const void *g, int64_t rows, int n,
+                                  float eps, void *dx, float *dg, float *rinv, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  return dtype == BF16 ? launch_rms_t<bf16>(x, dy, g, rows, n, eps, dx, dg, rinv, st)
+                       : launch_rms_t<float>(x, dy, g, rows, n, eps, dx, dg, rinv, st);
+}
 
 hipError_t launch_attention_backward(int dtype, const AttnBwdArgs &a, hipStream_t st) {
   if ((int64_t)a.BH * a.S == 0) return hipSuccess;

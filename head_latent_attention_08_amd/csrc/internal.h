@@ -119,6 +119,10 @@ struct AttnBwdArgs {
   float scale;
 };
 hipError_t launch_attention_backward(int dtype, const AttnBwdArgs &a, hipStream_t st);
+// RMSNorm backward over rows x [rows, n] (contiguous): dx like x, dg fp32 [n],
+// rinv fp32 [rows] scratch.
+hipError_t launch_rmsnorm_backward(int dtype, const void *x, const void *dy, const void *g, int64_t rows, int n,
+                                  float eps, void *dx, float *dg, float *rinv, hipStream_t st);
 
 hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src,
                             int64_t lds, int64_t rows, int width,

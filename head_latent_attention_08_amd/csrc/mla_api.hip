@@ -1032,6 +1032,28 @@ mla_status mla_attention_backward(int32_t dtype, int64_t batch_heads, int64_t se
   return MLA_OK;
 }
 
+mla_status mla_rmsnorm_backward(int32_t dtype, const void *x, const void *dy, const void *g, int64_t rows,
+                                int32_t n, float eps, void *dx, float *dg, void *workspace, size_t workspace_bytes,
+                                void *hip_stream) {
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "dtype %d is neither 0 (fp32) nor 1 (bf16)", dtype);
+  if (rows < 0 || rows > INT32_MAX) return fail(MLA_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31 - 1]");
+  if (n < 1 || n > (1 << 20)) return fail(MLA_ERR_INVALID_ARGUMENT, "n must be in [1, 2^20]");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MLA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (rows == 0) return MLA_OK;
+  const void *ptrs[] = {x, dy, g, dx, dg, workspace};
+  for (const void *p : ptrs) {
+    if (!p) return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor or the workspace is NULL");
+    if ((uintptr_t)p % 4) return fail(MLA_ERR_INVALID_ARGUMENT, "tensors and workspace must be 4-byte aligned");
+  }
+  if (workspace_bytes < (size_t)rows * sizeof(float))
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", (size_t)rows * sizeof(float));
+  MLA_HIP(launch_rmsnorm_backward(dtype == MLA_DTYPE_BF16 ? BF16 : F32, x, dy, g, rows, n, eps, dx, dg,
+                                  reinterpret_cast<float *>(workspace), (hipStream_t)hip_stream),
+          "rmsnorm backward");
+  return MLA_OK;
+}
+
 int64_t mla_fp8_scale_pitch(int64_t rows) { return rows < 0 ? -1 : fp8_scale_pitch(rows); }
 
 static mla_status check_fp8_quant(const void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ldx,

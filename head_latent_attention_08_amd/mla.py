@@ -120,6 +120,9 @@ def load_library(path: str = LIB_PATH):
                                            ctypes.c_float, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     for fn in ("mla_attention_backward_workspace_size", "mla_attention_backward"):
         getattr(lib, fn).restype = st
+    lib.mla_rmsnorm_backward.argtypes = [ctypes.c_int32, P, P, P, i64, ctypes.c_int32, ctypes.c_float, P, P,
+                                         P, ctypes.c_size_t, P]
+    lib.mla_rmsnorm_backward.restype = st
     lib.mla_fp8_scale_pitch.argtypes = [i64]
     lib.mla_fp8_scale_pitch.restype = i64
     lib.mla_fp8_quantize_rows.argtypes = [P, ctypes.c_int32, i64, i64, i64, P, i64, P, i64, P]
@@ -433,6 +436,22 @@ def mla_attention_backward(q, k, v, o, dout, scale: float, workspace=None, strea
         dt, bh, S, dqk, dv_, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(dq), _ptr(dk),
         _ptr(dvt), _ptr(workspace), workspace.numel(), _stream(stream)))
     return dq, dk, dvt
+
+
+def mla_rmsnorm_backward(x, dy, g, eps: float, stream=None):
+    """(dx, dg) of the RMSNorm y = x r g over the last axis; x, dy [rows, n]
+    and g [n] contiguous device tensors of one dtype; dg is fp32."""
+    if any(not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype for t in (x, dy, g)):
+        raise ValueError("x, dy and g must be contiguous device tensors of one dtype")
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[x.dtype]
+    n = x.shape[-1]
+    rows = x.numel() // n
+    dx = torch.empty_like(x)
+    dg = torch.empty(n, dtype=torch.float32, device=x.device)
+    ws = torch.empty(max(rows, 1), dtype=torch.float32, device=x.device)
+    _check(load_library().mla_rmsnorm_backward(dt, _ptr(x), _ptr(dy), _ptr(g), rows, n, eps, _ptr(dx), _ptr(dg),
+                                               _ptr(ws), ws.numel() * 4, _stream(stream)))
+    return dx, dg
 
 
 def mla_fp8_scale_pitch(rows: int) -> int:

@@ -367,6 +367,20 @@ MLA_API mla_status mla_attention_backward(int32_t dtype, int64_t batch_heads, in
                                   const void *dout, void *dq, void *dk, void *dv,
                                   void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* RMSNorm backward (the norm on c_q of the MLA module of "The Evolving
+ * Transformer -- DeepSeek V2 & V3", section 01; y = x r g with
+ * r = (mean(x^2) + eps)^-1/2 per row): dx = r (g dy) - x r^3 mean(x g dy) and
+ * dg = sum over rows of dy x r.  x, dy, dx [rows, n] contiguous and g [n] in
+ * dtype (fp32 or bf16); dg fp32 [n] (summed over rows in order:
+ * deterministic); the workspace holds 4 bytes per row.  Device pointers,
+ * 4-byte aligned, owned by the caller.
+ * Status: INVALID_ARGUMENT for NULL or misaligned pointers (rows > 0),
+ * rows < 0 or > 2^31 - 1, n < 1 or > 2^20, eps < 0 or non-finite, a bad
+ * dtype; WORKSPACE_TOO_SMALL below 4 * rows bytes; HIP for a failed launch. */
+MLA_API mla_status mla_rmsnorm_backward(int32_t dtype, const void *x, const void *dy, const void *g,
+                                int64_t rows, int32_t n, float eps, void *dx, float *dg,
+                                void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* ---------------------------------------------------------- measurement
  * While set, every mla_prefill_forward / mla_decode_absorbed call made on
  * this thread records events[k] (hipEvent_t handles the caller created) on

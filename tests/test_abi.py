@@ -268,3 +268,16 @@ def test_attention_backward_arguments_rejected_without_launch():
         assert call(**kw) == 1, kw
     assert call(wsb=100) == 3                      # workspace too small
     assert call(bh=0, ptr=None, ws=None) == 0      # nothing to do, nothing launched
+
+
+def test_rmsnorm_backward_arguments_rejected_without_launch():
+    lib = m.load_library()
+    P = ctypes.c_void_p
+    fake = P(1 << 40)
+    def call(dtype=0, rows=4, n=64, eps=1e-6, ptr=fake, ws=fake, wsb=64):
+        return lib.mla_rmsnorm_backward(dtype, ptr, ptr, ptr, rows, n, ctypes.c_float(eps), ptr, ptr, ws, wsb, None)
+    for kw in (dict(dtype=3), dict(rows=-1), dict(n=0), dict(n=(1 << 20) + 1), dict(eps=-1.0),
+               dict(eps=float("nan")), dict(ptr=None), dict(ptr=P((1 << 40) + 2)), dict(ws=None)):
+        assert call(**kw) == 1, kw
+    assert call(wsb=8) == 3
+    assert call(rows=0, ptr=None, ws=None) == 0

@@ -85,3 +85,27 @@ def test_rope_backward_is_rotation_by_negated_positions():
         lhs = np.sum(orc.apply_rope(x, pos.astype(np.int64), cfg) * y)
         rhs = np.sum(x * ref)
         assert abs(lhs - rhs) <= 1e-9 * (abs(lhs) + 1)
+
+
+@pytest.mark.parametrize("dtype,rows,n", [("fp32", 300, 1536), ("fp32", 7, 100), ("bf16", 257, 1536)])
+def test_rmsnorm_backward_matches_oracle(dtype, rows, n):
+    # the RMSNorm on c_q (r_q = 1536 at V3): dx per row, dg over all rows
+    m = _m()
+    bf = dtype == "bf16"
+    rng = np.random.default_rng(rows + n)
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    dy = rng.standard_normal((rows, n)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(n)).astype(np.float32)
+    if bf:
+        x, dy, g = si.round_bf16(x), si.round_bf16(dy), si.round_bf16(g)
+    td = torch.bfloat16 if bf else torch.float32
+    dev = lambda a: torch.from_numpy(a).to(td).cuda()
+    dx, dg = m.mla_rmsnorm_backward(dev(x), dev(dy), dev(g), 1e-6)
+    torch.cuda.synchronize()
+    rdx, rdg = ab.rmsnorm_backward(x, g, dy, 1e-6)
+    assert_close_rows(dx.float().cpu().numpy(), rdx, dtype, "dx")
+    # dg sums rows of products rounded per step in fp32: relative to the
+    # summed magnitudes
+    mag = np.sum(np.abs(dy.astype(np.float64) * x), axis=0) / np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=1)).min()
+    err = np.abs(dg.cpu().numpy() - rdg)
+    assert np.all(err <= 1e-5 * mag + 1e-6), err.max()
