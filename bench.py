@@ -44,17 +44,17 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "1a3d437ba863dcf428fa406e9ffce47827b53d72f5382ed9d3b04e39b335124b",
-        "FETCH_SIZE_KiB": 242949.3, "WRITE_SIZE_KiB": 131080.5},
+        "sha256": "ea85110b5eed357482d032ed7bc86a802bbe10f39fb890d72b6950e737c47c6d",
+        "FETCH_SIZE_KiB": 242840.7, "WRITE_SIZE_KiB": 131082.3},
     "out_proj": {
-        "sha256": "271d66d0b1d94d15fa8482fca4bce65e280ab064bb80b4cda277d769fa320c0b",
-        "FETCH_SIZE_KiB": 1513323.5, "WRITE_SIZE_KiB": 57792.0},
+        "sha256": "f2f7684e95ac95bc1f6cc80c8c9f4e0b76da1cc03f961c0ce621c58002cc43a8",
+        "FETCH_SIZE_KiB": 1512488.6, "WRITE_SIZE_KiB": 57792.0},
     "latent_attention": {
-        "sha256": "11a1c2ef811f88f020b9959285eac89e154fb3b4b7e269dd5095ff8e9b5c8684",
-        "FETCH_SIZE_KiB": 181372.8, "WRITE_SIZE_KiB": 76843.0},
+        "sha256": "a0abdfcb7ad6f8d0b728cb1fa3a739ec974d702ec4f12213538ce9f9a77d3c47",
+        "FETCH_SIZE_KiB": 181369.2, "WRITE_SIZE_KiB": 76843.0},
     "fp8_out_proj": {
-        "sha256": "e9d138f0b318379ea0c39c55ac233d5204ae42f839f53f4d02f38b641cebf2ab",
-        "FETCH_SIZE_KiB": 380538.4, "WRITE_SIZE_KiB": 57792.0},
+        "sha256": "021cff372681f1e6cbe0171176805f770b6a5ad0c8cfd8630917d4935dad36af",
+        "FETCH_SIZE_KiB": 380698.0, "WRITE_SIZE_KiB": 57792.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
