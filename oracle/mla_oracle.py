@@ -35,7 +35,9 @@ Readings where the pages are silent (each is listed in the design doc):
 * inv_freq_i = theta^(-2i/d_r); pair i of both conventions uses inv_freq_i;
   the rotation is by +angle; positions start at 0; angles are float64.
 * YaRN uses the index-space linear ramp between the correction dims of
-  beta_fast and beta_slow (parity unpinned by the pages beyond its reductions).
+  beta_fast and beta_slow; the pages fix only its reductions, and the tests
+  pin the rest to the DeepSeek-V3 code of `transformers` that the RoPE page
+  names.
 * Decode: the new token sits at position L_b (= rows already cached) and
   attends to cache rows 0..L_b including itself; the cache holds c_kv and the
   post-RoPE k_pe, in the layout of the convention in use.

@@ -1,0 +1,121 @@
+"""A CPU model of the bf16 storage of the HIP path's intermediates.
+
+TEST INFRASTRUCTURE ONLY: it derives the tolerances of the GPU parity tests
+whose inputs cannot meet the plain bf16 bound.  It is the oracle's arithmetic
+(float64, the same steps) with a round-to-nearest-even bf16 rounding inserted
+wherever the HIP path stores a tensor in bf16 between kernels or feeds one to
+a bf16 matrix core:
+
+* prefill: c_q (the down-projection output) and its RMS-normalised value,
+  c_kv, k_pe (before and after RoPE), q_nope, q_pe (before and after RoPE),
+  k_nope, v, the softmax probabilities fed to the P V product, o, and y;
+* absorbed decode: c_q and its normalised value, q_nope, q_pe (before and
+  after RoPE), the new latent row (before and after RoPE), q_lat, the
+  probabilities fed to the P C product, o_lat, o and y.
+
+Everything else is exact (float64): the products' accumulation, the softmax
+max and sum.  So the model's error against the oracle is the error that bf16
+storage alone forces on a given input, whatever the kernels do; a kernel
+that meets it within a small factor adds little error of its own.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as orc
+from synth_inputs import round_bf16
+
+
+def _round(a):
+    return round_bf16(np.asarray(a, dtype=np.float64).astype(np.float32)).astype(np.float64)
+
+
+def _keep(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def _attention_bf16_p(q, k, v, scale, _r, q_pos=None):
+    """Causal softmax attention with the probabilities rounded to bf16 for
+    the P V product (the normaliser is the exact sum)."""
+    sq, sk = q.shape[0], k.shape[0]
+    if q_pos is None:
+        q_pos = np.arange(sq)
+    s = scale * (q @ k.T)
+    s = np.where(np.arange(sk)[None, :] > np.asarray(q_pos)[:, None], -np.inf, s)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    return (_r(p) @ v) / p.sum(axis=-1, keepdims=True)
+
+
+def bound(strict: float, modelled: float) -> float:
+    """Tolerance for an input whose bf16 storage alone forces an error of
+    ``modelled``: the strict bound, or 1.6 x the modelled error where that is
+    larger (the HIP path's own roundings fall differently from the model's,
+    so its error scatters around the modelled one)."""
+    return max(strict, 1.6 * modelled)
+
+
+def prefill_bf16(cfg: orc.Cfg, w: dict, x, rounding: bool = True):
+    """y [B, S, D] of the prefill with bf16 storage of the intermediates
+    (rounding=False: no rounding at all, i.e. the oracle's result)."""
+    _r = _round if rounding else _keep
+    x = np.asarray(x, dtype=np.float64)
+    B, S, _ = x.shape
+    H = cfg.num_attention_heads
+    dn, dr, dv = cfg.qk_nope_head_dim, cfg.qk_rope_head_dim, cfg.v_head_dim
+    f = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
+    pos = np.arange(S)
+    c_q = _r(x @ f["w_down_q"].T)
+    c_qn = _r(orc.rmsnorm(c_q, f["q_norm"], cfg.rms_norm_eps))
+    q_nope = _r(c_qn @ f["w_up_q"].T).reshape(B, S, H, dn)
+    q_pe = _r(c_qn @ f["w_qr"].T).reshape(B, S, H, dr)
+    c_kv = _r(x @ f["w_down_kv"].T)
+    k_pe = _r(x @ f["w_kr"].T)
+    q_pe = _r(np.stack([orc.apply_rope(q_pe[b], pos, cfg) for b in range(B)]))
+    k_pe = _r(np.stack([orc.apply_rope(k_pe[b], pos, cfg) for b in range(B)]))
+    k_nope = _r(c_kv @ f["w_up_k"].T).reshape(B, S, H, dn)
+    v = _r(c_kv @ f["w_up_v"].T).reshape(B, S, H, dv)
+    scale = orc.softmax_scale(cfg)
+    o = np.empty((B, S, H, dv))
+    for b in range(B):
+        for h in range(H):
+            q = np.concatenate([q_nope[b, :, h], q_pe[b, :, h]], axis=-1)
+            k = np.concatenate([k_nope[b, :, h], k_pe[b]], axis=-1)
+            o[b, :, h] = _attention_bf16_p(q, k, v[b, :, h], scale, _r)
+    o = _r(o).reshape(B, S, H * dv)
+    return _r(o @ f["wo"].T)
+
+
+def decode_absorbed_bf16(cfg: orc.Cfg, w: dict, x, cache, lens, rounding: bool = True):
+    """y [B, D] of one absorbed decode step with bf16 storage of the
+    intermediates (cache rows are bf16 values already; rounding=False: the
+    oracle's result)."""
+    _r = _round if rounding else _keep
+    x = np.asarray(x, dtype=np.float64)
+    B = x.shape[0]
+    H = cfg.num_attention_heads
+    dn, dr, dv = cfg.qk_nope_head_dim, cfg.qk_rope_head_dim, cfg.v_head_dim
+    r = cfg.kv_lora_rank
+    f = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
+    wuk = f["w_up_k"].reshape(H, dn, r)
+    wuv = f["w_up_v"].reshape(H, dv, r)
+    scale = orc.softmax_scale(cfg)
+    y = np.empty((B, cfg.hidden_size))
+    for b in range(B):
+        L = int(lens[b])
+        xb = x[b]
+        c_qn = _r(orc.rmsnorm(_r(xb @ f["w_down_q"].T), f["q_norm"], cfg.rms_norm_eps))
+        q_nope = _r(c_qn @ f["w_up_q"].T).reshape(H, dn)
+        q_pe = _r(orc.apply_rope(_r(c_qn @ f["w_qr"].T).reshape(1, H, dr), [L], cfg)[0])
+        c_new = _r(xb @ f["w_down_kv"].T)
+        k_new = _r(orc.apply_rope(_r(xb @ f["w_kr"].T)[None, :], [L], cfg)[0])
+        rows = np.concatenate([np.asarray(cache[b, :L], dtype=np.float64),
+                               np.concatenate([c_new, k_new])[None]], axis=0)
+        c, kp = rows[:, :r], rows[:, r:]
+        q_lat = _r(np.einsum("hd,hdr->hr", q_nope, wuk))
+        s = scale * (q_lat @ c.T + q_pe @ kp.T)
+        p = np.exp(s - s.max(axis=-1, keepdims=True))
+        o_lat = _r((_r(p) @ c) / p.sum(axis=-1, keepdims=True))
+        o = _r(np.einsum("hvr,hr->hv", wuv, o_lat))
+        y[b] = _r(o.reshape(-1) @ f["wo"].T)
+    return y
