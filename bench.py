@@ -261,6 +261,122 @@ def attention_backward_line(m, S, log, reps=2):
             "note": "vector-ALU kernels (no MFMA yet)"}
 
 
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _short_name(name):
+    """Kernel name without namespaces and arguments.  rocprofv3 prints some
+    names mangled; those in this library's namespace are decoded here (the
+    kernel name and its type / integer template arguments), since the
+    system demangler does not know the bf16 type's code."""
+    import re
+    m = re.match(r"_ZN3mla12_GLOBAL__N_1(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        rest = name[m.end():]
+        base, rest = rest[:n], rest[n:]
+        args = []
+        if rest.startswith("I"):
+            rest = rest[1:]
+            while rest and not rest.startswith("E"):
+                t = re.match(r"DF16b|f|L[ib]\d+E|Li-?\d+E", rest)
+                if not t:
+                    break
+                tok = t.group(0)
+                args.append({"DF16b": "bf16", "f": "float"}.get(
+                    tok, tok[2:-1] if tok.startswith("Li") else ("true" if tok == "Lb1E" else "false")))
+                rest = rest[t.end():]
+        return base + (f"<{', '.join(args)}>" if args else "")
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "").replace("mla::", "")
+    return n.split("(")[0][:96]
+
+
+def summarize_trace(path):
+    """Markdown table of a rocprofv3 kernel trace (kernel_trace.csv): one row
+    per (kernel, grid size), with the launch count and the mean, median and
+    min duration.  Separate rows per grid keep the projection GEMMs apart."""
+    import statistics
+    rows = _read_csv(path)
+    groups = {}
+    for r in rows:
+        key = (_short_name(r["Kernel_Name"]),
+               int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
+               * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1),
+               int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 0)) or 0))
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault(key, []).append(d)
+    out = ["| kernel | grid (threads) | workgroups | launches | mean us | median us | min us | total us |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{name}` | {grid} | {grid // wg if wg else '-'} | {len(ds)} | "
+                   f"{statistics.mean(ds):.1f} | {statistics.median(ds):.1f} | {min(ds):.1f} | "
+                   f"{sum(ds):.1f} |")
+    return "\n".join(out)
+
+
+def summarize_counters(path):
+    """Markdown table of a rocprofv3 --pmc run (counter_collection.csv): per
+    (kernel, grid size), the mean of each counter over its dispatches, plus
+    what the counters give directly.  GRBM_GUI_ACTIVE is summed over the
+    eight XCDs, so GRBM_GUI_ACTIVE / 8 / duration is the clock; the SQ cycle
+    counters are summed over the SIMDs (1024) or CUs (256) they name:
+      clock MHz   = GRBM_GUI_ACTIVE / 8 / duration
+      MFMA busy   = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024)
+      bf16 MFMA TFLOP/s executed = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 / duration
+      LDS busy    = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / 8 x 256)
+      LDS conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+    (MFMA busy cycles count 1024 bf16 FLOPs each: one SIMD's dense rate.)"""
+    rows = _read_csv(path)
+    groups = {}
+    for r in rows:
+        key = (_short_name(r["Kernel_Name"]), int(r.get("Grid_Size", 0) or 0))
+        g = groups.setdefault(key, {"dispatch": {}, "dur": {}})
+        did = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        g["dispatch"].setdefault(did, {})
+        g["dispatch"][did][r["Counter_Name"]] = g["dispatch"][did].get(r["Counter_Name"], 0.0) + \
+            float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            g["dur"][did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    names = sorted({c for g in groups.values() for d in g["dispatch"].values() for c in d})
+    head = "| kernel | grid | dispatches | mean us | " + " | ".join(names)
+    extra = []
+    has = lambda *cs: all(c in names for c in cs)
+    if has("GRBM_GUI_ACTIVE"):
+        extra.append("clock MHz")
+    if has("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"):
+        extra.append("MFMA busy")
+    if has("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+        extra.append("bf16 MFMA TFLOP/s")
+    if has("SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"):
+        extra.append("LDS busy")
+    if has("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT"):
+        extra.append("LDS conflict share")
+    out = [head + "".join(f" | {e}" for e in extra) + " |",
+           "|" + "---|" * (4 + len(names) + len(extra))]
+    for (name, grid), g in sorted(groups.items()):
+        ds = list(g["dispatch"].values())
+        mean = {c: sum(d.get(c, 0.0) for d in ds) / len(ds) for c in names}
+        dur = sum(g["dur"].values()) / len(g["dur"]) if g["dur"] else float("nan")
+        cells = [f"`{name}`", str(grid), str(len(ds)), f"{dur:.1f}"] + [f"{mean[c]:.4g}" for c in names]
+        cyc = mean.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        if "clock MHz" in extra:
+            cells.append(f"{cyc / dur:.0f}")
+        if "MFMA busy" in extra:
+            cells.append(f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024.0):.3f}" if cyc else "-")
+        if "bf16 MFMA TFLOP/s" in extra:
+            cells.append(f"{512.0 * mean['SQ_INSTS_VALU_MFMA_MOPS_BF16'] / (dur * 1e-6) / 1e12:.1f}")
+        if "LDS busy" in extra:
+            cells.append(f"{mean['SQ_LDS_IDX_ACTIVE'] / (cyc * 256.0):.3f}" if cyc else "-")
+        if "LDS conflict share" in extra:
+            a = mean["SQ_LDS_IDX_ACTIVE"]
+            cells.append(f"{mean['SQ_LDS_BANK_CONFLICT'] / a:.3f}" if a else "-")
+        out.append("| " + " | ".join(cells) + " |")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +397,12 @@ def main():
                     help="decode cache replicas rotated per step (defeats the 256 MB MALL)")
     ap.add_argument("--kernel-sha", action="store_true",
                     help="print the source hashes the traffic table is keyed on and exit")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print a per-(kernel, grid) markdown table of a rocprofv3 kernel "
+                         "trace and exit (no GPU)")
+    ap.add_argument("--summarize-counters", metavar="COUNTER_COLLECTION_CSV",
+                    help="print a per-(kernel, grid) markdown table of a rocprofv3 --pmc "
+                         "run and exit (no GPU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times: the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -292,6 +414,12 @@ def main():
 
     if args.kernel_sha:
         print(json.dumps({k: kernel_sha(k) for k in KERNEL_SOURCES}))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return
 
     import numpy as np

@@ -178,7 +178,19 @@ mla_status check_weights(const mla_weights *w) {
     if (!aligned16(x.p))
       return fail(MLA_ERR_INVALID_ARGUMENT, "weight %s is not 16-byte aligned", x.name);
   }
+  if (w->kv_norm && !aligned16(w->kv_norm))  // optional: NULL means no norm on c_kv
+    return fail(MLA_ERR_INVALID_ARGUMENT, "weight kv_norm is not 16-byte aligned");
   return MLA_OK;
+}
+
+// RMSNorm of c_q (always) and of c_kv (when kv_norm gains are given) in the
+// down-projection output rows [c_q ‖ c_kv ‖ k_pe] of pitch ld.
+hipError_t launch_down_norms(const mla_config &c, const mla_weights *w, char *down, int64_t rows,
+                             int64_t ld, hipStream_t st) {
+  hipError_t e = launch_rmsnorm(c.dtype, down, rows, ld, c.q_lora_rank, w->q_norm, c.rms_norm_eps, st);
+  if (e != hipSuccess || !w->kv_norm) return e;
+  return launch_rmsnorm(c.dtype, down + (size_t)c.q_lora_rank * dtype_size(c.dtype), rows, ld,
+                        c.kv_lora_rank, w->kv_norm, c.rms_norm_eps, st);
 }
 
 struct PrefillPlan {
@@ -405,8 +417,7 @@ static mla_status prefill_common(const mla_config *cfg, const mla_weights *w, co
   }
   // 2. RMSNorm(c_q)
   MLA_MARK(1);
-  MLA_HIP(launch_rmsnorm(c.dtype, down, M, p.ld_down, rq, w->q_norm, c.rms_norm_eps, st),
-          "rmsnorm");
+  MLA_HIP(launch_down_norms(c, w, down, M, p.ld_down, st), "rmsnorm");
   // 3. RoPE of the shared key at positions 0..S-1
   MLA_MARK(2);
   MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, M, S, (int64_t)S * p.ld_down,
@@ -676,7 +687,7 @@ mla_status mla_prefill_chunk(const mla_config *cfg, const mla_weights *w, const 
     g.workspace_bytes = p.gemm_bytes;
     MLA_HIP(launch_gemm(g, st), "down projection");
   }
-  MLA_HIP(launch_rmsnorm(c.dtype, down, M, p.ld_down, rq, w->q_norm, c.rms_norm_eps, st), "rmsnorm");
+  MLA_HIP(launch_down_norms(c, w, down, M, p.ld_down, st), "rmsnorm");
   MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, M, M, (int64_t)M * p.ld_down,
                       p.ld_down, 1, 0, pos, tab, st),
           "rope k_pe");
@@ -853,8 +864,7 @@ mla_status decode_impl(const mla_config *cfg, const mla_weights *w, const void *
     MLA_HIP(launch_gemm(g, st), "decode down projection");
   }
   MLA_MARK(1);
-  MLA_HIP(launch_rmsnorm(c.dtype, down, B, p.ld_down, rq, w->q_norm, c.rms_norm_eps, st),
-          "decode rmsnorm");
+  MLA_HIP(launch_down_norms(c, w, down, B, p.ld_down, st), "decode rmsnorm");
   // 2. RoPE of the new key at position lens[b], then append [c_kv ‖ k_pe] at row lens[b]
   MLA_MARK(2);
   MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, B, B, 0, p.ld_down, 1, 0, pos,
@@ -1001,35 +1011,60 @@ mla_status mla_attention_backward_workspace_size(int64_t batch_heads, int64_t se
   return MLA_OK;
 }
 
-mla_status mla_attention_backward(int32_t dtype, int64_t batch_heads, int64_t seq, int32_t d_qk, int32_t d_v,
-                                  float scale, const void *q, const void *k, const void *v, const void *o,
-                                  const void *dout, void *dq, void *dk, void *dv, void *workspace,
-                                  size_t workspace_bytes, void *hip_stream) {
+}  // extern "C"
+
+namespace {
+// Checks shared by mla_attention_backward and its allocation-free variant;
+// *need receives the scratch bytes the call uses.
+mla_status check_attention_backward(int32_t dtype, int64_t batch_heads, int64_t seq, int32_t d_qk, int32_t d_v,
+                                    float scale, const void *const *ptrs, int n_ptrs, size_t *need) {
   if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16)
     return fail(MLA_ERR_INVALID_ARGUMENT, "dtype %d is neither 0 (fp32) nor 1 (bf16)", dtype);
-  size_t need = 0;
-  mla_status s = mla_attention_backward_workspace_size(batch_heads, seq, &need);
+  mla_status s = mla_attention_backward_workspace_size(batch_heads, seq, need);
   if (s != MLA_OK) return s;
   if (d_qk < 8 || d_qk > 256 || d_qk % 8 || d_v < 8 || d_v > 256 || d_v % 8)
     return fail(MLA_ERR_INVALID_ARGUMENT, "d_qk and d_v must be multiples of 8 in [8, 256]");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
   if (batch_heads * seq == 0) return MLA_OK;
-  const void *ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
-  for (const void *p : ptrs) {
-    if (!p) return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor or the workspace is NULL");
-    if ((uintptr_t)p % 16) return fail(MLA_ERR_INVALID_ARGUMENT, "tensors and workspace must be 16-byte aligned");
+  for (int i = 0; i < n_ptrs; ++i) {
+    if (!ptrs[i]) return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor or the workspace is NULL");
+    if ((uintptr_t)ptrs[i] % 16)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "tensors and workspace must be 16-byte aligned");
   }
-  if (workspace_bytes < need)
-    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  return MLA_OK;
+}
+
+mla_status run_attention_backward(int32_t dtype, int64_t batch_heads, int64_t seq, int32_t d_qk, int32_t d_v,
+                                  float scale, const void *q, const void *k, const void *v, const void *o,
+                                  const void *dout, void *dq, void *dk, void *dv, float *row_stats,
+                                  void *hip_stream) {
   AttnBwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dvo = dv;
-  a.lse = reinterpret_cast<float *>(workspace);
+  a.lse = row_stats;
   a.delta = a.lse + batch_heads * seq;
   a.BH = (int)batch_heads; a.S = (int)seq; a.dqk = d_qk; a.dv = d_v; a.scale = scale;
   MLA_HIP(launch_attention_backward(dtype == MLA_DTYPE_BF16 ? BF16 : F32, a, (hipStream_t)hip_stream),
           "attention backward");
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_attention_backward(int32_t dtype, int64_t batch_heads, int64_t seq, int32_t d_qk, int32_t d_v,
+                                  float scale, const void *q, const void *k, const void *v, const void *o,
+                                  const void *dout, void *dq, void *dk, void *dv, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream) {
+  size_t need = 0;
+  const void *ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+  mla_status s = check_attention_backward(dtype, batch_heads, seq, d_qk, d_v, scale, ptrs, 9, &need);
+  if (s != MLA_OK || batch_heads * seq == 0) return s;
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  return run_attention_backward(dtype, batch_heads, seq, d_qk, d_v, scale, q, k, v, o, dout, dq, dk, dv,
+                                reinterpret_cast<float *>(workspace), hip_stream);
 }
 
 mla_status mla_rmsnorm_backward(int32_t dtype, const void *x, const void *dy, const void *g, int64_t rows,

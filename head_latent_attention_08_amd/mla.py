@@ -58,7 +58,8 @@ class Config(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "w_down_q", "q_norm", "w_up_q", "w_qr", "w_down_kv", "w_kr", "w_up_k", "w_up_v", "wo")]
+        "w_down_q", "q_norm", "w_up_q", "w_qr", "w_down_kv", "kv_norm", "w_kr", "w_up_k", "w_up_v",
+        "wo")]
 
 
 class PrefillLayout(ctypes.Structure):
@@ -73,6 +74,8 @@ class DecodeLayout(ctypes.Structure):
 
 
 WEIGHT_NAMES = [f[0] for f in Weights._fields_]
+# optional weights: absent or None means NULL (kv_norm: no norm on c_kv)
+OPTIONAL_WEIGHTS = ("kv_norm",)
 
 _lib = None
 
@@ -200,11 +203,16 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def make_weights(w: dict) -> Weights:
+    ptrs = []
     for n in WEIGHT_NAMES:
-        t = w[n]
+        t = w.get(n) if n in OPTIONAL_WEIGHTS else w[n]
+        if t is None:
+            ptrs.append(None)
+            continue
         if not (t.is_cuda and t.is_contiguous()):
             raise ValueError(f"weight {n} must be a contiguous device tensor")
-    return Weights(*[w[n].data_ptr() for n in WEIGHT_NAMES])
+        ptrs.append(t.data_ptr())
+    return Weights(*ptrs)
 
 
 def mla_softmax_scale(cfg: MlaConfig) -> float:
@@ -421,9 +429,7 @@ def mla_prefill_chunk(cfg: MlaConfig, weights: dict, x: torch.Tensor, latent_cac
 def mla_attention_backward(q, k, v, o, dout, scale: float, workspace=None, stream=None):
     """(dq, dk, dv) of causal attention; q, k [..., S, d_qk], v, o, dout
     [..., S, d_v], contiguous, one dtype (fp32 or bf16)."""
-    ts = (q, k, v, o, dout)
-    if any(not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype for t in ts):
-        raise ValueError("q, k, v, o and dout must be contiguous device tensors of one dtype")
+    _check_attention_backward_shapes(q, k, v, o, dout)
     dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[q.dtype]
     S, dqk, dv_ = q.shape[-2], q.shape[-1], v.shape[-1]
     bh = q.numel() // max(S * dqk, 1)
@@ -438,9 +444,28 @@ def mla_attention_backward(q, k, v, o, dout, scale: float, workspace=None, strea
     return dq, dk, dvt
 
 
+def _check_attention_backward_shapes(q, k, v, o, dout):
+    ts = (q, k, v, o, dout)
+    # only q's S and d_qk and v's d_v reach the library: every other shape
+    # must follow from them, or the kernels would read past the buffers
+    if q.dim() < 2 or k.shape != q.shape:
+        raise ValueError(f"k {tuple(k.shape)} must have q's shape {tuple(q.shape)}")
+    if v.shape[:-1] != q.shape[:-1]:
+        raise ValueError(f"v {tuple(v.shape)} must match q {tuple(q.shape)} but for the last axis")
+    if o.shape != v.shape or dout.shape != v.shape:
+        raise ValueError(f"o {tuple(o.shape)} and dout {tuple(dout.shape)} must have v's shape "
+                         f"{tuple(v.shape)}")
+    if any(not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype for t in ts):
+        raise ValueError("q, k, v, o and dout must be contiguous device tensors of one dtype")
+
+
 def mla_rmsnorm_backward(x, dy, g, eps: float, stream=None):
     """(dx, dg) of the RMSNorm y = x r g over the last axis; x, dy [rows, n]
     and g [n] contiguous device tensors of one dtype; dg is fp32."""
+    if x.dim() < 1 or dy.shape != x.shape:
+        raise ValueError(f"dy {tuple(dy.shape)} must have x's shape {tuple(x.shape)}")
+    if g.shape != (x.shape[-1],):
+        raise ValueError(f"g {tuple(g.shape)} must be ({x.shape[-1]},)")
     if any(not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype for t in (x, dy, g)):
         raise ValueError("x, dy and g must be contiguous device tensors of one dtype")
     dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[x.dtype]

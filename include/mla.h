@@ -16,7 +16,9 @@
  *
  * Where the pages are silent this library reads them as follows:
  *   - RMSNorm(c_q) = c_q * (mean(c_q^2) + eps)^-1/2 * q_norm, before both
- *     w_up_q and w_qr; there is no norm on c_kv.
+ *     w_up_q and w_qr; there is no norm on c_kv unless the caller passes
+ *     kv_norm gains (checkpoints that normalise the latent), in which case
+ *     c_kv gets the same RMSNorm before it is cached or up-projected.
  *   - k_pe = w_kr x is ONE shared rope_dim vector per token (w_kr is
  *     [rope_dim, hidden]), broadcast to every head.
  *   - softmax scale = (nope + rope)^-1/2, times mscale(factor,
@@ -104,6 +106,11 @@ typedef struct {                  /* device pointers, nn.Linear [out][in]      *
   const void *w_up_q;             /* [H*d_n, r_q]                              */
   const void *w_qr;               /* [H*d_r, r_q]                              */
   const void *w_down_kv;          /* [r_kv, D]                                 */
+  const void *kv_norm;            /* [r_kv] RMSNorm gain of c_kv, or NULL:     */
+                                  /* NULL = no norm on c_kv (the pages name    */
+                                  /* none); non-NULL: c_kv is RMS-normalised   */
+                                  /* (eps = rms_norm_eps) with these gains     */
+                                  /* before it is cached or up-projected       */
   const void *w_kr;               /* [d_r, D]   shared RoPE key              */
   const void *w_up_k;             /* [H*d_n, r_kv]                             */
   const void *w_up_v;             /* [H*d_v, r_kv]                             */

@@ -20,6 +20,7 @@ from .mla_oracle import (  # noqa: F401
     apply_rope,
     deinterleave_perm,
     rmsnorm,
+    latent,
     softmax_scale,
     causal_attention,
     mla_prefill,

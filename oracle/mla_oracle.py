@@ -28,7 +28,8 @@ Sources (pages, by title and section):
 Readings where the pages are silent (each is listed in the design doc):
 
 * RMSNorm is x * (mean(x^2) + eps)^-1/2 * g, applied to c_q before both w_up_q
-  and w_qr; there is no norm on c_kv.
+  and w_qr; there is no norm on c_kv (optional kv_norm gains, for
+  checkpoints that normalise the latent, apply the same norm to c_kv).
 * The RoPE key k_pe is one shared d_r vector per token, broadcast to all heads.
 * The softmax scale is (d_nope + d_rope)^-1/2, also in decode; with YaRN it is
   multiplied by mscale(factor, mscale_all_dim)^2.
@@ -201,6 +202,16 @@ def rmsnorm(x, g, eps):
     return x / np.sqrt(ms + eps) * g
 
 
+def latent(cfg: Cfg, w: dict, x):
+    """c_kv = x W_dkv^T, the cached latent.  The pages put no norm on it; a
+    checkpoint may carry RMSNorm gains for it (w["kv_norm"]), which are then
+    applied like the norm on c_q."""
+    c_kv = x @ _f64(w["w_down_kv"]).T
+    if w.get("kv_norm") is not None:
+        c_kv = rmsnorm(c_kv, _f64(w["kv_norm"]), cfg.rms_norm_eps)
+    return c_kv
+
+
 def softmax_scale(cfg: Cfg) -> float:
     """1/sqrt(d_nope + d_rope), times mscale(factor, mscale_all_dim)^2 with
     YaRN (the MLA listing divides the scores by sqrt(dk))."""
@@ -255,7 +266,7 @@ def mla_prefill(cfg: Cfg, w: dict, x, want_intermediates: bool = False):
     q_nope = (c_qn @ _f64(w["w_up_q"]).T).reshape(B, S, H, dn)
     q_pe = (c_qn @ _f64(w["w_qr"]).T).reshape(B, S, H, dr)
     # KV path: the cached latent, and the shared RoPE key bypassing it
-    c_kv = x @ _f64(w["w_down_kv"]).T
+    c_kv = latent(cfg, w, x)
     k_pe = x @ _f64(w["w_kr"]).T  # [B, S, dr]
     q_pe = np.stack([apply_rope(q_pe[b], pos, cfg) for b in range(B)])
     k_pe = np.stack([apply_rope(k_pe[b], pos, cfg) for b in range(B)])
@@ -313,7 +324,7 @@ def mla_prefill_rows(cfg: Cfg, w: dict, x, rows, batch: int = 0):
     dn, dr, dv = cfg.qk_nope_head_dim, cfg.qk_rope_head_dim, cfg.v_head_dim
     rows = np.asarray(rows, dtype=np.int64)
     pos = np.arange(S)
-    c_kv = xb @ _f64(w["w_down_kv"]).T
+    c_kv = latent(cfg, w, xb)
     k_pe = apply_rope(xb @ _f64(w["w_kr"]).T, pos, cfg)
     xr = xb[rows]
     c_qn = rmsnorm(xr @ _f64(w["w_down_q"]).T, _f64(w["q_norm"]), cfg.rms_norm_eps)
@@ -345,7 +356,7 @@ def _decode_new_token(cfg: Cfg, w: dict, xb, p):
     c_qn = rmsnorm(xb @ _f64(w["w_down_q"]).T, _f64(w["q_norm"]), cfg.rms_norm_eps)
     q_nope = (c_qn @ _f64(w["w_up_q"]).T).reshape(H, dn)
     q_pe = apply_rope((c_qn @ _f64(w["w_qr"]).T).reshape(1, H, dr), [p], cfg)[0]
-    c_kv = xb @ _f64(w["w_down_kv"]).T
+    c_kv = latent(cfg, w, xb)
     k_pe = apply_rope((xb @ _f64(w["w_kr"]).T)[None, :], [p], cfg)[0]
     return q_nope, q_pe, np.concatenate([c_kv, k_pe])
 

@@ -42,6 +42,35 @@ def test_library_exports_every_declared_symbol():
     assert exported == _declared()
 
 
+def test_weights_struct_matches_header():
+    # the binding's field order is the header's mla_weights order
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct {                  /* device pointers"):]
+    body = body[:body.index("} mla_weights;")]
+    fields = re.findall(r"const void \*(\w+);", body)
+    assert fields == [f[0] for f in b.Weights._fields_]
+    assert "kv_norm" in fields and fields.index("kv_norm") == fields.index("w_down_kv") + 1
+
+
+def test_kv_norm_is_optional_and_checked():
+    # NULL kv_norm (no norm on c_kv) passes validation up to the workspace
+    # check; a misaligned one is rejected before any launch
+    lib = m.load_library()
+    cfg = m.MlaConfig(**V3)
+    need = m.mla_prefill_workspace_size(cfg, 1, 16)
+    good = ctypes.c_void_p(0x10000)
+    names = [f[0] for f in b.Weights._fields_]
+    ptrs = [0x10000] * len(names)
+    ptrs[names.index("kv_norm")] = 0
+    w = b.Weights(*ptrs)
+    assert _raw_prefill(lib, cfg, w, good, good, good, need - 1) == b.MLA_ERR_WORKSPACE_TOO_SMALL
+    ptrs[names.index("kv_norm")] = 0x10008
+    w = b.Weights(*ptrs)
+    assert _raw_prefill(lib, cfg, w, good, good, good, need) == b.MLA_ERR_INVALID_ARGUMENT
+    assert b"kv_norm" in lib.mla_last_error()
+    assert b.OPTIONAL_WEIGHTS == ("kv_norm",)
+
+
 def test_version_and_scale():
     assert "gfx950" in m.mla_version()
     assert m.mla_softmax_scale(m.MlaConfig(**V3)) == pytest.approx(192 ** -0.5, rel=1e-7)
@@ -126,7 +155,7 @@ def test_varlen_sizes_and_arguments_rejected_without_launch():
     lib = m.load_library()
     c = cfg.c()
     good = ctypes.c_void_p(0x10000)
-    w = b.Weights(*([0x10000] * 9))
+    w = b.Weights(*([0x10000] * 10))
     need = m.mla_prefill_varlen_workspace_size(cfg, 2, 16)
     st = lib.mla_prefill_varlen_forward(ctypes.byref(c), ctypes.byref(w), good, None, 2, 16, good,
                                         None, good, need, None)
@@ -153,7 +182,7 @@ def test_chunk_sizes_and_arguments_rejected_without_launch():
     lib = m.load_library()
     c = cfg.c()
     good = ctypes.c_void_p(0x10000)
-    w = b.Weights(*([0x10000] * 9))
+    w = b.Weights(*([0x10000] * 10))
     need = m.mla_prefill_chunk_workspace_size(cfg, 2, 8, 64, 64)
     st = lib.mla_prefill_chunk(ctypes.byref(c), ctypes.byref(w), good, 2, 8, good, 64, None, 64,
                                good, good, need, None)
@@ -178,10 +207,10 @@ def test_null_and_misaligned_pointers_rejected_without_launch():
     cfg = m.MlaConfig(**V3)
     need = m.mla_prefill_workspace_size(cfg, 1, 16)
     good = ctypes.c_void_p(0x10000)
-    w = b.Weights(*([0x10000] * 9))
+    w = b.Weights(*([0x10000] * 10))
     assert _raw_prefill(lib, cfg, None, good, good, good, need) == b.MLA_ERR_INVALID_ARGUMENT
     assert b"weights" in lib.mla_last_error()
-    wnull = b.Weights(*([0x10000] * 8 + [0]))
+    wnull = b.Weights(*([0x10000] * 9 + [0]))
     assert _raw_prefill(lib, cfg, wnull, good, good, good, need) == b.MLA_ERR_INVALID_ARGUMENT
     assert b"wo" in lib.mla_last_error()
     assert _raw_prefill(lib, cfg, w, None, good, good, need) == b.MLA_ERR_INVALID_ARGUMENT
@@ -281,3 +310,25 @@ def test_rmsnorm_backward_arguments_rejected_without_launch():
         assert call(**kw) == 1, kw
     assert call(wsb=8) == 3
     assert call(rows=0, ptr=None, ws=None) == 0
+
+
+def test_backward_wrappers_check_shapes_before_the_library():
+    # the binding raises on shapes that the C ABI cannot see (it only gets
+    # q's S and d_qk and v's d_v), before any call: CPU tensors suffice
+    import torch
+    q = torch.zeros(2, 16, 24)
+    v = torch.zeros(2, 16, 8)
+    bad = [
+        (torch.zeros(2, 15, 24), v, v, v, "k"),      # shorter k
+        (q, torch.zeros(2, 12, 8), v, v, "v"),       # shorter v
+        (q, v, torch.zeros(2, 16, 16), v, "o"),      # wider o
+        (q, v, v, torch.zeros(1, 16, 8), "dout"),    # fewer heads in dout
+    ]
+    for k, vv, o, do, what in bad:
+        with pytest.raises(ValueError, match=what):
+            m.mla_attention_backward(q, k, vv, o, do, 0.5)
+    x = torch.zeros(4, 32)
+    with pytest.raises(ValueError, match="dy"):
+        m.mla_rmsnorm_backward(x, torch.zeros(4, 31), torch.zeros(32), 1e-6)
+    with pytest.raises(ValueError, match="g"):
+        m.mla_rmsnorm_backward(x, torch.zeros(4, 32), torch.zeros(16), 1e-6)

@@ -1,0 +1,105 @@
+"""GPU parity with and without the optional RMSNorm on c_kv (kv_norm gains).
+
+The pages put no norm on the latent, so kv_norm = NULL is the default and
+every other test runs that way; checkpoints that normalise c_kv pass gains,
+and then the cached rows and everything read from them (w_up_k, w_up_v, the
+absorbed decode) see the normalised latent.  Both ways are checked here
+against the oracle on the tiny (fp32) and small (bf16) configs: prefill
+outputs and latent rows, the absorbed decode and its appended cache rows,
+a multi-token decode step and a chunked prefill."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from tests.gpu_util import gpu, mla_cfg, require_gpu, si, to_dev, to_np, weights_to_dev
+from tests.helpers import assert_close_rows, oracle_cfg, shrink
+
+pytestmark = gpu
+
+
+def _m():
+    require_gpu()
+    import head_latent_attention_08_amd as m
+    return m
+
+
+def _gains(w, dtype, seed, on):
+    w = dict(w)
+    if on:
+        r = w["w_down_kv"].shape[0]
+        g = 1.0 + 0.2 * np.random.default_rng(seed).standard_normal(r).astype(np.float32)
+        w["kv_norm"] = si._store(g, dtype)
+    return w
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+@pytest.mark.parametrize("on", [False, True])
+def test_prefill_kv_norm(name, on):
+    m = _m()
+    c = si.CONFIGS[name]
+    dt = c["dtype"]
+    x, w = si.make_inputs(c, seq=100 if name == "small" else None, gains="random")
+    w = _gains(w, dt, 51, on)
+    cfg = mla_cfg(c, rope="interleaved")
+    y, lat, _ = m.mla_prefill_forward(cfg, weights_to_dev(w, dt), to_dev(x, dt), want_latent=True)
+    torch.cuda.synchronize()
+    ref, inter = orc.mla_prefill(oracle_cfg(c, rope="interleaved"), w, x, want_intermediates=True)
+    assert_close_rows(to_np(y), ref, dt, "y")
+    assert_close_rows(to_np(lat), np.concatenate([inter["c_kv"], inter["k_pe"]], -1), dt, "latent")
+    if on:  # the norm really changed the latent (gains differ from 1)
+        plain = orc.mla_prefill(oracle_cfg(c, rope="interleaved"),
+                                {k: v for k, v in w.items() if k != "kv_norm"}, x)
+        assert np.abs(plain - ref).max() > 10 * np.abs(to_np(y) - ref).max()
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+@pytest.mark.parametrize("on", [False, True])
+def test_decode_kv_norm(name, on):
+    m = _m()
+    c = si.CONFIGS[name]
+    dt = c["dtype"]
+    B, cap = 4, 96
+    x, w, lens, cache = si.make_decode_inputs(c, batch=B, capacity=cap, len_lo=0, len_hi=cap - 2,
+                                              gains="random", seed=5200)
+    w = _gains(w, dt, 52, on)
+    cfg = mla_cfg(c, rope="interleaved")
+    cache_d = to_dev(cache, dt)
+    y, _ = m.mla_decode_absorbed(cfg, weights_to_dev(w, dt), to_dev(x, dt), cache_d,
+                                 torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    ref, new_rows = orc.mla_decode_absorbed(oracle_cfg(c, rope="interleaved"), w, x, cache, lens)
+    assert_close_rows(to_np(y), ref, dt, "y")
+    got = to_np(cache_d)
+    assert_close_rows(np.stack([got[b, lens[b]] for b in range(B)]), new_rows, dt, "new rows")
+
+
+@pytest.mark.parametrize("on", [False, True])
+def test_multi_token_decode_and_chunk_kv_norm(on):
+    # T new tokens per sequence, absorbed (multi-token decode) and expanded
+    # (chunked prefill), against the multi-token oracle
+    m = _m()
+    c = si.CONFIGS["small"]
+    B, T, cap = 2, 6, 80
+    x, w, lens, cache = si.make_decode_inputs(c, batch=B, capacity=cap, len_lo=10, len_hi=60,
+                                              gains="random", seed=5300)
+    xs = si._store(np.random.default_rng(5301).standard_normal((B, T, c["hidden_size"])).astype(
+        np.float32), "bf16")
+    w = _gains(w, "bf16", 53, on)
+    cfg = mla_cfg(c, rope="interleaved")
+    ref, new_rows = orc.mla_decode_absorbed_multi(oracle_cfg(c, rope="interleaved"), w, xs, cache,
+                                                  lens)
+    wd = weights_to_dev(w, "bf16")
+    lens_d = torch.from_numpy(lens).cuda()
+    cache_a = to_dev(cache, "bf16")
+    ya, _ = m.mla_decode_absorbed_multi(cfg, wd, to_dev(xs, "bf16"), cache_a, lens_d)
+    cache_e = to_dev(cache, "bf16")
+    ye, _ = m.mla_prefill_chunk(cfg, wd, to_dev(xs, "bf16"), cache_e, lens_d,
+                                int(lens.sum()) + B * T)
+    torch.cuda.synchronize()
+    for y, cd, what in ((ya, cache_a, "absorbed"), (ye, cache_e, "chunk")):
+        assert_close_rows(to_np(y).reshape(B * T, -1), ref.reshape(B * T, -1), "bf16", what)
+        got = to_np(cd)
+        for b in range(B):
+            assert_close_rows(got[b, lens[b]:lens[b] + T], new_rows[b], "bf16", what + " rows")

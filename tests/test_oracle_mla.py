@@ -353,3 +353,64 @@ def test_latent_cache_is_small():
     c = si.V3
     assert c["kv_lora_rank"] + c["qk_rope_head_dim"] == 576
     assert 576 / (2 * c["num_attention_heads"] * c["qk_nope_head_dim"]) < 0.02
+
+
+# ------------------------------------------------------- optional c_kv norm --
+
+def _with_kv_norm(w, rng, gain_one=False):
+    w = dict(w)
+    r = w["w_down_kv"].shape[0]
+    w["kv_norm"] = np.ones(r) if gain_one else 1.0 + 0.1 * rng.standard_normal(r)
+    return w
+
+
+def test_kv_norm_latent_rows_have_unit_rms_and_match_torch():
+    # with gains 1 and eps 0 every cached c_kv row has RMS 1; with random
+    # gains it is torch's rms_norm of x W_dkv^T
+    cfg, x, w = _tiny_inputs()
+    rng = np.random.default_rng(41)
+    cfg0 = orc.Cfg(**{**cfg.__dict__, "rms_norm_eps": 0.0})
+    _, inter = orc.mla_prefill(cfg0, _with_kv_norm(w, rng, gain_one=True), x, want_intermediates=True)
+    np.testing.assert_allclose(np.sqrt(np.mean(inter["c_kv"] ** 2, axis=-1)), 1.0, rtol=1e-12)
+    wn = _with_kv_norm(w, rng)
+    _, inter = orc.mla_prefill(cfg, wn, x, want_intermediates=True)
+    ref = F.rms_norm(torch.from_numpy(x @ w["w_down_kv"].T), (w["w_down_kv"].shape[0],),
+                     torch.from_numpy(wn["kv_norm"]), eps=cfg.rms_norm_eps).numpy()
+    np.testing.assert_allclose(inter["c_kv"], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_kv_norm_makes_output_invariant_to_latent_scale():
+    # the norm sits between w_down_kv and everything that reads c_kv (cache,
+    # w_up_k, w_up_v): scaling w_down_kv leaves y unchanged at eps 0, and
+    # without the norm it does not
+    cfg, x, w = _tiny_inputs()
+    cfg0 = orc.Cfg(**{**cfg.__dict__, "rms_norm_eps": 0.0})
+    wn = _with_kv_norm(w, np.random.default_rng(42))
+    ws = dict(wn, w_down_kv=wn["w_down_kv"] * 7.5)
+    np.testing.assert_allclose(orc.mla_prefill(cfg0, ws, x), orc.mla_prefill(cfg0, wn, x),
+                               rtol=1e-10, atol=1e-12)
+    w_plain = {k: v for k, v in wn.items() if k != "kv_norm"}
+    w_plain_s = dict(w_plain, w_down_kv=w_plain["w_down_kv"] * 7.5)
+    assert np.abs(orc.mla_prefill(cfg0, w_plain_s, x) - orc.mla_prefill(cfg0, w_plain, x)).max() > 1e-3
+    # an explicit None is the pages' reading (no norm)
+    np.testing.assert_array_equal(orc.mla_prefill(cfg, dict(w, kv_norm=None), x),
+                                  orc.mla_prefill(cfg, w, x))
+
+
+@pytest.mark.parametrize("conv", ["half_split", "interleaved"])
+def test_kv_norm_decode_after_prefill_and_absorbed_equals_expanded(conv):
+    # with the norm, the cached rows a prefill leaves serve the next decode
+    # step, whose output is the prefill's next row; absorbed == expanded
+    cfg, x, w = _tiny_inputs(conv, S=12)
+    wn = _with_kv_norm(w, np.random.default_rng(43))
+    full = orc.mla_prefill(cfg, wn, x)
+    _, inter = orc.mla_prefill(cfg, wn, x[:, :11], want_intermediates=True)
+    cache = np.concatenate([inter["c_kv"], inter["k_pe"]], axis=-1)
+    cache = np.concatenate([cache, np.zeros((1, 4, cache.shape[-1]))], axis=1)
+    lens = np.array([11])
+    ya, rows = orc.mla_decode_absorbed(cfg, wn, x[:, 11], cache, lens)
+    ye, _ = orc.mla_decode_expanded(cfg, wn, x[:, 11], cache, lens)
+    np.testing.assert_allclose(ya, full[:, 11], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ya, ye, rtol=1e-12, atol=1e-13)
+    _, inter12 = orc.mla_prefill(cfg, wn, x, want_intermediates=True)
+    np.testing.assert_allclose(rows[0, :cfg.kv_lora_rank], inter12["c_kv"][0, 11], rtol=1e-12)
