@@ -19,6 +19,8 @@ from .mla import (  # noqa: F401
     mla_decode_layout_of,
     mla_decode_workspace_size,
     mla_attention_backward,
+    mla_attention_backward_noalloc,
+    mla_attention_backward_noalloc_max_rows,
     mla_fp8_gemm,
     mla_rmsnorm_backward,
     mla_fp8_quantize_blocks,

@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/mla.h"
@@ -1049,6 +1050,35 @@ mla_status run_attention_backward(int32_t dtype, int64_t batch_heads, int64_t se
   return MLA_OK;
 }
 
+// ---- allocation-free attention backward (scratch array) ----
+// Scratch of the allocation-free attention backward: the rows' log-sum-exp
+// and rowsum(dO * O), 8 bytes per row, for at most 2^21 rows (16 MB).  Each
+// GPU the library runs on holds its own copy until the process ends.
+// Host code never uses this name as an address (on the host it stands for
+// the symbol, not for device memory): the device address comes from
+// hipGetSymbolAddress, once per device, and is passed to the kernels.
+constexpr int64_t kNoallocMaxRows = (int64_t)1 << 21;
+static __device__ __align__(256) float scratch[2 * kNoallocMaxRows];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on first use with
+// the device current), or an error status.
+mla_status scratch_of_device(int dev, float **out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "device %d is beyond the %d devices supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    MLA_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "scratch symbol address");
+    g_scratch_ptr[dev] = static_cast<float *>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+// ---- end of the allocation-free scratch ----
 }  // namespace
 
 extern "C" {
@@ -1066,6 +1096,38 @@ mla_status mla_attention_backward(int32_t dtype, int64_t batch_heads, int64_t se
   return run_attention_backward(dtype, batch_heads, seq, d_qk, d_v, scale, q, k, v, o, dout, dq, dk, dv,
                                 reinterpret_cast<float *>(workspace), hip_stream);
 }
+
+// ---- allocation-free attention backward (entry points) ----
+int64_t mla_attention_backward_noalloc_max_rows(void) { return kNoallocMaxRows; }
+
+mla_status mla_attention_backward_noalloc(int32_t dtype, int64_t batch_heads, int64_t seq, int32_t d_qk,
+                                          int32_t d_v, float scale, const void *q, const void *k,
+                                          const void *v, const void *o, const void *dout, void *dq, void *dk,
+                                          void *dv, void *hip_stream) {
+  size_t need = 0;
+  const void *ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  mla_status s = check_attention_backward(dtype, batch_heads, seq, d_qk, d_v, scale, ptrs, 8, &need);
+  if (s != MLA_OK || batch_heads * seq == 0) return s;
+  if (batch_heads * seq > kNoallocMaxRows)
+    return fail(MLA_ERR_INVALID_ARGUMENT,
+                "batch_heads x seq = %lld rows exceeds the %lld rows of the built-in scratch",
+                (long long)(batch_heads * seq), (long long)kNoallocMaxRows);
+  int dev = -1;
+  MLA_HIP(hipGetDevice(&dev), "current device");
+  if (hip_stream) {
+    hipDevice_t sdev = -1;
+    MLA_HIP(hipStreamGetDevice((hipStream_t)hip_stream, &sdev), "stream device");
+    if (sdev != dev)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "the stream belongs to device %d, not the current device %d",
+                  (int)sdev, dev);
+  }
+  float *scr = nullptr;
+  if ((s = scratch_of_device(dev, &scr)) != MLA_OK) return s;
+  return run_attention_backward(dtype, batch_heads, seq, d_qk, d_v, scale, q, k, v, o, dout, dq, dk, dv, scr,
+                                hip_stream);
+}
+
+// ---- end of the allocation-free entry points ----
 
 mla_status mla_rmsnorm_backward(int32_t dtype, const void *x, const void *dy, const void *g, int64_t rows,
                                 int32_t n, float eps, void *dx, float *dg, void *workspace, size_t workspace_bytes,

@@ -123,6 +123,11 @@ def load_library(path: str = LIB_PATH):
                                            ctypes.c_float, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     for fn in ("mla_attention_backward_workspace_size", "mla_attention_backward"):
         getattr(lib, fn).restype = st
+    lib.mla_attention_backward_noalloc.argtypes = [ctypes.c_int32, i64, i64, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_float, P, P, P, P, P, P, P, P, P]
+    lib.mla_attention_backward_noalloc.restype = st
+    lib.mla_attention_backward_noalloc_max_rows.argtypes = []
+    lib.mla_attention_backward_noalloc_max_rows.restype = i64
     lib.mla_rmsnorm_backward.argtypes = [ctypes.c_int32, P, P, P, i64, ctypes.c_int32, ctypes.c_float, P, P,
                                          P, ctypes.c_size_t, P]
     lib.mla_rmsnorm_backward.restype = st
@@ -457,6 +462,32 @@ def _check_attention_backward_shapes(q, k, v, o, dout):
                          f"{tuple(v.shape)}")
     if any(not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype for t in ts):
         raise ValueError("q, k, v, o and dout must be contiguous device tensors of one dtype")
+
+
+def mla_attention_backward_noalloc_max_rows() -> int:
+    """Rows (batch_heads x seq) the allocation-free backward's built-in
+    scratch holds."""
+    return int(load_library().mla_attention_backward_noalloc_max_rows())
+
+
+def mla_attention_backward_noalloc(q, k, v, o, dout, scale: float, dq=None, dk=None, dv=None,
+                                   stream=None):
+    """mla_attention_backward without a workspace (the library's built-in
+    scratch); the outputs may be passed in, so the call need not allocate."""
+    _check_attention_backward_shapes(q, k, v, o, dout)
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[q.dtype]
+    S, dqk, dv_ = q.shape[-2], q.shape[-1], v.shape[-1]
+    bh = q.numel() // max(S * dqk, 1)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous device tensors shaped like q, k, v")
+    _check(load_library().mla_attention_backward_noalloc(
+        dt, bh, S, dqk, dv_, scale, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(dq), _ptr(dk),
+        _ptr(dv), _stream(stream)))
+    return dq, dk, dv
 
 
 def mla_rmsnorm_backward(x, dy, g, eps: float, stream=None):

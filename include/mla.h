@@ -374,6 +374,27 @@ MLA_API mla_status mla_attention_backward(int32_t dtype, int64_t batch_heads, in
                                   const void *dout, void *dq, void *dk, void *dv,
                                   void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Allocation-free variant of mla_attention_backward, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight training or
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, results
+ * and errors as mla_attention_backward, without the workspace: the rows'
+ * log-sum-exp and rowsum(dO * O) go to a scratch array built into the
+ * library (8 bytes per row, 16 MB; each GPU the library runs on holds its own
+ * copy until the process ends).  The call allocates nothing.  It runs on the
+ * current device; a non-NULL hip_stream must belong to it.  Every call on a
+ * GPU shares that GPU's scratch, which keeps the last call's contents (the
+ * call writes every row it reads before reading it): calls that overlap on
+ * one GPU, on any streams, race and give wrong results.
+ * Status: as mla_attention_backward; INVALID_ARGUMENT also when
+ * batch_heads * seq exceeds mla_attention_backward_noalloc_max_rows() or the
+ * stream belongs to another device; HIP if the scratch cannot be located. */
+MLA_API int64_t mla_attention_backward_noalloc_max_rows(void);
+MLA_API mla_status mla_attention_backward_noalloc(int32_t dtype, int64_t batch_heads, int64_t seq,
+                                          int32_t d_qk, int32_t d_v, float scale, const void *q,
+                                          const void *k, const void *v, const void *o,
+                                          const void *dout, void *dq, void *dk, void *dv,
+                                          void *hip_stream);
+
 /* RMSNorm backward (the norm on c_q of the MLA module of "The Evolving
  * Transformer -- DeepSeek V2 & V3", section 01; y = x r g with
  * r = (mean(x^2) + eps)^-1/2 per row): dx = r (g dy) - x r^3 mean(x g dy) and
