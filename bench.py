@@ -132,10 +132,14 @@ def cpu_baseline(c_pre, x, w, c_dec, xd, wd, lens, cache, seconds_hint=True):
 
     import oracle as orc
     from tests.helpers import oracle_cfg
+    blas = "unknown"
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        bl = [i for i in info if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in bl] or [1])
+        if bl:
+            blas = f"{bl[0].get('internal_api', '?')} {bl[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
     s_sample = x.shape[1]  # the whole S=4096 prefill: about 10 s of float64 work
@@ -159,6 +163,7 @@ def cpu_baseline(c_pre, x, w, c_dec, xd, wd, lens, cache, seconds_hint=True):
             "unit": "GB/s",
             "sample": f"absorbed decode of all {n_seq} sequences ({t_dec:.2f} s)",
         },
+        "blas": blas,
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
     }
@@ -226,6 +231,61 @@ def fp8_projections(m, S, log, reps=20):
     del ops, o
     torch.cuda.empty_cache()
     return res
+
+
+def long_context_line(m, log, reps=3):
+    """Long-context V3 prefill with YaRN RoPE: B=1, S=32768, factor 40 over
+    an original 4096 context, beta 32/1, mscale 1/1 (the configuration whose
+    260 sampled rows the GPU tests check against the oracle, same seeded
+    inputs).  Per-stage times from the library's stage events; the roofline
+    entry is for its dominant kernel (attention: 78% of the FLOPs)."""
+    import torch
+    import synth_inputs as si
+    from tests.gpu_util import mla_cfg, to_dev, weights_to_dev
+    c = si.CONFIGS["v3_yarn"]
+    B, S = c["batch"], c["seq"]
+    log(f"bench: generating long-context inputs (B={B}, S={S}, seed {c['seed']})")
+    x, w = si.make_inputs(c)
+    xd, wd = to_dev(x, "bf16"), weights_to_dev(w, "bf16")
+    del x, w
+    cfg = mla_cfg(c)
+    y = torch.empty((B, S, c["hidden_size"]), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m.mla_prefill_workspace_size(cfg, B, S), dtype=torch.uint8, device="cuda")
+    n_ev = len(m.PREFILL_STAGES) + 1
+    m.mla_prefill_forward(cfg, wd, xd, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        for ev in e:
+            ev.record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    for e in evs:
+        m.mla_set_stage_events([ev.cuda_event for ev in e])
+        m.mla_prefill_forward(cfg, wd, xd, y=y, workspace=ws)
+        m.mla_set_stage_events(None)
+    torch.cuda.synchronize()
+    import statistics
+    stage = {n: statistics.median(e[k].elapsed_time(e[k + 1]) for e in evs)
+             for k, n in enumerate(m.PREFILL_STAGES)}
+    whole = [e[0].elapsed_time(e[-1]) for e in evs]
+    proj, attn, per = prefill_flops(c, B, S)
+    ms = statistics.median(whole)
+    tf = (proj + attn) / (ms * 1e-3) / 1e12
+    stage_tf = {k: per[k] / (stage[k] * 1e-3) / 1e12 for k in per}
+    log(f"bench: long-context prefill S={S} YaRN: {ms:.2f} ms, {tf:.0f} TFLOP/s "
+        f"(attention {stage['attention']:.2f} ms, {stage_tf['attention']:.0f} TFLOP/s)")
+    del xd, wd, y, ws
+    torch.cuda.empty_cache()
+    return {"workload": "v3_yarn_prefill_b1_s32768", "batch": B, "seq_len": S,
+            "rope": "interleaved, YaRN factor 40, original 4096, beta 32/1, mscale 1/1",
+            "gflop": (proj + attn) / 1e9, "ms": ms, "ms_min": min(whole), "tflops": tf,
+            "frac_of_bf16_peak": tf / MI355X_BF16_TFLOPS, "stage_ms": stage, "stage_tflops": stage_tf,
+            "roofline": {"bound": "mfma", "kernel": "attention", "achieved": stage_tf["attention"],
+                         "peak": MI355X_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": stage_tf["attention"] / MI355X_BF16_TFLOPS,
+                         "flops_per_launch": per["attention"], "ms_per_launch": stage["attention"]}}
 
 
 def attention_backward_line(m, S, log, reps=2):
@@ -387,6 +447,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the causal attention backward (context line)")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the S=32768 YaRN prefill (context line)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the block-scaled FP8 projection products (context line)")
     ap.add_argument("--no-multi-token", action="store_true",
@@ -524,7 +586,7 @@ def main():
             for k, n in enumerate(names):
                 per[n].append(e[k].elapsed_time(e[k + 1]))
             whole.append(e[0].elapsed_time(e[-1]))
-        return {n: float(np.mean(v)) for n, v in per.items()}, float(np.mean(whole)), \
+        return {n: float(np.median(v)) for n, v in per.items()}, float(np.median(whole)), \
             float(np.min(whole))
 
     pst, pre_ms, pre_min = stage_ms(pev, m.PREFILL_STAGES)
@@ -634,6 +696,8 @@ def main():
                                 "tflops": c_fl / (c_ms * 1e-3) / 1e12, "gflop": c_fl / 1e9}
         log(f"bench: prefill chunk {Tc} tokens after {Lc} cached rows: {c_ms:.3f} ms, "
             f"{c_fl / (c_ms * 1e-3) / 1e12:.0f} TFLOP/s")
+    if not args.no_long_context:
+        out["long_context"] = long_context_line(m, log)
     if not args.no_fp8:
         out["fp8_projections"] = fp8_projections(m, S, log)
     if not args.no_backward:
