@@ -288,6 +288,46 @@ def long_context_line(m, log, reps=3):
                          "flops_per_launch": per["attention"], "ms_per_launch": stage["attention"]}}
 
 
+def fp8_prefill_line(m, cfg_pre, wd_pre, xd_pre, bf16_ms, log, reps=20):
+    """The V3 prefill (B=1, S=4096) with its four projection products on
+    block-scaled FP8 and attention in bf16 (mla_prefill_forward_fp8), same
+    inputs as the headline; weights quantised once outside the timed region.
+    Per-stage medians from the stage events; FLOPs counted as for the bf16
+    prefill."""
+    import statistics
+    import torch
+    B, S = xd_pre.shape[0], xd_pre.shape[1]
+    buf, w8 = m.mla_fp8_prepare_weights(cfg_pre, wd_pre)
+    y = torch.empty_like(xd_pre)
+    ws = torch.empty(m.mla_prefill_fp8_workspace_size(cfg_pre, B, S), dtype=torch.uint8, device="cuda")
+    for _ in range(5):
+        m.mla_prefill_forward_fp8(cfg_pre, wd_pre, w8, xd_pre, y=y, workspace=ws)
+    n_ev = len(m.PREFILL_STAGES) + 1
+    evs = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        for ev in e:
+            ev.record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    for e in evs:
+        m.mla_set_stage_events([ev.cuda_event for ev in e])
+        m.mla_prefill_forward_fp8(cfg_pre, wd_pre, w8, xd_pre, y=y, workspace=ws)
+        m.mla_set_stage_events(None)
+    torch.cuda.synchronize()
+    stage = {n: statistics.median(e[k].elapsed_time(e[k + 1]) for e in evs)
+             for k, n in enumerate(m.PREFILL_STAGES)}
+    ms = statistics.median(e[0].elapsed_time(e[-1]) for e in evs)
+    import synth_inputs as si
+    proj, attn, _ = prefill_flops(si.CONFIGS["v3_prefill"], B, S)
+    tf = (proj + attn) / (ms * 1e-3) / 1e12
+    log(f"bench: fp8 prefill S={S}: {ms:.3f} ms, {tf:.0f} TFLOP/s (bf16 prefill {bf16_ms:.3f} ms)")
+    del buf, y, ws
+    torch.cuda.empty_cache()
+    return {"workload": "v3_prefill_b1_s4096, projections block-scaled fp8 (e4m3), attention bf16",
+            "ms": ms, "tflops": tf, "speedup_vs_bf16": bf16_ms / ms, "stage_ms": stage}
+
+
 def attention_backward_line(m, S, log, reps=2):
     """Causal attention backward (dQ, dK, dV) at the V3 prefill attention
     shape: 128 heads, S tokens, d_qk 192, d_v 128, bf16, seeded device draws
@@ -696,6 +736,8 @@ def main():
                                 "tflops": c_fl / (c_ms * 1e-3) / 1e12, "gflop": c_fl / 1e9}
         log(f"bench: prefill chunk {Tc} tokens after {Lc} cached rows: {c_ms:.3f} ms, "
             f"{c_fl / (c_ms * 1e-3) / 1e12:.0f} TFLOP/s")
+    if not args.no_fp8:
+        out["fp8_prefill"] = fp8_prefill_line(m, cfg_pre, wd_pre, xd_pre, pre_ms, log)
     if not args.no_long_context:
         out["long_context"] = long_context_line(m, log)
     if not args.no_fp8:

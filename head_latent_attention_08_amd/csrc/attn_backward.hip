@@ -296,14 +296,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 
 // RMSNorm backward of y = x r g, r = (mean(x^2) + eps)^-1/2 per row:
 // dx = r (g dy) - x r^3 mean(x g dy), one workgroup per row (rinv kept per
-// row); dg[c] = sum over rows of dy x r, one thread per column over all rows
-// in order (deterministic).
+// row).  dg[c] = sum over rows of dy x r in two fixed-order levels: chunks of
+// RB_CHUNK rows give fp32 partials (one thread per column of a chunk), then
+// the partials of each column are added chunk by chunk (deterministic, and
+// the whole GPU takes part instead of one workgroup per 256 columns).
+constexpr int RB_CHUNK = 64;
+
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_bwd_rows_kernel(const T *x, const T *dy, const T *g, int n,
-                                                               float eps, T *dx, float *rinv) {
+__global__ __launch_bounds__(256) void rmsnorm_bwd_rows_kernel(const T *x, int64_t ldx, const T *dy, int64_t ldy,
+                                                               const T *g, int n, float eps, T *dx, int64_t lddx,
+                                                               float *rinv) {
   __shared__ float red[2][4];
   const int64_t row = blockIdx.x;
-  const T *xr = x + row * n, *dr = dy + row * n;
+  const T *xr = x + row * ldx, *dr = dy + row * ldy;
   float ss = 0.f, xg = 0.f;
   for (int c = threadIdx.x; c < n; c += 256) {
     const float xv = (float)xr[c];
@@ -322,28 +327,44 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_rows_kernel(const T *x, const
   const float r = 1.f / sqrtf(ss / n + eps);
   const float k = r * r * r * xg / n;
   for (int c = threadIdx.x; c < n; c += 256)
-    dx[row * n + c] = (T)(r * (float)g[c] * (float)dr[c] - (float)xr[c] * k);
+    dx[row * lddx + c] = (T)(r * (float)g[c] * (float)dr[c] - (float)xr[c] * k);
   if (threadIdx.x == 0) rinv[row] = r;
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_bwd_dg_kernel(const T *x, const T *dy, int64_t rows, int n,
-                                                             const float *rinv, float *dg) {
+__global__ __launch_bounds__(256) void rmsnorm_bwd_dg_part_kernel(const T *x, int64_t ldx, const T *dy,
+                                                                  int64_t ldy, int64_t rows, int n,
+                                                                  const float *rinv, float *part) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * RB_CHUNK;
+  if (c >= n) return;
+  const int64_t r1 = min(r0 + RB_CHUNK, rows);
+  float acc = 0.f;
+  for (int64_t r = r0; r < r1; ++r) acc = fmaf((float)dy[r * ldy + c] * (float)x[r * ldx + c], rinv[r], acc);
+  part[(int64_t)blockIdx.y * n + c] = acc;
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_bwd_dg_sum_kernel(const float *part, int chunks, int n, float *dg) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= n) return;
   float acc = 0.f;
-  for (int64_t r = 0; r < rows; ++r) acc = fmaf((float)dy[r * n + c] * (float)x[r * n + c], rinv[r], acc);
+  for (int i = 0; i < chunks; ++i) acc += part[(int64_t)i * n + c];
   dg[c] = acc;
 }
 
 template <typename T>
-hipError_t launch_rms_t(const void *x, const void *dy, const void *g, int64_t rows, int n, float eps, void *dx,
-                        float *dg, float *rinv, hipStream_t st) {
+hipError_t launch_rms_t(const void *x, int64_t ldx, const void *dy, int64_t ldy, const void *g, int64_t rows, int n,
+                        float eps, void *dx, int64_t lddx, float *dg, float *scratch, hipStream_t st) {
+  float *rinv = scratch, *part = scratch + rows;
+  const int chunks = (int)((rows + RB_CHUNK - 1) / RB_CHUNK);
   hipLaunchKernelGGL(rmsnorm_bwd_rows_kernel<T>, dim3((unsigned)rows), dim3(256), 0, st,
-                     reinterpret_cast<const T *>(x), reinterpret_cast<const T *>(dy),
-                     reinterpret_cast<const T *>(g), n, eps, reinterpret_cast<T *>(dx), rinv);
-  hipLaunchKernelGGL(rmsnorm_bwd_dg_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const T *>(x), reinterpret_cast<const T *>(dy), rows, n, rinv, dg);
+                     reinterpret_cast<const T *>(x), ldx, reinterpret_cast<const T *>(dy), ldy,
+                     reinterpret_cast<const T *>(g), n, eps, reinterpret_cast<T *>(dx), lddx, rinv);
+  hipLaunchKernelGGL(rmsnorm_bwd_dg_part_kernel<T>, dim3((unsigned)((n + 255) / 256), (unsigned)chunks), dim3(256), 0,
+                     st, reinterpret_cast<const T *>(x), ldx, reinterpret_cast<const T *>(dy), ldy, rows, n, rinv,
+                     part);
+  hipLaunchKernelGGL(rmsnorm_bwd_dg_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, chunks,
+                     n, dg);
   return hipGetLastError();
 }
 
@@ -359,11 +380,16 @@ template <typename T> hipError_t launch_t(const AttnBwdArgs &a, hipStream_t st) 
 
 }  // namespace
 
-hipError_t launch_rmsnorm_backward(int dtype, const void *x, const void *dy, const void *g, int64_t rows, int n,
-                                  float eps, void *dx, float *dg, float *rinv, hipStream_t st) {
+size_t rmsnorm_backward_scratch_floats(int64_t rows, int n) {
+  return (size_t)rows + (size_t)((rows + RB_CHUNK - 1) / RB_CHUNK) * (size_t)n;
+}
+
+hipError_t launch_rmsnorm_backward(int dtype, const void *x, int64_t ldx, const void *dy, int64_t ldy, const void *g,
+                                   int64_t rows, int n, float eps, void *dx, int64_t lddx, float *dg, float *scratch,
+                                   hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  return dtype == BF16 ? launch_rms_t<bf16>(x, dy, g, rows, n, eps, dx, dg, rinv, st)
-                       : launch_rms_t<float>(x, dy, g, rows, n, eps, dx, dg, rinv, st);
+  return dtype == BF16 ? launch_rms_t<bf16>(x, ldx, dy, ldy, g, rows, n, eps, dx, lddx, dg, scratch, st)
+                       : launch_rms_t<float>(x, ldx, dy, ldy, g, rows, n, eps, dx, lddx, dg, scratch, st);
 }
 
 hipError_t launch_attention_backward(int dtype, const AttnBwdArgs &a, hipStream_t st) {

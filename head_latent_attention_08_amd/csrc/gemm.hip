@@ -38,7 +38,7 @@ __device__ inline void load_chunk(const T *p, bool ok, uint4 &v) {
   else v = make_uint4(0, 0, 0, 0);
 }
 
-template <typename T, bool BKN>
+template <typename T, bool BKN, bool AKM>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   using C = GemmCfg<T>;
   using MF = Mfma32<T>;
@@ -55,12 +55,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   // global -> register staging: each thread owns two 16-byte chunks of A and B
   uint4 ra[2], rb[2];
   auto fetch = [&](int k0) {
+    if constexpr (!AKM) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int c = tid + 256 * i;
-      int row = c >> 2, ch = c & 3;
-      int m = m0 + row, k = k0 + ch * VEC;
-      load_chunk<T>(A + (int64_t)m * p.lda + k, m < p.M && k < p.K, ra[i]);
+      for (int i = 0; i < 2; ++i) {
+        int c = tid + 256 * i;
+        int row = c >> 2, ch = c & 3;
+        int m = m0 + row, k = k0 + ch * VEC;
+        load_chunk<T>(A + (int64_t)m * p.lda + k, m < p.M && k < p.K, ra[i]);
+      }
+    } else {
+      // A stored [K][M] (M contiguous): chunks of VEC consecutive m of one k
+      constexpr int CPR = BM / VEC;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int c = tid + 256 * i;
+        int kr = c / CPR, mc = c % CPR;
+        int k = k0 + kr, m = m0 + mc * VEC;
+        load_chunk<T>(A + (int64_t)k * p.lda + m, k < p.K && m < p.M, ra[i]);
+      }
     }
     if constexpr (!BKN) {
 #pragma unroll
@@ -86,11 +98,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     }
   };
   auto stash = [&](int buf) {
+    if constexpr (!AKM) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int c = tid + 256 * i;
-      int row = c >> 2, ch = c & 3;
-      *reinterpret_cast<uint4 *>(&As[buf][row * PITCH + ch * VEC]) = ra[i];
+      for (int i = 0; i < 2; ++i) {
+        int c = tid + 256 * i;
+        int row = c >> 2, ch = c & 3;
+        *reinterpret_cast<uint4 *>(&As[buf][row * PITCH + ch * VEC]) = ra[i];
+      }
+    } else {
+      constexpr int CPR = BM / VEC;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int c = tid + 256 * i;
+        int kr = c / CPR, mc = c % CPR;
+        const T *v = reinterpret_cast<const T *>(&ra[i]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) As[buf][(mc * VEC + e) * PITCH + kr] = v[e];
+      }
     }
     if constexpr (!BKN) {
 #pragma unroll
@@ -748,7 +772,7 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   p.H = d.H;
   p.nseg = d.nseg;
   for (int i = 0; i < 3; ++i) p.seg[i] = d.seg[i];
-  bool big = d.dtype == BF16 && !d.b_kn && d.batch == 1 && d.K % GB_K == 0 && d.M >= 512 &&
+  bool big = d.dtype == BF16 && !d.b_kn && !d.a_km && d.batch == 1 && d.K % GB_K == 0 && d.M >= 512 &&
              d.N % 8 == 0 && (int64_t)d.M * d.lda < (1LL << 31);
   for (int i = 0; i < d.nseg && big; ++i)
     big = d.seg[i].n_begin % 16 == 0 && (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
@@ -762,7 +786,7 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
     if (10 * t256 <= 6 * cus && t192 <= cus && tr_aligned(d, 192)) return launch_big<3, 3>(p, d, 0, d.N, st);
     return launch_big<4, 4>(p, d, 0, d.N, st);
   }
-  bool skinny = d.dtype == BF16 && !d.b_kn && d.M <= SK_MMAX && d.K % SK_K == 0 && d.N % 8 == 0 &&
+  bool skinny = d.dtype == BF16 && !d.b_kn && !d.a_km && d.M <= SK_MMAX && d.K % SK_K == 0 && d.N % 8 == 0 &&
                 d.batch * ((d.M + SK_M - 1) / SK_M) <= 65535;
   for (int i = 0; i < d.nseg && skinny; ++i) skinny = d.seg[i].n_begin % SK_N == 0;
   if (skinny) {
@@ -786,13 +810,20 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   }
   dim3 grid((d.N + BN - 1) / BN, (d.M + BM - 1) / BM, d.batch);
   dim3 block(256);
-  if (d.dtype == BF16) {
-    if (d.b_kn) hipLaunchKernelGGL((gemm_kernel<bf16, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gemm_kernel<bf16, false>), grid, block, 0, st, p);
-  } else {
-    if (d.b_kn) hipLaunchKernelGGL((gemm_kernel<float, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((gemm_kernel<float, false>), grid, block, 0, st, p);
+#define MLA_GEMM_GENERIC(T_)                                                                  \
+  if (d.a_km) {                                                                               \
+    if (d.b_kn) hipLaunchKernelGGL((gemm_kernel<T_, true, true>), grid, block, 0, st, p);     \
+    else hipLaunchKernelGGL((gemm_kernel<T_, false, true>), grid, block, 0, st, p);           \
+  } else {                                                                                    \
+    if (d.b_kn) hipLaunchKernelGGL((gemm_kernel<T_, true, false>), grid, block, 0, st, p);    \
+    else hipLaunchKernelGGL((gemm_kernel<T_, false, false>), grid, block, 0, st, p);          \
   }
+  if (d.dtype == BF16) {
+    MLA_GEMM_GENERIC(bf16)
+  } else {
+    MLA_GEMM_GENERIC(float)
+  }
+#undef MLA_GEMM_GENERIC
   return hipGetLastError();
 }
 

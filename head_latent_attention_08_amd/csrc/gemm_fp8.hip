@@ -68,7 +68,16 @@ struct Fp8GemmParams {
   int64_t lda, ld_sa, ldb, ld_sb, ldc;
   void *c;
   int M, N, K, c_f32;
+  // column-range output mapping (bf16 C; c and ldc unused): nseg > 0
+  int S = 1, H = 1, nseg = 0;
+  GemmSeg seg[3];
 };
+
+__device__ inline int f8_seg_of(const Fp8GemmParams &p, int n) {
+  return (p.nseg > 1 && n >= p.seg[1].n_begin) ? ((p.nseg > 2 && n >= p.seg[2].n_begin) ? 2 : 1) : 0;
+}
+// fields of column range s, read with constant indices only
+#define F8_SEG(p, s, f) ((s) == 0 ? (p).seg[0].f : ((s) == 1 ? (p).seg[1].f : (p).seg[2].f))
 
 __global__ __launch_bounds__(F8_THREADS) void fp8_gemm_kernel(Fp8GemmParams p, int tiles_m, int tiles_n,
                                                               int remap, int group_m) {
@@ -278,6 +287,50 @@ __global__ __launch_bounds__(F8_THREADS) void fp8_gemm_kernel(Fp8GemmParams p, i
   // 16-byte row runs
   __syncthreads();
   bf16 *Cs = reinterpret_cast<bf16 *>(lds);
+  if (p.nseg > 0 && F8_SEG(p, f8_seg_of(p, min(n0, p.N - 1)), tr)) {
+    // channel-major column range (aligned to the tile on the host): the tile
+    // goes to LDS transposed, a lane writing its four consecutive rows of a
+    // column as one 8-byte store; then lanes take 8-token runs of a column
+    constexpr int TP = F8_BM + 8;
+    static_assert(F8_BN * TP * 2 <= F8_LDS, "transposed tile must fit the LDS area");
+    const int st0 = f8_seg_of(p, min(n0, p.N - 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16 v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)acc[i][jj][4 * q + e];
+          *reinterpret_cast<uint2 *>(&Cs[(wn * 128 + jj * 32 + l32) * TP + wm * 128 + i * 32 +
+                                         acc_row(4 * q, lane)]) = *reinterpret_cast<const uint2 *>(v4);
+        }
+    __syncthreads();
+    bf16 *t_C = reinterpret_cast<bf16 *>(F8_SEG(p, st0, C));
+    const int t_dh = F8_SEG(p, st0, dh), t_nb = F8_SEG(p, st0, n_begin);
+    constexpr int RG = F8_BM / 8;  // 8-token runs per column
+    for (int it = 0; it < (F8_BM * F8_BN / 8) / F8_THREADS; ++it) {
+      const int c = tid + F8_THREADS * it;
+      const int col = c / RG, rg = c - col * RG;
+      const int m = m0 + rg * 8, n = n0 + col;
+      if (m >= p.M || n >= p.N) continue;
+      const int nn = n - t_nb;
+      const int h = nn / t_dh, d = nn - h * t_dh;
+      const int b = m / p.S, sq = m - b * p.S;
+      const bf16 *src = &Cs[col * TP + rg * 8];
+      if (sq + 8 <= p.S && m + 8 <= p.M) {
+        *reinterpret_cast<uint4 *>(t_C + ((int64_t)(b * p.H + h) * t_dh + d) * p.S + sq) =
+            *reinterpret_cast<const uint4 *>(src);
+      } else {
+        for (int e = 0; e < 8 && m + e < p.M; ++e) {
+          const int me = m + e, be = me / p.S, se = me - be * p.S;
+          t_C[((int64_t)(be * p.H + h) * t_dh + d) * p.S + se] = src[e];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -293,8 +346,17 @@ __global__ __launch_bounds__(F8_THREADS) void fp8_gemm_kernel(Fp8GemmParams p, i
     const int row = c / RUNS, cc = c - row * RUNS;
     const int m = m0 + row, n = n0 + cc * 8;
     if (m >= p.M || n >= p.N) continue;
-    *reinterpret_cast<uint4 *>(C + (int64_t)m * p.ldc + n) =
-        *reinterpret_cast<const uint4 *>(&Cs[row * F8_CPITCH + cc * 8]);
+    bf16 *dst = C + (int64_t)m * p.ldc + n;
+    if (p.nseg > 0) {
+      // head-major scatter: a run of 8 columns lies in one head of one range
+      const int s = f8_seg_of(p, n);
+      const int nn = n - F8_SEG(p, s, n_begin), dh = F8_SEG(p, s, dh);
+      const int h = nn / dh, d = nn - h * dh;
+      const int b = m / p.S, sq = m - b * p.S;
+      dst = reinterpret_cast<bf16 *>(F8_SEG(p, s, C)) +
+            ((int64_t)(b * p.H + h) * p.S + sq) * F8_SEG(p, s, ld) + F8_SEG(p, s, off) + d;
+    }
+    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * F8_CPITCH + cc * 8]);
   }
 }
 
@@ -445,6 +507,21 @@ hipError_t launch_fp8_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int
   const int tm = (M + F8_BM - 1) / F8_BM, tn = (N + F8_BN - 1) / F8_BN;
   const int T = tm * tn;
   const int group_m = K >= 8192 ? 8 : (K <= 2048 ? 2 : 4);
+  hipLaunchKernelGGL(fp8_gemm_kernel, dim3(T), dim3(F8_THREADS), 0, st, p, tm, tn, (T % 8 == 0) ? 1 : 0,
+                     group_m);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm_seg(const Fp8GemmDesc &d, hipStream_t st) {
+  if (d.M == 0) return hipSuccess;
+  Fp8GemmParams p{d.a, d.sa, d.b, d.sb, d.lda, d.ld_sa, d.ldb, d.ld_sb, 0, nullptr, d.M, d.N, d.K, 0};
+  p.S = d.S;
+  p.H = d.H;
+  p.nseg = d.nseg;
+  for (int s = 0; s < 3; ++s) p.seg[s] = d.seg[s];
+  const int tm = (d.M + F8_BM - 1) / F8_BM, tn = (d.N + F8_BN - 1) / F8_BN;
+  const int T = tm * tn;
+  const int group_m = d.K >= 8192 ? 8 : (d.K <= 2048 ? 2 : 4);
   hipLaunchKernelGGL(fp8_gemm_kernel, dim3(T), dim3(F8_THREADS), 0, st, p, tm, tn, (T % 8 == 0) ? 1 : 0,
                      group_m);
   return hipGetLastError();

@@ -37,6 +37,7 @@ struct GemmDesc {
   int64_t lda = 0, strideA = 0;  // elements
   int64_t strideB = 0, strideC = 0;
   bool b_kn = false;  // B stored [K][N] (N contiguous) instead of [N][K]
+  bool a_km = false;  // A stored [K][M] (M contiguous, M a multiple of 8) instead of [M][K]
   int S = 1, H = 1;
   int nseg = 1;
   GemmSeg seg[3];
@@ -107,6 +108,16 @@ hipError_t launch_fp8_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int
                            int64_t ldb, const uint8_t *sb, int64_t ld_sb, void *c, int c_dtype, int64_t ldc, int M,
                            int N, int K, hipStream_t st);
 int64_t fp8_scale_pitch(int64_t rows);
+// The same product (bf16 C) with the column-range output mapping of GemmSeg:
+// B is one stacked code matrix with its scale bytes (seg[s].B and ldb
+// unused); a channel-major range must start on a multiple of 256 columns.
+struct Fp8GemmDesc {
+  const uint8_t *a = nullptr, *sa = nullptr, *b = nullptr, *sb = nullptr;
+  int64_t lda = 0, ld_sa = 0, ldb = 0, ld_sb = 0;
+  int M = 0, N = 0, K = 0, S = 1, H = 1, nseg = 1;
+  GemmSeg seg[3];
+};
+hipError_t launch_fp8_gemm_seg(const Fp8GemmDesc &d, hipStream_t st);
 
 // Causal attention backward over BH heads of S rows: q, k [BH, S, dqk], v,
 // o, dout [BH, S, dv] in, dq, dk [BH, S, dqk] and dvo [BH, S, dv] out (all of
@@ -119,10 +130,28 @@ struct AttnBwdArgs {
   float scale;
 };
 hipError_t launch_attention_backward(int dtype, const AttnBwdArgs &a, hipStream_t st);
-// RMSNorm backward over rows x [rows, n] (contiguous): dx like x, dg fp32 [n],
-// rinv fp32 [rows] scratch.
-hipError_t launch_rmsnorm_backward(int dtype, const void *x, const void *dy, const void *g, int64_t rows, int n,
-                                  float eps, void *dx, float *dg, float *rinv, hipStream_t st);
+// RMSNorm backward over rows of x [rows, n] (row pitches ldx, ldy, lddx):
+// dx like x, dg fp32 [n] summed in a fixed order; scratch holds
+// rmsnorm_backward_scratch_floats(rows, n) floats.
+size_t rmsnorm_backward_scratch_floats(int64_t rows, int n);
+hipError_t launch_rmsnorm_backward(int dtype, const void *x, int64_t ldx, const void *dy, int64_t ldy, const void *g,
+                                   int64_t rows, int n, float eps, void *dx, int64_t lddx, float *dg, float *scratch,
+                                   hipStream_t st);
+
+// MLA backward layout helpers (16-byte chunks; widths and column offsets
+// multiples of 8 elements):
+//   to_heads = false: dst[(b S + s) dp + dcol + h w + c] = src[((b H + h) S + s) sp + scol + c]
+//   to_heads = true:  dst[((b H + h) S + s) dp + dcol + c] = src[(b S + s) sp + scol + h w + c]
+hipError_t launch_permute_heads(int dtype, bool to_heads, const void *src, int64_t sp, int scol, void *dst,
+                                int64_t dp, int dcol, int w, int B, int S, int H, hipStream_t st);
+// kh [B, H, S, dn + dr] = [k_nope [B, H, S, dn] ‖ shared k_pe (rows of pitch ld_kpe)]
+hipError_t launch_build_keys(int dtype, const void *kn, const void *kpe, int64_t ld_kpe, void *kh, int dn, int dr,
+                             int B, int S, int H, hipStream_t st);
+// dst[(b S + s) ldd + c] = sum over h in order of src[((b H + h) S + s) sp + scol + c], c < w
+hipError_t launch_head_sum(int dtype, const void *src, int64_t sp, int scol, void *dst, int64_t ldd, int w, int B,
+                           int S, int H, hipStream_t st);
+// pos[t] = -(t % S)
+hipError_t launch_neg_positions(int32_t *pos, int64_t n, int S, hipStream_t st);
 
 hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src,
                             int64_t lds, int64_t rows, int width,

@@ -513,6 +513,294 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
                         hip_stream, nullptr, 0);
 }
 
+// ---------------------------------------------------------------- FP8 prefill
+// The prefill with its four projection products on block-scaled FP8 (E4M3
+// codes, power-of-two scale per 1 x 128 activation tile and 128 x 128
+// weight block), attention, norms and RoPE in bf16 / fp32 as in the bf16
+// path.  Activations are quantised right after the kernel that produces them.
+namespace {
+
+struct Fp8Dims {
+  int64_t N[4], K[4];  // down, q up, kv up, out
+};
+
+Fp8Dims fp8_dims(const mla_config &c) {
+  const int64_t H = c.num_heads;
+  Fp8Dims d;
+  d.N[0] = c.q_lora_rank + c.kv_lora_rank + c.qk_rope_head_dim;
+  d.K[0] = c.hidden_size;
+  d.N[1] = H * (c.qk_nope_head_dim + c.qk_rope_head_dim);
+  d.K[1] = c.q_lora_rank;
+  d.N[2] = H * (c.qk_nope_head_dim + c.v_head_dim);
+  d.K[2] = c.kv_lora_rank;
+  d.N[3] = c.hidden_size;
+  d.K[3] = H * c.v_head_dim;
+  return d;
+}
+
+mla_status check_fp8_config(const mla_config *cfg) {
+  mla_status s = check_config(cfg);
+  if (s != MLA_OK) return s;
+  if (cfg->dtype != MLA_DTYPE_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "the FP8 prefill takes bf16 activations and weights");
+  const Fp8Dims d = fp8_dims(*cfg);
+  for (int i = 0; i < 4; ++i)
+    if (d.K[i] % 128)
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "FP8 products need reduction lengths that are multiples of 128 (hidden_size, "
+                  "q_lora_rank, kv_lora_rank and num_heads * v_head_dim)");
+  if (((int64_t)cfg->num_heads * cfg->qk_nope_head_dim) % 256)
+    return fail(MLA_ERR_UNSUPPORTED, "num_heads * qk_nope_head_dim must be a multiple of 256 for the FP8 "
+                                     "kv up-projection (its v range starts a tile)");
+  return MLA_OK;
+}
+
+// Bytes of one stacked code matrix and its scale bytes, 256-byte aligned.
+size_t fp8_matrix_bytes(int64_t N, int64_t K) {
+  return round_up((size_t)N * K, 256) + round_up((size_t)(K / 128) * fp8_scale_pitch(N), 256);
+}
+
+mla_status check_fp8_matrix(const mla_fp8_matrix &m, int64_t N, int64_t K, const char *name) {
+  if (!m.codes || !m.scales) return fail(MLA_ERR_INVALID_ARGUMENT, "FP8 %s: codes or scales NULL", name);
+  if (((uintptr_t)m.codes & 15) || ((uintptr_t)m.scales & 3))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "FP8 %s: codes must be 16-byte and scales 4-byte aligned", name);
+  if (m.ld < K || m.ld % 16 || m.ld_scales < fp8_scale_pitch(N) || m.ld_scales % 4)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "FP8 %s: ld must be >= %lld and a multiple of 16, ld_scales >= "
+                "%lld and a multiple of 4", name, (long long)K, (long long)fp8_scale_pitch(N));
+  return MLA_OK;
+}
+
+struct Fp8PrefillPlan {
+  PrefillPlan base;
+  int64_t pitch_m;
+  size_t off_x8, off_sx, off_cq8, off_scq, off_ckv8, off_sckv, off_o8, off_so, total;
+};
+
+Fp8PrefillPlan plan_prefill_fp8(const mla_config &c, int64_t B, int64_t S) {
+  Fp8PrefillPlan p;
+  p.base = plan_prefill(c, B, S);
+  const int64_t M = B * S;
+  p.pitch_m = fp8_scale_pitch(M);
+  size_t off = p.base.total;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  const Fp8Dims d = fp8_dims(c);
+  p.off_x8 = take((size_t)M * d.K[0]);
+  p.off_sx = take((size_t)(d.K[0] / 128) * p.pitch_m);
+  p.off_cq8 = take((size_t)M * d.K[1]);
+  p.off_scq = take((size_t)(d.K[1] / 128) * p.pitch_m);
+  p.off_ckv8 = take((size_t)M * d.K[2]);
+  p.off_sckv = take((size_t)(d.K[2] / 128) * p.pitch_m);
+  p.off_o8 = take((size_t)M * d.K[3]);
+  p.off_so = take((size_t)(d.K[3] / 128) * p.pitch_m);
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+mla_status mla_fp8_weights_size(const mla_config *cfg, size_t *bytes) {
+  mla_status s = check_fp8_config(cfg);
+  if (s != MLA_OK) return s;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  const Fp8Dims d = fp8_dims(*cfg);
+  size_t n = 0;
+  for (int i = 0; i < 4; ++i) n += fp8_matrix_bytes(d.N[i], d.K[i]);
+  *bytes = n;
+  return MLA_OK;
+}
+
+mla_status mla_fp8_prepare_weights(const mla_config *cfg, const mla_weights *w, void *buffer,
+                                   size_t buffer_bytes, mla_fp8_weights *out, void *hip_stream) {
+  mla_status s = check_fp8_config(cfg);
+  if (s != MLA_OK) return s;
+  if ((s = check_weights(w)) != MLA_OK) return s;
+  if (!buffer || !out) return fail(MLA_ERR_INVALID_ARGUMENT, "buffer and out must not be NULL");
+  if ((uintptr_t)buffer & 255) return fail(MLA_ERR_INVALID_ARGUMENT, "buffer must be 256-byte aligned");
+  size_t need = 0;
+  mla_fp8_weights_size(cfg, &need);
+  if (buffer_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "buffer has %zu bytes, needs %zu", buffer_bytes, need);
+  const mla_config &c = *cfg;
+  const Fp8Dims d = fp8_dims(c);
+  hipStream_t st = (hipStream_t)hip_stream;
+  uint8_t *base = (uint8_t *)buffer;
+  mla_fp8_matrix *mats[4] = {&out->down, &out->q_up, &out->kv_up, &out->out};
+  size_t off = 0;
+  for (int i = 0; i < 4; ++i) {
+    mats[i]->codes = base + off;
+    mats[i]->ld = d.K[i];
+    mats[i]->scales = base + off + round_up((size_t)d.N[i] * d.K[i], 256);
+    mats[i]->ld_scales = fp8_scale_pitch(d.N[i]);
+    off += fp8_matrix_bytes(d.N[i], d.K[i]);
+  }
+  const int64_t H = c.num_heads;
+  // each source matrix is block-quantised on its own, into its rows of the stack
+  struct Part {
+    int mat;
+    const void *src;
+    int64_t rows, row0;
+  } parts[] = {
+      {0, w->w_down_q, c.q_lora_rank, 0},
+      {0, w->w_down_kv, c.kv_lora_rank, c.q_lora_rank},
+      {0, w->w_kr, c.qk_rope_head_dim, c.q_lora_rank + c.kv_lora_rank},
+      {1, w->w_up_q, H * c.qk_nope_head_dim, 0},
+      {1, w->w_qr, H * c.qk_rope_head_dim, H * c.qk_nope_head_dim},
+      {2, w->w_up_k, H * c.qk_nope_head_dim, 0},
+      {2, w->w_up_v, H * c.v_head_dim, H * c.qk_nope_head_dim},
+      {3, w->wo, c.hidden_size, 0},
+  };
+  for (const Part &pt : parts) {
+    mla_fp8_matrix &m = *mats[pt.mat];
+    MLA_HIP(launch_fp8_quant_blocks(BF16, pt.src, pt.rows, d.K[pt.mat], d.K[pt.mat],
+                                    const_cast<uint8_t *>(m.codes) + pt.row0 * m.ld, m.ld,
+                                    const_cast<uint8_t *>(m.scales) + pt.row0, m.ld_scales, st),
+            "fp8 weight quantisation");
+  }
+  return MLA_OK;
+}
+
+mla_status mla_prefill_fp8_workspace_size(const mla_config *cfg, int64_t batch, int64_t seq,
+                                          size_t *bytes) {
+  mla_status s = check_prefill_sizes(cfg, batch, seq);
+  if (s != MLA_OK) return s;
+  if ((s = check_fp8_config(cfg)) != MLA_OK) return s;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = plan_prefill_fp8(*cfg, batch, seq).total;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_forward_fp8(const mla_config *cfg, const mla_weights *w, const mla_fp8_weights *w8,
+                                   const void *x, int64_t batch, int64_t seq, void *y, void *latent_out,
+                                   void *workspace, size_t workspace_bytes, void *hip_stream) {
+  mla_status s = check_prefill_sizes(cfg, batch, seq);
+  if (s != MLA_OK) return s;
+  if ((s = check_fp8_config(cfg)) != MLA_OK) return s;
+  if (!w || !w->q_norm || !aligned16(w->q_norm))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "weights->q_norm must be a 16-byte aligned device pointer");
+  if (w->kv_norm && !aligned16(w->kv_norm))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "weight kv_norm is not 16-byte aligned");
+  if (!w8) return fail(MLA_ERR_INVALID_ARGUMENT, "FP8 weights are NULL");
+  const mla_config &c = *cfg;
+  const Fp8Dims d = fp8_dims(c);
+  const mla_fp8_matrix *mats[4] = {&w8->down, &w8->q_up, &w8->kv_up, &w8->out};
+  const char *names[4] = {"down", "q_up", "kv_up", "out"};
+  for (int i = 0; i < 4; ++i)
+    if ((s = check_fp8_matrix(*mats[i], d.N[i], d.K[i], names[i])) != MLA_OK) return s;
+  if (!x || !y || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "x, y and workspace must not be NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (latent_out && !aligned16(latent_out)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "x, y, latent_out and workspace must be 16-byte aligned");
+  const Fp8PrefillPlan p = plan_prefill_fp8(c, batch, seq);
+  if (workspace_bytes < p.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, p.total);
+
+  hipStream_t st = (hipStream_t)hip_stream;
+  char *ws = (char *)workspace;
+  char *down = ws + p.base.off_down, *q = ws + p.base.off_q, *kn = ws + p.base.off_kn,
+       *v = ws + p.base.off_v, *o = ws + p.base.off_o;
+  uint8_t *x8 = (uint8_t *)(ws + p.off_x8), *sx = (uint8_t *)(ws + p.off_sx);
+  uint8_t *cq8 = (uint8_t *)(ws + p.off_cq8), *scq = (uint8_t *)(ws + p.off_scq);
+  uint8_t *ckv8 = (uint8_t *)(ws + p.off_ckv8), *sckv = (uint8_t *)(ws + p.off_sckv);
+  uint8_t *o8 = (uint8_t *)(ws + p.off_o8), *so = (uint8_t *)(ws + p.off_so);
+  const int B = (int)batch, S = (int)seq, M = B * S, H = c.num_heads;
+  const int D = c.hidden_size, rq = c.q_lora_rank, rkv = c.kv_lora_rank;
+  const int dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim, dqk = dn + dr;
+  const int64_t ld_down = p.base.ld_down, pm = p.pitch_m;
+  const size_t es = 2;
+  const RopeTab tab = make_rope_tab(c.rope, dr);
+  auto product = [&](int i, const uint8_t *a, const uint8_t *sa, int nseg, const GemmSeg *segs, int Sv,
+                     int Hv) {
+    Fp8GemmDesc g;
+    g.a = a;
+    g.sa = sa;
+    g.lda = d.K[i];
+    g.ld_sa = pm;
+    g.b = mats[i]->codes;
+    g.sb = mats[i]->scales;
+    g.ldb = mats[i]->ld;
+    g.ld_sb = mats[i]->ld_scales;
+    g.M = M;
+    g.N = (int)d.N[i];
+    g.K = (int)d.K[i];
+    g.S = Sv;
+    g.H = Hv;
+    g.nseg = nseg;
+    for (int k = 0; k < nseg; ++k) g.seg[k] = segs[k];
+    return launch_fp8_gemm_seg(g, st);
+  };
+
+  // 1. x quantised in 1 x 128 tiles, then [c_q ‖ c_kv ‖ k_pe] (plain rows)
+  MLA_MARK(0);
+  MLA_HIP(launch_fp8_quant_rows(BF16, x, M, D, D, x8, D, sx, pm, st), "fp8 quantise x");
+  {
+    const GemmSeg seg{nullptr, 0, 0, down, (int)d.N[0], ld_down, 0};
+    MLA_HIP(product(0, x8, sx, 1, &seg, M, 1), "fp8 down projection");
+  }
+  // 2. RMSNorm(c_q) (and c_kv with kv_norm gains)
+  MLA_MARK(1);
+  MLA_HIP(launch_down_norms(c, w, down, M, ld_down, st), "rmsnorm");
+  // 3. RoPE of the shared key, latent copy
+  MLA_MARK(2);
+  MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, M, S, (int64_t)S * ld_down, ld_down, 1, 0,
+                      nullptr, tab, st),
+          "rope k_pe");
+  if (latent_out)
+    MLA_HIP(launch_copy_rows(c.dtype, latent_out, rkv + dr, down + (size_t)rq * es, ld_down, M, rkv + dr, st),
+            "latent copy");
+  // 4. c_q and c_kv quantised; q = [q_nope ‖ q_pe] per head
+  MLA_MARK(3);
+  MLA_HIP(launch_fp8_quant_rows(BF16, down, M, rq, ld_down, cq8, rq, scq, pm, st), "fp8 quantise c_q");
+  MLA_HIP(launch_fp8_quant_rows(BF16, down + (size_t)rq * es, M, rkv, ld_down, ckv8, rkv, sckv, pm, st),
+          "fp8 quantise c_kv");
+  {
+    const GemmSeg segs[2] = {GemmSeg{nullptr, 0, 0, q, dn, dqk, 0},
+                             GemmSeg{nullptr, 0, H * dn, q, dr, dqk, dn}};
+    MLA_HIP(product(1, cq8, scq, 2, segs, S, H), "fp8 q up-projection");
+  }
+  MLA_MARK(4);
+  MLA_HIP(launch_rope(c.dtype, q + (size_t)dn * es, M, S, (int64_t)H * S * dqk, dqk, H, (int64_t)S * dqk,
+                      nullptr, tab, st),
+          "rope q_pe");
+  // 5. k_nope head-major, v channel-major
+  MLA_MARK(5);
+  {
+    const GemmSeg segs[2] = {GemmSeg{nullptr, 0, 0, kn, dn, dn, 0},
+                             GemmSeg{nullptr, 0, H * dn, v, dv, dv, 0, 1}};
+    MLA_HIP(product(2, ckv8, sckv, 2, segs, S, H), "fp8 kv up-projection");
+  }
+  // 6. causal attention (bf16 operands, fp32 softmax)
+  MLA_MARK(6);
+  {
+    PrefillAttnArgs a;
+    a.q = q;
+    a.k_nope = kn;
+    a.k_pe = down + (size_t)(rq + rkv) * es;
+    a.ld_kpe = ld_down;
+    a.vt = v;
+    a.o = o;
+    a.B = B;
+    a.S = S;
+    a.H = H;
+    a.scale = resolve_scale(c);
+    a.Sk = S;
+    MLA_HIP(launch_prefill_attention(c.dtype, dn, dr, dv, a, st), "attention");
+  }
+  // 7. o quantised; y = o wo^T
+  MLA_MARK(7);
+  MLA_HIP(launch_fp8_quant_rows(BF16, o, M, H * dv, (int64_t)H * dv, o8, (int64_t)H * dv, so, pm, st),
+          "fp8 quantise o");
+  {
+    const GemmSeg seg{nullptr, 0, 0, y, D, D, 0};
+    MLA_HIP(product(3, o8, so, 1, &seg, M, 1), "fp8 output projection");
+  }
+  MLA_MARK(8);
+  return MLA_OK;
+}
+
 static mla_status check_varlen(const mla_config *cfg, int64_t n_seq, int64_t total) {
   if (n_seq < 1 || n_seq > (1 << 24))
     return fail(MLA_ERR_INVALID_ARGUMENT, "n_seq must be in [1, 2^24]");
@@ -1129,6 +1417,14 @@ mla_status mla_attention_backward_noalloc(int32_t dtype, int64_t batch_heads, in
 
 // ---- end of the allocation-free entry points ----
 
+mla_status mla_rmsnorm_backward_workspace_size(int64_t rows, int32_t n, size_t *bytes) {
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (rows < 0 || rows > INT32_MAX) return fail(MLA_ERR_INVALID_ARGUMENT, "rows must be in [0, 2^31 - 1]");
+  if (n < 1 || n > (1 << 20)) return fail(MLA_ERR_INVALID_ARGUMENT, "n must be in [1, 2^20]");
+  *bytes = rmsnorm_backward_scratch_floats(rows, n) * sizeof(float);
+  return MLA_OK;
+}
+
 mla_status mla_rmsnorm_backward(int32_t dtype, const void *x, const void *dy, const void *g, int64_t rows,
                                 int32_t n, float eps, void *dx, float *dg, void *workspace, size_t workspace_bytes,
                                 void *hip_stream) {
@@ -1143,9 +1439,9 @@ mla_status mla_rmsnorm_backward(int32_t dtype, const void *x, const void *dy, co
     if (!p) return fail(MLA_ERR_INVALID_ARGUMENT, "a tensor or the workspace is NULL");
     if ((uintptr_t)p % 4) return fail(MLA_ERR_INVALID_ARGUMENT, "tensors and workspace must be 4-byte aligned");
   }
-  if (workspace_bytes < (size_t)rows * sizeof(float))
-    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", (size_t)rows * sizeof(float));
-  MLA_HIP(launch_rmsnorm_backward(dtype == MLA_DTYPE_BF16 ? BF16 : F32, x, dy, g, rows, n, eps, dx, dg,
+  const size_t need = rmsnorm_backward_scratch_floats(rows, n) * sizeof(float);
+  if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", need);
+  MLA_HIP(launch_rmsnorm_backward(dtype == MLA_DTYPE_BF16 ? BF16 : F32, x, n, dy, n, g, rows, n, eps, dx, n, dg,
                                   reinterpret_cast<float *>(workspace), (hipStream_t)hip_stream),
           "rmsnorm backward");
   return MLA_OK;

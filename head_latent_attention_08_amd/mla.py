@@ -62,6 +62,15 @@ class Weights(ctypes.Structure):
         "wo")]
 
 
+class Fp8Matrix(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("ld", ctypes.c_int64), ("scales", ctypes.c_void_p),
+                ("ld_scales", ctypes.c_int64)]
+
+
+class Fp8Weights(ctypes.Structure):
+    _fields_ = [(n, Fp8Matrix) for n in ("down", "q_up", "kv_up", "out")]
+
+
 class PrefillLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("c_q", "c_kv", "k_pe", "q", "k_nope", "v", "o")] + [
         ("ld_down", ctypes.c_int64), ("total", ctypes.c_size_t)]
@@ -131,6 +140,18 @@ def load_library(path: str = LIB_PATH):
     lib.mla_rmsnorm_backward.argtypes = [ctypes.c_int32, P, P, P, i64, ctypes.c_int32, ctypes.c_float, P, P,
                                          P, ctypes.c_size_t, P]
     lib.mla_rmsnorm_backward.restype = st
+    lib.mla_rmsnorm_backward_workspace_size.argtypes = [i64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_rmsnorm_backward_workspace_size.restype = st
+    lib.mla_fp8_weights_size.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_fp8_prepare_weights.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P, ctypes.c_size_t,
+                                            ctypes.POINTER(Fp8Weights), P]
+    lib.mla_prefill_fp8_workspace_size.argtypes = [ctypes.POINTER(Config), i64, i64,
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_prefill_forward_fp8.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights),
+                                            ctypes.POINTER(Fp8Weights), P, i64, i64, P, P, P, ctypes.c_size_t, P]
+    for fn in ("mla_fp8_weights_size", "mla_fp8_prepare_weights", "mla_prefill_fp8_workspace_size",
+               "mla_prefill_forward_fp8"):
+        getattr(lib, fn).restype = st
     lib.mla_fp8_scale_pitch.argtypes = [i64]
     lib.mla_fp8_scale_pitch.restype = i64
     lib.mla_fp8_quantize_rows.argtypes = [P, ctypes.c_int32, i64, i64, i64, P, i64, P, i64, P]
@@ -504,10 +525,60 @@ def mla_rmsnorm_backward(x, dy, g, eps: float, stream=None):
     rows = x.numel() // n
     dx = torch.empty_like(x)
     dg = torch.empty(n, dtype=torch.float32, device=x.device)
-    ws = torch.empty(max(rows, 1), dtype=torch.float32, device=x.device)
+    need = ctypes.c_size_t(0)
+    _check(load_library().mla_rmsnorm_backward_workspace_size(rows, n, ctypes.byref(need)))
+    ws = torch.empty(max(need.value, 16), dtype=torch.uint8, device=x.device)
     _check(load_library().mla_rmsnorm_backward(dt, _ptr(x), _ptr(dy), _ptr(g), rows, n, eps, _ptr(dx), _ptr(dg),
-                                               _ptr(ws), ws.numel() * 4, _stream(stream)))
+                                               _ptr(ws), ws.numel(), _stream(stream)))
     return dx, dg
+
+
+def mla_fp8_prepare_weights(cfg: MlaConfig, weights: dict, stream=None):
+    """Block-quantise the bf16 projection weights for mla_prefill_forward_fp8.
+    Returns (buffer, Fp8Weights): the device buffer owns the codes and scale
+    bytes; keep it alive while the struct is used."""
+    lib = load_library()
+    c = cfg.c()
+    n = ctypes.c_size_t(0)
+    _check(lib.mla_fp8_weights_size(ctypes.byref(c), ctypes.byref(n)))
+    dev = next(iter(weights.values())).device
+    buf = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    w = make_weights(weights)
+    w8 = Fp8Weights()
+    _check(lib.mla_fp8_prepare_weights(ctypes.byref(c), ctypes.byref(w), _ptr(buf), n.value, ctypes.byref(w8),
+                                       _stream(stream)))
+    return buf, w8
+
+
+def mla_prefill_fp8_workspace_size(cfg: MlaConfig, batch: int, seq: int) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().mla_prefill_fp8_workspace_size(ctypes.byref(c), batch, seq, ctypes.byref(n)))
+    return n.value
+
+
+def mla_prefill_forward_fp8(cfg: MlaConfig, weights: dict, w8: Fp8Weights, x: torch.Tensor, y=None,
+                            latent_out=None, workspace=None, stream=None, want_latent: bool = False):
+    """The prefill with FP8 projections (w8 from mla_fp8_prepare_weights; from
+    `weights` only q_norm and the optional kv_norm are read).  Returns
+    (y, latent_out, workspace)."""
+    B, S, D = x.shape
+    dev = x.device
+    if y is None:
+        y = torch.empty((B, S, D), dtype=cfg.torch_dtype, device=dev)
+    if latent_out is None and want_latent:
+        latent_out = torch.empty((B, S, cfg.kv_lora_rank + cfg.qk_rope_head_dim), dtype=cfg.torch_dtype,
+                                 device=dev)
+    need = mla_prefill_fp8_workspace_size(cfg, B, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _device_check(x, y, latent_out, workspace)
+    w = make_weights(weights)
+    c = cfg.c()
+    _check(load_library().mla_prefill_forward_fp8(
+        ctypes.byref(c), ctypes.byref(w), ctypes.byref(w8), _ptr(x), B, S, _ptr(y), _ptr(latent_out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y, latent_out, workspace
 
 
 def mla_fp8_scale_pitch(rows: int) -> int:

@@ -351,6 +351,60 @@ MLA_API mla_status mla_fp8_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa
                         void *c, int32_t c_dtype, int64_t ldc, int64_t M, int64_t N, int64_t K,
                         void *hip_stream);
 
+/* ------------------------------------------------------------- FP8 prefill
+ * The prefill of mla_prefill_forward with its four projection products on
+ * block-scaled FP8, the scheme of the "Deep Seek V3" notes (section
+ * "infrastructure", the FP8 bullets): the linear layers run in E4M3 with
+ * fine-grained scales (1 x 128 tiles of each activation, 128 x 128 blocks of
+ * each weight, power-of-two scales as in mla_fp8_quantize_rows / _blocks)
+ * and fp32 accumulation, while attention, RMSNorm and RoPE stay in higher
+ * precision (bf16 storage, fp32 arithmetic).  The activations x, RMSNorm(c_q),
+ * c_kv and the attention output o are quantised right after the kernel that
+ * produces them.
+ *
+ * Weights: each projection's matrices are stacked by rows into one code
+ * matrix (each matrix block-quantised on its own, so a block never spans
+ * two matrices) with one scale byte per row and 128 columns. */
+typedef struct {
+  const uint8_t *codes;    /* [N, K] E4M3 codes, row pitch ld bytes          */
+  int64_t ld;              /* >= K, multiple of 16                           */
+  const uint8_t *scales;   /* [K / 128][ld_scales] E8M0 bytes, one per row    */
+  int64_t ld_scales;       /* >= mla_fp8_scale_pitch(N), multiple of 4        */
+} mla_fp8_matrix;
+
+typedef struct {
+  mla_fp8_matrix down;     /* [r_q + r_kv + d_r, D]: w_down_q, w_down_kv, w_kr */
+  mla_fp8_matrix q_up;     /* [H (d_n + d_r), r_q]: w_up_q, then w_qr          */
+  mla_fp8_matrix kv_up;    /* [H (d_n + d_v), r_kv]: w_up_k, then w_up_v       */
+  mla_fp8_matrix out;      /* [D, H d_v]: wo                                   */
+} mla_fp8_weights;
+
+/* Bytes of the buffer mla_fp8_prepare_weights fills for *cfg.
+ * Status: INVALID_ARGUMENT for a bad config; UNSUPPORTED unless bf16 with
+ * hidden_size, q_lora_rank, kv_lora_rank and num_heads * v_head_dim multiples
+ * of 128 and num_heads * qk_nope_head_dim a multiple of 256. */
+MLA_API mla_status mla_fp8_weights_size(const mla_config *cfg, size_t *bytes);
+/* Quantise the bf16 weights *w (device) into buffer (device, 256-byte
+ * aligned, mla_fp8_weights_size bytes, owned by the caller) and describe the
+ * result in *out (host struct; its pointers point into buffer).  Weights are
+ * static: call once, reuse for every forward.  Asynchronous on hip_stream.
+ * Status: as mla_fp8_weights_size; INVALID_ARGUMENT for NULL or misaligned
+ * pointers; WORKSPACE_TOO_SMALL for a short buffer; HIP. */
+MLA_API mla_status mla_fp8_prepare_weights(const mla_config *cfg, const mla_weights *w, void *buffer,
+                                   size_t buffer_bytes, mla_fp8_weights *out, void *hip_stream);
+MLA_API mla_status mla_prefill_fp8_workspace_size(const mla_config *cfg, int64_t batch, int64_t seq,
+                                          size_t *bytes);
+/* y = MLA(x) as mla_prefill_forward, with the projections on *w8.  From *w
+ * only the RMSNorm gains are read (q_norm; kv_norm or NULL).  Arguments,
+ * layouts, latent_out and stage events as mla_prefill_forward (stage 0 also
+ * quantises x, stage 3 c_q and c_kv, stage 7 o).
+ * Status: as mla_prefill_forward and mla_fp8_weights_size; INVALID_ARGUMENT
+ * for NULL or misaligned FP8 matrices or pitches below their minimum. */
+MLA_API mla_status mla_prefill_forward_fp8(const mla_config *cfg, const mla_weights *w,
+                                   const mla_fp8_weights *w8, const void *x, int64_t batch,
+                                   int64_t seq, void *y, void *latent_out, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream);
+
 /* ------------------------------------------------------ attention backward
  * Gradients of the causal attention of "The Evolving Transformer -- DeepSeek
  * V2 & V3", section 01 (per head P = softmax(scale Q K^T, tril mask),
@@ -400,11 +454,15 @@ MLA_API mla_status mla_attention_backward_noalloc(int32_t dtype, int64_t batch_h
  * r = (mean(x^2) + eps)^-1/2 per row): dx = r (g dy) - x r^3 mean(x g dy) and
  * dg = sum over rows of dy x r.  x, dy, dx [rows, n] contiguous and g [n] in
  * dtype (fp32 or bf16); dg fp32 [n] (summed over rows in order:
- * deterministic); the workspace holds 4 bytes per row.  Device pointers,
- * 4-byte aligned, owned by the caller.
+ * deterministic: fixed chunks of 64 rows, then the chunks in order); the
+ * workspace holds mla_rmsnorm_backward_workspace_size bytes (4 per row plus
+ * 4 per column per 64-row chunk).  Device pointers, 4-byte aligned, owned by
+ * the caller.
  * Status: INVALID_ARGUMENT for NULL or misaligned pointers (rows > 0),
  * rows < 0 or > 2^31 - 1, n < 1 or > 2^20, eps < 0 or non-finite, a bad
- * dtype; WORKSPACE_TOO_SMALL below 4 * rows bytes; HIP for a failed launch. */
+ * dtype; WORKSPACE_TOO_SMALL below the workspace size; HIP for a failed
+ * launch. */
+MLA_API mla_status mla_rmsnorm_backward_workspace_size(int64_t rows, int32_t n, size_t *bytes);
 MLA_API mla_status mla_rmsnorm_backward(int32_t dtype, const void *x, const void *dy, const void *g,
                                 int64_t rows, int32_t n, float eps, void *dx, float *dg,
                                 void *workspace, size_t workspace_bytes, void *hip_stream);

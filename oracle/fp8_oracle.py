@@ -136,3 +136,109 @@ def dequant_weight(codes, e):
 def fp8_gemm(qa, ea, qb, eb):
     """C [M, N] = dequant_act(qa, ea) @ dequant_weight(qb, eb)^T in float64."""
     return dequant_act(qa, ea) @ dequant_weight(qb, eb).T
+
+
+def quantized_product(x, w):
+    """x [M, K] times w [N, K]^T with x quantised in 1 x 128 tiles and w in
+    128 x 128 blocks, the product in float64 (the block-scaled FP8 product of
+    the notes' scheme, applied to one projection)."""
+    qa, ea = quantize_act_tiles(x)
+    qb, eb = quantize_weight_blocks(w)
+    return fp8_gemm(qa, ea, qb, eb)
+
+
+def qdq_act(x):
+    """x [M, K] after 1 x 128 tile quantisation (dequantised, float64)."""
+    return dequant_act(*quantize_act_tiles(x))
+
+
+def qdq_weight(w):
+    """w [N, K] after 128 x 128 block quantisation (dequantised, float64)."""
+    return dequant_weight(*quantize_weight_blocks(w))
+
+
+def mla_prefill_fp8(cfg, w, x):
+    """The MLA prefill with its four projection products in block-scaled FP8.
+
+    The notes' scheme keeps attention, normalisation and the rest in higher
+    precision and runs the linear layers in FP8 with fine-grained scales.
+    So, following the MLA listing of "The Evolving Transformer -- DeepSeek V2
+    & V3" (section 01) step by step as the float64 oracle does, each
+    projection's input activation is quantised in 1 x 128 tiles and each
+    weight matrix in 128 x 128 blocks (every matrix on its own), and the
+    product is taken of the dequantised values:
+
+      down  [c_q ‖ c_kv ‖ k_pe] = q(x) [q(W_dq); q(W_dkv); q(W_kr)]^T
+      q up  [q_nope ‖ q_pe]     = q(RMSNorm(c_q)) [q(W_uq); q(W_qr)]^T
+      kv up [k_nope ‖ v]        = q(c_kv) [q(W_uk); q(W_uv)]^T
+      out   y                   = q(o) q(W_o)^T
+
+    RMSNorm, RoPE and the causal softmax attention are the float64 oracle's.
+    x: [B, S, D]; returns y [B, S, D]."""
+    from . import mla_oracle as mo
+    x = np.asarray(x, dtype=np.float64)
+    B, S, D = x.shape
+    H = cfg.num_attention_heads
+    dn, dr, dv = cfg.qk_nope_head_dim, cfg.qk_rope_head_dim, cfg.v_head_dim
+    f = {k: np.asarray(v, dtype=np.float64) for k, v in w.items() if v is not None}
+    xf = x.reshape(B * S, D)
+    c_q = quantized_product(xf, f["w_down_q"])
+    c_kv = quantized_product(xf, f["w_down_kv"])
+    k_pe = quantized_product(xf, f["w_kr"])
+    c_qn = mo.rmsnorm(c_q, f["q_norm"], cfg.rms_norm_eps)
+    if "kv_norm" in f:
+        c_kv = mo.rmsnorm(c_kv, f["kv_norm"], cfg.rms_norm_eps)
+    q_nope = quantized_product(c_qn, f["w_up_q"]).reshape(B, S, H, dn)
+    q_pe = quantized_product(c_qn, f["w_qr"]).reshape(B, S, H, dr)
+    k_nope = quantized_product(c_kv, f["w_up_k"]).reshape(B, S, H, dn)
+    v = quantized_product(c_kv, f["w_up_v"]).reshape(B, S, H, dv)
+    pos = np.arange(S)
+    q_pe = np.stack([mo.apply_rope(q_pe[b], pos, cfg) for b in range(B)])
+    k_pe = np.stack([mo.apply_rope(k_pe.reshape(B, S, dr)[b], pos, cfg) for b in range(B)])
+    scale = mo.softmax_scale(cfg)
+    o = np.empty((B, S, H, dv))
+    for b in range(B):
+        for h in range(H):
+            q = np.concatenate([q_nope[b, :, h], q_pe[b, :, h]], axis=-1)
+            k = np.concatenate([k_nope[b, :, h], k_pe[b]], axis=-1)
+            o[b, :, h] = mo.causal_attention(q, k, v[b, :, h], scale)
+    y = quantized_product(o.reshape(B * S, H * dv), f["wo"])
+    return y.reshape(B, S, D)
+
+
+def mla_prefill_fp8_rows(cfg, w, x, rows, batch: int = 0):
+    """y[batch, r] of :func:`mla_prefill_fp8` for the query rows ``rows``,
+    with the latent [S, r_kv + d_r] of every token.  Same quantisation and
+    arithmetic; the queries are formed only for ``rows`` (their activation
+    tiles are row-local, so quantising a subset of rows changes nothing) and
+    the keys and values head by head, so V3 sizes fit in memory."""
+    from . import mla_oracle as mo
+    xb = np.asarray(x[batch], dtype=np.float64)
+    S, D = xb.shape
+    H = cfg.num_attention_heads
+    dn, dr, dv = cfg.qk_nope_head_dim, cfg.qk_rope_head_dim, cfg.v_head_dim
+    rows = np.asarray(rows, dtype=np.int64)
+    f = {k: np.asarray(v, dtype=np.float64) for k, v in w.items() if v is not None}
+    pos = np.arange(S)
+    xq = qdq_act(xb)  # x quantised once; its tiles are row-local
+    c_kv = xq @ qdq_weight(f["w_down_kv"]).T
+    if "kv_norm" in f:
+        c_kv = mo.rmsnorm(c_kv, f["kv_norm"], cfg.rms_norm_eps)
+    k_pe = mo.apply_rope(xq @ qdq_weight(f["w_kr"]).T, pos, cfg)
+    c_qn = mo.rmsnorm(xq[rows] @ qdq_weight(f["w_down_q"]).T, f["q_norm"], cfg.rms_norm_eps)
+    q_nope = quantized_product(c_qn, f["w_up_q"]).reshape(len(rows), H, dn)
+    q_pe = mo.apply_rope(quantized_product(c_qn, f["w_qr"]).reshape(len(rows), H, dr), rows, cfg)
+    kmax = int(rows.max()) + 1
+    # the kv up-projection of the quantised latent: operands quantised once
+    ca = qdq_act(c_kv[:kmax])
+    wuk = qdq_weight(f["w_up_k"])
+    wuv = qdq_weight(f["w_up_v"])
+    scale = mo.softmax_scale(cfg)
+    o = np.empty((len(rows), H, dv))
+    for h in range(H):
+        k = np.concatenate([ca @ wuk[h * dn:(h + 1) * dn].T, k_pe[:kmax]], axis=-1)
+        v = ca @ wuv[h * dv:(h + 1) * dv].T
+        q = np.concatenate([q_nope[:, h], q_pe[:, h]], axis=-1)
+        o[:, h] = mo.causal_attention(q, k, v, scale, q_pos=rows)
+    y = quantized_product(o.reshape(len(rows), H * dv), f["wo"])
+    return y, np.concatenate([c_kv, k_pe], axis=-1)

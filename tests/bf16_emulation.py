@@ -119,3 +119,75 @@ def decode_absorbed_bf16(cfg: orc.Cfg, w: dict, x, cache, lens, rounding: bool =
         o = _r(np.einsum("hvr,hr->hv", wuv, o_lat))
         y[b] = _r(o.reshape(-1) @ f["wo"].T)
     return y
+
+
+def prefill_fp8_bf16(cfg: orc.Cfg, w: dict, x):
+    """y [B, S, D] of the FP8 prefill (oracle.fp8_oracle.mla_prefill_fp8)
+    with bf16 storage of the intermediates the HIP path keeps in bf16 (the
+    projection outputs, RMSNorm(c_q), post-RoPE q_pe / k_pe, the softmax
+    probabilities, o, y); each projection input is quantised from those
+    stored values, as on the device."""
+    from oracle import fp8_oracle as fo
+    _r = _round
+    x = np.asarray(x, dtype=np.float64)
+    B, S, D = x.shape
+    H = cfg.num_attention_heads
+    dn, dr, dv = cfg.qk_nope_head_dim, cfg.qk_rope_head_dim, cfg.v_head_dim
+    f = {k: np.asarray(v, dtype=np.float64) for k, v in w.items() if v is not None}
+    xf = x.reshape(B * S, D)
+    c_q = _r(fo.quantized_product(xf, f["w_down_q"]))
+    c_kv = _r(fo.quantized_product(xf, f["w_down_kv"]))
+    k_pe = _r(fo.quantized_product(xf, f["w_kr"]))
+    c_qn = _r(orc.rmsnorm(c_q, f["q_norm"], cfg.rms_norm_eps))
+    if "kv_norm" in f:
+        c_kv = _r(orc.rmsnorm(c_kv, f["kv_norm"], cfg.rms_norm_eps))
+    q_nope = _r(fo.quantized_product(c_qn, f["w_up_q"])).reshape(B, S, H, dn)
+    q_pe = _r(fo.quantized_product(c_qn, f["w_qr"])).reshape(B, S, H, dr)
+    k_nope = _r(fo.quantized_product(c_kv, f["w_up_k"])).reshape(B, S, H, dn)
+    v = _r(fo.quantized_product(c_kv, f["w_up_v"])).reshape(B, S, H, dv)
+    pos = np.arange(S)
+    q_pe = _r(np.stack([orc.apply_rope(q_pe[b], pos, cfg) for b in range(B)]))
+    k_pe = _r(np.stack([orc.apply_rope(k_pe.reshape(B, S, dr)[b], pos, cfg) for b in range(B)]))
+    scale = orc.softmax_scale(cfg)
+    o = np.empty((B, S, H, dv))
+    for b in range(B):
+        for h in range(H):
+            q = np.concatenate([q_nope[b, :, h], q_pe[b, :, h]], axis=-1)
+            k = np.concatenate([k_nope[b, :, h], k_pe[b]], axis=-1)
+            o[b, :, h] = _attention_bf16_p(q, k, v[b, :, h], scale, _r)
+    o = _r(o).reshape(B * S, H * dv)
+    return _r(fo.quantized_product(o, f["wo"])).reshape(B, S, D)
+
+
+def prefill_fp8_bf16_rows(cfg: orc.Cfg, w: dict, x, rows, batch: int = 0):
+    """Rows ``rows`` of :func:`prefill_fp8_bf16` (keys and values head by
+    head, queries only for those rows), for V3 sizes."""
+    from oracle import fp8_oracle as fo
+    _r = _round
+    xb = np.asarray(x[batch], dtype=np.float64)
+    S, D = xb.shape
+    H = cfg.num_attention_heads
+    dn, dr, dv = cfg.qk_nope_head_dim, cfg.qk_rope_head_dim, cfg.v_head_dim
+    rows = np.asarray(rows, dtype=np.int64)
+    f = {k: np.asarray(v, dtype=np.float64) for k, v in w.items() if v is not None}
+    pos = np.arange(S)
+    xq = fo.qdq_act(xb)
+    c_kv = _r(xq @ fo.qdq_weight(f["w_down_kv"]).T)
+    if "kv_norm" in f:
+        c_kv = _r(orc.rmsnorm(c_kv, f["kv_norm"], cfg.rms_norm_eps))
+    k_pe = _r(orc.apply_rope(_r(xq @ fo.qdq_weight(f["w_kr"]).T), pos, cfg))
+    c_qn = _r(orc.rmsnorm(_r(xq[rows] @ fo.qdq_weight(f["w_down_q"]).T), f["q_norm"], cfg.rms_norm_eps))
+    q_nope = _r(fo.quantized_product(c_qn, f["w_up_q"])).reshape(len(rows), H, dn)
+    q_pe = _r(orc.apply_rope(_r(fo.quantized_product(c_qn, f["w_qr"])).reshape(len(rows), H, dr), rows, cfg))
+    kmax = int(rows.max()) + 1
+    ca = fo.qdq_act(c_kv[:kmax])
+    wuk = fo.qdq_weight(f["w_up_k"])
+    wuv = fo.qdq_weight(f["w_up_v"])
+    scale = orc.softmax_scale(cfg)
+    o = np.empty((len(rows), H, dv))
+    for h in range(H):
+        k = np.concatenate([_r(ca @ wuk[h * dn:(h + 1) * dn].T), k_pe[:kmax]], axis=-1)
+        v = _r(ca @ wuv[h * dv:(h + 1) * dv].T)
+        q = np.concatenate([q_nope[:, h], q_pe[:, h]], axis=-1)
+        o[:, h] = _attention_bf16_p(q, k, v, scale, _r, q_pos=rows)
+    return _r(fo.quantized_product(_r(o).reshape(len(rows), H * dv), f["wo"]))

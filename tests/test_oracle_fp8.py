@@ -159,3 +159,55 @@ def test_weight_block_exponent_is_local():
     diff = np.argwhere(e1 != e0)
     assert diff.tolist() == [[1, 2]]
     assert e0.shape == (3, 3)
+
+
+# ------------------------------------------------ FP8 prefill (row p, F4) --
+
+def test_fp8_prefill_with_exact_products_is_the_prefill(monkeypatch):
+    # the FP8 prefill oracle is the prefill oracle's steps with each
+    # projection product replaced by its quantised form: with the product
+    # made exact again it must be the float64 prefill itself
+    from oracle import fp8_oracle as fo
+    import oracle as orc
+    from tests.helpers import oracle_cfg, si
+    c = si.CONFIGS["small"]
+    x, w = si.make_inputs(c, seq=40, gains="random")
+    cfg = oracle_cfg(c, rope="interleaved")
+    monkeypatch.setattr(fo, "quantized_product", lambda a, b: np.asarray(a) @ np.asarray(b, dtype=np.float64).T)
+    np.testing.assert_allclose(fo.mla_prefill_fp8(cfg, w, x), orc.mla_prefill(cfg, w, x), rtol=1e-12,
+                               atol=1e-12)
+    w2 = dict(w, kv_norm=np.ones(c["kv_lora_rank"], dtype=np.float32) * 1.5)
+    np.testing.assert_allclose(fo.mla_prefill_fp8(cfg, w2, x), orc.mla_prefill(cfg, w2, x), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_fp8_prefill_quantises_each_projection_input():
+    # every product sees quantised operands: the result differs from the
+    # exact prefill by an E4M3-sized error (3 mantissa bits: 2^-4 relative
+    # per element, averaged down over the reductions), never by more
+    from oracle import fp8_oracle as fo
+    import oracle as orc
+    from tests.helpers import oracle_cfg, row_errors, si
+    c = si.CONFIGS["small"]
+    x, w = si.make_inputs(c, seq=64, gains="random")
+    cfg = oracle_cfg(c, rope="interleaved")
+    rel, _ = row_errors(fo.mla_prefill_fp8(cfg, w, x), orc.mla_prefill(cfg, w, x))
+    assert 1e-3 < rel.max() < 0.15, rel.max()
+    # the quantised product of one projection is fp8_gemm of the quantised operands
+    xa = x.reshape(-1, x.shape[-1]).astype(np.float64)
+    qa, ea = fo.quantize_act_tiles(xa)
+    qb, eb = fo.quantize_weight_blocks(w["w_down_q"])
+    np.testing.assert_array_equal(fo.quantized_product(xa, w["w_down_q"]), fo.fp8_gemm(qa, ea, qb, eb))
+
+
+def test_fp8_prefill_rows_match_full_fp8_prefill():
+    from oracle import fp8_oracle as fo
+    from tests.helpers import oracle_cfg, si
+    c = si.CONFIGS["small"]
+    x, w = si.make_inputs(c, seq=48, gains="random")
+    cfg = oracle_cfg(c, rope="interleaved")
+    full = fo.mla_prefill_fp8(cfg, w, x)
+    rows = np.array([0, 5, 17, 47])
+    yr, lat = fo.mla_prefill_fp8_rows(cfg, w, x, rows, batch=1)
+    np.testing.assert_allclose(yr, full[1, rows], rtol=1e-12, atol=1e-12)
+    assert lat.shape == (48, c["kv_lora_rank"] + c["qk_rope_head_dim"])
