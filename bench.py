@@ -356,9 +356,31 @@ def attention_backward_line(m, S, log, reps=2):
     log(f"bench: attention backward H={H} S={S}: {ms:.2f} ms, {tf:.1f} TFLOP/s")
     del q, k, v, o, do
     torch.cuda.empty_cache()
+    # the whole MLA backward (forward recomputed, every gradient) on the V3
+    # prefill's inputs with a seeded upstream gradient
+    import synth_inputs as si
+    from tests.gpu_util import mla_cfg, to_dev, weights_to_dev
+    c = si.CONFIGS["v3_prefill"]
+    x, w = si.make_inputs(c, seq=S)
+    xd, wd = to_dev(x, "bf16"), weights_to_dev(w, "bf16")
+    dy = torch.randn(xd.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    cfg = mla_cfg(c)
+    ws = torch.empty(m.mla_backward_workspace_size(cfg, 1, S), dtype=torch.uint8, device="cuda")
+    m.mla_backward(cfg, wd, xd, dy, workspace=ws)
+    torch.cuda.synchronize()
+    e0.record(st)
+    m.mla_backward(cfg, wd, xd, dy, workspace=ws)
+    e1.record(st)
+    torch.cuda.synchronize()
+    full_ms = e0.elapsed_time(e1)
+    log(f"bench: MLA backward (forward recomputed, all gradients) S={S}: {full_ms:.2f} ms")
+    del xd, wd, dy, ws
+    torch.cuda.empty_cache()
     return {"heads": H, "seq_len": S, "d_qk": dqk, "d_v": dv, "dtype": "bf16", "ms": ms,
             "gflop": fl / 1e9, "tflops": tf, "frac_of_bf16_peak": tf / MI355X_BF16_TFLOPS,
-            "note": "vector-ALU kernels (no MFMA yet)"}
+            "note": "vector-ALU kernels (no MFMA yet)",
+            "mla_backward_ms": full_ms,
+            "mla_backward_note": "mla_backward at V3 sizes, B=1: forward recomputed, dx and every weight gradient"}
 
 
 def _read_csv(path):

@@ -513,6 +513,310 @@ mla_status mla_prefill_forward(const mla_config *cfg, const mla_weights *w, cons
                         hip_stream, nullptr, 0);
 }
 
+// ---------------------------------------------------------------- MLA backward
+// Every gradient of y = MLA(x) for an upstream dy: the forward's steps are
+// run again (the intermediates the backward reads land in the workspace),
+// then the chain rule back through them, in reverse order.
+namespace {
+
+struct BackwardPlan {
+  PrefillPlan fwd;
+  size_t off_cq_raw, off_ckv_raw, off_vh, off_kh, off_oh, off_doh, off_dqh, off_dkh, off_dvh, off_att,
+      off_pos, off_gq, off_gkv, off_dcqn, off_dckv, off_ddown, off_wq, off_wkv, off_wd, off_rms, total;
+};
+
+BackwardPlan plan_backward(const mla_config &c, int64_t B, int64_t S) {
+  BackwardPlan p;
+  p.fwd = plan_prefill(c, B, S);
+  const size_t es = dtype_size(c.dtype);
+  const int64_t M = B * S, H = c.num_heads;
+  const int64_t rq = c.q_lora_rank, rkv = c.kv_lora_rank, D = c.hidden_size;
+  const int64_t dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim;
+  size_t off = p.fwd.total;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  p.off_cq_raw = take((size_t)M * rq * es);
+  p.off_ckv_raw = take((size_t)M * rkv * es);
+  p.off_vh = take((size_t)M * H * dv * es);
+  p.off_kh = take((size_t)M * H * (dn + dr) * es);
+  p.off_oh = take((size_t)M * H * dv * es);
+  p.off_doh = take((size_t)M * H * dv * es);
+  p.off_dqh = take((size_t)M * H * (dn + dr) * es);
+  p.off_dkh = take((size_t)M * H * (dn + dr) * es);
+  p.off_dvh = take((size_t)M * H * dv * es);
+  p.off_att = take((size_t)M * H * 2 * sizeof(float));
+  p.off_pos = take((size_t)M * sizeof(int32_t));
+  p.off_gq = take((size_t)M * H * (dn + dr) * es);
+  p.off_gkv = take((size_t)M * H * (dn + dv) * es);
+  p.off_dcqn = take((size_t)M * rq * es);
+  p.off_dckv = take((size_t)M * rkv * es);
+  p.off_ddown = take((size_t)M * p.fwd.ld_down * es);
+  p.off_wq = take((size_t)H * (dn + dr) * rq * es);
+  p.off_wkv = take((size_t)H * (dn + dv) * rkv * es);
+  p.off_wd = take((size_t)(rq + rkv + dr) * D * es);
+  p.off_rms = take(std::max(rmsnorm_backward_scratch_floats(M, (int)rq), rmsnorm_backward_scratch_floats(M, (int)rkv)) *
+                   sizeof(float));
+  p.total = off;
+  return p;
+}
+
+// A plain row-major product C [M, N] (pitch ldc) = op(A) op(B): A stored
+// [M][K] (pitch lda) or, a_km, [K][M]; B stored [N][K] or, b_kn, [K][N].
+hipError_t plain_gemm(int dtype, const void *A, int64_t lda, bool a_km, const void *B, int64_t ldb, bool b_kn,
+                      void *C, int64_t ldc, int M, int N, int K, hipStream_t st) {
+  GemmDesc g;
+  g.dtype = dtype;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.A = A;
+  g.lda = lda;
+  g.a_km = a_km;
+  g.b_kn = b_kn;
+  g.S = M;
+  g.H = 1;
+  g.nseg = 1;
+  g.seg[0] = GemmSeg{B, ldb, 0, C, N, ldc, 0};
+  return launch_gemm(g, st);
+}
+
+}  // namespace
+
+mla_status mla_backward_workspace_size(const mla_config *cfg, int64_t batch, int64_t seq, size_t *bytes) {
+  mla_status s = check_prefill_sizes(cfg, batch, seq);
+  if (s != MLA_OK) return s;
+  if (!bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (batch * seq * cfg->num_heads > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "batch x seq x num_heads must stay below 2^31");
+  *bytes = plan_backward(*cfg, batch, seq).total;
+  return MLA_OK;
+}
+
+mla_status mla_backward(const mla_config *cfg, const mla_weights *w, const void *x, int64_t batch, int64_t seq,
+                        const void *dy, void *dx, const mla_weight_grads *grads, void *workspace,
+                        size_t workspace_bytes, void *hip_stream) {
+  size_t need = 0;
+  mla_status s = mla_backward_workspace_size(cfg, batch, seq, &need);
+  if (s != MLA_OK) return s;
+  if ((s = check_weights(w)) != MLA_OK) return s;
+  if (!x || !dy || !dx || !workspace || !grads)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "x, dy, dx, grads and workspace must not be NULL");
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(workspace))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "x, dy, dx and workspace must be 16-byte aligned");
+  {
+    const struct {
+      const char *name;
+      const void *p;
+    } gs[] = {{"w_down_q", grads->w_down_q}, {"q_norm", grads->q_norm}, {"w_up_q", grads->w_up_q},
+              {"w_qr", grads->w_qr},         {"w_down_kv", grads->w_down_kv}, {"w_kr", grads->w_kr},
+              {"w_up_k", grads->w_up_k},     {"w_up_v", grads->w_up_v},       {"wo", grads->wo}};
+    for (auto &g : gs)
+      if (!g.p || !aligned16(g.p)) return fail(MLA_ERR_INVALID_ARGUMENT, "gradient %s is NULL or not 16-byte aligned", g.name);
+    if (w->kv_norm && (!grads->kv_norm || !aligned16(grads->kv_norm)))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "gradient kv_norm is NULL or not 16-byte aligned (weights carry kv_norm)");
+  }
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+
+  const mla_config &c = *cfg;
+  const BackwardPlan p = plan_backward(c, batch, seq);
+  hipStream_t st = (hipStream_t)hip_stream;
+  const int dt = c.dtype;
+  const size_t es = dtype_size(dt);
+  char *ws = (char *)workspace;
+  auto at = [&](size_t off) { return ws + off; };
+  char *down = at(p.fwd.off_down), *q = at(p.fwd.off_q), *kn = at(p.fwd.off_kn), *vt = at(p.fwd.off_v),
+       *o = at(p.fwd.off_o);
+  char *cq_raw = at(p.off_cq_raw), *ckv_raw = at(p.off_ckv_raw), *vh = at(p.off_vh), *kh = at(p.off_kh),
+       *oh = at(p.off_oh), *doh = at(p.off_doh), *dqh = at(p.off_dqh), *dkh = at(p.off_dkh), *dvh = at(p.off_dvh);
+  char *gq = at(p.off_gq), *gkv = at(p.off_gkv), *dcqn = at(p.off_dcqn), *dckv = at(p.off_dckv),
+       *ddown = at(p.off_ddown), *wq = at(p.off_wq), *wkv = at(p.off_wkv), *wd = at(p.off_wd);
+  int32_t *pos_neg = reinterpret_cast<int32_t *>(at(p.off_pos));
+  float *rms = reinterpret_cast<float *>(at(p.off_rms));
+  const int B = (int)batch, S = (int)seq, M = B * S, H = c.num_heads;
+  const int D = c.hidden_size, rq = c.q_lora_rank, rkv = c.kv_lora_rank;
+  const int dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim, dqk = dn + dr;
+  const int64_t ld = p.fwd.ld_down;
+  const RopeTab tab = make_rope_tab(c.rope, dr);
+  const float scale = resolve_scale(c);
+
+  // ---- forward, keeping what the backward reads
+  {
+    GemmDesc g;
+    g.dtype = dt;
+    g.M = M;
+    g.N = rq + rkv + dr;
+    g.K = D;
+    g.A = x;
+    g.lda = D;
+    g.S = M;
+    g.H = 1;
+    g.nseg = 3;
+    g.seg[0] = GemmSeg{w->w_down_q, D, 0, down, rq, ld, 0};
+    g.seg[1] = GemmSeg{w->w_down_kv, D, rq, down, rkv, ld, rq};
+    g.seg[2] = GemmSeg{w->w_kr, D, rq + rkv, down, dr, ld, rq + rkv};
+    MLA_HIP(launch_gemm(g, st), "down projection");
+  }
+  MLA_HIP(launch_copy_rows(dt, cq_raw, rq, down, ld, M, rq, st), "c_q copy");
+  if (w->kv_norm) MLA_HIP(launch_copy_rows(dt, ckv_raw, rkv, down + (size_t)rq * es, ld, M, rkv, st), "c_kv copy");
+  MLA_HIP(launch_down_norms(c, w, down, M, ld, st), "rmsnorm");
+  MLA_HIP(launch_rope(dt, down + (size_t)(rq + rkv) * es, M, S, (int64_t)S * ld, ld, 1, 0, nullptr, tab, st),
+          "rope k_pe");
+  {
+    GemmDesc g;
+    g.dtype = dt;
+    g.M = M;
+    g.N = H * dqk;
+    g.K = rq;
+    g.A = down;
+    g.lda = ld;
+    g.S = S;
+    g.H = H;
+    g.nseg = 2;
+    g.seg[0] = GemmSeg{w->w_up_q, rq, 0, q, dn, dqk, 0};
+    g.seg[1] = GemmSeg{w->w_qr, rq, H * dn, q, dr, dqk, dn};
+    MLA_HIP(launch_gemm(g, st), "q up-projection");
+  }
+  MLA_HIP(launch_rope(dt, q + (size_t)dn * es, M, S, (int64_t)H * S * dqk, dqk, H, (int64_t)S * dqk, nullptr, tab,
+                      st),
+          "rope q_pe");
+  {
+    GemmDesc g;
+    g.dtype = dt;
+    g.M = M;
+    g.N = H * (dn + dv);
+    g.K = rkv;
+    g.A = down + (size_t)rq * es;
+    g.lda = ld;
+    g.S = S;
+    g.H = H;
+    g.nseg = 2;
+    g.seg[0] = GemmSeg{w->w_up_k, rkv, 0, kn, dn, dn, 0};
+    g.seg[1] = GemmSeg{w->w_up_v, rkv, H * dn, vt, dv, dv, 0, 1};  // channel-major for the forward attention
+    MLA_HIP(launch_gemm(g, st), "kv up-projection");
+    GemmDesc gv = g;  // and row-major per head for the backward
+    gv.N = H * dv;
+    gv.nseg = 1;
+    gv.seg[0] = GemmSeg{w->w_up_v, rkv, 0, vh, dv, dv, 0};
+    MLA_HIP(launch_gemm(gv, st), "v up-projection");
+  }
+  {
+    PrefillAttnArgs a;
+    a.q = q;
+    a.k_nope = kn;
+    a.k_pe = down + (size_t)(rq + rkv) * es;
+    a.ld_kpe = ld;
+    a.vt = vt;
+    a.o = o;
+    a.B = B;
+    a.S = S;
+    a.H = H;
+    a.scale = scale;
+    a.Sk = S;
+    MLA_HIP(launch_prefill_attention(dt, dn, dr, dv, a, st), "attention");
+  }
+
+  // ---- backward
+  // y = o wo^T: dwo = dy^T o, do = dy wo (per head)
+  MLA_HIP(plain_gemm(dt, dy, D, true, o, (int64_t)H * dv, true, grads->wo, (int64_t)H * dv, D, H * dv, M, st),
+          "dwo");
+  {
+    GemmDesc g;
+    g.dtype = dt;
+    g.M = M;
+    g.N = H * dv;
+    g.K = D;
+    g.A = dy;
+    g.lda = D;
+    g.b_kn = true;
+    g.S = S;
+    g.H = H;
+    g.nseg = 1;
+    g.seg[0] = GemmSeg{w->wo, (int64_t)H * dv, 0, doh, dv, dv, 0};
+    MLA_HIP(launch_gemm(g, st), "do");
+  }
+  // attention backward per head on K = [k_nope ‖ k_pe] and the stored o
+  MLA_HIP(launch_build_keys(dt, kn, down + (size_t)(rq + rkv) * es, ld, kh, dn, dr, B, S, H, st), "keys");
+  MLA_HIP(launch_permute_heads(dt, true, o, (int64_t)H * dv, 0, oh, dv, 0, dv, B, S, H, st), "o per head");
+  {
+    AttnBwdArgs a;
+    a.q = q;
+    a.k = kh;
+    a.v = vh;
+    a.o = oh;
+    a.dout = doh;
+    a.dq = dqh;
+    a.dk = dkh;
+    a.dvo = dvh;
+    a.lse = reinterpret_cast<float *>(at(p.off_att));
+    a.delta = a.lse + (int64_t)M * H;
+    a.BH = B * H;
+    a.S = S;
+    a.dqk = dqk;
+    a.dv = dv;
+    a.scale = scale;
+    MLA_HIP(launch_attention_backward(dt == MLA_DTYPE_BF16 ? BF16 : F32, a, st), "attention backward");
+  }
+  // RoPE backward (rotation at negated positions) of dq_pe; the shared key's
+  // gradient summed over heads, then rotated back, into ddown's k_pe columns
+  MLA_HIP(launch_neg_positions(pos_neg, M, S, st), "negated positions");
+  MLA_HIP(launch_rope(dt, dqh + (size_t)dn * es, M, S, (int64_t)H * S * dqk, dqk, H, (int64_t)S * dqk, pos_neg, tab,
+                      st),
+          "rope backward q_pe");
+  MLA_HIP(launch_head_sum(dt, dkh, dqk, dn, ddown + (size_t)(rq + rkv) * es, ld, dr, B, S, H, st), "k_pe head sum");
+  MLA_HIP(launch_rope(dt, ddown + (size_t)(rq + rkv) * es, M, S, (int64_t)S * ld, ld, 1, 0, pos_neg, tab, st),
+          "rope backward k_pe");
+  // token-major gradients: gq = [dq_nope ‖ dq_pe_raw], gkv = [dk_nope ‖ dv]
+  const int64_t lgq = (int64_t)H * dqk, lgkv = (int64_t)H * (dn + dv);
+  MLA_HIP(launch_permute_heads(dt, false, dqh, dqk, 0, gq, lgq, 0, dn, B, S, H, st), "dq_nope rows");
+  MLA_HIP(launch_permute_heads(dt, false, dqh, dqk, dn, gq, lgq, H * dn, dr, B, S, H, st), "dq_pe rows");
+  MLA_HIP(launch_permute_heads(dt, false, dkh, dqk, 0, gkv, lgkv, 0, dn, B, S, H, st), "dk_nope rows");
+  MLA_HIP(launch_permute_heads(dt, false, dvh, dv, 0, gkv, lgkv, H * dn, dv, B, S, H, st), "dv rows");
+  // the up-projection weights stacked along their output rows
+  MLA_HIP(launch_copy_rows(dt, wq, rq, w->w_up_q, rq, (int64_t)H * dn, rq, st), "stack w_up_q");
+  MLA_HIP(launch_copy_rows(dt, wq + (size_t)H * dn * rq * es, rq, w->w_qr, rq, (int64_t)H * dr, rq, st), "stack w_qr");
+  MLA_HIP(launch_copy_rows(dt, wkv, rkv, w->w_up_k, rkv, (int64_t)H * dn, rkv, st), "stack w_up_k");
+  MLA_HIP(launch_copy_rows(dt, wkv + (size_t)H * dn * rkv * es, rkv, w->w_up_v, rkv, (int64_t)H * dv, rkv, st),
+          "stack w_up_v");
+  MLA_HIP(launch_copy_rows(dt, wd, D, w->w_down_q, D, rq, D, st), "stack w_down_q");
+  MLA_HIP(launch_copy_rows(dt, wd + (size_t)rq * D * es, D, w->w_down_kv, D, rkv, D, st), "stack w_down_kv");
+  MLA_HIP(launch_copy_rows(dt, wd + (size_t)(rq + rkv) * D * es, D, w->w_kr, D, dr, D, st), "stack w_kr");
+  // q side: dW_uq, dW_qr, dc_qn
+  MLA_HIP(plain_gemm(dt, gq, lgq, true, down, ld, true, grads->w_up_q, rq, H * dn, rq, M, st), "dw_up_q");
+  MLA_HIP(plain_gemm(dt, gq + (size_t)H * dn * es, lgq, true, down, ld, true, grads->w_qr, rq, H * dr, rq, M, st),
+          "dw_qr");
+  MLA_HIP(plain_gemm(dt, gq, lgq, false, wq, rq, true, dcqn, rq, M, rq, H * dqk, st), "dc_q");
+  // kv side: dW_uk, dW_uv, dc_kv
+  MLA_HIP(plain_gemm(dt, gkv, lgkv, true, down + (size_t)rq * es, ld, true, grads->w_up_k, rkv, H * dn, rkv, M, st),
+          "dw_up_k");
+  MLA_HIP(plain_gemm(dt, gkv + (size_t)H * dn * es, lgkv, true, down + (size_t)rq * es, ld, true, grads->w_up_v, rkv,
+                     H * dv, rkv, M, st),
+          "dw_up_v");
+  MLA_HIP(plain_gemm(dt, gkv, lgkv, false, wkv, rkv, true, dckv, rkv, M, rkv, H * (dn + dv), st), "dc_kv");
+  // norms: dc_q (and dc_kv) into ddown's columns, the gains' gradients in fp32
+  if (w->kv_norm) {
+    MLA_HIP(launch_rmsnorm_backward(dt, ckv_raw, rkv, dckv, rkv, w->kv_norm, M, rkv, c.rms_norm_eps,
+                                    ddown + (size_t)rq * es, ld, grads->kv_norm, rms, st),
+            "kv norm backward");
+  } else {
+    MLA_HIP(launch_copy_rows(dt, ddown + (size_t)rq * es, ld, dckv, rkv, M, rkv, st), "dc_kv copy");
+  }
+  MLA_HIP(launch_rmsnorm_backward(dt, cq_raw, rq, dcqn, rq, w->q_norm, M, rq, c.rms_norm_eps, ddown, ld,
+                                  grads->q_norm, rms, st),
+          "q norm backward");
+  // down projections: dx and the three weights
+  MLA_HIP(plain_gemm(dt, ddown, ld, false, wd, D, true, dx, D, M, D, rq + rkv + dr, st), "dx");
+  MLA_HIP(plain_gemm(dt, ddown, ld, true, x, D, true, grads->w_down_q, D, rq, D, M, st), "dw_down_q");
+  MLA_HIP(plain_gemm(dt, ddown + (size_t)rq * es, ld, true, x, D, true, grads->w_down_kv, D, rkv, D, M, st),
+          "dw_down_kv");
+  MLA_HIP(plain_gemm(dt, ddown + (size_t)(rq + rkv) * es, ld, true, x, D, true, grads->w_kr, D, dr, D, M, st),
+          "dw_kr");
+  return MLA_OK;
+}
+
 // ---------------------------------------------------------------- FP8 prefill
 // The prefill with its four projection products on block-scaled FP8 (E4M3
 // codes, power-of-two scale per 1 x 128 activation tile and 128 x 128

@@ -71,6 +71,11 @@ class Fp8Weights(ctypes.Structure):
     _fields_ = [(n, Fp8Matrix) for n in ("down", "q_up", "kv_up", "out")]
 
 
+class WeightGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_down_q", "q_norm", "w_up_q", "w_qr", "w_down_kv", "kv_norm", "w_kr", "w_up_k", "w_up_v", "wo")]
+
+
 class PrefillLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("c_q", "c_kv", "k_pe", "q", "k_nope", "v", "o")] + [
         ("ld_down", ctypes.c_int64), ("total", ctypes.c_size_t)]
@@ -142,6 +147,11 @@ def load_library(path: str = LIB_PATH):
     lib.mla_rmsnorm_backward.restype = st
     lib.mla_rmsnorm_backward_workspace_size.argtypes = [i64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_rmsnorm_backward_workspace_size.restype = st
+    lib.mla_backward_workspace_size.argtypes = [ctypes.POINTER(Config), i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_backward.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P, i64, i64, P, P,
+                                 ctypes.POINTER(WeightGrads), P, ctypes.c_size_t, P]
+    lib.mla_backward_workspace_size.restype = st
+    lib.mla_backward.restype = st
     lib.mla_fp8_weights_size.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_fp8_prepare_weights.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), P, ctypes.c_size_t,
                                             ctypes.POINTER(Fp8Weights), P]
@@ -450,6 +460,42 @@ def mla_prefill_chunk(cfg: MlaConfig, weights: dict, x: torch.Tensor, latent_cac
         max_keys, _ptr(y), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return y, workspace
+
+
+def mla_backward_workspace_size(cfg: MlaConfig, batch: int, seq: int) -> int:
+    n = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().mla_backward_workspace_size(ctypes.byref(c), batch, seq, ctypes.byref(n)))
+    return n.value
+
+
+def mla_backward(cfg: MlaConfig, weights: dict, x: torch.Tensor, dy: torch.Tensor, workspace=None,
+                 stream=None):
+    """Gradients of <dy, MLA(x)>: returns (dx, grads) with grads[name] shaped
+    like weights[name] (cfg dtype; the RMSNorm gains' gradients fp32)."""
+    B, S, D = x.shape
+    if dy.shape != x.shape:
+        raise ValueError(f"dy {tuple(dy.shape)} must have x's shape {tuple(x.shape)}")
+    dev = x.device
+    need = mla_backward_workspace_size(cfg, B, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _device_check(x, dy, workspace)
+    grads = {}
+    for n in WEIGHT_NAMES:
+        t = weights.get(n)
+        if t is None:
+            continue
+        grads[n] = torch.empty(t.shape, dtype=torch.float32 if n in ("q_norm", "kv_norm") else cfg.torch_dtype,
+                               device=dev)
+    dx = torch.empty_like(x)
+    g = WeightGrads(*[grads[n].data_ptr() if n in grads else None for n in WEIGHT_NAMES])
+    w = make_weights(weights)
+    c = cfg.c()
+    _check(load_library().mla_backward(ctypes.byref(c), ctypes.byref(w), _ptr(x), B, S, _ptr(dy), _ptr(dx),
+                                       ctypes.byref(g), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dx, grads
 
 
 def mla_attention_backward(q, k, v, o, dout, scale: float, workspace=None, stream=None):

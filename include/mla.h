@@ -467,6 +467,47 @@ MLA_API mla_status mla_rmsnorm_backward(int32_t dtype, const void *x, const void
                                 int64_t rows, int32_t n, float eps, void *dx, float *dg,
                                 void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* ------------------------------------------------------------ MLA backward
+ * Every gradient of the prefill y = MLA(x) (the training half of the pages:
+ * the forward of "The Evolving Transformer -- DeepSeek V2 & V3", section 01,
+ * whose gradients the "DSV3 Native PyTorch Reference" README checks by
+ * finite differences) for an upstream gradient dy: the chain rule back
+ * through the output projection, the causal attention (per head, as
+ * mla_attention_backward), the RoPE rotations (the rotation at negated
+ * positions), the shared RoPE key (its gradient summed over heads in a fixed
+ * order), the up-projections, the RMSNorms and the down-projections.  The
+ * forward's intermediates are recomputed into the workspace first.
+ *   x, dy      [B, S, D]   device, read
+ *   dx         [B, S, D]   device, written
+ *   grads      host struct of device pointers, written: each weight's
+ *              gradient in cfg->dtype, shaped like the weight ([out][in]);
+ *              the RMSNorm gains' gradients in fp32 (kv_norm only when
+ *              w->kv_norm is not NULL; it may be NULL otherwise)
+ * Weight gradients are sums over all B * S tokens.  Deterministic: every
+ * sum runs in a fixed order.  Asynchronous on hip_stream; the caller owns
+ * every buffer.
+ * Status: as mla_prefill_forward; INVALID_ARGUMENT also for NULL or
+ * misaligned dy, dx or gradients, or B * S * num_heads >= 2^31. */
+typedef struct {
+  void *w_down_q;                 /* [r_q, D]                                  */
+  float *q_norm;                  /* [r_q]  fp32                               */
+  void *w_up_q;                   /* [H*d_n, r_q]                              */
+  void *w_qr;                     /* [H*d_r, r_q]                              */
+  void *w_down_kv;                /* [r_kv, D]                                 */
+  float *kv_norm;                 /* [r_kv] fp32, or NULL without kv_norm      */
+  void *w_kr;                     /* [d_r, D]                                  */
+  void *w_up_k;                   /* [H*d_n, r_kv]                             */
+  void *w_up_v;                   /* [H*d_v, r_kv]                             */
+  void *wo;                       /* [D, H*d_v]                                */
+} mla_weight_grads;
+
+MLA_API mla_status mla_backward_workspace_size(const mla_config *cfg, int64_t batch, int64_t seq,
+                                       size_t *bytes);
+MLA_API mla_status mla_backward(const mla_config *cfg, const mla_weights *w, const void *x,
+                        int64_t batch, int64_t seq, const void *dy, void *dx,
+                        const mla_weight_grads *grads, void *workspace, size_t workspace_bytes,
+                        void *hip_stream);
+
 /* ---------------------------------------------------------- measurement
  * While set, every mla_prefill_forward / mla_decode_absorbed call made on
  * this thread records events[k] (hipEvent_t handles the caller created) on

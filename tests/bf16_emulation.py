@@ -191,3 +191,86 @@ def prefill_fp8_bf16_rows(cfg: orc.Cfg, w: dict, x, rows, batch: int = 0):
         q = np.concatenate([q_nope[:, h], q_pe[:, h]], axis=-1)
         o[:, h] = _attention_bf16_p(q, k, v, scale, _r, q_pos=rows)
     return _r(fo.quantized_product(_r(o).reshape(len(rows), H * dv), f["wo"]))
+
+
+def mla_backward_bf16(cfg: orc.Cfg, w: dict, x, dy, rounding: bool = True):
+    """The MLA backward oracle's chain rule (oracle.mla_backward_oracle) with
+    bf16 storage wherever the HIP path stores bf16: the forward intermediates
+    (c_q before and after its norm, c_kv, k_pe, q, k_nope, v, o), do, the
+    attention backward's dq / dk / dv, the shared key's summed gradient and
+    both RoPE backwards, dc_qn, dc_kv, dc_q, and every output (dx and the
+    weight gradients; the gains' gradients stay fp32).  Sums run exactly."""
+    from oracle.attn_backward_oracle import causal_attention_backward, rmsnorm_backward
+    from oracle.mla_backward_oracle import rope_backward
+    _r = _round if rounding else _keep
+    x, dy = np.asarray(x, dtype=np.float64), np.asarray(dy, dtype=np.float64)
+    B, S, D = x.shape
+    H = cfg.num_attention_heads
+    dn, dr, dv = cfg.qk_nope_head_dim, cfg.qk_rope_head_dim, cfg.v_head_dim
+    f = {k: np.asarray(v, dtype=np.float64) for k, v in w.items() if v is not None}
+    eps = cfg.rms_norm_eps
+    pos = np.arange(S)
+    M = B * S
+    xf = x.reshape(M, D)
+    c_q = _r(xf @ f["w_down_q"].T)
+    c_qn = _r(orc.rmsnorm(c_q, f["q_norm"], eps))
+    c_kv_raw = _r(xf @ f["w_down_kv"].T)
+    c_kv = _r(orc.rmsnorm(c_kv_raw, f["kv_norm"], eps)) if "kv_norm" in f else c_kv_raw
+    k_pe = _r(np.stack([orc.apply_rope(_r(xf @ f["w_kr"].T).reshape(B, S, dr)[b], pos, cfg) for b in range(B)]))
+    q_nope = _r(c_qn @ f["w_up_q"].T).reshape(B, S, H, dn)
+    q_pe = _r(np.stack([orc.apply_rope(_r(c_qn @ f["w_qr"].T).reshape(B, S, H, dr)[b], pos, cfg)
+                        for b in range(B)]))
+    k_nope = _r(c_kv @ f["w_up_k"].T).reshape(B, S, H, dn)
+    v = _r(c_kv @ f["w_up_v"].T).reshape(B, S, H, dv)
+    scale = orc.softmax_scale(cfg)
+    o = np.empty((B, S, H, dv))
+    qh = np.empty((B, H, S, dn + dr))
+    kh = np.empty((B, H, S, dn + dr))
+    for b in range(B):
+        for h in range(H):
+            qh[b, h] = np.concatenate([q_nope[b, :, h], q_pe[b, :, h]], axis=-1)
+            kh[b, h] = np.concatenate([k_nope[b, :, h], k_pe[b]], axis=-1)
+            o[b, :, h] = _attention_bf16_p(qh[b, h], kh[b, h], v[b, :, h], scale, _r)
+    of = _r(o).reshape(M, H * dv)
+    g = {}
+    dyf = dy.reshape(M, D)
+    g["wo"] = _r(dyf.T @ of)
+    do = _r(dyf @ f["wo"]).reshape(B, S, H, dv)
+    dq_nope = np.empty((B, S, H, dn))
+    dq_pe = np.empty((B, S, H, dr))
+    dk_nope = np.empty((B, S, H, dn))
+    dk_pe = np.zeros((B, S, dr))
+    dvv = np.empty((B, S, H, dv))
+    for b in range(B):
+        for h in range(H):
+            dqh, dkh, dvh = (_r(t) for t in causal_attention_backward(qh[b, h], kh[b, h], v[b, :, h],
+                                                                      do[b, :, h], scale,
+                                                                      o=of.reshape(B, S, H, dv)[b, :, h]))
+            dq_nope[b, :, h], dq_pe[b, :, h] = dqh[:, :dn], dqh[:, dn:]
+            dk_nope[b, :, h] = dkh[:, :dn]
+            dk_pe[b] += dkh[:, dn:]
+            dvv[b, :, h] = dvh
+    dk_pe = _r(dk_pe)
+    dq_pe_raw = _r(np.stack([rope_backward(dq_pe[b], pos, cfg) for b in range(B)])).reshape(M, H * dr)
+    dk_pe_raw = _r(np.stack([rope_backward(dk_pe[b], pos, cfg) for b in range(B)])).reshape(M, dr)
+    dq_nope = dq_nope.reshape(M, H * dn)
+    dk_nope = dk_nope.reshape(M, H * dn)
+    dvv = dvv.reshape(M, H * dv)
+    g["w_up_q"] = _r(dq_nope.T @ c_qn)
+    g["w_qr"] = _r(dq_pe_raw.T @ c_qn)
+    dc_qn = _r(dq_nope @ f["w_up_q"] + dq_pe_raw @ f["w_qr"])
+    g["w_up_k"] = _r(dk_nope.T @ c_kv)
+    g["w_up_v"] = _r(dvv.T @ c_kv)
+    dc_kv = _r(dk_nope @ f["w_up_k"] + dvv @ f["w_up_v"])
+    if "kv_norm" in f:
+        dc_kv_raw, g["kv_norm"] = rmsnorm_backward(c_kv_raw, f["kv_norm"], dc_kv, eps)
+        dc_kv_raw = _r(dc_kv_raw)
+    else:
+        dc_kv_raw = dc_kv
+    dc_q, g["q_norm"] = rmsnorm_backward(c_q, f["q_norm"], dc_qn, eps)
+    dc_q = _r(dc_q)
+    g["w_down_q"] = _r(dc_q.T @ xf)
+    g["w_down_kv"] = _r(dc_kv_raw.T @ xf)
+    g["w_kr"] = _r(dk_pe_raw.T @ xf)
+    dx = _r(dc_q @ f["w_down_q"] + dc_kv_raw @ f["w_down_kv"] + dk_pe_raw @ f["w_kr"])
+    return dx.reshape(B, S, D), g

@@ -54,3 +54,20 @@ def test_decode_score_range_exceeds_strict_bound_under_the_model():
                          orc.mla_decode_absorbed(cfg, w, x, cache, lens)[0])
     assert ab.max() > 3e-2, ab.max()
     assert be.bound(2e-2, rel.max()) < 3e-2 and be.bound(3e-2, ab.max()) < 1e-1
+
+
+def test_backward_model_without_rounding_is_the_oracle():
+    from oracle.mla_backward_oracle import mla_backward
+    c = si.CONFIGS["small"]
+    x, w = si.make_inputs(c, seq=20, batch=2, gains="random")
+    dy = np.random.default_rng(5).standard_normal(x.shape)
+    cfg = oracle_cfg(c, rope="interleaved")
+    rdx, rg = mla_backward(cfg, w, x, dy)
+    mdx, mg = be.mla_backward_bf16(cfg, w, x, dy, rounding=False)
+    np.testing.assert_allclose(mdx, rdx, rtol=1e-12, atol=1e-12)
+    for k in rg:
+        np.testing.assert_allclose(mg[k], rg[k], rtol=1e-12, atol=1e-12, err_msg=k)
+    # with bf16 storage the weight gradients move by about the strict bound
+    mdx, mg = be.mla_backward_bf16(cfg, w, x, dy)
+    _, ab = row_errors(mg["w_up_q"], rg["w_up_q"])
+    assert 3e-3 < ab.max() < 1e-1, ab.max()
