@@ -378,7 +378,7 @@ def attention_backward_line(m, S, log, reps=2):
     torch.cuda.empty_cache()
     return {"heads": H, "seq_len": S, "d_qk": dqk, "d_v": dv, "dtype": "bf16", "ms": ms,
             "gflop": fl / 1e9, "tflops": tf, "frac_of_bf16_peak": tf / MI355X_BF16_TFLOPS,
-            "note": "vector-ALU kernels (no MFMA yet)",
+            "note": "bf16 32x32x16 MFMA kernels: row statistics, dK/dV per key block, dQ per query block (no atomics)",
             "mla_backward_ms": full_ms,
             "mla_backward_note": "mla_backward at V3 sizes, B=1: forward recomputed, dx and every weight gradient"}
 

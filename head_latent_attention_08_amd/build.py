@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["gemm.hip", "gemm_fp8.hip", "elementwise.hip", "attn_prefill.hip", "attn_backward.hip", "mla_backward.hip", "decode.hip", "mla_api.hip"]
+SOURCES = ["gemm.hip", "gemm_fp8.hip", "elementwise.hip", "attn_prefill.hip", "attn_backward.hip", "attn_backward_mfma.hip", "mla_backward.hip", "decode.hip", "mla_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

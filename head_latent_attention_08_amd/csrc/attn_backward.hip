@@ -394,6 +394,7 @@ hipError_t launch_rmsnorm_backward(int dtype, const void *x, int64_t ldx, const 
 
 hipError_t launch_attention_backward(int dtype, const AttnBwdArgs &a, hipStream_t st) {
   if ((int64_t)a.BH * a.S == 0) return hipSuccess;
+  if (attention_backward_mfma_supported(dtype, a.dqk, a.dv)) return launch_attention_backward_mfma(a, st);
   return dtype == BF16 ? launch_t<bf16>(a, st) : launch_t<float>(a, st);
 }
 

@@ -127,7 +127,6 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
                 NCT = C::NCT;
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGEB];
   __shared__ __attribute__((aligned(16))) T Qs[NQL > 0 ? HPB * QPITCH : VEC];
-  extern __shared__ int starts[];  // [B + 1]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
@@ -147,38 +146,37 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
   const int h = hg * HPB + wave * HPW + l32;
   const bool wave_live = hg * HPB + wave * HPW < H;
 
-  // prefix sums of per-sequence row counts
-  for (int b = tid; b < B; b += DTHREADS) starts[b + 1] = seq_vrows(a.lens, b, a.cap, a.q_len);
-  __syncthreads();
-  if (wave == 0) {
-    int carry = 0;
-    for (int c0 = 0; c0 < B; c0 += 64) {
-      const int b = c0 + lane;
-      int v = b < B ? starts[b + 1] : 0;
+  // The virtual rows (seq_vrows) of the sequences laid end to end: the
+  // total, cut into n_blocks equal ranges, and the first sequence holding
+  // row r0 with the row it starts at.  Every wave works these out by itself
+  // (64 sequences per step, an in-register prefix sum), so no LDS and no
+  // barrier depend on the batch size.
+  int total = 0;
+  for (int b0 = lane; b0 < B; b0 += 64) total += seq_vrows(a.lens, b0, a.cap, a.q_len);
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(v, o);
-        if (lane >= o) v += u;
-      }
-      if (b < B) starts[b + 1] = carry + v;
-      carry += __shfl(v, 63);
-    }
-    if (lane == 0) starts[0] = 0;
-  }
-  __syncthreads();
-  const int total = starts[B];
+  for (int o = 32; o >= 1; o >>= 1) total += __shfl_xor(total, o);
+  total = __builtin_amdgcn_readfirstlane(total);  // the same in every lane
   const int per = (total + a.n_blocks - 1) / a.n_blocks;
   int r0 = blk * per;
   const int r1 = min(r0 + per, total);
   if (r0 >= r1) return;
-  // first sequence holding row r0: the number of sequences ending at or
-  // before it (row-count prefix sums are non-decreasing), one ballot per 64
-  int b = 0;
+  int b = 0, sb = 0;  // sequence b starts at virtual row sb
   for (int c0 = 0; c0 < B; c0 += 64) {
     const int i = c0 + lane;
-    const int n = __popcll(__ballot(i < B && starts[i + 1] <= r0));
-    b += n;
-    if (n < 64) break;
+    int v = i < B ? seq_vrows(a.lens, i, a.cap, a.q_len) : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    const int ends = sb + v;  // end of sequence i
+    const int n = __popcll(__ballot(i < B && ends <= r0));
+    b = c0 + n;
+    if (n < 64) {
+      if (n > 0) sb = __builtin_amdgcn_readlane(ends, n - 1);
+      break;
+    }
+    sb = __builtin_amdgcn_readlane(ends, 63);
   }
 
   const float sl2 = a.scale * LOG2E;
@@ -217,11 +215,12 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
 
   while (r0 < r1 && b < B) {
     // sequence b's real rows sit at [rs, re) of the virtual row axis
-    const int re = starts[b + 1];
-    const int rs = re > starts[b] ? starts[b] + PIECE_COST_ROWS : re;
+    const int re = sb + seq_vrows(a.lens, b, a.cap, a.q_len);
+    const int rs = re > sb ? sb + PIECE_COST_ROWS : re;
     const int pb = max(r0, rs), pe = min(r1, re);
     if (pb >= pe) {  // only virtual rows of b in this range (uniform)
       r0 = re;
+      sb = re;
       ++b;
       continue;
     }
@@ -514,6 +513,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
       }
     }
     r0 = re;
+    sb = re;
     ++b;
   }
 #undef DEC_DMA
@@ -707,8 +707,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16 *qn, int64_t ldq
 template <typename T, int R, int DR>
 hipError_t launch_t(const DecodeAttnArgs &a, hipStream_t st) {
   dim3 grid(a.n_blocks * ((a.H + HPB - 1) / HPB));
-  size_t shm = (size_t)(a.B + 1) * sizeof(int);
-  hipLaunchKernelGGL((decode_attn_kernel<T, R, DR>), grid, dim3(DTHREADS), shm, st, a);
+  hipLaunchKernelGGL((decode_attn_kernel<T, R, DR>), grid, dim3(DTHREADS), 0, st, a);
   return hipGetLastError();
 }
 

@@ -130,6 +130,10 @@ struct AttnBwdArgs {
   float scale;
 };
 hipError_t launch_attention_backward(int dtype, const AttnBwdArgs &a, hipStream_t st);
+// The same on the matrix cores (bf16; d_qk, d_v one of 192/128, 96/64,
+// 64/64); launch_attention_backward takes it where it applies.
+bool attention_backward_mfma_supported(int dtype, int dqk, int dv);
+hipError_t launch_attention_backward_mfma(const AttnBwdArgs &a, hipStream_t st);
 // RMSNorm backward over rows of x [rows, n] (row pitches ldx, ldy, lddx):
 // dx like x, dg fp32 [n] summed in a fixed order; scratch holds
 // rmsnorm_backward_scratch_floats(rows, n) floats.

@@ -137,6 +137,15 @@ def test_bad_sizes_rejected():
         with pytest.raises(m.MlaError) as e:
             m.mla_decode_multi_workspace_size(cfg, 4, T, cap)
         assert e.value.status == b.MLA_ERR_INVALID_ARGUMENT
+    # the batch limit of both decode entries is 4096 sequences (the decode
+    # attention's LDS no longer depends on the batch)
+    assert m.mla_decode_workspace_size(cfg, 4096, 41) > 0
+    assert m.mla_decode_multi_workspace_size(cfg, 4096, 2, 41) > 0
+    for fn in (lambda: m.mla_decode_workspace_size(cfg, 4097, 41),
+               lambda: m.mla_decode_multi_workspace_size(cfg, 4097, 2, 41)):
+        with pytest.raises(m.MlaError) as e:
+            fn()
+        assert e.value.status == b.MLA_ERR_INVALID_ARGUMENT
     # q_len = 1 needs what the single-token call needs; more tokens need more
     one = m.mla_decode_multi_workspace_size(cfg, 64, 1, 8193)
     assert one == m.mla_decode_workspace_size(cfg, 64, 8193)

@@ -247,6 +247,29 @@ def test_v3_decode_full():
     assert_close_rows(got_rows, new_rows, "bf16", "new cache rows")
 
 
+def test_v3_decode_batch_4096_sampled():
+    # the largest batch the decode entry takes, with short histories (0..40
+    # rows): each row range holds many sequences; sampled sequences (and the
+    # ends of the batch) against the oracle, with their new cache rows
+    m = _m()
+    c = si.CONFIGS["v3_decode"]
+    B, cap = 4096, 41
+    print(f"v3 decode: B={B} cap={cap} lens U{{0..40}}, seed 4200", flush=True)
+    x, w, lens, cache = si.make_decode_inputs(c, batch=B, capacity=cap, len_lo=0, len_hi=40, seed=4200)
+    cfg = mla_cfg(c)
+    cache_d = to_dev(cache, "bf16")
+    y, _ = m.mla_decode_absorbed(cfg, weights_to_dev(w, "bf16"), to_dev(x, "bf16"), cache_d,
+                                 torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4201)
+    pick = np.unique(np.concatenate([[0, 1, 2494, 2495, 2496, B - 1], rng.choice(B, 40, replace=False)]))
+    ref, new_rows = orc.mla_decode_absorbed(oracle_cfg(c), w, x[pick], cache[pick], lens[pick])
+    assert_close_rows(to_np(y)[pick], ref, "bf16", "y")
+    sel = torch.from_numpy(pick).cuda()
+    got_rows = to_np(cache_d[sel, torch.from_numpy(lens[pick].astype(np.int64)).cuda()])
+    assert_close_rows(got_rows, new_rows, "bf16", "new cache rows")
+
+
 def test_v3_decode_expanded_spot_check():
     # the expanded definition (per-head K/V up-projection of every cached
     # row) on a few sequences agrees with the GPU's absorbed result
