@@ -757,6 +757,11 @@ static hipError_t launch_big(const GemmParams &p, const GemmDesc &d, int n_lo, i
   return hipGetLastError();
 }
 
+bool gemm_takes_large_tiles(int dtype, int M, int N, int K) {
+  return dtype == BF16 && K % GB_K == 0 && M >= 512 && N % 8 == 0 && (int64_t)M * K < (1LL << 31) &&
+         (int64_t)N * K < (1LL << 31);
+}
+
 hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   if (d.M <= 0 || d.N <= 0 || d.K <= 0 || d.batch <= 0) return hipSuccess;
   GemmParams p;

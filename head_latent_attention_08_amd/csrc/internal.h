@@ -48,6 +48,10 @@ struct GemmDesc {
 };
 
 hipError_t launch_gemm(const GemmDesc &d, hipStream_t st);
+// Whether launch_gemm runs a product of these sizes on the large-tile bf16
+// kernel when both operands are K-contiguous (single batch, one column range
+// starting at 0, ldb = K).
+bool gemm_takes_large_tiles(int dtype, int M, int N, int K);
 
 // Scratch bytes launch_gemm can use for split-K partials of an M x N x K
 // product (0 when it never splits).
@@ -154,6 +158,9 @@ hipError_t launch_build_keys(int dtype, const void *kn, const void *kpe, int64_t
 // dst[(b S + s) ldd + c] = sum over h in order of src[((b H + h) S + s) sp + scol + c], c < w
 hipError_t launch_head_sum(int dtype, const void *src, int64_t sp, int scol, void *dst, int64_t ldd, int w, int B,
                            int S, int H, hipStream_t st);
+// dst[c ldd + r] = src[r lds + c] for r < R, c < C (bf16; R, C, lds, ldd
+// multiples of 8, pointers 16-byte aligned)
+hipError_t launch_transpose(const void *src, int64_t lds, int R, int C, void *dst, int64_t ldd, hipStream_t st);
 // pos[t] = -(t % S)
 hipError_t launch_neg_positions(int32_t *pos, int64_t n, int S, hipStream_t st);
 

@@ -522,8 +522,18 @@ namespace {
 struct BackwardPlan {
   PrefillPlan fwd;
   size_t off_cq_raw, off_ckv_raw, off_vh, off_kh, off_oh, off_doh, off_dqh, off_dkh, off_dvh, off_att,
-      off_pos, off_gq, off_gkv, off_dcqn, off_dckv, off_ddown, off_wq, off_wkv, off_wd, off_rms, total;
+      off_pos, off_gq, off_gkv, off_dcqn, off_dckv, off_ddown, off_wq, off_wkv, off_wd, off_rms, off_tr, total;
 };
+
+// Elements of transposed operand copies a backward product C [M, N] =
+// op(A) op(B) (contraction K) needs: bf16 products the large-tile kernel
+// takes get their transposed operands (A stored [K][M], B stored [K][N])
+// rewritten K-contiguous, an HBM-bound pass that the general kernel's
+// strided reads of the same operands cost many times over.
+size_t bwd_tr_elems(int dtype, int64_t M, int64_t N, int64_t K, bool a_km, bool b_kn) {
+  if (!(a_km || b_kn) || M % 8 || N % 8 || !gemm_takes_large_tiles(dtype, (int)M, (int)N, (int)K)) return 0;
+  return (a_km ? round_up((size_t)(M * K), 128) : 0) + (b_kn ? (size_t)(N * K) : 0);
+}
 
 BackwardPlan plan_backward(const mla_config &c, int64_t B, int64_t S) {
   BackwardPlan p;
@@ -559,6 +569,16 @@ BackwardPlan plan_backward(const mla_config &c, int64_t B, int64_t S) {
   p.off_wd = take((size_t)(rq + rkv + dr) * D * es);
   p.off_rms = take(std::max(rmsnorm_backward_scratch_floats(M, (int)rq), rmsnorm_backward_scratch_floats(M, (int)rkv)) *
                    sizeof(float));
+  // the largest transposed-operand need over the backward's products
+  const int dt = c.dtype;
+  const size_t tr = std::max({bwd_tr_elems(dt, D, H * dv, M, true, true), bwd_tr_elems(dt, M, H * dv, D, false, true),
+                              bwd_tr_elems(dt, H * dn, rq, M, true, true), bwd_tr_elems(dt, H * dr, rq, M, true, true),
+                              bwd_tr_elems(dt, M, rq, H * (dn + dr), false, true),
+                              bwd_tr_elems(dt, H * dn, rkv, M, true, true), bwd_tr_elems(dt, H * dv, rkv, M, true, true),
+                              bwd_tr_elems(dt, M, rkv, H * (dn + dv), false, true),
+                              bwd_tr_elems(dt, M, D, rq + rkv + dr, false, true), bwd_tr_elems(dt, rq, D, M, true, true),
+                              bwd_tr_elems(dt, rkv, D, M, true, true), bwd_tr_elems(dt, dr, D, M, true, true)});
+  p.off_tr = take(tr * es);
   p.total = off;
   return p;
 }
@@ -581,6 +601,30 @@ hipError_t plain_gemm(int dtype, const void *A, int64_t lda, bool a_km, const vo
   g.nseg = 1;
   g.seg[0] = GemmSeg{B, ldb, 0, C, N, ldc, 0};
   return launch_gemm(g, st);
+}
+
+// plain_gemm for the backward's products, with the transposed operands of
+// those bwd_tr_elems names rewritten K-contiguous into tr first.
+hipError_t bwd_gemm(int dtype, const void *A, int64_t lda, bool a_km, const void *B, int64_t ldb, bool b_kn, void *C,
+                    int64_t ldc, int M, int N, int K, char *tr, hipStream_t st) {
+  if (bwd_tr_elems(dtype, M, N, K, a_km, b_kn) > 0) {
+    char *t = tr;
+    if (a_km) {
+      hipError_t e = launch_transpose(A, lda, K, M, t, K, st);
+      if (e != hipSuccess) return e;
+      A = t;
+      lda = K;
+      t += round_up((size_t)M * K, 128) * 2;  // bf16
+    }
+    if (b_kn) {
+      hipError_t e = launch_transpose(B, ldb, K, N, t, K, st);
+      if (e != hipSuccess) return e;
+      B = t;
+      ldb = K;
+    }
+    a_km = b_kn = false;
+  }
+  return plain_gemm(dtype, A, lda, a_km, B, ldb, b_kn, C, ldc, M, N, K, st);
 }
 
 }  // namespace
@@ -636,6 +680,7 @@ mla_status mla_backward(const mla_config *cfg, const mla_weights *w, const void 
        *ddown = at(p.off_ddown), *wq = at(p.off_wq), *wkv = at(p.off_wkv), *wd = at(p.off_wd);
   int32_t *pos_neg = reinterpret_cast<int32_t *>(at(p.off_pos));
   float *rms = reinterpret_cast<float *>(at(p.off_rms));
+  char *tr = at(p.off_tr);
   const int B = (int)batch, S = (int)seq, M = B * S, H = c.num_heads;
   const int D = c.hidden_size, rq = c.q_lora_rank, rkv = c.kv_lora_rank;
   const int dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim, dv = c.v_head_dim, dqk = dn + dr;
@@ -721,7 +766,7 @@ mla_status mla_backward(const mla_config *cfg, const mla_weights *w, const void 
 
   // ---- backward
   // y = o wo^T: dwo = dy^T o, do = dy wo (per head)
-  MLA_HIP(plain_gemm(dt, dy, D, true, o, (int64_t)H * dv, true, grads->wo, (int64_t)H * dv, D, H * dv, M, st),
+  MLA_HIP(bwd_gemm(dt, dy, D, true, o, (int64_t)H * dv, true, grads->wo, (int64_t)H * dv, D, H * dv, M, tr, st),
           "dwo");
   {
     GemmDesc g;
@@ -736,6 +781,11 @@ mla_status mla_backward(const mla_config *cfg, const mla_weights *w, const void 
     g.H = H;
     g.nseg = 1;
     g.seg[0] = GemmSeg{w->wo, (int64_t)H * dv, 0, doh, dv, dv, 0};
+    if (bwd_tr_elems(dt, M, H * dv, D, false, true) > 0) {  // wo^T, K-contiguous
+      MLA_HIP(launch_transpose(w->wo, (int64_t)H * dv, D, H * dv, tr, D, st), "wo transpose");
+      g.b_kn = false;
+      g.seg[0] = GemmSeg{tr, D, 0, doh, dv, dv, 0};
+    }
     MLA_HIP(launch_gemm(g, st), "do");
   }
   // attention backward per head on K = [k_nope ‖ k_pe] and the stored o
@@ -785,17 +835,17 @@ mla_status mla_backward(const mla_config *cfg, const mla_weights *w, const void 
   MLA_HIP(launch_copy_rows(dt, wd + (size_t)rq * D * es, D, w->w_down_kv, D, rkv, D, st), "stack w_down_kv");
   MLA_HIP(launch_copy_rows(dt, wd + (size_t)(rq + rkv) * D * es, D, w->w_kr, D, dr, D, st), "stack w_kr");
   // q side: dW_uq, dW_qr, dc_qn
-  MLA_HIP(plain_gemm(dt, gq, lgq, true, down, ld, true, grads->w_up_q, rq, H * dn, rq, M, st), "dw_up_q");
-  MLA_HIP(plain_gemm(dt, gq + (size_t)H * dn * es, lgq, true, down, ld, true, grads->w_qr, rq, H * dr, rq, M, st),
+  MLA_HIP(bwd_gemm(dt, gq, lgq, true, down, ld, true, grads->w_up_q, rq, H * dn, rq, M, tr, st), "dw_up_q");
+  MLA_HIP(bwd_gemm(dt, gq + (size_t)H * dn * es, lgq, true, down, ld, true, grads->w_qr, rq, H * dr, rq, M, tr, st),
           "dw_qr");
-  MLA_HIP(plain_gemm(dt, gq, lgq, false, wq, rq, true, dcqn, rq, M, rq, H * dqk, st), "dc_q");
+  MLA_HIP(bwd_gemm(dt, gq, lgq, false, wq, rq, true, dcqn, rq, M, rq, H * dqk, tr, st), "dc_q");
   // kv side: dW_uk, dW_uv, dc_kv
-  MLA_HIP(plain_gemm(dt, gkv, lgkv, true, down + (size_t)rq * es, ld, true, grads->w_up_k, rkv, H * dn, rkv, M, st),
+  MLA_HIP(bwd_gemm(dt, gkv, lgkv, true, down + (size_t)rq * es, ld, true, grads->w_up_k, rkv, H * dn, rkv, M, tr, st),
           "dw_up_k");
-  MLA_HIP(plain_gemm(dt, gkv + (size_t)H * dn * es, lgkv, true, down + (size_t)rq * es, ld, true, grads->w_up_v, rkv,
-                     H * dv, rkv, M, st),
+  MLA_HIP(bwd_gemm(dt, gkv + (size_t)H * dn * es, lgkv, true, down + (size_t)rq * es, ld, true, grads->w_up_v, rkv,
+                     H * dv, rkv, M, tr, st),
           "dw_up_v");
-  MLA_HIP(plain_gemm(dt, gkv, lgkv, false, wkv, rkv, true, dckv, rkv, M, rkv, H * (dn + dv), st), "dc_kv");
+  MLA_HIP(bwd_gemm(dt, gkv, lgkv, false, wkv, rkv, true, dckv, rkv, M, rkv, H * (dn + dv), tr, st), "dc_kv");
   // norms: dc_q (and dc_kv) into ddown's columns, the gains' gradients in fp32
   if (w->kv_norm) {
     MLA_HIP(launch_rmsnorm_backward(dt, ckv_raw, rkv, dckv, rkv, w->kv_norm, M, rkv, c.rms_norm_eps,
@@ -808,11 +858,11 @@ mla_status mla_backward(const mla_config *cfg, const mla_weights *w, const void 
                                   grads->q_norm, rms, st),
           "q norm backward");
   // down projections: dx and the three weights
-  MLA_HIP(plain_gemm(dt, ddown, ld, false, wd, D, true, dx, D, M, D, rq + rkv + dr, st), "dx");
-  MLA_HIP(plain_gemm(dt, ddown, ld, true, x, D, true, grads->w_down_q, D, rq, D, M, st), "dw_down_q");
-  MLA_HIP(plain_gemm(dt, ddown + (size_t)rq * es, ld, true, x, D, true, grads->w_down_kv, D, rkv, D, M, st),
+  MLA_HIP(bwd_gemm(dt, ddown, ld, false, wd, D, true, dx, D, M, D, rq + rkv + dr, tr, st), "dx");
+  MLA_HIP(bwd_gemm(dt, ddown, ld, true, x, D, true, grads->w_down_q, D, rq, D, M, tr, st), "dw_down_q");
+  MLA_HIP(bwd_gemm(dt, ddown + (size_t)rq * es, ld, true, x, D, true, grads->w_down_kv, D, rkv, D, M, tr, st),
           "dw_down_kv");
-  MLA_HIP(plain_gemm(dt, ddown + (size_t)(rq + rkv) * es, ld, true, x, D, true, grads->w_kr, D, dr, D, M, st),
+  MLA_HIP(bwd_gemm(dt, ddown + (size_t)(rq + rkv) * es, ld, true, x, D, true, grads->w_kr, D, dr, D, M, tr, st),
           "dw_kr");
   return MLA_OK;
 }

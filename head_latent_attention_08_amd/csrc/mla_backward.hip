@@ -77,6 +77,35 @@ __global__ __launch_bounds__(256) void head_sum_kernel(const T *src, int64_t sp,
   }
 }
 
+// 64 x 64 tiles through LDS: 16-byte loads of source rows, 16-byte stores of
+// destination rows (each gathered from eight LDS rows; the 144-byte pitch
+// puts those eight 2-byte reads in distinct banks).
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16 *src, int64_t lds, int R, int C, bf16 *dst,
+                                                        int64_t ldd) {
+  __shared__ __attribute__((aligned(16))) bf16 t[64][72];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ch = tid + 256 * i;  // source row ch / 8, columns 8 (ch % 8) ..
+    const int r = ch >> 3, c = (ch & 7) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < R && c0 + c < C) v = *reinterpret_cast<const uint4 *>(src + (int64_t)(r0 + r) * lds + c0 + c);
+    *reinterpret_cast<uint4 *>(&t[r][c]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ch = tid + 256 * i;  // destination row (source column) ch / 8, its columns 8 (ch % 8) ..
+    const int c = ch >> 3, r = (ch & 7) * 8;
+    if (c0 + c < C && r0 + r < R) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = t[r + e][c];
+      *reinterpret_cast<bf16x8 *>(dst + (int64_t)(c0 + c) * ldd + r0 + r) = v;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void neg_positions_kernel(int32_t *pos, int64_t n, int S) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t < n) pos[t] = -(int32_t)(t % S);
@@ -134,6 +163,15 @@ hipError_t launch_head_sum(int dtype, const void *src, int64_t sp, int scol, voi
     hipLaunchKernelGGL(head_sum_kernel<float>, dim3(grid_for(items)), dim3(256), 0, st,
                        reinterpret_cast<const float *>(src), sp, scol, reinterpret_cast<float *>(dst), ldd, w, B,
                        S, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void *src, int64_t lds, int R, int C, void *dst, int64_t ldd, hipStream_t st) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  if (R % 8 || C % 8 || lds % 8 || ldd % 8 || ((uintptr_t)src | (uintptr_t)dst) % 16 || (R + 63) / 64 > 65535)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64)), dim3(256), 0, st,
+                     reinterpret_cast<const bf16 *>(src), lds, R, C, reinterpret_cast<bf16 *>(dst), ldd);
   return hipGetLastError();
 }
 

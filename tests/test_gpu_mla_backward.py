@@ -100,6 +100,14 @@ def test_mla_backward_small_bf16(conv, kv_norm):
     _compare(*_run(c, conv, S=130, B=2, seed=1302 + kv_norm, kv_norm=kv_norm))
 
 
+def test_mla_backward_small_bf16_large_tile_products():
+    # 512 tokens: every weight-gradient product with 512+ output rows and the
+    # dc / dx products run on the large-tile kernel, their transposed
+    # operands rewritten K-contiguous first
+    c = si.CONFIGS["small"]
+    _compare(*_run(c, "half_split", S=256, B=2, seed=1307, kv_norm=True))
+
+
 def test_mla_backward_small_fp32_ragged():
     # 1 and 67 tokens: partial tiles everywhere, one-token sequences
     c = shrink(si.CONFIGS["small"], dtype="fp32")
