@@ -125,7 +125,8 @@ hipError_t launch_fp8_gemm_seg(const Fp8GemmDesc &d, hipStream_t st);
 
 // Causal attention backward over BH heads of S rows: q, k [BH, S, dqk], v,
 // o, dout [BH, S, dv] in, dq, dk [BH, S, dqk] and dvo [BH, S, dv] out (all of
-// one dtype), lse and delta fp32 [BH * S] scratch.
+// one dtype); lse and delta fp32 [BH * S] scratch, delta = lse + BH * S (the
+// matrix-core kernels use the 2 BH S floats from lse as (lse, delta) pairs).
 struct AttnBwdArgs {
   const void *q, *k, *v, *o, *dout;
   void *dq, *dk, *dvo;
