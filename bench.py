@@ -515,8 +515,9 @@ def main():
                     help="skip the block-scaled FP8 projection products (context line)")
     ap.add_argument("--no-multi-token", action="store_true",
                     help="skip the multi-token decode lines (q_len 2 and 4)")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one of the two workloads only (profiling aid; no JSON line)")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
+                    help="time one of the two workloads, or the backward context line, only "
+                         "(profiling aid; no JSON line)")
     ap.add_argument("--replicas", type=int, default=3,
                     help="decode cache replicas rotated per step (defeats the 256 MB MALL)")
     ap.add_argument("--kernel-sha", action="store_true",
@@ -566,6 +567,12 @@ def main():
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
+
+    if args.only == "backward":
+        torch.cuda.set_device(0)
+        r = attention_backward_line(m, si.CONFIGS["v3_prefill"]["seq"], log)
+        log(f"bench: backward only: attention {r['ms']:.2f} ms, MLA backward {r['mla_backward_ms']:.2f} ms")
+        return
 
     torch.cuda.set_device(0)
     c_pre = si.CONFIGS["v3_prefill"]

@@ -24,6 +24,13 @@ struct GemmParams {
   int64_t lda, strideA, strideB, strideC;
   int M, N, K, S, H, nseg;
   GemmSeg seg[3];
+  // row RMSNorm split over a producer / consumer pair (GemmDesc)
+  float *rn_part;
+  const bf16 *rn_gain;
+  int rn_cols;
+  const float *rs_part;
+  int rs_chunks;
+  float rs_eps;
 };
 
 template <typename T> struct GemmCfg {
@@ -204,7 +211,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 // A (64*TM) x (64*TN) output tile per 256-thread workgroup: four waves in a
 // 2x2 grid of (32*TM) x (32*TN) wave tiles (TM x TN MFMA 32x32 tiles, up to
 // 256 fp32 accumulators per lane held in the accumulation registers), one
-// wave per SIMD; the projections use the square 256x256 tile (TM = TN = 4).
+// wave per SIMD; the projections use the square 256x256 tile (TM = TN = 4),
+// short-K ones 256x128 (TM = 4, TN = 2: 128 accumulators, two waves per
+// SIMD, three stages).
 // A copy block of B rows takes its column range's weight matrix, so range
 // starts only need to be multiples of 16 (channel-major ranges, whose stores
 // differ, start on tile boundaries).
@@ -275,7 +284,7 @@ template <int Q> __device__ inline void wait_slabs_outstanding(int slabs) {
 
 // Launch window: output columns [n_base, n_base + tiles_n * tile N) of every row.
 template <int TM, int TN, int GB_NST>
-__global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int tiles_m, int tiles_n,
+__global__ __launch_bounds__(GB_THREADS) __attribute__((amdgpu_waves_per_eu(TM * TN <= 8 ? 2 : 1))) void gemm_big_kernel(GemmParams p, int tiles_m, int tiles_n,
                                                               int n_base, int remap, int group_m) {
   using BT = BigTile<TM, TN, GB_NST>;
   constexpr int NQ = BT::NQ, QH = BT::QH, ABLK = BT::ABLK;
@@ -455,15 +464,48 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
   // either all row-major or all channel-major.
   const int st0 = seg_of(p, min(n0, p.N - 1));
   if (!SEG_FIELD(p, st0, tr)) {
+    // consumer of a split RMSNorm: row m of the product is scaled by
+    // 1 / sqrt(mean of the squares of its normalised input row + eps), the
+    // producer's 64-column partial sums added in column order
+    __shared__ float rs_s[BT::M];
+    if (p.rs_part) {
+      for (int row = tid; row < BT::M; row += GB_THREADS) {
+        const float *pp = p.rs_part + (int64_t)min(m0 + row, p.M - 1) * p.rs_chunks;
+        float ss = 0.f;
+        for (int j = 0; j < p.rs_chunks; ++j) ss += pp[j];
+        rs_s[row] = 1.0f / sqrtf(ss / (float)(64 * p.rs_chunks) + p.rs_eps);
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 32 * TM + i * 32 + acc_row(r, lane);
+        const float rs = p.rs_part ? rs_s[row] : 1.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          Cs[(wm * 32 * TM + i * 32 + acc_row(r, lane)) * BT::CPITCH + wn * 32 * TN + j * 32 + l32] =
-              (bf16)acc[i][j][r];
+        for (int j = 0; j < TN; ++j)
+          Cs[row * BT::CPITCH + wn * 32 * TN + j * 32 + l32] = (bf16)(acc[i][j][r] * rs);
+      }
     __syncthreads();
+    // producer of a split RMSNorm: per row, the sum of squares of the stored
+    // values of each 64-column chunk of [0, rn_cols) in this tile
+    if (p.rn_part && n0 < p.rn_cols) {
+      const int nch = min(BT::N, p.rn_cols - n0) / 64, chunks = p.rn_cols / 64;
+      for (int row = tid; row < BT::M; row += GB_THREADS) {
+        if (m0 + row >= p.M) continue;
+        for (int j = 0; j < nch; ++j) {
+          float ss = 0.f;
+#pragma unroll
+          for (int c8 = 0; c8 < 64; c8 += 8) {
+            const bf16x8 v = *reinterpret_cast<const bf16x8 *>(&Cs[row * BT::CPITCH + j * 64 + c8]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf((float)v[e], (float)v[e], ss);
+          }
+          p.rn_part[(int64_t)(m0 + row) * chunks + n0 / 64 + j] = ss;
+        }
+      }
+    }
     constexpr int RUNS = BT::N / 8;
     for (int it = 0; it < (BT::M * RUNS) / GB_THREADS; ++it) {
       const int c = tid + GB_THREADS * it;
@@ -476,7 +518,13 @@ __global__ __launch_bounds__(GB_THREADS) void gemm_big_kernel(GemmParams p, int 
       const int b = m / p.S, sq = m - b * p.S;
       bf16 *dst = reinterpret_cast<bf16 *>(SEG_FIELD(p, s, C)) +
                   ((int64_t)(b * p.H + h) * p.S + sq) * SEG_FIELD(p, s, ld) + SEG_FIELD(p, s, off) + d;
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&Cs[row * BT::CPITCH + cc * 8]);
+      bf16x8 v = *reinterpret_cast<const bf16x8 *>(&Cs[row * BT::CPITCH + cc * 8]);
+      if (p.rn_gain && n < p.rn_cols) {  // the producer stores its normalised columns times the gains
+        const bf16x8 gv = *reinterpret_cast<const bf16x8 *>(p.rn_gain + n);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)((float)v[e] * (float)gv[e]);
+      }
+      *reinterpret_cast<bf16x8 *>(dst) = v;
     }
   } else {
     // Channel-major destination: the tile goes to LDS transposed (column n
@@ -746,15 +794,23 @@ static bool tr_aligned(const GemmDesc &d, int bn) {
   return true;
 }
 
-template <int TM, int TN>
+template <int TM, int TN, int NST = GB_STAGES>
 static hipError_t launch_big(const GemmParams &p, const GemmDesc &d, int n_lo, int n_hi, hipStream_t st) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
   const int tm = (d.M + BM - 1) / BM, tn = (n_hi - n_lo + BN - 1) / BN;
   const int T = tm * tn;
   const int group_m = d.K >= 4096 ? 8 : (d.K <= 1024 ? 2 : 4);
-  hipLaunchKernelGGL((gemm_big_kernel<TM, TN, GB_STAGES>), dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn, n_lo,
+  hipLaunchKernelGGL((gemm_big_kernel<TM, TN, NST>), dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn, n_lo,
                      (T % 8 == 0) ? 1 : 0, group_m);
   return hipGetLastError();
+}
+
+bool gemm_uses_large_tiles(const GemmDesc &d) {
+  bool big = d.dtype == BF16 && !d.b_kn && !d.a_km && d.batch == 1 && d.K % GB_K == 0 && d.M >= 512 &&
+             d.N % 8 == 0 && (int64_t)d.M * d.lda < (1LL << 31);
+  for (int i = 0; i < d.nseg && big; ++i)
+    big = d.seg[i].n_begin % 16 == 0 && (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
+  return big && tr_aligned(d, BigTile<4, 4, GB_STAGES>::N);
 }
 
 bool gemm_takes_large_tiles(int dtype, int M, int N, int K) {
@@ -777,11 +833,13 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   p.H = d.H;
   p.nseg = d.nseg;
   for (int i = 0; i < 3; ++i) p.seg[i] = d.seg[i];
-  bool big = d.dtype == BF16 && !d.b_kn && !d.a_km && d.batch == 1 && d.K % GB_K == 0 && d.M >= 512 &&
-             d.N % 8 == 0 && (int64_t)d.M * d.lda < (1LL << 31);
-  for (int i = 0; i < d.nseg && big; ++i)
-    big = d.seg[i].n_begin % 16 == 0 && (int64_t)d.N * d.seg[i].ldb < (1LL << 31);
-  if (big && tr_aligned(d, BigTile<4, 4, GB_STAGES>::N)) {
+  p.rn_part = d.rn_part;
+  p.rn_gain = reinterpret_cast<const bf16 *>(d.rn_gain);
+  p.rn_cols = d.rn_cols;
+  p.rs_part = d.rs_part;
+  p.rs_chunks = d.rs_chunks;
+  p.rs_eps = d.rs_eps;
+  if (gemm_uses_large_tiles(d)) {
     // A product whose 256x256 tiles would leave most CUs idle in its only
     // round (the down projection: 144 tiles) runs as 192x192 tiles, which
     // fill one round (242 tiles) at a somewhat lower efficiency per tile.
@@ -789,8 +847,15 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
     const int64_t t256 = (int64_t)((d.M + 255) / 256) * ((d.N + 255) / 256);
     const int64_t t192 = (int64_t)((d.M + 191) / 192) * ((d.N + 191) / 192);
     if (10 * t256 <= 6 * cus && t192 <= cus && tr_aligned(d, 192)) return launch_big<3, 3>(p, d, 0, d.N, st);
+    // Short K (the kv up-projection, K = 512): 256x128 tiles through three
+    // stages fit two workgroups per CU (two waves per SIMD), so one's
+    // epilogue runs under the other's K loop (5% faster there; slower for
+    // long K, whose tiles are all main loop).
+    if (d.K <= 512 && tr_aligned(d, 128)) return launch_big<4, 2, 3>(p, d, 0, d.N, st);
     return launch_big<4, 4>(p, d, 0, d.N, st);
   }
+  // a split RMSNorm exists only in the large-tile kernel's epilogue
+  if (d.rn_part || d.rs_part) return hipErrorInvalidValue;
   bool skinny = d.dtype == BF16 && !d.b_kn && !d.a_km && d.M <= SK_MMAX && d.K % SK_K == 0 && d.N % 8 == 0 &&
                 d.batch * ((d.M + SK_M - 1) / SK_M) <= 65535;
   for (int i = 0; i < d.nseg && skinny; ++i) skinny = d.seg[i].n_begin % SK_N == 0;

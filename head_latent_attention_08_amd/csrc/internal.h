@@ -45,6 +45,20 @@ struct GemmDesc {
   // NULL or too small the kernels run without splitting K
   void *workspace = nullptr;
   size_t workspace_bytes = 0;
+  // Row RMSNorm split over two products y = RMSNorm(x W1^T) W2^T (large-tile
+  // kernel only; launch_gemm refuses them elsewhere).  Producer (x W1^T):
+  // for output columns [0, rn_cols) (a multiple of 64) it writes, per row m
+  // and 64-column chunk j, the sum of squares of the stored bf16 values to
+  // rn_part[m * rn_cols / 64 + j], and stores those columns multiplied by
+  // rn_gain (bf16).  Consumer (. W2^T, K = rn_cols): output row m is scaled
+  // by 1 / sqrt(sum_j rs_part[m * rs_chunks + j] / (64 rs_chunks) + rs_eps),
+  // j in order, before rounding.
+  float *rn_part = nullptr;
+  const void *rn_gain = nullptr;
+  int rn_cols = 0;
+  const float *rs_part = nullptr;
+  int rs_chunks = 0;
+  float rs_eps = 0.f;
 };
 
 hipError_t launch_gemm(const GemmDesc &d, hipStream_t st);
@@ -52,6 +66,8 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st);
 // kernel when both operands are K-contiguous (single batch, one column range
 // starting at 0, ldb = K).
 bool gemm_takes_large_tiles(int dtype, int M, int N, int K);
+// Whether launch_gemm runs this product on the large-tile kernel.
+bool gemm_uses_large_tiles(const GemmDesc &d);
 
 // Scratch bytes launch_gemm can use for split-K partials of an M x N x K
 // product (0 when it never splits).

@@ -197,8 +197,52 @@ hipError_t launch_down_norms(const mla_config &c, const mla_weights *w, char *do
 struct PrefillPlan {
   int64_t ld_down;
   size_t off_down, off_q, off_kn, off_v, off_o, total;
+  size_t off_qrms;  // split RMSNorm of c_q: [B*S, r_q / 64] fp32 partial sums of squares
+  bool q_norm_split;
   size_t off_start, off_last, off_pos, off_valid, off_ok;  // key-range prefills only
 };
+
+// The prefill's fused down-projection [c_q ‖ c_kv ‖ k_pe] = x [w_down_q;
+// w_down_kv; w_kr]^T and its q up-projection [q_nope ‖ q_pe] per head =
+// c_qn [w_up_q; w_qr]^T (w, x and the outputs may be NULL where only the
+// shapes matter).
+GemmDesc down_proj_desc(const mla_config &c, int64_t M, const mla_weights *w, const void *x, void *down,
+                        int64_t ld_down) {
+  const int D = c.hidden_size, rq = c.q_lora_rank, rkv = c.kv_lora_rank, dr = c.qk_rope_head_dim;
+  GemmDesc g;
+  g.dtype = c.dtype;
+  g.M = (int)M;
+  g.N = rq + rkv + dr;
+  g.K = D;
+  g.A = x;
+  g.lda = D;
+  g.S = (int)M;
+  g.H = 1;
+  g.nseg = 3;
+  g.seg[0] = GemmSeg{w ? w->w_down_q : nullptr, D, 0, down, rq, ld_down, 0};
+  g.seg[1] = GemmSeg{w ? w->w_down_kv : nullptr, D, rq, down, rkv, ld_down, rq};
+  g.seg[2] = GemmSeg{w ? w->w_kr : nullptr, D, rq + rkv, down, dr, ld_down, rq + rkv};
+  return g;
+}
+
+GemmDesc q_up_desc(const mla_config &c, int64_t M, int64_t S, const mla_weights *w, const void *down,
+                   int64_t ld_down, void *q) {
+  const int H = c.num_heads, rq = c.q_lora_rank, dn = c.qk_nope_head_dim, dr = c.qk_rope_head_dim;
+  const int dqk = dn + dr;
+  GemmDesc g;
+  g.dtype = c.dtype;
+  g.M = (int)M;
+  g.N = H * dqk;
+  g.K = rq;
+  g.A = down;
+  g.lda = ld_down;
+  g.S = (int)S;
+  g.H = H;
+  g.nseg = 2;
+  g.seg[0] = GemmSeg{w ? w->w_up_q : nullptr, rq, 0, q, dn, dqk, 0};
+  g.seg[1] = GemmSeg{w ? w->w_qr : nullptr, rq, H * dn, q, dr, dqk, dn};
+  return g;
+}
 
 PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S, bool varlen = false) {
   const size_t es = dtype_size(c.dtype);
@@ -224,6 +268,14 @@ PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S, bool varlen 
     p.off_valid = take((size_t)M * sizeof(int32_t));
     p.off_ok = take(sizeof(int32_t));
   }
+  // RMSNorm(c_q) split over the two products' epilogues when both run on the
+  // large-tile kernel (bf16): the down-projection leaves per-row partial sums
+  // of squares of c_q (per 64 columns) and stores c_q times the gains, the q
+  // up-projection scales each output row by the row's 1 / rms
+  p.q_norm_split = c.dtype == MLA_DTYPE_BF16 && c.q_lora_rank % 64 == 0 &&
+                   gemm_uses_large_tiles(down_proj_desc(c, M, nullptr, nullptr, nullptr, p.ld_down)) &&
+                   gemm_uses_large_tiles(q_up_desc(c, M, S, nullptr, nullptr, p.ld_down, nullptr));
+  p.off_qrms = take(p.q_norm_split ? (size_t)M * (c.q_lora_rank / 64) * sizeof(float) : 0);
   p.total = off;
   return p;
 }
@@ -349,6 +401,8 @@ mla_status mla_prefill_layout_of(const mla_config *cfg, int64_t batch, int64_t s
   layout->v = p.off_v;
   layout->o = p.off_o;
   layout->ld_down = p.ld_down;
+  layout->q_rms_part = p.off_qrms;
+  layout->q_rms_chunks = p.q_norm_split ? cfg->q_lora_rank / 64 : 0;
   layout->total = p.total;
   return MLA_OK;
 }
@@ -400,25 +454,26 @@ static mla_status prefill_common(const mla_config *cfg, const mla_weights *w, co
     MLA_HIP(launch_varlen_index(cu_seqlens, (int)n_seq, M, vl_start, vl_last, vl_pos, vl_valid,
                                 vl_ok, st),
             "sequence offsets");
+  float *qrms = reinterpret_cast<float *>(ws + p.off_qrms);
   {
-    GemmDesc g;
-    g.dtype = c.dtype;
-    g.M = M;
-    g.N = rq + rkv + dr;
-    g.K = D;
-    g.A = x;
-    g.lda = D;
-    g.S = M;
-    g.H = 1;
-    g.nseg = 3;
-    g.seg[0] = GemmSeg{w->w_down_q, D, 0, down, rq, p.ld_down, 0};
-    g.seg[1] = GemmSeg{w->w_down_kv, D, rq, down, rkv, p.ld_down, rq};
-    g.seg[2] = GemmSeg{w->w_kr, D, rq + rkv, down, dr, p.ld_down, rq + rkv};
+    GemmDesc g = down_proj_desc(c, M, w, x, down, p.ld_down);
+    if (p.q_norm_split) {
+      g.rn_part = qrms;
+      g.rn_gain = w->q_norm;
+      g.rn_cols = rq;
+    }
     MLA_HIP(launch_gemm(g, st), "down projection");
   }
-  // 2. RMSNorm(c_q)
+  // 2. RMSNorm(c_q) (here unless split over the projections' epilogues), and
+  // of c_kv when kv_norm gains are given
   MLA_MARK(1);
-  MLA_HIP(launch_down_norms(c, w, down, M, p.ld_down, st), "rmsnorm");
+  if (p.q_norm_split) {
+    if (w->kv_norm)
+      MLA_HIP(launch_rmsnorm(c.dtype, down + (size_t)rq * es, M, p.ld_down, rkv, w->kv_norm, c.rms_norm_eps, st),
+              "rmsnorm c_kv");
+  } else {
+    MLA_HIP(launch_down_norms(c, w, down, M, p.ld_down, st), "rmsnorm");
+  }
   // 3. RoPE of the shared key at positions 0..S-1
   MLA_MARK(2);
   MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, M, S, (int64_t)S * p.ld_down,
@@ -431,18 +486,12 @@ static mla_status prefill_common(const mla_config *cfg, const mla_weights *w, co
   // 4. q = [q_nope ‖ q_pe] per head, then RoPE of q_pe
   MLA_MARK(3);
   {
-    GemmDesc g;
-    g.dtype = c.dtype;
-    g.M = M;
-    g.N = H * dqk;
-    g.K = rq;
-    g.A = down;
-    g.lda = p.ld_down;
-    g.S = S;
-    g.H = H;
-    g.nseg = 2;
-    g.seg[0] = GemmSeg{w->w_up_q, rq, 0, q, dn, dqk, 0};
-    g.seg[1] = GemmSeg{w->w_qr, rq, H * dn, q, dr, dqk, dn};
+    GemmDesc g = q_up_desc(c, M, S, w, down, p.ld_down, q);
+    if (p.q_norm_split) {
+      g.rs_part = qrms;
+      g.rs_chunks = rq / 64;
+      g.rs_eps = c.rms_norm_eps;
+    }
     MLA_HIP(launch_gemm(g, st), "q up-projection");
   }
   MLA_MARK(4);

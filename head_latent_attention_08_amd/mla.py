@@ -78,7 +78,8 @@ class WeightGrads(ctypes.Structure):
 
 class PrefillLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("c_q", "c_kv", "k_pe", "q", "k_nope", "v", "o")] + [
-        ("ld_down", ctypes.c_int64), ("total", ctypes.c_size_t)]
+        ("ld_down", ctypes.c_int64), ("q_rms_part", ctypes.c_size_t), ("q_rms_chunks", ctypes.c_int64),
+        ("total", ctypes.c_size_t)]
 
 
 class DecodeLayout(ctypes.Structure):

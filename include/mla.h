@@ -118,17 +118,28 @@ typedef struct {                  /* device pointers, nn.Linear [out][in]      *
 } mla_weights;
 
 /* Byte offsets, inside the workspace, of the intermediates a prefill leaves
- * there (all in cfg->dtype, valid once the stream has run the call):
+ * there (all in cfg->dtype unless stated, valid once the stream has run the
+ * call):
  *   c_q   [B*S, r_q]           c_q = x w_down_q^T, then RMS-normalised in place
+ *                              (q_rms_chunks = 0), or, with the RMSNorm split
+ *                              over the down- and q up-projection (q_rms_chunks
+ *                              > 0), c_q times the q_norm gains
  *   c_kv  [B*S, r_kv]          latent;  k_pe [B*S, d_r] post-RoPE
  *   q     [B, H, S, d_n+d_r]   q_nope ‖ post-RoPE q_pe per head
  *   k_nope[B, H, S, d_n]       v [B, H, d_v, S] (channel-major: keys contiguous)
  *   o     [B*S, H*d_v]         attention output, head-major columns
+ *   q_rms_part [B*S, q_rms_chunks] fp32: per row, the sums of squares of c_q
+ *                              over 64-column chunks; the normalised row is
+ *                              c_q[r] * g / sqrt(sum / r_q + eps)
  * Row strides: c_q, c_kv and k_pe share one row of ld_down elements
- * (c_q at column 0, c_kv at r_q, k_pe at r_q + r_kv). */
+ * (c_q at column 0, c_kv at r_q, k_pe at r_q + r_kv).  The split is used
+ * for bf16 when r_q is a multiple of 64 and both products run on the
+ * large-tile kernel (B*S >= 512, among others). */
 typedef struct {
   size_t c_q, c_kv, k_pe, q, k_nope, v, o;
   int64_t ld_down;
+  size_t q_rms_part;
+  int64_t q_rms_chunks;
   size_t total;
 } mla_prefill_layout;
 

@@ -89,6 +89,13 @@ def test_workspace_sizes():
     offs = [lay.c_q, lay.q, lay.k_nope, lay.v, lay.o]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.c_kv == lay.c_q + 1536 * 2 and lay.k_pe == lay.c_kv + 512 * 2
+    # bf16 at 4096 tokens: RMSNorm(c_q) split over the two projections, one
+    # fp32 partial per 64 columns of c_q and row, inside the workspace
+    assert lay.q_rms_chunks == 1536 // 64
+    assert lay.q_rms_part % 256 == 0 and lay.q_rms_part + 4096 * 24 * 4 <= lay.total
+    # fp32, or too few rows for the large-tile products: normalised in place
+    assert m.mla_prefill_layout_of(m.MlaConfig(**V3, dtype=m.DTYPE_F32), 1, 4096).q_rms_chunks == 0
+    assert m.mla_prefill_layout_of(cfg, 1, 256).q_rms_chunks == 0
     d = m.mla_decode_workspace_size(cfg, 64, 8193)
     dl = m.mla_decode_layout_of(cfg, 64, 8193)
     assert dl.total == d and dl.n_splits >= 1

@@ -34,13 +34,15 @@ def _gains(w, dtype, seed, on):
     return w
 
 
-@pytest.mark.parametrize("name", ["tiny", "small"])
+@pytest.mark.parametrize("name,seq", [("tiny", None), ("small", 100), ("small", 512)])
 @pytest.mark.parametrize("on", [False, True])
-def test_prefill_kv_norm(name, on):
+def test_prefill_kv_norm(name, seq, on):
+    # small at 2 x 512 tokens: RMSNorm(c_q) split over the projections' epilogues
+    # while the c_kv norm runs as its own pass
     m = _m()
     c = si.CONFIGS[name]
     dt = c["dtype"]
-    x, w = si.make_inputs(c, seq=100 if name == "small" else None, gains="random")
+    x, w = si.make_inputs(c, seq=seq, gains="random")
     w = _gains(w, dt, 51, on)
     cfg = mla_cfg(c, rope="interleaved")
     y, lat, _ = m.mla_prefill_forward(cfg, weights_to_dev(w, dt), to_dev(x, dt), want_latent=True)

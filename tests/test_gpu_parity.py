@@ -128,8 +128,16 @@ def _check_intermediates(m, cfg, c, x, ws, inter, dtype):
         "v": inter["v"].transpose(0, 2, 1, 3),
         "o": inter["o"].reshape(M, H * dv),
     }
+    if lay.q_rms_chunks:
+        # RMSNorm split over the projections: c_q holds c_q * g, the partial
+        # sums of squares give each row's 1 / rms
+        part = to_np(ws_view(ws, lay.q_rms_part, (M, lay.q_rms_chunks), torch.float32))
+        eps = cfg.rms_norm_eps
+        rinv = 1.0 / np.sqrt(part.astype(np.float64).sum(axis=1) / rq + eps)
+        got["c_qn"] = to_np(got["c_qn"]) * rinv[:, None]
     for k in refs:
-        assert_close_rows(to_np(got[k]), refs[k], dtype, k)
+        g = got[k] if isinstance(got[k], np.ndarray) else to_np(got[k])
+        assert_close_rows(g, refs[k], dtype, k)
 
 
 def test_prefill_tiny_fp32():
