@@ -472,7 +472,17 @@ __global__ __launch_bounds__(GB_THREADS) __attribute__((amdgpu_waves_per_eu(TM *
       for (int row = tid; row < BT::M; row += GB_THREADS) {
         const float *pp = p.rs_part + (int64_t)min(m0 + row, p.M - 1) * p.rs_chunks;
         float ss = 0.f;
-        for (int j = 0; j < p.rs_chunks; ++j) ss += pp[j];
+        if ((p.rs_chunks & 3) == 0) {  // 16-byte loads, the same order
+          for (int j = 0; j < p.rs_chunks; j += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(pp + j);
+            ss += v.x;
+            ss += v.y;
+            ss += v.z;
+            ss += v.w;
+          }
+        } else {
+          for (int j = 0; j < p.rs_chunks; ++j) ss += pp[j];
+        }
         rs_s[row] = 1.0f / sqrtf(ss / (float)(64 * p.rs_chunks) + p.rs_eps);
       }
       __syncthreads();
