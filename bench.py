@@ -44,17 +44,17 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "ea85110b5eed357482d032ed7bc86a802bbe10f39fb890d72b6950e737c47c6d",
-        "FETCH_SIZE_KiB": 242840.7, "WRITE_SIZE_KiB": 131082.3},
+        "sha256": "568e686ca48263d48750d2464347b49160517848733cd17a9a8730a3d41152ee",
+        "FETCH_SIZE_KiB": 243551.7, "WRITE_SIZE_KiB": 131090.8},
     "out_proj": {
-        "sha256": "f2f7684e95ac95bc1f6cc80c8c9f4e0b76da1cc03f961c0ce621c58002cc43a8",
-        "FETCH_SIZE_KiB": 1512488.6, "WRITE_SIZE_KiB": 57792.0},
+        "sha256": "4d6d3a4e74300e006af2c754c51c452ff410a1a8b2e1a8524389f25cb469f66e",
+        "FETCH_SIZE_KiB": 1526079.4, "WRITE_SIZE_KiB": 57344.0},
     "latent_attention": {
-        "sha256": "a0abdfcb7ad6f8d0b728cb1fa3a739ec974d702ec4f12213538ce9f9a77d3c47",
-        "FETCH_SIZE_KiB": 181369.2, "WRITE_SIZE_KiB": 76843.0},
+        "sha256": "60ec3fd5e4d44fc8ba548518df16a1b8a327f31a700aedbd12d33f6a1efba23f",
+        "FETCH_SIZE_KiB": 181376.4, "WRITE_SIZE_KiB": 76843.0},
     "fp8_out_proj": {
-        "sha256": "021cff372681f1e6cbe0171176805f770b6a5ad0c8cfd8630917d4935dad36af",
-        "FETCH_SIZE_KiB": 380698.0, "WRITE_SIZE_KiB": 57792.0},
+        "sha256": "58394bc4cb444ddcacdb7151609927b6591156e25c9031e50bb370a95b01b4dc",
+        "FETCH_SIZE_KiB": 380429.3, "WRITE_SIZE_KiB": 57792.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
