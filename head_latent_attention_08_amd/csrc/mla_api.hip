@@ -571,7 +571,7 @@ namespace {
 struct BackwardPlan {
   PrefillPlan fwd;
   size_t off_cq_raw, off_ckv_raw, off_vh, off_kh, off_oh, off_doh, off_dqh, off_dkh, off_dvh, off_att,
-      off_pos, off_gq, off_gkv, off_dcqn, off_dckv, off_ddown, off_wq, off_wkv, off_wd, off_rms, off_tr, total;
+      off_pos, off_gq, off_gkv, off_dcqn, off_dckv, off_ddown, off_wq, off_wkv, off_wd, off_rms, off_tr, off_dwd, total;
 };
 
 // Elements of transposed operand copies a backward product C [M, N] =
@@ -626,8 +626,11 @@ BackwardPlan plan_backward(const mla_config &c, int64_t B, int64_t S) {
                               bwd_tr_elems(dt, H * dn, rkv, M, true, true), bwd_tr_elems(dt, H * dv, rkv, M, true, true),
                               bwd_tr_elems(dt, M, rkv, H * (dn + dv), false, true),
                               bwd_tr_elems(dt, M, D, rq + rkv + dr, false, true), bwd_tr_elems(dt, rq, D, M, true, true),
-                              bwd_tr_elems(dt, rkv, D, M, true, true), bwd_tr_elems(dt, dr, D, M, true, true)});
+                              bwd_tr_elems(dt, rkv, D, M, true, true), bwd_tr_elems(dt, dr, D, M, true, true),
+                              bwd_tr_elems(dt, rq + rkv + dr, D, M, true, true)});
   p.off_tr = take(tr * es);
+  // the stacked down-projection weights' gradient [r_q + r_kv + d_r, D]
+  p.off_dwd = take((size_t)(rq + rkv + dr) * D * es);
   p.total = off;
   return p;
 }
@@ -908,11 +911,16 @@ mla_status mla_backward(const mla_config *cfg, const mla_weights *w, const void 
           "q norm backward");
   // down projections: dx and the three weights
   MLA_HIP(bwd_gemm(dt, ddown, ld, false, wd, D, true, dx, D, M, D, rq + rkv + dr, tr, st), "dx");
-  MLA_HIP(bwd_gemm(dt, ddown, ld, true, x, D, true, grads->w_down_q, D, rq, D, M, tr, st), "dw_down_q");
-  MLA_HIP(bwd_gemm(dt, ddown + (size_t)rq * es, ld, true, x, D, true, grads->w_down_kv, D, rkv, D, M, tr, st),
-          "dw_down_kv");
-  MLA_HIP(bwd_gemm(dt, ddown + (size_t)(rq + rkv) * es, ld, true, x, D, true, grads->w_kr, D, dr, D, M, tr, st),
-          "dw_kr");
+  // the three weights' gradients as one product over ddown's stacked
+  // columns [c_q ‖ c_kv ‖ k_pe] (2112 output rows at V3: one well-filled
+  // large-tile launch instead of three, the 64-row k_pe one on the general
+  // kernel), then split by rows
+  const int nd = rq + rkv + dr;
+  char *dwd = at(p.off_dwd);
+  MLA_HIP(bwd_gemm(dt, ddown, ld, true, x, D, true, dwd, D, nd, D, M, tr, st), "dw_down");
+  MLA_HIP(launch_copy_rows(dt, grads->w_down_q, D, dwd, D, rq, D, st), "dw_down_q rows");
+  MLA_HIP(launch_copy_rows(dt, grads->w_down_kv, D, dwd + (size_t)rq * D * es, D, rkv, D, st), "dw_down_kv rows");
+  MLA_HIP(launch_copy_rows(dt, grads->w_kr, D, dwd + (size_t)(rq + rkv) * D * es, D, dr, D, st), "dw_kr rows");
   return MLA_OK;
 }
 
