@@ -531,7 +531,9 @@ MLA_API mla_status mla_backward(const mla_config *cfg, const mla_weights *w, con
  *            3 q up-projection, 4 q_pe RoPE, 5 absorption, 6 latent
  *            attention, 7 split merge, 8 un-absorption, 9 output projection
  *                                                         (11 events)
- * events = NULL (or n_events = 0) switches it off.  The library keeps the
+ * A NULL entry records nothing at that boundary (each recorded event costs
+ * the stream a few microseconds, so a caller timing one stage may mark only
+ * its ends).  events = NULL (or n_events = 0) switches it off.  The library keeps the
  * pointer array until then; the caller keeps it alive.  A failing
  * hipEventRecord makes the call return MLA_ERR_HIP. */
 MLA_API mla_status mla_set_stage_events(void *const *events, int32_t n_events);
