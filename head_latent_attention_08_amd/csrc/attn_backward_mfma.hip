@@ -169,10 +169,17 @@ __device__ inline uint32_t lds_addr(const void *p) {
 }
 
 // Workgroup -> (head, block): the blocks of a head run on one XCD
-// (workgroup ids go to the eight XCDs round-robin), longest blocks first.
+// (workgroup ids go to the eight XCDs round-robin), longest blocks first; an
+// XCD takes its heads two at a time with their blocks interleaved, so the
+// long blocks of the last heads do not start at the end.
 __device__ inline void block_of(int BH, int nb, int &bh, int &blk, bool reverse) {
   const int w = blockIdx.x;
-  if ((BH & 7) == 0) {
+  if ((BH & 15) == 0) {
+    const int local = w >> 3;
+    const int grp = local / (2 * nb), r = local - grp * (2 * nb);
+    bh = (w & 7) * (BH >> 3) + 2 * grp + (r & 1);
+    blk = r >> 1;
+  } else if ((BH & 7) == 0) {
     const int local = w >> 3;
     bh = (w & 7) * (BH >> 3) + local / nb;
     blk = local % nb;
