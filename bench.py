@@ -48,17 +48,17 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "568e686ca48263d48750d2464347b49160517848733cd17a9a8730a3d41152ee",
-        "FETCH_SIZE_KiB": 243515.9, "WRITE_SIZE_KiB": 131089.5},
+        "sha256": "c511da3c7417c124cc3c7d1fee685482bb104699cc10372cf5733ff62001307d",
+        "FETCH_SIZE_KiB": 323771.1, "WRITE_SIZE_KiB": 131956.6},
     "out_proj": {
         "sha256": "3f81ecbcf74995c225203be078b7e0960ecd0518a9979b43eefe6ac6a4456729",
-        "FETCH_SIZE_KiB": 1444157.2, "WRITE_SIZE_KiB": 57344.0},
+        "FETCH_SIZE_KiB": 1440347.3, "WRITE_SIZE_KiB": 57344.0},
     "latent_attention": {
         "sha256": "60ec3fd5e4d44fc8ba548518df16a1b8a327f31a700aedbd12d33f6a1efba23f",
         "FETCH_SIZE_KiB": 181371.2, "WRITE_SIZE_KiB": 76843.0},
     "fp8_out_proj": {
         "sha256": "58394bc4cb444ddcacdb7151609927b6591156e25c9031e50bb370a95b01b4dc",
-        "FETCH_SIZE_KiB": 380348.3, "WRITE_SIZE_KiB": 57792.0},
+        "FETCH_SIZE_KiB": 380563.2, "WRITE_SIZE_KiB": 57792.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
