@@ -273,6 +273,39 @@ template <typename P> __device__ inline P *uniform_ptr(P *q) {
                                (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
 }
 
+// Row-major stores of one thread's 8-column run: rows r0, r0 + RSTEP, .. of
+// the LDS tile, U at a time (their LDS reads issued together).  dst points at
+// row r0's destination; a step moves it RSTEP rows down its sequence, and a
+// step past the sequence's end (s >= S) on to the next sequence, H - 1
+// sequences of this head's rows further.  With GAIN the values are scaled by
+// gv (bf16 products, as stored by a split-RMSNorm producer).
+template <int PASSES, int U, int RSTEP, int CPITCH, bool GAIN>
+__device__ __forceinline__ void store_row_runs(const bf16 *Cs, int r0, int cc, bf16 *dst, int64_t ld, int m, int M,
+                                               int sq, int S, int64_t wrap, bf16x8 gv) {
+  for (int it = 0; it < PASSES; it += U) {
+    bf16x8 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const bf16x8 *>(&Cs[(r0 + RSTEP * (it + u)) * CPITCH + cc * 8]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (m < M) {
+        if constexpr (GAIN) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[u][e] = (bf16)((float)v[u][e] * (float)gv[e]);
+        }
+        *reinterpret_cast<bf16x8 *>(dst) = v[u];
+      }
+      m += RSTEP;
+      sq += RSTEP;
+      dst += RSTEP * ld;
+      while (sq >= S) {
+        sq -= S;
+        dst += wrap;
+      }
+    }
+  }
+}
+
 // vmcnt immediates of the K loop, per wave: q copies per slab
 template <int Q> __device__ inline void wait_slabs_outstanding(int slabs) {
   if (slabs >= 4) __builtin_amdgcn_s_waitcnt(GB_VMCNT(4 * Q));
@@ -487,16 +520,29 @@ __global__ __launch_bounds__(GB_THREADS) __attribute__((amdgpu_waves_per_eu(TM *
       }
       __syncthreads();
     }
+    // A lane's rows of row block i are 8q + 4g + e (q, e < 4): their scale
+    // factors are read as four 16-byte words ahead of the block's LDS stores,
+    // so no store waits on a read.
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+      float rsv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 v = make_float4(1.f, 1.f, 1.f, 1.f);
+        if (p.rs_part) v = *reinterpret_cast<const float4 *>(&rs_s[wm * 32 * TM + i * 32 + 8 * q + 4 * g]);
+        rsv[4 * q] = v.x;
+        rsv[4 * q + 1] = v.y;
+        rsv[4 * q + 2] = v.z;
+        rsv[4 * q + 3] = v.w;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wm * 32 * TM + i * 32 + acc_row(r, lane);
-        const float rs = p.rs_part ? rs_s[row] : 1.0f;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          Cs[row * BT::CPITCH + wn * 32 * TN + j * 32 + l32] = (bf16)(acc[i][j][r] * rs);
+          Cs[row * BT::CPITCH + wn * 32 * TN + j * 32 + l32] = (bf16)(acc[i][j][r] * rsv[r]);
       }
+    }
     __syncthreads();
     // producer of a split RMSNorm: per row, the sum of squares of the stored
     // values of each 64-column chunk of [0, rn_cols) in this tile
@@ -516,25 +562,62 @@ __global__ __launch_bounds__(GB_THREADS) __attribute__((amdgpu_waves_per_eu(TM *
         }
       }
     }
-    constexpr int RUNS = BT::N / 8;
-    for (int it = 0; it < (BT::M * RUNS) / GB_THREADS; ++it) {
-      const int c = tid + GB_THREADS * it;
-      const int row = c / RUNS, cc = c - row * RUNS;
-      const int m = m0 + row, n = n0 + cc * 8;
-      if (m >= p.M || n >= p.N) continue;
-      const int s = seg_of(p, n);
-      const int nn = n - SEG_FIELD(p, s, n_begin), dh = SEG_FIELD(p, s, dh);
-      const int h = nn / dh, d = nn - h * dh;
-      const int b = m / p.S, sq = m - b * p.S;
-      bf16 *dst = reinterpret_cast<bf16 *>(SEG_FIELD(p, s, C)) +
-                  ((int64_t)(b * p.H + h) * p.S + sq) * SEG_FIELD(p, s, ld) + SEG_FIELD(p, s, off) + d;
-      bf16x8 v = *reinterpret_cast<const bf16x8 *>(&Cs[row * BT::CPITCH + cc * 8]);
-      if (p.rn_gain && n < p.rn_cols) {  // the producer stores its normalised columns times the gains
-        const bf16x8 gv = *reinterpret_cast<const bf16x8 *>(p.rn_gain + n);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (bf16)((float)v[e] * (float)gv[e]);
+    // Stores: 8-column runs, U passes at a time (their LDS reads issued
+    // together).  Row m goes to row (b H + h) S + s of its range's output
+    // (b = m / S, s = m % S, h the head of the column).
+    constexpr int RUNS = BT::N / 8, PASSES = BT::M * RUNS / GB_THREADS;
+    static_assert(BT::M * RUNS % GB_THREADS == 0, "runs must split evenly over the threads");
+    constexpr int U = PASSES % 8 == 0 ? 8 : PASSES % 6 == 0 ? 6 : PASSES % 4 == 0 ? 4 : 1;
+    if constexpr (GB_THREADS % RUNS == 0) {
+      // a thread keeps one run of columns; its rows step by RSTEP
+      constexpr int RSTEP = GB_THREADS / RUNS;
+      const int cc = tid % RUNS, r0 = tid / RUNS;
+      const int n = n0 + cc * 8;
+      if (n < p.N) {
+        const int s = seg_of(p, n);
+        const int nn = n - SEG_FIELD(p, s, n_begin), dh = SEG_FIELD(p, s, dh);
+        const int h = nn / dh, d = nn - h * dh;
+        const int64_t ld = SEG_FIELD(p, s, ld);
+        bf16 *cb = reinterpret_cast<bf16 *>(SEG_FIELD(p, s, C)) + SEG_FIELD(p, s, off) + d;
+        const int m = m0 + r0, b = m / p.S, sq = m - b * p.S;
+        bf16 *dst = cb + ((int64_t)(b * p.H + h) * p.S + sq) * ld;
+        const int64_t wrap = (int64_t)(p.H - 1) * p.S * ld;
+        if (p.rn_gain && n < p.rn_cols) {  // the producer stores its normalised columns times the gains
+          const bf16x8 gv = *reinterpret_cast<const bf16x8 *>(p.rn_gain + n);
+          store_row_runs<PASSES, U, RSTEP, BT::CPITCH, true>(Cs, r0, cc, dst, ld, m, p.M, sq, p.S, wrap, gv);
+        } else {
+          store_row_runs<PASSES, U, RSTEP, BT::CPITCH, false>(Cs, r0, cc, dst, ld, m, p.M, sq, p.S, wrap, bf16x8{});
+        }
       }
-      *reinterpret_cast<bf16x8 *>(dst) = v;
+    } else {
+      for (int it = 0; it < PASSES; it += U) {
+        bf16x8 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = tid + GB_THREADS * (it + u);
+          const int row = c / RUNS, cc = c - row * RUNS;
+          v[u] = *reinterpret_cast<const bf16x8 *>(&Cs[row * BT::CPITCH + cc * 8]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = tid + GB_THREADS * (it + u);
+          const int row = c / RUNS, cc = c - row * RUNS;
+          const int m = m0 + row, n = n0 + cc * 8;
+          if (m >= p.M || n >= p.N) continue;
+          const int s = seg_of(p, n);
+          const int nn = n - SEG_FIELD(p, s, n_begin), dh = SEG_FIELD(p, s, dh);
+          const int h = nn / dh, d = nn - h * dh;
+          const int b = m / p.S, sq = m - b * p.S;
+          bf16 *dst = reinterpret_cast<bf16 *>(SEG_FIELD(p, s, C)) +
+                      ((int64_t)(b * p.H + h) * p.S + sq) * SEG_FIELD(p, s, ld) + SEG_FIELD(p, s, off) + d;
+          if (p.rn_gain && n < p.rn_cols) {  // the producer stores its normalised columns times the gains
+            const bf16x8 gv = *reinterpret_cast<const bf16x8 *>(p.rn_gain + n);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[u][e] = (bf16)((float)v[u][e] * (float)gv[e]);
+          }
+          *reinterpret_cast<bf16x8 *>(dst) = v[u];
+        }
+      }
     }
   } else {
     // Channel-major destination: the tile goes to LDS transposed (column n
@@ -558,25 +641,52 @@ __global__ __launch_bounds__(GB_THREADS) __attribute__((amdgpu_waves_per_eu(TM *
                                          acc_row(4 * q, lane)]) = *reinterpret_cast<const uint2 *>(v4);
         }
     __syncthreads();
+    // Column n's run of tokens m .. m+7 goes to row (b H + h) dh + d = b H dh
+    // + (n - range start) of its range, at token s (b = m / S, s = m % S).
     bf16 *t_C = reinterpret_cast<bf16 *>(SEG_FIELD(p, st0, C));
     const int t_dh = SEG_FIELD(p, st0, dh), t_nb = SEG_FIELD(p, st0, n_begin);
-    constexpr int RG = BT::M / 8;  // 8-token runs per column
-    for (int it = 0; it < (BT::M * BT::N / 8) / GB_THREADS; ++it) {
-      const int c = tid + GB_THREADS * it;
-      const int col = c / RG, rg = c - col * RG;
-      const int m = m0 + rg * 8, n = n0 + col;
-      if (m >= p.M || n >= p.N) continue;
-      const int nn = n - t_nb;
-      const int h = nn / t_dh, d = nn - h * t_dh;
+    constexpr int RG = BT::M / 8, TPASSES = BT::M * BT::N / 8 / GB_THREADS;  // 8-token runs per column
+    static_assert(BT::M * BT::N / 8 % GB_THREADS == 0, "runs must split evenly over the threads");
+    constexpr int TU = TPASSES % 8 == 0 ? 8 : TPASSES % 4 == 0 ? 4 : 1;
+    bool tfast = false;
+    if constexpr (GB_THREADS % RG == 0) {
+      // a thread keeps one run of tokens; its columns step by CSTEP, U passes
+      // at a time (their LDS reads issued together)
+      constexpr int CSTEP = GB_THREADS / RG;
+      const int rg = tid % RG, col0 = tid / RG;
+      const int m = m0 + rg * 8;
       const int b = m / p.S, sq = m - b * p.S;
-      const bf16 *src = &Cs[col * TP + rg * 8];
-      if (sq + 8 <= p.S && m + 8 <= p.M) {
-        *reinterpret_cast<uint4 *>(t_C + ((int64_t)(b * p.H + h) * t_dh + d) * p.S + sq) =
-            *reinterpret_cast<const uint4 *>(src);
-      } else {
-        for (int e = 0; e < 8 && m + e < p.M; ++e) {
-          const int me = m + e, be = me / p.S, se = me - be * p.S;
-          t_C[((int64_t)(be * p.H + h) * t_dh + d) * p.S + se] = src[e];
+      tfast = m + 8 <= p.M && sq + 8 <= p.S;
+      if (tfast) {
+        bf16 *dst = t_C + ((int64_t)b * p.H * t_dh + (n0 + col0 - t_nb)) * p.S + sq;
+        for (int it = 0; it < TPASSES; it += TU) {
+          uint4 v[TU];
+#pragma unroll
+          for (int u = 0; u < TU; ++u)
+            v[u] = *reinterpret_cast<const uint4 *>(&Cs[(col0 + CSTEP * (it + u)) * TP + rg * 8]);
+#pragma unroll
+          for (int u = 0; u < TU; ++u)
+            if (n0 + col0 + CSTEP * (it + u) < p.N)
+              *reinterpret_cast<uint4 *>(dst + (int64_t)(CSTEP * (it + u)) * p.S) = v[u];
+        }
+      }
+    }
+    if (!tfast) {
+      for (int it = 0; it < TPASSES; ++it) {
+        const int c = tid + GB_THREADS * it;
+        const int col = c / RG, rg = c - col * RG;
+        const int m = m0 + rg * 8, n = n0 + col;
+        if (m >= p.M || n >= p.N) continue;
+        const int b = m / p.S, sq = m - b * p.S;
+        const bf16 *src = &Cs[col * TP + rg * 8];
+        if (sq + 8 <= p.S && m + 8 <= p.M) {
+          *reinterpret_cast<uint4 *>(t_C + ((int64_t)b * p.H * t_dh + (n - t_nb)) * p.S + sq) =
+              *reinterpret_cast<const uint4 *>(src);
+        } else {
+          for (int e = 0; e < 8 && m + e < p.M; ++e) {
+            const int me = m + e, be = me / p.S, se = me - be * p.S;
+            t_C[((int64_t)be * p.H * t_dh + (n - t_nb)) * p.S + se] = src[e];
+          }
         }
       }
     }
