@@ -198,25 +198,41 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
   const uint32_t lds_k = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)Kl;
+  // Per copy k of this wave: its block's source rows (k_nope, or the shared
+  // k_pe) and their pitch, and this lane's byte offset from the tile's first
+  // row.  Every wave issues the first NKALL copies of a tile, the waves with
+  // a block left one more; a tile running past the last key (only the last
+  // tile can) clamps the rows, every other tile takes the fixed offsets.
+  const T *ksrc[NKPW];
+  int kpb[NKPW];
+  uint32_t koff[NKPW];
+#pragma unroll
+  for (int k = 0; k < NKPW; ++k) {
+    const bool nope = wave + NW * k < NKN;
+    ksrc[k] = nope ? kn : kpe;
+    kpb[k] = nope ? DN * ES : a.ld_kpe * ES;
+    koff[k] = (uint32_t)(drow[k] * kpb[k] + dcb[k]);
+  }
+  constexpr int NKALL = (NKN + NKP) / NW;
+  const bool kmore = wave + NW * NKALL < NKN + NKP;
+#define ATT_KCOPY(STG, J0, k, OFF)                                                      \
+  do {                                                                                  \
+    const char *src_ = reinterpret_cast<const char *>(ksrc[k]) + (int64_t)(J0) * kpb[k]; \
+    const uint32_t m0_ = lds_k + (STG) * KSTAGEB + (wave + NW * (k)) * 1024;            \
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"                   \
+                 :: "v"(OFF), "s"(src_), "s"(m0_) : "memory", "m0");                    \
+  } while (0)
 #define ATT_KDMA(STG, J0)                                                               \
   do {                                                                                  \
     const int j0_ = (J0);                                                               \
-    const int lim_ = SK - 1 - j0_;                                                      \
-    const T *bn_ = kn + (int64_t)j0_ * DN;                                              \
-    const T *bp_ = kpe + (int64_t)j0_ * a.ld_kpe;                                       \
-    _Pragma("unroll") for (int k = 0; k < NKPW; ++k) {                                  \
-      const int blk = wave + NW * k;                                                    \
-      const int r_ = min(drow[k], lim_);                                                \
-      const uint32_t m0_ = lds_k + (STG) * KSTAGEB + blk * 1024;                        \
-      if (blk < NKN) {                                                                  \
-        const uint32_t off_ = (uint32_t)(r_ * DN * ES + dcb[k]);                        \
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"               \
-                     :: "v"(off_), "s"(bn_), "s"(m0_) : "memory", "m0");                \
-      } else if (blk < NKN + NKP) {                                                     \
-        const uint32_t off_ = (uint32_t)(r_ * a.ld_kpe * ES + dcb[k]);                  \
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"               \
-                     :: "v"(off_), "s"(bp_), "s"(m0_) : "memory", "m0");                \
-      }                                                                                 \
+    if (j0_ + BKV <= SK) {                                                              \
+      _Pragma("unroll") for (int k = 0; k < NKPW; ++k)                                  \
+        if (k < NKALL || kmore) ATT_KCOPY(STG, j0_, k, koff[k]);                        \
+    } else {                                                                            \
+      const int lim_ = SK - 1 - j0_;                                                    \
+      _Pragma("unroll") for (int k = 0; k < NKPW; ++k)                                  \
+        if (k < NKALL || kmore)                                                         \
+          ATT_KCOPY(STG, j0_, k, (uint32_t)(min(drow[k], lim_) * kpb[k] + dcb[k]));     \
     }                                                                                   \
   } while (0)
 
@@ -235,17 +251,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     vch[k] = (lane & 3) ^ ((row >> 2) & 3);
   }
   const uint32_t lds_v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)Vl;
+  // this lane's byte offset from the tile's first key in a whole tile
+  uint32_t voff[NVPW];
+#pragma unroll
+  for (int k = 0; k < NVPW; ++k) voff[k] = (uint32_t)((vrow[k] * SK + 8 * vch[k]) * ES);
+#define ATT_VCOPY(STG, SRC, k, OFF)                                                     \
+  do {                                                                                  \
+    const uint32_t m0_ = lds_v + (STG) * (NVB * 1024) + (wave + NW * (k)) * 1024;       \
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"                   \
+                 :: "v"(OFF), "s"(SRC), "s"(m0_) : "memory", "m0");                     \
+  } while (0)
 #define ATT_VDMA(STG, J0)                                                               \
   do {                                                                                  \
     const int j0_ = (J0);                                                               \
-    _Pragma("unroll") for (int k = 0; k < NVPW; ++k) {                                  \
-      const int vb = wave + NW * k;                                                     \
-      if (vb < NVB) {                                                                   \
-        const uint32_t off_ = (uint32_t)((vrow[k] * SK + min(j0_ + 8 * vch[k], SK - 8)) * ES); \
-        const uint32_t m0_ = lds_v + (STG) * (NVB * 1024) + vb * 1024;                  \
-        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"               \
-                     :: "v"(off_), "s"(vt_bh), "s"(m0_) : "memory", "m0");              \
-      }                                                                                 \
+    if (j0_ + BKV <= SK) {                                                              \
+      const T *src_ = vt_bh + j0_;                                                      \
+      _Pragma("unroll") for (int k = 0; k < NVPW; ++k)                                  \
+        if (NVB % NW == 0 || wave + NW * k < NVB) ATT_VCOPY(STG, src_, k, voff[k]);     \
+    } else {                                                                            \
+      _Pragma("unroll") for (int k = 0; k < NVPW; ++k)                                  \
+        if (NVB % NW == 0 || wave + NW * k < NVB)                                       \
+          ATT_VCOPY(STG, vt_bh, k, (uint32_t)((vrow[k] * SK + min(j0_ + 8 * vch[k], SK - 8)) * ES)); \
     }                                                                                   \
   } while (0)
   // V^T copies of this wave per tile (0 .. NVPW), for the wait counts
@@ -543,10 +569,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 #undef ATT_KFRAG
 #undef ATT_KDMA
+#undef ATT_KCOPY
 #undef ATT_QK
 #undef ATT_FETCH
 #undef ATT_STASH
 #undef ATT_VDMA
+#undef ATT_VCOPY
 
   // normalise and store o[b, i, h, d]
   const float l_tot = half_swap_sum(l_run);
