@@ -69,6 +69,15 @@ __device__ inline int acc_row(int r, int lane) {
 }
 
 template <typename T> __device__ inline float to_f32(T v) { return (float)v; }
+
+// One RoPE rotation (a, b) -> (a cos - b sin, b cos + a sin) with a fixed
+// rounding (each product with sin rounded, then one fused multiply-add), so
+// that the rotation kernels and a GEMM epilogue that rotates its output
+// give the same bits.
+__device__ inline void rope_rot(float a, float b, float c, float s, float &ra, float &rb) {
+  ra = fmaf(a, c, -(b * s));
+  rb = fmaf(b, c, a * s);
+}
 template <typename T> __device__ inline T from_f32(float v) { return (T)v; }
 
 // 16-byte vector of T.

@@ -73,7 +73,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void rope_kernel(T *x, int64_t n_tok, int64_t S, int64_t sb,
                                                    int64_t ss, int n_heads, int64_t sh,
                                                    const int32_t *positions, RopeTab tab,
-                                                   int tpb) {
+                                                   int tpb, float *tab_out) {
   __shared__ float cs[256], sn[256];
   const int P = tab.pairs;
   const int64_t t0 = (int64_t)blockIdx.x * tpb;
@@ -86,6 +86,10 @@ __global__ __launch_bounds__(256) void rope_kernel(T *x, int64_t n_tok, int64_t 
       sincos(pos * tab.inv_freq[pr], &s, &c);
       cs[i] = (float)c * tab.amp;
       sn[i] = (float)s * tab.amp;
+      if (tab_out && blockIdx.y == 0) {
+        tab_out[t * 2 * P + pr] = cs[i];
+        tab_out[t * 2 * P + P + pr] = sn[i];
+      }
     }
   }
   __syncthreads();
@@ -100,9 +104,10 @@ __global__ __launch_bounds__(256) void rope_kernel(T *x, int64_t n_tok, int64_t 
     const int i0 = tab.convention == 0 ? pr : 2 * pr;
     const int i1 = tab.convention == 0 ? pr + P : 2 * pr + 1;
     const float a = to_f32(base[i0]), b = to_f32(base[i1]);
-    const float c = cs[tl * P + pr], s = sn[tl * P + pr];
-    base[i0] = from_f32<T>(a * c - b * s);
-    base[i1] = from_f32<T>(b * c + a * s);
+    float ra, rb;
+    rope_rot(a, b, cs[tl * P + pr], sn[tl * P + pr], ra, rb);
+    base[i0] = from_f32<T>(ra);
+    base[i1] = from_f32<T>(rb);
   }
 }
 
@@ -116,7 +121,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void rope_vec_kernel(T *x, int64_t n_tok, int64_t S, int64_t sb,
                                                        int64_t ss, int n_heads, int64_t sh,
                                                        const int32_t *positions, RopeTab tab,
-                                                       int tpb) {
+                                                       int tpb, float *tab_out) {
   static_assert(sizeof(T) == 2 || sizeof(T) == 4, "16-byte chunks of bf16 or fp32");
   constexpr int VEC = 16 / sizeof(T);
   __shared__ float cs[256], sn[256];
@@ -131,6 +136,10 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(T *x, int64_t n_tok, int6
       sincos(pos * tab.inv_freq[pr], &s, &c);
       cs[i] = (float)c * tab.amp;
       sn[i] = (float)s * tab.amp;
+      if (tab_out && blockIdx.y == 0) {
+        tab_out[t * 2 * P + pr] = cs[i];
+        tab_out[t * 2 * P + P + pr] = sn[i];
+      }
     }
   }
   __syncthreads();
@@ -153,9 +162,10 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(T *x, int64_t n_tok, int6
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float fa = to_f32(a[k]), fb = to_f32(b[k]), co = ct[8 * c + k], si = st[8 * c + k];
-      a[k] = from_f32<T>(fa * co - fb * si);
-      b[k] = from_f32<T>(fb * co + fa * si);
+      float ra, rb;
+      rope_rot(to_f32(a[k]), to_f32(b[k]), ct[8 * c + k], st[8 * c + k], ra, rb);
+      a[k] = from_f32<T>(ra);
+      b[k] = from_f32<T>(rb);
     }
 #pragma unroll
     for (int q = 0; q < 8 / VEC; ++q) {
@@ -170,10 +180,10 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(T *x, int64_t n_tok, int6
       *reinterpret_cast<uint4 *>(v + q * VEC) = *reinterpret_cast<const uint4 *>(base + 16 * c + q * VEC);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float fa = to_f32(v[2 * k]), fb = to_f32(v[2 * k + 1]);
-      const float co = ct[8 * c + k], si = st[8 * c + k];
-      v[2 * k] = from_f32<T>(fa * co - fb * si);
-      v[2 * k + 1] = from_f32<T>(fb * co + fa * si);
+      float ra, rb;
+      rope_rot(to_f32(v[2 * k]), to_f32(v[2 * k + 1]), ct[8 * c + k], st[8 * c + k], ra, rb);
+      v[2 * k] = from_f32<T>(ra);
+      v[2 * k + 1] = from_f32<T>(rb);
     }
 #pragma unroll
     for (int q = 0; q < 16 / VEC; ++q)
@@ -225,7 +235,7 @@ hipError_t launch_rmsnorm(int dtype, void *x, int64_t rows, int64_t ld, int n, c
 
 hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb, int64_t ss,
                        int n_heads, int64_t sh, const int32_t *positions, const RopeTab &tab,
-                       hipStream_t st) {
+                       hipStream_t st, float *tab_out) {
   if (n_tok <= 0) return hipSuccess;
   const int64_t vec = dtype == BF16 ? 8 : 4;
   const bool vector = tab.pairs % 8 == 0 && ((uintptr_t)x & 15) == 0 && sb % vec == 0 &&
@@ -238,10 +248,10 @@ hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb,
     dim3 grid((unsigned)((n_tok + tpb - 1) / tpb), (unsigned)((tpb * per_tok + 255) / 256));
     if (dtype == BF16)
       hipLaunchKernelGGL(rope_vec_kernel<bf16>, grid, dim3(256), 0, st, (bf16 *)x, n_tok, S, sb,
-                         ss, n_heads, sh, positions, tab, tpb);
+                         ss, n_heads, sh, positions, tab, tpb, tab_out);
     else
       hipLaunchKernelGGL(rope_vec_kernel<float>, grid, dim3(256), 0, st, (float *)x, n_tok, S,
-                         sb, ss, n_heads, sh, positions, tab, tpb);
+                         sb, ss, n_heads, sh, positions, tab, tpb, tab_out);
     return hipGetLastError();
   }
   int per_tok = n_heads * tab.pairs;
@@ -251,10 +261,10 @@ hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb,
   dim3 grid((unsigned)((n_tok + tpb - 1) / tpb));
   if (dtype == BF16)
     hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(256), 0, st, (bf16 *)x, n_tok, S, sb, ss,
-                       n_heads, sh, positions, tab, tpb);
+                       n_heads, sh, positions, tab, tpb, tab_out);
   else
     hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, st, (float *)x, n_tok, S, sb, ss,
-                       n_heads, sh, positions, tab, tpb);
+                       n_heads, sh, positions, tab, tpb, tab_out);
   return hipGetLastError();
 }
 

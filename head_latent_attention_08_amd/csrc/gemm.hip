@@ -31,6 +31,8 @@ struct GemmParams {
   const float *rs_part;
   int rs_chunks;
   float rs_eps;
+  const float *rope_tab;
+  int rope_seg, rope_conv;
 };
 
 template <typename T> struct GemmCfg {
@@ -568,7 +570,79 @@ __global__ __launch_bounds__(GB_THREADS) __attribute__((amdgpu_waves_per_eu(TM *
     constexpr int RUNS = BT::N / 8, PASSES = BT::M * RUNS / GB_THREADS;
     static_assert(BT::M * RUNS % GB_THREADS == 0, "runs must split evenly over the threads");
     constexpr int U = PASSES % 8 == 0 ? 8 : PASSES % 6 == 0 ? 6 : PASSES % 4 == 0 ? 4 : 1;
-    if constexpr (GB_THREADS % RUNS == 0) {
+    if (st0 == p.rope_seg) {
+      // A rotated range (its tiles hold whole heads, dh a multiple of 16, at
+      // most 128): a unit is 8 pairs of one row -- columns c..c+7 with their
+      // partners c+dh/2.. (half-split) or the 16 columns c..c+15
+      // (interleaved) -- in every head of the tile, rotated by the row's
+      // cos / sin of those pairs from the table and stored as 8-column runs.
+      // A thread's units (at most 8) have their table values loaded first.
+      const int dh = SEG_FIELD(p, st0, dh), P = dh >> 1, upr = dh >> 4;  // units per head row
+      const int64_t ld = SEG_FIELD(p, st0, ld);
+      bf16 *cb = reinterpret_cast<bf16 *>(SEG_FIELD(p, st0, C)) + SEG_FIELD(p, st0, off);
+      const int h0 = (n0 - SEG_FIELD(p, st0, n_begin)) / dh;  // the tile's first head
+      const int nh = min(BT::N, p.N - n0) / dh;                // heads in the tile
+      const int nunit = BT::M * upr;
+      // (formed here: hoisted to the kernel's start, values derived from the
+      // thread index would occupy a register through the K loop)
+      int tid_r = tid;
+      asm volatile("" : "+v"(tid_r));
+      constexpr int MAXU = BT::M * 8 / GB_THREADS;
+      float4 tcs[MAXU][4];
+#pragma unroll
+      for (int it = 0; it < MAXU; ++it) {
+        const int u = tid_r + GB_THREADS * it;
+        if (u < nunit) {
+          const int row = u / upr, k = u - row * upr;
+          const float *tb = p.rope_tab + (int64_t)min(m0 + row, p.M - 1) * dh + 8 * k;
+          tcs[it][0] = *reinterpret_cast<const float4 *>(tb);
+          tcs[it][1] = *reinterpret_cast<const float4 *>(tb + 4);
+          tcs[it][2] = *reinterpret_cast<const float4 *>(tb + P);
+          tcs[it][3] = *reinterpret_cast<const float4 *>(tb + P + 4);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < MAXU; ++it) {
+        const int u = tid_r + GB_THREADS * it;
+        if (u >= nunit) break;
+        const int row = u / upr, k = u - row * upr;
+        const int m = m0 + row;
+        if (m >= p.M) continue;
+        const float co[8] = {tcs[it][0].x, tcs[it][0].y, tcs[it][0].z, tcs[it][0].w,
+                             tcs[it][1].x, tcs[it][1].y, tcs[it][1].z, tcs[it][1].w};
+        const float si[8] = {tcs[it][2].x, tcs[it][2].y, tcs[it][2].z, tcs[it][2].w,
+                             tcs[it][3].x, tcs[it][3].y, tcs[it][3].z, tcs[it][3].w};
+        const int ca = p.rope_conv ? 16 * k : 8 * k, cbb = ca + (p.rope_conv ? 8 : P);  // within a head
+        const int b = m / p.S, sq = m - b * p.S;
+        bf16 *dst = cb + ((int64_t)(b * p.H + h0) * p.S + sq) * ld;
+        const int64_t hstep = (int64_t)p.S * ld;  // next head, same token
+        for (int hh = 0; hh < nh; ++hh, dst += hstep) {
+          bf16x8 va = *reinterpret_cast<const bf16x8 *>(&Cs[row * BT::CPITCH + hh * dh + ca]);
+          bf16x8 vb = *reinterpret_cast<const bf16x8 *>(&Cs[row * BT::CPITCH + hh * dh + cbb]);
+          float ra, rb;
+          if (p.rope_conv == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              rope_rot((float)va[j], (float)vb[j], co[j], si[j], ra, rb);
+              va[j] = (bf16)ra;
+              vb[j] = (bf16)rb;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              rope_rot((float)va[2 * j], (float)va[2 * j + 1], co[j], si[j], ra, rb);
+              va[2 * j] = (bf16)ra;
+              va[2 * j + 1] = (bf16)rb;
+              rope_rot((float)vb[2 * j], (float)vb[2 * j + 1], co[4 + j], si[4 + j], ra, rb);
+              vb[2 * j] = (bf16)ra;
+              vb[2 * j + 1] = (bf16)rb;
+            }
+          }
+          *reinterpret_cast<bf16x8 *>(dst + ca) = va;
+          *reinterpret_cast<bf16x8 *>(dst + cbb) = vb;
+        }
+      }
+    } else if constexpr (GB_THREADS % RUNS == 0) {
       // a thread keeps one run of columns; its rows step by RSTEP
       constexpr int RSTEP = GB_THREADS / RUNS;
       const int cc = tid % RUNS, r0 = tid / RUNS;
@@ -937,6 +1011,35 @@ bool gemm_uses_large_tiles(const GemmDesc &d) {
   return big && tr_aligned(d, BigTile<4, 4, GB_STAGES>::N);
 }
 
+// The large-tile configuration launch_gemm runs a product on: 0 for 256x256
+// tiles, 1 for 192x192, 2 for 256x128.
+//  * A product whose 256x256 tiles would leave most CUs idle in its only
+//    round (the down projection: 144 tiles) runs as 192x192 tiles, which
+//    fill one round (242 tiles) at a somewhat lower efficiency per tile.
+//  * Short K (the kv up-projection, K = 512): 256x128 tiles through three
+//    stages fit two workgroups per CU (two waves per SIMD), so one's
+//    epilogue runs under the other's K loop (5% faster there; slower for
+//    long K, whose tiles are all main loop).
+static int big_config(const GemmDesc &d) {
+  const int cus = device_cus();
+  const int64_t t256 = (int64_t)((d.M + 255) / 256) * ((d.N + 255) / 256);
+  const int64_t t192 = (int64_t)((d.M + 191) / 192) * ((d.N + 191) / 192);
+  if (10 * t256 <= 6 * cus && t192 <= cus && tr_aligned(d, 192)) return 1;
+  if (d.K <= 512 && tr_aligned(d, 128)) return 2;
+  return 0;
+}
+
+bool gemm_rope_fusable(const GemmDesc &d, int seg) {
+  if (seg < 0 || seg >= d.nseg || !gemm_uses_large_tiles(d)) return false;
+  static const int tile_n[3] = {256, 192, 128};
+  const int bn = tile_n[big_config(d)];
+  const GemmSeg &s = d.seg[seg];
+  const int end = seg + 1 < d.nseg ? d.seg[seg + 1].n_begin : d.N;
+  return !s.tr && s.dh % 16 == 0 && s.dh <= 128 && bn % s.dh == 0 && s.n_begin % bn == 0 &&
+         (end - s.n_begin) % s.dh == 0 && (end == d.N || end % bn == 0) &&
+         !(d.rn_part && s.n_begin < d.rn_cols);
+}
+
 bool gemm_takes_large_tiles(int dtype, int M, int N, int K) {
   return dtype == BF16 && K % GB_K == 0 && M >= 512 && N % 8 == 0 && (int64_t)M * K < (1LL << 31) &&
          (int64_t)N * K < (1LL << 31);
@@ -963,19 +1066,14 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st) {
   p.rs_part = d.rs_part;
   p.rs_chunks = d.rs_chunks;
   p.rs_eps = d.rs_eps;
+  p.rope_tab = d.rope_tab;
+  p.rope_seg = d.rope_tab ? d.rope_seg : -1;
+  p.rope_conv = d.rope_conv;
+  if (d.rope_tab && !gemm_rope_fusable(d, d.rope_seg)) return hipErrorInvalidValue;
   if (gemm_uses_large_tiles(d)) {
-    // A product whose 256x256 tiles would leave most CUs idle in its only
-    // round (the down projection: 144 tiles) runs as 192x192 tiles, which
-    // fill one round (242 tiles) at a somewhat lower efficiency per tile.
-    const int cus = device_cus();
-    const int64_t t256 = (int64_t)((d.M + 255) / 256) * ((d.N + 255) / 256);
-    const int64_t t192 = (int64_t)((d.M + 191) / 192) * ((d.N + 191) / 192);
-    if (10 * t256 <= 6 * cus && t192 <= cus && tr_aligned(d, 192)) return launch_big<3, 3>(p, d, 0, d.N, st);
-    // Short K (the kv up-projection, K = 512): 256x128 tiles through three
-    // stages fit two workgroups per CU (two waves per SIMD), so one's
-    // epilogue runs under the other's K loop (5% faster there; slower for
-    // long K, whose tiles are all main loop).
-    if (d.K <= 512 && tr_aligned(d, 128)) return launch_big<4, 2, 3>(p, d, 0, d.N, st);
+    const int cfg = big_config(d);
+    if (cfg == 1) return launch_big<3, 3>(p, d, 0, d.N, st);
+    if (cfg == 2) return launch_big<4, 2, 3>(p, d, 0, d.N, st);
     return launch_big<4, 4>(p, d, 0, d.N, st);
   }
   // a split RMSNorm exists only in the large-tile kernel's epilogue

@@ -59,6 +59,15 @@ struct GemmDesc {
   const float *rs_part = nullptr;
   int rs_chunks = 0;
   float rs_eps = 0.f;
+  // RoPE of the stored values of column range rope_seg (large-tile kernel
+  // only, and only where its tiles hold whole heads of that range; see
+  // gemm_rope_fusable): in each dh-wide head, pair i of row m -- columns
+  // (i, i + dh/2) for rope_conv 0 (half-split), (2i, 2i + 1) for 1
+  // (interleaved) -- is rotated by rope_tab[m * dh + i] (cos) and
+  // rope_tab[m * dh + dh/2 + i] (sin), as launch_rope's table holds them.
+  const float *rope_tab = nullptr;
+  int rope_seg = -1;
+  int rope_conv = 0;
 };
 
 hipError_t launch_gemm(const GemmDesc &d, hipStream_t st);
@@ -68,6 +77,10 @@ hipError_t launch_gemm(const GemmDesc &d, hipStream_t st);
 bool gemm_takes_large_tiles(int dtype, int M, int N, int K);
 // Whether launch_gemm runs this product on the large-tile kernel.
 bool gemm_uses_large_tiles(const GemmDesc &d);
+// Whether launch_gemm can rotate column range `seg` of this product in its
+// epilogue (bf16 large tiles whose columns hold whole heads of the range,
+// heads a multiple of 16 wide, no split RMSNorm producer on the range).
+bool gemm_rope_fusable(const GemmDesc &d, int seg);
 
 // Scratch bytes launch_gemm can use for split-K partials of an M x N x K
 // product (0 when it never splits).
@@ -87,11 +100,14 @@ struct RopeTab {
 };
 
 // In-place RoPE: element (t, h, i) at x + (t / S) * sb + (t % S) * ss + h * sh + i,
-// position positions[t] (device) or t % S when positions is NULL.
+// position positions[t] (device) or t % S when positions is NULL.  With
+// tab_out, token t's cos and sin (amplitude included) of its pairs are also
+// written to tab_out[t * rope_dim + i] and tab_out[t * rope_dim + pairs + i]
+// (the table a GEMM epilogue that rotates its output reads).
 hipError_t launch_rope(int dtype, void *x, int64_t n_tok, int64_t S, int64_t sb,
                        int64_t ss, int n_heads, int64_t sh,
                        const int32_t *positions, const RopeTab &tab,
-                       hipStream_t st);
+                       hipStream_t st, float *tab_out = nullptr);
 
 // Copy `width` contiguous elements per row: dst row t at dst + t * ldd from
 // src + t * lds (prefill latent output).

@@ -199,6 +199,8 @@ struct PrefillPlan {
   size_t off_down, off_q, off_kn, off_v, off_o, total;
   size_t off_qrms;  // split RMSNorm of c_q: [B*S, r_q / 64] fp32 partial sums of squares
   bool q_norm_split;
+  size_t off_rope;  // q_pe rotated in the q up-projection: [B*S, d_r] fp32 cos | sin per token
+  bool q_rope_fused;
   size_t off_start, off_last, off_pos, off_valid, off_ok;  // key-range prefills only
 };
 
@@ -276,6 +278,12 @@ PrefillPlan plan_prefill(const mla_config &c, int64_t B, int64_t S, bool varlen 
                    gemm_uses_large_tiles(down_proj_desc(c, M, nullptr, nullptr, nullptr, p.ld_down)) &&
                    gemm_uses_large_tiles(q_up_desc(c, M, S, nullptr, nullptr, p.ld_down, nullptr));
   p.off_qrms = take(p.q_norm_split ? (size_t)M * (c.q_lora_rank / 64) * sizeof(float) : 0);
+  // RoPE of q_pe in the q up-projection's epilogue where its tiles hold whole
+  // q_pe heads: the k_pe rotation (which runs first, at the same tokens'
+  // positions) leaves every token's cos / sin in a table for it
+  p.q_rope_fused = c.dtype == MLA_DTYPE_BF16 &&
+                   gemm_rope_fusable(q_up_desc(c, M, S, nullptr, nullptr, p.ld_down, nullptr), 1);
+  p.off_rope = take(p.q_rope_fused ? (size_t)M * c.qk_rope_head_dim * sizeof(float) : 0);
   p.total = off;
   return p;
 }
@@ -476,8 +484,9 @@ static mla_status prefill_common(const mla_config *cfg, const mla_weights *w, co
   }
   // 3. RoPE of the shared key at positions 0..S-1
   MLA_MARK(2);
+  float *rope_tab = p.q_rope_fused ? reinterpret_cast<float *>(ws + p.off_rope) : nullptr;
   MLA_HIP(launch_rope(c.dtype, down + (size_t)(rq + rkv) * es, M, S, (int64_t)S * p.ld_down,
-                      p.ld_down, 1, 0, vl_pos, tab, st),
+                      p.ld_down, 1, 0, vl_pos, tab, st, rope_tab),
           "rope k_pe");
   if (latent_out)
     MLA_HIP(launch_copy_rows(c.dtype, latent_out, rkv + dr, down + (size_t)rq * es, p.ld_down, M,
@@ -492,12 +501,18 @@ static mla_status prefill_common(const mla_config *cfg, const mla_weights *w, co
       g.rs_chunks = rq / 64;
       g.rs_eps = c.rms_norm_eps;
     }
+    if (p.q_rope_fused) {
+      g.rope_tab = rope_tab;
+      g.rope_seg = 1;
+      g.rope_conv = c.rope.convention;
+    }
     MLA_HIP(launch_gemm(g, st), "q up-projection");
   }
   MLA_MARK(4);
-  MLA_HIP(launch_rope(c.dtype, q + (size_t)dn * es, M, S, (int64_t)H * S * dqk, dqk, H,
-                      (int64_t)S * dqk, vl_pos, tab, st),
-          "rope q_pe");
+  if (!p.q_rope_fused)
+    MLA_HIP(launch_rope(c.dtype, q + (size_t)dn * es, M, S, (int64_t)H * S * dqk, dqk, H,
+                        (int64_t)S * dqk, vl_pos, tab, st),
+            "rope q_pe");
   // 5. k_nope [B, H, S, d_n] and v channel-major [B, H, d_v, S] per head
   MLA_MARK(5);
   {

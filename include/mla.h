@@ -525,7 +525,9 @@ MLA_API mla_status mla_backward(const mla_config *cfg, const mla_weights *w, con
  * the call's stream just before it launches stage k, and events[n_stages]
  * after its last launch, for every index < n_events.  Stage order:
  *   prefill: 0 down projections, 1 RMSNorm, 2 k_pe RoPE (+ latent copy),
- *            3 q up-projection, 4 q_pe RoPE, 5 kv up-projection,
+ *            3 q up-projection, 4 q_pe RoPE (no launch where the q
+ *            up-projection rotates q_pe in its epilogue: bf16 on large
+ *            tiles holding whole q_pe heads), 5 kv up-projection,
  *            6 attention, 7 output projection            (9 events)
  *   decode:  0 down projections, 1 RMSNorm, 2 k_pe RoPE + cache append,
  *            3 q up-projection, 4 q_pe RoPE, 5 absorption, 6 latent
