@@ -48,17 +48,17 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     "attention": {
-        "sha256": "c511da3c7417c124cc3c7d1fee685482bb104699cc10372cf5733ff62001307d",
-        "FETCH_SIZE_KiB": 323771.1, "WRITE_SIZE_KiB": 131956.6},
+        "sha256": "a75e34605cb7e18bf5230a138275282c9c872140e0170178a4c3d2c5c67205a6",
+        "FETCH_SIZE_KiB": 338164.8, "WRITE_SIZE_KiB": 132023.0},
     "out_proj": {
-        "sha256": "3f81ecbcf74995c225203be078b7e0960ecd0518a9979b43eefe6ac6a4456729",
-        "FETCH_SIZE_KiB": 1440347.3, "WRITE_SIZE_KiB": 57344.0},
+        "sha256": "1ce4fccadccf01107b93d0dad80251b2de984b467591e5025d7eb45a6ab40511",
+        "FETCH_SIZE_KiB": 1481169.8, "WRITE_SIZE_KiB": 57344.0},
     "latent_attention": {
-        "sha256": "60ec3fd5e4d44fc8ba548518df16a1b8a327f31a700aedbd12d33f6a1efba23f",
-        "FETCH_SIZE_KiB": 181371.2, "WRITE_SIZE_KiB": 76843.0},
+        "sha256": "2b2bbd277a1ef9ecc68089acdd0b8e2a391fc4763415004f3fdac3f04bb711be",
+        "FETCH_SIZE_KiB": 181372.7, "WRITE_SIZE_KiB": 76843.0},
     "fp8_out_proj": {
-        "sha256": "58394bc4cb444ddcacdb7151609927b6591156e25c9031e50bb370a95b01b4dc",
-        "FETCH_SIZE_KiB": 380563.2, "WRITE_SIZE_KiB": 57792.0},
+        "sha256": "d12584c8d003b594e35e2010205f90def85093e1799b289684299359a2e9cca4",
+        "FETCH_SIZE_KiB": 380295.3, "WRITE_SIZE_KiB": 57792.0},
 }
 METRIC = "MLA prefill TFLOP/s + absorbed-decode latent-cache GB/s, V3 shapes, 1 MI355X"
 
