@@ -139,6 +139,35 @@ def test_p5_shape_conventions():
     assert np.abs(d_ref).max() > 10 * np.abs(yp[rows[1:]] - yi[rows[1:]]).mean()
 
 
+def test_q_rope_in_up_projection_sampled_rows():
+    # At this shape (seq 2048, V3 sizes, bf16) the q up-projection rotates
+    # q_pe in its epilogue from the table the k_pe rotation writes: the
+    # workspace's q of sampled tokens (every head) against the oracle's
+    # c_q -> RMSNorm -> up-projections -> RoPE at those positions, both
+    # conventions.
+    m = _m()
+    c = shrink(si.CONFIGS["v3_prefill"], seed=7100)
+    x, w = si.make_inputs(c, seq=2048)
+    H, dn, dr = c["num_attention_heads"], c["qk_nope_head_dim"], c["qk_rope_head_dim"]
+    rows = np.array([0, 1, 31, 255, 256, 1000, 2047])
+    xs = np.asarray(x, dtype=np.float64)[0, rows]
+    for conv in ("interleaved", "half_split"):
+        print(f"q rows: seq 2048 {conv}, seed 7100", flush=True)
+        cfg = mla_cfg(c, rope=conv)
+        _, _, ws = m.mla_prefill_forward(cfg, weights_to_dev(w, "bf16"), to_dev(x, "bf16"))
+        torch.cuda.synchronize()
+        lay = m.mla_prefill_layout_of(cfg, 1, 2048)
+        q = to_np(ws[lay.q: lay.q + H * 2048 * (dn + dr) * 2].view(torch.bfloat16).view(H, 2048, dn + dr))
+        oc = oracle_cfg(c, rope=conv)
+        c_qn = orc.rmsnorm(xs @ np.asarray(w["w_down_q"], np.float64).T,
+                           np.asarray(w["q_norm"], np.float64), oc.rms_norm_eps)
+        q_nope = (c_qn @ np.asarray(w["w_up_q"], np.float64).T).reshape(len(rows), H, dn)
+        q_pe = orc.apply_rope((c_qn @ np.asarray(w["w_qr"], np.float64).T).reshape(len(rows), H, dr), rows, oc)
+        got = q[:, rows].transpose(1, 0, 2)  # [rows, H, dn + dr]
+        assert_close_rows(got[..., dn:], q_pe, "bf16", f"q_pe {conv}")
+        assert_close_rows(got[..., :dn], q_nope, "bf16", f"q_nope {conv}")
+
+
 def test_causality_bitwise():
     # perturbing tokens t >= t0 leaves every output row t < t0 bit-identical
     c = si.CONFIGS["small"]
