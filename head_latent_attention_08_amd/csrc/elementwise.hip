@@ -203,6 +203,19 @@ __global__ void copy_rows_kernel(T *dst, int64_t ldd, const T *src, int64_t lds,
   }
 }
 
+// The same copy in 16-byte chunks (widths, pitches and both bases a whole
+// number of chunks): a workgroup takes one row block of 256 / nch rows.
+__global__ __launch_bounds__(256) void copy_rows16_kernel(uint4 *dst, int64_t ldd, const uint4 *src,
+                                                          int64_t lds, int64_t rows, int nch) {
+  const int64_t total = rows * nch;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nch;
+    const int c = (int)(i - r * nch);
+    dst[r * ldd + c] = src[r * lds + c];
+  }
+}
+
 template <typename T>
 __global__ void cache_append_kernel(T *cache, int64_t cap, const int32_t *lens, int q_len,
                                     const T *src, int64_t lds, int width) {
@@ -421,6 +434,16 @@ hipError_t launch_gather_keys(int dtype, void *dst, int64_t n_rows, const void *
 hipError_t launch_copy_rows(int dtype, void *dst, int64_t ldd, const void *src, int64_t lds,
                             int64_t rows, int width, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  const int64_t es = dtype == BF16 ? 2 : 4;
+  if ((width * es) % 16 == 0 && (ldd * es) % 16 == 0 && (lds * es) % 16 == 0 &&
+      ((uintptr_t)dst & 15) == 0 && ((uintptr_t)src & 15) == 0) {
+    const int nch = (int)(width * es / 16);
+    const int64_t total = rows * nch;
+    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+    hipLaunchKernelGGL(copy_rows16_kernel, dim3(blocks), dim3(256), 0, st, (uint4 *)dst, ldd * es / 16,
+                       (const uint4 *)src, lds * es / 16, rows, nch);
+    return hipGetLastError();
+  }
   int64_t total = rows * width;
   unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
   if (dtype == BF16)
