@@ -11,6 +11,8 @@
 // grid of 64x64 wave tiles (2x2 MFMA tiles each), K in 64-byte slabs staged
 // through double-buffered LDS with register prefetch of the next slab.
 
+#include <numeric>
+
 #include "common.h"
 #include "internal.h"
 
@@ -320,7 +322,8 @@ template <int Q> __device__ inline void wait_slabs_outstanding(int slabs) {
 // Launch window: output columns [n_base, n_base + tiles_n * tile N) of every row.
 template <int TM, int TN, int GB_NST>
 __global__ __launch_bounds__(GB_THREADS) __attribute__((amdgpu_waves_per_eu(TM * TN <= 8 ? 2 : 1))) void gemm_big_kernel(GemmParams p, int tiles_m, int tiles_n,
-                                                              int n_base, int remap, int group_m) {
+                                                              int n_base, int remap, int group_m,
+                                                              int cstride) {
   using BT = BigTile<TM, TN, GB_NST>;
   constexpr int NQ = BT::NQ, QH = BT::QH, ABLK = BT::ABLK;
   __shared__ __attribute__((aligned(16))) bf16 lds[BT::LDS];
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(GB_THREADS) __attribute__((amdgpu_waves_per_eu(TM *
   const int first_m = grp * group_m;
   const int gm = min(tiles_m - first_m, group_m);
   const int tm = first_m + (t % per_group) % gm;
-  const int tn = (t % per_group) / gm;
+  const int tn = (t % per_group) / gm * cstride % tiles_n;  // cstride: coprime column stride (or 1)
   const int m0 = tm * BT::M, n0 = n_base + tn * BT::N;
   const int nk = p.K / GB_K;
 
@@ -998,8 +1001,19 @@ static hipError_t launch_big(const GemmParams &p, const GemmDesc &d, int n_lo, i
   // measured best for K >= 1536 (eight: +1% on the out- and down-
   // projections, sixteen: +37%); short K runs one tile row at a time.
   const int group_m = d.K <= 1024 ? 1 : 4;
+  // With a rotated column range (whose tiles take longer) the tile columns
+  // are visited with a stride coprime to their count, so that every XCD's
+  // contiguous share of tiles holds its part of that range instead of some
+  // XCDs getting all of it (same panels per group, so the same L2 reuse).
+  int cstride = 1;
+  if (p.rope_tab)
+    for (int s : {5, 7, 11, 13})
+      if (s < tn && std::gcd(s, tn) == 1) {
+        cstride = s;
+        break;
+      }
   hipLaunchKernelGGL((gemm_big_kernel<TM, TN, NST>), dim3(T), dim3(GB_THREADS), 0, st, p, tm, tn, n_lo,
-                     (T % 8 == 0) ? 1 : 0, group_m);
+                     (T % 8 == 0) ? 1 : 0, group_m, cstride);
   return hipGetLastError();
 }
 
