@@ -54,8 +54,8 @@ TRAFFIC = {
         "sha256": "1ce4fccadccf01107b93d0dad80251b2de984b467591e5025d7eb45a6ab40511",
         "FETCH_SIZE_KiB": 1481169.8, "WRITE_SIZE_KiB": 57344.0},
     "latent_attention": {
-        "sha256": "2b2bbd277a1ef9ecc68089acdd0b8e2a391fc4763415004f3fdac3f04bb711be",
-        "FETCH_SIZE_KiB": 181372.7, "WRITE_SIZE_KiB": 76843.0},
+        "sha256": "5141dfedf8eddf2bfb5d071cb0d96d3dd0c523d724a8b3c07b2caf60f1727ef4",
+        "FETCH_SIZE_KiB": 181457.15, "WRITE_SIZE_KiB": 38571.0},
     "fp8_out_proj": {
         "sha256": "d12584c8d003b594e35e2010205f90def85093e1799b289684299359a2e9cca4",
         "FETCH_SIZE_KiB": 380295.3, "WRITE_SIZE_KiB": 57792.0},

@@ -21,6 +21,9 @@
 // o_lat, running max, running sum) per sequence piece, in slot (range + b)
 // -- unique because range and sequence indices both rise along the rows.  A
 // merge kernel combines the pieces of each sequence with log-sum-exp weights.
+// With a bf16 cache the partial o_lat is stored in bf16 (half the bytes the
+// attention kernel writes and the merge reads back, one extra rounding that
+// the final bf16 output would mostly absorb); with fp32 it stays fp32.
 //
 // Inside a workgroup: four waves, 32 heads each (one head per lane pair), on
 // 32x32x16 MFMAs.  A wave computes S^T = C Q^T (32 cache rows x 32 heads per
@@ -43,6 +46,8 @@
 
 #include "common.h"
 #include "internal.h"
+
+#include <type_traits>
 
 namespace mla {
 namespace {
@@ -81,6 +86,31 @@ struct DecCfg {
   static constexpr int NQL = NQF - NQR;
   static constexpr int QPITCH = NQL * MF::KSTEP + VEC;
   static constexpr int NCT = RP / 32;
+};
+
+// Four consecutive channels of a split partial as stored: bf16 for a bf16
+// cache (the only 2-byte element type here), else fp32.
+template <typename T> struct Part4 {
+  static constexpr bool NARROW = sizeof(T) == 2;
+  using elem = std::conditional_t<NARROW, T, float>;
+  using raw = std::conditional_t<NARROW, uint2, f32x4>;
+  __device__ static raw pack(float a, float b, float c, float d) {
+    if constexpr (NARROW) {
+      const bf16x2 lo = {from_f32<T>(a), from_f32<T>(b)};
+      const bf16x2 hi = {from_f32<T>(c), from_f32<T>(d)};
+      return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    } else {
+      return f32x4{a, b, c, d};
+    }
+  }
+  __device__ static f32x4 unpack(raw r) {
+    if constexpr (NARROW) {  // a bf16 is the upper half of the fp32 with its bits
+      return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                   __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+    } else {
+      return r;
+    }
+  }
 };
 
 constexpr int NSTAGE = 3;  // cache tiles in flight: current, next, and the one after
@@ -493,20 +523,61 @@ __global__ __launch_bounds__(DTHREADS) void decode_attn_kernel(DecodeAttnArgs a)
 
     // partial of this sequence piece: unnormalised o_lat (log2-domain max,
     // sum).  o_lat is stored in the accumulator layout, 32 heads x RP
-    // channels per block: channel tile d, row quad q, lane, 4 floats, so each
-    // store instruction writes 1 KB of consecutive bytes.
-    if (wave_live) {
-      const float l_tot = l_run + __shfl_xor(l_run, 32);
-      const int slot = blk + b;
-      float *po = a.part_o + ((int64_t)slot * ((H + HPW - 1) / HPW) + hg * (HPB / HPW) + wave) *
-                                 (HPW * NCT * 32) + lane * 4;
+    // channels per block: channel tile d, row quad q, lane, 4 values, so each
+    // store instruction writes consecutive bytes (1 KB in fp32, 512 B in bf16).
+    using P4 = Part4<T>;
+    typename P4::elem *po =
+        reinterpret_cast<typename P4::elem *>(a.part_o) +
+        ((int64_t)(blk + b) * ((H + HPW - 1) / HPW) + hg * (HPB / HPW) + wave) * (HPW * NCT * 32) + lane * 4;
+    // channel tiles per wave per round of the LDS bounce below
+    constexpr int DPR = NSTAGE * STAGEB / (4 * 4 * 1024) < NCT ? NSTAGE * STAGEB / (4 * 4 * 1024) : NCT;
+    if constexpr (P4::NARROW && DPR >= 1) {
+      // The accumulators pass through the idle cache stages: each lane
+      // writes its fp32 quads to LDS and reads them back into vector
+      // registers to convert them.  Converting straight from the
+      // accumulation registers moves the MFMAs' accumulators to the vector
+      // registers, where they do not fit beside the tile loop's operands.
+      // Every wave is past its tile loop once the first barrier is passed;
+      // a lane reads only what it wrote, and the barriers keep the stores
+      // and loads in order.  (Shapes whose stages are too small for this
+      // have few accumulators and convert them directly.)
+      f32x4 *bounce = reinterpret_cast<f32x4 *>(lds + wave * (DPR * 4 * 1024)) + lane;
+#pragma unroll
+      for (int d0 = 0; d0 < NCT; d0 += DPR) {
+        __syncthreads();
+        if (wave_live) {
+#pragma unroll
+          for (int dd = 0; dd < DPR; ++dd)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (d0 + dd < NCT)
+                bounce[(dd * 4 + q) * 64] = f32x4{o[d0 + dd][4 * q], o[d0 + dd][4 * q + 1],
+                                                  o[d0 + dd][4 * q + 2], o[d0 + dd][4 * q + 3]};
+        }
+        __syncthreads();
+        if (wave_live) {
+#pragma unroll
+          for (int dd = 0; dd < DPR; ++dd)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (d0 + dd < NCT) {
+                const f32x4 v = bounce[(dd * 4 + q) * 64];
+                *reinterpret_cast<typename P4::raw *>(po + ((d0 + dd) * 4 + q) * 256) =
+                    P4::pack(v[0], v[1], v[2], v[3]);
+              }
+        }
+      }
+    } else if (wave_live) {
 #pragma unroll
       for (int d = 0; d < NCT; ++d)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v = {o[d][4 * q], o[d][4 * q + 1], o[d][4 * q + 2], o[d][4 * q + 3]};
-          *reinterpret_cast<f32x4 *>(po + (d * 4 + q) * 256) = v;
-        }
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<typename P4::raw *>(po + (d * 4 + q) * 256) =
+              P4::pack(o[d][4 * q], o[d][4 * q + 1], o[d][4 * q + 2], o[d][4 * q + 3]);
+    }
+    if (wave_live) {
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const int slot = blk + b;
       if (h < H && g == 0) {
         a.part_ml[((int64_t)slot * H + h) * 2 + 0] = m_ref * sl2;
         a.part_ml[((int64_t)slot * H + h) * 2 + 1] = l_tot;
@@ -604,25 +675,28 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeAttnArgs a) {
     // two register sets: the loads of piece i + 1 are in flight while piece
     // i is accumulated (loads past the last piece re-read it and are not
     // used; unconditional loads keep the wait counts exact)
-    const f32x4 *po = reinterpret_cast<const f32x4 *>(
-        a.part_o + ((int64_t)(i0 + b) * n_hb + hb) * (HPW * RP)) + tid;
-    const int64_t pstride = (int64_t)n_hb * HPW * RP / 4;  // f32x4 per piece
-    f32x4 va[NCH], vb[NCH];
+    using P4 = Part4<T>;
+    using raw = typename P4::raw;
+    const raw *po = reinterpret_cast<const raw *>(reinterpret_cast<const typename P4::elem *>(a.part_o) +
+                                                  ((int64_t)(i0 + b) * n_hb + hb) * (HPW * RP)) +
+                    tid;
+    const int64_t pstride = (int64_t)n_hb * HPW * RP / 4;  // four-channel chunks per piece
+    raw va[NCH], vb[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) va[k] = po[k * 256];
     for (int i = 0; i < np; i += 2) {
-      const f32x4 *pb = po + min(i + 1, np - 1) * pstride;
+      const raw *pb = po + min(i + 1, np - 1) * pstride;
 #pragma unroll
       for (int k = 0; k < NCH; ++k) vb[k] = pb[k * 256];
       const float wa = wsh[hl][i];
       const float wb = i + 1 < np ? wsh[hl][i + 1] : 0.f;
 #pragma unroll
-      for (int k = 0; k < NCH; ++k) acc[k] += wa * va[k];
-      const f32x4 *pa = po + min(i + 2, np - 1) * pstride;
+      for (int k = 0; k < NCH; ++k) acc[k] += wa * P4::unpack(va[k]);
+      const raw *pa = po + min(i + 2, np - 1) * pstride;
 #pragma unroll
       for (int k = 0; k < NCH; ++k) va[k] = pa[k * 256];
 #pragma unroll
-      for (int k = 0; k < NCH; ++k) acc[k] += wb * vb[k];
+      for (int k = 0; k < NCH; ++k) acc[k] += wb * P4::unpack(vb[k]);
     }
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {

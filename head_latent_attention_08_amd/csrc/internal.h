@@ -246,8 +246,8 @@ struct DecodeAttnArgs {
   const void *cache;  // [B, cap, r + dr]
   const int32_t *lens;
   void *o_lat;        // [B, H, r]
-  float *part_o;      // [(n_blocks + B), ceil(H/32)] blocks of 32 heads x r padded to 32
-                      // (MFMA accumulator order)
+  void *part_o;       // [(n_blocks + B), ceil(H/32)] blocks of 32 heads x r padded to 32
+                      // (MFMA accumulator order); bf16 for a bf16 cache, else fp32
   float *part_ml;     // [(n_blocks + B), H, 2]
   int64_t cap;
   int B, H;

@@ -314,9 +314,10 @@ DecodePlan plan_decode(const mla_config &c, int64_t Bseq, int64_t T = 1) {
   p.off_down = take((size_t)B * p.ld_down * es);
   p.off_qn = take((size_t)B * H * c.qk_nope_head_dim * es);
   p.off_qlat = take((size_t)B * H * (r + dr) * es);
-  // attention partials: blocks of 32 heads x (r rounded up to 32) channels
+  // attention partials: blocks of 32 heads x (r rounded up to 32) channels,
+  // bf16 for a bf16 cache, else fp32
   p.off_po = take((size_t)(p.n_blocks + Bseq) * ((T * H + 31) / 32) * 32 * ((r + 31) / 32 * 32) *
-                  sizeof(float));
+                  (es == 2 ? es : sizeof(float)));
   p.off_pml = take((size_t)(p.n_blocks + Bseq) * T * H * 2 * sizeof(float));
   p.off_olat = take((size_t)B * H * r * es);
   p.off_o = take((size_t)B * H * c.v_head_dim * es);
@@ -1644,7 +1645,7 @@ mla_status decode_impl(const mla_config *cfg, const mla_weights *w, const void *
     a.cache = latent_cache;
     a.lens = cache_lens;
     a.o_lat = olat;
-    a.part_o = (float *)(ws + p.off_po);
+    a.part_o = ws + p.off_po;
     a.part_ml = (float *)(ws + p.off_pml);
     a.cap = cache_capacity;
     a.B = Bs;
